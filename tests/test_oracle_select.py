@@ -1,0 +1,114 @@
+"""Pins of the oracle's precision selection.
+
+* MixKVQ query awareness (page "速读" and "背景知识与关键观察", error-only
+  ablation in the appendix): on the tiny workload the four outlier Key
+  channels whose query is NOT attenuated hold the top saliency ranks (they are
+  BF16 tier), the four attenuated ones fall below every normal channel in
+  A_d, while an error-only ranking (A_d = S_d) puts all eight first;
+* ranking agrees with a brute-force Fraction computation of
+  mean|Q| * (max k - min k)/3 (the psi grid is exact for these inputs);
+* ties go to the lower index; the record encodes order and tiers;
+* PN-Mix Eq.6: ranking agrees with float64 means of pair norms when there is
+  no near tie, is invariant to token order, and a zero-Key pair ranks last;
+  the adjacent and half-split layouts pair the right channels.
+"""
+from fractions import Fraction
+
+import numpy as np
+
+import kvq_synth as synth
+from oracle import select
+from oracle.numerics import bf16_fraction, bf16_to_f64
+
+
+def tiny_inputs():
+    w = synth.WORKLOADS["tiny_mixkvq"]
+    q, k, _ = synth.prefill(w, "cpu")
+    qb = synth.bf16_bits(q)[0]                           # [g, Lq, D]
+    kb = synth.bf16_bits(k)[0, 0, : w.n_pages * 128]     # [Lk, D]
+    return w, qb, kb, synth.outlier_channels(w)[0, 0]
+
+
+def test_query_aware_tiers_on_tiny_workload():
+    w, qb, kb, oc = tiny_inputs()
+    tier, perm, rank = select.mixkvq_select(qb, kb, w.n_bf16, w.n_u4)
+    plain, attenuated = oc[4:], oc[:4]
+    assert set(rank[plain].tolist()) == {0, 1, 2, 3}
+    assert np.all(tier[plain] == select.TIER_BF16)
+    normal = np.setdiff1d(np.arange(128), oc)
+    keys = select.mixkvq_keys(qb, kb)
+    assert max(keys[c] for c in attenuated) < min(keys[c] for c in normal)
+    # error-only ablation: rank by range alone puts all eight outliers first
+    k = bf16_to_f64(kb)
+    rng = k.max(axis=0) - k.min(axis=0)
+    assert set(np.argsort(-rng, kind="stable")[:8].tolist()) == set(oc.tolist())
+    # tier sizes and channel order
+    assert (tier == select.TIER_BF16).sum() == 16 and (tier == select.TIER_U4).sum() == 32
+    assert sorted(perm.tolist()) == list(range(128))
+    assert np.all(tier[perm[:16]] == 2) and np.all(tier[perm[16:48]] == 1) and np.all(tier[perm[48:]] == 0)
+    for lo, hi in ((0, 16), (16, 48), (48, 128)):
+        assert np.all(np.diff(perm[lo:hi].astype(int)) > 0)
+
+
+def test_mixkvq_rank_matches_fraction_brute_force():
+    rng = np.random.default_rng(4)
+    g, Lq, Lk = 2, 9, 11
+    q = (rng.standard_normal((g, Lq, 128)) * rng.uniform(0.1, 3, 128)).astype(np.float32)
+    k = (rng.standard_normal((Lk, 128)) * rng.uniform(0.1, 3, 128)).astype(np.float32)
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    A = []
+    for d in range(128):
+        imp = sum(abs(bf16_fraction(int(x))) for x in qb[:, :, d].ravel()) / (g * Lq)
+        col = [bf16_fraction(int(x)) for x in kb[:, d]]
+        A.append(imp * (max(col) - min(col)) / 3)
+    expect = sorted(range(128), key=lambda d: (-A[d], d))
+    _, _, rank = select.mixkvq_select(qb, kb, 8, 24)
+    assert [int(np.nonzero(rank == r)[0][0]) for r in range(128)] == expect
+
+
+def test_ties_go_to_lower_channel_and_record():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 4, 128)).astype(np.float32)
+    k = rng.standard_normal((6, 128)).astype(np.float32)
+    q[:, :, 9] = q[:, :, 3] * 0 + 50.0
+    q[:, :, 3] = 50.0
+    k[:, 9] = k[:, 3]
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    tier, perm, rank = select.mixkvq_select(qb, kb, 1, 1)
+    assert rank[3] == 0 and rank[9] == 1
+    rec = select.mixkvq_record(tier, perm)
+    assert rec[0] == 3 and rec[1] == 9
+    assert (rec[128 + 3 // 4] >> (2 * (3 % 4))) & 3 == select.TIER_BF16
+    assert (rec[128 + 9 // 4] >> (2 * (9 % 4))) & 3 == select.TIER_U4
+
+
+def test_pnmix_ranking_float_means_and_invariance():
+    rng = np.random.default_rng(6)
+    g, Lq, Lk = 4, 40, 50
+    scale = rng.uniform(0.2, 2.0, 128)
+    q = (rng.standard_normal((g, Lq, 128)) * scale).astype(np.float32)
+    k = (rng.standard_normal((Lk, 128)) * scale[::-1]).astype(np.float32)
+    k[:, 5] = 0.0
+    k[:, 69] = 0.0            # pair 5 of the half-split layout has a zero Key
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    for layout in ("half", "adjacent"):
+        a, b = select.pair_channels(layout)
+        qf, kf = bf16_to_f64(qb), bf16_to_f64(kb)
+        qn = np.sqrt(qf[..., a] ** 2 + qf[..., b] ** 2).reshape(-1, 64).mean(axis=0)
+        kn = np.sqrt(kf[..., a] ** 2 + kf[..., b] ** 2).mean(axis=0)
+        sigma = qn * kn
+        srt = np.sort(sigma)[::-1]
+        assert srt[31] - srt[32] > 1e-9 * srt[31]          # no near tie at the cut
+        pair_hi, ch, rec = select.pnmix_select(qb, kb, 32, layout)
+        assert set(np.nonzero(pair_hi)[0].tolist()) == set(np.argsort(-sigma)[:32].tolist())
+        assert ch.sum() == 64 and np.array_equal(select.hi_channels_from_record(rec, layout), ch)
+        perm_t = rng.permutation(Lk)
+        keys1 = select.pnmix_keys(qb, kb, layout)
+        keys2 = select.pnmix_keys(qb[:, ::-1], kb[perm_t], layout)
+        assert keys1 == keys2                                  # exact, order independent
+    keys = select.pnmix_keys(qb, kb, "half")
+    assert keys[5] == 0 and min(keys) == 0
+    assert select.pair_channels("half")[1][5] == 69 and select.pair_channels("adjacent")[1][5] == 11
