@@ -1,0 +1,198 @@
+/*
+ * libkvq - mixed-precision low-bit KV cache for single-token decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI: every argument is a host pointer, a device pointer or a size.
+ * The caller owns every buffer and the HIP stream; the library never
+ * allocates, frees or synchronizes, keeps no mutable global state and is
+ * safe to call from several threads. Every call validates its arguments on
+ * the host first; on an error it returns a status and launches nothing, and
+ * no output is touched. Device pointers must be 16-byte aligned. Kernels are
+ * launched asynchronously on `stream` (a hipStream_t; NULL = default stream);
+ * a launch failure is reported as KVQ_HIP_ERROR.
+ *
+ * Sources of the operations (cited by page title and section):
+ *  - MixKVQ (ACL 2026) summary: salience score A_d = I_d * S_d, the
+ *    BF16 / UINT4 / UINT2 Key tiers ("方法细节"), GQA aggregation, lazy
+ *    update with a 128-token full-precision residual ("MixKVQ的系统级实现
+ *    细节", "通过延迟更新进行摊销调度"), Algorithm 1 (Prefill, Decoding,
+ *    KeyQuant, GroupQuant).
+ *  - PN-Mix reproduction notes: RoPE-pair score (Eq.6), min-max (Eq.2) and
+ *    1-bit midpoint correction (Eq.7), H3/L1 bit planes (Appendix G), sinks
+ *    and residual, the cache API (from_prefill / append / attention /
+ *    storage).
+ *  - QJL (AAAI 2025) summary: Definition 3.1, Algorithm 1 (sign sketch,
+ *    norm, EstimateScores), orthogonalised S.
+ *  - KIVI quantization-axes blog: per-channel Keys / per-token Values,
+ *    round-half-to-even, low-bits-first packing, one global softmax,
+ *    storage formula.
+ *
+ * Fixed geometry: head_dim D = 128; a page holds G_K = R = 128 tokens (one
+ * Key group per channel per page); Values use 32-channel groups at 2 bits.
+ * All model tensors are bfloat16; metadata scales/offsets are bfloat16
+ * (scale = the bf16 nearest to the exact (max-min)/(2^b-1), offset = the
+ * exact minimum; a constant group stores scale +0.0, codes 0); QJL norms
+ * are binary16. Decode outputs are float32.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_HEAD_DIM 128
+#define KVQ_PAGE_TOKENS 128
+#define KVQ_VALUE_GROUP 32
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_INVALID_ARG = 1,        /* null/misaligned pointer, bad size or count */
+  KVQ_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  KVQ_WORKSPACE_TOO_SMALL = 3,
+  KVQ_CAPACITY = 4,           /* page index beyond max_pages */
+  KVQ_HIP_ERROR = 5           /* a kernel launch failed */
+} kvq_status;
+
+typedef enum kvq_key_mode {
+  KVQ_KEY_MIXKVQ = 0,         /* query-aware 3-tier per-channel Keys */
+  KVQ_KEY_PNMIX = 1,          /* RoPE-pair mask, 3-bit / 1-bit midpoint planes */
+  KVQ_KEY_QJL = 2             /* 1-bit sign sketch sign(S k) plus ||k||_2 */
+} kvq_key_mode;
+
+typedef enum kvq_pair_layout {
+  KVQ_PAIR_HALF_SPLIT = 0,    /* RoPE pair i = (i, i + 64): Llama-style rotate-half */
+  KVQ_PAIR_ADJACENT = 1       /* RoPE pair i = (2i, 2i + 1) */
+} kvq_pair_layout;
+
+/* Status bits written (OR-ed) into *status_flags by kvq_flush_quantize. */
+#define KVQ_FLAG_NONFINITE 1u   /* a non-finite input was seen; that group's codes are unspecified */
+#define KVQ_FLAG_SPAN 2u        /* a group spans more than 38 binades; its codes may be off by one */
+#define KVQ_FLAG_MASK 4u        /* a PN-Mix record selects a pair count other than n_hi_pairs */
+
+/* Plain-old-data configuration, passed by pointer to every call. */
+typedef struct kvq_config {
+  int32_t abi_version;        /* must equal KVQ_ABI_VERSION */
+  int32_t key_mode;           /* kvq_key_mode */
+  int32_t batch;              /* B >= 1 */
+  int32_t n_q_heads;          /* Hq, a multiple of Hkv; Hq/Hkv in {1,2,4,8,16} */
+  int32_t n_kv_heads;         /* Hkv >= 1 */
+  int32_t head_dim;           /* must be 128 */
+  int32_t max_pages;          /* page slots per (batch, kv head) in the arena */
+  int32_t n_bf16;             /* MixKVQ: channels kept in BF16 (tier 1) */
+  int32_t n_u4;               /* MixKVQ: channels at UINT4 (tier 2); the rest UINT2 */
+  int32_t pair_layout;        /* PN-Mix: kvq_pair_layout */
+  int32_t n_hi_pairs;         /* PN-Mix: high-precision pairs, floor(r*D/2) (32 at r=0.5) */
+  int32_t qjl_m;              /* QJL: sketch rows m, a multiple of 64, at most 512 */
+  int32_t reserved[4];        /* must be zero */
+} kvq_config;
+
+/* Persistent cache bytes of one layer for all (batch, kv head) pairs, by
+ * region; logical sizes (codes at their bit width, 2-byte metadata), as in
+ * the KIVI blog storage formula and the PN-Mix storage() accounting. */
+typedef struct kvq_storage_breakdown {
+  uint64_t key_full;          /* BF16-tier Key channels (MixKVQ) */
+  uint64_t key_codes;         /* packed Key codes / sign bits */
+  uint64_t key_meta;          /* Key scales+offsets (MixKVQ, PN-Mix) or norms (QJL) */
+  uint64_t value_codes;
+  uint64_t value_meta;
+  uint64_t residual;          /* BF16 residual tokens, K and V */
+  uint64_t sink;              /* BF16 attention-sink tokens, K and V */
+  uint64_t selection;         /* selection records (channel order + tiers, or pair mask) */
+  uint64_t total;
+  double key_bits_per_element;/* Key bits per element over quantized + sink tokens */
+} kvq_storage_breakdown;
+
+/* ABI version of the loaded library. */
+int32_t kvq_abi_version(void);
+
+/* Static, never-freed description of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+/* Byte stride of one page in the arena (a multiple of 256) for this
+ * configuration. The arena is [batch][n_kv_heads][max_pages] pages. */
+kvq_status kvq_page_bytes(const kvq_config* cfg, size_t* bytes);
+
+/* Bytes of the selection record of one (batch, kv head); the mask buffer of
+ * kvq_select_channels holds batch*n_kv_heads records back to back.
+ * MixKVQ: 160 bytes = channel order u8[128] (BF16 tier, then UINT4, then
+ * UINT2, each ascending) + 2-bit tier codes (0 UINT2, 1 UINT4, 2 BF16, low
+ * bits first). PN-Mix: 8 bytes, bit i = RoPE pair i kept at 3 bits.
+ * QJL: 0 (S is an input). */
+kvq_status kvq_mask_bytes(const kvq_config* cfg, size_t* bytes);
+
+/* Device workspace kvq_decode_attention needs for n_pages pages. */
+kvq_status kvq_workspace_bytes(const kvq_config* cfg, int32_t n_pages, size_t* bytes);
+
+/* Host-only and pure: persistent bytes of a cache holding n_quant_tokens
+ * quantized tokens (a multiple of 128), n_resid residual and n_sink sink
+ * tokens per (batch, kv head). KIVI blog section 7; PN-Mix storage(). */
+kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant_tokens, int32_t n_resid,
+                             int32_t n_sink, kvq_storage_breakdown* out);
+
+/* Precision selection at prefill, once per (batch, kv head).
+ *  MixKVQ ("方法细节", "MixKVQ的系统级实现细节"): for every channel d,
+ *    SQ_d = sum of |Q| over the l_q prefill queries of all query heads that
+ *    share the kv head, range_d = max - min of K over the l_k Key tokens to be
+ *    quantized; channels ranked by SQ_d * range_d (ties: lower d first);
+ *    the n_bf16 best are BF16, the next n_u4 UINT4, the rest UINT2.
+ *  PN-Mix (Eq.6): pairs ranked by sum_t ||q pair|| * sum_s ||k pair||
+ *    (query sum over the whole GQA group), top n_hi_pairs kept at 3 bits.
+ *  Both rank on exact integer sums of the per-element values rounded to a
+ *  2^-64 grid, so the result does not depend on summation order.
+ * q_pre: device bf16, element (b, h, t, d) at q_pre[((b*Hq + h)*q_stride + t)*128 + d]
+ * k_pre: device bf16, element (b, h, t, d) at k_pre[((b*Hkv + h)*k_stride + t)*128 + d]
+ * mask_out: device, batch*n_kv_heads records of kvq_mask_bytes bytes.
+ * Preconditions: finite inputs with |q|, |k| < 2^30.
+ * QJL returns KVQ_UNSUPPORTED (S is generated by the caller). */
+kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t l_q, int64_t q_stride,
+                               const void* k_pre, int64_t l_k, int64_t k_stride, void* mask_out,
+                               void* stream);
+
+/* Quantize and pack n_pages full 128-token segments into pages
+ * first_page .. first_page + n_pages - 1 of every (batch, kv head)
+ * (MixKVQ Algorithm 1 KeyQuant/GroupQuant at a buffer flush; PN-Mix
+ * append; QJL Algorithm 1 steps 2-3). Keys: per channel over the 128
+ * tokens (tier per the MixKVQ record; 3-bit or 1-bit-midpoint per the PN-Mix
+ * mask; sign sketch + binary16 norm for QJL). Values: per token, 4 groups of
+ * 32 channels, 2 bits.
+ * k_src/v_src: device bf16, token t of page p of (b, h) at
+ *   src[((b*Hkv + h)*src_stride + p*128 + t)*128 + d].
+ * mask: the records of kvq_select_channels (ignored for QJL).
+ * qjl_s: device bf16 [qjl_m][128] (QJL only, else may be NULL).
+ * page_arena: device, [batch][n_kv_heads][max_pages] pages of kvq_page_bytes.
+ * status_flags: device uint32 (not NULL) the kernels OR KVQ_FLAG_* bits into.
+ * Returns KVQ_CAPACITY if first_page + n_pages > max_pages. */
+kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src,
+                              int64_t src_stride, int32_t n_pages, const void* mask,
+                              const void* qjl_s, void* page_arena, int32_t first_page,
+                              uint32_t* status_flags, void* stream);
+
+/* Single-token decode attention over [sinks | pages 0..n_pages-1 | residual]
+ * with one global softmax (KIVI blog section 6; MixKVQ Algorithm 1
+ * Decoding; PN-Mix cache.attention; QJL EstimateScores + softmax):
+ *   out[b, h, :] = sum_t softmax_t(logit_t) * v^_t,
+ *   logit_t = softmax_scale * q . k^_t for BF16 and dequantized keys,
+ *   logit_t = softmax_scale * sqrt(pi/2)/m * nu_t * <S q, sign(S k_t)> for QJL pages.
+ * q: device bf16 [batch][n_q_heads][128]; query head h uses kv head h / (Hq/Hkv).
+ * sink_k/sink_v: device bf16 [batch][n_kv_heads][n_sink][128] (n_sink <= 128; may be NULL if 0).
+ * resid_k/resid_v: device bf16 [batch][n_kv_heads][resid_stride][128], first
+ *   n_resid tokens visible (0 <= n_resid <= 128; may be NULL if 0).
+ * out: device float32 [batch][n_q_heads][128].
+ * workspace: device, at least kvq_workspace_bytes(cfg, n_pages) bytes. */
+kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena,
+                                int32_t n_pages, const void* mask, const void* qjl_s,
+                                const void* sink_k, const void* sink_v, int32_t n_sink,
+                                const void* resid_k, const void* resid_v, int32_t n_resid,
+                                int32_t resid_stride, float softmax_scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

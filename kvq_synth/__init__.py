@@ -171,8 +171,8 @@ def qjl_matrix(w: Workload, device="cpu") -> torch.Tensor:
         qmat = qmat * np.sign(np.diag(rmat))[None, :]
         lengths = np.linalg.norm(gen.standard_normal((HEAD_DIM, HEAD_DIM)), axis=1)
         blocks.append(qmat.T * lengths[:, None])
-    s = np.concatenate(blocks, axis=0)[:m]
-    return torch.from_numpy(s.astype(np.float32)).to(torch.bfloat16).to(device)
+    s = np.ascontiguousarray(np.concatenate(blocks, axis=0)[:m], dtype=np.float32)
+    return torch.from_numpy(s).to(torch.bfloat16).contiguous().to(device)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -1,0 +1,266 @@
+// libkvq C ABI: host-side validation, geometry queries, storage accounting
+// and kernel dispatch. Every entry point checks its arguments before it
+// launches anything; on error nothing is launched and no output is touched.
+#include <math.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static kvq_status check_config(const kvq_config* c) {
+  if (!c) return KVQ_INVALID_ARG;
+  if (c->abi_version != KVQ_ABI_VERSION) return KVQ_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (c->reserved[i] != 0) return KVQ_INVALID_ARG;
+  if (c->head_dim != D) return c->head_dim > 0 ? KVQ_UNSUPPORTED : KVQ_INVALID_ARG;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_pages < 1) return KVQ_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads) return KVQ_INVALID_ARG;
+  const int g = c->n_q_heads / c->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return KVQ_UNSUPPORTED;
+  switch (c->key_mode) {
+    case KVQ_KEY_MIXKVQ:
+      if (c->n_bf16 < 0 || c->n_u4 < 0 || c->n_bf16 + c->n_u4 > D) return KVQ_INVALID_ARG;
+      break;
+    case KVQ_KEY_PNMIX:
+      if (c->pair_layout != KVQ_PAIR_HALF_SPLIT && c->pair_layout != KVQ_PAIR_ADJACENT) return KVQ_INVALID_ARG;
+      if (c->n_hi_pairs < 0 || c->n_hi_pairs > D / 2) return KVQ_INVALID_ARG;
+      break;
+    case KVQ_KEY_QJL:
+      if (c->qjl_m < 64 || c->qjl_m % 64) return KVQ_INVALID_ARG;
+      if (c->qjl_m > 256) return KVQ_UNSUPPORTED;
+      break;
+    default:
+      return KVQ_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+static size_t page_stride(const kvq_config* c) {
+  if (c->key_mode == KVQ_KEY_MIXKVQ) return (size_t)mix_geo(c->n_bf16, c->n_u4).stride;
+  if (c->key_mode == KVQ_KEY_PNMIX) return (size_t)pn_geo(2 * c->n_hi_pairs).stride;
+  return (size_t)qjl_geo(c->qjl_m).stride;
+}
+
+static size_t record_bytes(const kvq_config* c) {
+  if (c->key_mode == KVQ_KEY_MIXKVQ) return MIX_RECORD;
+  if (c->key_mode == KVQ_KEY_PNMIX) return PN_RECORD;
+  return 0;
+}
+
+static int n_page_splits(const kvq_config* c, int n_pages) {
+  if (n_pages <= 0) return 0;
+  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads);
+  return (n_pages + pps - 1) / pps;
+}
+
+static size_t workspace_for(const kvq_config* c, int n_pages) {
+  size_t splits = (size_t)n_page_splits(c, n_pages) + 1;
+  size_t rows = (size_t)c->batch * c->n_q_heads;
+  size_t bytes = splits * rows * 130 * sizeof(float);
+  if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)c->qjl_m * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_INVALID_ARG: return "invalid argument";
+    case KVQ_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KVQ_CAPACITY: return "page index beyond max_pages";
+    case KVQ_HIP_ERROR: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_page_bytes(const kvq_config* cfg, size_t* bytes) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return KVQ_INVALID_ARG;
+  *bytes = page_stride(cfg);
+  return KVQ_OK;
+}
+
+kvq_status kvq_mask_bytes(const kvq_config* cfg, size_t* bytes) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return KVQ_INVALID_ARG;
+  *bytes = record_bytes(cfg);
+  return KVQ_OK;
+}
+
+kvq_status kvq_workspace_bytes(const kvq_config* cfg, int32_t n_pages, size_t* bytes) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!bytes || n_pages < 0 || n_pages > cfg->max_pages) return KVQ_INVALID_ARG;
+  *bytes = workspace_for(cfg, n_pages);
+  return KVQ_OK;
+}
+
+// KIVI blog section 7 / PN-Mix storage(): logical bytes, 2-byte metadata.
+kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant, int32_t n_resid, int32_t n_sink,
+                             kvq_storage_breakdown* out) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out || n_quant < 0 || n_quant % PAGE || n_resid < 0 || n_sink < 0) return KVQ_INVALID_ARG;
+  const uint64_t H = (uint64_t)cfg->batch * cfg->n_kv_heads;
+  const uint64_t pages = (uint64_t)(n_quant / PAGE);
+  const uint64_t T = (uint64_t)n_quant;
+  kvq_storage_breakdown o;
+  memset(&o, 0, sizeof(o));
+  o.value_codes = H * T * D * 2 / 8;
+  o.value_meta = H * T * (D / GV) * 2 * 2;
+  o.residual = H * 2 * (uint64_t)n_resid * D * 2;
+  o.sink = H * 2 * (uint64_t)n_sink * D * 2;
+  double key_bits_quant = 0.0;   // Key bits per element of a quantized token
+  if (cfg->key_mode == KVQ_KEY_MIXKVQ) {
+    const int n2 = D - cfg->n_bf16 - cfg->n_u4;
+    o.key_full = H * T * cfg->n_bf16 * 2;
+    o.key_codes = H * T * (4 * (uint64_t)cfg->n_u4 + 2 * (uint64_t)n2) / 8;
+    o.key_meta = H * pages * (uint64_t)(cfg->n_u4 + n2) * 2 * 2;
+    o.selection = H * (D + D / 4);
+    key_bits_quant = (16.0 * cfg->n_bf16 + 4.0 * cfg->n_u4 + 2.0 * n2 + 32.0 * (cfg->n_u4 + n2) / PAGE) / D;
+  } else if (cfg->key_mode == KVQ_KEY_PNMIX) {
+    const uint64_t n_hi = 2 * (uint64_t)cfg->n_hi_pairs;
+    o.key_codes = H * (T * D + T * n_hi * 2) / 8;
+    o.key_meta = H * pages * D * 2 * 2;
+    o.selection = H * ((D / 2 + 7) / 8);
+    key_bits_quant = (D + 2.0 * n_hi + 32.0 * D / PAGE) / D;
+  } else {
+    o.key_codes = H * T * (uint64_t)cfg->qjl_m / 8;
+    o.key_meta = H * T * 2;
+    o.selection = 0;
+    key_bits_quant = ((double)cfg->qjl_m + 16.0) / D;
+  }
+  o.total = o.key_full + o.key_codes + o.key_meta + o.value_codes + o.value_meta + o.residual + o.sink + o.selection;
+  const double toks = (double)n_quant + n_sink;
+  o.key_bits_per_element = toks > 0 ? (key_bits_quant * n_quant + 16.0 * n_sink) / toks : 0.0;
+  *out = o;
+  return KVQ_OK;
+}
+
+kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t l_q, int64_t q_stride,
+                               const void* k_pre, int64_t l_k, int64_t k_stride, void* mask_out, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (cfg->key_mode == KVQ_KEY_QJL) return KVQ_UNSUPPORTED;
+  if (!q_pre || !k_pre || !mask_out) return KVQ_INVALID_ARG;
+  if (!aligned16(q_pre) || !aligned16(k_pre)) return KVQ_INVALID_ARG;
+  if (l_q < 1 || l_k < 1 || q_stride < l_q || k_stride < l_k) return KVQ_INVALID_ARG;
+  SelectArgs a;
+  a.q = (const uint16_t*)q_pre;
+  a.k = (const uint16_t*)k_pre;
+  a.l_q = l_q;
+  a.q_stride = q_stride;
+  a.l_k = l_k;
+  a.k_stride = k_stride;
+  a.n_q_heads = cfg->n_q_heads;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n16 = cfg->n_bf16;
+  a.n4 = cfg->n_u4;
+  a.n_hi_pairs = cfg->n_hi_pairs;
+  a.pair_layout = cfg->pair_layout;
+  a.out = (uint8_t*)mask_out;
+  return launch_select(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
+                              int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
+                              int32_t first_page, uint32_t* status_flags, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!k_src || !v_src || !page_arena || !status_flags) return KVQ_INVALID_ARG;
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(page_arena)) return KVQ_INVALID_ARG;
+  if (n_pages < 0 || first_page < 0 || src_stride < (int64_t)n_pages * PAGE) return KVQ_INVALID_ARG;
+  if ((int64_t)first_page + n_pages > cfg->max_pages) return KVQ_CAPACITY;
+  if (cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
+  if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
+  if (n_pages == 0) return KVQ_OK;
+  FlushArgs a;
+  a.k_src = (const uint16_t*)k_src;
+  a.v_src = (const uint16_t*)v_src;
+  a.src_stride = src_stride;
+  a.mask = (const uint8_t*)mask;
+  a.qjl_s = (const uint16_t*)qjl_s;
+  a.arena = (uint8_t*)page_arena;
+  a.page_stride = (int64_t)page_stride(cfg);
+  a.max_pages = cfg->max_pages;
+  a.first_page = first_page;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n16 = cfg->n_bf16;
+  a.n4 = cfg->n_u4;
+  a.n_hi = 2 * cfg->n_hi_pairs;
+  a.pair_layout = cfg->pair_layout;
+  a.qjl_m = cfg->qjl_m;
+  a.flags = status_flags;
+  return launch_flush(cfg->key_mode, a, n_pages, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK
+                                                                                                : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena, int32_t n_pages,
+                                const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
+                                int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
+                                int32_t resid_stride, float softmax_scale, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  const int g = cfg->n_q_heads / cfg->n_kv_heads;
+  if (g > 8) return KVQ_UNSUPPORTED;
+  if (!q || !out || !workspace || !aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_INVALID_ARG;
+  if (n_pages < 0 || n_pages > cfg->max_pages) return KVQ_INVALID_ARG;
+  if (n_pages > 0 && (!page_arena || !aligned16(page_arena))) return KVQ_INVALID_ARG;
+  if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
+  if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
+  if (n_sink < 0 || n_sink > PAGE || n_resid < 0 || n_resid > PAGE) return KVQ_INVALID_ARG;
+  if (n_sink > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v))) return KVQ_INVALID_ARG;
+  if (n_resid > 0 && (!resid_k || !resid_v || !aligned16(resid_k) || !aligned16(resid_v) || resid_stride < n_resid))
+    return KVQ_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return KVQ_INVALID_ARG;
+  if (workspace_bytes < workspace_for(cfg, n_pages)) return KVQ_WORKSPACE_TOO_SMALL;
+  DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.arena = (const uint8_t*)page_arena;
+  a.page_stride = (int64_t)page_stride(cfg);
+  a.max_pages = cfg->max_pages;
+  a.n_pages = n_pages;
+  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
+  a.n_page_splits = n_page_splits(cfg, n_pages);
+  a.mask = (const uint8_t*)mask;
+  const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
+  const size_t part_bytes = ((size_t)a.n_page_splits + 1) * rows * 130 * sizeof(float);
+  a.partial = (float*)workspace;
+  a.sq = (const float*)((uint8_t*)workspace + part_bytes);
+  a.sink_k = (const uint16_t*)sink_k;
+  a.sink_v = (const uint16_t*)sink_v;
+  a.n_sink = n_sink;
+  a.resid_k = (const uint16_t*)resid_k;
+  a.resid_v = (const uint16_t*)resid_v;
+  a.n_resid = n_resid;
+  a.resid_stride = resid_stride;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.qjl_coef = cfg->key_mode == KVQ_KEY_QJL ? (float)(sqrt(M_PI / 2.0) / cfg->qjl_m) : 0.f;
+  a.batch = cfg->batch;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n_q_heads = cfg->n_q_heads;
+  a.n16 = cfg->n_bf16;
+  a.n4 = cfg->n_u4;
+  a.n_hi = 2 * cfg->n_hi_pairs;
+  a.pair_layout = cfg->pair_layout;
+  a.qjl_m = cfg->qjl_m;
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, out, (hipStream_t)stream) == hipSuccess
+             ? KVQ_OK
+             : KVQ_HIP_ERROR;
+}
+
+}  // extern "C"

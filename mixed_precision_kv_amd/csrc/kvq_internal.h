@@ -1,0 +1,205 @@
+// Internal definitions shared by the libkvq translation units: page geometry,
+// bf16/f16 helpers and the exact-rounding primitives the flush kernels use.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;            // head dimension
+constexpr int PAGE = 128;         // tokens per page (Key group along time)
+constexpr int GV = 32;            // value channels per group
+constexpr int V_CODE_BYTES = 4096;
+constexpr int V_META_BYTES = 2048;
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// ---------------------------------------------------------------- geometry
+// MixKVQ page: [K_BF16 | K_CODES | K_META | V_CODES | V_META]
+//  K_BF16 : n16 channel rows of 256 B, token 16*i + r at byte 16*r + 2*i
+//  K_CODES: fragments of 8 slots x 128 tokens x 2 bits (256 B); slots are
+//           the low/high halves of every UINT4 code (padded to a multiple of
+//           8 slots) followed by the UINT2 codes
+//  K_META : per fragment 8 bf16 slot scales then 8 bf16 slot offsets
+struct MixGeo {
+  int n16, n4, n2, s4, n_slots, F, off_codes, off_meta, off_v, used, stride;
+};
+__host__ __device__ inline MixGeo mix_geo(int n16, int n4) {
+  MixGeo g;
+  g.n16 = n16;
+  g.n4 = n4;
+  g.n2 = D - n16 - n4;
+  g.s4 = round_up(2 * n4, 8);
+  g.n_slots = g.s4 + g.n2;
+  g.F = (g.n_slots + 7) / 8;
+  g.off_codes = 256 * n16;
+  g.off_meta = g.off_codes + 256 * g.F;
+  g.off_v = g.off_meta + 32 * g.F;
+  g.used = g.off_v + V_CODE_BYTES + V_META_BYTES;
+  g.stride = round_up(g.used, 256);
+  return g;
+}
+
+// PN-Mix page: [LSB plane (2048) | UP plane | K_META (512) | V_CODES | V_META]
+struct PnGeo {
+  int n_hi, n_up_frag, off_up, off_meta, off_v, used, stride;
+};
+__host__ __device__ inline PnGeo pn_geo(int n_hi) {
+  PnGeo g;
+  g.n_hi = n_hi;
+  g.n_up_frag = (n_hi + 7) / 8;
+  g.off_up = 2048;
+  g.off_meta = g.off_up + 256 * g.n_up_frag;
+  g.off_v = g.off_meta + 512;
+  g.used = g.off_v + V_CODE_BYTES + V_META_BYTES;
+  g.stride = round_up(g.used, 256);
+  return g;
+}
+
+// QJL page: [sign bits (16*m) | norms (256) | V_CODES | V_META]
+struct QjlGeo {
+  int m, off_norm, off_v, used, stride;
+};
+__host__ __device__ inline QjlGeo qjl_geo(int m) {
+  QjlGeo g;
+  g.m = m;
+  g.off_norm = 16 * m;
+  g.off_v = g.off_norm + 256;
+  g.used = g.off_v + V_CODE_BYTES + V_META_BYTES;
+  g.stride = round_up(g.used, 256);
+  return g;
+}
+
+constexpr int MIX_RECORD = 160;   // channel order u8[128] + 2-bit tiers [32]
+constexpr int PN_RECORD = 8;      // 64 pair bits
+
+// ---------------------------------------------------------------- number formats
+__host__ __device__ inline float bf16_to_f32(uint16_t b) {
+  union { uint32_t u; float f; } c;
+  c.u = (uint32_t)b << 16;
+  return c.f;
+}
+__host__ __device__ inline double bf16_to_f64(uint16_t b) { return (double)bf16_to_f32(b); }
+
+// Correctly rounded (ties-to-even) bf16 of a finite double; zero -> +0.0.
+__host__ __device__ inline uint16_t f64_to_bf16_rne(double v) {
+  if (v == 0.0) return 0;
+  union { double d; uint64_t u; } c;
+  c.d = v;
+  uint64_t u = c.u;
+  uint16_t sign = (uint16_t)((u >> 48) & 0x8000);
+  int e = (int)((u >> 52) & 0x7FF) - 1023;
+  uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);   // 53 bits, value = sig * 2^(e-52)
+  int q_exp;          // exponent of the result quantum
+  if (e >= -126) q_exp = e - 7;
+  else q_exp = -133;
+  int shift = q_exp - (e - 52);                           // bits to drop from sig
+  uint64_t q;
+  if (shift >= 64) {
+    q = 0;
+  } else {
+    q = sig >> shift;
+    uint64_t rem = sig & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) q += 1;
+  }
+  if (e >= -126) {
+    int ex = e;
+    if (q == 256) { q = 128; ex += 1; }
+    return (uint16_t)(sign | ((uint16_t)(ex + 127) << 7) | (uint16_t)(q - 128));
+  }
+  return (uint16_t)(sign | (uint16_t)q);   // q == 128 encodes the smallest normal
+}
+
+// binary16 bit pattern of the correctly rounded sqrt(s) for an exact s >= 0
+// given in double. Midpoints are decided on their squares (exact in double).
+__device__ inline uint16_t sqrt_to_f16_rne(double s) {
+  if (s <= 0.0) return 0;
+  double r = sqrt(s);
+  _Float16 h = (_Float16)(float)r;   // candidate, fixed below
+  uint16_t c;
+  __builtin_memcpy(&c, &h, 2);
+  for (int it = 0; it < 4; ++it) {
+    _Float16 hv, hu, hd;
+    uint16_t cu = (uint16_t)(c + 1), cd = (uint16_t)(c - 1);
+    __builtin_memcpy(&hv, &c, 2);
+    __builtin_memcpy(&hu, &cu, 2);
+    __builtin_memcpy(&hd, &cd, 2);
+    double v = (double)(float)hv;
+    if (c < 0x7BFF) {
+      double mid = 0.5 * (v + (double)(float)hu);
+      double m2 = mid * mid;                 // 13-bit mid -> exact square
+      if (s > m2 || (s == m2 && (c & 1))) { c = cu; continue; }
+    }
+    if (c > 0) {
+      double mid = 0.5 * (v + (double)(float)hd);
+      double m2 = mid * mid;
+      if (s < m2 || (s == m2 && (c & 1))) { c = cd; continue; }
+    }
+    break;
+  }
+  return c;
+}
+
+__host__ __device__ inline int bf16_exp_field(uint16_t b) { return (b >> 7) & 0xFF; }
+
+// ---------------------------------------------------------------- kernel argument blocks
+// Flush (kvq_flush.hip): source rows, selection records, arena geometry.
+struct FlushArgs {
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t src_stride;
+  const uint8_t* mask;
+  const uint16_t* qjl_s;
+  uint8_t* arena;
+  int64_t page_stride;
+  int max_pages;
+  int first_page;
+  int n_kv_heads;
+  int n16, n4;
+  int n_hi;
+  int pair_layout;
+  int qjl_m;
+  unsigned* flags;
+};
+struct SelectArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t l_q, q_stride, l_k, k_stride;
+  int n_q_heads, n_kv_heads;
+  int n16, n4;
+  int n_hi_pairs, pair_layout;
+  uint8_t* out;
+};
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* arena;
+  int64_t page_stride;
+  int max_pages, n_pages, pps, n_page_splits;
+  const uint8_t* mask;
+  const float* sq;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  int n_sink;
+  const uint16_t* resid_k;
+  const uint16_t* resid_v;
+  int n_resid, resid_stride;
+  float scale_log2;
+  float qjl_coef;
+  float* partial;
+  int batch, n_kv_heads, n_q_heads;
+  int n16, n4;
+  int n_hi, pair_layout;
+  int qjl_m;
+};
+
+hipError_t launch_flush(int key_mode, const FlushArgs& a, int n_pages, int batch, hipStream_t stream);
+hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, float* out, hipStream_t s);
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads);
+
+}  // namespace kvq

@@ -1,0 +1,218 @@
+// Precision selection at prefill.
+//
+// MixKVQ ("方法细节" salience A_d = I_d * S_d; "MixKVQ的系统级实现细节": the
+// importance aggregates every query head sharing the KV head): channels are
+// ranked by SQ_d * range_d, where SQ_d = sum |Q_{t,d}| over the group's
+// prefill queries and range_d = max - min of the Key tokens to be quantized;
+// the positive factors 1/L_q and 1/(2^B - 1) do not change the order.
+// PN-Mix (Eq.6): RoPE pairs ranked by sum ||q pair|| * sum ||k pair||.
+//
+// Sums are exact: every |q| (or pair norm, the correctly rounded double
+// sqrt(a^2 + b^2)) is rounded to the grid 2^-64 and added as a 128-bit
+// integer, so the result does not depend on how the work is split. One
+// workgroup of 1024 threads handles one (batch, kv head): 64 column lanes x
+// 16 row lanes stream the rows with coalesced loads.
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef unsigned __int128 u128;
+
+// round_half_even(|bf16| * 2^64) as an integer (|x| < 2^63 assumed)
+__device__ inline u128 psi_bf16(uint16_t bits) {
+  int e = (bits >> 7) & 0xFF;
+  uint32_t sig = (bits & 0x7F) | (e ? 0x80u : 0u);
+  int ex = (e ? e : 1) - 134;          // value = sig * 2^ex
+  int s = ex + 64;
+  if (sig == 0) return 0;
+  if (s >= 0) return (u128)sig << s;
+  int rs = -s;
+  if (rs > 9) return 0;
+  uint32_t q = sig >> rs;
+  uint32_t rem = sig & ((1u << rs) - 1);
+  uint32_t half = 1u << (rs - 1);
+  if (rem > half || (rem == half && (q & 1))) q += 1;
+  return (u128)q;
+}
+
+// round_half_even(y * 2^64) for a finite double y >= 0 (y < 2^63)
+__device__ inline u128 psi_f64(double y) {
+  if (y <= 0.0) return 0;
+  double z = y * 18446744073709551616.0;     // exact scaling by 2^64
+  if (z < 9007199254740992.0) return (u128)(uint64_t)rint(z);
+  union { double d; uint64_t u; } c;
+  c.d = z;
+  int e = (int)((c.u >> 52) & 0x7FF) - 1023;
+  uint64_t sig = (c.u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  return (u128)sig << (e - 52);
+}
+
+// 128 x 128 -> 256-bit product as four 64-bit limbs (little end first)
+__device__ inline void mul128(u128 a, u128 b, uint64_t out[4]) {
+  uint64_t a0 = (uint64_t)a, a1 = (uint64_t)(a >> 64), b0 = (uint64_t)b, b1 = (uint64_t)(b >> 64);
+  u128 p00 = (u128)a0 * b0, p01 = (u128)a0 * b1, p10 = (u128)a1 * b0, p11 = (u128)a1 * b1;
+  u128 mid = (p00 >> 64) + (uint64_t)p01 + (uint64_t)p10;
+  out[0] = (uint64_t)p00;
+  out[1] = (uint64_t)mid;
+  u128 hi = (mid >> 64) + (p01 >> 64) + (p10 >> 64) + p11;
+  out[2] = (uint64_t)hi;
+  out[3] = (uint64_t)(hi >> 64);
+}
+__device__ inline int cmp256(const uint64_t x[4], const uint64_t y[4]) {
+  for (int i = 3; i >= 0; --i) {
+    if (x[i] != y[i]) return x[i] > y[i] ? 1 : -1;
+  }
+  return 0;
+}
+
+
+// ------------------------------------------------------------------ MixKVQ
+__global__ __launch_bounds__(1024) void select_mixkvq_kernel(SelectArgs A) {
+  __shared__ u128 part[16][D];                 // 32 KB
+  __shared__ float kmin[16][D], kmax[16][D];
+  __shared__ double key_hi[D], key_lo[D];
+  __shared__ int rank_s[D];
+  __shared__ uint8_t tier_s[D];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int g = A.n_q_heads / A.n_kv_heads;
+  const int j = threadIdx.x & 63, rl = threadIdx.x >> 6;   // channel pair, row lane
+
+  u128 s0 = 0, s1 = 0;
+  const int64_t rows = (int64_t)g * A.l_q;
+  for (int64_t R = rl; R < rows; R += 16) {
+    int hh = (int)(R / A.l_q);
+    int64_t t = R - (int64_t)hh * A.l_q;
+    const uint16_t* row = A.q + (((int64_t)b * A.n_q_heads + (int64_t)kvh * g + hh) * A.q_stride + t) * D;
+    uint32_t w = reinterpret_cast<const uint32_t*>(row)[j];
+    s0 += psi_bf16((uint16_t)(w & 0x7FFF));
+    s1 += psi_bf16((uint16_t)((w >> 16) & 0x7FFF));
+  }
+  part[rl][2 * j] = s0;
+  part[rl][2 * j + 1] = s1;
+
+  float mn0 = INFINITY, mn1 = INFINITY, mx0 = -INFINITY, mx1 = -INFINITY;
+  for (int64_t t = rl; t < A.l_k; t += 16) {
+    const uint16_t* row = A.k + (((int64_t)b * A.n_kv_heads + kvh) * A.k_stride + t) * D;
+    uint32_t w = reinterpret_cast<const uint32_t*>(row)[j];
+    float v0 = bf16_to_f32((uint16_t)w), v1 = bf16_to_f32((uint16_t)(w >> 16));
+    mn0 = fminf(mn0, v0); mx0 = fmaxf(mx0, v0);
+    mn1 = fminf(mn1, v1); mx1 = fmaxf(mx1, v1);
+  }
+  kmin[rl][2 * j] = mn0; kmin[rl][2 * j + 1] = mn1;
+  kmax[rl][2 * j] = mx0; kmax[rl][2 * j + 1] = mx1;
+  __syncthreads();
+
+  if (threadIdx.x < D) {
+    int d = threadIdx.x;
+    u128 sq = 0;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      sq += part[r][d];
+      mn = fminf(mn, kmin[r][d]);
+      mx = fmaxf(mx, kmax[r][d]);
+    }
+    double range = (A.l_k > 0) ? (double)mx - (double)mn : 0.0;
+    // double-double key: (hi + lo) * range with hi + lo == sq exactly
+    double hi = (double)sq;
+    double lo = (double)(__int128)(sq - (u128)hi);
+    double p = hi * range;
+    double e = fma(hi, range, -p) + lo * range;
+    double kh = p + e;                          // renormalise
+    double kl = e - (kh - p);
+    key_hi[d] = kh;
+    key_lo[d] = kl;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    int d = threadIdx.x, r = 0;
+    for (int o = 0; o < D; ++o) {
+      bool better = key_hi[o] > key_hi[d] || (key_hi[o] == key_hi[d] && key_lo[o] > key_lo[d]);
+      bool same = key_hi[o] == key_hi[d] && key_lo[o] == key_lo[d];
+      if (better || (same && o < d)) ++r;
+    }
+    rank_s[d] = r;
+    tier_s[d] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
+  }
+  __syncthreads();
+  uint8_t* rec = A.out + ((int64_t)b * A.n_kv_heads + kvh) * MIX_RECORD;
+  if (threadIdx.x < D) {
+    int d = threadIdx.x, t = tier_s[d];
+    int base = t == 2 ? 0 : (t == 1 ? A.n16 : A.n16 + A.n4);
+    int pos = base;
+    for (int o = 0; o < d; ++o) pos += tier_s[o] == t;
+    rec[pos] = (uint8_t)d;
+  } else if (threadIdx.x < D + 32) {
+    int q = threadIdx.x - D;
+    rec[D + q] = (uint8_t)(tier_s[4 * q] | (tier_s[4 * q + 1] << 2) | (tier_s[4 * q + 2] << 4) | (tier_s[4 * q + 3] << 6));
+  }
+}
+
+// ------------------------------------------------------------------ PN-Mix
+__global__ __launch_bounds__(1024) void select_pnmix_kernel(SelectArgs A) {
+  __shared__ u128 qpart[16][64], kpart[16][64];
+  __shared__ u128 qn[64], kn[64];
+  __shared__ uint8_t hi_s[64];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int g = A.n_q_heads / A.n_kv_heads;
+  const int i = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int d0 = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? i : 2 * i;
+  const int d1 = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? i + 64 : 2 * i + 1;
+
+  u128 sq = 0;
+  const int64_t rows = (int64_t)g * A.l_q;
+  for (int64_t R = rl; R < rows; R += 16) {
+    int hh = (int)(R / A.l_q);
+    int64_t t = R - (int64_t)hh * A.l_q;
+    const uint16_t* row = A.q + (((int64_t)b * A.n_q_heads + (int64_t)kvh * g + hh) * A.q_stride + t) * D;
+    double x = bf16_to_f64(row[d0]), y = bf16_to_f64(row[d1]);
+    sq += psi_f64(sqrt(fma(x, x, y * y)));
+  }
+  u128 sk = 0;
+  for (int64_t t = rl; t < A.l_k; t += 16) {
+    const uint16_t* row = A.k + (((int64_t)b * A.n_kv_heads + kvh) * A.k_stride + t) * D;
+    double x = bf16_to_f64(row[d0]), y = bf16_to_f64(row[d1]);
+    sk += psi_f64(sqrt(fma(x, x, y * y)));
+  }
+  qpart[rl][i] = sq;
+  kpart[rl][i] = sk;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    u128 a = 0, c = 0;
+    for (int r = 0; r < 16; ++r) {
+      a += qpart[r][threadIdx.x];
+      c += kpart[r][threadIdx.x];
+    }
+    qn[threadIdx.x] = a;
+    kn[threadIdx.x] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int me = threadIdx.x, r = 0;
+    uint64_t kme[4];
+    mul128(qn[me], kn[me], kme);
+    for (int o = 0; o < 64; ++o) {
+      uint64_t ko[4];
+      mul128(qn[o], kn[o], ko);
+      int c = cmp256(ko, kme);
+      if (c > 0 || (c == 0 && o < me)) ++r;
+    }
+    hi_s[me] = r < A.n_hi_pairs;
+  }
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    uint8_t byte = 0;
+    for (int k = 0; k < 8; ++k) byte |= hi_s[8 * threadIdx.x + k] << k;
+    A.out[((int64_t)b * A.n_kv_heads + kvh) * PN_RECORD + threadIdx.x] = byte;
+  }
+}
+
+hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream) {
+  dim3 grid(a.n_kv_heads, batch);
+  if (key_mode == KVQ_KEY_MIXKVQ)
+    hipLaunchKernelGGL(select_mixkvq_kernel, grid, dim3(1024), 0, stream, a);
+  else
+    hipLaunchKernelGGL(select_pnmix_kernel, grid, dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

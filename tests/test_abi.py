@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every entry point include/kvq.h declares,
+and its host-only calls (geometry, storage accounting, argument validation)
+agree with the oracle. No compute call is made here (no GPU needed)."""
+import os
+import re
+import ctypes
+
+import pytest
+
+import mixed_precision_kv_amd as kvq
+from oracle import layout, storage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|int32_t|const char\*)\s+(kvq_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.LIB_PATH):
+        from mixed_precision_kv_amd.build import build
+        build()
+    return kvq.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(kvq.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert kvq.kvq_abi_version() == 1
+    assert kvq.kvq_status_string(0) == "ok"
+
+
+def test_config_struct_matches_header():
+    assert ctypes.sizeof(kvq.KvqConfig) == 16 * 4
+    assert ctypes.sizeof(kvq.KvqStorage) == 9 * 8 + 8
+
+
+@pytest.mark.parametrize("n16,n4", [(16, 32), (1, 12), (0, 0), (128, 0), (3, 7)])
+def test_mixkvq_page_bytes(lib, n16, n4):
+    cfg = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 2, 8, 2, 10, n_bf16=n16, n_u4=n4)
+    assert kvq.kvq_page_bytes(cfg) == layout.mixkvq_geometry(n16, n4)["stride"]
+    assert kvq.kvq_mask_bytes(cfg) == 160
+
+
+def test_pnmix_qjl_page_bytes(lib):
+    cfg = kvq.make_config(kvq.KVQ_KEY_PNMIX, 1, 4, 1, 4, n_hi_pairs=32)
+    assert kvq.kvq_page_bytes(cfg) == layout.pnmix_geometry(64)["stride"] == 10752
+    assert kvq.kvq_mask_bytes(cfg) == 8
+    cfg = kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 4, qjl_m=256)
+    assert kvq.kvq_page_bytes(cfg) == layout.qjl_geometry(256)["stride"] == 10496
+    assert kvq.kvq_mask_bytes(cfg) == 0
+
+
+def test_storage_matches_oracle(lib):
+    cfg = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 8, 32, 8, 64, n_bf16=1, n_u4=12)
+    got = kvq.kvq_storage_bytes(cfg, 8192, 128, 0)
+    ref = storage.mixkvq_breakdown(n_kv_heads=64, d=128, n16=1, n4=12, n_quant=8192, n_resid=128)
+    assert got["key_full"] == ref["k_bf16"] and got["key_codes"] == ref["k_codes"]
+    assert got["key_meta"] == ref["k_meta"] and got["value_codes"] == ref["v_codes"]
+    assert got["value_meta"] == ref["v_meta"] and got["residual"] == ref["residual"]
+    assert got["total"] == ref["total"]
+    # PN-Mix at the 32K configuration: about 2.26 K bits (residual excluded)
+    cfg = kvq.make_config(kvq.KVQ_KEY_PNMIX, 1, 1, 1, 256, n_hi_pairs=32)
+    got = kvq.kvq_storage_bytes(cfg, 32768, 0, 32)
+    assert abs(got["key_bits_per_element"] - float(storage.pnmix_key_bits(d=128, n_quant=32768, n_sink=32))) < 1e-12
+    pn = storage.pnmix_breakdown(h_kv_d=128, n_sink=32, n_quant=32768, n_resid=128)
+    got = kvq.kvq_storage_bytes(cfg, 32768, 128, 32)
+    assert got["key_codes"] == pn["k_codes"] and got["key_meta"] == pn["k_meta"]
+    assert got["sink"] == pn["sink"] and got["residual"] == pn["residual"] and got["selection"] == pn["mask"]
+
+
+def test_validation_rejects_before_launch(lib):
+    cfg = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=16, n_u4=32)
+    bad = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, head_dim=64)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_page_bytes(bad)
+    assert e.value.status == kvq.KVQ_UNSUPPORTED
+    for field, value, status in (("n_q_heads", 6, kvq.KVQ_UNSUPPORTED), ("n_kv_heads", 3, kvq.KVQ_INVALID_ARG),
+                                 ("abi_version", 2, kvq.KVQ_INVALID_ARG),
+                                 ("n_bf16", 120, kvq.KVQ_INVALID_ARG), ("key_mode", 7, kvq.KVQ_INVALID_ARG)):
+        c = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=16, n_u4=32)
+        setattr(c, field, value)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_page_bytes(c)
+        assert e.value.status == status
+    S = lib
+    st = S.kvq_select_channels(ctypes.byref(cfg), None, 10, 10, None, 10, 10, None, None)
+    assert st == kvq.KVQ_INVALID_ARG
+    st = S.kvq_flush_quantize(ctypes.byref(cfg), 16, 16, 128, 1, 16, None, 16, 8, 16, None)
+    assert st == kvq.KVQ_CAPACITY
+    st = S.kvq_flush_quantize(ctypes.byref(cfg), 8, 16, 128, 1, 16, None, 16, 0, 16, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # misaligned source
+    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, 16, 16, 129, 129,
+                                0.088, 16, 16, 1 << 20, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # residual longer than 128
+    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+                                0.088, 16, 16, 16, None)
+    assert st == kvq.KVQ_WORKSPACE_TOO_SMALL
+    qcfg = kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 8, qjl_m=256)
+    st = S.kvq_select_channels(ctypes.byref(qcfg), 16, 10, 10, 16, 10, 10, 16, None)
+    assert st == kvq.KVQ_UNSUPPORTED
+    assert kvq.kvq_workspace_bytes(cfg, 8) > 0
