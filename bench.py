@@ -1,0 +1,285 @@
+"""Benchmark of the libkvq hot path on one MI355X.
+
+A step is one pass of the hot path on the Llama-3.1-8B-shaped layer (batch 8,
+32 query / 8 KV heads, 64 packed pages + 128 BF16 residual tokens per KV
+head, MixKVQ 1/12/115 Key tiers): one decode-attention call over the packed
+cache, then one flush of the full 128-token residual into a new page. The
+inputs (packed pages, residual, selection records, query) are resident in
+HBM before the timed region. To keep the 256 MB Infinity Cache from serving
+the 51 MB cache, the steps rotate over several copies of it.
+
+Prints one JSON line. `value` is the step's algorithmic packed-KV bytes
+(decode reads + flush reads and writes) divided by the step time; the
+decode-only GB/s, its fraction of the 8 TB/s HBM peak and the flush rate in
+tokens/s are reported beside it, as is the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "quantized decode-attn packed-KV GB/s (% of HBM peak); flush tokens/s"
+
+
+def logical_page_bytes(w) -> int:
+    """Bytes one page must hold at its logical bit widths (no padding)."""
+    v = 128 * 128 * 2 // 8 + 128 * 4 * 2 * 2
+    if w.key_mode == 0:
+        n2 = 128 - w.n_bf16 - w.n_u4
+        k = 128 * w.n_bf16 * 2 + 128 * (4 * w.n_u4 + 2 * n2) // 8 + (w.n_u4 + n2) * 2 * 2
+    elif w.key_mode == 1:
+        n_hi = 2 * w.n_hi_pairs
+        k = 128 * 128 // 8 + 128 * n_hi * 2 // 8 + 128 * 2 * 2
+    else:
+        k = 128 * w.qjl_m // 8 + 128 * 2
+    return k + v
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one decode call: packed pages, BF16 sinks and
+    residual, the selection record, the query and the float32 output."""
+    heads = w.batch * w.n_kv_heads
+    g = w.group
+    rec = {0: 160, 1: 8, 2: 0}[w.key_mode]
+    per_head = (w.n_pages * logical_page_bytes(w) + (w.n_sink + w.n_resid) * 128 * 2 * 2 + rec
+                + g * 128 * 2 + g * 128 * 4)
+    extra = 256 * 128 * 2 if w.key_mode == 2 else 0
+    return heads * per_head + extra
+
+
+def flush_bytes(w) -> int:
+    """One 128-token flush: read K and V (bf16), read the record, write a page."""
+    heads = w.batch * w.n_kv_heads
+    rec = {0: 160, 1: 8, 2: 0}[w.key_mode]
+    return heads * (128 * 128 * 2 * 2 + rec + logical_page_bytes(w))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_8k")
+    ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for >400 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", default="qwen32b_32k", help="extra decode-only workload ('' to skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    return ap.parse_args()
+
+
+class Rig:
+    """Resident inputs for a workload, with `copies` rotated cache copies."""
+
+    def __init__(self, w, copies, torch, kvq, synth):
+        self.w, self.torch, self.kvq = w, torch, kvq
+        dev = "cuda"
+        self.g = w.group
+        self.max_pages = w.n_pages + 1
+        self.cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, self.max_pages,
+                                   n_bf16=w.n_bf16, n_u4=w.n_u4, n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m)
+        pb = kvq.kvq_page_bytes(self.cfg)
+        H = w.batch * w.n_kv_heads
+        L = w.prefill_tokens
+        q, k, v = synth.prefill(w, dev)
+        self.S = synth.qjl_matrix(w, dev) if w.key_mode == 2 else None
+        self.mask = torch.zeros(max(1, H * kvq.kvq_mask_bytes(self.cfg)), dtype=torch.uint8, device=dev)
+        if w.key_mode == 0:
+            kvq.kvq_select_channels(self.cfg, q, L, k.data_ptr() + w.n_sink * 256, w.n_pages * 128, self.mask,
+                                    k_stride=L)
+        elif w.key_mode == 1:
+            kvq.kvq_select_channels(self.cfg, q, L, k, L, self.mask)
+        del q
+        arena = torch.zeros(H * self.max_pages * pb, dtype=torch.uint8, device=dev)
+        self.flags = torch.zeros(4, dtype=torch.int32, device=dev)
+        kvq.kvq_flush_quantize(self.cfg, k.data_ptr() + w.n_sink * 256, v.data_ptr() + w.n_sink * 256, L,
+                               w.n_pages, self.mask, self.S, arena, 0, self.flags)
+        rk = torch.zeros(w.batch, w.n_kv_heads, 128, 128, dtype=torch.bfloat16, device=dev)
+        rv = torch.zeros_like(rk)
+        t0 = w.n_sink + w.n_pages * 128
+        if w.n_resid:
+            rk[:, :, :w.n_resid] = k[:, :, t0:t0 + w.n_resid]
+            rv[:, :, :w.n_resid] = v[:, :, t0:t0 + w.n_resid]
+        self.sink_k = k[:, :, :w.n_sink].contiguous() if w.n_sink else None
+        self.sink_v = v[:, :, :w.n_sink].contiguous() if w.n_sink else None
+        del k, v
+        self.arenas = [arena] + [arena.clone() for _ in range(copies - 1)]
+        self.rks = [rk] + [rk.clone() for _ in range(copies - 1)]
+        self.rvs = [rv] + [rv.clone() for _ in range(copies - 1)]
+        self.q = synth.decode_query(w, dev)
+        self.out = torch.zeros(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
+        self.ws_bytes = kvq.kvq_workspace_bytes(self.cfg, w.n_pages)
+        self.ws = torch.zeros(self.ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+        self.scale = 1.0 / math.sqrt(128)
+        torch.cuda.synchronize()
+
+    def decode(self, i):
+        w = self.w
+        c = i % len(self.arenas)
+        self.kvq.kvq_decode_attention(self.cfg, self.q, self.arenas[c], w.n_pages, self.mask, self.S,
+                                      self.sink_k, self.sink_v, w.n_sink, self.rks[c], self.rvs[c], w.n_resid,
+                                      128, self.scale, self.out, self.ws, self.ws_bytes)
+
+    def flush(self, i):
+        w = self.w
+        c = i % len(self.arenas)
+        self.kvq.kvq_flush_quantize(self.cfg, self.rks[c], self.rvs[c], 128, 1, self.mask, self.S,
+                                    self.arenas[c], w.n_pages, self.flags)
+
+
+def time_steps(rig, torch, steps, warmup, with_flush):
+    for i in range(warmup):
+        rig.decode(i)
+        if with_flush:
+            rig.flush(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        a, b, c = ev[i]
+        a.record()
+        rig.decode(warmup + i)
+        b.record()
+        if with_flush:
+            rig.flush(warmup + i)
+        c.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec = [a.elapsed_time(b) for a, b, _ in ev]
+    fl = [b.elapsed_time(c) for _, b, c in ev]
+    return wall, dec, fl
+
+
+def cpu_baseline(w, synth, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole (batch, kv head) slices of batch 0. Per slice the step is the same
+    as on the GPU (one page flush + one decode over all pages); the
+    selection and the prefill flush that build the slice's cache are setup
+    and are not timed. Runs single-threaded on the host."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oatt, flush as oflush, select as osel
+    w1 = w.scaled(batch=1)
+    q, k, v = synth.prefill(w1, "cpu")
+    qd = synth.decode_query(w1, "cpu")
+    bits = synth.bf16_bits
+    g = w.group
+    per_slice_bytes = (decode_bytes(w) + flush_bytes(w)) / (w.batch * w.n_kv_heads)
+    done, t_used, slices = 0.0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for h in range(w.n_kv_heads):
+            qb, kb, vb = bits(q[0, h * g:(h + 1) * g]), bits(k[0, h]), bits(v[0, h])
+            tier, perm, _ = osel.mixkvq_select(qb, kb[:w.n_pages * 128], w.n_bf16, w.n_u4)
+            rec = osel.mixkvq_record(tier, perm)
+            t0 = time.perf_counter()
+            first = oflush.flush_mixkvq_page(kb[:128], vb[:128], perm, w.n_bf16, w.n_u4)
+            t_flush = time.perf_counter() - t0
+            pages = [first] + [oflush.flush_mixkvq_page(kb[128 * p:128 * p + 128], vb[128 * p:128 * p + 128],
+                                                        perm, w.n_bf16, w.n_u4) for p in range(1, w.n_pages)]
+            t0 = time.perf_counter()
+            oatt.decode_arena_head(0, bits(qd[0, h * g:(h + 1) * g]), pages, 1 / math.sqrt(128), n16=w.n_bf16,
+                                   n4=w.n_u4, perm=rec[:128], resid_k=kb[w.n_pages * 128:],
+                                   resid_v=vb[w.n_pages * 128:])
+            t_used += t_flush + (time.perf_counter() - t0)
+            done += per_slice_bytes
+            slices += 1
+            if t_used > budget_s:
+                break
+    return done / t_used / 1e9, slices, t_used
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is "
+              "described in DESIGN.md but not run", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    import kvq_synth as synth
+    import mixed_precision_kv_amd as kvq
+    kvq.load()
+
+    w = synth.WORKLOADS[args.workload]
+    cache_mb = decode_bytes(w) / 1e6
+    copies = args.rotate or max(1, math.ceil(400.0 / cache_mb))
+    print(f"[bench] {w.name}: {cache_mb:.1f} MB per decode, rotating {copies} copies", file=sys.stderr, flush=True)
+    rig = Rig(w, copies, torch, kvq, synth)
+    wall, dec, fl = time_steps(rig, torch, args.steps, args.warmup, with_flush=True)
+    dbytes, fbytes = decode_bytes(w), flush_bytes(w)
+    ms_step = wall / args.steps * 1e3
+    dec_ms = sum(dec) / len(dec)
+    fl_ms = sum(fl) / len(fl)
+    dec_gbps = dbytes / (dec_ms * 1e-3) / 1e9
+    step_gbps = (dbytes + fbytes) / (ms_step * 1e-3) / 1e9
+    flush_tok_s = w.batch * 128 / (fl_ms * 1e-3)
+    # warm-cache decode (no rotation) as a secondary number
+    warm = Rig.__new__(Rig)
+    warm.__dict__.update(rig.__dict__)
+    warm.arenas, warm.rks, warm.rvs = rig.arenas[:1], rig.rks[:1], rig.rvs[:1]
+    _, dec_w, _ = time_steps(warm, torch, args.steps, 3, with_flush=False)
+    dec_warm_gbps = dbytes / (sum(dec_w) / len(dec_w) * 1e-3) / 1e9
+    del warm, rig
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if args.secondary:
+        w2 = synth.WORKLOADS[args.secondary]
+        mb2 = decode_bytes(w2) / 1e6
+        print(f"[bench] secondary {w2.name}: {mb2:.1f} MB per decode", file=sys.stderr, flush=True)
+        rig2 = Rig(w2, max(1, math.ceil(400.0 / mb2)), torch, kvq, synth)
+        _, dec2, _ = time_steps(rig2, torch, max(10, args.steps // 2), 3, with_flush=False)
+        d2 = sum(dec2) / len(dec2)
+        extra = {"workload": w2.name, "decode_ms": d2, "decode_GBps": decode_bytes(w2) / (d2 * 1e-3) / 1e9,
+                 "decode_frac_hbm_peak": decode_bytes(w2) / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del rig2
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        gbps, slices, secs = cpu_baseline(w, synth, args.cpu_seconds)
+        cpu = {"value": gbps, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{slices} (batch, kv head) slices of {w.name}, each one page flush + one decode over "
+                         f"{w.n_pages} pages and {w.n_resid} residual tokens; {secs:.1f} s timed, single-threaded"}
+
+    line = {
+        "metric": METRIC,
+        "value": step_gbps,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA operands, f32 accumulate and softmax",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "quantized_tokens": w.n_pages * 128, "residual_tokens": w.n_resid,
+                   "key_tiers_bf16_u4_u2": [w.n_bf16, w.n_u4, 128 - w.n_bf16 - w.n_u4],
+                   "cache_copies_rotated": copies},
+        "decode_GBps": dec_gbps,
+        "decode_frac_hbm_peak": dec_gbps / HBM_PEAK_GBPS,
+        "decode_ms": dec_ms,
+        "decode_warm_GBps": dec_warm_gbps,
+        "flush_tokens_per_s": flush_tok_s,
+        "flush_ms": fl_ms,
+        "roofline": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode_kernel", "bytes_per_launch": dbytes},
+        "secondary": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

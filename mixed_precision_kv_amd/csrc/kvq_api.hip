@@ -61,6 +61,7 @@ static size_t workspace_for(const kvq_config* c, int n_pages) {
   size_t rows = (size_t)c->batch * c->n_q_heads;
   size_t bytes = splits * rows * 130 * sizeof(float);
   if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)c->qjl_m * sizeof(float);
+  bytes += (size_t)c->batch * c->n_kv_heads * sizeof(unsigned);   // split arrival counters
   return (bytes + 255) / 256 * 256;
 }
 
@@ -239,8 +240,11 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   a.mask = (const uint8_t*)mask;
   const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
   const size_t part_bytes = ((size_t)a.n_page_splits + 1) * rows * 130 * sizeof(float);
+  const size_t sq_bytes = cfg->key_mode == KVQ_KEY_QJL ? rows * (size_t)cfg->qjl_m * sizeof(float) : 0;
   a.partial = (float*)workspace;
   a.sq = (const float*)((uint8_t*)workspace + part_bytes);
+  a.counter = (unsigned*)((uint8_t*)workspace + part_bytes + sq_bytes);
+  a.out = out;
   a.sink_k = (const uint16_t*)sink_k;
   a.sink_v = (const uint16_t*)sink_v;
   a.n_sink = n_sink;
@@ -258,7 +262,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   a.n_hi = 2 * cfg->n_hi_pairs;
   a.pair_layout = cfg->pair_layout;
   a.qjl_m = cfg->qjl_m;
-  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, out, (hipStream_t)stream) == hipSuccess
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream) == hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;
 }

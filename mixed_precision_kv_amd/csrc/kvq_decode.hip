@@ -7,7 +7,8 @@
 // Work split: workgroup = one wave64 = one (page range, kv head, batch); the
 // last split of every (batch, kv head) handles the BF16 segment (sinks and
 // residual). Each split writes (max, sum, unnormalised output) per query
-// head; a combine kernel merges them (log-sum-exp).
+// head; the last split to finish for a (batch, kv head) merges them
+// (log-sum-exp) in the same launch.
 //
 // Per page, per kv head, the g query heads of the GQA group are processed
 // together on MFMA v_mfma_f32_16x16x32_f16 (16x16 tiles, 64 lanes):
@@ -233,6 +234,45 @@ __device__ inline void key_operand(const float* qv, const u32x4& sw, const u32x4
   split8(prod, hi, lo);
 }
 
+// The split that arrives last for a (batch, kv head) merges all partials of
+// its G query heads (log-sum-exp) and resets the arrival counter, so one
+// launch produces the final output. Release: every split fences its partial
+// stores before counting in; acquire: the last split fences before reading.
+template <int G>
+__device__ inline void finish_split(const DecodeArgs& A, int b, int kvh, int lane) {
+  __threadfence();
+  const int total = A.n_page_splits + 1;
+  unsigned* ctr = A.counter + (int64_t)b * A.n_kv_heads + kvh;
+  int old = 0;
+  if (lane == 0) old = (int)atomicAdd(ctr, 1u);
+  old = __shfl(old, 0);
+  if (old != total - 1) return;
+  __threadfence();
+  const int64_t rows = (int64_t)A.batch * A.n_q_heads;
+#pragma unroll 1
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t row = (int64_t)b * A.n_q_heads + kvh * G + hh;
+    float M = -INFINITY;
+    for (int s = 0; s < total; ++s) M = fmaxf(M, A.partial[(s * rows + row) * RECORD]);
+    float l = 0.f, o0 = 0.f, o1 = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < total; ++s) {
+        const float* rec = A.partial + (s * rows + row) * RECORD;
+        const float ms = rec[0];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f(ms - M);
+        l = fmaf(w, rec[1], l);
+        o0 = fmaf(w, rec[2 + 2 * lane], o0);
+        o1 = fmaf(w, rec[3 + 2 * lane], o1);
+      }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    A.out[row * D + 2 * lane] = o0 * inv;
+    A.out[row * D + 2 * lane + 1] = o1 * inv;
+  }
+  if (lane == 0) *ctr = 0u;
+}
+
 // ------------------------------------------------------------------ decode kernel
 template <int MODE, int G>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
@@ -314,6 +354,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
       rec[2 + 2 * lane] = o[hh][0];
       rec[2 + 2 * lane + 1] = o[hh][1];
     }
+    finish_split<G>(A, b, kvh, lane);
     return;
   }
 
@@ -546,6 +587,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
     }
   }
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col);
+  finish_split<G>(A, b, kvh, lane);
 }
 
 // QJL projection: S q for every query head (float accumulation of bf16 products).
@@ -562,24 +604,6 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, con
     for (int d = 0; d < D; ++d) acc = fmaf(bf16_to_f32(srow[d]), qs[d], acc);
     sq[(int64_t)row * m + i] = acc;
   }
-}
-
-// log-sum-exp merge of the split partials
-__global__ __launch_bounds__(128) void combine_kernel(const float* partial, float* out, int n_splits, int rows) {
-  const int row = blockIdx.x, ch = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, partial[((int64_t)s * rows + row) * RECORD]);
-  float l = 0.f, o = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float* rec = partial + ((int64_t)s * rows + row) * RECORD;
-      if (rec[0] == -INFINITY) continue;
-      float w = exp2f(rec[0] - M);
-      l = fmaf(w, rec[1], l);
-      o = fmaf(w, rec[2 + ch], o);
-    }
-  }
-  out[(int64_t)row * D + ch] = l > 0.f ? o / l : 0.f;
 }
 
 int decode_pages_per_split(int n_pages, int batch, int n_kv_heads) {
@@ -602,7 +626,7 @@ static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, float* out, hipStream_t s) {
+hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (key_mode == KVQ_KEY_QJL) {
     hipLaunchKernelGGL(qjl_project_kernel, dim3(a.batch * a.n_q_heads), dim3(256), 0, s, a.q, qjl_s,
@@ -615,10 +639,7 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_
   if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
   else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
   else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, s, a.partial, out,
-                     a.n_page_splits + 1, a.batch * a.n_q_heads);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace kvq
