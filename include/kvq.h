@@ -183,10 +183,9 @@ kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const vo
  * resid_k/resid_v: device bf16 [batch][n_kv_heads][resid_stride][128], first
  *   n_resid tokens visible (0 <= n_resid <= 128; may be NULL if 0).
  * out: device float32 [batch][n_q_heads][128].
- * workspace: device, at least kvq_workspace_bytes(cfg, n_pages) bytes, zeroed
- *   once before its first use; every call leaves it zeroed where it matters
- *   (the per-(batch, kv head) split counters), so it can be reused. Calls that
- *   share one workspace must be ordered (same stream); concurrent calls race. */
+ * workspace: device, at least kvq_workspace_bytes(cfg, n_pages) bytes (split
+ *   partials; for QJL also S q). Calls sharing one workspace must be ordered
+ *   on one stream; concurrent calls on the same workspace race. */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena,
                                 int32_t n_pages, const void* mask, const void* qjl_s,
                                 const void* sink_k, const void* sink_v, int32_t n_sink,

@@ -50,18 +50,18 @@ static size_t record_bytes(const kvq_config* c) {
   return 0;
 }
 
-static int n_page_splits(const kvq_config* c, int n_pages) {
+static int n_page_splits(const kvq_config* c, int n_pages, bool segment) {
   if (n_pages <= 0) return 0;
-  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads);
+  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads, segment);
   return (n_pages + pps - 1) / pps;
 }
 
 static size_t workspace_for(const kvq_config* c, int n_pages) {
-  size_t splits = (size_t)n_page_splits(c, n_pages) + 1;
+  // the split count without a BF16 segment is the larger one
+  size_t splits = (size_t)n_page_splits(c, n_pages, false) + 1;
   size_t rows = (size_t)c->batch * c->n_q_heads;
   size_t bytes = splits * rows * 130 * sizeof(float);
   if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)c->qjl_m * sizeof(float);
-  bytes += (size_t)c->batch * c->n_kv_heads * sizeof(unsigned);   // split arrival counters
   return (bytes + 255) / 256 * 256;
 }
 
@@ -235,15 +235,14 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   a.page_stride = (int64_t)page_stride(cfg);
   a.max_pages = cfg->max_pages;
   a.n_pages = n_pages;
-  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
-  a.n_page_splits = n_page_splits(cfg, n_pages);
+  const bool segment = n_sink + n_resid > 0;
+  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads, segment) : 1;
+  a.n_page_splits = n_page_splits(cfg, n_pages, segment);
   a.mask = (const uint8_t*)mask;
   const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
   const size_t part_bytes = ((size_t)a.n_page_splits + 1) * rows * 130 * sizeof(float);
-  const size_t sq_bytes = cfg->key_mode == KVQ_KEY_QJL ? rows * (size_t)cfg->qjl_m * sizeof(float) : 0;
   a.partial = (float*)workspace;
   a.sq = (const float*)((uint8_t*)workspace + part_bytes);
-  a.counter = (unsigned*)((uint8_t*)workspace + part_bytes + sq_bytes);
   a.out = out;
   a.sink_k = (const uint16_t*)sink_k;
   a.sink_v = (const uint16_t*)sink_v;

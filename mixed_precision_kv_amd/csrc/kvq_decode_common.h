@@ -1,0 +1,318 @@
+// Decode helpers shared by the generic and the pipelined decode kernels:
+// MFMA operand expansion, online softmax with the value MFMA, partial writes
+// and the BF16 (sink + residual) segment.
+#pragma once
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float B_SCALE = 0.015625f;   // 2^-6 applied to every Key B operand (f16 range headroom)
+constexpr float B_UNSCALE = 64.0f;
+constexpr int MAX_KS = 8;              // max Key k-steps of 32 slots
+constexpr int RECORD = 130;            // partial record per query head: m, l, out[128]
+
+
+__device__ inline uint32_t rd(const u32x4& v, int i) { return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w)); }
+
+__device__ inline u32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ inline uint32_t h2u(half2v h) {
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
+// fp4 pair conversion: byte `sel` of w (two nibbles 0b00cc / 0b000c) -> f16 (c_lo, c_hi)
+template <int SEL>
+__device__ inline uint32_t cvt2(uint32_t w) {
+  return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, SEL));
+}
+
+__device__ inline half8 u4_to_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  half8 h;
+  __builtin_memcpy(&h, &v, 16);
+  return h;
+}
+
+// 2-bit block dword w (tiles 2w, 2w+1 of one row) -> A fragments of both tiles
+__device__ inline void expand2(uint32_t w, half8& t0, half8& t1) {
+  uint32_t we = w & 0x33333333u, wo = (w >> 2) & 0x33333333u;
+  t0 = u4_to_h8(cvt2<0>(we), cvt2<0>(wo), cvt2<1>(we), cvt2<1>(wo));
+  t1 = u4_to_h8(cvt2<2>(we), cvt2<2>(wo), cvt2<3>(we), cvt2<3>(wo));
+}
+
+// 1-bit dword (tiles 4q..4q+3 of one row) -> A fragments of 4 tiles
+__device__ inline void expand1(uint32_t w, half8* t) {
+  uint32_t m0 = w & 0x11111111u, m1 = (w >> 1) & 0x11111111u, m2 = (w >> 2) & 0x11111111u,
+           m3 = (w >> 3) & 0x11111111u;
+  t[0] = u4_to_h8(cvt2<0>(m0), cvt2<0>(m1), cvt2<0>(m2), cvt2<0>(m3));
+  t[1] = u4_to_h8(cvt2<1>(m0), cvt2<1>(m1), cvt2<1>(m2), cvt2<1>(m3));
+  t[2] = u4_to_h8(cvt2<2>(m0), cvt2<2>(m1), cvt2<2>(m2), cvt2<2>(m3));
+  t[3] = u4_to_h8(cvt2<3>(m0), cvt2<3>(m1), cvt2<3>(m2), cvt2<3>(m3));
+}
+
+__device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ inline f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32). Softmax weights below 2^-126
+// flush to zero, which changes no result at float precision.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_bf(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// hi/lo f16 split of 8 products
+__device__ inline void split8(const float* x, half8& hi, half8& lo) {
+  for (int e = 0; e < 8; ++e) {
+    _Float16 h = (_Float16)x[e];
+    hi[e] = h;
+    lo[e] = (_Float16)(x[e] - (float)h);
+  }
+}
+
+__device__ inline float wave_max_groups(float v) {   // max over the 4 lane groups sharing a column
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ inline float wave_sum_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Online-softmax state of one lane (one head; one value group per pass).
+template <int NPASS>
+struct SoftState {
+  float m;          // running max (log2 domain)
+  float l;          // partial sum of p over this lane's tokens
+  float z[NPASS];   // partial sum of p * value offset, per pass
+  f32x4 acc[8];     // value accumulators of the 8 value tiles (16 channels each)
+};
+
+// Consume one page: logit[i][e] is the raw Key accumulator of tile i row e
+// (token 16 i + 4 a + e); the log2-domain logit is logit * xs + xb.
+template <int G, int NPASS>
+__device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)[8], float xs, float xb,
+                                      const u32x4 (&vc)[4], const uint8_t* vmeta, int a, int col) {
+  constexpr int C = 16 / G;
+  float pm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pm = fmaxf(pm, logit[i][e]);
+  pm = fmaf(wave_max_groups(pm), xs, xb);
+  const float mn = fmaxf(st.m, pm);
+  if (__any(mn > st.m)) {
+    const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) st.z[P] *= alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st.acc[u] *= alpha;
+    st.m = mn;
+  }
+  const float shift = xb - st.m;
+  float p[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[i][e] = fast_exp2(fmaf(logit[i][e], xs, shift));
+      st.l += p[i][e];
+    }
+  const int jl = col / G;
+#pragma unroll
+  for (int P = 0; P < NPASS; ++P) {
+    const int j = (jl + P * C) & 3;            // this lane's value group in pass P
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint8_t* mb = vmeta + 512 * ks + 128 * a + 32 * j;
+      const u32x4 sw = ld16(mb), zw = ld16(mb + 16);
+      half8 B;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = rd(sw, e >> 1), zz = rd(zw, e >> 1);
+        const float s = (e & 1) ? hi_bf(w) : lo_bf(w);
+        const float z = (e & 1) ? hi_bf(zz) : lo_bf(zz);
+        const float pe = p[2 * ks + (e >> 2)][e & 3];     // token pi(ks, a, e)
+        B[e] = (_Float16)(pe * s);
+        st.z[P] = fmaf(pe, z, st.z[P]);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {            // value tiles 2w, 2w+1 hold group w
+        if (w / C != P) continue;
+        half8 A0, A1;
+        expand2(rd(vc[ks], w), A0, A1);
+        st.acc[2 * w] = mfma(A0, B, st.acc[2 * w]);
+        st.acc[2 * w + 1] = mfma(A1, B, st.acc[2 * w + 1]);
+      }
+    }
+  }
+}
+
+// LDS staging area (8 KB) for write_partial: the BF16-segment buffer, free
+// once a split's page loop has ended.
+template <class Smem>
+__device__ inline float* stage_buf(Smem& S) {
+  return &S.u.p_lds[0][0];
+}
+
+// Write this split's (m, l, out) for the lane's head. Lane (a, col) holds
+// rows 4a..4a+3 of all 8 value tiles for column col = (copy jl, head h);
+// only tiles of value group jl + P*C are meaningful. The tiles go through
+// LDS with static indices (stage: 64 lanes x 32 floats), then every lane
+// writes 2 channels of each head's record, coalesced.
+template <int G, int NPASS>
+__device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, int split, int b, int kvh, int a,
+                                     int col, float* stage) {
+  constexpr int C = 16 / G;
+  const int lane = threadIdx.x;
+  const float l = wave_sum_groups(st.l);
+  float z[NPASS];
+#pragma unroll
+  for (int P = 0; P < NPASS; ++P) z[P] = wave_sum_groups(st.z[P]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int P = (u >> 1) / C;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) stage[(col * 8 + u) * 4 * 4 + a * 4 + e] = st.acc[u][e] + (P < NPASS ? z[P] : 0.f);
+  }
+  __syncthreads();
+  const int h = col % G, jl = col / G;
+  float* base = A.partial + (((int64_t)split * A.batch + b) * A.n_q_heads + kvh * G) * RECORD;
+  if (a == 0 && jl == 0) {
+    base[h * RECORD] = st.m;
+    base[h * RECORD + 1] = l;
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ch = 2 * lane + k;                 // channel = 16 u + 4 a' + e
+      const int u = ch >> 4, aa = (ch >> 2) & 3, e = ch & 3;
+      const int j = u >> 1, c = (j % C) * G + hh;  // column holding (group j, head hh)
+      base[hh * RECORD + 2 + ch] = stage[(c * 8 + u) * 16 + aa * 4 + e];
+    }
+  }
+}
+
+
+// Key slot operand for k-step ks: B = q * s * 2^-6 (hi/lo), bias += q . z
+__device__ inline void key_operand(const float* qv, const u32x4& sw, const u32x4& zw, half8& hi, half8& lo,
+                                   float& bias) {
+  float prod[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = rd(sw, e >> 1), z = rd(zw, e >> 1);
+    prod[e] = qv[e] * ((e & 1) ? hi_bf(w) : lo_bf(w)) * B_SCALE;
+    bias = fmaf(qv[e], (e & 1) ? hi_bf(z) : lo_bf(z), bias);
+  }
+  split8(prod, hi, lo);
+}
+
+// Key slot operand from pre-scaled query values (q * 2^-6): B = q * s (hi/lo)
+__device__ inline void key_operand_scaled(const float* qv, const u32x4& sw, half8& hi, half8& lo) {
+  float prod[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = rd(sw, e >> 1);
+    prod[e] = qv[e] * ((e & 1) ? hi_bf(w) : lo_bf(w));
+  }
+  split8(prod, hi, lo);
+}
+
+__device__ inline bf16x8 as_bf16x8(const u32x4& v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// BF16 segment (attention sinks + residual), one wave: q.k on the bf16 MFMA
+// (exact products), probabilities staged in LDS, p.V on the VALU with each
+// lane owning two channels. Writes the split's partial record.
+template <int G>
+__device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int kvh, int lane, float (*p_lds)[8],
+                                    float* mh) {
+  const int a = lane >> 4, r = lane & 15, col = r, h = col % G;
+  const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
+  const uint16_t* qrow = A.q + ((int64_t)b * A.n_q_heads + kvh * G + h) * D;
+  const int T = A.n_sink + A.n_resid;
+  bf16x8 Bq[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 raw = ld16(reinterpret_cast<const uint8_t*>(qrow + 32 * ks + 8 * a));
+    __builtin_memcpy(&Bq[ks], &raw, 16);
+  }
+  float mloc = -INFINITY;
+  const int nt = (T + 15) / 16;
+  for (int i = 0; i < nt; ++i) {
+    const int t = 16 * i + r;                // A row = token
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (t < A.n_sink)
+        raw = ld16(reinterpret_cast<const uint8_t*>(A.sink_k + (head * A.n_sink + t) * D + 32 * ks + 8 * a));
+      else if (t < T)
+        raw = ld16(reinterpret_cast<const uint8_t*>(A.resid_k + (head * A.resid_stride + (t - A.n_sink)) * D +
+                                                    32 * ks + 8 * a));
+      bf16x8 Ak;
+      __builtin_memcpy(&Ak, &raw, 16);
+      acc = mfma_bf(Ak, Bq[ks], acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 16 * i + 4 * a + e;
+      const float x = tok < T ? acc[e] * A.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, x);
+      if (col < G) p_lds[tok][col] = x;
+    }
+  }
+  const float m = wave_max_groups(mloc);
+  if (a == 0 && col < G) mh[col] = m;
+  __syncthreads();
+  for (int idx = lane; idx < 16 * nt * G; idx += 64) {
+    const int tok = idx / G, hh = idx % G;
+    p_lds[tok][hh] = tok < T ? fast_exp2(p_lds[tok][hh] - mh[hh]) : 0.f;
+  }
+  __syncthreads();
+  float o[G][2], lsum[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) o[hh][0] = o[hh][1] = lsum[hh] = 0.f;
+  for (int t = 0; t < T; ++t) {              // lane owns channels 2 lane, 2 lane + 1
+    const uint16_t* vrow = t < A.n_sink ? A.sink_v + (head * A.n_sink + t) * D
+                                        : A.resid_v + (head * A.resid_stride + (t - A.n_sink)) * D;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(vrow)[lane];
+    const float v0 = lo_bf(w), v1 = hi_bf(w);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float pp = p_lds[t][hh];
+      o[hh][0] = fmaf(pp, v0, o[hh][0]);
+      o[hh][1] = fmaf(pp, v1, o[hh][1]);
+      lsum[hh] += pp;
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float* rec = A.partial + (((int64_t)split * A.batch + b) * A.n_q_heads + kvh * G + hh) * RECORD;
+    if (lane == 0) {
+      rec[0] = T > 0 ? mh[hh] : -INFINITY;
+      rec[1] = lsum[hh];
+    }
+    rec[2 + 2 * lane] = o[hh][0];
+    rec[2 + 2 * lane + 1] = o[hh][1];
+  }
+}
+
+}  // namespace kvq

@@ -1,0 +1,598 @@
+// Software-pipelined decode kernels for the common shapes (GQA group 4 or 8,
+// the workloads' Key layouts). Same arithmetic as the generic kernel in
+// kvq_decode.hip (see there for the method and the MFMA conventions); what
+// differs is the memory pipeline:
+//  * every loop index is a compile-time constant (templates on the number
+//    of Key k-steps and BF16-tier loads), so no runtime selects remain;
+//  * while page p is computed, page p+1 is already in flight: its code
+//    fragments are prefetched into registers and its scale/offset metadata
+//    is copied straight into a double-buffered LDS slot with
+//    global_load_lds_dwordx4 (no VGPRs), one wait per page.
+//  * the first page's loads are issued before the per-split set-up (query
+//    staging, slot tables), so set-up and the first memory latency overlap;
+//  * LDS holds only what one split needs (about 14 KB for GQA group 8), so
+//    eight single-wave workgroups stay resident per CU.
+// LDS metadata slot of a page: [0, 1024) Key meta (MixKVQ, PN-Mix) or norms
+// (QJL), [1024, 3072) value meta.
+#include "kvq_decode_common.h"
+
+namespace kvq {
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ inline void async16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds_base, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// The memory clobber keeps the compiler from moving LDS reads above it.
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for this wave's LDS operations (orders plain LDS stores before an
+// asynchronous global->LDS copy into the same bytes).
+__device__ inline void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ inline u32x4 lds16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+constexpr int META_SLOT = 3072;
+
+// Shared memory of the MixKVQ / PN-Mix kernels. The page-loop tables and the
+// BF16-segment / partial staging buffer (8 KB) share one union; the bf16
+// query is staged in the value-meta half of slot 1 during set-up.
+template <int G, int NKS>
+struct PgSmem {
+  union {
+    struct {
+      float qslot[NKS][4][G][8];   // [k-step][lane group][head][e]: q * 2^-6 of the slot's channel
+      bf16x8 qz[NKS][4][G];        // raw bf16 q of the slot's channel (offset MFMA operand)
+      uint8_t meta[2][META_SLOT];  // double-buffered page metadata
+    } pg;
+    float p_lds[256][8];
+  } u;
+  int slot_ch[32 * NKS];
+  float mh[16];
+};
+
+template <int G>
+struct QjSmem {
+  union {
+    struct {
+      half8 bq[2][8][4][G];        // S q hi/lo [k-step][lane group][head]
+      uint8_t meta[2][META_SLOT];
+    } qj;
+    float p_lds[256][8];
+  } u;
+  float mh[16];
+};
+
+// value meta (2048 B) of a page -> LDS slot + 1024: two async loads
+__device__ inline void issue_vmeta(const uint8_t* vmeta_g, uint8_t* slot, int lane) {
+  async16(vmeta_g + 16 * lane, slot + 1024);
+  async16(vmeta_g + 1024 + 16 * lane, slot + 2048);
+}
+
+// query heads kvh*G .. kvh*G+G-1 of batch b as 16-byte chunks (8 bf16), G/4 per lane
+template <int G>
+__device__ inline void load_q(const DecodeArgs& A, int b, int kvh, int lane, u32x4 (&qv)[G / 4]) {
+  const uint8_t* qg = reinterpret_cast<const uint8_t*>(A.q + ((int64_t)b * A.n_q_heads + kvh * G) * D);
+#pragma unroll
+  for (int j = 0; j < G / 4; ++j) qv[j] = ld16(qg + 16 * (lane + 64 * j));
+}
+
+template <int G>
+__device__ inline void stage_q(const u32x4 (&qv)[G / 4], uint8_t* qb, int lane) {
+#pragma unroll
+  for (int j = 0; j < G / 4; ++j) *reinterpret_cast<u32x4*>(qb + 16 * (lane + 64 * j)) = qv[j];
+}
+
+__device__ inline float qb_at(const uint8_t* qb, int h, int ch) {
+  return bf16_to_f32(reinterpret_cast<const uint16_t*>(qb)[h * D + ch]);
+}
+
+// ------------------------------------------------------------------ MixKVQ
+template <int NKS, int NB>
+struct MixCodes {
+  u32x4 kc[NKS];
+  u32x4 vc[4];
+  u32x4 bf[NB > 0 ? NB : 1];
+};
+
+template <int NKS, int NB>
+__device__ inline void mix_load(MixCodes<NKS, NB>& c, const uint8_t* page, const MixGeo& g, int a, int r) {
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int f = 4 * ks + a;
+    c.kc[ks] = (u32x4){0u, 0u, 0u, 0u};
+    if (f < g.F) c.kc[ks] = ld16(page + g.off_codes + 256 * f + 16 * r);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int ch = 8 * a + e;
+    c.bf[e] = (u32x4){0u, 0u, 0u, 0u};
+    if (ch < g.n16) c.bf[e] = ld16(page + 256 * ch + 16 * r);
+  }
+}
+
+__device__ inline void mix_issue_meta(const uint8_t* page, uint8_t* slot, const MixGeo& g, int lane) {
+  if (lane < 2 * g.F) async16(page + g.off_meta + 16 * lane, slot);
+  issue_vmeta(page + g.off_v + V_CODE_BYTES, slot, lane);
+}
+
+template <int G, int NKS, int NB, int NPASS>
+__device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c, const uint8_t* slot,
+                                const PgSmem<G, NKS>& S, const bf16x8& Bq, float xs, float scale_log2, int a,
+                                int h, int col) {
+  f32x4 logit[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  f32x4 zacc = {0.f, 0.f, 0.f, 0.f};       // sum_slot q * offset, identical in every row
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint8_t* km = slot + 32 * (4 * ks + a);
+    const u32x4 sw = lds16(km), zw = lds16(km + 16);
+    half8 Bhi, Blo;
+    key_operand_scaled(S.u.pg.qslot[ks][a][h], sw, Bhi, Blo);
+    zacc = mfma_bf(as_bf16x8(zw), S.u.pg.qz[ks][a][h], zacc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      half8 A0, A1;
+      expand2(rd(c.kc[ks], w), A0, A1);
+      logit[2 * w] = mfma(A0, Bhi, logit[2 * w]);
+      logit[2 * w] = mfma(A0, Blo, logit[2 * w]);
+      logit[2 * w + 1] = mfma(A1, Bhi, logit[2 * w + 1]);
+      logit[2 * w + 1] = mfma(A1, Blo, logit[2 * w + 1]);
+    }
+  }
+  if constexpr (NB > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t tmp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        tmp[e] = e < NB ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1))) : (uint16_t)0;
+      bf16x8 Ak;
+      __builtin_memcpy(&Ak, tmp, 16);
+      logit[i] = mfma_bf(Ak, Bq, logit[i]);
+    }
+  }
+  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot + 1024, a, col);
+}
+
+// Registers of 256 VGPRs (two waves per SIMD) fit every variant except the
+// eight-channel BF16 tier, which keeps one wave per SIMD rather than spill.
+template <int G, int NKS, int NB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 : 2))) void decode_mix_fast(
+    DecodeArgs A) {
+  constexpr int C = 16 / G;
+  constexpr int NPASS = (4 + C - 1) / C;
+  __shared__ PgSmem<G, NKS> S;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
+  if (split == A.n_page_splits) {
+    bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
+    return;
+  }
+  const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
+  const MixGeo g = mix_geo(A.n16, A.n4);
+  const uint8_t* rec = A.mask + head * MIX_RECORD;
+  const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
+  const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
+
+  // set-up loads: query rows, the slot -> channel map and the BF16 channels
+  u32x4 qv[G / 4];
+  load_q<G>(A, b, kvh, lane, qv);
+  int sch[(32 * NKS + 63) / 64];
+#pragma unroll
+  for (int j = 0; j < (32 * NKS + 63) / 64; ++j) {
+    const int s = lane + 64 * j;
+    int ch = -1;
+    if (s < 2 * g.n4) ch = rec[g.n16 + (s >> 1)];
+    else if (s >= g.s4 && s < g.s4 + g.n2) ch = rec[g.n16 + g.n4 + (s - g.s4)];
+    sch[j] = ch;
+  }
+  int bch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bch[e] = (8 * a + e < g.n16) ? rec[8 * a + e] : -1;
+  // Key meta past the page's own 32 F bytes is read as zero scale / offset
+  for (int i = lane; i < 2 * 1024 / 16; i += 64) {
+    const int sl = i / 64, o = (i % 64) * 16;
+    *reinterpret_cast<u32x4*>(&S.u.pg.meta[sl][o]) = (u32x4){0u, 0u, 0u, 0u};
+  }
+  wait_lgkm0();
+  // first page in flight during the set-up
+  MixCodes<NKS, NB> c0, c1;
+  mix_issue_meta(pages, S.u.pg.meta[0], g, lane);
+  mix_load(c0, pages, g, a, r);
+
+  uint8_t* qb = S.u.pg.meta[1] + 1024;    // bf16 q staging, free until page 1's metadata arrives
+  stage_q<G>(qv, qb, lane);
+#pragma unroll
+  for (int j = 0; j < (32 * NKS + 63) / 64; ++j)
+    if (lane + 64 * j < 32 * NKS) S.slot_ch[lane + 64 * j] = sch[j];
+  __syncthreads();
+  for (int idx = lane; idx < NKS * 4 * G * 8; idx += 64) {
+    const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
+    const int ch = S.slot_ch[8 * (4 * ks + aa) + e];
+    const float qf = ch >= 0 ? qb_at(qb, hh, ch) : 0.f;
+    S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
+    S.u.pg.qz[ks][aa][hh][e] = (__bf16)qf;     // exact: q is bf16
+  }
+  bf16x8 Bq;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 ? qb_at(qb, h, bch[e]) * B_SCALE : 0.f);
+  __syncthreads();
+
+  SoftState<NPASS> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float xs = A.scale_log2 * B_UNSCALE;
+
+  for (int it = 0; it < np; it += 2) {
+    // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
+    if (it + 1 < np) {
+      mix_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.pg.meta[1], g, lane);
+      wait_vm<3>();
+      mix_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
+    } else {
+      wait_vm<0>();
+    }
+    mix_page<G, NKS, NB, NPASS>(st, c0, S.u.pg.meta[0], S, Bq, xs, A.scale_log2, a, h, col);
+    if (it + 1 >= np) break;
+    if (it + 2 < np) {
+      mix_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, S.u.pg.meta[0], g, lane);
+      wait_vm<3>();
+      mix_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
+    } else {
+      wait_vm<0>();
+    }
+    mix_page<G, NKS, NB, NPASS>(st, c1, S.u.pg.meta[1], S, Bq, xs, A.scale_log2, a, h, col);
+  }
+  __syncthreads();
+  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
+}
+
+// ------------------------------------------------------------------ PN-Mix
+struct PnCodes {
+  u32x4 lsb[2];
+  u32x4 up[2];
+  u32x4 vc[4];
+};
+
+__device__ inline void pn_load(PnCodes& c, const uint8_t* page, const PnGeo& g, int a, int r) {
+#pragma unroll
+  for (int P2 = 0; P2 < 2; ++P2) c.lsb[P2] = ld16(page + 1024 * P2 + 256 * a + 16 * r);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int f = 4 * ks + a;
+    c.up[ks] = (u32x4){0u, 0u, 0u, 0u};
+    if (f < g.n_up_frag) c.up[ks] = ld16(page + g.off_up + 256 * f + 16 * r);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
+}
+
+__device__ inline void pn_issue_meta(const uint8_t* page, uint8_t* slot, const PnGeo& g, int lane) {
+  if (lane < 32) async16(page + g.off_meta + 16 * lane, slot);   // 512 B of slot scales/offsets
+  issue_vmeta(page + g.off_v + V_CODE_BYTES, slot, lane);
+}
+
+template <int G, int NPASS>
+__device__ inline void pn_page(SoftState<NPASS>& st, const PnCodes& c, const uint8_t* slot,
+                               const PgSmem<G, 4>& S, float xs, float scale_log2, int a, int h, int col) {
+  f32x4 logit[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint8_t* km = slot + 32 * (4 * ks + a);
+    const u32x4 sw = lds16(km), zw = lds16(km + 16);
+    half8 Bhi, Blo;
+    key_operand_scaled(S.u.pg.qslot[ks][a][h], sw, Bhi, Blo);
+    zacc = mfma_bf(as_bf16x8(zw), S.u.pg.qz[ks][a][h], zacc);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {        // LSB plane: 1-bit codes, weight s
+      half8 At[4];
+      expand1(rd(c.lsb[ks >> 1], 2 * (ks & 1) + q2), At);
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        logit[4 * q2 + T] = mfma(At[T], Bhi, logit[4 * q2 + T]);
+        logit[4 * q2 + T] = mfma(At[T], Blo, logit[4 * q2 + T]);
+      }
+    }
+    if (ks < 2) {                           // upper two bits of the high channels, weight 2 s
+      const half8 Uh = Bhi * (_Float16)2.0f, Ul = Blo * (_Float16)2.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        half8 A0, A1;
+        expand2(rd(c.up[ks], w), A0, A1);
+        logit[2 * w] = mfma(A0, Uh, logit[2 * w]);
+        logit[2 * w] = mfma(A0, Ul, logit[2 * w]);
+        logit[2 * w + 1] = mfma(A1, Uh, logit[2 * w + 1]);
+        logit[2 * w + 1] = mfma(A1, Ul, logit[2 * w + 1]);
+      }
+    }
+  }
+  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot + 1024, a, col);
+}
+
+template <int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_pn_fast(DecodeArgs A) {
+  constexpr int C = 16 / G;
+  constexpr int NPASS = (4 + C - 1) / C;
+  __shared__ PgSmem<G, 4> S;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
+  if (split == A.n_page_splits) {
+    bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
+    return;
+  }
+  const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
+  const PnGeo g = pn_geo(A.n_hi);
+  const uint8_t* rec = A.mask + head * PN_RECORD;
+  const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
+  const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
+
+  u32x4 qv[G / 4];
+  load_q<G>(A, b, kvh, lane, qv);
+  // slot order: high channels ascending, then low ones. Lane d < D/2 owns
+  // channels d and d + 64 (half split) or 2d, 2d+1 (adjacent): find its rank.
+  uint32_t bits[2];
+  bits[0] = (uint32_t)rec[0] | (uint32_t)rec[1] << 8 | (uint32_t)rec[2] << 16 | (uint32_t)rec[3] << 24;
+  bits[1] = (uint32_t)rec[4] | (uint32_t)rec[5] << 8 | (uint32_t)rec[6] << 16 | (uint32_t)rec[7] << 24;
+
+  PnCodes c0, c1;
+  pn_issue_meta(pages, S.u.pg.meta[0], g, lane);
+  pn_load(c0, pages, g, a, r);
+
+  uint8_t* qb = S.u.pg.meta[1] + 1024;
+  stage_q<G>(qv, qb, lane);
+  {
+    const uint64_t mask = (uint64_t)bits[0] | (uint64_t)bits[1] << 32;   // pair p is high iff bit p
+    const int nh = __builtin_popcountll(mask);                            // high pairs
+    // channel d -> pair; the slot of channel d counts the channels before it in its class
+    for (int d = lane; d < D; d += 64) {
+      const bool half = A.pair_layout == KVQ_PAIR_HALF_SPLIT;
+      const int pair = half ? (d & 63) : (d >> 1);
+      const bool hi = (mask >> pair) & 1;
+      // channels before d in the same class: for half split, pairs below (d & 63)
+      // in this half plus all of that class in the first half when d >= 64
+      int before;
+      const uint64_t below = pair == 0 ? 0ull : (mask & ((1ull << pair) - 1));
+      if (half) {
+        const int cnt = __builtin_popcountll(below);
+        const int in_first = hi ? nh : 64 - nh;
+        before = (hi ? cnt : pair - cnt) + (d >= 64 ? in_first : 0);
+      } else {
+        const int cnt = __builtin_popcountll(below);
+        before = 2 * (hi ? cnt : pair - cnt) + (d & 1);
+      }
+      S.slot_ch[hi ? before : 2 * nh + before] = d;
+    }
+  }
+  __syncthreads();
+  for (int idx = lane; idx < 4 * 4 * G * 8; idx += 64) {
+    const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
+    const float qf = qb_at(qb, hh, S.slot_ch[8 * (4 * ks + aa) + e]);
+    S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
+    S.u.pg.qz[ks][aa][hh][e] = (__bf16)qf;
+  }
+  __syncthreads();
+
+  SoftState<NPASS> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float xs = A.scale_log2 * B_UNSCALE;
+
+  for (int it = 0; it < np; it += 2) {
+    if (it + 1 < np) {
+      pn_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.pg.meta[1], g, lane);
+      wait_vm<3>();
+      pn_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
+    } else {
+      wait_vm<0>();
+    }
+    pn_page<G, NPASS>(st, c0, S.u.pg.meta[0], S, xs, A.scale_log2, a, h, col);
+    if (it + 1 >= np) break;
+    if (it + 2 < np) {
+      pn_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, S.u.pg.meta[0], g, lane);
+      wait_vm<3>();
+      pn_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
+    } else {
+      wait_vm<0>();
+    }
+    pn_page<G, NPASS>(st, c1, S.u.pg.meta[1], S, xs, A.scale_log2, a, h, col);
+  }
+  __syncthreads();
+  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
+}
+
+// ------------------------------------------------------------------ QJL (m = 256)
+struct QjCodes {
+  u32x4 bits[4];
+  u32x4 vc[4];
+};
+
+__device__ inline void qj_load(QjCodes& c, const uint8_t* page, const QjlGeo& g, int a, int r) {
+#pragma unroll
+  for (int P2 = 0; P2 < 4; ++P2) c.bits[P2] = ld16(page + 1024 * P2 + 256 * a + 16 * r);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
+}
+
+__device__ inline void qj_issue_meta(const uint8_t* page, uint8_t* slot, const QjlGeo& g, int lane) {
+  if (lane < 16) async16(page + g.off_norm + 16 * lane, slot);     // 256 B of norms
+  issue_vmeta(page + g.off_v + V_CODE_BYTES, slot, lane);
+}
+
+template <int G, int NPASS>
+__device__ inline void qj_page(SoftState<NPASS>& st, const QjCodes& c, const uint8_t* slot,
+                               const QjSmem<G>& S, float ssum, float xs, int a, int h, int col) {
+  f32x4 logit[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int P2 = 0; P2 < 4; ++P2) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ks = 2 * P2 + hf;
+      const half8 Bh = S.u.qj.bq[0][ks][a][h], Bl = S.u.qj.bq[1][ks][a][h];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        half8 At[4];
+        expand1(rd(c.bits[P2], 2 * hf + q2), At);
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          logit[4 * q2 + T] = mfma(At[T], Bh, logit[4 * q2 + T]);
+          logit[4 * q2 + T] = mfma(At[T], Bl, logit[4 * q2 + T]);
+        }
+      }
+    }
+  }
+  // nu_t * (2 <Sq, bits> - sum Sq); tokens 16 i + 4 a + e have their norms at 32 a + 4 i + e
+  const uint8_t* nb = slot + 64 * a;
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const u32x4 nw = lds16(nb + 16 * qd);
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * qd + ii;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = rd(nw, 2 * ii + (e >> 1));
+        const uint16_t hb = (uint16_t)(w >> (16 * (e & 1)));
+        _Float16 hv;
+        __builtin_memcpy(&hv, &hb, 2);
+        logit[i][e] = (float)hv * (2.0f * logit[i][e] - ssum);
+      }
+    }
+  }
+  consume_values<G, NPASS>(st, logit, xs, 0.f, c.vc, slot + 1024, a, col);
+}
+
+template <int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_qjl_fast(DecodeArgs A) {
+  constexpr int C = 16 / G;
+  constexpr int NPASS = (4 + C - 1) / C;
+  __shared__ QjSmem<G> S;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
+  if (split == A.n_page_splits) {
+    bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
+    return;
+  }
+  const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
+  const QjlGeo g = qjl_geo(A.qjl_m);
+  const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
+  const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
+
+  QjCodes c0, c1;
+  qj_issue_meta(pages, S.u.qj.meta[0], g, lane);
+  qj_load(c0, pages, g, a, r);
+
+  const int hq = kvh * G + h;
+  const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * A.qjl_m;
+  float ssum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sqrow[32 * ks + 8 * a + e] * B_SCALE;
+    half8 hi, lo;
+    split8(x, hi, lo);
+    if (col < G) {
+      S.u.qj.bq[0][ks][a][h] = hi;
+      S.u.qj.bq[1][ks][a][h] = lo;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ssum += (float)hi[e] + (float)lo[e];
+  }
+  ssum = wave_sum_groups(ssum);
+  __syncthreads();
+
+  SoftState<NPASS> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
+
+  for (int it = 0; it < np; it += 2) {
+    if (it + 1 < np) {
+      qj_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.qj.meta[1], g, lane);
+      wait_vm<3>();
+      qj_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
+    } else {
+      wait_vm<0>();
+    }
+    qj_page<G, NPASS>(st, c0, S.u.qj.meta[0], S, ssum, xs, a, h, col);
+    if (it + 1 >= np) break;
+    if (it + 2 < np) {
+      qj_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, S.u.qj.meta[0], g, lane);
+      wait_vm<3>();
+      qj_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
+    } else {
+      wait_vm<0>();
+    }
+    qj_page<G, NPASS>(st, c1, S.u.qj.meta[1], S, ssum, xs, a, h, col);
+  }
+  __syncthreads();
+  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
+}
+
+// ------------------------------------------------------------------ dispatch
+template <int G, int NKS>
+static bool launch_mix_nb(const DecodeArgs& a, int nb, dim3 grid, hipStream_t s) {
+  if (nb == 0) hipLaunchKernelGGL((decode_mix_fast<G, NKS, 0>), grid, dim3(64), 0, s, a);
+  else if (nb == 1) hipLaunchKernelGGL((decode_mix_fast<G, NKS, 1>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_mix_fast<G, NKS, 8>), grid, dim3(64), 0, s, a);
+  return true;
+}
+
+// Returns true when a pipelined kernel covers the configuration.
+bool launch_decode_fast(int key_mode, const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const int g = a.n_q_heads / a.n_kv_heads;
+  if (g != 4 && g != 8) return false;
+  if (key_mode == KVQ_KEY_MIXKVQ) {
+    const MixGeo geo = mix_geo(a.n16, a.n4);
+    const int nks = (geo.F + 3) / 4;
+    if (a.n16 > 8) return false;   // the fast path keeps the BF16 tier in lane group 0 (<= 8 channels)
+    const int nb = a.n16 == 0 ? 0 : (a.n16 == 1 ? 1 : 8);
+    if (nks == 5) {
+      if (g == 4) return launch_mix_nb<4, 5>(a, nb, grid, s);
+      return launch_mix_nb<8, 5>(a, nb, grid, s);
+    }
+    if (nks == 4) {
+      if (g == 4) return launch_mix_nb<4, 4>(a, nb, grid, s);
+      return launch_mix_nb<8, 4>(a, nb, grid, s);
+    }
+    return false;
+  }
+  if (key_mode == KVQ_KEY_PNMIX) {
+    if (a.n_hi != 64) return false;
+    if (g == 4) hipLaunchKernelGGL((decode_pn_fast<4>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_pn_fast<8>), grid, dim3(64), 0, s, a);
+    return true;
+  }
+  if (a.qjl_m != 256) return false;
+  if (g == 4) hipLaunchKernelGGL((decode_qjl_fast<4>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_qjl_fast<8>), grid, dim3(64), 0, s, a);
+  return true;
+}
+
+}  // namespace kvq

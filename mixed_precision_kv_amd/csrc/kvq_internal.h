@@ -192,7 +192,6 @@ struct DecodeArgs {
   float qjl_coef;
   float* partial;                 // [n_splits][B][Hq][130]: m, l, out[128]
   float* out;                     // [B][Hq][128]
-  unsigned* counter;              // [B][Hkv] split arrival counters (zero between calls)
   int batch, n_kv_heads, n_q_heads;
   int n16, n4;
   int n_hi, pair_layout;
@@ -202,6 +201,7 @@ struct DecodeArgs {
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int n_pages, int batch, hipStream_t stream);
 hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s);
-int decode_pages_per_split(int n_pages, int batch, int n_kv_heads);
+constexpr int DECODE_SLOTS = 2048;
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, bool segment);
 
 }  // namespace kvq
