@@ -312,22 +312,54 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, con
   }
 }
 
-// log-sum-exp merge of the split partials: one workgroup per query head
-__global__ __launch_bounds__(128) void combine_kernel(const float* partial, float* out, int n_splits, int rows) {
-  const int row = blockIdx.x, ch = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, partial[((int64_t)s * rows + row) * RECORD]);
-  float l = 0.f, o = 0.f;
+// log-sum-exp merge of the split partials: one workgroup per query head.
+// Every part's (m, l) is read in parallel (one part per thread), the weights
+// 2^(m_s - M) go through LDS, then thread ch sums its channel over the parts
+// with independent loads.
+__global__ __launch_bounds__(128) void combine_kernel(const float* partial, float* out, int n_parts, int rows) {
+  const int row = blockIdx.x, t = threadIdx.x;
+  __shared__ float wsh[128];
+  __shared__ float red[4];
+  float mloc = -INFINITY;
+  for (int s = t; s < n_parts; s += 128) mloc = fmaxf(mloc, partial[((int64_t)s * rows + row) * RECORD]);
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  if ((t & 63) == 0) red[t >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  float l = 0.f, acc = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float* rec = partial + ((int64_t)s * rows + row) * RECORD;
-      if (rec[0] == -INFINITY) continue;
-      const float w = fast_exp2(rec[0] - M);
-      l = fmaf(w, rec[1], l);
-      o = fmaf(w, rec[2 + ch], o);
+    for (int s0 = 0; s0 < n_parts; s0 += 128) {
+      const int s = s0 + t;
+      float wv = 0.f;
+      if (s < n_parts) {
+        const float* rec = partial + ((int64_t)s * rows + row) * RECORD;
+        const float ms = rec[0];
+        wv = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+        l = fmaf(wv, rec[1], l);
+      }
+      __syncthreads();
+      wsh[t] = wv;
+      __syncthreads();
+      const int n = min(128, n_parts - s0);
+      const float* base = partial + ((int64_t)s0 * rows + row) * RECORD + 2 + t;
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        const float v0 = base[(int64_t)(j + 0) * rows * RECORD], v1 = base[(int64_t)(j + 1) * rows * RECORD];
+        const float v2 = base[(int64_t)(j + 2) * rows * RECORD], v3 = base[(int64_t)(j + 3) * rows * RECORD];
+        acc = fmaf(wsh[j], v0, acc);
+        acc = fmaf(wsh[j + 1], v1, acc);
+        acc = fmaf(wsh[j + 2], v2, acc);
+        acc = fmaf(wsh[j + 3], v3, acc);
+      }
+      for (; j < n; ++j) acc = fmaf(wsh[j], base[(int64_t)j * rows * RECORD], acc);
     }
   }
-  out[(int64_t)row * D + ch] = l > 0.f ? o / l : 0.f;
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  __syncthreads();
+  if ((t & 63) == 0) red[2 + (t >> 6)] = l;
+  __syncthreads();
+  const float L = red[2] + red[3];
+  out[(int64_t)row * D + t] = L > 0.f ? acc / L : 0.f;
 }
 
 bool launch_decode_fast(int key_mode, const DecodeArgs& a, dim3 grid, hipStream_t s);

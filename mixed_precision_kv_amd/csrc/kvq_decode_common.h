@@ -238,9 +238,12 @@ __device__ inline bf16x8 as_bf16x8(const u32x4& v) {
   return r;
 }
 
-// BF16 segment (attention sinks + residual), one wave: q.k on the bf16 MFMA
-// (exact products), probabilities staged in LDS, p.V on the VALU with each
-// lane owning two channels. Writes the split's partial record.
+// BF16 segment (attention sinks + residual), one wave, in chunks of 32
+// tokens: all Key and Value loads of a chunk are issued together; q.k runs on
+// the bf16 MFMA (exact products); each lane turns its own 8 logits into
+// probabilities against the running per-head maximum and stages them in LDS;
+// p.V runs on the VALU with each lane owning two channels of every head.
+// Writes the split's partial record. p_lds needs 32 x 8 floats, mh 16.
 template <int G>
 __device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int kvh, int lane, float (*p_lds)[8],
                                     float* mh) {
@@ -254,60 +257,85 @@ __device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int k
     u32x4 raw = ld16(reinterpret_cast<const uint8_t*>(qrow + 32 * ks + 8 * a));
     __builtin_memcpy(&Bq[ks], &raw, 16);
   }
-  float mloc = -INFINITY;
-  const int nt = (T + 15) / 16;
-  for (int i = 0; i < nt; ++i) {
-    const int t = 16 * i + r;                // A row = token
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (t < A.n_sink)
-        raw = ld16(reinterpret_cast<const uint8_t*>(A.sink_k + (head * A.n_sink + t) * D + 32 * ks + 8 * a));
-      else if (t < T)
-        raw = ld16(reinterpret_cast<const uint8_t*>(A.resid_k + (head * A.resid_stride + (t - A.n_sink)) * D +
-                                                    32 * ks + 8 * a));
-      bf16x8 Ak;
-      __builtin_memcpy(&Ak, &raw, 16);
-      acc = mfma_bf(Ak, Bq[ks], acc);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tok = 16 * i + 4 * a + e;
-      const float x = tok < T ? acc[e] * A.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, x);
-      if (col < G) p_lds[tok][col] = x;
-    }
-  }
-  const float m = wave_max_groups(mloc);
-  if (a == 0 && col < G) mh[col] = m;
-  __syncthreads();
-  for (int idx = lane; idx < 16 * nt * G; idx += 64) {
-    const int tok = idx / G, hh = idx % G;
-    p_lds[tok][hh] = tok < T ? fast_exp2(p_lds[tok][hh] - mh[hh]) : 0.f;
-  }
-  __syncthreads();
+  float m_run = -INFINITY;                   // running max of this lane's head (log2 domain)
   float o[G][2], lsum[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) o[hh][0] = o[hh][1] = lsum[hh] = 0.f;
-  for (int t = 0; t < T; ++t) {              // lane owns channels 2 lane, 2 lane + 1
-    const uint16_t* vrow = t < A.n_sink ? A.sink_v + (head * A.n_sink + t) * D
-                                        : A.resid_v + (head * A.resid_stride + (t - A.n_sink)) * D;
-    const uint32_t w = reinterpret_cast<const uint32_t*>(vrow)[lane];
-    const float v0 = lo_bf(w), v1 = hi_bf(w);
+  for (int t0 = 0; t0 < T; t0 += 32) {
+    u32x4 kr[2][4];
+    uint32_t vr[32];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int t = t0 + 16 * i2 + r;        // A row = token
+      const uint16_t* krow = t < A.n_sink ? A.sink_k + (head * A.n_sink + t) * D
+                                          : A.resid_k + (head * A.resid_stride + (t - A.n_sink)) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kr[i2][ks] = t < T ? ld16(reinterpret_cast<const uint8_t*>(krow + 32 * ks + 8 * a)) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int t = t0 + j;
+      const uint16_t* vrow = t < A.n_sink ? A.sink_v + (head * A.n_sink + t) * D
+                                          : A.resid_v + (head * A.resid_stride + (t - A.n_sink)) * D;
+      vr[j] = t < T ? reinterpret_cast<const uint32_t*>(vrow)[lane] : 0u;
+    }
+    float x[2][4];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 Ak;
+        __builtin_memcpy(&Ak, &kr[i2][ks], 16);
+        acc = mfma_bf(Ak, Bq[ks], acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = t0 + 16 * i2 + 4 * a + e;
+        x[i2][e] = tok < T ? acc[e] * A.scale_log2 : -INFINITY;
+        cm = fmaxf(cm, x[i2][e]);
+      }
+    }
+    const float m_new = fmaxf(m_run, wave_max_groups(cm));   // finite: the chunk has a token
+    const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    if (col < G) {
+#pragma unroll
+      for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p_lds[16 * i2 + 4 * a + e][col] = fast_exp2(x[i2][e] - m_new);
+      if (a == 0) mh[col] = alpha;
+    }
+    __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float pp = p_lds[t][hh];
-      o[hh][0] = fmaf(pp, v0, o[hh][0]);
-      o[hh][1] = fmaf(pp, v1, o[hh][1]);
-      lsum[hh] += pp;
+      const float al = mh[hh];
+      o[hh][0] *= al;
+      o[hh][1] *= al;
+      lsum[hh] *= al;
     }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float v0 = lo_bf(vr[j]), v1 = hi_bf(vr[j]);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float pp = p_lds[j][hh];
+        o[hh][0] = fmaf(pp, v0, o[hh][0]);
+        o[hh][1] = fmaf(pp, v1, o[hh][1]);
+        lsum[hh] += pp;
+      }
+    }
+    __syncthreads();
   }
+  if (a == 0 && col < G) mh[8 + col] = m_run;
+  __syncthreads();
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     float* rec = A.partial + (((int64_t)split * A.batch + b) * A.n_q_heads + kvh * G + hh) * RECORD;
     if (lane == 0) {
-      rec[0] = T > 0 ? mh[hh] : -INFINITY;
+      rec[0] = mh[8 + hh];
       rec[1] = lsum[hh];
     }
     rec[2 + 2 * lane] = o[hh][0];
