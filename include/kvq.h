@@ -29,10 +29,14 @@
  *
  * Fixed geometry: head_dim D = 128; a page holds G_K = R = 128 tokens (one
  * Key group per channel per page); Values use 32-channel groups at 2 bits.
- * All model tensors are bfloat16; metadata scales/offsets are bfloat16
- * (scale = the bf16 nearest to the exact (max-min)/(2^b-1), offset = the
- * exact minimum; a constant group stores scale +0.0, codes 0); QJL norms
- * are binary16. Decode outputs are float32.
+ * All model tensors are bfloat16. Quantization scales/offsets are IEEE
+ * binary16, as the PN-Mix GPU run ("本地复现") and the KIVI storage budget
+ * (section 7) keep them: scale = the binary16 nearest to the exact
+ * (max-min)/(2^b-1), offset = the binary16 nearest to the group minimum
+ * (exact for bf16 inputs inside the binary16 range); a constant group stores
+ * scale +0.0, codes 0; a scale or offset beyond the binary16 range is stored
+ * as infinity and reported with KVQ_FLAG_RANGE. QJL norms are binary16.
+ * Decode outputs are float32.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -73,6 +77,7 @@ typedef enum kvq_pair_layout {
 #define KVQ_FLAG_NONFINITE 1u   /* a non-finite input was seen; that group's codes are unspecified */
 #define KVQ_FLAG_SPAN 2u        /* a group spans more than 38 binades; its codes may be off by one */
 #define KVQ_FLAG_MASK 4u        /* a PN-Mix record selects a pair count other than n_hi_pairs */
+#define KVQ_FLAG_RANGE 8u       /* a group's scale or offset exceeds the binary16 range (stored as inf) */
 
 /* Plain-old-data configuration, passed by pointer to every call. */
 typedef struct kvq_config {

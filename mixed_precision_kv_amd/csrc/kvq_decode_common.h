@@ -71,6 +71,13 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_bf(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// 8 binary16 values (scales or offsets of 8 slots / tokens) from 16 bytes
+__device__ inline half8 as_half8(const u32x4& v) {
+  half8 h;
+  __builtin_memcpy(&h, &v, 16);
+  return h;
+}
+
 // hi/lo f16 split of 8 products
 __device__ inline void split8(const float* x, half8& hi, half8& lo) {
   for (int e = 0; e < 8; ++e) {
@@ -138,16 +145,13 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const uint8_t* mb = vmeta + 512 * ks + 128 * a + 32 * j;
-      const u32x4 sw = ld16(mb), zw = ld16(mb + 16);
+      const half8 s8 = as_half8(ld16(mb)), z8 = as_half8(ld16(mb + 16));
       half8 B;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = rd(sw, e >> 1), zz = rd(zw, e >> 1);
-        const float s = (e & 1) ? hi_bf(w) : lo_bf(w);
-        const float z = (e & 1) ? hi_bf(zz) : lo_bf(zz);
         const float pe = p[2 * ks + (e >> 2)][e & 3];     // token pi(ks, a, e)
-        B[e] = (_Float16)(pe * s);
-        st.z[P] = fmaf(pe, z, st.z[P]);
+        B[e] = (_Float16)fmaf(pe, (float)s8[e], 0.0f);   // one v_fma_mix (f16 source and result)
+        st.z[P] = fmaf(pe, (float)z8[e], st.z[P]);
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {            // value tiles 2w, 2w+1 hold group w
@@ -209,27 +213,30 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
 
 
 // Key slot operand for k-step ks: B = q * s * 2^-6 (hi/lo), bias += q . z
+// (s, z binary16; q * s has at most 8 + 11 significant bits, so hi + lo
+// carry it exactly unless it leaves the binary16 range)
 __device__ inline void key_operand(const float* qv, const u32x4& sw, const u32x4& zw, half8& hi, half8& lo,
                                    float& bias) {
+  const half8 s8 = as_half8(sw), z8 = as_half8(zw);
   float prod[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t w = rd(sw, e >> 1), z = rd(zw, e >> 1);
-    prod[e] = qv[e] * ((e & 1) ? hi_bf(w) : lo_bf(w)) * B_SCALE;
-    bias = fmaf(qv[e], (e & 1) ? hi_bf(z) : lo_bf(z), bias);
+    prod[e] = qv[e] * (float)s8[e] * B_SCALE;
+    bias = fmaf(qv[e], (float)z8[e], bias);
   }
   split8(prod, hi, lo);
 }
 
 // Key slot operand from pre-scaled query values (q * 2^-6): B = q * s (hi/lo)
 __device__ inline void key_operand_scaled(const float* qv, const u32x4& sw, half8& hi, half8& lo) {
-  float prod[8];
+  const half8 s8 = as_half8(sw);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t w = rd(sw, e >> 1);
-    prod[e] = qv[e] * ((e & 1) ? hi_bf(w) : lo_bf(w));
+    // q * s is exact in float (8 + 11 bits); both halves are single v_fma_mix
+    const _Float16 h = (_Float16)fmaf(qv[e], (float)s8[e], 0.0f);
+    hi[e] = h;
+    lo[e] = (_Float16)fmaf(qv[e], (float)s8[e], -(float)h);
   }
-  split8(prod, hi, lo);
 }
 
 __device__ inline bf16x8 as_bf16x8(const u32x4& v) {

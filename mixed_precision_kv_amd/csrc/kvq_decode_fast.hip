@@ -47,7 +47,7 @@ struct PgSmem {
   union {
     struct {
       float qslot[NKS][4][G][8];   // [k-step][lane group][head][e]: q * 2^-6 of the slot's channel
-      bf16x8 qz[NKS][4][G];        // raw bf16 q of the slot's channel (offset MFMA operand)
+      half8 qz[NKS][4][G];         // q of the slot's channel as binary16 (offset MFMA operand)
       uint8_t meta[2][META_SLOT];  // double-buffered page metadata
     } pg;
     float p_lds[256][8];
@@ -137,7 +137,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
     half8 Bhi, Blo;
     key_operand_scaled(S.u.pg.qslot[ks][a][h], sw, Bhi, Blo);
-    zacc = mfma_bf(as_bf16x8(zw), S.u.pg.qz[ks][a][h], zacc);
+    zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       half8 A0, A1;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     const int ch = S.slot_ch[8 * (4 * ks + aa) + e];
     const float qf = ch >= 0 ? qb_at(qb, hh, ch) : 0.f;
     S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
-    S.u.pg.qz[ks][aa][hh][e] = (__bf16)qf;     // exact: q is bf16
+    S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
   }
   bf16x8 Bq;
 #pragma unroll
@@ -298,7 +298,7 @@ __device__ inline void pn_page(SoftState<NPASS>& st, const PnCodes& c, const uin
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
     half8 Bhi, Blo;
     key_operand_scaled(S.u.pg.qslot[ks][a][h], sw, Bhi, Blo);
-    zacc = mfma_bf(as_bf16x8(zw), S.u.pg.qz[ks][a][h], zacc);
+    zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {        // LSB plane: 1-bit codes, weight s
       half8 At[4];
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
     const float qf = qb_at(qb, hh, S.slot_ch[8 * (4 * ks + aa) + e]);
     S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
-    S.u.pg.qz[ks][aa][hh][e] = (__bf16)qf;
+    S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;
   }
   __syncthreads();
 

@@ -13,8 +13,10 @@
 // Exactness. Codes are round-half-even of the exact (2^b-1)(x-m)/(M-m): an
 // estimate from a reciprocal is corrected by comparing 2(2^b-1)(x-m) with
 // (2c+-1)(M-m) in double precision, exact while a group spans at most 38
-// binades (checked; KVQ_FLAG_SPAN otherwise). Scales are the bf16 nearest to
-// the exact quotient (one rounding from a correctly rounded double).
+// binades (checked; KVQ_FLAG_SPAN otherwise). Scales and offsets are the
+// binary16 nearest to the exact values (one rounding from a double that is
+// either exact or correctly rounded and never a binary16 midpoint); values
+// beyond the binary16 range are stored as infinity with KVQ_FLAG_RANGE.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -26,8 +28,8 @@ struct GroupParam {
   float m;         // group minimum (exact bf16 value)
   float M;         // group maximum
   float inv;       // levels / (M - m), an estimate used before the exact fix-up
-  uint16_t scale;  // stored bf16 scale
-  uint16_t offset; // stored bf16 offset
+  uint16_t scale;  // stored binary16 scale
+  uint16_t offset; // stored binary16 offset
 };
 
 // value token t of a page lives at src[(base + t) * 128 + d]
@@ -70,10 +72,10 @@ __device__ inline void scan_merge_xor(Scan& s, int mask) {
   s.nonfinite = s.nonfinite || __shfl_xor((int)s.nonfinite, mask);
 }
 
-__device__ inline uint16_t bf16_bits_of(float v) {
-  union { float f; uint32_t u; } c;
-  c.f = v;
-  return (v == 0.0f) ? (uint16_t)0 : (uint16_t)(c.u >> 16);
+__device__ inline bool f16_is_inf(uint16_t h) { return (h & 0x7FFF) == 0x7C00; }
+
+__device__ inline void flag_range(const GroupParam& p, unsigned* flags) {
+  if (f16_is_inf(p.scale) || f16_is_inf(p.offset)) atomicOr(flags, KVQ_FLAG_RANGE);
 }
 
 // min-max quantizer parameters for `levels` = 2^b - 1
@@ -81,16 +83,18 @@ __device__ inline GroupParam make_param(const Scan& s, int levels, unsigned* fla
   GroupParam p;
   p.m = s.mn;
   p.M = s.mn;
-  p.offset = bf16_bits_of(s.mn);
+  p.offset = s.mn == INFINITY ? (uint16_t)0 : f64_to_f16_rne((double)s.mn);
   p.inv = 0.0f;
   p.scale = 0;
   if (s.nonfinite) atomicOr(flags, KVQ_FLAG_NONFINITE);
   if (s.emax - s.emin > 38) atomicOr(flags, KVQ_FLAG_SPAN);
-  if (!(s.mx > s.mn)) return p;   // constant group (or non-finite)
-  p.M = s.mx;
-  double den = (double)s.mx - (double)s.mn;
-  p.inv = (float)((double)levels / den);
-  p.scale = f64_to_bf16_rne(den / (double)levels);
+  if (s.mx > s.mn) {
+    p.M = s.mx;
+    const double den = (double)s.mx - (double)s.mn;
+    p.inv = (float)((double)levels / den);
+    p.scale = f64_to_f16_rne(den / (double)levels);
+  }
+  flag_range(p, flags);
   return p;
 }
 
@@ -101,14 +105,16 @@ __device__ inline GroupParam make_param_mid(const Scan& s, unsigned* flags) {
   p.M = s.mn;
   p.inv = 0.0f;
   p.scale = 0;
-  p.offset = bf16_bits_of(s.mn);
+  p.offset = s.mn == INFINITY ? (uint16_t)0 : f64_to_f16_rne((double)s.mn);
   if (s.nonfinite) atomicOr(flags, KVQ_FLAG_NONFINITE);
   if (s.emax - s.emin > 38) atomicOr(flags, KVQ_FLAG_SPAN);
-  if (!(s.mx > s.mn)) return p;
-  p.M = s.mx;
-  double den = (double)s.mx - (double)s.mn;
-  p.scale = f64_to_bf16_rne(0.5 * den);
-  p.offset = f64_to_bf16_rne(0.25 * (3.0 * (double)s.mn + (double)s.mx));
+  if (s.mx > s.mn) {
+    p.M = s.mx;
+    const double den = (double)s.mx - (double)s.mn;
+    p.scale = f64_to_f16_rne(0.5 * den);
+    p.offset = f64_to_f16_rne(0.25 * (3.0 * (double)s.mn + (double)s.mx));
+  }
+  flag_range(p, flags);
   return p;
 }
 
@@ -292,7 +298,8 @@ __global__ __launch_bounds__(256) void flush_mixkvq_kernel(FlushArgs A) {
         if (slot < 2 * g.n4) {
           const GroupParam& q = S.kp[g.n16 + (slot >> 1)];
           if (slot & 1) {
-            sc = q.scale == 0 ? 0 : f64_to_bf16_rne(4.0 * bf16_to_f64(q.scale));   // 4s, no offset
+            sc = q.scale == 0 ? 0 : f64_to_f16_rne(4.0 * f16_to_f64(q.scale));   // 4s, no offset
+            if (f16_is_inf(sc) && !half) atomicOr(A.flags, KVQ_FLAG_RANGE);
           } else {
             sc = q.scale;
             of = q.offset;

@@ -24,7 +24,7 @@ __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m *
 //  K_CODES: fragments of 8 slots x 128 tokens x 2 bits (256 B); slots are
 //           the low/high halves of every UINT4 code (padded to a multiple of
 //           8 slots) followed by the UINT2 codes
-//  K_META : per fragment 8 bf16 slot scales then 8 bf16 slot offsets
+//  K_META : per fragment 8 binary16 slot scales then 8 binary16 slot offsets
 struct MixGeo {
   int n16, n4, n2, s4, n_slots, F, off_codes, off_meta, off_v, used, stride;
 };
@@ -85,34 +85,48 @@ __host__ __device__ inline float bf16_to_f32(uint16_t b) {
 }
 __host__ __device__ inline double bf16_to_f64(uint16_t b) { return (double)bf16_to_f32(b); }
 
-// Correctly rounded (ties-to-even) bf16 of a finite double; zero -> +0.0.
-__host__ __device__ inline uint16_t f64_to_bf16_rne(double v) {
-  if (v == 0.0) return 0;
+// Correctly rounded (ties-to-even) IEEE binary16 of a double: subnormals
+// down to 2^-24, +-infinity past the largest finite value (65504), and +0.0
+// for a result that rounds to zero. A non-finite input maps to infinity of
+// its sign (NaN is not produced here: callers flag non-finite groups).
+__host__ __device__ inline uint16_t f64_to_f16_rne(double v) {
   union { double d; uint64_t u; } c;
   c.d = v;
-  uint64_t u = c.u;
-  uint16_t sign = (uint16_t)((u >> 48) & 0x8000);
-  int e = (int)((u >> 52) & 0x7FF) - 1023;
-  uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);   // 53 bits, value = sig * 2^(e-52)
-  int q_exp;          // exponent of the result quantum
-  if (e >= -126) q_exp = e - 7;
-  else q_exp = -133;
-  int shift = q_exp - (e - 52);                           // bits to drop from sig
+  const uint64_t u = c.u;
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000);
+  const int ef = (int)((u >> 52) & 0x7FF);
+  if (ef == 0x7FF) return (uint16_t)(sign | 0x7C00);
+  if (v == 0.0 || ef == 0) return 0;                      // zero and double subnormals (far below 2^-25)
+  const int e = ef - 1023;
+  if (e > 15) return (uint16_t)(sign | 0x7C00);
+  const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);   // value = sig * 2^(e-52)
+  const int q_exp = e >= -14 ? e - 10 : -24;             // exponent of the result quantum
+  const int shift = q_exp - (e - 52);                    // >= 42
   uint64_t q;
   if (shift >= 64) {
     q = 0;
   } else {
     q = sig >> shift;
-    uint64_t rem = sig & ((1ull << shift) - 1);
-    uint64_t half = 1ull << (shift - 1);
+    const uint64_t rem = sig & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
     if (rem > half || (rem == half && (q & 1))) q += 1;
   }
-  if (e >= -126) {
+  if (q == 0) return 0;
+  if (e >= -14) {
     int ex = e;
-    if (q == 256) { q = 128; ex += 1; }
-    return (uint16_t)(sign | ((uint16_t)(ex + 127) << 7) | (uint16_t)(q - 128));
+    if (q == 2048) { q = 1024; ex += 1; }
+    if (ex > 15) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | ((uint16_t)(ex + 15) << 10) | (uint16_t)(q - 1024));
   }
-  return (uint16_t)(sign | (uint16_t)q);   // q == 128 encodes the smallest normal
+  return (uint16_t)(sign | (uint16_t)q);   // q == 1024 encodes the smallest normal
+}
+
+__host__ __device__ inline double f16_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  const double s = (h & 0x8000) ? -1.0 : 1.0;
+  if (e == 0x1F) return m ? NAN : s * INFINITY;
+  if (e == 0) return s * (double)m * 0x1p-24;
+  return s * (double)(1024 + m) * __builtin_ldexp(1.0, e - 25);
 }
 
 // binary16 bit pattern of the correctly rounded sqrt(s) for an exact s >= 0

@@ -29,7 +29,7 @@ A 2-bit region stores fragment f (256 bytes) at 256*f.
 The value-code region (4096 bytes) holds, for k-step s < 4 and lane group
 a < 4, a 2-bit block at 1024*s + 256*a with X[r][u][k] = code of
 V[pi(s,a,k)][16*u + r], where pi(s,a,k) = 32*s + 16*(k//4) + 4*a + k%4. The
-value-meta region (2048 bytes) holds at 512*s + 128*a + 32*j the bf16 scales
+value-meta region (2048 bytes) holds at 512*s + 128*a + 32*j the f16 scales
 of V[pi(s,a,k)] for channel group j (k = 0..7) followed by their offsets.
 
 Status: the byte order is this library's own convention (parity unpinned as
@@ -40,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_fraction, rn_bf16_bits
+from .numerics import f16_fraction, rn_f16_meta_bits
 
 PAGE = 128
 D = 128
@@ -178,7 +178,7 @@ def _bytes_u16(b) -> np.ndarray:
 
 # --------------------------------------------------------------- value part
 def pack_v(vcodes, vscale, voff) -> np.ndarray:
-    """vcodes [128 t][128 ch] 2-bit; vscale/voff [128 t][4] bf16 bits."""
+    """vcodes [128 t][128 ch] 2-bit; vscale/voff [128 t][4] f16 bits."""
     codes = np.zeros(V_CODE_BYTES, np.uint8)
     meta = np.zeros(V_META_BYTES, np.uint8)
     for s in range(4):
@@ -231,8 +231,11 @@ def mixkvq_geometry(n16: int, n4: int):
                 off_meta=off_meta, off_v=off_v, used=used, stride=_round_up(used, 256))
 
 
-def _times4_bf16(bits: int) -> int:
-    return rn_bf16_bits(4 * bf16_fraction(bits))
+def _times4_f16(bits: int) -> int:
+    """binary16 of 4 s (exact unless it overflows to infinity)."""
+    if (bits & 0x7C00) == 0x7C00:
+        return bits
+    return rn_f16_meta_bits(4 * f16_fraction(bits))
 
 
 def pack_mixkvq_page(n16, n4, perm, kbits, k4, k2, v):
@@ -256,7 +259,7 @@ def pack_mixkvq_page(n16, n4, perm, kbits, k4, k2, v):
         slots[2 * j] = c4[j] & 3
         slots[2 * j + 1] = c4[j] >> 2
         sc[2 * j], of[2 * j] = s4v[j], o4v[j]
-        sc[2 * j + 1], of[2 * j + 1] = _times4_bf16(int(s4v[j])), 0
+        sc[2 * j + 1], of[2 * j + 1] = _times4_f16(int(s4v[j])), 0
     c2, s2v, o2v = k2
     for j in range(g["n2"]):
         slots[g["s4"] + j] = c2[j]
@@ -317,7 +320,7 @@ def pnmix_slot_channels(hi_mask_channels: np.ndarray):
 
 def pack_pnmix_page(hi_channels, codes, scale, offset, v):
     """codes [128 ch][128 t] (3-bit for high channels, 1-bit for low),
-    scale/offset [128 ch] bf16 bits, hi_channels bool [128]."""
+    scale/offset [128 ch] f16 bits, hi_channels bool [128]."""
     order, n_hi = pnmix_slot_channels(hi_channels)
     g = pnmix_geometry(n_hi)
     page = np.zeros(g["stride"], np.uint8)

@@ -52,7 +52,7 @@ def rne_div(num: int, den: int) -> int:
     return q
 
 
-def _round_to_format(x: Fraction, fmt) -> int:
+def _round_to_format(x: Fraction, fmt, overflow: str = "raise") -> int:
     p, emin, bias, ew = fmt
     if x == 0:
         return 0
@@ -81,6 +81,8 @@ def _round_to_format(x: Fraction, fmt) -> int:
         exp_field = e + bias
         mant = m - (1 << (p - 1))
     if exp_field >= (1 << ew) - 1:
+        if overflow == "inf":             # IEEE round-to-nearest overflow: +-infinity
+            return (sign << (ew + p - 1)) | (((1 << ew) - 1) << (p - 1))
         raise OverflowError("value out of range of the target format")
     return (sign << (ew + p - 1)) | (exp_field << (p - 1)) | mant
 
@@ -95,6 +97,29 @@ def rn_bf16_bits(x: Fraction) -> int:
 def rn_f16_bits(x: Fraction) -> int:
     """Bit pattern of the IEEE binary16 nearest to x (ties to even)."""
     return _round_to_format(Fraction(x), _F16)
+
+
+def rn_f16_meta_bits(x: Fraction) -> int:
+    """binary16 nearest to x (ties to even) as stored for a quantization scale
+    or offset: a value beyond the binary16 range becomes +-infinity (the
+    flush reports it), a result that rounds to zero is stored as +0.0."""
+    b = _round_to_format(Fraction(x), _F16, overflow="inf")
+    return 0 if (b & 0x7FFF) == 0 else b
+
+
+def f16_fraction(bits: int) -> Fraction:
+    """Exact value of one finite binary16 bit pattern."""
+    bits = int(bits) & 0xFFFF
+    if (bits & 0x7C00) == 0x7C00:
+        raise ValueError("non-finite f16")
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 10) & 0x1F
+    m = bits & 0x3FF
+    if e == 0:
+        return sign * Fraction(m, 1 << 24)
+    val = Fraction(1024 + m, 1024)
+    ex = e - 15
+    return sign * (val * (1 << ex) if ex >= 0 else val / (1 << -ex))
 
 
 def rn_f16_sqrt_bits(s: Fraction) -> int:

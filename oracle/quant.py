@@ -11,11 +11,15 @@ Readings fixed here (where the pages leave a step open):
 * the code is RNE of the EXACT rational (2^B - 1)(x - m)/(M - m), not of a
   division by an already rounded step (the KIVI teaching code divides by a
   float step; on its worked examples both agree);
-* scale is stored as bf16, the correctly rounded value of the exact real
-  (M - m)/(2^B - 1); offset is the group minimum copied exactly (bf16, the
-  input dtype, as the KIVI pack path allocates metadata in the input dtype);
+* scale and offset are stored as IEEE binary16: PN-Mix's GPU path keeps its
+  metadata in FP16 (section "本地复现"), and the KIVI blog's storage budget
+  (section 7) prices origin and step as FP16 each. The scale is the binary16
+  nearest to the exact real (M - m)/(2^B - 1) (ties to even); the offset is
+  the binary16 nearest to the group minimum, which is exact for bf16 inputs
+  inside the binary16 range. A scale or offset beyond that range is stored as
+  infinity (the flush raises a range flag for it);
 * a constant group (M == m) stores codes 0, scale +0.0 and offset m;
-* zero is stored as +0.0.
+* a zero scale or offset is stored as +0.0.
 
 1-bit midpoint correction (PN-Mix page "核心公式" Eq.7): s = (M - m)/2,
 z = (3m + M)/4 and q = clip(round((x - z)/s), 0, 1). Worked out exactly,
@@ -28,7 +32,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from .numerics import bf16_fraction, rn_bf16_bits
+from .numerics import bf16_fraction, f16_to_f64, rn_f16_meta_bits
 
 _SPAN_LIMIT = 48   # int64 path is exact while the group's binade span is <= this
 
@@ -73,16 +77,16 @@ def _rne_div_vec(num, den):
 
 
 def _min_bits(bits_row, X_row):
+    """binary16 offset bits of the row minimum (a bf16 input value)."""
     i = int(np.argmin(X_row))
-    b = int(bits_row[i])
-    return 0 if (b & 0x7FFF) == 0 else b
+    return rn_f16_meta_bits(bf16_fraction(int(bits_row[i])))
 
 
 def quantize_groups(bits: np.ndarray, nbits: int):
     """Quantize each row of ``bits`` (uint16 bf16 patterns, [n_groups, G]).
 
-    Returns (codes uint8 [n_groups, G], scale bf16 bits [n_groups],
-    offset bf16 bits [n_groups]). Exact: codes come from integer arithmetic
+    Returns (codes uint8 [n_groups, G], scale f16 bits [n_groups],
+    offset f16 bits [n_groups]). Exact: codes come from integer arithmetic
     on the exact values; the scale is rounded once from the exact rational."""
     bits = np.atleast_2d(np.asarray(bits, dtype=np.uint16))
     levels = (1 << nbits) - 1
@@ -102,15 +106,15 @@ def quantize_groups(bits: np.ndarray, nbits: int):
         offset[g] = _min_bits(bits[g], X[g])
         if not const[g]:
             exact = Fraction(int(den[g]), levels) * (Fraction(2) ** int(e0[g]))
-            scale[g] = rn_bf16_bits(exact)
+            scale[g] = rn_f16_meta_bits(exact)
     return codes.astype(np.uint8), scale, offset
 
 
 def quantize_groups_midpoint(bits: np.ndarray):
     """1-bit midpoint-corrected quantizer (PN-Mix Eq.7) on each row.
 
-    Returns (codes uint8, scale bf16 bits = RN((M-m)/2), offset bf16 bits =
-    RN((3m+M)/4)); a constant row gives codes 0, scale 0, offset m."""
+    Returns (codes uint8, scale f16 bits = RN((M-m)/2), offset f16 bits =
+    RN((3m+M)/4)); a constant row gives codes 0, scale 0, offset RN(m)."""
     bits = np.atleast_2d(np.asarray(bits, dtype=np.uint16))
     X, e0 = _exact_ints(bits)
     xmin = X.min(axis=1)
@@ -127,17 +131,17 @@ def quantize_groups_midpoint(bits: np.ndarray):
             offset[g] = _min_bits(bits[g], X[g])
             continue
         unit = Fraction(2) ** int(e0[g])
-        scale[g] = rn_bf16_bits(Fraction(int(den[g]), 2) * unit)
-        offset[g] = rn_bf16_bits(Fraction(3 * int(xmin[g]) + int(xmax[g]), 4) * unit)
+        scale[g] = rn_f16_meta_bits(Fraction(int(den[g]), 2) * unit)
+        offset[g] = rn_f16_meta_bits(Fraction(3 * int(xmin[g]) + int(xmax[g]), 4) * unit)
     return codes, scale, offset
 
 
 def dequantize(codes, scale_bits, offset_bits) -> np.ndarray:
     """x^ = offset + scale * code, in float64 (exact for these formats).
 
-    ``scale_bits``/``offset_bits`` broadcast against ``codes``."""
-    from .numerics import bf16_to_f64
-    return bf16_to_f64(offset_bits) + bf16_to_f64(scale_bits) * np.asarray(codes, dtype=np.float64)
+    ``scale_bits``/``offset_bits`` (binary16 patterns) broadcast against
+    ``codes``."""
+    return f16_to_f64(offset_bits) + f16_to_f64(scale_bits) * np.asarray(codes, dtype=np.float64)
 
 
 def quantize_group_reference(values, nbits: int):

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from oracle import layout
-from oracle.numerics import bf16_fraction, bf16_to_f64
+from oracle.numerics import bf16_fraction, bf16_to_f64, f16_fraction, f16_to_f64
 from oracle.quant import (dequantize, quantize_group_reference, quantize_groups,
                           quantize_groups_midpoint)
 
@@ -129,11 +129,13 @@ def test_error_bound_half_step(nbits):
     grid = m + codes * step
     assert np.all(np.abs(vals - grid) <= step / 2 * (1 + 1e-12))
     assert codes.max() <= (1 << nbits) - 1
-    # stored (bf16-rounded) scale: bound grows by at most (2^b-1)|s - step|
-    s = bf16_to_f64(scale)[:, None]
+    # stored (binary16-rounded) scale: bound grows by at most (2^b-1)|s - step|
+    s = f16_to_f64(scale)[:, None]
+    assert np.all(np.abs(s - step) <= step * 2.0 ** -11)
     rec = dequantize(codes, scale[:, None], offset[:, None])
     assert np.all(np.abs(vals - rec) <= step / 2 + ((1 << nbits) - 1) * np.abs(s - step) + 1e-12)
-    assert np.array_equal(bf16_to_f64(offset)[:, None], m)
+    # bf16 minima inside the binary16 range are stored exactly
+    assert np.array_equal(f16_to_f64(offset)[:, None], m)
 
 
 def test_rne_ties_go_to_even():
@@ -179,12 +181,23 @@ def test_brute_force_small_groups(nbits):
         assert codes[0].tolist() == _nearest_level_codes(vals, nbits)
         ref_codes, ref_step, ref_m = quantize_group_reference(vals, nbits)
         assert codes[0].tolist() == ref_codes
-        assert bf16_fraction(int(offset[0])) == ref_m
+        # metadata: numpy's own double -> binary16 rounding (ties to even,
+        # overflow to infinity) of the exact value; the exact value is not a
+        # binary16 midpoint to within double precision here
+        assert int(offset[0]) == _np_f16_bits(ref_m)
         if ref_step:
-            s = bf16_fraction(int(scale[0]))
-            # correctly rounded: no bf16 value is closer to the exact step
-            ulp = Fraction(2) ** (math.floor(math.log2(float(ref_step))) - 7)
-            assert abs(s - ref_step) <= ulp / 2
+            assert int(scale[0]) == _np_f16_bits(ref_step)
+            if abs(ref_step) < 65504:
+                s = f16_fraction(int(scale[0]))
+                # correctly rounded: no binary16 value is closer to the exact step
+                e = max(math.floor(math.log2(float(ref_step))), -14)
+                assert abs(s - ref_step) <= Fraction(2) ** (e - 10) / 2
+
+
+def _np_f16_bits(x) -> int:
+    with np.errstate(over="ignore"):
+        b = int(np.array([float(x)]).astype(np.float16).view(np.uint16)[0])
+    return 0 if (b & 0x7FFF) == 0 else b
 
 
 def test_exhaustive_two_bit_patterns():
@@ -219,14 +232,35 @@ def test_midpoint_one_bit():
     rec = np.where(codes == 1, hi_level, lo_level)
     assert np.all(np.abs(vals - rec) <= (M - m) / 4 * (1 + 1e-12))
     assert np.array_equal(codes == 1, 2 * (vals - m) > (M - m))
-    # stored levels are the bf16 roundings of z and z + s
-    z = bf16_to_f64(offset)[:, None]
-    s = bf16_to_f64(scale)[:, None]
-    assert np.all(np.abs(z - lo_level) <= np.abs(lo_level) * 2.0 ** -8)
-    assert np.all(np.abs(s - (M - m) / 2) <= (M - m) / 2 * 2.0 ** -8)
+    # stored levels are the binary16 roundings of z and s
+    z = f16_to_f64(offset)[:, None]
+    s = f16_to_f64(scale)[:, None]
+    assert np.all(np.abs(z - lo_level) <= np.maximum(np.abs(lo_level) * 2.0 ** -11, 2.0 ** -25))
+    assert np.all(np.abs(s - (M - m) / 2) <= (M - m) / 2 * 2.0 ** -11)
     # exact midpoint rounds half-to-even to code 0; constant group keeps origin
     c, s1, o1 = quantize_groups_midpoint(bf([0.0, 1.0, 2.0, 0.5, 1.5])[None, :])
     assert c[0].tolist() == [0, 0, 1, 0, 1]
-    assert bf16_fraction(int(s1[0])) == 1 and bf16_fraction(int(o1[0])) == Fraction(1, 2)
+    assert f16_fraction(int(s1[0])) == 1 and f16_fraction(int(o1[0])) == Fraction(1, 2)
     c, s2, o2 = quantize_groups_midpoint(bf([7.0] * 5)[None, :])
-    assert not c.any() and s2[0] == 0 and bf16_fraction(int(o2[0])) == 7
+    assert not c.any() and s2[0] == 0 and f16_fraction(int(o2[0])) == 7
+
+
+def test_f16_metadata_rounding_pins():
+    """IEEE binary16 facts the metadata rounding must reproduce: the largest
+    finite value, the overflow threshold (ties to even go to infinity),
+    subnormal ties, and +0.0 for results that round to zero."""
+    from oracle.numerics import rn_f16_meta_bits
+    assert rn_f16_meta_bits(Fraction(65504)) == 0x7BFF
+    assert rn_f16_meta_bits(Fraction(65519)) == 0x7BFF
+    assert rn_f16_meta_bits(Fraction(65520)) == 0x7C00          # tie -> even -> infinity
+    assert rn_f16_meta_bits(Fraction(-70000)) == 0xFC00
+    assert rn_f16_meta_bits(Fraction(1, 1 << 24)) == 0x0001      # smallest subnormal
+    assert rn_f16_meta_bits(Fraction(1, 1 << 25)) == 0            # tie -> even (zero)
+    assert rn_f16_meta_bits(Fraction(-1, 1 << 25)) == 0           # stored as +0.0
+    assert rn_f16_meta_bits(Fraction(3, 1 << 25)) == 0x0002      # tie between 1 and 2 quanta -> 2
+    assert rn_f16_meta_bits(Fraction(1, 3)) == 0x3555
+    assert f16_fraction(0x3555) == Fraction(1365, 4096)
+    # a group reaching beyond the binary16 range stores an infinite offset / scale
+    codes, scale, offset = quantize_groups(bf([-131072.0, 0.0, 131072.0, 5.0])[None, :], 2)
+    assert offset[0] == 0xFC00 and scale[0] == 0x7C00
+    assert codes[0].tolist() == [0, 2, 3, 2]
