@@ -362,20 +362,26 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* partial, floa
   out[(int64_t)row * D + t] = L > 0.f ? acc / L : 0.f;
 }
 
-bool launch_decode_fast(int key_mode, const DecodeArgs& a, dim3 grid, hipStream_t s);
+bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s);
 
 // Pages per split: the page splits of every (batch, kv head) plus, when the
 // call has sink or residual tokens, one BF16-segment workgroup per (batch, kv
-// head) are sized to fill DECODE_SLOTS single-wave workgroups (256 CUs x 8
-// resident waves on MI355X) in one round, with the pages spread evenly.
-int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, bool segment) {
+// head) are sized to fill `slots` resident workgroups in one round, with the
+// pages spread evenly. DECODE_SLOTS (256 CUs x 8 resident single-wave
+// workgroups on MI355X) bounds every kernel's split count, and the workspace
+// is sized for it.
+int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, bool segment, int slots) {
   const int64_t pairs = (int64_t)batch * n_kv_heads;
-  const int64_t budget = DECODE_SLOTS - (segment ? pairs : 0);
+  const int64_t budget = (int64_t)slots - (segment ? pairs : 0);
   int64_t splits = budget / pairs;
   if (splits < 1) splits = 1;
   int64_t pps = (n_pages + splits - 1) / splits;
   if (pps < 1) pps = 1;
   return (int)pps;
+}
+
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, bool segment) {
+  return decode_pages_per_split_slots(n_pages, batch, n_kv_heads, segment, DECODE_SLOTS);
 }
 
 template <int MODE>
@@ -390,7 +396,8 @@ static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s) {
+hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s) {
+  DecodeArgs a = args;
   const int g = a.n_q_heads / a.n_kv_heads;
   if (key_mode == KVQ_KEY_QJL) {
     hipLaunchKernelGGL(qjl_project_kernel, dim3(a.batch * a.n_q_heads), dim3(256), 0, s, a.q, qjl_s,
@@ -398,29 +405,28 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_parts = a.n_page_splits + (a.n_sink + a.n_resid > 0 ? 1 : 0);
-  if (n_parts == 0) {   // nothing to attend to: every output row is zero
+  const bool segment = a.n_sink + a.n_resid > 0;
+  if (a.n_page_splits + (segment ? 1 : 0) == 0) {   // nothing to attend to: every output row is zero
     hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, s, a.partial, a.out, 0,
                        a.batch * a.n_q_heads);
     return hipGetLastError();
   }
-  dim3 grid(n_parts, a.n_kv_heads, a.batch);
   hipError_t e = hipSuccess;
-  // The pipelined kernels cover the common shapes; KVQ_FORCE_GENERIC_DECODE
-  // selects the generic kernel (same results) so tests can exercise both.
-  const bool fast = getenv("KVQ_FORCE_GENERIC_DECODE") == nullptr && launch_decode_fast(key_mode, a, grid, s);
+  // The warp-specialised kernels cover the common shapes (and may choose
+  // their own split count); KVQ_FORCE_GENERIC_DECODE selects the generic
+  // kernel (same results) so tests can exercise both.
+  const bool fast = getenv("KVQ_FORCE_GENERIC_DECODE") == nullptr && launch_decode_fast(key_mode, a, s);
   if (fast) {
     e = hipGetLastError();
-  } else if (key_mode == KVQ_KEY_MIXKVQ) {
-    e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
-  } else if (key_mode == KVQ_KEY_PNMIX) {
-    e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
   } else {
-    e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
+    dim3 grid(a.n_page_splits + (segment ? 1 : 0), a.n_kv_heads, a.batch);
+    if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
+    else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
+    else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, s, a.partial, a.out,
-                     n_parts, a.batch * a.n_q_heads);
+                     a.n_page_splits + (segment ? 1 : 0), a.batch * a.n_q_heads);
   return hipGetLastError();
 }
 

@@ -130,28 +130,27 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
     st.m = mn;
   }
   const float shift = xb - st.m;
-  float p[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[i][e] = fast_exp2(fmaf(logit[i][e], xs, shift));
-      st.l += p[i][e];
-    }
   const int jl = col / G;
+  // k-step outer: the 8 probabilities of tiles 2ks, 2ks+1 are formed right
+  // before they are used (in every pass), so only 8 stay live at a time.
 #pragma unroll
-  for (int P = 0; P < NPASS; ++P) {
-    const int j = (jl + P * C) & 3;            // this lane's value group in pass P
+  for (int ks = 0; ks < 4; ++ks) {
+    float p[8];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(fmaf(logit[2 * ks + (e >> 2)][e & 3], xs, shift));   // token pi(ks, a, e)
+      st.l += p[e];
+    }
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) {
+      const int j = (jl + P * C) & 3;            // this lane's value group in pass P
       const uint8_t* mb = vmeta + 512 * ks + 128 * a + 32 * j;
       const half8 s8 = as_half8(ld16(mb)), z8 = as_half8(ld16(mb + 16));
       half8 B;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = p[2 * ks + (e >> 2)][e & 3];     // token pi(ks, a, e)
-        B[e] = (_Float16)fmaf(pe, (float)s8[e], 0.0f);   // one v_fma_mix (f16 source and result)
-        st.z[P] = fmaf(pe, (float)z8[e], st.z[P]);
+        B[e] = (_Float16)fmaf(p[e], (float)s8[e], 0.0f);   // one v_fma_mix (f16 source and result)
+        st.z[P] = fmaf(p[e], (float)z8[e], st.z[P]);
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {            // value tiles 2w, 2w+1 hold group w
@@ -181,7 +180,7 @@ template <int G, int NPASS>
 __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, int split, int b, int kvh, int a,
                                      int col, float* stage) {
   constexpr int C = 16 / G;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;   // lane within the calling wave
   const float l = wave_sum_groups(st.l);
   float z[NPASS];
 #pragma unroll
@@ -237,6 +236,35 @@ __device__ inline void key_operand_scaled(const float* qv, const u32x4& sw, half
     hi[e] = h;
     lo[e] = (_Float16)fmaf(qv[e], (float)s8[e], -(float)h);
   }
+}
+
+// Hi/lo column split (pipelined kernels): columns col < 8 carry the f16 hi
+// part of the Key operand, columns col >= 8 the lo part, so one MFMA per
+// tile covers both; the two partial logits are then added across the lanes
+// col and col ^ 8 of each 16-lane row (DPP row_ror:8).
+__device__ inline float from_partner8(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ inline void join_halves(f32x4 (&logit)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) logit[i][e] += from_partner8(logit[i][e]);
+}
+
+// This lane's half of B = q * s (q pre-scaled by 2^-6): hi part, or lo part
+__device__ inline half8 key_operand_half(const float* qv, const u32x4& sw, bool lo_col) {
+  const half8 s8 = as_half8(sw);
+  half8 B;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const _Float16 hh = (_Float16)fmaf(qv[e], (float)s8[e], 0.0f);
+    const _Float16 ll = (_Float16)fmaf(qv[e], (float)s8[e], -(float)hh);
+    B[e] = lo_col ? ll : hh;
+  }
+  return B;
 }
 
 __device__ inline bf16x8 as_bf16x8(const u32x4& v) {

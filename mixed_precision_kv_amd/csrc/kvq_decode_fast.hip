@@ -1,13 +1,21 @@
 // Software-pipelined decode kernels for the common shapes (GQA group 4 or 8,
 // the workloads' Key layouts). Same arithmetic as the generic kernel in
 // kvq_decode.hip (see there for the method and the MFMA conventions); what
-// differs is the memory pipeline:
+// differs is the memory pipeline and the MFMA column layout:
 //  * every loop index is a compile-time constant (templates on the number
 //    of Key k-steps and BF16-tier loads), so no runtime selects remain;
-//  * while page p is computed, page p+1 is already in flight: its code
-//    fragments are prefetched into registers and its scale/offset metadata
-//    is copied straight into a double-buffered LDS slot with
-//    global_load_lds_dwordx4 (no VGPRs), one wait per page.
+//  * MFMA columns 0-7 carry the f16 hi part of the Key operand and columns
+//    8-15 the lo part, so one MFMA per tile covers both halves; the partial
+//    logits are joined across lanes col and col ^ 8 (DPP);
+//  * while page p is computed, page p+1 is in flight. PN-Mix and QJL split
+//    the next page into a Key part (codes + metadata, requested before the
+//    Key phase) and a value part (requested between the phases, into the
+//    registers the previous value phase released); every load is
+//    unconditional and the metadata reaches LDS through registers, which
+//    keeps the compiler's wait counts exact. MixKVQ, whose larger Key part
+//    leaves no registers for that, copies its metadata straight into a
+//    double-buffered LDS slot with global_load_lds_dwordx4 and prefetches
+//    its codes into registers, one wait per page;
 //  * the first page's loads are issued before the per-split set-up (query
 //    staging, slot tables), so set-up and the first memory latency overlap;
 //  * LDS holds only what one split needs (about 14 KB for GQA group 8), so
@@ -92,6 +100,61 @@ __device__ inline float qb_at(const uint8_t* qb, int h, int ch) {
   return bf16_to_f32(reinterpret_cast<const uint16_t*>(qb)[h * D + ch]);
 }
 
+// A page's metadata in registers: 16 bytes of Key meta (or norms) and 32
+// bytes of value meta per lane, written to an LDS slot by commit_meta.
+__device__ inline void load_vmeta(u32x4 (&m)[3], const uint8_t* vmeta_g, int lane) {
+  m[1] = ld16(vmeta_g + 16 * lane);
+  m[2] = ld16(vmeta_g + 1024 + 16 * lane);
+}
+
+__device__ inline void commit_meta(const u32x4 (&m)[3], uint8_t* slot, int lane) {
+  *reinterpret_cast<u32x4*>(slot + 16 * lane) = m[0];
+  *reinterpret_cast<u32x4*>(slot + 1024 + 16 * lane) = m[1];
+  *reinterpret_cast<u32x4*>(slot + 2048 + 16 * lane) = m[2];
+}
+
+// ------------------------------------------------------------------ page loop
+// Two register sets per part, used alternately: the Key part of page p+1
+// (codes + metadata) is requested before page p's Key phase, the Value part
+// (value codes) between page p's Key and Value phases, i.e. into registers
+// that page p-1's Value phase has just released. Each part is in flight for
+// about one page of compute, and only one Value set is live in the Key phase.
+// Every load is unconditional (same count per page), which keeps the
+// compiler's wait counts exact.
+template <class KP, class VP, class LK, class LV, class PG>
+__device__ inline void page_loop(int np, KP (&k)[2], VP (&v)[2], LK load_k, LV load_v, PG page) {
+  for (int it = 0; it < np; it += 2) {
+    if (it + 1 < np) load_k(k[1], it + 1);
+    page(k[0], v[0], 0, [&] {
+      if (it + 1 < np) load_v(v[1], it + 1);
+    });
+    if (it + 1 >= np) break;
+    if (it + 2 < np) load_k(k[0], it + 2);
+    page(k[1], v[1], 1, [&] {
+      if (it + 2 < np) load_v(v[0], it + 2);
+    });
+  }
+}
+
+struct ValCodes {
+  u32x4 vc[4];
+};
+
+__device__ inline void load_vcodes(ValCodes& v, const uint8_t* page, int off_v, int a, int r) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) v.vc[ks] = ld16(page + off_v + 1024 * ks + 256 * a + 16 * r);
+}
+
+template <int G, int NPASS>
+__device__ inline void init_state(SoftState<NPASS>& st) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
 // ------------------------------------------------------------------ MixKVQ
 template <int NKS, int NB>
 struct MixCodes {
@@ -135,17 +198,14 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
   for (int ks = 0; ks < NKS; ++ks) {
     const uint8_t* km = slot + 32 * (4 * ks + a);
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
-    half8 Bhi, Blo;
-    key_operand_scaled(S.u.pg.qslot[ks][a][h], sw, Bhi, Blo);
+    const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       half8 A0, A1;
       expand2(rd(c.kc[ks], w), A0, A1);
-      logit[2 * w] = mfma(A0, Bhi, logit[2 * w]);
-      logit[2 * w] = mfma(A0, Blo, logit[2 * w]);
-      logit[2 * w + 1] = mfma(A1, Bhi, logit[2 * w + 1]);
-      logit[2 * w + 1] = mfma(A1, Blo, logit[2 * w + 1]);
+      logit[2 * w] = mfma(A0, B, logit[2 * w]);
+      logit[2 * w + 1] = mfma(A1, B, logit[2 * w + 1]);
     }
   }
   if constexpr (NB > 0) {
@@ -157,9 +217,10 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
         tmp[e] = e < NB ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1))) : (uint16_t)0;
       bf16x8 Ak;
       __builtin_memcpy(&Ak, tmp, 16);
-      logit[i] = mfma_bf(Ak, Bq, logit[i]);
+      logit[i] = mfma_bf(Ak, Bq, logit[i]);   // Bq is zero in the lo columns
     }
   }
+  join_halves(logit);
   consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot + 1024, a, col);
 }
 
@@ -224,7 +285,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   }
   bf16x8 Bq;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 ? qb_at(qb, h, bch[e]) * B_SCALE : 0.f);
+  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qb_at(qb, h, bch[e]) * B_SCALE : 0.f);
   __syncthreads();
 
   SoftState<NPASS> st;
@@ -261,68 +322,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
 }
 
 // ------------------------------------------------------------------ PN-Mix
-struct PnCodes {
+struct PnKey {
+  u32x4 m[3];
   u32x4 lsb[2];
   u32x4 up[2];
-  u32x4 vc[4];
 };
 
-__device__ inline void pn_load(PnCodes& c, const uint8_t* page, const PnGeo& g, int a, int r) {
+__device__ inline void pn_load_key(PnKey& c, const uint8_t* page, const PnGeo& g, int lane, int a, int r) {
+  c.m[0] = ld16(page + g.off_meta + 16 * (lane & 31));   // 512 B of slot scales/offsets (lanes 32+ repeat them)
+  load_vmeta(c.m, page + g.off_v + V_CODE_BYTES, lane);
 #pragma unroll
   for (int P2 = 0; P2 < 2; ++P2) c.lsb[P2] = ld16(page + 1024 * P2 + 256 * a + 16 * r);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int f = 4 * ks + a;
-    c.up[ks] = (u32x4){0u, 0u, 0u, 0u};
-    if (f < g.n_up_frag) c.up[ks] = ld16(page + g.off_up + 256 * f + 16 * r);
-  }
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
+  for (int ks = 0; ks < 2; ++ks) c.up[ks] = ld16(page + g.off_up + 256 * min(4 * ks + a, g.n_up_frag - 1) + 16 * r);
 }
 
-__device__ inline void pn_issue_meta(const uint8_t* page, uint8_t* slot, const PnGeo& g, int lane) {
-  if (lane < 32) async16(page + g.off_meta + 16 * lane, slot);   // 512 B of slot scales/offsets
-  issue_vmeta(page + g.off_v + V_CODE_BYTES, slot, lane);
-}
-
-template <int G, int NPASS>
-__device__ inline void pn_page(SoftState<NPASS>& st, const PnCodes& c, const uint8_t* slot,
-                               const PgSmem<G, 4>& S, float xs, float scale_log2, int a, int h, int col) {
-  f32x4 logit[8];
+template <int G>
+__device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, const uint8_t* slot,
+                               const PgSmem<G, 4>& S, int a, int h, int col) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+  zacc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const uint8_t* km = slot + 32 * (4 * ks + a);
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
-    half8 Bhi, Blo;
-    key_operand_scaled(S.u.pg.qslot[ks][a][h], sw, Bhi, Blo);
+    const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {        // LSB plane: 1-bit codes, weight s
       half8 At[4];
       expand1(rd(c.lsb[ks >> 1], 2 * (ks & 1) + q2), At);
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        logit[4 * q2 + T] = mfma(At[T], Bhi, logit[4 * q2 + T]);
-        logit[4 * q2 + T] = mfma(At[T], Blo, logit[4 * q2 + T]);
-      }
+      for (int T = 0; T < 4; ++T) logit[4 * q2 + T] = mfma(At[T], B, logit[4 * q2 + T]);
     }
     if (ks < 2) {                           // upper two bits of the high channels, weight 2 s
-      const half8 Uh = Bhi * (_Float16)2.0f, Ul = Blo * (_Float16)2.0f;
+      const half8 U = B * (_Float16)2.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         half8 A0, A1;
         expand2(rd(c.up[ks], w), A0, A1);
-        logit[2 * w] = mfma(A0, Uh, logit[2 * w]);
-        logit[2 * w] = mfma(A0, Ul, logit[2 * w]);
-        logit[2 * w + 1] = mfma(A1, Uh, logit[2 * w + 1]);
-        logit[2 * w + 1] = mfma(A1, Ul, logit[2 * w + 1]);
+        logit[2 * w] = mfma(A0, U, logit[2 * w]);
+        logit[2 * w + 1] = mfma(A1, U, logit[2 * w + 1]);
       }
     }
   }
-  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot + 1024, a, col);
+  join_halves(logit);
 }
 
 template <int G>
@@ -344,38 +389,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
-  // slot order: high channels ascending, then low ones. Lane d < D/2 owns
-  // channels d and d + 64 (half split) or 2d, 2d+1 (adjacent): find its rank.
   uint32_t bits[2];
   bits[0] = (uint32_t)rec[0] | (uint32_t)rec[1] << 8 | (uint32_t)rec[2] << 16 | (uint32_t)rec[3] << 24;
   bits[1] = (uint32_t)rec[4] | (uint32_t)rec[5] << 8 | (uint32_t)rec[6] << 16 | (uint32_t)rec[7] << 24;
 
-  PnCodes c0, c1;
-  pn_issue_meta(pages, S.u.pg.meta[0], g, lane);
-  pn_load(c0, pages, g, a, r);
+  PnKey kp[2];
+  ValCodes vp[2];
+  pn_load_key(kp[0], pages, g, lane, a, r);
+  load_vcodes(vp[0], pages, g.off_v, a, r);
 
   uint8_t* qb = S.u.pg.meta[1] + 1024;
   stage_q<G>(qv, qb, lane);
   {
+    // slot order: high channels ascending, then low ones; the slot of
+    // channel d counts the channels before it in its class
     const uint64_t mask = (uint64_t)bits[0] | (uint64_t)bits[1] << 32;   // pair p is high iff bit p
     const int nh = __builtin_popcountll(mask);                            // high pairs
-    // channel d -> pair; the slot of channel d counts the channels before it in its class
     for (int d = lane; d < D; d += 64) {
       const bool half = A.pair_layout == KVQ_PAIR_HALF_SPLIT;
       const int pair = half ? (d & 63) : (d >> 1);
       const bool hi = (mask >> pair) & 1;
-      // channels before d in the same class: for half split, pairs below (d & 63)
-      // in this half plus all of that class in the first half when d >= 64
-      int before;
       const uint64_t below = pair == 0 ? 0ull : (mask & ((1ull << pair) - 1));
-      if (half) {
-        const int cnt = __builtin_popcountll(below);
-        const int in_first = hi ? nh : 64 - nh;
-        before = (hi ? cnt : pair - cnt) + (d >= 64 ? in_first : 0);
-      } else {
-        const int cnt = __builtin_popcountll(below);
-        before = 2 * (hi ? cnt : pair - cnt) + (d & 1);
-      }
+      const int cnt = __builtin_popcountll(below);
+      int before;
+      if (half) before = (hi ? cnt : pair - cnt) + (d >= 64 ? (hi ? nh : 64 - nh) : 0);
+      else before = 2 * (hi ? cnt : pair - cnt) + (d & 1);
       S.slot_ch[hi ? before : 2 * nh + before] = d;
     }
   }
@@ -389,59 +427,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   __syncthreads();
 
   SoftState<NPASS> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  init_state<G, NPASS>(st);
   const float xs = A.scale_log2 * B_UNSCALE;
-
-  for (int it = 0; it < np; it += 2) {
-    if (it + 1 < np) {
-      pn_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.pg.meta[1], g, lane);
-      wait_vm<3>();
-      pn_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
-    } else {
-      wait_vm<0>();
-    }
-    pn_page<G, NPASS>(st, c0, S.u.pg.meta[0], S, xs, A.scale_log2, a, h, col);
-    if (it + 1 >= np) break;
-    if (it + 2 < np) {
-      pn_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, S.u.pg.meta[0], g, lane);
-      wait_vm<3>();
-      pn_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
-    } else {
-      wait_vm<0>();
-    }
-    pn_page<G, NPASS>(st, c1, S.u.pg.meta[1], S, xs, A.scale_log2, a, h, col);
-  }
+  page_loop(
+      np, kp, vp, [&](PnKey& k, int p) { pn_load_key(k, pages + (int64_t)p * A.page_stride, g, lane, a, r); },
+      [&](ValCodes& v, int p) { load_vcodes(v, pages + (int64_t)p * A.page_stride, g.off_v, a, r); },
+      [&](const PnKey& k, const ValCodes& v, int s, auto mid) {
+        uint8_t* slot = S.u.pg.meta[s];
+        commit_meta(k.m, slot, lane);
+        f32x4 logit[8], zacc;
+        pn_keys<G>(logit, zacc, k, slot, S, a, h, col);
+        mid();
+        consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, slot + 1024, a, col);
+      });
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
 }
 
 // ------------------------------------------------------------------ QJL (m = 256)
-struct QjCodes {
+struct QjKey {
+  u32x4 m[3];
   u32x4 bits[4];
-  u32x4 vc[4];
 };
 
-__device__ inline void qj_load(QjCodes& c, const uint8_t* page, const QjlGeo& g, int a, int r) {
+__device__ inline void qj_load_key(QjKey& c, const uint8_t* page, const QjlGeo& g, int lane, int a, int r) {
+  c.m[0] = ld16(page + g.off_norm + 16 * (lane & 15));     // 256 B of norms (lanes 16+ repeat them)
+  load_vmeta(c.m, page + g.off_v + V_CODE_BYTES, lane);
 #pragma unroll
   for (int P2 = 0; P2 < 4; ++P2) c.bits[P2] = ld16(page + 1024 * P2 + 256 * a + 16 * r);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
 }
 
-__device__ inline void qj_issue_meta(const uint8_t* page, uint8_t* slot, const QjlGeo& g, int lane) {
-  if (lane < 16) async16(page + g.off_norm + 16 * lane, slot);     // 256 B of norms
-  issue_vmeta(page + g.off_v + V_CODE_BYTES, slot, lane);
-}
-
-template <int G, int NPASS>
-__device__ inline void qj_page(SoftState<NPASS>& st, const QjCodes& c, const uint8_t* slot,
-                               const QjSmem<G>& S, float ssum, float xs, int a, int h, int col) {
-  f32x4 logit[8];
+// Estimator logits nu_t * (2 <Sq, bits_t> - sum Sq) of one page (before the
+// sqrt(pi/2)/m and softmax factors, which ride on xs).
+template <int G>
+__device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey& c, const uint8_t* slot, const QjSmem<G>& S,
+                               float ssum, int a, int h, int col) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -449,20 +469,18 @@ __device__ inline void qj_page(SoftState<NPASS>& st, const QjCodes& c, const uin
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int ks = 2 * P2 + hf;
-      const half8 Bh = S.u.qj.bq[0][ks][a][h], Bl = S.u.qj.bq[1][ks][a][h];
+      const half8 B = S.u.qj.bq[col >> 3][ks][a][h];   // hi part in columns < 8, lo part above
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         half8 At[4];
         expand1(rd(c.bits[P2], 2 * hf + q2), At);
 #pragma unroll
-        for (int T = 0; T < 4; ++T) {
-          logit[4 * q2 + T] = mfma(At[T], Bh, logit[4 * q2 + T]);
-          logit[4 * q2 + T] = mfma(At[T], Bl, logit[4 * q2 + T]);
-        }
+        for (int T = 0; T < 4; ++T) logit[4 * q2 + T] = mfma(At[T], B, logit[4 * q2 + T]);
       }
     }
   }
-  // nu_t * (2 <Sq, bits> - sum Sq); tokens 16 i + 4 a + e have their norms at 32 a + 4 i + e
+  join_halves(logit);
+  // tokens 16 i + 4 a + e have their norms at 32 a + 4 i + e
   const uint8_t* nb = slot + 64 * a;
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
@@ -480,7 +498,6 @@ __device__ inline void qj_page(SoftState<NPASS>& st, const QjCodes& c, const uin
       }
     }
   }
-  consume_values<G, NPASS>(st, logit, xs, 0.f, c.vc, slot + 1024, a, col);
 }
 
 template <int G>
@@ -499,9 +516,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
   const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
 
-  QjCodes c0, c1;
-  qj_issue_meta(pages, S.u.qj.meta[0], g, lane);
-  qj_load(c0, pages, g, a, r);
+  QjKey kp[2];
+  ValCodes vp[2];
+  qj_load_key(kp[0], pages, g, lane, a, r);
+  load_vcodes(vp[0], pages, g.off_v, a, r);
 
   const int hq = kvh * G + h;
   const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * A.qjl_m;
@@ -524,48 +542,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   __syncthreads();
 
   SoftState<NPASS> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  init_state<G, NPASS>(st);
   const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
-
-  for (int it = 0; it < np; it += 2) {
-    if (it + 1 < np) {
-      qj_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.qj.meta[1], g, lane);
-      wait_vm<3>();
-      qj_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
-    } else {
-      wait_vm<0>();
-    }
-    qj_page<G, NPASS>(st, c0, S.u.qj.meta[0], S, ssum, xs, a, h, col);
-    if (it + 1 >= np) break;
-    if (it + 2 < np) {
-      qj_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, S.u.qj.meta[0], g, lane);
-      wait_vm<3>();
-      qj_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
-    } else {
-      wait_vm<0>();
-    }
-    qj_page<G, NPASS>(st, c1, S.u.qj.meta[1], S, ssum, xs, a, h, col);
-  }
+  page_loop(
+      np, kp, vp, [&](QjKey& k, int p) { qj_load_key(k, pages + (int64_t)p * A.page_stride, g, lane, a, r); },
+      [&](ValCodes& v, int p) { load_vcodes(v, pages + (int64_t)p * A.page_stride, g.off_v, a, r); },
+      [&](const QjKey& k, const ValCodes& v, int s, auto mid) {
+        uint8_t* slot = S.u.qj.meta[s];
+        commit_meta(k.m, slot, lane);
+        f32x4 logit[8];
+        qj_keys<G>(logit, k, slot, S, ssum, a, h, col);
+        mid();
+        consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, slot + 1024, a, col);
+      });
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
 }
 
 // ------------------------------------------------------------------ dispatch
-template <int G, int NKS>
-static bool launch_mix_nb(const DecodeArgs& a, int nb, dim3 grid, hipStream_t s) {
-  if (nb == 0) hipLaunchKernelGGL((decode_mix_fast<G, NKS, 0>), grid, dim3(64), 0, s, a);
-  else if (nb == 1) hipLaunchKernelGGL((decode_mix_fast<G, NKS, 1>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((decode_mix_fast<G, NKS, 8>), grid, dim3(64), 0, s, a);
-  return true;
+template <class K>
+static void launch1(K kernel, const DecodeArgs& a, hipStream_t s) {
+  const int n_parts = a.n_page_splits + (a.n_sink + a.n_resid > 0 ? 1 : 0);
+  hipLaunchKernelGGL(kernel, dim3(n_parts, a.n_kv_heads, a.batch), dim3(64), 0, s, a);
 }
 
-// Returns true when a pipelined kernel covers the configuration.
-bool launch_decode_fast(int key_mode, const DecodeArgs& a, dim3 grid, hipStream_t s) {
+template <int G, int NKS>
+static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
+  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0>, a, s);
+  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1>, a, s);
+  else launch1(decode_mix_fast<G, NKS, 8>, a, s);
+}
+
+// Launches the pipelined kernel when one covers the configuration (with the
+// split geometry in `a`); returns false (nothing launched) otherwise.
+bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (g != 4 && g != 8) return false;
   if (key_mode == KVQ_KEY_MIXKVQ) {
@@ -574,24 +584,26 @@ bool launch_decode_fast(int key_mode, const DecodeArgs& a, dim3 grid, hipStream_
     if (a.n16 > 8) return false;   // the fast path keeps the BF16 tier in lane group 0 (<= 8 channels)
     const int nb = a.n16 == 0 ? 0 : (a.n16 == 1 ? 1 : 8);
     if (nks == 5) {
-      if (g == 4) return launch_mix_nb<4, 5>(a, nb, grid, s);
-      return launch_mix_nb<8, 5>(a, nb, grid, s);
+      if (g == 4) launch_mix_nb<4, 5>(a, nb, s);
+      else launch_mix_nb<8, 5>(a, nb, s);
+      return true;
     }
     if (nks == 4) {
-      if (g == 4) return launch_mix_nb<4, 4>(a, nb, grid, s);
-      return launch_mix_nb<8, 4>(a, nb, grid, s);
+      if (g == 4) launch_mix_nb<4, 4>(a, nb, s);
+      else launch_mix_nb<8, 4>(a, nb, s);
+      return true;
     }
     return false;
   }
   if (key_mode == KVQ_KEY_PNMIX) {
     if (a.n_hi != 64) return false;
-    if (g == 4) hipLaunchKernelGGL((decode_pn_fast<4>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((decode_pn_fast<8>), grid, dim3(64), 0, s, a);
+    if (g == 4) launch1(decode_pn_fast<4>, a, s);
+    else launch1(decode_pn_fast<8>, a, s);
     return true;
   }
   if (a.qjl_m != 256) return false;
-  if (g == 4) hipLaunchKernelGGL((decode_qjl_fast<4>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((decode_qjl_fast<8>), grid, dim3(64), 0, s, a);
+  if (g == 4) launch1(decode_qjl_fast<4>, a, s);
+  else launch1(decode_qjl_fast<8>, a, s);
   return true;
 }
 

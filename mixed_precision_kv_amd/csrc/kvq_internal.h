@@ -217,5 +217,6 @@ hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream
 hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s);
 constexpr int DECODE_SLOTS = 2048;
 int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, bool segment);
+int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, bool segment, int slots);
 
 }  // namespace kvq
