@@ -12,10 +12,25 @@ Prints one JSON line. `value` is the step's algorithmic packed-KV bytes
 (decode reads + flush reads and writes) divided by the step time; the
 decode-only GB/s, its fraction of the 8 TB/s HBM peak and the flush rate in
 tokens/s are reported beside it, as is the CPU oracle on a bounded sample.
+The roofline object is the decode call (decode kernel + split combine),
+timed with HIP events on the stream the library launches on; its `traffic`
+comes from profiles/decode_llama8b_8k_traffic.txt (rocprofv3 FETCH_SIZE / WRITE_SIZE
+of the decode kernel, calibrated on a plain copy) and is null when the
+decode sources changed since those counters were taken.
+
+Helper modes used to make the committed profiles:
+  --copy-calibration MB   run torch's copy kernel on MB megabytes (for the
+                          counter calibration run under rocprofv3 --pmc)
+  --summarize-pmc FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR MB
+                          turn the four counter runs into
+                          profiles/decode_llama8b_8k_traffic.txt
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -23,6 +38,10 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_SOURCES = ["mixed_precision_kv_amd/csrc/kvq_decode_fast.hip", "mixed_precision_kv_amd/csrc/kvq_decode.hip",
+                  "mixed_precision_kv_amd/csrc/kvq_decode_common.h", "mixed_precision_kv_amd/csrc/kvq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_8k_traffic.txt")
 METRIC = "quantized decode-attn packed-KV GB/s (% of HBM peak); flush tokens/s"
 
 
@@ -59,6 +78,65 @@ def flush_bytes(w) -> int:
     return heads * (128 * 128 * 2 * 2 + rec + logical_page_bytes(w))
 
 
+def decode_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per decode-kernel launch from the committed counter runs, or
+    None when they are missing, for another workload, or older than the
+    decode sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("decode_source_sha256") != decode_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _pmc_rows(d, counter):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernel, each
+    scaled by what the counter reads for torch's copy of a known size."""
+    def avg(rows, pred):
+        v = [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+    is_dec = lambda n: "decode_" in n and "kvq::" in n
+    is_copy = lambda n: "copybuffer" in n.lower()   # the runtime's blit kernel behind copy_()
+    fk, nf = avg(_pmc_rows(fetch_dir, "FETCH_SIZE"), is_dec)
+    wk, nw = avg(_pmc_rows(write_dir, "WRITE_SIZE"), is_dec)
+    cf, _ = avg(_pmc_rows(copy_fetch_dir, "FETCH_SIZE"), is_copy)
+    cw, _ = avg(_pmc_rows(copy_write_dir, "WRITE_SIZE"), is_copy)
+    nbytes = copy_mb * 2 ** 20
+    f_fac = cf * 1024 / nbytes
+    w_fac = cw * 1024 / nbytes
+    fetch = fk * 1024 / f_fac
+    write = wk * 1024 / w_fac
+    import kvq_synth as synth
+    w = synth.WORKLOADS[workload]
+    out = {"workload": workload, "decode_source_sha256": decode_source_sha(),
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": [nf, nw],
+           "copy_bytes": nbytes, "copy_fetch_factor": f_fac, "copy_write_factor": w_fac,
+           "fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write,
+           "algorithmic_bytes_per_launch": decode_bytes(w)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,6 +147,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="qwen32b_32k", help="extra decode-only workload ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--decode-only", action="store_true", help="time the decode call only (for counter runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                          "COPY_WRITE_DIR", "MB"))
     return ap.parse_args()
 
 
@@ -194,6 +276,10 @@ def cpu_baseline(w, synth, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        d = args.summarize_pmc
+        summarize_pmc(d[0], d[1], d[2], d[3], int(d[4]), args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is "
               "described in DESIGN.md but not run", file=sys.stderr)
@@ -202,6 +288,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
     import kvq_synth as synth
     import mixed_precision_kv_amd as kvq
     kvq.load()
@@ -211,6 +306,10 @@ def main():
     copies = args.rotate or max(1, math.ceil(400.0 / cache_mb))
     print(f"[bench] {w.name}: {cache_mb:.1f} MB per decode, rotating {copies} copies", file=sys.stderr, flush=True)
     rig = Rig(w, copies, torch, kvq, synth)
+    if args.decode_only:
+        _, dec, _ = time_steps(rig, torch, args.steps, args.warmup, with_flush=False)
+        print(json.dumps({"workload": w.name, "decode_ms": sum(dec) / len(dec)}))
+        return
     wall, dec, fl = time_steps(rig, torch, args.steps, args.warmup, with_flush=True)
     dbytes, fbytes = decode_bytes(w), flush_bytes(w)
     ms_step = wall / args.steps * 1e3
@@ -260,7 +359,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA operands, f32 accumulate and softmax",
+        "dtype": "f16/f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "quantized_tokens": w.n_pages * 128, "residual_tokens": w.n_resid,
@@ -273,8 +372,9 @@ def main():
         "flush_tokens_per_s": flush_tok_s,
         "flush_ms": fl_ms,
         "roofline": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "decode_kernel", "bytes_per_launch": dbytes},
+                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": committed_traffic(w.name),
+                     "kernel": "kvq_decode_attention (decode_mix_fast + combine_kernel)",
+                     "bytes_per_launch": dbytes},
         "secondary": extra,
         "cpu_baseline": cpu,
     }
