@@ -5,10 +5,11 @@
 // Values per token over groups of 32 channels. PN-Mix Eq.2/Eq.7 and
 // Appendix G planes. QJL Algorithm 1 steps 2-3 (sign(S k) and ||k||).
 //
-// One workgroup of 256 threads handles one (page, kv head, batch). The page
-// tokens are staged in LDS; phase 1 reduces each group's min/max, phase 2
-// lets every thread produce whole 16-byte output units, so all global stores
-// are coalesced dwordx4 stores.
+// Several workgroups of 256 threads write one (page, kv head, batch): one per
+// value k-step and one per Key part (see "Work split" below). Each stages its
+// tokens in LDS, reduces every group's min / max (wave reductions), then
+// every thread produces one 32-bit word of packed output, so consecutive
+// threads store consecutive words.
 //
 // Exactness. Codes are round-half-even of the exact (2^b-1)(x-m)/(M-m): an
 // estimate from a reciprocal is corrected by comparing 2(2^b-1)(x-m) with
@@ -31,13 +32,6 @@ struct GroupParam {
   uint16_t scale;  // stored binary16 scale
   uint16_t offset; // stored binary16 offset
 };
-
-// value token t of a page lives at src[(base + t) * 128 + d]
-__device__ inline void stage_page(uint16_t* lds, const uint16_t* src, int64_t row0) {
-  const uint4* s = reinterpret_cast<const uint4*>(src + row0 * D);
-  uint4* d = reinterpret_cast<uint4*>(lds);
-  for (int i = threadIdx.x; i < PAGE * D / 8; i += blockDim.x) d[i] = s[i];
-}
 
 // min / max / flags over n values read by a strided accessor (all in LDS)
 struct Scan {
@@ -146,385 +140,415 @@ __device__ inline int mid_code(const GroupParam& p, float x) {
 
 __device__ inline void store16(uint8_t* dst, uint4 v) { *reinterpret_cast<uint4*>(dst) = v; }
 
-// ------------------------------------------------------------------ values
-// Per-token value parameters: 128 tokens x 4 groups, thread t -> groups 2t, 2t+1.
-__device__ inline void value_params(const uint16_t* sv, GroupParam* vp, unsigned* flags) {
-  for (int g = threadIdx.x; g < PAGE * 4; g += blockDim.x) {
-    int t = g >> 2, j = g & 3;
-    Scan s;
-    scan_init(s);
-    for (int c = 0; c < GV; ++c) scan_add(s, sv[t * D + GV * j + c]);
-    vp[g] = make_param(s, 3, flags);
-  }
+__device__ inline void store4(uint8_t* dst, uint32_t v) { *reinterpret_cast<uint32_t*>(dst) = v; }
+
+// rows row0 .. row0 + n_rows - 1 of a [*, 128] bf16 source into LDS
+__device__ inline void stage_rows(uint16_t* lds, const uint16_t* src, int64_t row0, int n_rows) {
+  const uint4* s = reinterpret_cast<const uint4*>(src + row0 * D);
+  uint4* d = reinterpret_cast<uint4*>(lds);
+  for (int i = threadIdx.x; i < n_rows * D / 8; i += blockDim.x) d[i] = s[i];
 }
-
-__device__ inline int pi_token(int s, int a, int k) { return 32 * s + 16 * (k >> 2) + 4 * a + (k & 3); }
-
-// value code region unit (s, a, r): 16 bytes = V-tiles u = 0..7, 8 tokens each
-__device__ inline uint4 value_code_unit(const uint16_t* sv, const GroupParam* vp, int s, int a, int r) {
-  uint32_t w4[4];
-  for (int w = 0; w < 4; ++w) {
-    uint32_t word = 0;
-    for (int p = 0; p < 16; ++p) {
-      int u = 2 * w + (p >> 3);
-      int k = c_swap[p & 7];
-      int t = pi_token(s, a, k);
-      int ch = 16 * u + r;
-      int code = quant_code(vp[t * 4 + (ch >> 5)], 3, bf16_to_f32(sv[t * D + ch]));
-      word |= (uint32_t)code << (2 * p);
-    }
-    w4[w] = word;
-  }
-  return make_uint4(w4[0], w4[1], w4[2], w4[3]);
-}
-
-// value meta unit (s, a, j, half): 8 scales (half 0) or 8 offsets (half 1)
-__device__ inline uint4 value_meta_unit(const GroupParam* vp, int s, int a, int j, int half) {
-  uint32_t w4[4];
-  for (int w = 0; w < 4; ++w) {
-    uint16_t lo, hi;
-    const GroupParam& p0 = vp[pi_token(s, a, 2 * w) * 4 + j];
-    const GroupParam& p1 = vp[pi_token(s, a, 2 * w + 1) * 4 + j];
-    lo = half ? p0.offset : p0.scale;
-    hi = half ? p1.offset : p1.scale;
-    w4[w] = (uint32_t)lo | ((uint32_t)hi << 16);
-  }
-  return make_uint4(w4[0], w4[1], w4[2], w4[3]);
-}
-
-// Stage the page's Values in `tile`, quantize per token and write the value
-// code region (256 units) and value meta region (128 units).
-__device__ inline void value_part(uint8_t* page, uint16_t* tile, GroupParam* vp, const uint16_t* v_src,
-                                  int64_t row0, unsigned* flags) {
-  __syncthreads();                      // the tile may still be read by the Key phase
-  stage_page(tile, v_src, row0);
-  __syncthreads();
-  value_params(tile, vp, flags);
-  __syncthreads();
-  const uint16_t* sv = tile;
-  for (int u = threadIdx.x; u < 384; u += blockDim.x) {
-    if (u < 256) {
-      int s = u >> 6, a = (u >> 4) & 3, r = u & 15;
-      store16(page + 1024 * s + 256 * a + 16 * r, value_code_unit(sv, vp, s, a, r));
-    } else {
-      int m = u - 256;
-      int s = m >> 5, a = (m >> 3) & 3, j = (m >> 1) & 3, half = m & 1;
-      store16(page + V_CODE_BYTES + 512 * s + 128 * a + 32 * j + 16 * half, value_meta_unit(vp, s, a, j, half));
-    }
-  }
-}
-
-// ------------------------------------------------------------------ MixKVQ
-
-struct FlushSmem {
-  uint16_t tile[PAGE * D];      // staged Keys, then Values
-  GroupParam kp[D];             // Key group parameters
-  GroupParam vp[PAGE * 4];      // Value group parameters
-};
 
 __device__ inline uint4 pack8(const uint16_t* v) {
   return make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16), v[4] | ((uint32_t)v[5] << 16),
                     v[6] | ((uint32_t)v[7] << 16));
 }
 
-__global__ __launch_bounds__(256) void flush_mixkvq_kernel(FlushArgs A) {
-  __shared__ FlushSmem S;
-  __shared__ uint8_t perm[D];
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t head = (int64_t)b * A.n_kv_heads + h;
-  const int64_t row0 = head * A.src_stride + (int64_t)p * PAGE;
-  uint8_t* page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
-  const MixGeo g = mix_geo(A.n16, A.n4);
-  uint16_t* sk = S.tile;
+// Work split. A page is written by several workgroups of 256 threads: one
+// per value k-step (32 tokens, V_PARTS of them) and one or more Key parts.
+// Every thread produces one 32-bit word of packed output, so a page takes
+// a few microseconds of latency rather than a long serial loop.
+constexpr int V_PARTS = 4;
 
-  if (threadIdx.x < D) perm[threadIdx.x] = A.mask[head * MIX_RECORD + threadIdx.x];
-  stage_page(sk, A.k_src, row0);
+// ------------------------------------------------------------------ values
+struct VPartSmem {
+  uint16_t tile[32 * D];        // the k-step's 32 tokens
+  GroupParam vp[32 * 4];        // their per-token group parameters
+};
+
+// Value k-step s of a page (tokens 32 s .. 32 s + 31, per-token groups of 32
+// channels): code units (a, r) of the code region and the k-step's 512
+// bytes of scales / offsets.
+__device__ inline void flush_value_part(uint8_t* page_v, const uint16_t* v_src, int64_t row0, int s,
+                                        unsigned* flags, VPartSmem& S) {
+  stage_rows(S.tile, v_src, row0 + 32 * s, 32);
   __syncthreads();
-
-  // Key channel parameters, two threads per channel position
-  {
-    int c = threadIdx.x >> 1, half = threadIdx.x & 1;
-    int d = perm[c];
-    Scan s;
-    scan_init(s);
-    for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(s, sk[t * D + d]);
-    scan_merge_xor(s, 1);
-    if (half == 0) {
-      if (c < g.n16) {
-        if (s.nonfinite) atomicOr(A.flags, KVQ_FLAG_NONFINITE);
-      } else {
-        S.kp[c] = make_param(s, c < g.n16 + g.n4 ? 15 : 3, A.flags);
-      }
-    }
+  {  // 128 groups, two threads each
+    const int gi = threadIdx.x >> 1, half = threadIdx.x & 1, tl = gi >> 2, j = gi & 3;
+    Scan sc;
+    scan_init(sc);
+    for (int c = 16 * half; c < 16 * half + 16; ++c) scan_add(sc, S.tile[tl * D + GV * j + c]);
+    scan_merge_xor(sc, 1);
+    if (half == 0) S.vp[gi] = make_param(sc, 3, flags);
   }
   __syncthreads();
+  {  // code unit (a, r), word w: V-tiles 2w, 2w+1 (value group w) of the 8 tokens pi(s, a, k)
+    const int t = threadIdx.x, a = t >> 6, r = (t >> 2) & 15, w = t & 3;
+    uint32_t word = 0;
+    for (int p = 0; p < 16; ++p) {
+      const int u = 2 * w + (p >> 3), k = c_swap[p & 7];
+      const int tl = 16 * (k >> 2) + 4 * a + (k & 3);   // pi(s, a, k) - 32 s
+      word |= (uint32_t)quant_code(S.vp[tl * 4 + w], 3, bf16_to_f32(S.tile[tl * D + 16 * u + r])) << (2 * p);
+    }
+    store4(page_v + 1024 * s + 256 * a + 16 * r + 4 * w, word);
+  }
+  if (threadIdx.x < 128) {  // meta unit (a, j, half), dword w: tokens pi(s, a, 2w) and pi(s, a, 2w + 1)
+    const int t = threadIdx.x, a = t >> 5, j = (t >> 3) & 3, half = (t >> 2) & 1, w = t & 3;
+    const int t0 = 16 * ((2 * w) >> 2) + 4 * a + ((2 * w) & 3);
+    const int t1 = 16 * ((2 * w + 1) >> 2) + 4 * a + ((2 * w + 1) & 3);
+    const GroupParam& p0 = S.vp[t0 * 4 + j];
+    const GroupParam& p1 = S.vp[t1 * 4 + j];
+    const uint16_t lo = half ? p0.offset : p0.scale, hi = half ? p1.offset : p1.scale;
+    store4(page_v + V_CODE_BYTES + 512 * s + 128 * a + 32 * j + 16 * half + 4 * w, (uint32_t)lo | ((uint32_t)hi << 16));
+  }
+}
 
-  const int n_bf = 16 * g.n16, n_codes = 16 * g.F, n_meta = 2 * g.F;
-  for (int u = threadIdx.x; u < n_bf + n_codes + n_meta; u += blockDim.x) {
-    if (u < n_bf) {                       // BF16 tier: channel row c, token row r, 8 tiles
-      int c = u >> 4, r = u & 15, d = perm[c];
-      uint16_t v[8];
-      for (int i = 0; i < 8; ++i) v[i] = sk[(16 * i + r) * D + d];
-      store16(page + 256 * c + 16 * r, pack8(v));
-    } else if (u < n_bf + n_codes) {      // code fragment f, token row r
-      int f = (u - n_bf) >> 4, r = (u - n_bf) & 15;
-      uint32_t w4[4];
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-        for (int pp = 0; pp < 16; ++pp) {
-          int t = 16 * (2 * w + (pp >> 3)) + r;
-          int slot = 8 * f + c_swap[pp & 7];
-          int code = 0;
-          if (slot < 2 * g.n4) {
-            int c = g.n16 + (slot >> 1);
-            int full = quant_code(S.kp[c], 15, bf16_to_f32(sk[t * D + perm[c]]));
-            code = (slot & 1) ? (full >> 2) : (full & 3);
-          } else if (slot >= g.s4 && slot < g.s4 + g.n2) {
-            int c = g.n16 + g.n4 + (slot - g.s4);
-            code = quant_code(S.kp[c], 3, bf16_to_f32(sk[t * D + perm[c]]));
-          }
-          word |= (uint32_t)code << (2 * pp);
+struct KPartSmem {
+  uint16_t tile[PAGE * D];      // the page's Keys
+  GroupParam kp[D];             // Key group parameters (by slot or channel position)
+  uint8_t ch[D];                // channel order (MixKVQ) / slot -> channel (PN-Mix)
+};
+
+// ------------------------------------------------------------------ MixKVQ keys
+// Slot -> channel position (into the record's channel order), its levels and
+// whether it owns the channel's parameters (the low half of a UINT4 code).
+__device__ inline int mix_slot_pos(const MixGeo& g, int slot, int& levels, bool& primary) {
+  if (slot < 2 * g.n4) {
+    levels = 15;
+    primary = !(slot & 1);
+    return g.n16 + (slot >> 1);
+  }
+  if (slot >= g.s4 && slot < g.s4 + g.n2) {
+    levels = 3;
+    primary = true;
+    return g.n16 + g.n4 + (slot - g.s4);
+  }
+  return -1;
+}
+
+// Key part fg: fragments 4 fg .. 4 fg + 3 (codes and scales / offsets); part
+// 0 also writes the BF16-tier rows.
+__device__ inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int fg,
+                                          KPartSmem& S) {
+  const MixGeo g = mix_geo(A.n16, A.n4);
+  if (threadIdx.x < D) S.ch[threadIdx.x] = A.mask[head * MIX_RECORD + threadIdx.x];
+  stage_rows(S.tile, A.k_src, row0, PAGE);
+  __syncthreads();
+  {  // parameters of the group's 32 slots, eight threads per slot (16 tokens each)
+    const int ls = threadIdx.x >> 3, part = threadIdx.x & 7;
+    int levels = 0;
+    bool primary = false;
+    const int pos = mix_slot_pos(g, 32 * fg + ls, levels, primary);
+    Scan sc;
+    scan_init(sc);
+    if (pos >= 0 && primary) {
+      const int d = S.ch[pos];
+      for (int t = 16 * part; t < 16 * part + 16; ++t) scan_add(sc, S.tile[t * D + d]);
+    }
+    scan_merge_xor(sc, 1);
+    scan_merge_xor(sc, 2);
+    scan_merge_xor(sc, 4);
+    if (part == 0 && pos >= 0 && primary) S.kp[ls] = make_param(sc, levels, A.flags);
+  }
+  __syncthreads();
+  {  // code fragment f, token row r, word w (tiles 2w, 2w+1)
+    const int t = threadIdx.x, f = 4 * fg + (t >> 6), r = (t >> 2) & 15, w = t & 3;
+    if (f < g.F) {
+      uint32_t word = 0;
+      for (int pp = 0; pp < 16; ++pp) {
+        const int tok = 16 * (2 * w + (pp >> 3)) + r;
+        const int slot = 8 * f + c_swap[pp & 7];
+        int levels = 0;
+        bool primary = false;
+        const int pos = mix_slot_pos(g, slot, levels, primary);
+        int code = 0;
+        if (pos >= 0) {
+          const GroupParam& q = S.kp[(slot - 32 * fg) & (levels == 15 ? ~1 : ~0)];
+          const int full = quant_code(q, levels, bf16_to_f32(S.tile[tok * D + S.ch[pos]]));
+          code = levels == 15 ? ((slot & 1) ? (full >> 2) : (full & 3)) : full;
         }
-        w4[w] = word;
+        word |= (uint32_t)code << (2 * pp);
       }
-      store16(page + g.off_codes + 256 * f + 16 * r, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-    } else {                              // slot scales (half 0) / offsets (half 1)
-      int m = u - n_bf - n_codes;
-      int f = m >> 1, half = m & 1;
-      uint16_t v[8];
-      for (int k = 0; k < 8; ++k) {
-        int slot = 8 * f + k;
+      store4(page + g.off_codes + 256 * f + 16 * r + 4 * w, word);
+    }
+  }
+  if (threadIdx.x < 32) {  // scales (half 0) / offsets (half 1) of fragment f, dword w: slots 8f + 2w, 8f + 2w + 1
+    const int t = threadIdx.x, f = 4 * fg + (t >> 3), half = (t >> 2) & 1, w = t & 3;
+    if (f < g.F) {
+      uint16_t v[2];
+      for (int k = 0; k < 2; ++k) {
+        const int slot = 8 * f + 2 * w + k;
+        int levels = 0;
+        bool primary = false;
+        const int pos = mix_slot_pos(g, slot, levels, primary);
         uint16_t sc = 0, of = 0;
-        if (slot < 2 * g.n4) {
-          const GroupParam& q = S.kp[g.n16 + (slot >> 1)];
-          if (slot & 1) {
-            sc = q.scale == 0 ? 0 : f64_to_f16_rne(4.0 * f16_to_f64(q.scale));   // 4s, no offset
+        if (pos >= 0) {
+          const GroupParam& q = S.kp[(slot - 32 * fg) & (levels == 15 ? ~1 : ~0)];
+          if (levels == 15 && (slot & 1)) {   // high half of a UINT4 code: 4 s, no offset
+            sc = q.scale == 0 ? 0 : f64_to_f16_rne(4.0 * f16_to_f64(q.scale));
             if (f16_is_inf(sc) && !half) atomicOr(A.flags, KVQ_FLAG_RANGE);
           } else {
             sc = q.scale;
             of = q.offset;
           }
-        } else if (slot >= g.s4 && slot < g.s4 + g.n2) {
-          const GroupParam& q = S.kp[g.n16 + g.n4 + (slot - g.s4)];
-          sc = q.scale;
-          of = q.offset;
         }
         v[k] = half ? of : sc;
       }
-      store16(page + g.off_meta + 32 * f + 16 * half, pack8(v));
+      store4(page + g.off_meta + 32 * f + 16 * half + 4 * w, (uint32_t)v[0] | ((uint32_t)v[1] << 16));
     }
   }
-  value_part(page + g.off_v, S.tile, S.vp, A.v_src, row0, A.flags);
+  if (fg == 0) {  // BF16 tier: channel row c, token row r, 8 tiles
+    bool bad = false;
+    for (int u = threadIdx.x; u < 16 * g.n16; u += blockDim.x) {
+      const int c = u >> 4, r = u & 15, d = S.ch[c];
+      uint16_t v[8];
+      for (int i = 0; i < 8; ++i) {
+        v[i] = S.tile[(16 * i + r) * D + d];
+        bad = bad || bf16_exp_field(v[i]) == 0xFF;
+      }
+      store16(page + 256 * c + 16 * r, pack8(v));
+    }
+    if (bad) atomicOr(A.flags, KVQ_FLAG_NONFINITE);
+  }
 }
 
-// ------------------------------------------------------------------ PN-Mix
-__global__ __launch_bounds__(256) void flush_pnmix_kernel(FlushArgs A) {
-  __shared__ FlushSmem S;
-  __shared__ uint8_t slot_ch[D];
-  __shared__ uint8_t is_hi[D];
-  __shared__ int n_hi_s;
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t head = (int64_t)b * A.n_kv_heads + h;
-  const int64_t row0 = head * A.src_stride + (int64_t)p * PAGE;
-  uint8_t* page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
+// ------------------------------------------------------------------ PN-Mix keys
+// Key part 0: LSB plane; part 1: upper-2-bit plane and slot scales / offsets.
+__device__ inline void flush_pn_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int part,
+                                         KPartSmem& S, int* n_hi_s) {
   const PnGeo g = pn_geo(A.n_hi);
-  uint16_t* sk = S.tile;
-
+  __shared__ uint8_t is_hi[D];
   if (threadIdx.x < D) {
-    int d = threadIdx.x;
-    int pair = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? (d & 63) : (d >> 1);
+    const int d = threadIdx.x;
+    const int pair = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? (d & 63) : (d >> 1);
     is_hi[d] = (A.mask[head * PN_RECORD + (pair >> 3)] >> (pair & 7)) & 1;
   }
-  stage_page(sk, A.k_src, row0);
+  stage_rows(S.tile, A.k_src, row0, PAGE);
   __syncthreads();
   if (threadIdx.x == 0) {   // slot order: high channels ascending, then low ones
     int nh = 0;
     for (int d = 0; d < D; ++d)
-      if (is_hi[d]) slot_ch[nh++] = (uint8_t)d;
+      if (is_hi[d]) S.ch[nh++] = (uint8_t)d;
     int nl = nh;
     for (int d = 0; d < D; ++d)
-      if (!is_hi[d]) slot_ch[nl++] = (uint8_t)d;
-    n_hi_s = nh;
+      if (!is_hi[d]) S.ch[nl++] = (uint8_t)d;
+    *n_hi_s = nh;
     if (nh != A.n_hi) atomicOr(A.flags, KVQ_FLAG_MASK);
   }
   __syncthreads();
-  const int n_hi = min(n_hi_s, A.n_hi);
-
+  const int nhs = *n_hi_s;
+  const int n_hi = min(nhs, A.n_hi);
   {
-    int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
-    int d = slot_ch[slot];
-    Scan s;
-    scan_init(s);
-    for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(s, sk[t * D + d]);
-    scan_merge_xor(s, 1);
-    if (half == 0) S.kp[slot] = slot < n_hi_s ? make_param(s, 7, A.flags) : make_param_mid(s, A.flags);
+    const int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int d = S.ch[slot];
+    Scan sc;
+    scan_init(sc);
+    for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(sc, S.tile[t * D + d]);
+    scan_merge_xor(sc, 1);
+    if (half == 0) S.kp[slot] = slot < nhs ? make_param(sc, 7, A.flags) : make_param_mid(sc, A.flags);
   }
   __syncthreads();
-
-  const int n_lsb = 128, n_up = 16 * g.n_up_frag, n_meta = 32;
-  for (int u = threadIdx.x; u < n_lsb + n_up + n_meta; u += blockDim.x) {
-    if (u < n_lsb) {                     // LSB plane: fragment pair P, lane group a, row r
-      int P = u >> 6, a = (u >> 4) & 3, r = u & 15;
-      uint32_t w4[4];
-      for (int half = 0; half < 2; ++half) {
-        int f = 4 * (2 * P + half) + a;
-        for (int q = 0; q < 2; ++q) {
-          uint32_t word = 0;
-          for (int bit = 0; bit < 32; ++bit) {
-            int bb = bit & 7;
-            int slot = 8 * f + 2 * (bb & 3) + (bb >> 2);
-            int t = 16 * (4 * q + (bit >> 3)) + r;
-            float x = bf16_to_f32(sk[t * D + slot_ch[slot]]);
-            int code = slot < n_hi_s ? quant_code(S.kp[slot], 7, x) : mid_code(S.kp[slot], x);
-            word |= (uint32_t)(code & 1) << bit;
-          }
-          w4[2 * half + q] = word;
-        }
+  if (part == 0) {   // LSB plane: 128 units (pair P, lane group a, row r) x 4 words
+    for (int wi = threadIdx.x; wi < 512; wi += blockDim.x) {
+      const int u = wi >> 2, wq = wi & 3;
+      const int P = u >> 6, a = (u >> 4) & 3, r = u & 15, half = wq >> 1, q = wq & 1;
+      const int f = 4 * (2 * P + half) + a;
+      uint32_t word = 0;
+      for (int bit = 0; bit < 32; ++bit) {
+        const int bb = bit & 7;
+        const int slot = 8 * f + 2 * (bb & 3) + (bb >> 2);
+        const int t = 16 * (4 * q + (bit >> 3)) + r;
+        const float x = bf16_to_f32(S.tile[t * D + S.ch[slot]]);
+        const int code = slot < nhs ? quant_code(S.kp[slot], 7, x) : mid_code(S.kp[slot], x);
+        word |= (uint32_t)(code & 1) << bit;
       }
-      store16(page + 1024 * P + 256 * a + 16 * r, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-    } else if (u < n_lsb + n_up) {       // upper-2-bit plane of the high channels
-      int f = (u - n_lsb) >> 4, r = (u - n_lsb) & 15;
-      uint32_t w4[4];
-      for (int w = 0; w < 4; ++w) {
+      store4(page + 1024 * P + 256 * a + 16 * r + 4 * wq, word);
+    }
+  } else {           // upper plane units (fragment f, row r) x 4 words, then 32 meta units x 4 dwords
+    const int n_up = 16 * g.n_up_frag * 4;
+    for (int wi = threadIdx.x; wi < n_up + 128; wi += blockDim.x) {
+      if (wi < n_up) {
+        const int f = wi >> 6, r = (wi >> 2) & 15, w = wi & 3;
         uint32_t word = 0;
         for (int pp = 0; pp < 16; ++pp) {
-          int t = 16 * (2 * w + (pp >> 3)) + r;
-          int slot = 8 * f + c_swap[pp & 7];
+          const int t = 16 * (2 * w + (pp >> 3)) + r;
+          const int slot = 8 * f + c_swap[pp & 7];
           int code = 0;
-          if (slot < n_hi) code = quant_code(S.kp[slot], 7, bf16_to_f32(sk[t * D + slot_ch[slot]])) >> 1;
+          if (slot < n_hi) code = quant_code(S.kp[slot], 7, bf16_to_f32(S.tile[t * D + S.ch[slot]])) >> 1;
           word |= (uint32_t)code << (2 * pp);
         }
-        w4[w] = word;
+        store4(page + g.off_up + 256 * f + 16 * r + 4 * w, word);
+      } else {
+        const int m = wi - n_up, f = m >> 3, half = (m >> 2) & 1, w = m & 3;
+        const GroupParam& p0 = S.kp[8 * f + 2 * w];
+        const GroupParam& p1 = S.kp[8 * f + 2 * w + 1];
+        const uint16_t lo = half ? p0.offset : p0.scale, hi = half ? p1.offset : p1.scale;
+        store4(page + g.off_meta + 32 * f + 16 * half + 4 * w, (uint32_t)lo | ((uint32_t)hi << 16));
       }
-      store16(page + g.off_up + 256 * f + 16 * r, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-    } else {                             // per-slot scale / offset
-      int m = u - n_lsb - n_up;
-      int f = m >> 1, half = m & 1;
-      uint16_t v[8];
-      for (int k = 0; k < 8; ++k) v[k] = half ? S.kp[8 * f + k].offset : S.kp[8 * f + k].scale;
-      store16(page + g.off_meta + 32 * f + 16 * half, pack8(v));
     }
   }
-  value_part(page + g.off_v, S.tile, S.vp, A.v_src, row0, A.flags);
 }
 
-// ------------------------------------------------------------------ QJL
+// ------------------------------------------------------------------ QJL keys
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int QJL_MAX_M = 512;
+struct QPartSmem {
+  uint16_t tile[PAGE * D];
+  uint32_t bits[64 * 4];        // the part's 64 sketch rows x 128 tokens
+  float snorm[64];
+  float knorm[PAGE];
+  double ksq[PAGE];
+};
 
-// sign(S_i . k_t) for i < m, t < 128 with bf16 MFMA (products exact, float
-// accumulation). A sign is accepted when |dot| > 2^-16 ||S_i|| ||k_t||, which
-// exceeds the float summation error bound; otherwise the dot product is
-// recomputed in double.
-__global__ __launch_bounds__(256) void flush_qjl_kernel(FlushArgs A) {
-  __shared__ FlushSmem S;
-  __shared__ uint32_t bits[QJL_MAX_M * 4];
-  __shared__ float snorm[QJL_MAX_M];
-  __shared__ float knorm[PAGE];
-  __shared__ double ksq[PAGE];
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t head = (int64_t)b * A.n_kv_heads + h;
-  const int64_t row0 = head * A.src_stride + (int64_t)p * PAGE;
-  uint8_t* page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
-  const int m = A.qjl_m;
-  const QjlGeo g = qjl_geo(m);
+// Key part P: sketch rows 64 P .. 64 P + 63 (fragment pair P of the sign
+// region); part 0 also writes the norms. sign(S_i . k_t) comes from a bf16
+// MFMA (exact products, float accumulation) and is accepted when |dot| >
+// 2^-16 ||S_i|| ||k_t||, which exceeds the float summation error bound;
+// otherwise the dot product is recomputed in double.
+__device__ inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int64_t row0, int P, QPartSmem& S) {
+  const QjlGeo g = qjl_geo(A.qjl_m);
   const uint16_t* ss = A.qjl_s;         // S [m][128] stays in L2
-  uint16_t* sk = S.tile;
-
-  stage_page(sk, A.k_src, row0);
-  for (int i = threadIdx.x; i < m * 4; i += blockDim.x) bits[i] = 0;
+  stage_rows(S.tile, A.k_src, row0, PAGE);
+  S.bits[threadIdx.x] = 0;              // 256 words
   __syncthreads();
-  for (int i = threadIdx.x; i < m + PAGE; i += blockDim.x) {
-    const uint16_t* row = i < m ? ss + (size_t)i * D : sk + (i - m) * D;
+  for (int i = threadIdx.x; i < 64 + PAGE; i += blockDim.x) {
+    const uint16_t* row = i < 64 ? ss + (size_t)(64 * P + i) * D : S.tile + (i - 64) * D;
     double acc = 0.0;
     bool bad = false;
     for (int d = 0; d < D; ++d) {
-      uint16_t v = row[d];
+      const uint16_t v = row[d];
       if (bf16_exp_field(v) == 0xFF) bad = true;
-      double x = bf16_to_f64(v);
+      const double x = bf16_to_f64(v);
       acc = fma(x, x, acc);
     }
     if (bad) atomicOr(A.flags, KVQ_FLAG_NONFINITE);
-    if (i < m) {
-      snorm[i] = (float)sqrt(acc);
+    if (i < 64) {
+      S.snorm[i] = (float)sqrt(acc);
     } else {
-      knorm[i - m] = (float)sqrt(acc);
-      ksq[i - m] = acc;
+      S.knorm[i - 64] = (float)sqrt(acc);
+      S.ksq[i - 64] = acc;
     }
   }
   __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int a = lane >> 4, r = lane & 15;
-  const int n_tiles = (m / 16) * 8;
-  for (int tile = wave; tile < n_tiles; tile += 4) {
-    int ti = tile >> 3, tt = tile & 7;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ss + (size_t)(16 * ti + r) * D + 32 * ks + 8 * a);
-      bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(sk + (16 * tt + r) * D + 32 * ks + 8 * a);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-    }
-    for (int e = 0; e < 4; ++e) {        // D[row = sketch 16 ti + 4 a + e][col = token 16 tt + r]
-      int i = 16 * ti + 4 * a + e, t = 16 * tt + r;
-      float dot = acc[e];
-      bool pos;
-      if (fabsf(dot) > 0x1.0p-16f * snorm[i] * knorm[t]) {
-        pos = dot >= 0.f;
-      } else {
-        double x = 0.0;
-        for (int d = 0; d < D; ++d) x = fma(bf16_to_f64(ss[(size_t)i * D + d]), bf16_to_f64(sk[t * D + d]), x);
-        pos = x >= 0.0;
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int a = lane >> 4, r = lane & 15;
+    for (int tile = wave; tile < 32; tile += 4) {   // 4 row tiles x 8 token tiles
+      const int ti = tile >> 3, tt = tile & 7;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ss + (size_t)(64 * P + 16 * ti + r) * D + 32 * ks + 8 * a);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(S.tile + (16 * tt + r) * D + 32 * ks + 8 * a);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
       }
-      if (pos) atomicOr(&bits[i * 4 + (t >> 5)], 1u << (t & 31));
-    }
-  }
-  __syncthreads();
-
-  const int n_bit_units = m;               // (m / 64) pairs x 4 lane groups x 16 rows
-  for (int u = threadIdx.x; u < n_bit_units + 16; u += blockDim.x) {
-    if (u < n_bit_units) {
-      int P = u >> 6, aa = (u >> 4) & 3, rr = u & 15;
-      uint32_t w4[4];
-      for (int half = 0; half < 2; ++half) {
-        int f = 4 * (2 * P + half) + aa;
-        for (int q = 0; q < 2; ++q) {
-          uint32_t word = 0;
-          for (int bit = 0; bit < 32; ++bit) {
-            int bb = bit & 7;
-            int srow = 8 * f + 2 * (bb & 3) + (bb >> 2);
-            int t = 16 * (4 * q + (bit >> 3)) + rr;
-            word |= ((bits[srow * 4 + (t >> 5)] >> (t & 31)) & 1u) << bit;
-          }
-          w4[2 * half + q] = word;
+      for (int e = 0; e < 4; ++e) {        // D[row = sketch 16 ti + 4 a + e][col = token 16 tt + r]
+        const int il = 16 * ti + 4 * a + e, t = 16 * tt + r;
+        const float dot = acc[e];
+        bool pos;
+        if (fabsf(dot) > 0x1.0p-16f * S.snorm[il] * S.knorm[t]) {
+          pos = dot >= 0.f;
+        } else {
+          double x = 0.0;
+          for (int d = 0; d < D; ++d)
+            x = fma(bf16_to_f64(ss[(size_t)(64 * P + il) * D + d]), bf16_to_f64(S.tile[t * D + d]), x);
+          pos = x >= 0.0;
         }
+        if (pos) atomicOr(&S.bits[il * 4 + (t >> 5)], 1u << (t & 31));
       }
-      store16(page + 1024 * P + 256 * aa + 16 * rr, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-    } else {                               // norms: position 32 a + 4 i + e holds token 16 i + 4 a + e
-      int q = u - n_bit_units;
-      uint16_t v[8];
-      for (int k = 0; k < 8; ++k) {
-        int pos = 8 * q + k;
-        int aa = pos >> 5, i = (pos >> 2) & 7, e = pos & 3;
-        v[k] = sqrt_to_f16_rne(ksq[16 * i + 4 * aa + e]);
-      }
-      store16(page + g.off_norm + 16 * q, pack8(v));
     }
   }
-  value_part(page + g.off_v, S.tile, S.vp, A.v_src, row0, A.flags);
+  __syncthreads();
+  {  // unit (aa, rr) of pair P, word wq = 2 half + q
+    const int t = threadIdx.x, u = t >> 2, wq = t & 3, aa = u >> 4, rr = u & 15, half = wq >> 1, q = wq & 1;
+    const int fl = 4 * half + aa;         // fragment 8 P + fl, local rows 8 fl .. 8 fl + 7
+    uint32_t word = 0;
+    for (int bit = 0; bit < 32; ++bit) {
+      const int bb = bit & 7;
+      const int il = 8 * fl + 2 * (bb & 3) + (bb >> 2);
+      const int tok = 16 * (4 * q + (bit >> 3)) + rr;
+      word |= ((S.bits[il * 4 + (tok >> 5)] >> (tok & 31)) & 1u) << bit;
+    }
+    store4(page + 1024 * P + 256 * aa + 16 * rr + 4 * wq, word);
+  }
+  if (P == 0 && threadIdx.x < 64) {   // norms: position 32 a + 4 i + e holds token 16 i + 4 a + e
+    const int qd = threadIdx.x >> 2, w = threadIdx.x & 3;
+    uint16_t v[2];
+    for (int k = 0; k < 2; ++k) {
+      const int pos = 8 * qd + 2 * w + k;
+      const int aa = pos >> 5, i = (pos >> 2) & 7, e = pos & 3;
+      v[k] = sqrt_to_f16_rne(S.ksq[16 * i + 4 * aa + e]);
+    }
+    store4(page + g.off_norm + 16 * qd + 4 * w, (uint32_t)v[0] | ((uint32_t)v[1] << 16));
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+__device__ inline void part_coords(const FlushArgs& A, int parts, int& part, int64_t& head, int64_t& row0,
+                                   uint8_t*& page) {
+  const int p = blockIdx.x / parts;
+  part = blockIdx.x % parts;
+  head = (int64_t)blockIdx.z * A.n_kv_heads + blockIdx.y;
+  row0 = head * A.src_stride + (int64_t)p * PAGE;
+  page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
+}
+
+__global__ __launch_bounds__(256) void flush_mixkvq_kernel(FlushArgs A, int parts) {
+  __shared__ union {
+    VPartSmem v;
+    KPartSmem k;
+  } S;
+  int part;
+  int64_t head, row0;
+  uint8_t* page;
+  part_coords(A, parts, part, head, row0, page);
+  const MixGeo g = mix_geo(A.n16, A.n4);
+  if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+  else flush_mix_key_part(A, page, head, row0, part - V_PARTS, S.k);
+}
+
+__global__ __launch_bounds__(256) void flush_pnmix_kernel(FlushArgs A, int parts) {
+  __shared__ union {
+    VPartSmem v;
+    KPartSmem k;
+  } S;
+  __shared__ int n_hi_s;
+  int part;
+  int64_t head, row0;
+  uint8_t* page;
+  part_coords(A, parts, part, head, row0, page);
+  const PnGeo g = pn_geo(A.n_hi);
+  if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+  else flush_pn_key_part(A, page, head, row0, part - V_PARTS, S.k, &n_hi_s);
+}
+
+__global__ __launch_bounds__(256) void flush_qjl_kernel(FlushArgs A, int parts) {
+  __shared__ union {
+    VPartSmem v;
+    QPartSmem q;
+  } S;
+  int part;
+  int64_t head, row0;
+  uint8_t* page;
+  part_coords(A, parts, part, head, row0, page);
+  const QjlGeo g = qjl_geo(A.qjl_m);
+  if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+  else flush_qjl_key_part(A, page, row0, part - V_PARTS, S.q);
 }
 
 // ------------------------------------------------------------------ launcher
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int n_pages, int batch, hipStream_t stream) {
-  dim3 grid(n_pages, a.n_kv_heads, batch);
+  int parts;
+  if (key_mode == KVQ_KEY_MIXKVQ) parts = V_PARTS + max(1, (mix_geo(a.n16, a.n4).F + 3) / 4);   // part 0 also writes the BF16 rows
+  else if (key_mode == KVQ_KEY_PNMIX) parts = V_PARTS + 2;
+  else parts = V_PARTS + a.qjl_m / 64;
+  dim3 grid(n_pages * parts, a.n_kv_heads, batch);
   if (key_mode == KVQ_KEY_MIXKVQ)
-    hipLaunchKernelGGL(flush_mixkvq_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(flush_mixkvq_kernel, grid, dim3(256), 0, stream, a, parts);
   else if (key_mode == KVQ_KEY_PNMIX)
-    hipLaunchKernelGGL(flush_pnmix_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(flush_pnmix_kernel, grid, dim3(256), 0, stream, a, parts);
   else
-    hipLaunchKernelGGL(flush_qjl_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(flush_qjl_kernel, grid, dim3(256), 0, stream, a, parts);
   return hipGetLastError();
 }
 
