@@ -19,7 +19,7 @@ KVQ_ABI_VERSION = 1
 KVQ_OK, KVQ_INVALID_ARG, KVQ_UNSUPPORTED, KVQ_WORKSPACE_TOO_SMALL, KVQ_CAPACITY, KVQ_HIP_ERROR = range(6)
 KVQ_KEY_MIXKVQ, KVQ_KEY_PNMIX, KVQ_KEY_QJL = 0, 1, 2
 KVQ_PAIR_HALF_SPLIT, KVQ_PAIR_ADJACENT = 0, 1
-KVQ_FLAG_NONFINITE, KVQ_FLAG_SPAN, KVQ_FLAG_MASK = 1, 2, 4
+KVQ_FLAG_NONFINITE, KVQ_FLAG_SPAN, KVQ_FLAG_MASK, KVQ_FLAG_RANGE = 1, 2, 4, 8
 
 EXPORTED = (
     "kvq_abi_version", "kvq_status_string", "kvq_page_bytes", "kvq_mask_bytes",

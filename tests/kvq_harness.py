@@ -77,6 +77,10 @@ class Pipeline:
         w = self.w
         n_pages = w.n_pages if n_pages is None else n_pages
         n_resid = w.n_resid if n_resid is None else n_resid
+        need = kvq.kvq_workspace_bytes(self.cfg, n_pages)
+        if need > self.ws_bytes:
+            self.ws_bytes = need
+            self.ws = torch.zeros(need // 4 + 64, dtype=torch.float32, device=self.dev)
         kvq.kvq_decode_attention(self.cfg, self.q_dec, self.arena, n_pages, self.mask, self.S,
                                  self.sink_k, self.sink_v, w.n_sink, self.resid_k, self.resid_v, n_resid, 128,
                                  self.scale, self.out, self.ws, self.ws_bytes)

@@ -1,0 +1,194 @@
+"""GPU edge cases of libkvq against the oracle.
+
+* The generic decode kernel (KVQ_FORCE_GENERIC_DECODE) against the oracle
+  and against the pipelined kernels.
+* Degenerate visible sets: no pages, only residual; no pages and no
+  residual; a prefix of the flushed pages.
+* The tiny MixKVQ flow of the workload list: decode over 8 pages + 64
+  residual tokens, append 64 tokens, flush the full residual into page 8
+  (bit-exact), decode again over 9 pages.
+* Flush status flags: non-finite inputs, values beyond the binary16 range,
+  groups spanning more than 38 binades; constant groups bit-exact.
+* PN-Mix with the adjacent pair layout.
+* Repeated decode calls give identical bits.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as synth
+import mixed_precision_kv_amd as kvq
+from kvq_harness import Pipeline, rel_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a ROCm GPU")]
+
+TOL = 2e-3
+
+
+def check_decode(p, n_pages, n_resid, tag):
+    out = p.out.cpu().numpy()
+    g = p.g
+    for b in range(p.w.batch):
+        for h in range(p.w.n_kv_heads):
+            rec = p.gpu_record(b, h) if p.w.key_mode != synth.QJL else None
+            pages = [p.oracle_page(b, h, pg, rec) for pg in range(n_pages)]
+            ref, _ = p.oracle_decode(b, h, pages, rec, n_resid=n_resid)
+            err = rel_err(out[b, h * g:(h + 1) * g], ref)
+            assert np.all(err <= TOL), (tag, b, h, err)
+
+
+def built(w, **kw):
+    print(f"\n[case] {w}", flush=True)
+    p = Pipeline(w, **kw)
+    p.select()
+    p.flush_prefill()
+    torch.cuda.synchronize()
+    return p
+
+
+@pytest.fixture
+def generic_decode():
+    os.environ["KVQ_FORCE_GENERIC_DECODE"] = "1"
+    yield
+    os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
+
+
+@pytest.mark.parametrize("name", ["llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k"])
+def test_generic_decode_matches_oracle_and_fast(name, generic_decode):
+    base = synth.WORKLOADS[name]
+    w = base.scaled(batch=1, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=3, n_resid=min(base.n_resid, 40),
+                    seed=base.seed + 100)
+    p = built(w)
+    p.decode()
+    torch.cuda.synchronize()
+    generic = p.out.clone()
+    check_decode(p, w.n_pages, w.n_resid, name + "/generic")
+    os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
+    p.decode()
+    torch.cuda.synchronize()
+    fast = p.out.clone()
+    check_decode(p, w.n_pages, w.n_resid, name + "/fast")
+    ref = generic.cpu().numpy().reshape(-1, 128)
+    assert np.all(rel_err(fast.cpu().numpy().reshape(-1, 128), ref) <= 2 * TOL)
+
+
+@pytest.mark.parametrize("name", ["llama8b_8k", "pnmix_16k", "qjl_32k"])
+def test_degenerate_visible_sets(name):
+    base = synth.WORKLOADS[name]
+    w = base.scaled(batch=2, n_kv_heads=1, n_q_heads=base.group, n_pages=4, n_resid=60, seed=base.seed + 200)
+    p = built(w)
+    # no pages: sinks (PN-Mix) + residual only
+    p.decode(n_pages=0, n_resid=60)
+    torch.cuda.synchronize()
+    check_decode(p, 0, 60, name + "/no-pages")
+    # a prefix of the flushed pages, no residual
+    p.decode(n_pages=2, n_resid=0)
+    torch.cuda.synchronize()
+    check_decode(p, 2, 0, name + "/prefix")
+    # nothing visible (no sinks either): every output is zero
+    if w.n_sink == 0:
+        p.out.fill_(7.0)
+        p.decode(n_pages=0, n_resid=0)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(p.out).item() == 0
+
+
+def test_tiny_decode_append_flush_decode():
+    w = synth.WORKLOADS["tiny_mixkvq"]
+    p = built(w)
+    assert int(p.flags[0].item()) == 0
+    p.decode()
+    torch.cuda.synchronize()
+    check_decode(p, w.n_pages, w.n_resid, "tiny/first decode")
+    # 64 more seeded tokens fill the residual to 128, which is flushed into page 8
+    k_new, v_new = synth.appended_kv(w, w.n_append, "cuda")
+    p.resid_k[:, :, w.n_resid:w.n_resid + w.n_append] = k_new
+    p.resid_v[:, :, w.n_resid:w.n_resid + w.n_append] = v_new
+    kvq.kvq_flush_quantize(p.cfg, p.resid_k, p.resid_v, 128, 1, p.mask, None, p.arena, w.n_pages, p.flags)
+    torch.cuda.synchronize()
+    assert int(p.flags[0].item()) == 0
+    rec = p.gpu_record(0, 0)
+    from oracle import flush as oflush
+    ref = oflush.flush_mixkvq_page(p.bits(p.resid_k[0, 0]), p.bits(p.resid_v[0, 0]), rec[:128], w.n_bf16, w.n_u4)
+    assert np.array_equal(p.gpu_page(0, 0, w.n_pages), ref)
+    # decode over the 9 pages, empty residual
+    p.decode(n_pages=w.n_pages + 1, n_resid=0)
+    torch.cuda.synchronize()
+    out = p.out.cpu().numpy()
+    pages = [p.oracle_page(0, 0, pg, rec) for pg in range(w.n_pages)] + [ref]
+    refo, _ = p.oracle_decode(0, 0, pages, rec, n_resid=0)
+    assert np.all(rel_err(out[0, :w.group], refo) <= TOL)
+
+
+def _flush_one(p, k, v):
+    """Flush one page from explicit [B, Hkv, 128, D] K / V into page 0."""
+    p.flags.zero_()
+    kvq.kvq_flush_quantize(p.cfg, k, v, 128, 1, p.mask, p.S, p.arena, 0, p.flags)
+    torch.cuda.synchronize()
+    return int(p.flags[0].item())
+
+
+def test_flush_constant_groups_and_flags():
+    w = synth.WORKLOADS["tiny_mixkvq"].scaled(n_pages=1, n_resid=0, n_append=0, seed=1301)
+    p = built(w)
+    rec = p.gpu_record(0, 0)
+    from oracle import flush as oflush
+    k = p.k_pre[:, :, :128].clone()
+    v = p.v_pre[:, :, :128].clone()
+    # constant Key channels (every tier) and constant value groups: bit-exact, no flag
+    for d in (int(rec[0]), int(rec[20]), int(rec[100]), 5):
+        k[0, 0, :, d] = 1.5
+    v[0, 0, 3, 0:32] = -2.25
+    v[0, 0, 7, :] = 0.0
+    assert _flush_one(p, k, v) == 0
+    ref = oflush.flush_mixkvq_page(p.bits(k[0, 0]), p.bits(v[0, 0]), rec[:128], w.n_bf16, w.n_u4)
+    assert np.array_equal(p.gpu_page(0, 0, 0), ref)
+    # beyond the binary16 range: infinite scale / offset, KVQ_FLAG_RANGE, still bit-exact
+    k2 = k.clone()
+    k2[0, 0, 10, int(rec[100])] = 4.0e5
+    v2 = v.clone()
+    v2[0, 0, 9, 40] = -3.0e5
+    f = _flush_one(p, k2, v2)
+    assert f & kvq.KVQ_FLAG_RANGE and not f & (kvq.KVQ_FLAG_NONFINITE | kvq.KVQ_FLAG_SPAN), f
+    ref = oflush.flush_mixkvq_page(p.bits(k2[0, 0]), p.bits(v2[0, 0]), rec[:128], w.n_bf16, w.n_u4)
+    assert np.array_equal(p.gpu_page(0, 0, 0), ref)
+    # a value group spanning more than 38 binades: KVQ_FLAG_SPAN
+    v3 = v.clone()
+    v3[0, 0, 11, 64] = 2.0 ** -60
+    v3[0, 0, 11, 65] = 2.0 ** 20
+    assert _flush_one(p, k, v3) & kvq.KVQ_FLAG_SPAN
+    # a non-finite input: KVQ_FLAG_NONFINITE
+    v4 = v.clone()
+    v4[0, 0, 2, 2] = float("nan")
+    assert _flush_one(p, k, v4) & kvq.KVQ_FLAG_NONFINITE
+    k5 = k.clone()
+    k5[0, 0, 4, int(rec[0])] = float("inf")          # a BF16-tier channel
+    assert _flush_one(p, k5, v) & kvq.KVQ_FLAG_NONFINITE
+
+
+def test_pnmix_adjacent_pairs():
+    base = synth.WORKLOADS["pnmix_16k"]
+    w = base.scaled(batch=1, n_kv_heads=2, n_q_heads=8, n_pages=2, n_resid=33, seed=1401)
+    p = built(w, pair_layout="adjacent")
+    for h in range(w.n_kv_heads):
+        assert np.array_equal(p.gpu_record(0, h), p.oracle_record(0, h))
+        for pg in range(w.n_pages):
+            assert np.array_equal(p.gpu_page(0, h, pg), p.oracle_page(0, h, pg, p.gpu_record(0, h)))
+    p.decode()
+    torch.cuda.synchronize()
+    check_decode(p, w.n_pages, w.n_resid, "pnmix/adjacent")
+
+
+def test_decode_is_deterministic():
+    w = synth.WORKLOADS["llama8b_8k"].scaled(batch=2, n_pages=6, seed=1501)
+    p = built(w)
+    p.decode()
+    torch.cuda.synchronize()
+    first = p.out.clone()
+    for _ in range(3):
+        p.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(first, p.out)
