@@ -8,12 +8,18 @@ inputs (packed pages, residual, selection records, query) are resident in
 HBM before the timed region. To keep the 256 MB Infinity Cache from serving
 the 51 MB cache, the steps rotate over several copies of it.
 
+The K timed steps are captured once into a HIP graph (torch.cuda.graph; the
+library launches on torch's current stream, which is the capture stream) and
+replayed once between two device synchronisations, so the host's per-call
+launch cost is not part of the step time; `ms_per_step` is that wall time
+over K. The decode call and the flush are timed the same way on their own
+(K calls per graph, HIP events on the replay stream around the replay).
+
 Prints one JSON line. `value` is the step's algorithmic packed-KV bytes
 (decode reads + flush reads and writes) divided by the step time; the
 decode-only GB/s, its fraction of the 8 TB/s HBM peak and the flush rate in
 tokens/s are reported beside it, as is the CPU oracle on a bounded sample.
-The roofline object is the decode call (decode kernel + split combine),
-timed with HIP events on the stream the library launches on; its `traffic`
+The roofline object is the decode call (decode kernel + split combine); its `traffic`
 comes from profiles/decode_llama8b_8k_traffic.txt (rocprofv3 FETCH_SIZE / WRITE_SIZE
 of the decode kernel, calibrated on a plain copy) and is null when the
 decode sources changed since those counters were taken.
@@ -146,7 +152,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for >400 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="qwen32b_32k", help="extra decode-only workload ('' to skip)")
-    ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--decode-only", action="store_true", help="time the decode call only (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -214,6 +220,7 @@ class Rig:
 
 
 def time_steps(rig, torch, steps, warmup, with_flush):
+    """Eager calls, each bracketed by HIP events (used for counter runs)."""
     for i in range(warmup):
         rig.decode(i)
         if with_flush:
@@ -235,6 +242,41 @@ def time_steps(rig, torch, steps, warmup, with_flush):
     dec = [a.elapsed_time(b) for a, b, _ in ev]
     fl = [b.elapsed_time(c) for _, b, c in ev]
     return wall, dec, fl
+
+
+def capture(torch, calls):
+    """One HIP graph holding `calls` in order. The library launches on torch's
+    current stream, which is the capture stream inside torch.cuda.graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_timed(torch, g):
+    """(GPU ms from HIP events on the replay stream, host wall s) of one replay,
+    bracketed by device synchronisation on both sides."""
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b), time.perf_counter() - t0
+
+
+def graph_time(torch, calls, warmup_calls):
+    """Per-call GPU ms of `calls` replayed as one graph, after one replay of a
+    graph of `warmup_calls`."""
+    if warmup_calls:
+        capture(torch, warmup_calls).replay()
+    g = capture(torch, calls)
+    gpu_ms, wall = replay_timed(torch, g)
+    del g
+    return gpu_ms / len(calls), wall
 
 
 def cpu_baseline(w, synth, budget_s):
@@ -310,21 +352,32 @@ def main():
         _, dec, _ = time_steps(rig, torch, args.steps, args.warmup, with_flush=False)
         print(json.dumps({"workload": w.name, "decode_ms": sum(dec) / len(dec)}))
         return
-    wall, dec, fl = time_steps(rig, torch, args.steps, args.warmup, with_flush=True)
+    K, W = args.steps, args.warmup
     dbytes, fbytes = decode_bytes(w), flush_bytes(w)
-    ms_step = wall / args.steps * 1e3
-    dec_ms = sum(dec) / len(dec)
-    fl_ms = sum(fl) / len(fl)
+
+    def step(i):
+        return [lambda i=i: rig.decode(i), lambda i=i: rig.flush(i)]
+
+    # the timed region: K whole steps (decode + flush, rotating over the cache
+    # copies) replayed as one HIP graph, so host launch cost stays outside
+    warm_calls = [c for i in range(W) for c in step(i)]
+    if warm_calls:
+        capture(torch, warm_calls).replay()
+    g_steps = capture(torch, [c for i in range(K) for c in step(W + i)])
+    step_gpu_ms, wall = replay_timed(torch, g_steps)
+    del g_steps
+    ms_step = wall / K * 1e3
+    # the dominant call (decode) and the flush on their own, same protocol
+    dec_ms, _ = graph_time(torch, [lambda i=i: rig.decode(i) for i in range(K)],
+                           [lambda i=i: rig.decode(i) for i in range(W)])
+    fl_ms, _ = graph_time(torch, [lambda i=i: rig.flush(i) for i in range(K)], [])
     dec_gbps = dbytes / (dec_ms * 1e-3) / 1e9
     step_gbps = (dbytes + fbytes) / (ms_step * 1e-3) / 1e9
     flush_tok_s = w.batch * 128 / (fl_ms * 1e-3)
     # warm-cache decode (no rotation) as a secondary number
-    warm = Rig.__new__(Rig)
-    warm.__dict__.update(rig.__dict__)
-    warm.arenas, warm.rks, warm.rvs = rig.arenas[:1], rig.rks[:1], rig.rvs[:1]
-    _, dec_w, _ = time_steps(warm, torch, args.steps, 3, with_flush=False)
-    dec_warm_gbps = dbytes / (sum(dec_w) / len(dec_w) * 1e-3) / 1e9
-    del warm, rig
+    dec_w_ms, _ = graph_time(torch, [lambda: rig.decode(0)] * K, [lambda: rig.decode(0)] * 3)
+    dec_warm_gbps = dbytes / (dec_w_ms * 1e-3) / 1e9
+    del rig
     torch.cuda.empty_cache()
 
     extra = {}
@@ -333,8 +386,9 @@ def main():
         mb2 = decode_bytes(w2) / 1e6
         print(f"[bench] secondary {w2.name}: {mb2:.1f} MB per decode", file=sys.stderr, flush=True)
         rig2 = Rig(w2, max(1, math.ceil(400.0 / mb2)), torch, kvq, synth)
-        _, dec2, _ = time_steps(rig2, torch, max(10, args.steps // 2), 3, with_flush=False)
-        d2 = sum(dec2) / len(dec2)
+        k2 = max(10, K // 2)
+        d2, _ = graph_time(torch, [lambda i=i: rig2.decode(i) for i in range(k2)],
+                           [lambda i=i: rig2.decode(i) for i in range(3)])
         extra = {"workload": w2.name, "decode_ms": d2, "decode_GBps": decode_bytes(w2) / (d2 * 1e-3) / 1e9,
                  "decode_frac_hbm_peak": decode_bytes(w2) / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
         del rig2
@@ -356,6 +410,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_gpu_ms": step_gpu_ms / K,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

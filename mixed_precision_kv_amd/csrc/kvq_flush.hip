@@ -22,13 +22,14 @@
 
 namespace kvq {
 
-__constant__ int c_swap[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+// 0 2 1 3 4 6 5 7: swaps bits 0 and 1 of a 3-bit index
+__device__ constexpr int swap01(int k) { return (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1); }
 
 // 16 bytes per group; M - m is recomputed exactly in double from m and M.
 struct GroupParam {
   float m;         // group minimum (exact bf16 value)
   float M;         // group maximum
-  float inv;       // levels / (M - m), an estimate used before the exact fix-up
+  float inv;       // levels / (M - m) (2 / (M - m) for a midpoint group); NaN sends every code to the exact path
   uint16_t scale;  // stored binary16 scale
   uint16_t offset; // stored binary16 offset
 };
@@ -46,17 +47,17 @@ __device__ inline void scan_init(Scan& s) {
   s.emax = -1000;
   s.nonfinite = false;
 }
+// branch-free: a non-finite value only raises the flag; zeros leave the
+// exponent range alone (subnormals count as exponent field 1)
 __device__ inline void scan_add(Scan& s, uint16_t b) {
-  int e = bf16_exp_field(b);
-  if (e == 0xFF) { s.nonfinite = true; return; }
-  float v = bf16_to_f32(b);
-  s.mn = fminf(s.mn, v);
-  s.mx = fmaxf(s.mx, v);
-  if ((b & 0x7FFF) != 0) {
-    int ee = e == 0 ? 1 : e;
-    s.emin = min(s.emin, ee);
-    s.emax = max(s.emax, e);
-  }
+  const int e = bf16_exp_field(b);
+  const bool fin = e != 0xFF, nz = (b & 0x7FFF) != 0 && fin;
+  const float v = bf16_to_f32(b);
+  s.nonfinite = s.nonfinite || !fin;
+  s.mn = fminf(s.mn, fin ? v : INFINITY);
+  s.mx = fmaxf(s.mx, fin ? v : -INFINITY);
+  s.emin = min(s.emin, nz ? max(e, 1) : 1000);
+  s.emax = max(s.emax, nz ? e : -1000);
 }
 __device__ inline void scan_merge_xor(Scan& s, int mask) {
   s.mn = fminf(s.mn, __shfl_xor(s.mn, mask));
@@ -86,6 +87,7 @@ __device__ inline GroupParam make_param(const Scan& s, int levels, unsigned* fla
     p.M = s.mx;
     const double den = (double)s.mx - (double)s.mn;
     p.inv = (float)((double)levels / den);
+    if (!(p.inv >= 0x1.0p-126f && p.inv <= 0x1.0p126f)) p.inv = NAN;   // outside the fast path's bound
     p.scale = f64_to_f16_rne(den / (double)levels);
   }
   flag_range(p, flags);
@@ -105,6 +107,8 @@ __device__ inline GroupParam make_param_mid(const Scan& s, unsigned* flags) {
   if (s.mx > s.mn) {
     p.M = s.mx;
     const double den = (double)s.mx - (double)s.mn;
+    p.inv = (float)(2.0 / den);
+    if (!(p.inv >= 0x1.0p-126f && p.inv <= 0x1.0p126f)) p.inv = NAN;
     p.scale = f64_to_f16_rne(0.5 * den);
     p.offset = f64_to_f16_rne(0.25 * (3.0 * (double)s.mn + (double)s.mx));
   }
@@ -112,14 +116,14 @@ __device__ inline GroupParam make_param_mid(const Scan& s, unsigned* flags) {
   return p;
 }
 
-// Exact round-half-even code of x for levels = 2^b - 1. The float estimate
+// Exact round-half-even code of x for levels = 2^b - 1. The double estimate
 // is within one of the true code; the fix-up compares 2*levels*(x-m) with
 // (2c -+ 1)(M-m), all exact in double for groups spanning <= 38 binades.
-__device__ inline int quant_code(const GroupParam& p, int levels, float x) {
+__device__ inline int quant_code_exact(const GroupParam& p, int levels, float x) {
   if (!(p.M > p.m)) return 0;
   double den = (double)p.M - (double)p.m;
   double two_num = 2.0 * (double)levels * ((double)x - (double)p.m);
-  int c = __float2int_rn((x - p.m) * p.inv);
+  int c = (int)rint(0.5 * two_num / den);   // within one of the exact code
   c = max(0, min(levels, c));
   if (c > 0) {
     double lo = (double)(2 * c - 1) * den;
@@ -132,9 +136,34 @@ __device__ inline int quant_code(const GroupParam& p, int levels, float x) {
   return c;
 }
 
-// PN-Mix Eq.7 code: 1 iff 2(x - m) > M - m (the exact midpoint rounds to 0)
+// Fast path: t = (x - m) * levels / (M - m) in float is within 4 ulp of the
+// exact quotient (x - m and levels / (M - m) each rounded once, then the
+// product), i.e. within 2^-20 for t <= 15. If t is farther than 0.5 - 2^-14
+// from a half-integer boundary its nearest integer is the exact code;
+// otherwise (ties and near-ties) the double-precision path decides. A
+// constant group has inv = 0, so t = 0.
+__device__ inline int quant_code(const GroupParam& p, int levels, float x) {
+  const float t = (x - p.m) * p.inv;
+  const float c = rintf(t);
+  if (fabsf(t - c) < 0.49993896f) return (int)c;
+  return quant_code_exact(p, levels, x);
+}
+
+// The fast path on its own, for straight-line loops: `amb` collects the
+// codes that the exact path has to redo.
+__device__ inline int fast_code(float m, float inv, float x, bool& amb) {
+  const float t = (x - m) * inv;
+  const float c = rintf(t);
+  amb = !(fabsf(t - c) < 0.49993896f);
+  return (int)c;
+}
+
+// PN-Mix Eq.7 code: 1 iff 2(x - m) > M - m (the exact midpoint rounds to 0).
+// inv = 2 / (M - m) here; the double comparison settles t within 2^-14 of 1.
 __device__ inline int mid_code(const GroupParam& p, float x) {
   if (!(p.M > p.m)) return 0;
+  const float t = (x - p.m) * p.inv;
+  if (fabsf(t - 1.0f) > 0x1.0p-14f) return t > 1.0f ? 1 : 0;
   return 2.0 * ((double)x - (double)p.m) > ((double)p.M - (double)p.m) ? 1 : 0;
 }
 
@@ -142,11 +171,20 @@ __device__ inline void store16(uint8_t* dst, uint4 v) { *reinterpret_cast<uint4*
 
 __device__ inline void store4(uint8_t* dst, uint32_t v) { *reinterpret_cast<uint32_t*>(dst) = v; }
 
-// rows row0 .. row0 + n_rows - 1 of a [*, 128] bf16 source into LDS
-__device__ inline void stage_rows(uint16_t* lds, const uint16_t* src, int64_t row0, int n_rows) {
+// rows row0 .. row0 + NROWS - 1 of a [*, 128] bf16 source into LDS, by the
+// 256 threads of the workgroup: every load is issued before the first LDS
+// store, so the staging costs one memory latency.
+template <int NROWS>
+__device__ inline void stage_rows(uint16_t* lds, const uint16_t* src, int64_t row0) {
+  constexpr int N = NROWS * D / 8 / 256;
+  static_assert(N * 256 * 8 == NROWS * D, "whole 16-byte chunks per thread");
   const uint4* s = reinterpret_cast<const uint4*>(src + row0 * D);
   uint4* d = reinterpret_cast<uint4*>(lds);
-  for (int i = threadIdx.x; i < n_rows * D / 8; i += blockDim.x) d[i] = s[i];
+  uint4 v[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = s[threadIdx.x + 256 * j];
+#pragma unroll
+  for (int j = 0; j < N; ++j) d[threadIdx.x + 256 * j] = v[j];
 }
 
 __device__ inline uint4 pack8(const uint16_t* v) {
@@ -169,26 +207,53 @@ struct VPartSmem {
 // Value k-step s of a page (tokens 32 s .. 32 s + 31, per-token groups of 32
 // channels): code units (a, r) of the code region and the k-step's 512
 // bytes of scales / offsets.
-__device__ inline void flush_value_part(uint8_t* page_v, const uint16_t* v_src, int64_t row0, int s,
+__device__ __attribute__((always_inline)) inline void flush_value_part(uint8_t* page_v, const uint16_t* v_src, int64_t row0, int s,
                                         unsigned* flags, VPartSmem& S) {
-  stage_rows(S.tile, v_src, row0 + 32 * s, 32);
+  stage_rows<32>(S.tile, v_src, row0 + 32 * s);
   __syncthreads();
   {  // 128 groups, two threads each
     const int gi = threadIdx.x >> 1, half = threadIdx.x & 1, tl = gi >> 2, j = gi & 3;
     Scan sc;
     scan_init(sc);
-    for (int c = 16 * half; c < 16 * half + 16; ++c) scan_add(sc, S.tile[tl * D + GV * j + c]);
+    const uint4* src = reinterpret_cast<const uint4*>(S.tile + tl * D + GV * j + 16 * half);
+    const uint4 c0 = src[0], c1 = src[1];
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) scan_add(sc, (uint16_t)(cw[c >> 1] >> (16 * (c & 1))));
     scan_merge_xor(sc, 1);
     if (half == 0) S.vp[gi] = make_param(sc, 3, flags);
   }
   __syncthreads();
   {  // code unit (a, r), word w: V-tiles 2w, 2w+1 (value group w) of the 8 tokens pi(s, a, k)
     const int t = threadIdx.x, a = t >> 6, r = (t >> 2) & 15, w = t & 3;
-    uint32_t word = 0;
-    for (int p = 0; p < 16; ++p) {
-      const int u = 2 * w + (p >> 3), k = c_swap[p & 7];
+    float m[8], inv[8], x[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
       const int tl = 16 * (k >> 2) + 4 * a + (k & 3);   // pi(s, a, k) - 32 s
-      word |= (uint32_t)quant_code(S.vp[tl * 4 + w], 3, bf16_to_f32(S.tile[tl * D + 16 * u + r])) << (2 * p);
+      m[k] = S.vp[tl * 4 + w].m;
+      inv[k] = S.vp[tl * 4 + w].inv;
+    }
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int u = 2 * w + (p >> 3), k = swap01(p & 7);
+      const int tl = 16 * (k >> 2) + 4 * a + (k & 3);
+      x[p] = bf16_to_f32(S.tile[tl * D + 16 * u + r]);
+    }
+    uint32_t word = 0, redo = 0;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int k = swap01(p & 7);
+      bool amb;
+      word |= (uint32_t)fast_code(m[k], inv[k], x[p], amb) << (2 * p);
+      redo |= (uint32_t)amb << p;
+    }
+    while (redo) {   // the few codes within 2^-14 of a rounding midpoint, one by one
+      const int p = __builtin_ctz(redo);
+      redo &= redo - 1;
+      const int u = 2 * w + (p >> 3), k = swap01(p & 7);
+      const int tl = 16 * (k >> 2) + 4 * a + (k & 3);
+      const uint32_t c = quant_code_exact(S.vp[tl * 4 + w], 3, bf16_to_f32(S.tile[tl * D + 16 * u + r]));
+      word = (word & ~(3u << (2 * p))) | c << (2 * p);
     }
     store4(page_v + 1024 * s + 256 * a + 16 * r + 4 * w, word);
   }
@@ -203,10 +268,33 @@ __device__ inline void flush_value_part(uint8_t* page_v, const uint16_t* v_src, 
   }
 }
 
+// Key tiles are read down columns (one channel over many tokens); rows of
+// 130 elements (65 dwords) put the 64 rows a wave reads in 64 different banks.
+constexpr int KS = D + 2;
+
+// rows row0 .. row0 + PAGE - 1 into an LDS tile with row stride KS (dword stores)
+__device__ inline void stage_rows_padded(uint16_t* lds, const uint16_t* src, int64_t row0) {
+  constexpr int N = PAGE * D / 8 / 256;
+  const uint4* s = reinterpret_cast<const uint4*>(src + row0 * D);
+  uint4 v[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = s[threadIdx.x + 256 * j];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int i = threadIdx.x + 256 * j, row = i >> 4, c = i & 15;
+    uint32_t* d = reinterpret_cast<uint32_t*>(lds + row * KS + 8 * c);
+    d[0] = v[j].x;
+    d[1] = v[j].y;
+    d[2] = v[j].z;
+    d[3] = v[j].w;
+  }
+}
+
 struct KPartSmem {
-  uint16_t tile[PAGE * D];      // the page's Keys
+  uint16_t tile[PAGE * KS];     // the page's Keys, row stride KS
   GroupParam kp[D];             // Key group parameters (by slot or channel position)
   uint8_t ch[D];                // channel order (MixKVQ) / slot -> channel (PN-Mix)
+  int kinfo[32];                // MixKVQ slot of the part: channel | shift << 8 | mask << 10 | param << 12 | u4 << 20
 };
 
 // ------------------------------------------------------------------ MixKVQ keys
@@ -228,11 +316,12 @@ __device__ inline int mix_slot_pos(const MixGeo& g, int slot, int& levels, bool&
 
 // Key part fg: fragments 4 fg .. 4 fg + 3 (codes and scales / offsets); part
 // 0 also writes the BF16-tier rows.
-__device__ inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int fg,
+__device__ __attribute__((always_inline)) inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int fg,
                                           KPartSmem& S) {
   const MixGeo g = mix_geo(A.n16, A.n4);
-  if (threadIdx.x < D) S.ch[threadIdx.x] = A.mask[head * MIX_RECORD + threadIdx.x];
-  stage_rows(S.tile, A.k_src, row0, PAGE);
+  const uint8_t chv = A.mask[head * MIX_RECORD + (threadIdx.x & (D - 1))];   // in flight with the staging
+  stage_rows_padded(S.tile, A.k_src, row0);
+  if (threadIdx.x < D) S.ch[threadIdx.x] = chv;
   __syncthreads();
   {  // parameters of the group's 32 slots, eight threads per slot (16 tokens each)
     const int ls = threadIdx.x >> 3, part = threadIdx.x & 7;
@@ -243,31 +332,58 @@ __device__ inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int
     scan_init(sc);
     if (pos >= 0 && primary) {
       const int d = S.ch[pos];
-      for (int t = 16 * part; t < 16 * part + 16; ++t) scan_add(sc, S.tile[t * D + d]);
+      for (int t = 16 * part; t < 16 * part + 16; ++t) scan_add(sc, S.tile[t * KS + d]);
     }
     scan_merge_xor(sc, 1);
     scan_merge_xor(sc, 2);
     scan_merge_xor(sc, 4);
     if (part == 0 && pos >= 0 && primary) S.kp[ls] = make_param(sc, levels, A.flags);
+    if (part == 0 && pos < 0) S.kp[ls] = GroupParam{0.f, 0.f, 0.f, 0, 0};   // empty slot: code 0
+    if (part == 1) {
+      const bool u4 = levels == 15;
+      const int d = pos >= 0 ? S.ch[pos] : 0;
+      const int shift = u4 && !primary ? 2 : 0;           // high half of a UINT4 code
+      const int mask = pos >= 0 ? 3 : 0;
+      const int pidx = u4 ? (ls & ~1) : ls;               // the UINT4 pair's parameters sit at its even slot
+      S.kinfo[ls] = d | shift << 8 | mask << 10 | pidx << 12 | (int)u4 << 20;
+    }
   }
   __syncthreads();
   {  // code fragment f, token row r, word w (tiles 2w, 2w+1)
     const int t = threadIdx.x, f = 4 * fg + (t >> 6), r = (t >> 2) & 15, w = t & 3;
     if (f < g.F) {
-      uint32_t word = 0;
+      int info[8];
+      float m[8], inv[8], x[16];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        info[k] = S.kinfo[8 * (t >> 6) + k];
+        const GroupParam& q = S.kp[(info[k] >> 12) & 255];
+        m[k] = q.m;
+        inv[k] = q.inv;
+      }
+#pragma unroll
       for (int pp = 0; pp < 16; ++pp) {
         const int tok = 16 * (2 * w + (pp >> 3)) + r;
-        const int slot = 8 * f + c_swap[pp & 7];
-        int levels = 0;
-        bool primary = false;
-        const int pos = mix_slot_pos(g, slot, levels, primary);
-        int code = 0;
-        if (pos >= 0) {
-          const GroupParam& q = S.kp[(slot - 32 * fg) & (levels == 15 ? ~1 : ~0)];
-          const int full = quant_code(q, levels, bf16_to_f32(S.tile[tok * D + S.ch[pos]]));
-          code = levels == 15 ? ((slot & 1) ? (full >> 2) : (full & 3)) : full;
-        }
-        word |= (uint32_t)code << (2 * pp);
+        x[pp] = bf16_to_f32(S.tile[tok * KS + (info[swap01(pp & 7)] & 255)]);
+      }
+      uint32_t word = 0, redo = 0;
+#pragma unroll
+      for (int pp = 0; pp < 16; ++pp) {
+        const int k = swap01(pp & 7);
+        bool amb;
+        const int full = fast_code(m[k], inv[k], x[pp], amb);
+        word |= (uint32_t)((full >> ((info[k] >> 8) & 3)) & ((info[k] >> 10) & 3)) << (2 * pp);
+        redo |= (uint32_t)amb << pp;
+      }
+      while (redo) {   // the few codes within 2^-14 of a rounding midpoint, one by one
+        const int pp = __builtin_ctz(redo);
+        redo &= redo - 1;
+        const int in = S.kinfo[8 * (t >> 6) + swap01(pp & 7)];
+        const int tok = 16 * (2 * w + (pp >> 3)) + r;
+        const float xv = bf16_to_f32(S.tile[tok * KS + (in & 255)]);
+        const int full = quant_code_exact(S.kp[(in >> 12) & 255], (in >> 20) ? 15 : 3, xv);
+        const uint32_t c = (uint32_t)((full >> ((in >> 8) & 3)) & ((in >> 10) & 3));
+        word = (word & ~(3u << (2 * pp))) | c << (2 * pp);
       }
       store4(page + g.off_codes + 256 * f + 16 * r + 4 * w, word);
     }
@@ -303,7 +419,7 @@ __device__ inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int
       const int c = u >> 4, r = u & 15, d = S.ch[c];
       uint16_t v[8];
       for (int i = 0; i < 8; ++i) {
-        v[i] = S.tile[(16 * i + r) * D + d];
+        v[i] = S.tile[(16 * i + r) * KS + d];
         bad = bad || bf16_exp_field(v[i]) == 0xFF;
       }
       store16(page + 256 * c + 16 * r, pack8(v));
@@ -314,36 +430,35 @@ __device__ inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int
 
 // ------------------------------------------------------------------ PN-Mix keys
 // Key part 0: LSB plane; part 1: upper-2-bit plane and slot scales / offsets.
-__device__ inline void flush_pn_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int part,
-                                         KPartSmem& S, int* n_hi_s) {
+__device__ __attribute__((always_inline)) inline void flush_pn_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int part,
+                                         KPartSmem& S) {
   const PnGeo g = pn_geo(A.n_hi);
-  __shared__ uint8_t is_hi[D];
-  if (threadIdx.x < D) {
+  const uint8_t* rec = A.mask + head * PN_RECORD;   // bit p of the 8 bytes: pair p is high
+  uint64_t pm = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pm |= (uint64_t)rec[i] << (8 * i);
+  stage_rows_padded(S.tile, A.k_src, row0);
+  const int np_hi = __builtin_popcountll(pm);
+  const int nhs = 2 * np_hi;                         // high channels
+  if (threadIdx.x < D) {   // slot order: high channels ascending, then low ones
     const int d = threadIdx.x;
-    const int pair = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? (d & 63) : (d >> 1);
-    is_hi[d] = (A.mask[head * PN_RECORD + (pair >> 3)] >> (pair & 7)) & 1;
+    const bool halfsplit = A.pair_layout == KVQ_PAIR_HALF_SPLIT;
+    const int pair = halfsplit ? (d & 63) : (d >> 1);
+    const bool hi = (pm >> pair) & 1;
+    const int cnt = __builtin_popcountll(pair == 0 ? 0ull : (pm & ((1ull << pair) - 1)));
+    const int below = hi ? cnt : pair - cnt;         // channels of d's class with a lower pair
+    const int before = halfsplit ? below + (d >= 64 ? (hi ? np_hi : 64 - np_hi) : 0) : 2 * below + (d & 1);
+    S.ch[hi ? before : nhs + before] = (uint8_t)d;
   }
-  stage_rows(S.tile, A.k_src, row0, PAGE);
+  if (threadIdx.x == 0 && nhs != A.n_hi) atomicOr(A.flags, KVQ_FLAG_MASK);
   __syncthreads();
-  if (threadIdx.x == 0) {   // slot order: high channels ascending, then low ones
-    int nh = 0;
-    for (int d = 0; d < D; ++d)
-      if (is_hi[d]) S.ch[nh++] = (uint8_t)d;
-    int nl = nh;
-    for (int d = 0; d < D; ++d)
-      if (!is_hi[d]) S.ch[nl++] = (uint8_t)d;
-    *n_hi_s = nh;
-    if (nh != A.n_hi) atomicOr(A.flags, KVQ_FLAG_MASK);
-  }
-  __syncthreads();
-  const int nhs = *n_hi_s;
   const int n_hi = min(nhs, A.n_hi);
   {
     const int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
     const int d = S.ch[slot];
     Scan sc;
     scan_init(sc);
-    for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(sc, S.tile[t * D + d]);
+    for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(sc, S.tile[t * KS + d]);
     scan_merge_xor(sc, 1);
     if (half == 0) S.kp[slot] = slot < nhs ? make_param(sc, 7, A.flags) : make_param_mid(sc, A.flags);
   }
@@ -358,7 +473,7 @@ __device__ inline void flush_pn_key_part(const FlushArgs& A, uint8_t* page, int6
         const int bb = bit & 7;
         const int slot = 8 * f + 2 * (bb & 3) + (bb >> 2);
         const int t = 16 * (4 * q + (bit >> 3)) + r;
-        const float x = bf16_to_f32(S.tile[t * D + S.ch[slot]]);
+        const float x = bf16_to_f32(S.tile[t * KS + S.ch[slot]]);
         const int code = slot < nhs ? quant_code(S.kp[slot], 7, x) : mid_code(S.kp[slot], x);
         word |= (uint32_t)(code & 1) << bit;
       }
@@ -372,9 +487,9 @@ __device__ inline void flush_pn_key_part(const FlushArgs& A, uint8_t* page, int6
         uint32_t word = 0;
         for (int pp = 0; pp < 16; ++pp) {
           const int t = 16 * (2 * w + (pp >> 3)) + r;
-          const int slot = 8 * f + c_swap[pp & 7];
+          const int slot = 8 * f + swap01(pp & 7);
           int code = 0;
-          if (slot < n_hi) code = quant_code(S.kp[slot], 7, bf16_to_f32(S.tile[t * D + S.ch[slot]])) >> 1;
+          if (slot < n_hi) code = quant_code(S.kp[slot], 7, bf16_to_f32(S.tile[t * KS + S.ch[slot]])) >> 1;
           word |= (uint32_t)code << (2 * pp);
         }
         store4(page + g.off_up + 256 * f + 16 * r + 4 * w, word);
@@ -395,7 +510,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct QPartSmem {
   uint16_t tile[PAGE * D];
-  uint32_t bits[64 * 4];        // the part's 64 sketch rows x 128 tokens
+  uint16_t srow[64 * D];        // the part's 64 sketch rows of S
+  union {
+    uint32_t bits[64 * 4];      // the part's 64 sketch rows x 128 tokens (bit t of row i: word 4 i + t / 32)
+    uint16_t bits16[64 * 8];    // the same, written 16 tokens at a time
+  };
   float snorm[64];
   float knorm[PAGE];
   double ksq[PAGE];
@@ -406,21 +525,25 @@ struct QPartSmem {
 // MFMA (exact products, float accumulation) and is accepted when |dot| >
 // 2^-16 ||S_i|| ||k_t||, which exceeds the float summation error bound;
 // otherwise the dot product is recomputed in double.
-__device__ inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int64_t row0, int P, QPartSmem& S) {
+__device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int64_t row0, int P, QPartSmem& S) {
   const QjlGeo g = qjl_geo(A.qjl_m);
-  const uint16_t* ss = A.qjl_s;         // S [m][128] stays in L2
-  stage_rows(S.tile, A.k_src, row0, PAGE);
-  S.bits[threadIdx.x] = 0;              // 256 words
+  stage_rows<64>(S.srow, A.qjl_s, 64 * P);    // S is [m][128] bf16
+  stage_rows<PAGE>(S.tile, A.k_src, row0);
   __syncthreads();
   for (int i = threadIdx.x; i < 64 + PAGE; i += blockDim.x) {
-    const uint16_t* row = i < 64 ? ss + (size_t)(64 * P + i) * D : S.tile + (i - 64) * D;
+    const uint16_t* row = i < 64 ? S.srow + i * D : S.tile + (i - 64) * D;
     double acc = 0.0;
     bool bad = false;
-    for (int d = 0; d < D; ++d) {
-      const uint16_t v = row[d];
-      if (bf16_exp_field(v) == 0xFF) bad = true;
-      const double x = bf16_to_f64(v);
-      acc = fma(x, x, acc);
+    for (int c = 0; c < D / 8; ++c) {
+      const uint4 w8 = reinterpret_cast<const uint4*>(row)[c];
+      const uint32_t wv[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint16_t v = (uint16_t)(wv[k >> 1] >> (16 * (k & 1)));
+        if (bf16_exp_field(v) == 0xFF) bad = true;
+        const double x = bf16_to_f64(v);
+        acc = fma(x, x, acc);
+      }
     }
     if (bad) atomicOr(A.flags, KVQ_FLAG_NONFINITE);
     if (i < 64) {
@@ -438,7 +561,7 @@ __device__ inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int
       const int ti = tile >> 3, tt = tile & 7;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ss + (size_t)(64 * P + 16 * ti + r) * D + 32 * ks + 8 * a);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(S.srow + (16 * ti + r) * D + 32 * ks + 8 * a);
         const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(S.tile + (16 * tt + r) * D + 32 * ks + 8 * a);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
       }
@@ -448,13 +571,16 @@ __device__ inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int
         bool pos;
         if (fabsf(dot) > 0x1.0p-16f * S.snorm[il] * S.knorm[t]) {
           pos = dot >= 0.f;
+        } else if (S.ksq[t] == 0.0) {    // k = 0: the dot product is exactly 0
+          pos = true;
         } else {
           double x = 0.0;
-          for (int d = 0; d < D; ++d)
-            x = fma(bf16_to_f64(ss[(size_t)(64 * P + il) * D + d]), bf16_to_f64(S.tile[t * D + d]), x);
+          for (int d = 0; d < D; ++d) x = fma(bf16_to_f64(S.srow[il * D + d]), bf16_to_f64(S.tile[t * D + d]), x);
           pos = x >= 0.0;
         }
-        if (pos) atomicOr(&S.bits[il * 4 + (t >> 5)], 1u << (t & 31));
+        // the 16 lanes of row group a hold tokens 16 tt .. 16 tt + 15 of sketch row il
+        const uint64_t bal = __ballot(pos);
+        if (r == 0) S.bits16[il * 8 + tt] = (uint16_t)(bal >> (16 * a));
       }
     }
   }
@@ -512,14 +638,13 @@ __global__ __launch_bounds__(256) void flush_pnmix_kernel(FlushArgs A, int parts
     VPartSmem v;
     KPartSmem k;
   } S;
-  __shared__ int n_hi_s;
   int part;
   int64_t head, row0;
   uint8_t* page;
   part_coords(A, parts, part, head, row0, page);
   const PnGeo g = pn_geo(A.n_hi);
   if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
-  else flush_pn_key_part(A, page, head, row0, part - V_PARTS, S.k, &n_hi_s);
+  else flush_pn_key_part(A, page, head, row0, part - V_PARTS, S.k);
 }
 
 __global__ __launch_bounds__(256) void flush_qjl_kernel(FlushArgs A, int parts) {

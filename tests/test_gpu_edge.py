@@ -192,3 +192,31 @@ def test_decode_is_deterministic():
         p.decode()
     torch.cuda.synchronize()
     assert torch.equal(first, p.out)
+
+
+@pytest.mark.parametrize("name", ["tiny_mixkvq", "pnmix_16k", "qjl_32k"])
+def test_flush_ties_bit_exact(name):
+    """Integer-valued K and V on 0..6 (and 0..30 in the UINT4 channels): many
+    codes fall exactly on a rounding midpoint, and PN-Mix values on the 1-bit
+    midpoint, so the tie-breaking path of every quantizer is exercised."""
+    base = synth.WORKLOADS[name]
+    w = base.scaled(batch=1, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=2, n_resid=0, n_append=0,
+                    seed=base.seed + 500)
+    p = built(w)
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    k = torch.randint(0, 7, (1, 2, 128, 128), generator=gen).to(torch.bfloat16)
+    v = torch.randint(0, 7, (1, 2, 128, 128), generator=gen).to(torch.bfloat16)
+    k[..., ::5] *= 5                                       # some channels on 0..30
+    k, v = k.cuda(), v.cuda()
+    assert _flush_one(p, k, v) == 0
+    from oracle import flush as oflush
+    from oracle import select as osel
+    for h in range(2):
+        kb, vb = p.bits(k[0, h]), p.bits(v[0, h])
+        if w.key_mode == synth.MIXKVQ:
+            ref = oflush.flush_mixkvq_page(kb, vb, p.gpu_record(0, h)[:128], w.n_bf16, w.n_u4)
+        elif w.key_mode == synth.PNMIX:
+            ref = oflush.flush_pnmix_page(kb, vb, osel.hi_channels_from_record(p.gpu_record(0, h)))
+        else:
+            ref = oflush.flush_qjl_page(kb, vb, p.bits(p.S))
+        assert np.array_equal(p.gpu_page(0, h, 0), ref), (name, h)
