@@ -14,10 +14,11 @@
 // Per page, per kv head, the g query heads of the GQA group are processed
 // together on MFMA v_mfma_f32_16x16x32_f16 (16x16 tiles, 64 lanes):
 //  * Keys: logits[token][col] = sum_slot code[token][slot] * B[slot][col].
-//    Codes (2-bit or 1-bit) become exact f16 integers through the fp4
-//    converter (an fp4 nibble 0b00cc is c/2; the converter's power-of-two
-//    scale 2 restores c). The per-page, per-channel Key scale is folded into
-//    the query (B = q * s, split into f16 hi + lo parts for ~22-bit
+//    Codes (2-bit or 1-bit) are masked straight out of the packed words as
+//    binary16 subnormals c * 2^(l - 24), one power of two l per 16-token
+//    tile, which the f16 MFMA multiplies exactly; the power is divided out
+//    of each tile's sums (no conversion instruction per code). The
+//    per-page, per-channel Key scale is folded into the query (B = q * s, split into f16 hi + lo parts for ~22-bit
 //    precision) and the offsets into a per-head bias q . z, the InnerQ idea
 //    of folding Key factors into the query. BF16-tier channels and the
 //    BF16 segment use the bf16 MFMA with the raw bf16 query (exact products).
@@ -127,16 +128,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         }
         half8 Bhi, Blo;
         key_operand(S.u.qslot[ks][a][h], sw, zw, Bhi, Blo, bias);
+        const u32x4 kc8 = kc >> 8u;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          half8 A0, A1;
-          expand2(rd(kc, w), A0, A1);
-          logit[2 * w] = mfma(A0, Bhi, logit[2 * w]);
-          logit[2 * w] = mfma(A0, Blo, logit[2 * w]);
-          logit[2 * w + 1] = mfma(A1, Bhi, logit[2 * w + 1]);
-          logit[2 * w + 1] = mfma(A1, Blo, logit[2 * w + 1]);
+        for (int i = 0; i < 8; ++i) {
+          const half8 At = tile2(kc, kc8, i);
+          logit[i] = mfma(At, Bhi, logit[i]);
+          logit[i] = mfma(At, Blo, logit[i]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
       for (int kb = 0; kb < NKB; ++kb) {        // BF16 tier, exact bf16 products
         u32x4 raw[8];
 #pragma unroll
@@ -197,30 +198,29 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         const u32x4 sw = ld16(page + g.off_meta + 32 * f), zw = ld16(page + g.off_meta + 32 * f + 16);
         half8 Bhi, Blo;
         key_operand(S.u.qslot[ks][a][h], sw, zw, Bhi, Blo, bias);
+        {                                        // LSB plane: 1-bit codes, weight s
+          const Row1 x = row1(rd(lsb[ks >> 1], 2 * (ks & 1)), rd(lsb[ks >> 1], 2 * (ks & 1) + 1));
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {       // LSB plane: 1-bit codes, weight s
-          half8 At[4];
-          expand1(rd(lsb[ks >> 1], 2 * (ks & 1) + q2), At);
-#pragma unroll
-          for (int T = 0; T < 4; ++T) {
-            logit[4 * q2 + T] = mfma(At[T], Bhi, logit[4 * q2 + T]);
-            logit[4 * q2 + T] = mfma(At[T], Blo, logit[4 * q2 + T]);
+          for (int T = 0; T < 8; ++T) {
+            const half8 At = tile1(x, T);
+            logit[T] = mfma(At, Bhi, logit[T]);
+            logit[T] = mfma(At, Blo, logit[T]);
           }
         }
         if (ks < NUP) {                          // upper 2 bits of high channels, weight 2 s
           const u32x4 up = f < g.n_up_frag ? ld16(page + g.off_up + 256 * f + 16 * r) : (u32x4){0u, 0u, 0u, 0u};
+          const u32x4 up8 = up >> 8u;
           const half8 Uh = Bhi * (_Float16)2.0f, Ul = Blo * (_Float16)2.0f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            half8 A0, A1;
-            expand2(rd(up, w), A0, A1);
-            logit[2 * w] = mfma(A0, Uh, logit[2 * w]);
-            logit[2 * w] = mfma(A0, Ul, logit[2 * w]);
-            logit[2 * w + 1] = mfma(A1, Uh, logit[2 * w + 1]);
-            logit[2 * w + 1] = mfma(A1, Ul, logit[2 * w + 1]);
+          for (int i = 0; i < 8; ++i) {
+            const half8 At = tile2(up, up8, i);
+            logit[i] = mfma(At, Uh, logit[i]);
+            logit[i] = mfma(At, Ul, logit[i]);
           }
         }
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
       bias = wave_sum_groups(bias);
       consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES, a, col);
     }
@@ -259,15 +259,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         for (int hf = 0; hf < 2; ++hf) {
           const int ks = 2 * P2 + hf;
           const half8 Bh = S.u.bq[0][ks][a][h], Bl = S.u.bq[1][ks][a][h];
+          const Row1 x = row1(rd(v, 2 * hf), rd(v, 2 * hf + 1));
 #pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            half8 At[4];
-            expand1(rd(v, 2 * hf + q2), At);
-#pragma unroll
-            for (int T = 0; T < 4; ++T) {
-              logit[4 * q2 + T] = mfma(At[T], Bh, logit[4 * q2 + T]);
-              logit[4 * q2 + T] = mfma(At[T], Bl, logit[4 * q2 + T]);
-            }
+          for (int T = 0; T < 8; ++T) {
+            const half8 At = tile1(x, T);
+            logit[T] = mfma(At, Bh, logit[T]);
+            logit[T] = mfma(At, Bl, logit[T]);
           }
         }
       }
@@ -285,7 +282,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
             const uint16_t hb = (uint16_t)(w >> (16 * (e & 1)));
             _Float16 hv;
             __builtin_memcpy(&hv, &hb, 2);
-            logit[i][e] = (float)hv * (2.0f * logit[i][e] - ssum);
+            logit[i][e] = (float)hv * fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum);
           }
         }
       }

@@ -29,12 +29,6 @@ __device__ inline uint32_t h2u(half2v h) {
   return u;
 }
 
-// fp4 pair conversion: byte `sel` of w (two nibbles 0b00cc / 0b000c) -> f16 (c_lo, c_hi)
-template <int SEL>
-__device__ inline uint32_t cvt2(uint32_t w) {
-  return h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, SEL));
-}
-
 __device__ inline half8 u4_to_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
   half8 h;
@@ -42,21 +36,32 @@ __device__ inline half8 u4_to_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
   return h;
 }
 
-// 2-bit block dword w (tiles 2w, 2w+1 of one row) -> A fragments of both tiles
-__device__ inline void expand2(uint32_t w, half8& t0, half8& t1) {
-  uint32_t we = w & 0x33333333u, wo = (w >> 2) & 0x33333333u;
-  t0 = u4_to_h8(cvt2<0>(we), cvt2<0>(wo), cvt2<1>(we), cvt2<1>(wo));
-  t1 = u4_to_h8(cvt2<2>(we), cvt2<2>(wo), cvt2<3>(we), cvt2<3>(wo));
+// Codes as MFMA operands without a conversion. In a 2-bit block row (four
+// dwords, see the page layout) the eight codes of tile T sit at bits 2T and
+// 16 + 2T of every dword; masking them out leaves binary16 subnormals
+// c * 2^(2T - 24), which the f16 MFMA multiplies exactly (gfx950 keeps f16
+// denormals). Tiles 4..7 are taken from the dwords shifted right by 8, so
+// tile T carries the factor 4^(T & 3) * 2^-24; tile_unscale undoes it.
+__device__ inline half8 tile2(const u32x4& w, const u32x4& w8, int T) {
+  const u32x4& s = T < 4 ? w : w8;
+  const uint32_t m = 0x00030003u << (2 * (T & 3));
+  return u4_to_h8(s.x & m, s.y & m, s.z & m, s.w & m);
 }
+__device__ constexpr float tile_unscale(int T) { return 16777216.0f / (float)(1 << (2 * (T & 3))); }
 
-// 1-bit dword (tiles 4q..4q+3 of one row) -> A fragments of 4 tiles
-__device__ inline void expand1(uint32_t w, half8* t) {
-  uint32_t m0 = w & 0x11111111u, m1 = (w >> 1) & 0x11111111u, m2 = (w >> 2) & 0x11111111u,
-           m3 = (w >> 3) & 0x11111111u;
-  t[0] = u4_to_h8(cvt2<0>(m0), cvt2<0>(m1), cvt2<0>(m2), cvt2<0>(m3));
-  t[1] = u4_to_h8(cvt2<1>(m0), cvt2<1>(m1), cvt2<1>(m2), cvt2<1>(m3));
-  t[2] = u4_to_h8(cvt2<2>(m0), cvt2<2>(m1), cvt2<2>(m2), cvt2<2>(m3));
-  t[3] = u4_to_h8(cvt2<3>(m0), cvt2<3>(m1), cvt2<3>(m2), cvt2<3>(m3));
+// A 1-bit block row (two dwords) with the shifted copies its tiles need:
+// tile T's bits sit at 16 h + 8 (T / 4) + 2 (T % 4) + z, so the same masks as
+// for 2-bit codes give b * 4^(T & 3) * 2^-24 (the same tile factor).
+struct Row1 {
+  uint32_t w0, w1, w0s1, w1s1, w0s8, w1s8, w0s9, w1s9;
+};
+__device__ inline Row1 row1(uint32_t w0, uint32_t w1) {
+  return Row1{w0, w1, w0 >> 1, w1 >> 1, w0 >> 8, w1 >> 8, w0 >> 9, w1 >> 9};
+}
+__device__ inline half8 tile1(const Row1& x, int T) {
+  const uint32_t m = 0x00010001u << (2 * (T & 3));
+  return T < 4 ? u4_to_h8(x.w0 & m, x.w1 & m, x.w0s1 & m, x.w1s1 & m)
+               : u4_to_h8(x.w0s8 & m, x.w1s8 & m, x.w0s9 & m, x.w1s9 & m);
 }
 
 __device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -87,15 +92,20 @@ __device__ inline void split8(const float* x, half8& hi, half8& lo) {
   }
 }
 
-__device__ inline float wave_max_groups(float v) {   // max over the 4 lane groups sharing a column
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Reductions over the 4 lane groups sharing a column (lanes 16 apart), with
+// the cross-row lane swaps: after a swap of v with itself the two results
+// hold v and its partner row's v, in one order or the other.
+__device__ inline float wave_max_groups(float v) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 __device__ inline float wave_sum_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
 // Online-softmax state of one lane (one head; one value group per pass).
@@ -152,13 +162,12 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
         B[e] = (_Float16)fmaf(p[e], (float)s8[e], 0.0f);   // one v_fma_mix (f16 source and result)
         st.z[P] = fmaf(p[e], (float)z8[e], st.z[P]);
       }
+      const u32x4 v8 = vc[ks] >> 8u;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {            // value tiles 2w, 2w+1 hold group w
         if (w / C != P) continue;
-        half8 A0, A1;
-        expand2(rd(vc[ks], w), A0, A1);
-        st.acc[2 * w] = mfma(A0, B, st.acc[2 * w]);
-        st.acc[2 * w + 1] = mfma(A1, B, st.acc[2 * w + 1]);
+        st.acc[2 * w] = mfma(tile2(vc[ks], v8, 2 * w), B, st.acc[2 * w]);
+        st.acc[2 * w + 1] = mfma(tile2(vc[ks], v8, 2 * w + 1), B, st.acc[2 * w + 1]);
       }
     }
   }
@@ -189,7 +198,8 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
   for (int u = 0; u < 8; ++u) {
     const int P = (u >> 1) / C;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) stage[(col * 8 + u) * 4 * 4 + a * 4 + e] = st.acc[u][e] + (P < NPASS ? z[P] : 0.f);
+    for (int e = 0; e < 4; ++e)   // value tiles carry the operand factor 4^(u & 3) * 2^-24
+      stage[(col * 8 + u) * 4 * 4 + a * 4 + e] = fmaf(st.acc[u][e], tile_unscale(u), P < NPASS ? z[P] : 0.f);
   }
   __syncthreads();
   const int h = col % G, jl = col / G;

@@ -47,6 +47,17 @@ __device__ inline u32x4 lds16(const uint8_t* p) { return *reinterpret_cast<const
 
 constexpr int META_SLOT = 3072;
 
+// Wave priority by progress through the split: waves with more pages left
+// issue first, so the two waves sharing a SIMD tend to finish together
+// rather than one running alone (with no latency hiding) at the end.
+__device__ inline void progress_prio(int it, int np) {
+  const int q = (4 * it) / (np > 0 ? np : 1);
+  if (q == 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Shared memory of the MixKVQ / PN-Mix kernels. The page-loop tables and the
 // BF16-segment / partial staging buffer (8 KB) share one union; the bf16
 // query is staged in the value-meta half of slot 1 during set-up.
@@ -124,6 +135,7 @@ __device__ inline void commit_meta(const u32x4 (&m)[3], uint8_t* slot, int lane)
 template <class KP, class VP, class LK, class LV, class PG>
 __device__ inline void page_loop(int np, KP (&k)[2], VP (&v)[2], LK load_k, LV load_v, PG page) {
   for (int it = 0; it < np; it += 2) {
+    progress_prio(it, np);
     if (it + 1 < np) load_k(k[1], it + 1);
     page(k[0], v[0], 0, [&] {
       if (it + 1 < np) load_v(v[1], it + 1);
@@ -200,14 +212,15 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
     const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
+    const u32x4 k8 = c.kc[ks] >> 8u;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      half8 A0, A1;
-      expand2(rd(c.kc[ks], w), A0, A1);
-      logit[2 * w] = mfma(A0, B, logit[2 * w]);
-      logit[2 * w + 1] = mfma(A1, B, logit[2 * w + 1]);
+      logit[2 * w] = mfma(tile2(c.kc[ks], k8, 2 * w), B, logit[2 * w]);
+      logit[2 * w + 1] = mfma(tile2(c.kc[ks], k8, 2 * w + 1), B, logit[2 * w + 1]);
     }
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);   // code operands carry 4^(i & 3) * 2^-24
   if constexpr (NB > 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -298,6 +311,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   const float xs = A.scale_log2 * B_UNSCALE;
 
   for (int it = 0; it < np; it += 2) {
+    progress_prio(it, np);
     // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
     if (it + 1 < np) {
       mix_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.pg.meta[1], g, lane);
@@ -349,24 +363,20 @@ __device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, c
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
     const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
+    {                                       // LSB plane: 1-bit codes, weight s
+      const Row1 x = row1(rd(c.lsb[ks >> 1], 2 * (ks & 1)), rd(c.lsb[ks >> 1], 2 * (ks & 1) + 1));
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {        // LSB plane: 1-bit codes, weight s
-      half8 At[4];
-      expand1(rd(c.lsb[ks >> 1], 2 * (ks & 1) + q2), At);
-#pragma unroll
-      for (int T = 0; T < 4; ++T) logit[4 * q2 + T] = mfma(At[T], B, logit[4 * q2 + T]);
+      for (int T = 0; T < 8; ++T) logit[T] = mfma(tile1(x, T), B, logit[T]);
     }
     if (ks < 2) {                           // upper two bits of the high channels, weight 2 s
       const half8 U = B * (_Float16)2.0f;
+      const u32x4 u8 = c.up[ks] >> 8u;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        half8 A0, A1;
-        expand2(rd(c.up[ks], w), A0, A1);
-        logit[2 * w] = mfma(A0, U, logit[2 * w]);
-        logit[2 * w + 1] = mfma(A1, U, logit[2 * w + 1]);
-      }
+      for (int i = 0; i < 8; ++i) logit[i] = mfma(tile2(c.up[ks], u8, i), U, logit[i]);
     }
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
   join_halves(logit);
 }
 
@@ -470,13 +480,9 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey& c, const uint8_t*
     for (int hf = 0; hf < 2; ++hf) {
       const int ks = 2 * P2 + hf;
       const half8 B = S.u.qj.bq[col >> 3][ks][a][h];   // hi part in columns < 8, lo part above
+      const Row1 x = row1(rd(c.bits[P2], 2 * hf), rd(c.bits[P2], 2 * hf + 1));
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        half8 At[4];
-        expand1(rd(c.bits[P2], 2 * hf + q2), At);
-#pragma unroll
-        for (int T = 0; T < 4; ++T) logit[4 * q2 + T] = mfma(At[T], B, logit[4 * q2 + T]);
-      }
+      for (int T = 0; T < 8; ++T) logit[T] = mfma(tile1(x, T), B, logit[T]);
     }
   }
   join_halves(logit);
@@ -494,7 +500,7 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey& c, const uint8_t*
         const uint16_t hb = (uint16_t)(w >> (16 * (e & 1)));
         _Float16 hv;
         __builtin_memcpy(&hv, &hb, 2);
-        logit[i][e] = (float)hv * (2.0f * logit[i][e] - ssum);
+        logit[i][e] = (float)hv * fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum);
       }
     }
   }

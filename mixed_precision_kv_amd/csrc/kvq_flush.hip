@@ -22,8 +22,6 @@
 
 namespace kvq {
 
-// 0 2 1 3 4 6 5 7: swaps bits 0 and 1 of a 3-bit index
-__device__ constexpr int swap01(int k) { return (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1); }
 
 // 16 bytes per group; M - m is recomputed exactly in double from m and M.
 struct GroupParam {
@@ -224,35 +222,35 @@ __device__ __attribute__((always_inline)) inline void flush_value_part(uint8_t* 
     if (half == 0) S.vp[gi] = make_param(sc, 3, flags);
   }
   __syncthreads();
-  {  // code unit (a, r), word w: V-tiles 2w, 2w+1 (value group w) of the 8 tokens pi(s, a, k)
+  {  // code unit (a, r), word w: every V-tile u (channel 16 u + r) of the two tokens pi(s, a, 2w + hh);
+     // the code of (u, hh) sits at bits 2 u + 16 hh
     const int t = threadIdx.x, a = t >> 6, r = (t >> 2) & 15, w = t & 3;
-    float m[8], inv[8], x[16];
+    float m[2][4], inv[2][4], x[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int tl = 16 * (k >> 2) + 4 * a + (k & 3);   // pi(s, a, k) - 32 s
-      m[k] = S.vp[tl * 4 + w].m;
-      inv[k] = S.vp[tl * 4 + w].inv;
-    }
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = 2 * w + hh, tl = 16 * (k >> 2) + 4 * a + (k & 3);   // pi(s, a, k) - 32 s
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int u = 2 * w + (p >> 3), k = swap01(p & 7);
-      const int tl = 16 * (k >> 2) + 4 * a + (k & 3);
-      x[p] = bf16_to_f32(S.tile[tl * D + 16 * u + r]);
+      for (int j = 0; j < 4; ++j) {
+        m[hh][j] = S.vp[tl * 4 + j].m;
+        inv[hh][j] = S.vp[tl * 4 + j].inv;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[8 * hh + u] = bf16_to_f32(S.tile[tl * D + 16 * u + r]);
     }
     uint32_t word = 0, redo = 0;
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
-      const int k = swap01(p & 7);
+      const int u = p & 7, hh = p >> 3;
       bool amb;
-      word |= (uint32_t)fast_code(m[k], inv[k], x[p], amb) << (2 * p);
+      word |= (uint32_t)fast_code(m[hh][u >> 1], inv[hh][u >> 1], x[p], amb) << (2 * p);
       redo |= (uint32_t)amb << p;
     }
     while (redo) {   // the few codes within 2^-14 of a rounding midpoint, one by one
       const int p = __builtin_ctz(redo);
       redo &= redo - 1;
-      const int u = 2 * w + (p >> 3), k = swap01(p & 7);
+      const int u = p & 7, k = 2 * w + (p >> 3);
       const int tl = 16 * (k >> 2) + 4 * a + (k & 3);
-      const uint32_t c = quant_code_exact(S.vp[tl * 4 + w], 3, bf16_to_f32(S.tile[tl * D + 16 * u + r]));
+      const uint32_t c = quant_code_exact(S.vp[tl * 4 + (u >> 1)], 3, bf16_to_f32(S.tile[tl * D + 16 * u + r]));
       word = (word & ~(3u << (2 * p))) | c << (2 * p);
     }
     store4(page_v + 1024 * s + 256 * a + 16 * r + 4 * w, word);
@@ -349,37 +347,35 @@ __device__ __attribute__((always_inline)) inline void flush_mix_key_part(const F
     }
   }
   __syncthreads();
-  {  // code fragment f, token row r, word w (tiles 2w, 2w+1)
+  {  // code fragment f, token row r, word w: slots 8f + 2w + hh of every tile u (token 16 u + r);
+     // the code of (u, hh) sits at bits 2 u + 16 hh
     const int t = threadIdx.x, f = 4 * fg + (t >> 6), r = (t >> 2) & 15, w = t & 3;
     if (f < g.F) {
-      int info[8];
-      float m[8], inv[8], x[16];
+      int info[2];
+      float m[2], inv[2], x[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        info[k] = S.kinfo[8 * (t >> 6) + k];
-        const GroupParam& q = S.kp[(info[k] >> 12) & 255];
-        m[k] = q.m;
-        inv[k] = q.inv;
-      }
+      for (int hh = 0; hh < 2; ++hh) {
+        info[hh] = S.kinfo[8 * (t >> 6) + 2 * w + hh];
+        const GroupParam& q = S.kp[(info[hh] >> 12) & 255];
+        m[hh] = q.m;
+        inv[hh] = q.inv;
 #pragma unroll
-      for (int pp = 0; pp < 16; ++pp) {
-        const int tok = 16 * (2 * w + (pp >> 3)) + r;
-        x[pp] = bf16_to_f32(S.tile[tok * KS + (info[swap01(pp & 7)] & 255)]);
+        for (int u = 0; u < 8; ++u) x[8 * hh + u] = bf16_to_f32(S.tile[(16 * u + r) * KS + (info[hh] & 255)]);
       }
       uint32_t word = 0, redo = 0;
 #pragma unroll
       for (int pp = 0; pp < 16; ++pp) {
-        const int k = swap01(pp & 7);
+        const int hh = pp >> 3;
         bool amb;
-        const int full = fast_code(m[k], inv[k], x[pp], amb);
-        word |= (uint32_t)((full >> ((info[k] >> 8) & 3)) & ((info[k] >> 10) & 3)) << (2 * pp);
+        const int full = fast_code(m[hh], inv[hh], x[pp], amb);
+        word |= (uint32_t)((full >> ((info[hh] >> 8) & 3)) & ((info[hh] >> 10) & 3)) << (2 * pp);
         redo |= (uint32_t)amb << pp;
       }
       while (redo) {   // the few codes within 2^-14 of a rounding midpoint, one by one
         const int pp = __builtin_ctz(redo);
         redo &= redo - 1;
-        const int in = S.kinfo[8 * (t >> 6) + swap01(pp & 7)];
-        const int tok = 16 * (2 * w + (pp >> 3)) + r;
+        const int in = S.kinfo[8 * (t >> 6) + 2 * w + (pp >> 3)];
+        const int tok = 16 * (pp & 7) + r;
         const float xv = bf16_to_f32(S.tile[tok * KS + (in & 255)]);
         const int full = quant_code_exact(S.kp[(in >> 12) & 255], (in >> 20) ? 15 : 3, xv);
         const uint32_t c = (uint32_t)((full >> ((in >> 8) & 3)) & ((in >> 10) & 3));
@@ -469,10 +465,9 @@ __device__ __attribute__((always_inline)) inline void flush_pn_key_part(const Fl
       const int P = u >> 6, a = (u >> 4) & 3, r = u & 15, half = wq >> 1, q = wq & 1;
       const int f = 4 * (2 * P + half) + a;
       uint32_t word = 0;
-      for (int bit = 0; bit < 32; ++bit) {
-        const int bb = bit & 7;
-        const int slot = 8 * f + 2 * (bb & 3) + (bb >> 2);
-        const int t = 16 * (4 * q + (bit >> 3)) + r;
+      for (int bit = 0; bit < 32; ++bit) {   // tile T, element 4 z + 2 q + h at bit 16 h + 8 (T / 4) + 2 (T % 4) + z
+        const int slot = 8 * f + 4 * (bit & 1) + 2 * q + (bit >> 4);
+        const int t = 16 * (4 * ((bit >> 3) & 1) + ((bit >> 1) & 3)) + r;
         const float x = bf16_to_f32(S.tile[t * KS + S.ch[slot]]);
         const int code = slot < nhs ? quant_code(S.kp[slot], 7, x) : mid_code(S.kp[slot], x);
         word |= (uint32_t)(code & 1) << bit;
@@ -485,9 +480,9 @@ __device__ __attribute__((always_inline)) inline void flush_pn_key_part(const Fl
       if (wi < n_up) {
         const int f = wi >> 6, r = (wi >> 2) & 15, w = wi & 3;
         uint32_t word = 0;
-        for (int pp = 0; pp < 16; ++pp) {
-          const int t = 16 * (2 * w + (pp >> 3)) + r;
-          const int slot = 8 * f + swap01(pp & 7);
+        for (int pp = 0; pp < 16; ++pp) {   // tile pp & 7, element 2 w + pp / 8 at bits 2 pp
+          const int t = 16 * (pp & 7) + r;
+          const int slot = 8 * f + 2 * w + (pp >> 3);
           int code = 0;
           if (slot < n_hi) code = quant_code(S.kp[slot], 7, bf16_to_f32(S.tile[t * KS + S.ch[slot]])) >> 1;
           word |= (uint32_t)code << (2 * pp);
@@ -589,10 +584,9 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
     const int t = threadIdx.x, u = t >> 2, wq = t & 3, aa = u >> 4, rr = u & 15, half = wq >> 1, q = wq & 1;
     const int fl = 4 * half + aa;         // fragment 8 P + fl, local rows 8 fl .. 8 fl + 7
     uint32_t word = 0;
-    for (int bit = 0; bit < 32; ++bit) {
-      const int bb = bit & 7;
-      const int il = 8 * fl + 2 * (bb & 3) + (bb >> 2);
-      const int tok = 16 * (4 * q + (bit >> 3)) + rr;
+    for (int bit = 0; bit < 32; ++bit) {   // tile T, element 4 z + 2 q + h at bit 16 h + 8 (T / 4) + 2 (T % 4) + z
+      const int il = 8 * fl + 4 * (bit & 1) + 2 * q + (bit >> 4);
+      const int tok = 16 * (4 * ((bit >> 3) & 1) + ((bit >> 1) & 3)) + rr;
       word |= ((S.bits[il * 4 + (tok >> 5)] >> (tok & 31)) & 1u) << bit;
     }
     store4(page + 1024 * P + 256 * aa + 16 * rr + 4 * wq, word);

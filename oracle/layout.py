@@ -11,20 +11,20 @@ states the order this library uses, written out independently of the HIP
 kernels; both must produce identical bytes.
 
 Conventions used below. A page holds tokens t = 0..127; tile i = t // 16 and
-row r = t % 16, so t = 16*i + r. SWAP = [0, 2, 1, 3, 4, 6, 5, 7].
+row r = t % 16, so t = 16*i + r.
 
 2-bit block (256 bytes) of an array X[r][i][k] (r < 16, i < 8, k < 8): the
-little-endian dword at byte 16*r + 4*w (w < 4) holds, at bits 2p and 2p+1,
-X[r][2*w + p//8][SWAP[p % 8]] for p = 0..15. Within every byte the lower code
-sits in the lower bits, as in the KIVI ``pack2`` rule.
+little-endian dword at byte 16*r + 4*w (w < 4) holds, for every tile i, the
+code X[r][i][2w] at bits 2i, 2i+1 and the code X[r][i][2w+1] at bits 16+2i,
+16+2i+1. So each byte is a run of four codes of one element along the tile
+axis, the lower code in the lower bits as in the KIVI ``pack2`` rule, and the
+codes of one tile sit at the same bit position in both 16-bit halves of all
+four dwords (the decode kernels mask a tile out of the dwords directly).
 
-1-bit block row (8 bytes) of X[r][i][k]: byte i holds, at bit b,
-X[r][i][2*(b % 4) + b//4].
-
-A 1-bit region stores its fragments (8 slots x 128 tokens) in pairs: for
-pair index P and lane group a < 4, the 16 bytes at 1024*P + 256*a + 16*r are
-row r of fragment 4*(2P) + a followed by row r of fragment 4*(2P+1) + a.
-A 2-bit region stores fragment f (256 bytes) at 256*f.
+1-bit block row (8 bytes) of X[r][i][k]: the little-endian dword w' < 2 at
+byte 4*w' holds X[r][i][4z + 2w' + h] at bit 16h + 8(i // 4) + 2(i % 4) + z
+(z, h < 2), so that tile i's bits sit, like its 2-bit codes, at the
+positions 2(i % 4) (+1) of one byte of each 16-bit half.
 
 The value-code region (4096 bytes) holds, for k-step s < 4 and lane group
 a < 4, a 2-bit block at 1024*s + 256*a with X[r][u][k] = code of
@@ -44,7 +44,6 @@ from .numerics import f16_fraction, rn_f16_meta_bits
 
 PAGE = 128
 D = 128
-SWAP = (0, 2, 1, 3, 4, 6, 5, 7)
 V_CODE_BYTES = 4096
 V_META_BYTES = 2048
 
@@ -65,8 +64,9 @@ def pack2_block(X) -> np.ndarray:
     for r in range(16):
         for w in range(4):
             word = 0
-            for p in range(16):
-                word |= int(X[r, 2 * w + p // 8, SWAP[p % 8]]) << (2 * p)
+            for i in range(8):
+                word |= int(X[r, i, 2 * w]) << (2 * i)
+                word |= int(X[r, i, 2 * w + 1]) << (16 + 2 * i)
             out[r, w] = word
     return out.astype("<u4").view(np.uint8).reshape(-1)
 
@@ -77,8 +77,9 @@ def unpack2_block(buf) -> np.ndarray:
     for r in range(16):
         for w in range(4):
             word = int(words[r, w])
-            for p in range(16):
-                X[r, 2 * w + p // 8, SWAP[p % 8]] = (word >> (2 * p)) & 3
+            for i in range(8):
+                X[r, i, 2 * w] = (word >> (2 * i)) & 3
+                X[r, i, 2 * w + 1] = (word >> (16 + 2 * i)) & 3
     return X
 
 
@@ -86,23 +87,29 @@ def pack1_rows(X) -> np.ndarray:
     """[16][8][8] bits -> 16 rows x 8 bytes."""
     X = np.asarray(X, dtype=np.uint8)
     assert X.shape == (16, 8, 8) and X.max(initial=0) <= 1
-    out = np.zeros((16, 8), dtype=np.uint8)
+    out = np.zeros((16, 2), dtype=np.uint32)
     for r in range(16):
-        for i in range(8):
-            byte = 0
-            for b in range(8):
-                byte |= int(X[r, i, 2 * (b % 4) + b // 4]) << b
-            out[r, i] = byte
-    return out
+        for w in range(2):
+            word = 0
+            for i in range(8):
+                for z in range(2):
+                    for h in range(2):
+                        word |= int(X[r, i, 4 * z + 2 * w + h]) << (16 * h + 8 * (i // 4) + 2 * (i % 4) + z)
+            out[r, w] = word
+    return out.astype("<u4").view(np.uint8).reshape(16, 8)
 
 
 def unpack1_rows(rows) -> np.ndarray:
     rows = np.asarray(rows, dtype=np.uint8).reshape(16, 8)
+    words = np.frombuffer(rows.tobytes(), dtype="<u4").reshape(16, 2)
     X = np.zeros((16, 8, 8), dtype=np.uint8)
     for r in range(16):
-        for i in range(8):
-            for b in range(8):
-                X[r, i, 2 * (b % 4) + b // 4] = (int(rows[r, i]) >> b) & 1
+        for w in range(2):
+            word = int(words[r, w])
+            for i in range(8):
+                for z in range(2):
+                    for h in range(2):
+                        X[r, i, 4 * z + 2 * w + h] = (word >> (16 * h + 8 * (i // 4) + 2 * (i % 4) + z)) & 1
     return X
 
 

@@ -91,17 +91,17 @@ def test_packing_low_bits_first(kivi):
     pk = kivi["packing"]
     codes, _, _ = quantize_groups(bf(pk["group"])[None, :], 2)
     assert codes[0].tolist() == pk["codes"]
-    # the byte holding block positions 0..3 follows the low-bits-first rule
+    # a byte of a block holds four codes along the tile axis, low bits first
     X = np.zeros((16, 8, 8), np.uint8)
     for p, c in enumerate(pk["codes"]):
-        X[0, 0, layout.SWAP[p]] = c
+        X[0, p, 0] = c
     blob = layout.pack2_block(X)
     assert blob[0] == pk["packed_byte"] and not blob[1:].any()
     assert np.array_equal(layout.unpack2_block(blob), X)
     # a short row: three codes occupy one byte, the padding is not a code
     X2 = np.zeros((16, 8, 8), np.uint8)
     for p, c in enumerate(pk["short_codes"]):
-        X2[0, 0, layout.SWAP[p]] = c
+        X2[0, p, 0] = c
     b2 = layout.pack2_block(X2)
     assert b2[0] == sum(c << (2 * i) for i, c in enumerate(pk["short_codes"]))
 
