@@ -309,54 +309,48 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, con
   }
 }
 
-// log-sum-exp merge of the split partials: one workgroup per query head.
-// Every part's (m, l) is read in parallel (one part per thread), the weights
-// 2^(m_s - M) go through LDS, then thread ch sums its channel over the parts
-// with independent loads.
-__global__ __launch_bounds__(128) void combine_kernel(const float* partial, float* out, int n_parts, int rows) {
-  const int row = blockIdx.x, t = threadIdx.x;
-  __shared__ float wsh[128];
-  __shared__ float red[4];
-  float mloc = -INFINITY;
-  for (int s = t; s < n_parts; s += 128) mloc = fmaxf(mloc, partial[((int64_t)s * rows + row) * RECORD]);
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-  if ((t & 63) == 0) red[t >> 6] = mloc;
-  __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  float l = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < n_parts; s0 += 128) {
-      const int s = s0 + t;
-      float wv = 0.f;
-      if (s < n_parts) {
-        const float* rec = partial + ((int64_t)s * rows + row) * RECORD;
-        const float ms = rec[0];
-        wv = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-        l = fmaf(wv, rec[1], l);
-      }
-      __syncthreads();
-      wsh[t] = wv;
-      __syncthreads();
-      const int n = min(128, n_parts - s0);
-      const float* base = partial + ((int64_t)s0 * rows + row) * RECORD + 2 + t;
-      int j = 0;
-      for (; j + 4 <= n; j += 4) {
-        const float v0 = base[(int64_t)(j + 0) * rows * RECORD], v1 = base[(int64_t)(j + 1) * rows * RECORD];
-        const float v2 = base[(int64_t)(j + 2) * rows * RECORD], v3 = base[(int64_t)(j + 3) * rows * RECORD];
-        acc = fmaf(wsh[j], v0, acc);
-        acc = fmaf(wsh[j + 1], v1, acc);
-        acc = fmaf(wsh[j + 2], v2, acc);
-        acc = fmaf(wsh[j + 3], v3, acc);
-      }
-      for (; j < n; ++j) acc = fmaf(wsh[j], base[(int64_t)j * rows * RECORD], acc);
+// log-sum-exp merge of the split partials: one wave per query head, lane l
+// owning channels 2l and 2l+1. Parts are taken 32 at a time: every load of a
+// batch (the 32 records' m and l and the lane's two channels) is issued
+// before any is used, and the batch is folded into a running maximum, so a
+// call with up to 32 parts costs one memory round trip.
+__global__ __launch_bounds__(64) void combine_kernel(const float* partial, float* out, int n_parts, int rows) {
+  constexpr int NB = 32;
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const int64_t stride = (int64_t)rows * RECORD;           // from one part's record to the next
+  const float* base = partial + (int64_t)row * RECORD;
+  float M = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < n_parts; s0 += NB) {
+    float ms[NB], ls[NB], v0[NB], v1[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {                          // clamped: in bounds, weight 0 past the end
+      const float* rec = base + min(s0 + j, n_parts - 1) * stride;
+      ms[j] = s0 + j < n_parts ? rec[0] : -INFINITY;
+      ls[j] = rec[1];
+      v0[j] = rec[2 + 2 * lane];
+      v1[j] = rec[3 + 2 * lane];
     }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bm = fmaxf(bm, ms[j]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) continue;
+    const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    l *= alpha;
+    o0 *= alpha;
+    o1 *= alpha;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float w = ms[j] == -INFINITY ? 0.f : fast_exp2(ms[j] - Mn);
+      l = fmaf(w, ls[j], l);
+      o0 = fmaf(w, v0[j], o0);
+      o1 = fmaf(w, v1[j], o1);
+    }
+    M = Mn;
   }
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-  __syncthreads();
-  if ((t & 63) == 0) red[2 + (t >> 6)] = l;
-  __syncthreads();
-  const float L = red[2] + red[3];
-  out[(int64_t)row * D + t] = L > 0.f ? acc / L : 0.f;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  out[(int64_t)row * D + 2 * lane] = o0 * inv;
+  out[(int64_t)row * D + 2 * lane + 1] = o1 * inv;
 }
 
 bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s);
@@ -404,7 +398,7 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
   }
   const bool segment = a.n_sink + a.n_resid > 0;
   if (a.n_page_splits + (segment ? 1 : 0) == 0) {   // nothing to attend to: every output row is zero
-    hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, s, a.partial, a.out, 0,
+    hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a.partial, a.out, 0,
                        a.batch * a.n_q_heads);
     return hipGetLastError();
   }
@@ -422,7 +416,7 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
     else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(128), 0, s, a.partial, a.out,
+  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a.partial, a.out,
                      a.n_page_splits + (segment ? 1 : 0), a.batch * a.n_q_heads);
   return hipGetLastError();
 }
