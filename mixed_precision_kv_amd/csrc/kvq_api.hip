@@ -50,15 +50,16 @@ static size_t record_bytes(const kvq_config* c) {
   return 0;
 }
 
-static int n_page_splits(const kvq_config* c, int n_pages, bool segment) {
+static int n_page_splits(const kvq_config* c, int n_pages, int n_seg) {
   if (n_pages <= 0) return 0;
-  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads, segment);
+  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads, n_seg);
   return (n_pages + pps - 1) / pps;
 }
 
 static size_t workspace_for(const kvq_config* c, int n_pages) {
-  // the split count without a BF16 segment is the larger one
-  size_t splits = (size_t)n_page_splits(c, n_pages, false) + 1;
+  // page splits shrink as segment workgroups are added: the page split count
+  // without a segment plus the most segment workgroups bounds every call
+  size_t splits = (size_t)n_page_splits(c, n_pages, 0) + MAX_SEG_SPLITS;
   size_t rows = (size_t)c->batch * c->n_q_heads;
   size_t bytes = splits * rows * 130 * sizeof(float);
   if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)c->qjl_m * sizeof(float);
@@ -221,7 +222,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   if (!q || !out || !workspace || !aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_INVALID_ARG;
   if (n_pages < 0 || n_pages > cfg->max_pages) return KVQ_INVALID_ARG;
   if (n_pages > 0 && (!page_arena || !aligned16(page_arena))) return KVQ_INVALID_ARG;
-  if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
+  if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
   if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
   if (n_sink < 0 || n_sink > PAGE || n_resid < 0 || n_resid > PAGE) return KVQ_INVALID_ARG;
   if (n_sink > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v))) return KVQ_INVALID_ARG;
@@ -235,12 +236,12 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   a.page_stride = (int64_t)page_stride(cfg);
   a.max_pages = cfg->max_pages;
   a.n_pages = n_pages;
-  const bool segment = n_sink + n_resid > 0;
-  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads, segment) : 1;
-  a.n_page_splits = n_page_splits(cfg, n_pages, segment);
+  a.n_seg_splits = seg_splits(n_sink + n_resid);
+  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads, a.n_seg_splits) : 1;
+  a.n_page_splits = n_page_splits(cfg, n_pages, a.n_seg_splits);
   a.mask = (const uint8_t*)mask;
   const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
-  const size_t part_bytes = ((size_t)a.n_page_splits + 1) * rows * 130 * sizeof(float);
+  const size_t part_bytes = ((size_t)a.n_page_splits + MAX_SEG_SPLITS) * rows * 130 * sizeof(float);
   a.partial = (float*)workspace;
   a.sq = (const float*)((uint8_t*)workspace + part_bytes);
   a.out = out;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   const int hq = kvh * G + h;
   const uint16_t* qrow = A.q + ((int64_t)b * A.n_q_heads + hq) * D;
 
-  if (split == A.n_page_splits) {
+  if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
     return;
   }
@@ -156,7 +156,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         }
       }
       bias = wave_sum_groups(bias);
-      consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES, a, col);
+      consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES,
+                                page + g.off_v + V_CODE_BYTES + 1024, a, col);
     }
   } else if constexpr (MODE == KVQ_KEY_PNMIX) {
     const PnGeo g = pn_geo(A.n_hi);
@@ -222,7 +223,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
       bias = wave_sum_groups(bias);
-      consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES, a, col);
+      consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES,
+                                page + g.off_v + V_CODE_BYTES + 1024, a, col);
     }
   } else {   // QJL
     const QjlGeo g = qjl_geo(A.qjl_m);
@@ -286,7 +288,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
           }
         }
       }
-      consume_values<G, NPASS>(st, logit, xs, 0.f, vc, page + g.off_v + V_CODE_BYTES, a, col);
+      consume_values<G, NPASS>(st, logit, xs, 0.f, vc, page + g.off_v + V_CODE_BYTES,
+                                page + g.off_v + V_CODE_BYTES + 1024, a, col);
     }
   }
   __syncthreads();
@@ -355,15 +358,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* partial, float
 
 bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s);
 
-// Pages per split: the page splits of every (batch, kv head) plus, when the
-// call has sink or residual tokens, one BF16-segment workgroup per (batch, kv
-// head) are sized to fill `slots` resident workgroups in one round, with the
-// pages spread evenly. DECODE_SLOTS (256 CUs x 8 resident single-wave
-// workgroups on MI355X) bounds every kernel's split count, and the workspace
-// is sized for it.
-int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, bool segment, int slots) {
+// Pages per split: the page splits of every (batch, kv head) plus its n_seg
+// BF16-segment workgroups (one per SEG_TOKENS sink / residual tokens) are
+// sized to fill `slots` resident workgroups in one round, with the pages
+// spread evenly. DECODE_SLOTS (256 CUs x 8 resident single-wave workgroups on
+// MI355X) bounds every kernel's split count, and the workspace is sized for it.
+int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int n_seg, int slots) {
   const int64_t pairs = (int64_t)batch * n_kv_heads;
-  const int64_t budget = (int64_t)slots - (segment ? pairs : 0);
+  const int64_t budget = (int64_t)slots - pairs * n_seg;
   int64_t splits = budget / pairs;
   if (splits < 1) splits = 1;
   int64_t pps = (n_pages + splits - 1) / splits;
@@ -371,8 +373,8 @@ int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, bool se
   return (int)pps;
 }
 
-int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, bool segment) {
-  return decode_pages_per_split_slots(n_pages, batch, n_kv_heads, segment, DECODE_SLOTS);
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, int n_seg) {
+  return decode_pages_per_split_slots(n_pages, batch, n_kv_heads, n_seg, DECODE_SLOTS);
 }
 
 template <int MODE>
@@ -396,8 +398,8 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const bool segment = a.n_sink + a.n_resid > 0;
-  if (a.n_page_splits + (segment ? 1 : 0) == 0) {   // nothing to attend to: every output row is zero
+  const int n_parts = a.n_page_splits + a.n_seg_splits;
+  if (n_parts == 0) {   // nothing to attend to: every output row is zero
     hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a.partial, a.out, 0,
                        a.batch * a.n_q_heads);
     return hipGetLastError();
@@ -410,14 +412,14 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
   if (fast) {
     e = hipGetLastError();
   } else {
-    dim3 grid(a.n_page_splits + (segment ? 1 : 0), a.n_kv_heads, a.batch);
+    dim3 grid(n_parts, a.n_kv_heads, a.batch);
     if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
     else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
     else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a.partial, a.out,
-                     a.n_page_splits + (segment ? 1 : 0), a.batch * a.n_q_heads);
+                     n_parts, a.batch * a.n_q_heads);
   return hipGetLastError();
 }
 

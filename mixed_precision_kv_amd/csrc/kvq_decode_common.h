@@ -22,6 +22,14 @@ constexpr int RECORD = 130;            // partial record per query head: m, l, o
 __device__ inline uint32_t rd(const u32x4& v, int i) { return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w)); }
 
 __device__ inline u32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// Byte idx of a record held one dword per lane (lane l: bytes 4l .. 4l+3);
+// every lane of the wave must execute it.
+__device__ inline int rec_byte(uint32_t recw, int idx) {
+  const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (idx >> 2), (int)recw);
+  return (int)((w >> (8 * (idx & 3))) & 0xffu);
+}
 
 __device__ inline uint32_t h2u(half2v h) {
   uint32_t u;
@@ -121,7 +129,8 @@ struct SoftState {
 // (token 16 i + 4 a + e); the log2-domain logit is logit * xs + xb.
 template <int G, int NPASS>
 __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)[8], float xs, float xb,
-                                      const u32x4 (&vc)[4], const uint8_t* vmeta, int a, int col) {
+                                      const u32x4 (&vc)[4], const uint8_t* vm_lo, const uint8_t* vm_hi, int a,
+                                      int col) {
   constexpr int C = 16 / G;
   float pm = -INFINITY;
 #pragma unroll
@@ -154,7 +163,7 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
       const int j = (jl + P * C) & 3;            // this lane's value group in pass P
-      const uint8_t* mb = vmeta + 512 * ks + 128 * a + 32 * j;
+      const uint8_t* mb = (ks < 2 ? vm_lo : vm_hi) + 512 * (ks & 1) + 128 * a + 32 * j;
       const half8 s8 = as_half8(ld16(mb)), z8 = as_half8(ld16(mb + 16));
       half8 B;
 #pragma unroll
@@ -283,19 +292,23 @@ __device__ inline bf16x8 as_bf16x8(const u32x4& v) {
   return r;
 }
 
-// BF16 segment (attention sinks + residual), one wave, in chunks of 32
-// tokens: all Key and Value loads of a chunk are issued together; q.k runs on
-// the bf16 MFMA (exact products); each lane turns its own 8 logits into
-// probabilities against the running per-head maximum and stages them in LDS;
-// p.V runs on the VALU with each lane owning two channels of every head.
-// Writes the split's partial record. p_lds needs 32 x 8 floats, mh 16.
+// BF16 segment (attention sinks + residual): workgroup split - n_page_splits
+// takes segment tokens [SEG_TOKENS c, SEG_TOKENS (c + 1)), so the segment's
+// memory latency is paid once, in parallel, rather than once per chunk.
+// One wave, in chunks of 32 tokens: all Key and Value loads of a chunk are
+// issued together; q.k runs on the bf16 MFMA (exact products); each lane
+// turns its own 8 logits into probabilities against the running per-head
+// maximum and stages them in LDS; p.V runs on the VALU with each lane owning
+// two channels of every head. Writes the split's partial record. p_lds needs
+// 32 x 8 floats, mh 16.
 template <int G>
 __device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int kvh, int lane, float (*p_lds)[8],
                                     float* mh) {
   const int a = lane >> 4, r = lane & 15, col = r, h = col % G;
   const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
   const uint16_t* qrow = A.q + ((int64_t)b * A.n_q_heads + kvh * G + h) * D;
-  const int T = A.n_sink + A.n_resid;
+  const int t_lo = SEG_TOKENS * (split - A.n_page_splits);
+  const int T = min(A.n_sink + A.n_resid, t_lo + SEG_TOKENS);   // end of this workgroup's tokens
   bf16x8 Bq[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -306,24 +319,26 @@ __device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int k
   float o[G][2], lsum[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) o[hh][0] = o[hh][1] = lsum[hh] = 0.f;
-  for (int t0 = 0; t0 < T; t0 += 32) {
+  for (int t0 = t_lo; t0 < T; t0 += 32) {
+    // Unconditional loads (straight-line issue, one wait): a token past T
+    // reads token T-1 again; its logit is -inf, so its probability is 0 and
+    // its finite row adds nothing.
     u32x4 kr[2][4];
     uint32_t vr[32];
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
-      const int t = t0 + 16 * i2 + r;        // A row = token
+      const int t = min(t0 + 16 * i2 + r, T - 1);   // A row = token
       const uint16_t* krow = t < A.n_sink ? A.sink_k + (head * A.n_sink + t) * D
                                           : A.resid_k + (head * A.resid_stride + (t - A.n_sink)) * D;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kr[i2][ks] = t < T ? ld16(reinterpret_cast<const uint8_t*>(krow + 32 * ks + 8 * a)) : (u32x4){0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < 4; ++ks) kr[i2][ks] = ld16(reinterpret_cast<const uint8_t*>(krow + 32 * ks + 8 * a));
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const int t = t0 + j;
+      const int t = min(t0 + j, T - 1);
       const uint16_t* vrow = t < A.n_sink ? A.sink_v + (head * A.n_sink + t) * D
                                           : A.resid_v + (head * A.resid_stride + (t - A.n_sink)) * D;
-      vr[j] = t < T ? reinterpret_cast<const uint32_t*>(vrow)[lane] : 0u;
+      vr[j] = reinterpret_cast<const uint32_t*>(vrow)[lane];
     }
     float x[2][4];
     float cm = -INFINITY;

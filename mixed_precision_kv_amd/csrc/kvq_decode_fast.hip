@@ -33,10 +33,15 @@ __device__ inline void async16(const uint8_t* src, uint8_t* lds_base) {
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
-// The memory clobber keeps the compiler from moving LDS reads above it.
+// Emitted through the builtin (not inline asm) so that the compiler's own
+// wait insertion knows which loads have completed: otherwise, with an
+// asynchronous LDS copy in flight, it drains every load before the first use
+// of a register loaded earlier. gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt (7) and lgkmcnt (15) left at "no wait".
 template <int N>
 __device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Wait for this wave's LDS operations (orders plain LDS stores before an
@@ -72,6 +77,22 @@ struct PgSmem {
     float p_lds[256][8];
   } u;
   int slot_ch[32 * NKS];
+  float mh[16];
+};
+
+// Shared memory of the MixKVQ kernel. The page metadata lives in six
+// separate 1 KB arrays (MixMeta), one per asynchronous copy: distinct LDS
+// objects let the compiler see that a copy in flight for the next page does
+// not alias this page's metadata, so its waits stay exact.
+template <int G, int NKS>
+struct MixSmem {
+  union {
+    struct {
+      float qslot[NKS][4][G][8];   // [k-step][lane group][head][e]: q * 2^-6 of the slot's channel
+      half8 qz[NKS][4][G];         // q of the slot's channel as binary16 (offset MFMA operand)
+    } pg;
+    float p_lds[256][8];
+  } u;
   float mh[16];
 };
 
@@ -175,40 +196,47 @@ struct MixCodes {
   u32x4 bf[NB > 0 ? NB : 1];
 };
 
+// The metadata slot of one page: Key meta, value meta of k-steps 0-1 and 2-3.
+struct MixSlot {
+  uint8_t* k;
+  uint8_t* v_lo;
+  uint8_t* v_hi;
+};
+
+// Every load is unconditional, with clamped indices, so the issue is
+// straight-line code the compiler counts exactly (no conditional load makes
+// it wait for everything in flight). A fragment past F repeats fragment F-1:
+// its slots meet a zero query, so it adds exactly 0. A BF16 row past n16
+// repeats row n16-1 and is masked to zero where it is used.
 template <int NKS, int NB>
 __device__ inline void mix_load(MixCodes<NKS, NB>& c, const uint8_t* page, const MixGeo& g, int a, int r) {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const int f = 4 * ks + a;
-    c.kc[ks] = (u32x4){0u, 0u, 0u, 0u};
-    if (f < g.F) c.kc[ks] = ld16(page + g.off_codes + 256 * f + 16 * r);
-  }
+  for (int ks = 0; ks < NKS; ++ks) c.kc[ks] = ld16(page + g.off_codes + 256 * min(4 * ks + a, g.F - 1) + 16 * r);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
 #pragma unroll
-  for (int e = 0; e < NB; ++e) {
-    const int ch = 8 * a + e;
-    c.bf[e] = (u32x4){0u, 0u, 0u, 0u};
-    if (ch < g.n16) c.bf[e] = ld16(page + 256 * ch + 16 * r);
-  }
+  for (int e = 0; e < NB; ++e) c.bf[e] = ld16(page + 256 * min(8 * a + e, g.n16 - 1) + 16 * r);
 }
 
-__device__ inline void mix_issue_meta(const uint8_t* page, uint8_t* slot, const MixGeo& g, int lane) {
-  if (lane < 2 * g.F) async16(page + g.off_meta + 16 * lane, slot);
-  issue_vmeta(page + g.off_v + V_CODE_BYTES, slot, lane);
+// Key meta: 1 KB from its start (the page continues with value codes, so the
+// copy stays inside the page); only its first 32 F bytes are read.
+__device__ inline void mix_issue_meta(const uint8_t* page, const MixSlot& slot, const MixGeo& g, int lane) {
+  async16(page + g.off_meta + 16 * lane, slot.k);
+  async16(page + g.off_v + V_CODE_BYTES + 16 * lane, slot.v_lo);
+  async16(page + g.off_v + V_CODE_BYTES + 1024 + 16 * lane, slot.v_hi);
 }
 
 template <int G, int NKS, int NB, int NPASS>
-__device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c, const uint8_t* slot,
-                                const PgSmem<G, NKS>& S, const bf16x8& Bq, float xs, float scale_log2, int a,
-                                int h, int col) {
+__device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c, const MixSlot& slot,
+                                const MixSmem<G, NKS>& S, const bf16x8& Bq, float xs, float scale_log2, int a,
+                                int h, int col, int f_last, int n16) {
   f32x4 logit[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   f32x4 zacc = {0.f, 0.f, 0.f, 0.f};       // sum_slot q * offset, identical in every row
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const uint8_t* km = slot + 32 * (4 * ks + a);
+    const uint8_t* km = slot.k + 32 * min(4 * ks + a, f_last);   // past F: zero query, any finite meta
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
     const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
@@ -227,14 +255,15 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
       uint16_t tmp[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        tmp[e] = e < NB ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1))) : (uint16_t)0;
+        tmp[e] = e < NB && 8 * a + e < n16 ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1)))
+                                           : (uint16_t)0;
       bf16x8 Ak;
       __builtin_memcpy(&Ak, tmp, 16);
       logit[i] = mfma_bf(Ak, Bq, logit[i]);   // Bq is zero in the lo columns
     }
   }
   join_halves(logit);
-  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot + 1024, a, col);
+  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot.v_lo, slot.v_hi, a, col);
 }
 
 // Registers of 256 VGPRs (two waves per SIMD) fit every variant except the
@@ -244,10 +273,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
-  __shared__ PgSmem<G, NKS> S;
+  __shared__ MixSmem<G, NKS> S;
+  __shared__ __attribute__((aligned(16))) uint8_t km0[1024], km1[1024], vl0[1024], vh0[1024], vl1[1024], vh1[1024];
+  __shared__ __attribute__((aligned(16))) uint8_t qb[G * D * 2];   // bf16 query rows of the group
+  const MixSlot slot0 = {km0, vl0, vh0}, slot1 = {km1, vl1, vh1};
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
-  if (split == A.n_page_splits) {
+  if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
     return;
   }
@@ -257,48 +289,62 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
   const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
 
-  // set-up loads: query rows, the slot -> channel map and the BF16 channels
+  // Set-up loads first (loads return in issue order, so they arrive before
+  // the page): the selection record as one dword per lane, the query rows.
+  // Then the first page, its metadata into registers: while an asynchronous
+  // LDS copy is in flight every wait the compiler inserts drains all loads,
+  // so the set-up issues none and its waits stay partial.
+  const uint32_t recw = ld4(A.mask + head * MIX_RECORD + 4 * min(lane, MIX_RECORD / 4 - 1));
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
-  int sch[(32 * NKS + 63) / 64];
+  u32x4 m0[3];
+  m0[0] = ld16(pages + g.off_meta + 16 * lane);
+  m0[1] = ld16(pages + g.off_v + V_CODE_BYTES + 16 * lane);
+  m0[2] = ld16(pages + g.off_v + V_CODE_BYTES + 1024 + 16 * lane);
+  MixCodes<NKS, NB> c0, c1;
+  mix_load(c0, pages, g, a, r);
+  __builtin_amdgcn_sched_barrier(0);
+  // slot -> channel of this lane's slots and the BF16-tier channels of its
+  // lane group, from the record
+  constexpr int NJ = (32 * NKS + 63) / 64;
+  int sch[NJ];
 #pragma unroll
-  for (int j = 0; j < (32 * NKS + 63) / 64; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int s = lane + 64 * j;
-    int ch = -1;
-    if (s < 2 * g.n4) ch = rec[g.n16 + (s >> 1)];
-    else if (s >= g.s4 && s < g.s4 + g.n2) ch = rec[g.n16 + g.n4 + (s - g.s4)];
-    sch[j] = ch;
+    int idx = -1;
+    if (s < 2 * g.n4) idx = g.n16 + (s >> 1);
+    else if (s >= g.s4 && s < g.s4 + g.n2) idx = g.n16 + g.n4 + (s - g.s4);
+    const int ch = rec_byte(recw, idx < 0 ? 0 : idx);
+    sch[j] = idx < 0 ? -1 : ch;
   }
   int bch[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) bch[e] = (8 * a + e < g.n16) ? rec[8 * a + e] : -1;
-  // Key meta past the page's own 32 F bytes is read as zero scale / offset
-  for (int i = lane; i < 2 * 1024 / 16; i += 64) {
-    const int sl = i / 64, o = (i % 64) * 16;
-    *reinterpret_cast<u32x4*>(&S.u.pg.meta[sl][o]) = (u32x4){0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; ++e) {
+    const int ch = rec_byte(recw, 8 * a + e);
+    bch[e] = 8 * a + e < g.n16 ? ch : -1;
   }
-  wait_lgkm0();
-  // first page in flight during the set-up
-  MixCodes<NKS, NB> c0, c1;
-  mix_issue_meta(pages, S.u.pg.meta[0], g, lane);
-  mix_load(c0, pages, g, a, r);
-
-  uint8_t* qb = S.u.pg.meta[1] + 1024;    // bf16 q staging, free until page 1's metadata arrives
   stage_q<G>(qv, qb, lane);
-#pragma unroll
-  for (int j = 0; j < (32 * NKS + 63) / 64; ++j)
-    if (lane + 64 * j < 32 * NKS) S.slot_ch[lane + 64 * j] = sch[j];
   __syncthreads();
-  for (int idx = lane; idx < NKS * 4 * G * 8; idx += 64) {
-    const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
-    const int ch = S.slot_ch[8 * (4 * ks + aa) + e];
-    const float qf = ch >= 0 ? qb_at(qb, hh, ch) : 0.f;
-    S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
-    S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
+  // q of each slot's channel, per head: q * 2^-6 (Key operand) and binary16 (offset operand)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int s = lane + 64 * j;
+    if (s < 32 * NKS) {
+      const int ks = s >> 5, aa = (s >> 3) & 3, e = s & 7, ch = sch[j];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float qf = ch >= 0 ? qb_at(qb, hh, ch) : 0.f;
+        S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
+        S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
+      }
+    }
   }
   bf16x8 Bq;
 #pragma unroll
   for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qb_at(qb, h, bch[e]) * B_SCALE : 0.f);
+  *reinterpret_cast<u32x4*>(km0 + 16 * lane) = m0[0];
+  *reinterpret_cast<u32x4*>(vl0 + 16 * lane) = m0[1];
+  *reinterpret_cast<u32x4*>(vh0 + 16 * lane) = m0[2];
   __syncthreads();
 
   SoftState<NPASS> st;
@@ -310,26 +356,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float xs = A.scale_log2 * B_UNSCALE;
 
+  // Each half: wait for everything in flight (all of it is the page about to
+  // be computed, requested one page earlier), then request the next page and
+  // compute this one. Draining before the copies are issued keeps the
+  // compiler from draining after them, which would wait for the next page.
   for (int it = 0; it < np; it += 2) {
     progress_prio(it, np);
     // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
+    wait_vm<0>();
     if (it + 1 < np) {
-      mix_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, S.u.pg.meta[1], g, lane);
-      wait_vm<3>();
+      mix_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, slot1, g, lane);
       mix_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
-    } else {
-      wait_vm<0>();
     }
-    mix_page<G, NKS, NB, NPASS>(st, c0, S.u.pg.meta[0], S, Bq, xs, A.scale_log2, a, h, col);
+    mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col, g.F - 1, g.n16);
     if (it + 1 >= np) break;
+    wait_vm<0>();
     if (it + 2 < np) {
-      mix_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, S.u.pg.meta[0], g, lane);
-      wait_vm<3>();
+      mix_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, slot0, g, lane);
       mix_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
-    } else {
-      wait_vm<0>();
     }
-    mix_page<G, NKS, NB, NPASS>(st, c1, S.u.pg.meta[1], S, Bq, xs, A.scale_log2, a, h, col);
+    mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col, g.F - 1, g.n16);
   }
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
@@ -387,7 +433,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   __shared__ PgSmem<G, 4> S;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
-  if (split == A.n_page_splits) {
+  if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
     return;
   }
@@ -448,7 +494,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         f32x4 logit[8], zacc;
         pn_keys<G>(logit, zacc, k, slot, S, a, h, col);
         mid();
-        consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, slot + 1024, a, col);
+        consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, slot + 1024, slot + 2048, a, col);
       });
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
@@ -513,7 +559,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   __shared__ QjSmem<G> S;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
-  if (split == A.n_page_splits) {
+  if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
     return;
   }
@@ -559,7 +605,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         f32x4 logit[8];
         qj_keys<G>(logit, k, slot, S, ssum, a, h, col);
         mid();
-        consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, slot + 1024, a, col);
+        consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, slot + 1024, slot + 2048, a, col);
       });
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
@@ -568,7 +614,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // ------------------------------------------------------------------ dispatch
 template <class K>
 static void launch1(K kernel, const DecodeArgs& a, hipStream_t s) {
-  const int n_parts = a.n_page_splits + (a.n_sink + a.n_resid > 0 ? 1 : 0);
+  const int n_parts = a.n_page_splits + a.n_seg_splits;
   hipLaunchKernelGGL(kernel, dim3(n_parts, a.n_kv_heads, a.batch), dim3(64), 0, s, a);
 }
 

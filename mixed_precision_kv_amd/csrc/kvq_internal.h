@@ -194,6 +194,7 @@ struct DecodeArgs {
   const uint8_t* arena;
   int64_t page_stride;
   int max_pages, n_pages, pps, n_page_splits;
+  int n_seg_splits;               // BF16-segment workgroups per (batch, kv head), SEG_TOKENS tokens each
   const uint8_t* mask;
   const float* sq;
   const uint16_t* sink_k;
@@ -216,7 +217,12 @@ hipError_t launch_flush(int key_mode, const FlushArgs& a, int n_pages, int batch
 hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s);
 constexpr int DECODE_SLOTS = 2048;
-int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, bool segment);
-int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, bool segment, int slots);
+// Sink + residual tokens per BF16-segment workgroup; at most 256 segment
+// tokens (128 sinks + 128 residual) make MAX_SEG_SPLITS workgroups.
+constexpr int SEG_TOKENS = 32;
+constexpr int MAX_SEG_SPLITS = 2 * PAGE / SEG_TOKENS;
+inline int seg_splits(int n_tokens) { return (n_tokens + SEG_TOKENS - 1) / SEG_TOKENS; }
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, int n_seg);
+int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int n_seg, int slots);
 
 }  // namespace kvq
