@@ -184,6 +184,8 @@ kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const vo
  *   logit_t = softmax_scale * q . k^_t for BF16 and dequantized keys,
  *   logit_t = softmax_scale * sqrt(pi/2)/m * nu_t * <S q, sign(S k_t)> for QJL pages.
  * q: device bf16 [batch][n_q_heads][128]; query head h uses kv head h / (Hq/Hkv).
+ * mask: the records of kvq_select_channels, 16-byte aligned (ignored for QJL
+ *   and when n_pages is 0).
  * sink_k/sink_v: device bf16 [batch][n_kv_heads][n_sink][128] (n_sink <= 128; may be NULL if 0).
  * resid_k/resid_v: device bf16 [batch][n_kv_heads][resid_stride][128], first
  *   n_resid tokens visible (0 <= n_resid <= 128; may be NULL if 0).

@@ -69,12 +69,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   for (int i = lane; i < G * D; i += 64)
     S.qf[i / D][i % D] = bf16_to_f32(A.q[((int64_t)b * A.n_q_heads + kvh * G + i / D) * D + i % D]);
   SoftState<NPASS> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  init_state(st);
   const int p0 = split * A.pps;
   const int p1 = min(A.n_pages, p0 + A.pps);
   const uint8_t* pages = A.arena + head * A.max_pages * A.page_stride;

@@ -117,13 +117,24 @@ __device__ inline float wave_sum_groups(float v) {
 }
 
 // Online-softmax state of one lane (one head; one value group per pass).
+// zl accumulates rows 4a..4a+3 of the offset MFMA (A rows 0-3: the value
+// offsets of groups 0-3, row 4: ones; B: the probabilities), so lane group 0
+// holds sum p * offset of value groups 0-3 and lane group 1 (row 4) sum p,
+// each for the head of the lane's column.
 template <int NPASS>
 struct SoftState {
   float m;          // running max (log2 domain)
-  float l;          // partial sum of p over this lane's tokens
-  float z[NPASS];   // partial sum of p * value offset, per pass
+  f32x4 zl;
   f32x4 acc[8];     // value accumulators of the 8 value tiles (16 channels each)
 };
+
+template <int NPASS>
+__device__ inline void init_state(SoftState<NPASS>& st) {
+  st.m = -INFINITY;
+  st.zl = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
 
 // Consume one page: logit[i][e] is the raw Key accumulator of tile i row e
 // (token 16 i + 4 a + e); the log2-domain logit is logit * xs + xb.
@@ -141,36 +152,47 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
   const float mn = fmaxf(st.m, pm);
   if (__any(mn > st.m)) {
     const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - mn);
-    st.l *= alpha;
-#pragma unroll
-    for (int P = 0; P < NPASS; ++P) st.z[P] *= alpha;
+    st.zl *= alpha;
 #pragma unroll
     for (int u = 0; u < 8; ++u) st.acc[u] *= alpha;
     st.m = mn;
   }
   const float shift = xb - st.m;
   const int jl = col / G;
+  // offset-MFMA A rows: row r < 4 reads the offsets of value group r, row 4
+  // is binary16 ones, rows 5-15 zero
+  const int zr = col < 4 ? col : 3;
+  const uint32_t zconst = col == 4 ? 0x3C003C00u : 0u;
   // k-step outer: the 8 probabilities of tiles 2ks, 2ks+1 are formed right
   // before they are used (in every pass), so only 8 stay live at a time.
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 8; ++e)
       p[e] = fast_exp2(fmaf(logit[2 * ks + (e >> 2)][e & 3], xs, shift));   // token pi(ks, a, e)
-      st.l += p[e];
+    const uint8_t* kb = (ks < 2 ? vm_lo : vm_hi) + 512 * (ks & 1) + 128 * a;
+    {
+      // sum p * offset per value group and sum p, on the MFMA (p as binary16)
+      const u32x4 zw = ld16(kb + 32 * zr + 16);
+      u32x4 za;
+      za.x = col < 4 ? zw.x : zconst;
+      za.y = col < 4 ? zw.y : zconst;
+      za.z = col < 4 ? zw.z : zconst;
+      za.w = col < 4 ? zw.w : zconst;
+      half8 ph;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ph[e] = (_Float16)p[e];
+      st.zl = mfma(as_half8(za), ph, st.zl);
     }
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
       const int j = (jl + P * C) & 3;            // this lane's value group in pass P
-      const uint8_t* mb = (ks < 2 ? vm_lo : vm_hi) + 512 * (ks & 1) + 128 * a + 32 * j;
-      const half8 s8 = as_half8(ld16(mb)), z8 = as_half8(ld16(mb + 16));
+      const half8 s8 = as_half8(ld16(kb + 32 * j));
       half8 B;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; ++e)
         B[e] = (_Float16)fmaf(p[e], (float)s8[e], 0.0f);   // one v_fma_mix (f16 source and result)
-        st.z[P] = fmaf(p[e], (float)z8[e], st.z[P]);
-      }
       const u32x4 v8 = vc[ks] >> 8u;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {            // value tiles 2w, 2w+1 hold group w
@@ -199,10 +221,18 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
                                      int col, float* stage) {
   constexpr int C = 16 / G;
   const int lane = threadIdx.x & 63;   // lane within the calling wave
-  const float l = wave_sum_groups(st.l);
+  // sum p (row 4: lane group 1) and sum p * offset of value group j (row j:
+  // lane group 0), for the head of this lane's column
+  const float l = __shfl(st.zl[0], 16 + col);
+  float zg[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) zg[j] = __shfl(st.zl[j], col);
   float z[NPASS];
 #pragma unroll
-  for (int P = 0; P < NPASS; ++P) z[P] = wave_sum_groups(st.z[P]);
+  for (int P = 0; P < NPASS; ++P) {
+    const int j = (col / G + P * C) & 3;
+    z[P] = j == 0 ? zg[0] : (j == 1 ? zg[1] : (j == 2 ? zg[2] : zg[3]));
+  }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int P = (u >> 1) / C;
@@ -273,17 +303,15 @@ __device__ inline void join_halves(f32x4 (&logit)[8]) {
     for (int e = 0; e < 4; ++e) logit[i][e] += from_partner8(logit[i][e]);
 }
 
-// This lane's half of B = q * s (q pre-scaled by 2^-6): hi part, or lo part
-__device__ inline half8 key_operand_half(const float* qv, const u32x4& sw, bool lo_col) {
+// This lane's half of B = q * s, with qh = binary16(q * 2^-6): the hi part
+// binary16(qh s) (columns 0-7) or its rounding error binary16(qh s - hi)
+// (columns 8-15, one fused rounding). Packed half-precision arithmetic, two
+// slots per instruction.
+__device__ inline half8 key_operand_half(const half8& qh, const u32x4& sw, bool lo_col) {
   const half8 s8 = as_half8(sw);
-  half8 B;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const _Float16 hh = (_Float16)fmaf(qv[e], (float)s8[e], 0.0f);
-    const _Float16 ll = (_Float16)fmaf(qv[e], (float)s8[e], -(float)hh);
-    B[e] = lo_col ? ll : hh;
-  }
-  return B;
+  const half8 hi = qh * s8;
+  const half8 lo = __builtin_elementwise_fma(qh, s8, -hi);
+  return lo_col ? lo : hi;
 }
 
 __device__ inline bf16x8 as_bf16x8(const u32x4& v) {

@@ -70,7 +70,7 @@ template <int G, int NKS>
 struct PgSmem {
   union {
     struct {
-      float qslot[NKS][4][G][8];   // [k-step][lane group][head][e]: q * 2^-6 of the slot's channel
+      half8 qh[NKS][4][G];         // [k-step][lane group][head]: binary16 q * 2^-6 of the slot's channel
       half8 qz[NKS][4][G];         // q of the slot's channel as binary16 (offset MFMA operand)
       uint8_t meta[2][META_SLOT];  // double-buffered page metadata
     } pg;
@@ -88,7 +88,7 @@ template <int G, int NKS>
 struct MixSmem {
   union {
     struct {
-      float qslot[NKS][4][G][8];   // [k-step][lane group][head][e]: q * 2^-6 of the slot's channel
+      half8 qh[NKS][4][G];         // [k-step][lane group][head]: binary16 q * 2^-6 of the slot's channel
       half8 qz[NKS][4][G];         // q of the slot's channel as binary16 (offset MFMA operand)
     } pg;
     float p_lds[256][8];
@@ -178,16 +178,6 @@ __device__ inline void load_vcodes(ValCodes& v, const uint8_t* page, int off_v, 
   for (int ks = 0; ks < 4; ++ks) v.vc[ks] = ld16(page + off_v + 1024 * ks + 256 * a + 16 * r);
 }
 
-template <int G, int NPASS>
-__device__ inline void init_state(SoftState<NPASS>& st) {
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-}
-
 // ------------------------------------------------------------------ MixKVQ
 template <int NKS, int NB>
 struct MixCodes {
@@ -238,7 +228,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
   for (int ks = 0; ks < NKS; ++ks) {
     const uint8_t* km = slot.k + 32 * min(4 * ks + a, f_last);   // past F: zero query, any finite meta
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
-    const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
+    const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
     const u32x4 k8 = c.kc[ks] >> 8u;
 #pragma unroll
@@ -334,7 +324,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         const float qf = ch >= 0 ? qb_at(qb, hh, ch) : 0.f;
-        S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
+        S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
         S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
       }
     }
@@ -348,12 +338,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   __syncthreads();
 
   SoftState<NPASS> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int P = 0; P < NPASS; ++P) st.z[P] = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  init_state(st);
   const float xs = A.scale_log2 * B_UNSCALE;
 
   // Each half: wait for everything in flight (all of it is the page about to
@@ -407,7 +392,7 @@ __device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, c
   for (int ks = 0; ks < 4; ++ks) {
     const uint8_t* km = slot + 32 * (4 * ks + a);
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
-    const half8 B = key_operand_half(S.u.pg.qslot[ks][a][h], sw, col >= 8);
+    const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
     {                                       // LSB plane: 1-bit codes, weight s
       const Row1 x = row1(rd(c.lsb[ks >> 1], 2 * (ks & 1)), rd(c.lsb[ks >> 1], 2 * (ks & 1) + 1));
@@ -477,13 +462,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   for (int idx = lane; idx < 4 * 4 * G * 8; idx += 64) {
     const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
     const float qf = qb_at(qb, hh, S.slot_ch[8 * (4 * ks + aa) + e]);
-    S.u.pg.qslot[ks][aa][hh][e] = qf * B_SCALE;
+    S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
     S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;
   }
   __syncthreads();
 
   SoftState<NPASS> st;
-  init_state<G, NPASS>(st);
+  init_state(st);
   const float xs = A.scale_log2 * B_UNSCALE;
   page_loop(
       np, kp, vp, [&](PnKey& k, int p) { pn_load_key(k, pages + (int64_t)p * A.page_stride, g, lane, a, r); },
@@ -594,7 +579,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   __syncthreads();
 
   SoftState<NPASS> st;
-  init_state<G, NPASS>(st);
+  init_state(st);
   const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
   page_loop(
       np, kp, vp, [&](QjKey& k, int p) { qj_load_key(k, pages + (int64_t)p * A.page_stride, g, lane, a, r); },
