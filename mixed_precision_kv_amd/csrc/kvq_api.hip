@@ -50,16 +50,15 @@ static size_t record_bytes(const kvq_config* c) {
   return 0;
 }
 
-static int n_page_splits(const kvq_config* c, int n_pages, int n_seg) {
+static int n_page_splits(const kvq_config* c, int n_pages) {
   if (n_pages <= 0) return 0;
-  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads, n_seg);
+  const int pps = decode_pages_per_split(n_pages, c->batch, c->n_kv_heads);
   return (n_pages + pps - 1) / pps;
 }
 
 static size_t workspace_for(const kvq_config* c, int n_pages) {
-  // page splits shrink as segment workgroups are added: the page split count
-  // without a segment plus the most segment workgroups bounds every call
-  size_t splits = (size_t)n_page_splits(c, n_pages, 0) + MAX_SEG_SPLITS;
+  // the page splits plus the most segment workgroups any call can have
+  size_t splits = (size_t)n_page_splits(c, n_pages) + MAX_SEG_SPLITS;
   size_t rows = (size_t)c->batch * c->n_q_heads;
   size_t bytes = splits * rows * 130 * sizeof(float);
   if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)c->qjl_m * sizeof(float);
@@ -237,8 +236,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   a.max_pages = cfg->max_pages;
   a.n_pages = n_pages;
   a.n_seg_splits = seg_splits(n_sink + n_resid);
-  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads, a.n_seg_splits) : 1;
-  a.n_page_splits = n_page_splits(cfg, n_pages, a.n_seg_splits);
+  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
+  a.n_page_splits = n_page_splits(cfg, n_pages);
   a.mask = (const uint8_t*)mask;
   const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
   const size_t part_bytes = ((size_t)a.n_page_splits + MAX_SEG_SPLITS) * rows * 130 * sizeof(float);

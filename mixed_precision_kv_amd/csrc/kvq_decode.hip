@@ -53,7 +53,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
   __shared__ DecodeSmem S;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const DecodeBlock blk = decode_block(A);
+  const int split = blk.split, kvh = blk.kvh, b = blk.b;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r;
   const int h = col % G;
   const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
@@ -308,42 +309,57 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, con
 }
 
 // log-sum-exp merge of the split partials: one wave per query head, lane l
-// owning channels 2l and 2l+1. Parts are taken 32 at a time: every load of a
-// batch (the 32 records' m and l and the lane's two channels) is issued
-// before any is used, and the batch is folded into a running maximum, so a
-// call with up to 32 parts costs one memory round trip.
+// owning channels 2l and 2l+1. Parts are taken 32 at a time: lane j loads
+// part j's (m, l) pair and every lane its two channels of all 32 records,
+// all before any is used, so a batch costs one memory round trip; the
+// maximum and the weighted sum of l are wave reductions, and the weights
+// reach every lane through LDS.
+__device__ inline float wave_max64(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ inline float wave_sum64(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 __global__ __launch_bounds__(64) void combine_kernel(const float* partial, float* out, int n_parts, int rows) {
   constexpr int NB = 32;
+  __shared__ float wsh[NB];
   const int row = blockIdx.x, lane = threadIdx.x;
   const int64_t stride = (int64_t)rows * RECORD;           // from one part's record to the next
   const float* base = partial + (int64_t)row * RECORD;
   float M = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   for (int s0 = 0; s0 < n_parts; s0 += NB) {
-    float ms[NB], ls[NB], v0[NB], v1[NB];
+    // clamped indices keep every load in bounds; parts past the end weigh 0
+    const float2 ml = *reinterpret_cast<const float2*>(base + min(s0 + (lane & (NB - 1)), n_parts - 1) * stride);
+    float2 v[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {                          // clamped: in bounds, weight 0 past the end
-      const float* rec = base + min(s0 + j, n_parts - 1) * stride;
-      ms[j] = s0 + j < n_parts ? rec[0] : -INFINITY;
-      ls[j] = rec[1];
-      v0[j] = rec[2 + 2 * lane];
-      v1[j] = rec[3 + 2 * lane];
-    }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) bm = fmaxf(bm, ms[j]);
-    const float Mn = fmaxf(M, bm);
-    if (Mn == -INFINITY) continue;
+    for (int j = 0; j < NB; ++j)
+      v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, n_parts - 1) * stride + 2 + 2 * lane);
+    const bool own = lane < NB && s0 + lane < n_parts;
+    const float mj = own ? ml.x : -INFINITY;
+    // straight-line (no early exit, so the loads above are not sunk below a
+    // branch): with nothing visible yet every weight is 0 and M stays -inf
+    const float Mn = fmaxf(M, wave_max64(mj));
     const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-    l *= alpha;
+    const float wj = mj == -INFINITY ? 0.f : fast_exp2(mj - Mn);
+    const float lw = wave_sum64(own ? wj * ml.y : 0.f);
+    if (lane < NB) wsh[lane] = wj;
+    __syncthreads();
+    l = fmaf(l, alpha, lw);
     o0 *= alpha;
     o1 *= alpha;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const float w = ms[j] == -INFINITY ? 0.f : fast_exp2(ms[j] - Mn);
-      l = fmaf(w, ls[j], l);
-      o0 = fmaf(w, v0[j], o0);
-      o1 = fmaf(w, v1[j], o1);
+      const float w = wsh[j];
+      o0 = fmaf(w, v[j].x, o0);
+      o1 = fmaf(w, v[j].y, o1);
     }
+    __syncthreads();
     M = Mn;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -353,14 +369,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* partial, float
 
 bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s);
 
-// Pages per split: the page splits of every (batch, kv head) plus its n_seg
-// BF16-segment workgroups (one per SEG_TOKENS sink / residual tokens) are
-// sized to fill `slots` resident workgroups in one round, with the pages
-// spread evenly. DECODE_SLOTS (256 CUs x 8 resident single-wave workgroups on
+// Pages per split: the page splits of every (batch, kv head) are sized to
+// fill `slots` resident workgroups in one round, with the pages spread
+// evenly; the BF16-segment workgroups are dispatched after them (see
+// decode_block). DECODE_SLOTS (256 CUs x 8 resident single-wave workgroups on
 // MI355X) bounds every kernel's split count, and the workspace is sized for it.
-int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int n_seg, int slots) {
+int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int slots) {
   const int64_t pairs = (int64_t)batch * n_kv_heads;
-  const int64_t budget = (int64_t)slots - pairs * n_seg;
+  const int64_t budget = slots;
   int64_t splits = budget / pairs;
   if (splits < 1) splits = 1;
   int64_t pps = (n_pages + splits - 1) / splits;
@@ -368,8 +384,8 @@ int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int n_s
   return (int)pps;
 }
 
-int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, int n_seg) {
-  return decode_pages_per_split_slots(n_pages, batch, n_kv_heads, n_seg, DECODE_SLOTS);
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads) {
+  return decode_pages_per_split_slots(n_pages, batch, n_kv_heads, DECODE_SLOTS);
 }
 
 template <int MODE>
@@ -407,7 +423,7 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
   if (fast) {
     e = hipGetLastError();
   } else {
-    dim3 grid(n_parts, a.n_kv_heads, a.batch);
+    dim3 grid(n_parts * a.n_kv_heads * a.batch);
     if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
     else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
     else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);

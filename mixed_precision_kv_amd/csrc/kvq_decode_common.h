@@ -320,6 +320,27 @@ __device__ inline bf16x8 as_bf16x8(const u32x4& v) {
   return r;
 }
 
+// Workgroup -> (batch, kv head, split) of a decode launch (one dimension):
+// every page split first, slice by slice, then the BF16-segment workgroups.
+// The page splits fill the resident slots; the short segment workgroups are
+// dispatched after them and take the slots page splits release.
+struct DecodeBlock {
+  int b, kvh, split;
+};
+__device__ inline DecodeBlock decode_block(const DecodeArgs& A) {
+  const int n_pw = A.batch * A.n_kv_heads * A.n_page_splits;
+  int w = blockIdx.x, slice, split;
+  if (w < n_pw) {
+    slice = w / A.n_page_splits;
+    split = w - slice * A.n_page_splits;
+  } else {
+    w -= n_pw;
+    slice = w / A.n_seg_splits;
+    split = A.n_page_splits + (w - slice * A.n_seg_splits);
+  }
+  return {slice / A.n_kv_heads, slice % A.n_kv_heads, split};
+}
+
 // BF16 segment (attention sinks + residual): workgroup split - n_page_splits
 // takes segment tokens [SEG_TOKENS c, SEG_TOKENS (c + 1)), so the segment's
 // memory latency is paid once, in parallel, rather than once per chunk.

@@ -267,7 +267,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   __shared__ __attribute__((aligned(16))) uint8_t km0[1024], km1[1024], vl0[1024], vh0[1024], vl1[1024], vh1[1024];
   __shared__ __attribute__((aligned(16))) uint8_t qb[G * D * 2];   // bf16 query rows of the group
   const MixSlot slot0 = {km0, vl0, vh0}, slot1 = {km1, vl1, vh1};
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const DecodeBlock blk = decode_block(A);
+  const int split = blk.split, kvh = blk.kvh, b = blk.b;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
   if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
@@ -416,7 +417,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
   __shared__ PgSmem<G, 4> S;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const DecodeBlock blk = decode_block(A);
+  const int split = blk.split, kvh = blk.kvh, b = blk.b;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
   if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
@@ -542,7 +544,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
   __shared__ QjSmem<G> S;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const DecodeBlock blk = decode_block(A);
+  const int split = blk.split, kvh = blk.kvh, b = blk.b;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
   if (split >= A.n_page_splits) {
     bf16_segment<G>(A, split, b, kvh, lane, S.u.p_lds, S.mh);
@@ -600,7 +603,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 template <class K>
 static void launch1(K kernel, const DecodeArgs& a, hipStream_t s) {
   const int n_parts = a.n_page_splits + a.n_seg_splits;
-  hipLaunchKernelGGL(kernel, dim3(n_parts, a.n_kv_heads, a.batch), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(kernel, dim3(n_parts * a.n_kv_heads * a.batch), dim3(64), 0, s, a);
 }
 
 template <int G, int NKS>

@@ -222,7 +222,7 @@ constexpr int DECODE_SLOTS = 2048;
 constexpr int SEG_TOKENS = 32;
 constexpr int MAX_SEG_SPLITS = 2 * PAGE / SEG_TOKENS;
 inline int seg_splits(int n_tokens) { return (n_tokens + SEG_TOKENS - 1) / SEG_TOKENS; }
-int decode_pages_per_split(int n_pages, int batch, int n_kv_heads, int n_seg);
-int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int n_seg, int slots);
+int decode_pages_per_split(int n_pages, int batch, int n_kv_heads);
+int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int slots);
 
 }  // namespace kvq
