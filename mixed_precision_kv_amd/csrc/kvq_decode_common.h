@@ -172,6 +172,11 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
     for (int e = 0; e < 8; ++e)
       p[e] = fast_exp2(fmaf(logit[2 * ks + (e >> 2)][e & 3], xs, shift));   // token pi(ks, a, e)
     const uint8_t* kb = (ks < 2 ? vm_lo : vm_hi) + 512 * (ks & 1) + 128 * a;
+    // p as binary16: the B operand of the offset MFMA, and p s of the value
+    // MFMAs as one packed multiply per two tokens (two roundings of p s)
+    half8 ph;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ph[e] = (_Float16)p[e];
     {
       // sum p * offset per value group and sum p, on the MFMA (p as binary16)
       const u32x4 zw = ld16(kb + 32 * zr + 16);
@@ -180,19 +185,13 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
       za.y = col < 4 ? zw.y : zconst;
       za.z = col < 4 ? zw.z : zconst;
       za.w = col < 4 ? zw.w : zconst;
-      half8 ph;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ph[e] = (_Float16)p[e];
       st.zl = mfma(as_half8(za), ph, st.zl);
     }
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
       const int j = (jl + P * C) & 3;            // this lane's value group in pass P
       const half8 s8 = as_half8(ld16(kb + 32 * j));
-      half8 B;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        B[e] = (_Float16)fmaf(p[e], (float)s8[e], 0.0f);   // one v_fma_mix (f16 source and result)
+      const half8 B = ph * s8;
       const u32x4 v8 = vc[ks] >> 8u;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {            // value tiles 2w, 2w+1 hold group w
