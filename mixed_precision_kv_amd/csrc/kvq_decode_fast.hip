@@ -316,15 +316,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   }
   stage_q<G>(qv, qb, lane);
   __syncthreads();
-  // q of each slot's channel, per head: q * 2^-6 (Key operand) and binary16 (offset operand)
+  // q of each slot's channel, per head: q * 2^-6 (Key operand) and binary16
+  // (offset operand). Every read of the staged q comes first, then the table
+  // writes: interleaved, each read would wait for the writes before it.
+  float qsl[NJ][G], qbf[8];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) qsl[j][hh] = qb_at(qb, hh, sch[j] >= 0 ? sch[j] : 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qbf[e] = qb_at(qb, h, bch[e] >= 0 ? bch[e] : 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int s = lane + 64 * j;
     if (s < 32 * NKS) {
-      const int ks = s >> 5, aa = (s >> 3) & 3, e = s & 7, ch = sch[j];
+      const int ks = s >> 5, aa = (s >> 3) & 3, e = s & 7;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float qf = ch >= 0 ? qb_at(qb, hh, ch) : 0.f;
+        const float qf = sch[j] >= 0 ? qsl[j][hh] : 0.f;
         S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
         S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
       }
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   }
   bf16x8 Bq;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qb_at(qb, h, bch[e]) * B_SCALE : 0.f);
+  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * B_SCALE : 0.f);
   *reinterpret_cast<u32x4*>(km0 + 16 * lane) = m0[0];
   *reinterpret_cast<u32x4*>(vl0 + 16 * lane) = m0[1];
   *reinterpret_cast<u32x4*>(vh0 + 16 * lane) = m0[2];
@@ -430,23 +440,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
   const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
 
+  // set-up loads (the record, the query rows), then the first page, before
+  // any of them is waited for
+  const uint64_t mask = *reinterpret_cast<const uint64_t*>(rec);   // pair p is high iff bit p
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
-  uint32_t bits[2];
-  bits[0] = (uint32_t)rec[0] | (uint32_t)rec[1] << 8 | (uint32_t)rec[2] << 16 | (uint32_t)rec[3] << 24;
-  bits[1] = (uint32_t)rec[4] | (uint32_t)rec[5] << 8 | (uint32_t)rec[6] << 16 | (uint32_t)rec[7] << 24;
 
   PnKey kp[2];
   ValCodes vp[2];
   pn_load_key(kp[0], pages, g, lane, a, r);
   load_vcodes(vp[0], pages, g.off_v, a, r);
+  __builtin_amdgcn_sched_barrier(0);
 
   uint8_t* qb = S.u.pg.meta[1] + 1024;
   stage_q<G>(qv, qb, lane);
   {
     // slot order: high channels ascending, then low ones; the slot of
     // channel d counts the channels before it in its class
-    const uint64_t mask = (uint64_t)bits[0] | (uint64_t)bits[1] << 32;   // pair p is high iff bit p
     const int nh = __builtin_popcountll(mask);                            // high pairs
     for (int d = lane; d < D; d += 64) {
       const bool half = A.pair_layout == KVQ_PAIR_HALF_SPLIT;
@@ -461,11 +471,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
   }
   __syncthreads();
-  for (int idx = lane; idx < 4 * 4 * G * 8; idx += 64) {
-    const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
-    const float qf = qb_at(qb, hh, S.slot_ch[8 * (4 * ks + aa) + e]);
-    S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
-    S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;
+  // q of each of this lane's two slots (s = lane, lane + 64), per head; every
+  // read comes before the table writes
+  int sch[2];
+  sch[0] = S.slot_ch[lane];
+  sch[1] = S.slot_ch[lane + 64];
+  float qsl[2][G];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) qsl[j][hh] = qb_at(qb, hh, sch[j]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = lane + 64 * j, ks = s >> 5, aa = (s >> 3) & 3, e = s & 7;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qsl[j][hh] * B_SCALE);   // exact unless |q| < 2^-11
+      S.u.pg.qz[ks][aa][hh][e] = (_Float16)qsl[j][hh];
+    }
   }
   __syncthreads();
 
@@ -556,19 +580,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
   const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
 
+  // S q of this lane's head first (all of it, so the set-up waits once),
+  // then the first page, before any load is waited for
+  const int hq = kvh * G + h;
+  const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * A.qjl_m;
+  float4 sqv[8][2];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) sqv[ks][hf] = *reinterpret_cast<const float4*>(sqrow + 32 * ks + 8 * a + 4 * hf);
   QjKey kp[2];
   ValCodes vp[2];
   qj_load_key(kp[0], pages, g, lane, a, r);
   load_vcodes(vp[0], pages, g.off_v, a, r);
+  __builtin_amdgcn_sched_barrier(0);
 
-  const int hq = kvh * G + h;
-  const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * A.qjl_m;
   float ssum = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = sqrow[32 * ks + 8 * a + e] * B_SCALE;
+    const float x[8] = {sqv[ks][0].x * B_SCALE, sqv[ks][0].y * B_SCALE, sqv[ks][0].z * B_SCALE, sqv[ks][0].w * B_SCALE,
+                        sqv[ks][1].x * B_SCALE, sqv[ks][1].y * B_SCALE, sqv[ks][1].z * B_SCALE, sqv[ks][1].w * B_SCALE};
     half8 hi, lo;
     split8(x, hi, lo);
     if (col < G) {
