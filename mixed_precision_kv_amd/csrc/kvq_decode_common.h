@@ -242,9 +242,11 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
   __syncthreads();
   const int h = col % G, jl = col / G;
   float* base = A.partial + (((int64_t)split * A.batch + b) * A.n_q_heads + kvh * G) * RECORD;
+  // streaming stores: the records are read once, by the combine pass, after
+  // the kernel has ended
   if (a == 0 && jl == 0) {
-    base[h * RECORD] = st.m;
-    base[h * RECORD + 1] = l;
+    __builtin_nontemporal_store(st.m, &base[h * RECORD]);
+    __builtin_nontemporal_store(l, &base[h * RECORD + 1]);
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -253,7 +255,7 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
       const int ch = 2 * lane + k;                 // channel = 16 u + 4 a' + e
       const int u = ch >> 4, aa = (ch >> 2) & 3, e = ch & 3;
       const int j = u >> 1, c = (j % C) * G + hh;  // column holding (group j, head hh)
-      base[hh * RECORD + 2 + ch] = stage[(c * 8 + u) * 16 + aa * 4 + e];
+      __builtin_nontemporal_store(stage[(c * 8 + u) * 16 + aa * 4 + e], &base[hh * RECORD + 2 + ch]);
     }
   }
 }

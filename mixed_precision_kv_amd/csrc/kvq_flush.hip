@@ -57,12 +57,24 @@ __device__ inline void scan_add(Scan& s, uint16_t b) {
   s.emin = min(s.emin, nz ? max(e, 1) : 1000);
   s.emax = max(s.emax, nz ? e : -1000);
 }
-__device__ inline void scan_merge_xor(Scan& s, int mask) {
-  s.mn = fminf(s.mn, __shfl_xor(s.mn, mask));
-  s.mx = fmaxf(s.mx, __shfl_xor(s.mx, mask));
-  s.emin = min(s.emin, __shfl_xor(s.emin, mask));
-  s.emax = max(s.emax, __shfl_xor(s.emax, mask));
-  s.nonfinite = s.nonfinite || __shfl_xor((int)s.nonfinite, mask);
+// Merge with a partner lane through a DPP lane move (one VALU instruction,
+// no LDS round trip). Applied for W = 1, 2, 4 in turn it reduces over 2, 4 or
+// 8 consecutive lanes: the xor-1 and xor-2 quad permutations, then the
+// half-row mirror (lane i with 7 - i of its 8), which pairs each lane with
+// the other quad.
+template <int W>
+__device__ inline int dpp_partner(int v) {
+  constexpr int ctrl = W == 1 ? 0xB1 : (W == 2 ? 0x4E : 0x141);   // quad_perm [1,0,3,2], [2,3,0,1]; row_half_mirror
+  static_assert(W == 1 || W == 2 || W == 4, "lane distance");
+  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+}
+template <int W>
+__device__ inline void scan_merge(Scan& s) {
+  s.mn = fminf(s.mn, __int_as_float(dpp_partner<W>(__float_as_int(s.mn))));
+  s.mx = fmaxf(s.mx, __int_as_float(dpp_partner<W>(__float_as_int(s.mx))));
+  s.emin = min(s.emin, dpp_partner<W>(s.emin));
+  s.emax = max(s.emax, dpp_partner<W>(s.emax));
+  s.nonfinite = s.nonfinite || dpp_partner<W>((int)s.nonfinite);
 }
 
 __device__ inline bool f16_is_inf(uint16_t h) { return (h & 0x7FFF) == 0x7C00; }
@@ -218,7 +230,7 @@ __device__ __attribute__((always_inline)) inline void flush_value_part(uint8_t* 
     const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
     for (int c = 0; c < 16; ++c) scan_add(sc, (uint16_t)(cw[c >> 1] >> (16 * (c & 1))));
-    scan_merge_xor(sc, 1);
+    scan_merge<1>(sc);
     if (half == 0) S.vp[gi] = make_param(sc, 3, flags);
   }
   __syncthreads();
@@ -332,9 +344,9 @@ __device__ __attribute__((always_inline)) inline void flush_mix_key_part(const F
       const int d = S.ch[pos];
       for (int t = 16 * part; t < 16 * part + 16; ++t) scan_add(sc, S.tile[t * KS + d]);
     }
-    scan_merge_xor(sc, 1);
-    scan_merge_xor(sc, 2);
-    scan_merge_xor(sc, 4);
+    scan_merge<1>(sc);
+    scan_merge<2>(sc);
+    scan_merge<4>(sc);
     if (part == 0 && pos >= 0 && primary) S.kp[ls] = make_param(sc, levels, A.flags);
     if (part == 0 && pos < 0) S.kp[ls] = GroupParam{0.f, 0.f, 0.f, 0, 0};   // empty slot: code 0
     if (part == 1) {
@@ -455,7 +467,7 @@ __device__ __attribute__((always_inline)) inline void flush_pn_key_part(const Fl
     Scan sc;
     scan_init(sc);
     for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(sc, S.tile[t * KS + d]);
-    scan_merge_xor(sc, 1);
+    scan_merge<1>(sc);
     if (half == 0) S.kp[slot] = slot < nhs ? make_param(sc, 7, A.flags) : make_param_mid(sc, A.flags);
   }
   __syncthreads();
