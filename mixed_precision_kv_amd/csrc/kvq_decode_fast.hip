@@ -32,6 +32,20 @@ __device__ inline void async16(const uint8_t* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds_base, 16, 0, 0);
 }
 
+// Buffer resource over [base, base + bytes): a buffer load at an offset past
+// the range returns zero without a memory request, so loads of absent
+// fragments / rows stay unconditional (exact wait counts) and cost no
+// traffic. bytes is a multiple of 16 at every use.
+__device__ inline __amdgpu_buffer_rsrc_t range_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline u32x4 ld16_in(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline void async16_in(__amdgpu_buffer_rsrc_t r, int off, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_base, 16, off, 0, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 // Emitted through the builtin (not inline asm) so that the compiler's own
 // wait insertion knows which loads have completed: otherwise, with an
@@ -193,25 +207,27 @@ struct MixSlot {
   uint8_t* v_hi;
 };
 
-// Every load is unconditional, with clamped indices, so the issue is
-// straight-line code the compiler counts exactly (no conditional load makes
-// it wait for everything in flight). A fragment past F repeats fragment F-1:
-// its slots meet a zero query, so it adds exactly 0. A BF16 row past n16
-// repeats row n16-1 and is masked to zero where it is used.
+// Every load is unconditional, so the issue is straight-line code the
+// compiler counts exactly (a conditional load makes it wait for everything in
+// flight). Fragments past F and BF16 rows past n16 are read through range-
+// limited buffer resources: they load as zero (zero codes, zero BF16 values)
+// and request nothing from memory.
 template <int NKS, int NB>
 __device__ inline void mix_load(MixCodes<NKS, NB>& c, const uint8_t* page, const MixGeo& g, int a, int r) {
+  const auto rk = range_rsrc(page + g.off_codes, 256 * g.F);
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) c.kc[ks] = ld16(page + g.off_codes + 256 * min(4 * ks + a, g.F - 1) + 16 * r);
+  for (int ks = 0; ks < NKS; ++ks) c.kc[ks] = ld16_in(rk, 256 * (4 * ks + a) + 16 * r);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) c.vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
+  const auto rb = range_rsrc(page, 256 * g.n16);
 #pragma unroll
-  for (int e = 0; e < NB; ++e) c.bf[e] = ld16(page + 256 * min(8 * a + e, g.n16 - 1) + 16 * r);
+  for (int e = 0; e < NB; ++e) c.bf[e] = ld16_in(rb, 256 * (8 * a + e) + 16 * r);
 }
 
-// Key meta: 1 KB from its start (the page continues with value codes, so the
-// copy stays inside the page); only its first 32 F bytes are read.
+// Key meta: the page's 32 F bytes into the first 1 KB of the slot, the rest
+// of that 1 KB zero (range-limited copy: zero scales and offsets past F).
 __device__ inline void mix_issue_meta(const uint8_t* page, const MixSlot& slot, const MixGeo& g, int lane) {
-  async16(page + g.off_meta + 16 * lane, slot.k);
+  async16_in(range_rsrc(page + g.off_meta, 32 * g.F), 16 * lane, slot.k);
   async16(page + g.off_v + V_CODE_BYTES + 16 * lane, slot.v_lo);
   async16(page + g.off_v + V_CODE_BYTES + 1024 + 16 * lane, slot.v_hi);
 }
@@ -219,14 +235,14 @@ __device__ inline void mix_issue_meta(const uint8_t* page, const MixSlot& slot, 
 template <int G, int NKS, int NB, int NPASS>
 __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c, const MixSlot& slot,
                                 const MixSmem<G, NKS>& S, const bf16x8& Bq, float xs, float scale_log2, int a,
-                                int h, int col, int f_last, int n16) {
+                                int h, int col) {
   f32x4 logit[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   f32x4 zacc = {0.f, 0.f, 0.f, 0.f};       // sum_slot q * offset, identical in every row
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const uint8_t* km = slot.k + 32 * min(4 * ks + a, f_last);   // past F: zero query, any finite meta
+    const uint8_t* km = slot.k + 32 * (4 * ks + a);   // past F: zero meta
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
     const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], sw, col >= 8);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
@@ -245,8 +261,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
       uint16_t tmp[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        tmp[e] = e < NB && 8 * a + e < n16 ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1)))
-                                           : (uint16_t)0;
+        tmp[e] = e < NB ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1))) : (uint16_t)0;
       bf16x8 Ak;
       __builtin_memcpy(&Ak, tmp, 16);
       logit[i] = mfma_bf(Ak, Bq, logit[i]);   // Bq is zero in the lo columns
@@ -289,7 +304,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
   u32x4 m0[3];
-  m0[0] = ld16(pages + g.off_meta + 16 * lane);
+  m0[0] = ld16_in(range_rsrc(pages + g.off_meta, 32 * g.F), 16 * lane);   // zero past the page's 32 F bytes
   m0[1] = ld16(pages + g.off_v + V_CODE_BYTES + 16 * lane);
   m0[2] = ld16(pages + g.off_v + V_CODE_BYTES + 1024 + 16 * lane);
   MixCodes<NKS, NB> c0, c1;
@@ -364,14 +379,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
       mix_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, slot1, g, lane);
       mix_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
     }
-    mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col, g.F - 1, g.n16);
+    mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col);
     if (it + 1 >= np) break;
     wait_vm<0>();
     if (it + 2 < np) {
       mix_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, slot0, g, lane);
       mix_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
     }
-    mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col, g.F - 1, g.n16);
+    mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col);
   }
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
