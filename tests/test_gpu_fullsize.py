@@ -114,3 +114,28 @@ def test_fullsize_residual_flush(full):
         else:
             ref = oflush.flush_qjl_page(kb, vb, p.bits(p.S))
         assert np.array_equal(p.gpu_page(b, h, w.n_pages), ref), (name, b, h)
+
+
+def test_fullsize_fidelity(full):
+    """Fidelity context (not a parity gate): against attention on the
+    unquantized bf16 cache of the same visible tokens, the mean KL(p_bf16 ||
+    p_quantized) over the slice's query heads (the oracle's probabilities on
+    the dequantized cache), and the GPU output's relative error and cosine.
+
+    The synthetic K and V are Gaussian (plus the outlier channels), the
+    hardest case for 2-bit codes: with 115 UINT2 Key channels the score
+    noise alone predicts a KL near 0.1, so the bounds are only sanity checks
+    that catch a broken path (wrong tokens, scale or order)."""
+    from oracle import attention as oatt
+    name, p, out = full
+    w = p.w
+    b, h = slices(w)[0]
+    rec = p.gpu_record(b, h) if w.key_mode != synth.QJL else None
+    _, probs_q = p.oracle_decode(b, h, oracle_pages(p, b, h), rec)
+    out_r, probs_r = p.reference_probs(b, h, w.n_pages, w.n_resid)
+    kl = float(np.mean([oatt.kl_divergence(pr, pq) for pr, pq in zip(probs_r, probs_q)]))
+    o = out.cpu().numpy()[b, h * p.g:(h + 1) * p.g].astype(np.float64)
+    rel = float(np.max(rel_err(o, out_r)))
+    cos = float(np.min(np.sum(o * out_r, -1) / (np.linalg.norm(o, axis=-1) * np.linalg.norm(out_r, axis=-1))))
+    print(f"[fidelity] {name} b{b} h{h}: KL {kl:.3e}, output rel err {rel:.3e}, cosine {cos:.5f}")
+    assert np.isfinite(kl) and kl < 1.0 and cos > 0.5, (name, kl, cos)
