@@ -200,6 +200,33 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
                                 int32_t resid_stride, float softmax_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvq_decode_attention, then kvq_flush_quantize, in one call: the decode step
+ * at which the residual has filled and is packed into the next page (KIVI
+ * blog section 6: the residual holds up to R tokens and is quantized when
+ * full; MixKVQ Algorithm 1, KeyQuant / GroupQuant at that flush). The flush
+ * does not depend on the decode's output, so it runs in the same launch as
+ * the decode's split merge rather than after it.
+ * Arguments: those of kvq_decode_attention (q .. workspace_bytes), then the
+ *   flush's source, count and target (flush_k_src, flush_v_src,
+ *   flush_src_stride, n_flush_pages, flush_first_page, status_flags: as
+ *   k_src, v_src, src_stride, n_pages, first_page, status_flags of
+ *   kvq_flush_quantize); cfg, mask, qjl_s, page_arena and stream serve both.
+ * Results: out, the written pages and the status bits are bit-identical to
+ *   the two calls made in that order on one stream; the flush writes after
+ *   the decode has read the arena, so the page ranges may overlap.
+ * Errors: any check of either call fails the whole call and launches
+ *   nothing. The workspace rule of kvq_decode_attention applies. */
+kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void* page_arena,
+                                      int32_t n_pages, const void* mask, const void* qjl_s,
+                                      const void* sink_k, const void* sink_v, int32_t n_sink,
+                                      const void* resid_k, const void* resid_v, int32_t n_resid,
+                                      int32_t resid_stride, float softmax_scale, float* out,
+                                      void* workspace, size_t workspace_bytes,
+                                      const void* flush_k_src, const void* flush_v_src,
+                                      int64_t flush_src_stride, int32_t n_flush_pages,
+                                      int32_t flush_first_page, uint32_t* status_flags,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

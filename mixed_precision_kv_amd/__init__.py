@@ -24,7 +24,7 @@ KVQ_FLAG_NONFINITE, KVQ_FLAG_SPAN, KVQ_FLAG_MASK, KVQ_FLAG_RANGE = 1, 2, 4, 8
 EXPORTED = (
     "kvq_abi_version", "kvq_status_string", "kvq_page_bytes", "kvq_mask_bytes",
     "kvq_workspace_bytes", "kvq_storage_bytes", "kvq_select_channels",
-    "kvq_flush_quantize", "kvq_decode_attention",
+    "kvq_flush_quantize", "kvq_decode_attention", "kvq_decode_attention_flush",
 )
 
 
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
         "kvq_flush_quantize": (I32, [cfgp, P, P, I64, I32, P, P, P, I32, P, P]),
         "kvq_decode_attention": (I32, [cfgp, P, P, I32, P, P, P, P, I32, P, P, I32, I32, ctypes.c_float,
                                        P, P, SZ, P]),
+        "kvq_decode_attention_flush": (I32, [cfgp, P, P, I32, P, P, P, P, I32, P, P, I32, I32, ctypes.c_float,
+                                             P, P, SZ, P, P, I64, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -168,6 +170,19 @@ def kvq_flush_quantize(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page
     _check("kvq_flush_quantize", load().kvq_flush_quantize(
         ctypes.byref(cfg), _ptr(k_src), _ptr(v_src), src_stride, n_pages, _ptr(mask), _ptr(qjl_s),
         _ptr(page_arena), first_page, _ptr(status_flags), _stream(stream)))
+
+
+def kvq_decode_attention_flush(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k,
+                               resid_v, n_resid, resid_stride, softmax_scale, out, workspace, workspace_bytes,
+                               flush_k_src, flush_v_src, flush_src_stride, n_flush_pages, flush_first_page,
+                               status_flags, *, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("kvq_decode_attention_flush", load().kvq_decode_attention_flush(
+        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), n_pages, _ptr(mask), _ptr(qjl_s), _ptr(sink_k),
+        _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride, softmax_scale, _ptr(out),
+        _ptr(workspace), workspace_bytes, _ptr(flush_k_src), _ptr(flush_v_src), flush_src_stride, n_flush_pages,
+        flush_first_page, _ptr(status_flags), _stream(stream)))
 
 
 def kvq_decode_attention(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k, resid_v,

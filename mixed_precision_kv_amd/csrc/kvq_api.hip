@@ -65,6 +65,95 @@ static size_t workspace_for(const kvq_config* c, int n_pages) {
   return (bytes + 255) / 256 * 256;
 }
 
+// Checks of kvq_flush_quantize and its kernel arguments (a is filled when
+// the result is KVQ_OK, also for n_pages == 0).
+static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
+                                int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
+                                int32_t first_page, uint32_t* status_flags, FlushArgs& a) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!k_src || !v_src || !page_arena || !status_flags) return KVQ_INVALID_ARG;
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(page_arena)) return KVQ_INVALID_ARG;
+  if (n_pages < 0 || first_page < 0 || src_stride < (int64_t)n_pages * PAGE) return KVQ_INVALID_ARG;
+  if ((int64_t)first_page + n_pages > cfg->max_pages) return KVQ_CAPACITY;
+  if (cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
+  if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
+  // one block per (page, part, kv head, batch) on a one-dimensional grid
+  if ((int64_t)n_pages * 16 * cfg->n_kv_heads * cfg->batch > INT32_MAX / 2) return KVQ_INVALID_ARG;
+  a.k_src = (const uint16_t*)k_src;
+  a.v_src = (const uint16_t*)v_src;
+  a.src_stride = src_stride;
+  a.mask = (const uint8_t*)mask;
+  a.qjl_s = (const uint16_t*)qjl_s;
+  a.arena = (uint8_t*)page_arena;
+  a.page_stride = (int64_t)page_stride(cfg);
+  a.max_pages = cfg->max_pages;
+  a.first_page = first_page;
+  a.n_pages = n_pages;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n16 = cfg->n_bf16;
+  a.n4 = cfg->n_u4;
+  a.n_hi = 2 * cfg->n_hi_pairs;
+  a.pair_layout = cfg->pair_layout;
+  a.qjl_m = cfg->qjl_m;
+  a.flags = status_flags;
+  return KVQ_OK;
+}
+
+// Checks of kvq_decode_attention and its kernel arguments.
+static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const void* page_arena, int32_t n_pages,
+                                 const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
+                                 int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
+                                 int32_t resid_stride, float softmax_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, DecodeArgs& a) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  const int g = cfg->n_q_heads / cfg->n_kv_heads;
+  if (g > 8) return KVQ_UNSUPPORTED;
+  if (!q || !out || !workspace || !aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_INVALID_ARG;
+  if (n_pages < 0 || n_pages > cfg->max_pages) return KVQ_INVALID_ARG;
+  if (n_pages > 0 && (!page_arena || !aligned16(page_arena))) return KVQ_INVALID_ARG;
+  if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
+  if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
+  if (n_sink < 0 || n_sink > PAGE || n_resid < 0 || n_resid > PAGE) return KVQ_INVALID_ARG;
+  if (n_sink > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v))) return KVQ_INVALID_ARG;
+  if (n_resid > 0 && (!resid_k || !resid_v || !aligned16(resid_k) || !aligned16(resid_v) || resid_stride < n_resid))
+    return KVQ_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return KVQ_INVALID_ARG;
+  if (workspace_bytes < workspace_for(cfg, n_pages)) return KVQ_WORKSPACE_TOO_SMALL;
+  a.q = (const uint16_t*)q;
+  a.arena = (const uint8_t*)page_arena;
+  a.page_stride = (int64_t)page_stride(cfg);
+  a.max_pages = cfg->max_pages;
+  a.n_pages = n_pages;
+  a.n_seg_splits = seg_splits(n_sink + n_resid);
+  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
+  a.n_page_splits = n_page_splits(cfg, n_pages);
+  a.mask = (const uint8_t*)mask;
+  const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
+  const size_t part_bytes = ((size_t)a.n_page_splits + MAX_SEG_SPLITS) * rows * 130 * sizeof(float);
+  a.partial = (float*)workspace;
+  a.sq = (const float*)((uint8_t*)workspace + part_bytes);
+  a.out = out;
+  a.sink_k = (const uint16_t*)sink_k;
+  a.sink_v = (const uint16_t*)sink_v;
+  a.n_sink = n_sink;
+  a.resid_k = (const uint16_t*)resid_k;
+  a.resid_v = (const uint16_t*)resid_v;
+  a.n_resid = n_resid;
+  a.resid_stride = resid_stride;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.qjl_coef = cfg->key_mode == KVQ_KEY_QJL ? (float)(sqrt(M_PI / 2.0) / cfg->qjl_m) : 0.f;
+  a.batch = cfg->batch;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n_q_heads = cfg->n_q_heads;
+  a.n16 = cfg->n_bf16;
+  a.n4 = cfg->n_u4;
+  a.n_hi = 2 * cfg->n_hi_pairs;
+  a.pair_layout = cfg->pair_layout;
+  a.qjl_m = cfg->qjl_m;
+  return KVQ_OK;
+}
 }  // namespace kvq
 
 using namespace kvq;
@@ -179,34 +268,11 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
 kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
                               int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
                               int32_t first_page, uint32_t* status_flags, void* stream) {
-  kvq_status st = check_config(cfg);
-  if (st != KVQ_OK) return st;
-  if (!k_src || !v_src || !page_arena || !status_flags) return KVQ_INVALID_ARG;
-  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(page_arena)) return KVQ_INVALID_ARG;
-  if (n_pages < 0 || first_page < 0 || src_stride < (int64_t)n_pages * PAGE) return KVQ_INVALID_ARG;
-  if ((int64_t)first_page + n_pages > cfg->max_pages) return KVQ_CAPACITY;
-  if (cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
-  if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
-  if (n_pages == 0) return KVQ_OK;
   FlushArgs a;
-  a.k_src = (const uint16_t*)k_src;
-  a.v_src = (const uint16_t*)v_src;
-  a.src_stride = src_stride;
-  a.mask = (const uint8_t*)mask;
-  a.qjl_s = (const uint16_t*)qjl_s;
-  a.arena = (uint8_t*)page_arena;
-  a.page_stride = (int64_t)page_stride(cfg);
-  a.max_pages = cfg->max_pages;
-  a.first_page = first_page;
-  a.n_kv_heads = cfg->n_kv_heads;
-  a.n16 = cfg->n_bf16;
-  a.n4 = cfg->n_u4;
-  a.n_hi = 2 * cfg->n_hi_pairs;
-  a.pair_layout = cfg->pair_layout;
-  a.qjl_m = cfg->qjl_m;
-  a.flags = status_flags;
-  return launch_flush(cfg->key_mode, a, n_pages, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK
-                                                                                                : KVQ_HIP_ERROR;
+  const kvq_status st = flush_prepare(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, first_page,
+                                      status_flags, a);
+  if (st != KVQ_OK || n_pages == 0) return st;
+  return launch_flush(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 
 kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena, int32_t n_pages,
@@ -214,56 +280,34 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
                                 int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
                                 int32_t resid_stride, float softmax_scale, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  kvq_status st = check_config(cfg);
-  if (st != KVQ_OK) return st;
-  const int g = cfg->n_q_heads / cfg->n_kv_heads;
-  if (g > 8) return KVQ_UNSUPPORTED;
-  if (!q || !out || !workspace || !aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_INVALID_ARG;
-  if (n_pages < 0 || n_pages > cfg->max_pages) return KVQ_INVALID_ARG;
-  if (n_pages > 0 && (!page_arena || !aligned16(page_arena))) return KVQ_INVALID_ARG;
-  if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
-  if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
-  if (n_sink < 0 || n_sink > PAGE || n_resid < 0 || n_resid > PAGE) return KVQ_INVALID_ARG;
-  if (n_sink > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v))) return KVQ_INVALID_ARG;
-  if (n_resid > 0 && (!resid_k || !resid_v || !aligned16(resid_k) || !aligned16(resid_v) || resid_stride < n_resid))
-    return KVQ_INVALID_ARG;
-  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return KVQ_INVALID_ARG;
-  if (workspace_bytes < workspace_for(cfg, n_pages)) return KVQ_WORKSPACE_TOO_SMALL;
   DecodeArgs a;
-  a.q = (const uint16_t*)q;
-  a.arena = (const uint8_t*)page_arena;
-  a.page_stride = (int64_t)page_stride(cfg);
-  a.max_pages = cfg->max_pages;
-  a.n_pages = n_pages;
-  a.n_seg_splits = seg_splits(n_sink + n_resid);
-  a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
-  a.n_page_splits = n_page_splits(cfg, n_pages);
-  a.mask = (const uint8_t*)mask;
-  const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
-  const size_t part_bytes = ((size_t)a.n_page_splits + MAX_SEG_SPLITS) * rows * 130 * sizeof(float);
-  a.partial = (float*)workspace;
-  a.sq = (const float*)((uint8_t*)workspace + part_bytes);
-  a.out = out;
-  a.sink_k = (const uint16_t*)sink_k;
-  a.sink_v = (const uint16_t*)sink_v;
-  a.n_sink = n_sink;
-  a.resid_k = (const uint16_t*)resid_k;
-  a.resid_v = (const uint16_t*)resid_v;
-  a.n_resid = n_resid;
-  a.resid_stride = resid_stride;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.qjl_coef = cfg->key_mode == KVQ_KEY_QJL ? (float)(sqrt(M_PI / 2.0) / cfg->qjl_m) : 0.f;
-  a.batch = cfg->batch;
-  a.n_kv_heads = cfg->n_kv_heads;
-  a.n_q_heads = cfg->n_q_heads;
-  a.n16 = cfg->n_bf16;
-  a.n4 = cfg->n_u4;
-  a.n_hi = 2 * cfg->n_hi_pairs;
-  a.pair_layout = cfg->pair_layout;
-  a.qjl_m = cfg->qjl_m;
+  const kvq_status st = decode_prepare(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k,
+                                       resid_v, n_resid, resid_stride, softmax_scale, out, workspace,
+                                       workspace_bytes, a);
+  if (st != KVQ_OK) return st;
   return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream) == hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void* page_arena, int32_t n_pages,
+                                      const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
+                                      int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
+                                      int32_t resid_stride, float softmax_scale, float* out, void* workspace,
+                                      size_t workspace_bytes, const void* flush_k_src, const void* flush_v_src,
+                                      int64_t flush_src_stride, int32_t n_flush_pages, int32_t flush_first_page,
+                                      uint32_t* status_flags, void* stream) {
+  DecodeArgs d;
+  kvq_status st = decode_prepare(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k, resid_v,
+                                 n_resid, resid_stride, softmax_scale, out, workspace, workspace_bytes, d);
+  if (st != KVQ_OK) return st;
+  FlushArgs f;
+  st = flush_prepare(cfg, flush_k_src, flush_v_src, flush_src_stride, n_flush_pages, mask, qjl_s, page_arena,
+                     flush_first_page, status_flags, f);
+  if (st != KVQ_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false) != hipSuccess) return KVQ_HIP_ERROR;
+  return launch_merge_flush(cfg->key_mode, d, f, cfg->batch, s) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 
 }  // extern "C"

@@ -31,6 +31,7 @@
 #include <stdlib.h>
 
 #include "kvq_decode_common.h"
+#include "kvq_merge.h"
 
 namespace kvq {
 
@@ -308,63 +309,10 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, con
   }
 }
 
-// log-sum-exp merge of the split partials: one wave per query head, lane l
-// owning channels 2l and 2l+1. Parts are taken 32 at a time: lane j loads
-// part j's (m, l) pair and every lane its two channels of all 32 records,
-// all before any is used, so a batch costs one memory round trip; the
-// maximum and the weighted sum of l are wave reductions, and the weights
-// reach every lane through LDS.
-__device__ inline float wave_max64(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
-__device__ inline float wave_sum64(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
+// Split merge: one single-wave workgroup per query head (merge_row).
+template <int NB>
 __global__ __launch_bounds__(64) void combine_kernel(const float* partial, float* out, int n_parts, int rows) {
-  constexpr int NB = 32;
-  __shared__ float wsh[NB];
-  const int row = blockIdx.x, lane = threadIdx.x;
-  const int64_t stride = (int64_t)rows * RECORD;           // from one part's record to the next
-  const float* base = partial + (int64_t)row * RECORD;
-  float M = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s0 = 0; s0 < n_parts; s0 += NB) {
-    // clamped indices keep every load in bounds; parts past the end weigh 0
-    const float2 ml = *reinterpret_cast<const float2*>(base + min(s0 + (lane & (NB - 1)), n_parts - 1) * stride);
-    float2 v[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, n_parts - 1) * stride + 2 + 2 * lane);
-    const bool own = lane < NB && s0 + lane < n_parts;
-    const float mj = own ? ml.x : -INFINITY;
-    // straight-line (no early exit, so the loads above are not sunk below a
-    // branch): with nothing visible yet every weight is 0 and M stays -inf
-    const float Mn = fmaxf(M, wave_max64(mj));
-    const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-    const float wj = mj == -INFINITY ? 0.f : fast_exp2(mj - Mn);
-    const float lw = wave_sum64(own ? wj * ml.y : 0.f);
-    if (lane < NB) wsh[lane] = wj;
-    __syncthreads();
-    l = fmaf(l, alpha, lw);
-    o0 *= alpha;
-    o1 *= alpha;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const float w = wsh[j];
-      o0 = fmaf(w, v[j].x, o0);
-      o1 = fmaf(w, v[j].y, o1);
-    }
-    __syncthreads();
-    M = Mn;
-  }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  out[(int64_t)row * D + 2 * lane] = o0 * inv;
-  out[(int64_t)row * D + 2 * lane + 1] = o1 * inv;
+  merge_row<NB>(partial, out, n_parts, rows, blockIdx.x);
 }
 
 bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s);
@@ -400,37 +348,44 @@ static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s) {
+int decode_parts(const DecodeArgs& a) { return a.n_page_splits + a.n_seg_splits; }
+
+hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s,
+                         bool with_merge) {
   DecodeArgs a = args;
   const int g = a.n_q_heads / a.n_kv_heads;
-  if (key_mode == KVQ_KEY_QJL) {
-    hipLaunchKernelGGL(qjl_project_kernel, dim3(a.batch * a.n_q_heads), dim3(256), 0, s, a.q, qjl_s,
-                       const_cast<float*>(a.sq), a.qjl_m, a.batch * a.n_q_heads);
-    hipError_t e = hipGetLastError();
+  const int n_parts = decode_parts(a);
+  const int rows = a.batch * a.n_q_heads;
+  if (n_parts > 0) {
+    if (key_mode == KVQ_KEY_QJL) {
+      hipLaunchKernelGGL(qjl_project_kernel, dim3(rows), dim3(256), 0, s, a.q, qjl_s, const_cast<float*>(a.sq),
+                         a.qjl_m, rows);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = hipSuccess;
+    // The warp-specialised kernels cover the common shapes (and may choose
+    // their own split count); KVQ_FORCE_GENERIC_DECODE selects the generic
+    // kernel (same results) so tests can exercise both.
+    const bool fast = getenv("KVQ_FORCE_GENERIC_DECODE") == nullptr && launch_decode_fast(key_mode, a, s);
+    if (fast) {
+      e = hipGetLastError();
+    } else {
+      dim3 grid(n_parts * a.n_kv_heads * a.batch);
+      if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
+      else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
+      else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
+    }
     if (e != hipSuccess) return e;
   }
-  const int n_parts = a.n_page_splits + a.n_seg_splits;
-  if (n_parts == 0) {   // nothing to attend to: every output row is zero
-    hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a.partial, a.out, 0,
-                       a.batch * a.n_q_heads);
-    return hipGetLastError();
+  if (!with_merge) return hipSuccess;
+  // with nothing to attend to (no part) every output row is zero
+  const dim3 cgrid(rows);
+  switch (merge_batch(n_parts)) {
+    case 16: hipLaunchKernelGGL(combine_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, n_parts, rows); break;
+    case 32: hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, n_parts, rows); break;
+    default: hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.partial, a.out, n_parts, rows); break;
   }
-  hipError_t e = hipSuccess;
-  // The warp-specialised kernels cover the common shapes (and may choose
-  // their own split count); KVQ_FORCE_GENERIC_DECODE selects the generic
-  // kernel (same results) so tests can exercise both.
-  const bool fast = getenv("KVQ_FORCE_GENERIC_DECODE") == nullptr && launch_decode_fast(key_mode, a, s);
-  if (fast) {
-    e = hipGetLastError();
-  } else {
-    dim3 grid(n_parts * a.n_kv_heads * a.batch);
-    if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
-    else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
-    else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
-  }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(64), 0, s, a.partial, a.out,
-                     n_parts, a.batch * a.n_q_heads);
   return hipGetLastError();
 }
 

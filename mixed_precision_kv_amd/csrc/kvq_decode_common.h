@@ -16,7 +16,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float B_SCALE = 0.015625f;   // 2^-6 applied to every Key B operand (f16 range headroom)
 constexpr float B_UNSCALE = 64.0f;
 constexpr int MAX_KS = 8;              // max Key k-steps of 32 slots
-constexpr int RECORD = 130;            // partial record per query head: m, l, out[128]
 
 
 __device__ inline uint32_t rd(const u32x4& v, int i) { return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w)); }

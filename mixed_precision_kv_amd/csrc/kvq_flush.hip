@@ -19,6 +19,7 @@
 // either exact or correctly rounded and never a binary16 midpoint); values
 // beyond the binary16 range are stored as infinity with KVQ_FLAG_RANGE.
 #include "kvq_internal.h"
+#include "kvq_merge.h"
 
 namespace kvq {
 
@@ -616,70 +617,118 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
 }
 
 // ------------------------------------------------------------------ kernels
-__device__ inline void part_coords(const FlushArgs& A, int parts, int& part, int64_t& head, int64_t& row0,
+// Block `lin` of a flush: (kv head of batch) lin / (n_pages parts), page and
+// part from the remainder; the parts of one page are adjacent.
+__device__ inline void part_coords(const FlushArgs& A, int parts, int lin, int& part, int64_t& head, int64_t& row0,
                                    uint8_t*& page) {
-  const int p = blockIdx.x / parts;
-  part = blockIdx.x % parts;
-  head = (int64_t)blockIdx.z * A.n_kv_heads + blockIdx.y;
+  const int per_head = A.n_pages * parts;
+  head = lin / per_head;
+  const int x = lin - (int)head * per_head;
+  const int p = x / parts;
+  part = x - p * parts;
   row0 = head * A.src_stride + (int64_t)p * PAGE;
   page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
 }
 
+// One flush block (256 threads): value k-step `part` (< V_PARTS) or a Key
+// part of its page.
+template <int MODE>
+__device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
+  int part;
+  int64_t head, row0;
+  uint8_t* page;
+  part_coords(A, parts, lin, part, head, row0, page);
+  if constexpr (MODE == KVQ_KEY_MIXKVQ) {
+    __shared__ union {
+      VPartSmem v;
+      KPartSmem k;
+    } S;
+    const MixGeo g = mix_geo(A.n16, A.n4);
+    if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+    else flush_mix_key_part(A, page, head, row0, part - V_PARTS, S.k);
+  } else if constexpr (MODE == KVQ_KEY_PNMIX) {
+    __shared__ union {
+      VPartSmem v;
+      KPartSmem k;
+    } S;
+    const PnGeo g = pn_geo(A.n_hi);
+    if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+    else flush_pn_key_part(A, page, head, row0, part - V_PARTS, S.k);
+  } else {
+    __shared__ union {
+      VPartSmem v;
+      QPartSmem q;
+    } S;
+    const QjlGeo g = qjl_geo(A.qjl_m);
+    if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+    else flush_qjl_key_part(A, page, row0, part - V_PARTS, S.q);
+  }
+}
+
 __global__ __launch_bounds__(256) void flush_mixkvq_kernel(FlushArgs A, int parts) {
-  __shared__ union {
-    VPartSmem v;
-    KPartSmem k;
-  } S;
-  int part;
-  int64_t head, row0;
-  uint8_t* page;
-  part_coords(A, parts, part, head, row0, page);
-  const MixGeo g = mix_geo(A.n16, A.n4);
-  if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
-  else flush_mix_key_part(A, page, head, row0, part - V_PARTS, S.k);
+  flush_block<KVQ_KEY_MIXKVQ>(A, parts, blockIdx.x);
 }
-
 __global__ __launch_bounds__(256) void flush_pnmix_kernel(FlushArgs A, int parts) {
-  __shared__ union {
-    VPartSmem v;
-    KPartSmem k;
-  } S;
-  int part;
-  int64_t head, row0;
-  uint8_t* page;
-  part_coords(A, parts, part, head, row0, page);
-  const PnGeo g = pn_geo(A.n_hi);
-  if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
-  else flush_pn_key_part(A, page, head, row0, part - V_PARTS, S.k);
+  flush_block<KVQ_KEY_PNMIX>(A, parts, blockIdx.x);
 }
-
 __global__ __launch_bounds__(256) void flush_qjl_kernel(FlushArgs A, int parts) {
-  __shared__ union {
-    VPartSmem v;
-    QPartSmem q;
-  } S;
-  int part;
-  int64_t head, row0;
-  uint8_t* page;
-  part_coords(A, parts, part, head, row0, page);
-  const QjlGeo g = qjl_geo(A.qjl_m);
-  if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
-  else flush_qjl_key_part(A, page, row0, part - V_PARTS, S.q);
+  flush_block<KVQ_KEY_QJL>(A, parts, blockIdx.x);
 }
 
-// ------------------------------------------------------------------ launcher
-hipError_t launch_flush(int key_mode, const FlushArgs& a, int n_pages, int batch, hipStream_t stream) {
-  int parts;
-  if (key_mode == KVQ_KEY_MIXKVQ) parts = V_PARTS + max(1, (mix_geo(a.n16, a.n4).F + 3) / 4);   // part 0 also writes the BF16 rows
-  else if (key_mode == KVQ_KEY_PNMIX) parts = V_PARTS + 2;
-  else parts = V_PARTS + a.qjl_m / 64;
-  dim3 grid(n_pages * parts, a.n_kv_heads, batch);
+// A decode call's split merge beside a flush, in one launch (the two are
+// independent): blocks [0, n_flush) are flush blocks, the rest merge four
+// query heads each, one per wave. The merge waves touch no LDS and reach no
+// barrier, so blocks of either kind run the same code as on their own.
+template <int MODE, int NB>
+__global__ __launch_bounds__(256) void merge_flush_kernel(FlushArgs A, int parts, int n_flush, const float* partial,
+                                                          float* out, int n_parts, int rows) {
+  const int blk = blockIdx.x;
+  if (blk < n_flush) {
+    flush_block<MODE>(A, parts, blk);
+    return;
+  }
+  const int row = 4 * (blk - n_flush) + (threadIdx.x >> 6);
+  if (row < rows) merge_row<NB>(partial, out, n_parts, rows, row);
+}
+
+// ------------------------------------------------------------------ launchers
+static int flush_parts(int key_mode, const FlushArgs& a) {
+  if (key_mode == KVQ_KEY_MIXKVQ) return V_PARTS + max(1, (mix_geo(a.n16, a.n4).F + 3) / 4);   // part 0 also writes the BF16 rows
+  if (key_mode == KVQ_KEY_PNMIX) return V_PARTS + 2;
+  return V_PARTS + a.qjl_m / 64;
+}
+
+hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream) {
+  const int parts = flush_parts(key_mode, a);
+  const dim3 grid(a.n_pages * parts * a.n_kv_heads * batch);
   if (key_mode == KVQ_KEY_MIXKVQ)
     hipLaunchKernelGGL(flush_mixkvq_kernel, grid, dim3(256), 0, stream, a, parts);
   else if (key_mode == KVQ_KEY_PNMIX)
     hipLaunchKernelGGL(flush_pnmix_kernel, grid, dim3(256), 0, stream, a, parts);
   else
     hipLaunchKernelGGL(flush_qjl_kernel, grid, dim3(256), 0, stream, a, parts);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static void launch_mf(dim3 grid, hipStream_t s, const FlushArgs& f, int parts, int n_flush, const DecodeArgs& d,
+                      int n_parts, int rows) {
+  hipLaunchKernelGGL((merge_flush_kernel<MODE, 16>), grid, dim3(256), 0, s, f, parts, n_flush, d.partial, d.out,
+                     n_parts, rows);
+}
+
+hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s) {
+  const int parts = flush_parts(key_mode, f);
+  const int n_flush = f.n_pages * parts * f.n_kv_heads * batch;
+  const int rows = d.batch * d.n_q_heads;
+  const int n_parts = decode_parts(d);
+  const dim3 grid(n_flush + (rows + 3) / 4);
+  // merge batches of 16 parts: the merge's result does not depend on the
+  // batch, and larger batches' registers would be the whole kernel's and cut
+  // the flush blocks' occupancy; the merge hides behind the flush either way
+  if (key_mode == KVQ_KEY_MIXKVQ) launch_mf<KVQ_KEY_MIXKVQ>(grid, s, f, parts, n_flush, d, n_parts, rows);
+  else if (key_mode == KVQ_KEY_PNMIX) launch_mf<KVQ_KEY_PNMIX>(grid, s, f, parts, n_flush, d, n_parts, rows);
+  else launch_mf<KVQ_KEY_QJL>(grid, s, f, parts, n_flush, d, n_parts, rows);
   return hipGetLastError();
 }
 

@@ -173,6 +173,7 @@ struct FlushArgs {
   int64_t page_stride;
   int max_pages;
   int first_page;
+  int n_pages;                    // pages written per (batch, kv head)
   int n_kv_heads;
   int n16, n4;
   int n_hi;
@@ -213,9 +214,15 @@ struct DecodeArgs {
   int qjl_m;
 };
 
-hipError_t launch_flush(int key_mode, const FlushArgs& a, int n_pages, int batch, hipStream_t stream);
+hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);
 hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream);
-hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s);
+// with_merge false: the split kernels only; the caller launches the merge
+// (launch_merge_flush) with the same DecodeArgs
+hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s,
+                         bool with_merge = true);
+int decode_parts(const DecodeArgs& a);
+hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s);
+constexpr int RECORD = 130;       // partial record per query head: m, l, out[128]
 constexpr int DECODE_SLOTS = 2048;
 // Sink + residual tokens per BF16-segment workgroup; at most 256 segment
 // tokens (128 sinks + 128 residual) make MAX_SEG_SPLITS workgroups.

@@ -1,0 +1,83 @@
+// The log-sum-exp merge of a decode call's split partials, shared by the
+// merge kernel of the decode call and the kernel that runs it beside a flush.
+#pragma once
+#include "kvq_internal.h"
+
+namespace kvq {
+
+__device__ inline float wave_max64(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ inline float wave_sum64(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Merge of one query head's split partials (m, l, out[128] per split, out
+// scaled by 2^-m) by one wave, lane l owning channels 2l and 2l+1:
+//   M = max_j m_j, w_j = 2^(m_j - M), out = (sum_j w_j out_j) / (sum_j w_j l_j).
+// M and the l sum come first, lane-parallel over the parts (lane i takes
+// parts i, i + 64, ...), then out is one fused multiply-add chain over the
+// parts in order, NB value rows at a time (NB <= 64), the weights reaching
+// the lanes as lane reads (no LDS, no barrier). The result does not depend
+// on NB, bit for bit. The first batch's loads are issued with the (m, l)
+// loads, before any reduction, so up to min(NB, 64) parts cost one memory
+// round trip. Zero parts give zero output.
+template <int NB>
+__device__ inline void merge_row(const float* partial, float* out, int n_parts, int rows, int row) {
+  static_assert(NB == 16 || NB == 32 || NB == 64, "batch of parts");
+  const int lane = threadIdx.x & 63;
+  float* dst = out + (int64_t)row * D + 2 * lane;
+  if (n_parts <= 0) {
+    dst[0] = 0.f;
+    dst[1] = 0.f;
+    return;
+  }
+  const int64_t stride = (int64_t)rows * RECORD;           // from one part's record to the next
+  const float* base = partial + (int64_t)row * RECORD;
+  const int last = n_parts - 1;                             // loads are clamped to parts that exist
+  const float2 ml = *reinterpret_cast<const float2*>(base + min(lane, last) * stride);
+  float2 v[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) v[j] = *reinterpret_cast<const float2*>(base + min(j, last) * stride + 2 + 2 * lane);
+  auto weight = [](float m, float Mx) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mx); };
+  float mloc = lane <= last ? ml.x : -INFINITY;
+  for (int p = lane + 64; p <= last; p += 64) mloc = fmaxf(mloc, base[p * stride]);
+  const float M = wave_max64(mloc);
+  float lloc = lane <= last ? weight(ml.x, M) * ml.y : 0.f;
+  for (int p = lane + 64; p <= last; p += 64) {
+    const float2 t = *reinterpret_cast<const float2*>(base + p * stride);
+    lloc += weight(t.x, M) * t.y;
+  }
+  const float l = wave_sum64(lloc);
+  float o0 = 0.f, o1 = 0.f;
+  float w = weight(ml.x, M);                                // lane j < NB: part j
+  for (int s0 = 0;;) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (s0 + j <= last) {                                 // uniform: parts past the end are skipped
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        o0 = fmaf(wj, v[j].x, o0);
+        o1 = fmaf(wj, v[j].y, o1);
+      }
+    }
+    s0 += NB;
+    if (s0 > last) break;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, last) * stride + 2 + 2 * lane);
+    w = weight(base[min(s0 + (lane & (NB - 1)), last) * stride], M);
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  dst[0] = o0 * inv;
+  dst[1] = o1 * inv;
+}
+
+// NB for a call with n_parts parts: one batch whenever n_parts <= 64.
+inline int merge_batch(int n_parts) { return n_parts <= 16 ? 16 : (n_parts <= 32 ? 32 : 64); }
+
+}  // namespace kvq

@@ -86,6 +86,23 @@ class Pipeline:
                                  self.scale, self.out, self.ws, self.ws_bytes)
         return self.out
 
+    def decode_flush(self, n_pages=None, n_resid=None, first_page=None, n_flush=1):
+        """kvq_decode_attention_flush: the decode of `decode`, then the
+        residual buffer (all 128 rows) flushed into pages first_page .."""
+        w = self.w
+        n_pages = w.n_pages if n_pages is None else n_pages
+        n_resid = w.n_resid if n_resid is None else n_resid
+        first_page = n_pages if first_page is None else first_page
+        need = kvq.kvq_workspace_bytes(self.cfg, n_pages)
+        if need > self.ws_bytes:
+            self.ws_bytes = need
+            self.ws = torch.zeros(need // 4 + 64, dtype=torch.float32, device=self.dev)
+        kvq.kvq_decode_attention_flush(self.cfg, self.q_dec, self.arena, n_pages, self.mask, self.S,
+                                       self.sink_k, self.sink_v, w.n_sink, self.resid_k, self.resid_v, n_resid,
+                                       128, self.scale, self.out, self.ws, self.ws_bytes, self.resid_k,
+                                       self.resid_v, 128, n_flush, first_page, self.flags)
+        return self.out
+
     # ------------------------------------------------------------ host views
     def gpu_page(self, b, h, p):
         base = ((b * self.w.n_kv_heads + h) * self.max_pages + p) * self.page_bytes

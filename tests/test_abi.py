@@ -102,6 +102,20 @@ def test_validation_rejects_before_launch(lib):
     st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
                                 0.088, 16, 16, 16, None)
     assert st == kvq.KVQ_WORKSPACE_TOO_SMALL
+    # the fused call fails as a whole when either half's check fails
+    big = 1 << 30
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+                                      0.088, 16, 16, big, 16, 16, 128, 1, 8, 16, None)
+    assert st == kvq.KVQ_CAPACITY                                  # flush past max_pages
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+                                      0.088, 16, 16, big, 16, 16, 128, 1, 2, None, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # no status word
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, 16, 16, 129, 129,
+                                      0.088, 16, 16, big, 16, 16, 128, 1, 2, 16, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # decode half: residual longer than 128
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+                                      0.088, 16, 16, 16, 16, 16, 128, 1, 2, 16, None)
+    assert st == kvq.KVQ_WORKSPACE_TOO_SMALL
     qcfg = kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 8, qjl_m=256)
     st = S.kvq_select_channels(ctypes.byref(qcfg), 16, 10, 10, 16, 10, 10, 16, None)
     assert st == kvq.KVQ_UNSUPPORTED
