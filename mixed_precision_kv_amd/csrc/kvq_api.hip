@@ -90,6 +90,7 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   a.max_pages = cfg->max_pages;
   a.first_page = first_page;
   a.n_pages = n_pages;
+  a.units = n_pages * cfg->n_kv_heads * cfg->batch;
   a.n_kv_heads = cfg->n_kv_heads;
   a.n16 = cfg->n_bf16;
   a.n4 = cfg->n_u4;

@@ -617,15 +617,19 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
 }
 
 // ------------------------------------------------------------------ kernels
-// Block `lin` of a flush: (kv head of batch) lin / (n_pages parts), page and
-// part from the remainder; the parts of one page are adjacent.
+// Block `lin` of a flush: part lin / units of page unit lin % units (unit:
+// head-major, page-minor). Part-major order puts the parts of one page
+// `units` blocks apart, so with units a multiple of 8 they land on the same
+// XCD (blocks go round-robin over the 8) and the Key parts, which each stage
+// the page's whole Key tile, share that XCD's L2 rather than each fetching
+// the tile from memory.
 __device__ inline void part_coords(const FlushArgs& A, int parts, int lin, int& part, int64_t& head, int64_t& row0,
                                    uint8_t*& page) {
-  const int per_head = A.n_pages * parts;
-  head = lin / per_head;
-  const int x = lin - (int)head * per_head;
-  const int p = x / parts;
-  part = x - p * parts;
+  (void)parts;
+  part = lin / A.units;
+  const int unit = lin - part * A.units;
+  head = unit / A.n_pages;
+  const int p = unit - (int)head * A.n_pages;
   row0 = head * A.src_stride + (int64_t)p * PAGE;
   page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
 }
@@ -700,7 +704,8 @@ static int flush_parts(int key_mode, const FlushArgs& a) {
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream) {
   const int parts = flush_parts(key_mode, a);
-  const dim3 grid(a.n_pages * parts * a.n_kv_heads * batch);
+  const dim3 grid(a.units * parts);
+  (void)batch;
   if (key_mode == KVQ_KEY_MIXKVQ)
     hipLaunchKernelGGL(flush_mixkvq_kernel, grid, dim3(256), 0, stream, a, parts);
   else if (key_mode == KVQ_KEY_PNMIX)
@@ -719,7 +724,8 @@ static void launch_mf(dim3 grid, hipStream_t s, const FlushArgs& f, int parts, i
 
 hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s) {
   const int parts = flush_parts(key_mode, f);
-  const int n_flush = f.n_pages * parts * f.n_kv_heads * batch;
+  const int n_flush = f.units * parts;
+  (void)batch;
   const int rows = d.batch * d.n_q_heads;
   const int n_parts = decode_parts(d);
   const dim3 grid(n_flush + (rows + 3) / 4);

@@ -174,6 +174,7 @@ struct FlushArgs {
   int max_pages;
   int first_page;
   int n_pages;                    // pages written per (batch, kv head)
+  int units;                      // pages written in all: n_pages * n_kv_heads * batch
   int n_kv_heads;
   int n16, n4;
   int n_hi;
