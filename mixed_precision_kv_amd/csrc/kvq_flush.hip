@@ -33,31 +33,66 @@ struct GroupParam {
   uint16_t offset; // stored binary16 offset
 };
 
-// min / max / flags over n values read by a strided accessor (all in LDS)
+// A group's finite minimum and maximum, the smallest nonzero magnitude and
+// whether a non-finite value occurred. The exponent span the exact code path
+// needs follows from them: the largest exponent field is that of
+// max(|mn|, |mx|), the smallest that of the smallest nonzero magnitude
+// (subnormals count as field 1).
 struct Scan {
-  float mn, mx;
-  int emin, emax;  // exponent fields of nonzero |x|
+  float mn, mx;      // over finite values
+  uint32_t am1;      // min over the values of (|bits| - 1) mod 2^16: 0xFFFF with no nonzero value,
+                     // >= 0x7F7F with no finite nonzero value
   bool nonfinite;
 };
-__device__ inline void scan_init(Scan& s) {
-  s.mn = INFINITY;
-  s.mx = -INFINITY;
-  s.emin = 1000;
-  s.emax = -1000;
-  s.nonfinite = false;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Scan of N words, each two bf16 values (low half first). The fast pass is
+// two values per step: three-operand float min / max over both halves and
+// 16-bit packed integer min / max of the magnitude bits; a word with a
+// non-finite value only marks the group, whose minimum and maximum are then
+// taken again over the finite values alone.
+template <int N>
+__device__ inline Scan scan_words(const uint32_t (&w)[N]) {
+  float mn = INFINITY, mx = -INFINITY;
+  u16x2 am1 = {0xFFFF, 0xFFFF}, amax = {0, 0};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const u16x2 a = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
+    am1 = __builtin_elementwise_min(am1, a - (u16x2){1, 1});   // zero wraps to 0xFFFF
+    amax = __builtin_elementwise_max(amax, a);
+    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+    mn = fminf(mn, fminf(lo, hi));
+    mx = fmaxf(mx, fmaxf(lo, hi));
+  }
+  Scan s;
+  s.am1 = min((uint32_t)am1.x, (uint32_t)am1.y);
+  s.nonfinite = max(amax.x, amax.y) >= 0x7F80;
+  if (s.nonfinite) {   // rare: minimum and maximum over the finite values
+    mn = INFINITY;
+    mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2 * N; ++i) {
+      const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const bool fin = (b & 0x7FFF) < 0x7F80;
+      const float v = __uint_as_float(b << 16);
+      mn = fminf(mn, fin ? v : INFINITY);
+      mx = fmaxf(mx, fin ? v : -INFINITY);
+    }
+  }
+  s.mn = mn;
+  s.mx = mx;
+  return s;
 }
-// branch-free: a non-finite value only raises the flag; zeros leave the
-// exponent range alone (subnormals count as exponent field 1)
-__device__ inline void scan_add(Scan& s, uint16_t b) {
-  const int e = bf16_exp_field(b);
-  const bool fin = e != 0xFF, nz = (b & 0x7FFF) != 0 && fin;
-  const float v = bf16_to_f32(b);
-  s.nonfinite = s.nonfinite || !fin;
-  s.mn = fminf(s.mn, fin ? v : INFINITY);
-  s.mx = fmaxf(s.mx, fin ? v : -INFINITY);
-  s.emin = min(s.emin, nz ? max(e, 1) : 1000);
-  s.emax = max(s.emax, nz ? e : -1000);
+
+// Exponent span of the group's nonzero finite values beyond 38 binades.
+__device__ inline bool scan_span(const Scan& s) {
+  if (s.am1 >= 0x7F7Fu) return false;   // no nonzero finite value
+  const int emin = max((int)((s.am1 + 1) >> 7), 1);
+  const int emax = (int)((__float_as_uint(fmaxf(fabsf(s.mn), fabsf(s.mx))) >> 23) & 0xFF);
+  return emax - emin > 38;
 }
+
 // Merge with a partner lane through a DPP lane move (one VALU instruction,
 // no LDS round trip). Applied for W = 1, 2, 4 in turn it reduces over 2, 4 or
 // 8 consecutive lanes: the xor-1 and xor-2 quad permutations, then the
@@ -73,15 +108,17 @@ template <int W>
 __device__ inline void scan_merge(Scan& s) {
   s.mn = fminf(s.mn, __int_as_float(dpp_partner<W>(__float_as_int(s.mn))));
   s.mx = fmaxf(s.mx, __int_as_float(dpp_partner<W>(__float_as_int(s.mx))));
-  s.emin = min(s.emin, dpp_partner<W>(s.emin));
-  s.emax = max(s.emax, dpp_partner<W>(s.emax));
+  s.am1 = min(s.am1, (uint32_t)dpp_partner<W>((int)s.am1));
   s.nonfinite = s.nonfinite || dpp_partner<W>((int)s.nonfinite);
 }
 
 __device__ inline bool f16_is_inf(uint16_t h) { return (h & 0x7FFF) == 0x7C00; }
 
-__device__ inline void flag_range(const GroupParam& p, unsigned* flags) {
-  if (f16_is_inf(p.scale) || f16_is_inf(p.offset)) atomicOr(flags, KVQ_FLAG_RANGE);
+// the status bits a group raises, OR-ed into *flags with one atomic
+__device__ inline void raise_flags(const Scan& s, const GroupParam& p, unsigned* flags) {
+  const unsigned f = (s.nonfinite ? KVQ_FLAG_NONFINITE : 0u) | (scan_span(s) ? KVQ_FLAG_SPAN : 0u) |
+                     (f16_is_inf(p.scale) || f16_is_inf(p.offset) ? KVQ_FLAG_RANGE : 0u);
+  if (f) atomicOr(flags, f);
 }
 
 // min-max quantizer parameters for `levels` = 2^b - 1
@@ -92,8 +129,6 @@ __device__ inline GroupParam make_param(const Scan& s, int levels, unsigned* fla
   p.offset = s.mn == INFINITY ? (uint16_t)0 : f64_to_f16_rne((double)s.mn);
   p.inv = 0.0f;
   p.scale = 0;
-  if (s.nonfinite) atomicOr(flags, KVQ_FLAG_NONFINITE);
-  if (s.emax - s.emin > 38) atomicOr(flags, KVQ_FLAG_SPAN);
   if (s.mx > s.mn) {
     p.M = s.mx;
     const double den = (double)s.mx - (double)s.mn;
@@ -101,7 +136,7 @@ __device__ inline GroupParam make_param(const Scan& s, int levels, unsigned* fla
     if (!(p.inv >= 0x1.0p-126f && p.inv <= 0x1.0p126f)) p.inv = NAN;   // outside the fast path's bound
     p.scale = f64_to_f16_rne(den / (double)levels);
   }
-  flag_range(p, flags);
+  raise_flags(s, p, flags);
   return p;
 }
 
@@ -113,8 +148,6 @@ __device__ inline GroupParam make_param_mid(const Scan& s, unsigned* flags) {
   p.inv = 0.0f;
   p.scale = 0;
   p.offset = s.mn == INFINITY ? (uint16_t)0 : f64_to_f16_rne((double)s.mn);
-  if (s.nonfinite) atomicOr(flags, KVQ_FLAG_NONFINITE);
-  if (s.emax - s.emin > 38) atomicOr(flags, KVQ_FLAG_SPAN);
   if (s.mx > s.mn) {
     p.M = s.mx;
     const double den = (double)s.mx - (double)s.mn;
@@ -123,7 +156,7 @@ __device__ inline GroupParam make_param_mid(const Scan& s, unsigned* flags) {
     p.scale = f64_to_f16_rne(0.5 * den);
     p.offset = f64_to_f16_rne(0.25 * (3.0 * (double)s.mn + (double)s.mx));
   }
-  flag_range(p, flags);
+  raise_flags(s, p, flags);
   return p;
 }
 
@@ -224,13 +257,10 @@ __device__ __attribute__((always_inline)) inline void flush_value_part(uint8_t* 
   __syncthreads();
   {  // 128 groups, two threads each
     const int gi = threadIdx.x >> 1, half = threadIdx.x & 1, tl = gi >> 2, j = gi & 3;
-    Scan sc;
-    scan_init(sc);
     const uint4* src = reinterpret_cast<const uint4*>(S.tile + tl * D + GV * j + 16 * half);
     const uint4 c0 = src[0], c1 = src[1];
     const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) scan_add(sc, (uint16_t)(cw[c >> 1] >> (16 * (c & 1))));
+    Scan sc = scan_words(cw);
     scan_merge<1>(sc);
     if (half == 0) S.vp[gi] = make_param(sc, 3, flags);
   }
@@ -339,12 +369,13 @@ __device__ __attribute__((always_inline)) inline void flush_mix_key_part(const F
     int levels = 0;
     bool primary = false;
     const int pos = mix_slot_pos(g, 32 * fg + ls, levels, primary);
-    Scan sc;
-    scan_init(sc);
-    if (pos >= 0 && primary) {
-      const int d = S.ch[pos];
-      for (int t = 16 * part; t < 16 * part + 16; ++t) scan_add(sc, S.tile[t * KS + d]);
-    }
+    uint32_t cw[8];
+    const int dd = pos >= 0 ? S.ch[pos] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      cw[i] = (uint32_t)S.tile[(16 * part + 2 * i) * KS + dd] | ((uint32_t)S.tile[(16 * part + 2 * i + 1) * KS + dd] << 16);
+    Scan sc = scan_words(cw);
+    if (!(pos >= 0 && primary)) sc = Scan{INFINITY, -INFINITY, 0xFFFFu, false};   // no parameters of its own
     scan_merge<1>(sc);
     scan_merge<2>(sc);
     scan_merge<4>(sc);
@@ -465,9 +496,11 @@ __device__ __attribute__((always_inline)) inline void flush_pn_key_part(const Fl
   {
     const int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
     const int d = S.ch[slot];
-    Scan sc;
-    scan_init(sc);
-    for (int t = half * 64; t < half * 64 + 64; ++t) scan_add(sc, S.tile[t * KS + d]);
+    uint32_t cw[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      cw[i] = (uint32_t)S.tile[(half * 64 + 2 * i) * KS + d] | ((uint32_t)S.tile[(half * 64 + 2 * i + 1) * KS + d] << 16);
+    Scan sc = scan_words(cw);
     scan_merge<1>(sc);
     if (half == 0) S.kp[slot] = slot < nhs ? make_param(sc, 7, A.flags) : make_param_mid(sc, A.flags);
   }
