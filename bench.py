@@ -221,6 +221,30 @@ class Rig:
         self.kvq.kvq_flush_quantize(self.cfg, self.rks[c], self.rvs[c], 128, 1, self.mask, self.S,
                                     self.arenas[c], w.n_pages, self.flags)
 
+    def make_paged(self, seed=7):
+        """For every cache copy, the same pages scattered over the pool by a
+        random permutation, and its page table."""
+        torch, w = self.torch, self.w
+        H = w.batch * w.n_kv_heads
+        pool = H * self.max_pages
+        gen = torch.Generator(device="cpu").manual_seed(seed)
+        self.paged, self.tables = [], []
+        for arena in self.arenas:
+            perm = torch.randperm(pool, generator=gen).cuda()
+            paged = torch.empty_like(arena)
+            paged.view(pool, -1).index_copy_(0, perm, arena.view(pool, -1))
+            self.paged.append(paged)
+            self.tables.append(perm.to(torch.int32).reshape(H, self.max_pages))
+        torch.cuda.synchronize()
+
+    def decode_paged(self, i):
+        w = self.w
+        c = i % len(self.arenas)
+        self.kvq.kvq_decode_attention(self.cfg, self.q, self.paged[c], w.n_pages, self.mask, self.S,
+                                      self.sink_k, self.sink_v, w.n_sink, self.rks[c], self.rvs[c], w.n_resid,
+                                      128, self.scale, self.out, self.ws, self.ws_bytes,
+                                      page_table=self.tables[c], table_stride=self.max_pages)
+
     def decode_flush(self, i):
         """One step in one call: the decode, then the residual flushed into
         page n_pages, the flush sharing a launch with the decode's merge."""
@@ -410,6 +434,10 @@ def main():
     # warm-cache decode (no rotation) as a secondary number
     dec_w_ms, _ = graph_time(torch, [lambda: rig.decode(0)] * K, [lambda: rig.decode(0)] * 3)
     dec_warm_gbps = dbytes / (dec_w_ms * 1e-3) / 1e9
+    # the same decode with its pages scattered over the pool (page table)
+    rig.make_paged()
+    dec_p_ms, _ = graph_time(torch, [lambda i=i: rig.decode_paged(i) for i in range(K)],
+                             [lambda i=i: rig.decode_paged(i) for i in range(W)])
     del rig
     torch.cuda.empty_cache()
 
@@ -422,8 +450,12 @@ def main():
         k2 = max(10, K // 2)
         d2, _ = graph_time(torch, [lambda i=i: rig2.decode(i) for i in range(k2)],
                            [lambda i=i: rig2.decode(i) for i in range(3)])
+        rig2.make_paged()
+        d2p, _ = graph_time(torch, [lambda i=i: rig2.decode_paged(i) for i in range(k2)],
+                            [lambda i=i: rig2.decode_paged(i) for i in range(3)])
         extra = {"workload": w2.name, "decode_ms": d2, "decode_GBps": decode_bytes(w2) / (d2 * 1e-3) / 1e9,
-                 "decode_frac_hbm_peak": decode_bytes(w2) / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                 "decode_frac_hbm_peak": decode_bytes(w2) / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "decode_paged_ms": d2p, "decode_paged_GBps": decode_bytes(w2) / (d2p * 1e-3) / 1e9}
         del rig2
         torch.cuda.empty_cache()
 
@@ -459,6 +491,8 @@ def main():
         "decode_frac_hbm_peak": dec_gbps / HBM_PEAK_GBPS,
         "decode_ms": dec_ms,
         "decode_warm_GBps": dec_warm_gbps,
+        "decode_paged_ms": dec_p_ms,
+        "decode_paged_GBps": dbytes / (dec_p_ms * 1e-3) / 1e9,
         "flush_tokens_per_s": flush_tok_s,
         "flush_ms": fl_ms,
         "roofline": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_HEAD_DIM 128
 #define KVQ_PAGE_TOKENS 128
 #define KVQ_VALUE_GROUP 32
@@ -78,6 +78,7 @@ typedef enum kvq_pair_layout {
 #define KVQ_FLAG_SPAN 2u        /* a group spans more than 38 binades; its codes may be off by one */
 #define KVQ_FLAG_MASK 4u        /* a PN-Mix record selects a pair count other than n_hi_pairs */
 #define KVQ_FLAG_RANGE 8u       /* a group's scale or offset exceeds the binary16 range (stored as inf) */
+#define KVQ_FLAG_TABLE 16u      /* a page-table entry of a flushed page lies outside the pool; that page is not written */
 
 /* Plain-old-data configuration, passed by pointer to every call. */
 typedef struct kvq_config {
@@ -169,12 +170,22 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
  *   src[((b*Hkv + h)*src_stride + p*128 + t)*128 + d].
  * mask: the records of kvq_select_channels (ignored for QJL).
  * qjl_s: device bf16 [qjl_m][128] (QJL only, else may be NULL).
- * page_arena: device, [batch][n_kv_heads][max_pages] pages of kvq_page_bytes.
+ * page_arena: device, batch * n_kv_heads * max_pages pages of kvq_page_bytes
+ *   (the page pool).
+ * page_table: NULL, or device int32 [batch][n_kv_heads][table_stride], 4-byte
+ *   aligned: entry p of (b, h) is the pool index of logical page p (a block
+ *   table as in vLLM, whose serving setup the MixKVQ runtime evaluation
+ *   follows; the pages leave the managing of non-contiguous blocks open).
+ *   NULL: logical page p of (b, h) is pool page (b * n_kv_heads + h) *
+ *   max_pages + p. An entry outside [0, pool) is not written to: that page
+ *   is skipped and KVQ_FLAG_TABLE raised.
  * status_flags: device uint32 (not NULL) the kernels OR KVQ_FLAG_* bits into.
- * Returns KVQ_CAPACITY if first_page + n_pages > max_pages. */
+ * Returns KVQ_CAPACITY if first_page + n_pages exceeds max_pages (no table)
+ * or table_stride (with a table). */
 kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src,
                               int64_t src_stride, int32_t n_pages, const void* mask,
-                              const void* qjl_s, void* page_arena, int32_t first_page,
+                              const void* qjl_s, void* page_arena, const int32_t* page_table,
+                              int32_t table_stride, int32_t first_page,
                               uint32_t* status_flags, void* stream);
 
 /* Single-token decode attention over [sinks | pages 0..n_pages-1 | residual]
@@ -184,6 +195,10 @@ kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const vo
  *   logit_t = softmax_scale * q . k^_t for BF16 and dequantized keys,
  *   logit_t = softmax_scale * sqrt(pi/2)/m * nu_t * <S q, sign(S k_t)> for QJL pages.
  * q: device bf16 [batch][n_q_heads][128]; query head h uses kv head h / (Hq/Hkv).
+ * page_arena, page_table, table_stride: as for kvq_flush_quantize; pages
+ *   0 .. n_pages - 1 are read (n_pages <= max_pages without a table, <=
+ *   table_stride with one). A table entry outside the pool is clamped into
+ *   it (that page's contribution is then unspecified).
  * mask: the records of kvq_select_channels, 16-byte aligned (ignored for QJL
  *   and when n_pages is 0).
  * sink_k/sink_v: device bf16 [batch][n_kv_heads][n_sink][128] (n_sink <= 128; may be NULL if 0).
@@ -194,6 +209,7 @@ kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const vo
  *   partials; for QJL also S q). Calls sharing one workspace must be ordered
  *   on one stream; concurrent calls on the same workspace race. */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena,
+                                const int32_t* page_table, int32_t table_stride,
                                 int32_t n_pages, const void* mask, const void* qjl_s,
                                 const void* sink_k, const void* sink_v, int32_t n_sink,
                                 const void* resid_k, const void* resid_v, int32_t n_resid,
@@ -210,13 +226,15 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
  *   flush's source, count and target (flush_k_src, flush_v_src,
  *   flush_src_stride, n_flush_pages, flush_first_page, status_flags: as
  *   k_src, v_src, src_stride, n_pages, first_page, status_flags of
- *   kvq_flush_quantize); cfg, mask, qjl_s, page_arena and stream serve both.
+ *   kvq_flush_quantize); cfg, mask, qjl_s, page_arena, page_table,
+ *   table_stride and stream serve both.
  * Results: out, the written pages and the status bits are bit-identical to
  *   the two calls made in that order on one stream; the flush writes after
  *   the decode has read the arena, so the page ranges may overlap.
  * Errors: any check of either call fails the whole call and launches
  *   nothing. The workspace rule of kvq_decode_attention applies. */
 kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void* page_arena,
+                                      const int32_t* page_table, int32_t table_stride,
                                       int32_t n_pages, const void* mask, const void* qjl_s,
                                       const void* sink_k, const void* sink_v, int32_t n_sink,
                                       const void* resid_k, const void* resid_v, int32_t n_resid,

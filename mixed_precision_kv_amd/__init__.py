@@ -15,11 +15,11 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_ABI_VERSION = 1
+KVQ_ABI_VERSION = 2
 KVQ_OK, KVQ_INVALID_ARG, KVQ_UNSUPPORTED, KVQ_WORKSPACE_TOO_SMALL, KVQ_CAPACITY, KVQ_HIP_ERROR = range(6)
 KVQ_KEY_MIXKVQ, KVQ_KEY_PNMIX, KVQ_KEY_QJL = 0, 1, 2
 KVQ_PAIR_HALF_SPLIT, KVQ_PAIR_ADJACENT = 0, 1
-KVQ_FLAG_NONFINITE, KVQ_FLAG_SPAN, KVQ_FLAG_MASK, KVQ_FLAG_RANGE = 1, 2, 4, 8
+KVQ_FLAG_NONFINITE, KVQ_FLAG_SPAN, KVQ_FLAG_MASK, KVQ_FLAG_RANGE, KVQ_FLAG_TABLE = 1, 2, 4, 8, 16
 
 EXPORTED = (
     "kvq_abi_version", "kvq_status_string", "kvq_page_bytes", "kvq_mask_bytes",
@@ -71,11 +71,11 @@ def load(path: str = LIB_PATH):
         "kvq_workspace_bytes": (I32, [cfgp, I32, ctypes.POINTER(SZ)]),
         "kvq_storage_bytes": (I32, [cfgp, I64, I32, I32, ctypes.POINTER(KvqStorage)]),
         "kvq_select_channels": (I32, [cfgp, P, I64, I64, P, I64, I64, P, P]),
-        "kvq_flush_quantize": (I32, [cfgp, P, P, I64, I32, P, P, P, I32, P, P]),
-        "kvq_decode_attention": (I32, [cfgp, P, P, I32, P, P, P, P, I32, P, P, I32, I32, ctypes.c_float,
+        "kvq_flush_quantize": (I32, [cfgp, P, P, I64, I32, P, P, P, P, I32, I32, P, P]),
+        "kvq_decode_attention": (I32, [cfgp, P, P, P, I32, I32, P, P, P, P, I32, P, P, I32, I32, ctypes.c_float,
                                        P, P, SZ, P]),
-        "kvq_decode_attention_flush": (I32, [cfgp, P, P, I32, P, P, P, P, I32, P, P, I32, I32, ctypes.c_float,
-                                             P, P, SZ, P, P, I64, I32, I32, P, P]),
+        "kvq_decode_attention_flush": (I32, [cfgp, P, P, P, I32, I32, P, P, P, P, I32, P, P, I32, I32,
+                                             ctypes.c_float, P, P, SZ, P, P, I64, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -166,20 +166,21 @@ def kvq_select_channels(cfg, q_pre, l_q, k_pre, l_k, mask_out, *, q_stride=None,
 
 
 def kvq_flush_quantize(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, first_page,
-                       status_flags, *, stream=None):
+                       status_flags, *, page_table=None, table_stride=0, stream=None):
     _check("kvq_flush_quantize", load().kvq_flush_quantize(
         ctypes.byref(cfg), _ptr(k_src), _ptr(v_src), src_stride, n_pages, _ptr(mask), _ptr(qjl_s),
-        _ptr(page_arena), first_page, _ptr(status_flags), _stream(stream)))
+        _ptr(page_arena), _ptr(page_table), table_stride, first_page, _ptr(status_flags), _stream(stream)))
 
 
 def kvq_decode_attention_flush(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k,
                                resid_v, n_resid, resid_stride, softmax_scale, out, workspace, workspace_bytes,
                                flush_k_src, flush_v_src, flush_src_stride, n_flush_pages, flush_first_page,
-                               status_flags, *, stream=None):
+                               status_flags, *, page_table=None, table_stride=0, stream=None):
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check("kvq_decode_attention_flush", load().kvq_decode_attention_flush(
-        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), n_pages, _ptr(mask), _ptr(qjl_s), _ptr(sink_k),
+        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), _ptr(page_table), table_stride, n_pages, _ptr(mask),
+        _ptr(qjl_s), _ptr(sink_k),
         _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride, softmax_scale, _ptr(out),
         _ptr(workspace), workspace_bytes, _ptr(flush_k_src), _ptr(flush_v_src), flush_src_stride, n_flush_pages,
         flush_first_page, _ptr(status_flags), _stream(stream)))
@@ -187,10 +188,11 @@ def kvq_decode_attention_flush(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k,
 
 def kvq_decode_attention(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k, resid_v,
                          n_resid, resid_stride, softmax_scale, out, workspace, workspace_bytes=None, *,
-                         stream=None):
+                         page_table=None, table_stride=0, stream=None):
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check("kvq_decode_attention", load().kvq_decode_attention(
-        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), n_pages, _ptr(mask), _ptr(qjl_s), _ptr(sink_k),
+        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), _ptr(page_table), table_stride, n_pages, _ptr(mask),
+        _ptr(qjl_s), _ptr(sink_k),
         _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride, softmax_scale, _ptr(out),
         _ptr(workspace), workspace_bytes, _stream(stream)))

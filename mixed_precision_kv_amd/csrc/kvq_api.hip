@@ -17,6 +17,7 @@ static kvq_status check_config(const kvq_config* c) {
     if (c->reserved[i] != 0) return KVQ_INVALID_ARG;
   if (c->head_dim != D) return c->head_dim > 0 ? KVQ_UNSUPPORTED : KVQ_INVALID_ARG;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_pages < 1) return KVQ_INVALID_ARG;
+  if ((int64_t)c->batch * c->n_kv_heads * c->max_pages > INT32_MAX) return KVQ_INVALID_ARG;   // pool indices are int32
   if (c->n_q_heads % c->n_kv_heads) return KVQ_INVALID_ARG;
   const int g = c->n_q_heads / c->n_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return KVQ_UNSUPPORTED;
@@ -37,6 +38,9 @@ static kvq_status check_config(const kvq_config* c) {
   }
   return KVQ_OK;
 }
+
+// pages in the arena: the pool a page table indexes
+static int pool_pages(const kvq_config* c) { return c->batch * c->n_kv_heads * c->max_pages; }
 
 static size_t page_stride(const kvq_config* c) {
   if (c->key_mode == KVQ_KEY_MIXKVQ) return (size_t)mix_geo(c->n_bf16, c->n_u4).stride;
@@ -69,13 +73,15 @@ static size_t workspace_for(const kvq_config* c, int n_pages) {
 // the result is KVQ_OK, also for n_pages == 0).
 static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
                                 int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
-                                int32_t first_page, uint32_t* status_flags, FlushArgs& a) {
+                                const int32_t* page_table, int32_t table_stride, int32_t first_page,
+                                uint32_t* status_flags, FlushArgs& a) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if (!k_src || !v_src || !page_arena || !status_flags) return KVQ_INVALID_ARG;
   if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(page_arena)) return KVQ_INVALID_ARG;
+  if (page_table && (table_stride < 1 || ((uintptr_t)page_table & 3u))) return KVQ_INVALID_ARG;
   if (n_pages < 0 || first_page < 0 || src_stride < (int64_t)n_pages * PAGE) return KVQ_INVALID_ARG;
-  if ((int64_t)first_page + n_pages > cfg->max_pages) return KVQ_CAPACITY;
+  if ((int64_t)first_page + n_pages > (page_table ? table_stride : cfg->max_pages)) return KVQ_CAPACITY;
   if (cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
   if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
   // one block per (page, part, kv head, batch) on a one-dimensional grid
@@ -87,6 +93,9 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   a.qjl_s = (const uint16_t*)qjl_s;
   a.arena = (uint8_t*)page_arena;
   a.page_stride = (int64_t)page_stride(cfg);
+  a.table = page_table;
+  a.table_stride = page_table ? table_stride : 0;
+  a.pool_pages = pool_pages(cfg);
   a.max_pages = cfg->max_pages;
   a.first_page = first_page;
   a.n_pages = n_pages;
@@ -102,7 +111,8 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
 }
 
 // Checks of kvq_decode_attention and its kernel arguments.
-static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const void* page_arena, int32_t n_pages,
+static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const void* page_arena,
+                                 const int32_t* page_table, int32_t table_stride, int32_t n_pages,
                                  const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
                                  int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
                                  int32_t resid_stride, float softmax_scale, float* out, void* workspace,
@@ -112,7 +122,8 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   const int g = cfg->n_q_heads / cfg->n_kv_heads;
   if (g > 8) return KVQ_UNSUPPORTED;
   if (!q || !out || !workspace || !aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_INVALID_ARG;
-  if (n_pages < 0 || n_pages > cfg->max_pages) return KVQ_INVALID_ARG;
+  if (page_table && (table_stride < 1 || ((uintptr_t)page_table & 3u))) return KVQ_INVALID_ARG;
+  if (n_pages < 0 || n_pages > (page_table ? table_stride : cfg->max_pages)) return KVQ_INVALID_ARG;
   if (n_pages > 0 && (!page_arena || !aligned16(page_arena))) return KVQ_INVALID_ARG;
   if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
   if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
@@ -125,6 +136,9 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.q = (const uint16_t*)q;
   a.arena = (const uint8_t*)page_arena;
   a.page_stride = (int64_t)page_stride(cfg);
+  a.table = page_table;
+  a.table_stride = page_table ? table_stride : 0;
+  a.pool_pages = pool_pages(cfg);
   a.max_pages = cfg->max_pages;
   a.n_pages = n_pages;
   a.n_seg_splits = seg_splits(n_sink + n_resid);
@@ -268,30 +282,33 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
 
 kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
                               int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
-                              int32_t first_page, uint32_t* status_flags, void* stream) {
+                              const int32_t* page_table, int32_t table_stride, int32_t first_page,
+                              uint32_t* status_flags, void* stream) {
   FlushArgs a;
-  const kvq_status st = flush_prepare(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, first_page,
-                                      status_flags, a);
+  const kvq_status st = flush_prepare(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, page_table,
+                                      table_stride, first_page, status_flags, a);
   if (st != KVQ_OK || n_pages == 0) return st;
   return launch_flush(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 
-kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena, int32_t n_pages,
+kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void* page_arena,
+                                const int32_t* page_table, int32_t table_stride, int32_t n_pages,
                                 const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
                                 int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
                                 int32_t resid_stride, float softmax_scale, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   DecodeArgs a;
-  const kvq_status st = decode_prepare(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k,
-                                       resid_v, n_resid, resid_stride, softmax_scale, out, workspace,
-                                       workspace_bytes, a);
+  const kvq_status st = decode_prepare(cfg, q, page_arena, page_table, table_stride, n_pages, mask, qjl_s, sink_k,
+                                       sink_v, n_sink, resid_k, resid_v, n_resid, resid_stride, softmax_scale, out,
+                                       workspace, workspace_bytes, a);
   if (st != KVQ_OK) return st;
   return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream) == hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;
 }
 
-kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void* page_arena, int32_t n_pages,
+kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void* page_arena,
+                                      const int32_t* page_table, int32_t table_stride, int32_t n_pages,
                                       const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
                                       int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
                                       int32_t resid_stride, float softmax_scale, float* out, void* workspace,
@@ -299,12 +316,13 @@ kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void
                                       int64_t flush_src_stride, int32_t n_flush_pages, int32_t flush_first_page,
                                       uint32_t* status_flags, void* stream) {
   DecodeArgs d;
-  kvq_status st = decode_prepare(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k, resid_v,
-                                 n_resid, resid_stride, softmax_scale, out, workspace, workspace_bytes, d);
+  kvq_status st = decode_prepare(cfg, q, page_arena, page_table, table_stride, n_pages, mask, qjl_s, sink_k, sink_v,
+                                 n_sink, resid_k, resid_v, n_resid, resid_stride, softmax_scale, out, workspace,
+                                 workspace_bytes, d);
   if (st != KVQ_OK) return st;
   FlushArgs f;
   st = flush_prepare(cfg, flush_k_src, flush_v_src, flush_src_stride, n_flush_pages, mask, qjl_s, page_arena,
-                     flush_first_page, status_flags, f);
+                     page_table, table_stride, flush_first_page, status_flags, f);
   if (st != KVQ_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
   if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false) != hipSuccess) return KVQ_HIP_ERROR;

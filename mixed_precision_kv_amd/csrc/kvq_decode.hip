@@ -74,7 +74,6 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   init_state(st);
   const int p0 = split * A.pps;
   const int p1 = min(A.n_pages, p0 + A.pps);
-  const uint8_t* pages = A.arena + head * A.max_pages * A.page_stride;
 
   if constexpr (MODE == KVQ_KEY_MIXKVQ) {
     const MixGeo g = mix_geo(A.n16, A.n4);
@@ -105,7 +104,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
     const float xs = A.scale_log2 * B_UNSCALE;
 
     for (int pg = p0; pg < p1; ++pg) {
-      const uint8_t* page = pages + (int64_t)pg * A.page_stride;
+      const uint8_t* page = page_ptr(A, head, pg);
       u32x4 vc[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
     const int NUP = (g.n_hi + 31) / 32;
     const float xs = A.scale_log2 * B_UNSCALE;
     for (int pg = p0; pg < p1; ++pg) {
-      const uint8_t* page = pages + (int64_t)pg * A.page_stride;
+      const uint8_t* page = page_ptr(A, head, pg);
       u32x4 vc[4], lsb[2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
@@ -245,7 +244,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
     __syncthreads();
     const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
     for (int pg = p0; pg < p1; ++pg) {
-      const uint8_t* page = pages + (int64_t)pg * A.page_stride;
+      const uint8_t* page = page_ptr(A, head, pg);
       u32x4 vc[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);

@@ -324,6 +324,14 @@ __device__ inline bf16x8 as_bf16x8(const u32x4& v) {
 // every page split first, slice by slice, then the BF16-segment workgroups.
 // The page splits fill the resident slots; the short segment workgroups are
 // dispatched after them and take the slots page splits release.
+// Address of logical page p of head `head`: through the page table when
+// there is one (the entry clamped into the pool), else contiguous.
+__device__ inline const uint8_t* page_ptr(const DecodeArgs& A, int64_t head, int p) {
+  if (A.table == nullptr) return A.arena + (head * A.max_pages + p) * A.page_stride;
+  const int v = A.table[head * A.table_stride + p];
+  return A.arena + (int64_t)min(max(v, 0), A.pool_pages - 1) * A.page_stride;
+}
+
 struct DecodeBlock {
   int b, kvh, split;
 };

@@ -46,6 +46,36 @@ __device__ inline void async16_in(__amdgpu_buffer_rsrc_t r, int off, uint8_t* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_base, 16, off, 0, 0, 0);
 }
 
+// Where a split's pages are. PAGED false: contiguous from the split's first
+// page. PAGED true: through the page table, lane i holding the pool index of
+// page p0 + i (np <= 64; one range-limited load, lanes past np read zero),
+// clamped into the pool; page `it` (uniform) is then one lane read away.
+template <bool PAGED>
+struct PageSet {
+  const uint8_t* base;
+  int64_t stride;
+  int tab;
+  __device__ const uint8_t* at(int it) const {
+    if constexpr (PAGED) return base + (int64_t)__builtin_amdgcn_readlane(tab, it) * stride;
+    else return base + (int64_t)it * stride;
+  }
+};
+template <bool PAGED>
+__device__ inline PageSet<PAGED> page_set(const DecodeArgs& A, int64_t head, int p0, int np, int lane) {
+  PageSet<PAGED> s;
+  s.stride = A.page_stride;
+  if constexpr (PAGED) {
+    const auto r = range_rsrc(reinterpret_cast<const uint8_t*>(A.table + head * A.table_stride + p0), 4 * np);
+    const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(r, 4 * lane, 0, 0);
+    s.tab = min(max(v, 0), A.pool_pages - 1);
+    s.base = A.arena;
+  } else {
+    s.tab = 0;
+    s.base = A.arena + (head * A.max_pages + p0) * A.page_stride;
+  }
+  return s;
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 // Emitted through the builtin (not inline asm) so that the compiler's own
 // wait insertion knows which loads have completed: otherwise, with an
@@ -273,7 +303,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
 
 // Registers of 256 VGPRs (two waves per SIMD) fit every variant except the
 // eight-channel BF16 tier, which keeps one wave per SIMD rather than spill.
-template <int G, int NKS, int NB>
+template <int G, int NKS, int NB, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 : 2))) void decode_mix_fast(
     DecodeArgs A) {
   constexpr int C = 16 / G;
@@ -293,7 +323,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   const MixGeo g = mix_geo(A.n16, A.n4);
   const uint8_t* rec = A.mask + head * MIX_RECORD;
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
-  const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
+  const PageSet<PAGED> pset = page_set<PAGED>(A, head, p0, np, lane);
 
   // Set-up loads first (loads return in issue order, so they arrive before
   // the page): the selection record as one dword per lane, the query rows.
@@ -303,6 +333,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   const uint32_t recw = ld4(A.mask + head * MIX_RECORD + 4 * min(lane, MIX_RECORD / 4 - 1));
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
+  const uint8_t* pages = pset.at(0);   // paged: waits for the table load only
   u32x4 m0[3];
   m0[0] = ld16_in(range_rsrc(pages + g.off_meta, 32 * g.F), 16 * lane);   // zero past the page's 32 F bytes
   m0[1] = ld16(pages + g.off_v + V_CODE_BYTES + 16 * lane);
@@ -376,15 +407,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
     wait_vm<0>();
     if (it + 1 < np) {
-      mix_issue_meta(pages + (int64_t)(it + 1) * A.page_stride, slot1, g, lane);
-      mix_load(c1, pages + (int64_t)(it + 1) * A.page_stride, g, a, r);
+      mix_issue_meta(pset.at(it + 1), slot1, g, lane);
+      mix_load(c1, pset.at(it + 1), g, a, r);
     }
     mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col);
     if (it + 1 >= np) break;
     wait_vm<0>();
     if (it + 2 < np) {
-      mix_issue_meta(pages + (int64_t)(it + 2) * A.page_stride, slot0, g, lane);
-      mix_load(c0, pages + (int64_t)(it + 2) * A.page_stride, g, a, r);
+      mix_issue_meta(pset.at(it + 2), slot0, g, lane);
+      mix_load(c0, pset.at(it + 2), g, a, r);
     }
     mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col);
   }
@@ -437,7 +468,7 @@ __device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, c
   join_halves(logit);
 }
 
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_pn_fast(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
@@ -453,13 +484,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const PnGeo g = pn_geo(A.n_hi);
   const uint8_t* rec = A.mask + head * PN_RECORD;
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
-  const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
+  const PageSet<PAGED> pset = page_set<PAGED>(A, head, p0, np, lane);
 
   // set-up loads (the record, the query rows), then the first page, before
   // any of them is waited for
   const uint64_t mask = *reinterpret_cast<const uint64_t*>(rec);   // pair p is high iff bit p
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
+  const uint8_t* pages = pset.at(0);   // paged: waits for the table load only
 
   PnKey kp[2];
   ValCodes vp[2];
@@ -512,8 +544,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   init_state(st);
   const float xs = A.scale_log2 * B_UNSCALE;
   page_loop(
-      np, kp, vp, [&](PnKey& k, int p) { pn_load_key(k, pages + (int64_t)p * A.page_stride, g, lane, a, r); },
-      [&](ValCodes& v, int p) { load_vcodes(v, pages + (int64_t)p * A.page_stride, g.off_v, a, r); },
+      np, kp, vp, [&](PnKey& k, int p) { pn_load_key(k, pset.at(p), g, lane, a, r); },
+      [&](ValCodes& v, int p) { load_vcodes(v, pset.at(p), g.off_v, a, r); },
       [&](const PnKey& k, const ValCodes& v, int s, auto mid) {
         uint8_t* slot = S.u.pg.meta[s];
         commit_meta(k.m, slot, lane);
@@ -578,7 +610,7 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey& c, const uint8_t*
   }
 }
 
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_qjl_fast(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
@@ -593,7 +625,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
   const QjlGeo g = qjl_geo(A.qjl_m);
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
-  const uint8_t* pages = A.arena + (head * A.max_pages + p0) * A.page_stride;
+  const PageSet<PAGED> pset = page_set<PAGED>(A, head, p0, np, lane);
 
   // S q of this lane's head first (all of it, so the set-up waits once),
   // then the first page, before any load is waited for
@@ -604,6 +636,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) sqv[ks][hf] = *reinterpret_cast<const float4*>(sqrow + 32 * ks + 8 * a + 4 * hf);
+  const uint8_t* pages = pset.at(0);   // paged: waits for the table load only
   QjKey kp[2];
   ValCodes vp[2];
   qj_load_key(kp[0], pages, g, lane, a, r);
@@ -631,8 +664,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   init_state(st);
   const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
   page_loop(
-      np, kp, vp, [&](QjKey& k, int p) { qj_load_key(k, pages + (int64_t)p * A.page_stride, g, lane, a, r); },
-      [&](ValCodes& v, int p) { load_vcodes(v, pages + (int64_t)p * A.page_stride, g.off_v, a, r); },
+      np, kp, vp, [&](QjKey& k, int p) { qj_load_key(k, pset.at(p), g, lane, a, r); },
+      [&](ValCodes& v, int p) { load_vcodes(v, pset.at(p), g.off_v, a, r); },
       [&](const QjKey& k, const ValCodes& v, int s, auto mid) {
         uint8_t* slot = S.u.qj.meta[s];
         commit_meta(k.m, slot, lane);
@@ -652,11 +685,16 @@ static void launch1(K kernel, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kernel, dim3(n_parts * a.n_kv_heads * a.batch), dim3(64), 0, s, a);
 }
 
+template <int G, int NKS, bool PAGED>
+static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
+  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0, PAGED>, a, s);
+  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1, PAGED>, a, s);
+  else launch1(decode_mix_fast<G, NKS, 8, PAGED>, a, s);
+}
 template <int G, int NKS>
 static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
-  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0>, a, s);
-  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1>, a, s);
-  else launch1(decode_mix_fast<G, NKS, 8>, a, s);
+  if (a.table) launch_mix_nb<G, NKS, true>(a, nb, s);
+  else launch_mix_nb<G, NKS, false>(a, nb, s);
 }
 
 // Launches the pipelined kernel when one covers the configuration (with the
@@ -664,6 +702,7 @@ static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
 bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (g != 4 && g != 8) return false;
+  if (a.table && a.pps > 64) return false;   // the split's page indices live in one register
   if (key_mode == KVQ_KEY_MIXKVQ) {
     const MixGeo geo = mix_geo(a.n16, a.n4);
     const int nks = (geo.F + 3) / 4;
@@ -683,13 +722,23 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   }
   if (key_mode == KVQ_KEY_PNMIX) {
     if (a.n_hi != 64) return false;
-    if (g == 4) launch1(decode_pn_fast<4>, a, s);
-    else launch1(decode_pn_fast<8>, a, s);
+    if (a.table) {
+      if (g == 4) launch1(decode_pn_fast<4, true>, a, s);
+      else launch1(decode_pn_fast<8, true>, a, s);
+    } else {
+      if (g == 4) launch1(decode_pn_fast<4, false>, a, s);
+      else launch1(decode_pn_fast<8, false>, a, s);
+    }
     return true;
   }
   if (a.qjl_m != 256) return false;
-  if (g == 4) launch1(decode_qjl_fast<4>, a, s);
-  else launch1(decode_qjl_fast<8>, a, s);
+  if (a.table) {
+    if (g == 4) launch1(decode_qjl_fast<4, true>, a, s);
+    else launch1(decode_qjl_fast<8, true>, a, s);
+  } else {
+    if (g == 4) launch1(decode_qjl_fast<4, false>, a, s);
+    else launch1(decode_qjl_fast<8, false>, a, s);
+  }
   return true;
 }
 

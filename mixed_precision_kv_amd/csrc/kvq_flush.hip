@@ -664,7 +664,12 @@ __device__ inline void part_coords(const FlushArgs& A, int parts, int lin, int& 
   head = unit / A.n_pages;
   const int p = unit - (int)head * A.n_pages;
   row0 = head * A.src_stride + (int64_t)p * PAGE;
-  page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
+  if (A.table == nullptr) {
+    page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
+  } else {   // an entry outside the pool: the page is not written (KVQ_FLAG_TABLE)
+    const int v = A.table[head * A.table_stride + A.first_page + p];
+    page = (v >= 0 && v < A.pool_pages) ? A.arena + (int64_t)v * A.page_stride : nullptr;
+  }
 }
 
 // One flush block (256 threads): value k-step `part` (< V_PARTS) or a Key
@@ -675,6 +680,10 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
   int64_t head, row0;
   uint8_t* page;
   part_coords(A, parts, lin, part, head, row0, page);
+  if (page == nullptr) {   // uniform over the block: no barrier is reached
+    if (threadIdx.x == 0 && part == 0) atomicOr(A.flags, KVQ_FLAG_TABLE);
+    return;
+  }
   if constexpr (MODE == KVQ_KEY_MIXKVQ) {
     __shared__ union {
       VPartSmem v;

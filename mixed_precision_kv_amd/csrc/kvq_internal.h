@@ -171,6 +171,9 @@ struct FlushArgs {
   const uint16_t* qjl_s;
   uint8_t* arena;
   int64_t page_stride;
+  const int32_t* table;           // pool index of logical page p of head h: table[h * table_stride + p]; null: contiguous
+  int table_stride;
+  int pool_pages;                 // pages in the arena: batch * n_kv_heads * max_pages
   int max_pages;
   int first_page;
   int n_pages;                    // pages written per (batch, kv head)
@@ -195,6 +198,9 @@ struct DecodeArgs {
   const uint16_t* q;
   const uint8_t* arena;
   int64_t page_stride;
+  const int32_t* table;           // as FlushArgs::table
+  int table_stride;
+  int pool_pages;
   int max_pages, n_pages, pps, n_page_splits;
   int n_seg_splits;               // BF16-segment workgroups per (batch, kv head), SEG_TOKENS tokens each
   const uint8_t* mask;

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(kvq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert kvq.kvq_abi_version() == 1
+    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 2
     assert kvq.kvq_status_string(0) == "ok"
 
 
@@ -82,7 +82,7 @@ def test_validation_rejects_before_launch(lib):
         kvq.kvq_page_bytes(bad)
     assert e.value.status == kvq.KVQ_UNSUPPORTED
     for field, value, status in (("n_q_heads", 6, kvq.KVQ_UNSUPPORTED), ("n_kv_heads", 3, kvq.KVQ_INVALID_ARG),
-                                 ("abi_version", 2, kvq.KVQ_INVALID_ARG),
+                                 ("abi_version", 3, kvq.KVQ_INVALID_ARG),
                                  ("n_bf16", 120, kvq.KVQ_INVALID_ARG), ("key_mode", 7, kvq.KVQ_INVALID_ARG)):
         c = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=16, n_u4=32)
         setattr(c, field, value)
@@ -92,30 +92,42 @@ def test_validation_rejects_before_launch(lib):
     S = lib
     st = S.kvq_select_channels(ctypes.byref(cfg), None, 10, 10, None, 10, 10, None, None)
     assert st == kvq.KVQ_INVALID_ARG
-    st = S.kvq_flush_quantize(ctypes.byref(cfg), 16, 16, 128, 1, 16, None, 16, 8, 16, None)
+    st = S.kvq_flush_quantize(ctypes.byref(cfg), 16, 16, 128, 1, 16, None, 16, None, 0, 8, 16, None)
     assert st == kvq.KVQ_CAPACITY
-    st = S.kvq_flush_quantize(ctypes.byref(cfg), 8, 16, 128, 1, 16, None, 16, 0, 16, None)
+    st = S.kvq_flush_quantize(ctypes.byref(cfg), 8, 16, 128, 1, 16, None, 16, None, 0, 0, 16, None)
     assert st == kvq.KVQ_INVALID_ARG                               # misaligned source
-    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, 16, 16, 129, 129,
+    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, None, 0, 2, 16, None, None, None, 0, 16, 16, 129, 129,
                                 0.088, 16, 16, 1 << 20, None)
     assert st == kvq.KVQ_INVALID_ARG                               # residual longer than 128
-    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, None, 0, 2, 16, None, None, None, 0, None, None, 0, 0,
                                 0.088, 16, 16, 16, None)
     assert st == kvq.KVQ_WORKSPACE_TOO_SMALL
     # the fused call fails as a whole when either half's check fails
     big = 1 << 30
-    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, None, 0, 2, 16, None, None, None, 0, None, None, 0, 0,
                                       0.088, 16, 16, big, 16, 16, 128, 1, 8, 16, None)
     assert st == kvq.KVQ_CAPACITY                                  # flush past max_pages
-    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, None, 0, 2, 16, None, None, None, 0, None, None, 0, 0,
                                       0.088, 16, 16, big, 16, 16, 128, 1, 2, None, None)
     assert st == kvq.KVQ_INVALID_ARG                               # no status word
-    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, 16, 16, 129, 129,
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, None, 0, 2, 16, None, None, None, 0, 16, 16, 129, 129,
                                       0.088, 16, 16, big, 16, 16, 128, 1, 2, 16, None)
     assert st == kvq.KVQ_INVALID_ARG                               # decode half: residual longer than 128
-    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, 2, 16, None, None, None, 0, None, None, 0, 0,
+    st = S.kvq_decode_attention_flush(ctypes.byref(cfg), 16, 16, None, 0, 2, 16, None, None, None, 0, None, None, 0, 0,
                                       0.088, 16, 16, 16, 16, 16, 128, 1, 2, 16, None)
     assert st == kvq.KVQ_WORKSPACE_TOO_SMALL
+    # page tables: the logical range is checked against table_stride, the
+    # table's alignment and stride are checked
+    st = S.kvq_flush_quantize(ctypes.byref(cfg), 16, 16, 128, 1, 16, None, 16, 16, 4, 4, 16, None)
+    assert st == kvq.KVQ_CAPACITY                                  # first_page + n_pages > table_stride
+    st = S.kvq_flush_quantize(ctypes.byref(cfg), 16, 16, 128, 1, 16, None, 16, 18, 8, 0, 16, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # misaligned table
+    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 16, 4, 5, 16, None, None, None, 0, None, None, 0, 0,
+                                0.088, 16, 16, big, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # n_pages > table_stride
+    st = S.kvq_decode_attention(ctypes.byref(cfg), 16, 16, 16, 0, 1, 16, None, None, None, 0, None, None, 0, 0,
+                                0.088, 16, 16, big, None)
+    assert st == kvq.KVQ_INVALID_ARG                               # table_stride 0
     qcfg = kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 8, qjl_m=256)
     st = S.kvq_select_channels(ctypes.byref(qcfg), 16, 10, 10, 16, 10, 10, 16, None)
     assert st == kvq.KVQ_UNSUPPORTED
