@@ -111,17 +111,19 @@ def kl_divergence(p_ref: np.ndarray, p_q: np.ndarray) -> float:
 
 def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0, perm=None,
                       mask_rec=None, pair_layout="half", s_bits=None,
-                      sink_k=None, sink_v=None, resid_k=None, resid_v=None):
+                      sink_k=None, sink_v=None, resid_k=None, resid_v=None, page_perms=None):
     """Decode for one (batch, KV head) from packed pages.
 
     q_bits_heads [g, D] bf16 bits; arena_pages: list of page byte arrays;
-    sink_*/resid_* [n, D] bf16 bits (or None). Returns (out [g, D], probs)."""
+    sink_*/resid_* [n, D] bf16 bits (or None); page_perms: MixKVQ channel
+    order of each page (per-flush reselection), else `perm` for every page.
+    Returns (out [g, D], probs)."""
     q = bf16_to_f64(q_bits_heads)
     Ks, Vs, bits_l, norms_l = [], [], [], []
     hi = hi_channels_from_record(mask_rec, pair_layout) if key_mode == 1 else None
-    for page in arena_pages:
+    for i, page in enumerate(arena_pages):
         if key_mode == 0:
-            K, V = dequant_mixkvq_page(page, n16, n4, perm)
+            K, V = dequant_mixkvq_page(page, n16, n4, perm if page_perms is None else page_perms[i])
         elif key_mode == 1:
             K, V = dequant_pnmix_page(page, hi)
         else:

@@ -72,23 +72,48 @@ def _rank_desc(keys) -> np.ndarray:
     return rank
 
 
+def query_sums(q_bits: np.ndarray) -> list:
+    """SQ_d = sum of psi(|q_d|) over every query row given (all heads of a
+    GQA group, any number of tokens), as exact Python ints. Sums of several
+    calls add: this is the running query-magnitude accumulator of the MixKVQ
+    system section (one decode query added per step)."""
+    q = np.abs(bf16_to_f64(q_bits)).reshape(-1, D)
+    sq = psi_sum(q, axis=0)
+    return [int(sq[d]) for d in range(D)]
+
+
+def mixkvq_keys_from_sums(sq, k_bits: np.ndarray):
+    """Exact rank keys SQ_d * range_d (Fractions, units of 2^-64) from given
+    query sums and the Key tokens [L_k, D] (bf16 bits) to be quantized."""
+    k = bf16_to_f64(k_bits)
+    rng = [Fraction(float(k[:, d].max())) - Fraction(float(k[:, d].min())) for d in range(D)]
+    return [Fraction(int(sq[d])) * rng[d] for d in range(D)]
+
+
 def mixkvq_keys(q_bits: np.ndarray, k_bits: np.ndarray):
     """Exact rank keys for one KV head.
 
     q_bits: [g, L_q, D] bf16 bits of the group's prefill queries.
     k_bits: [L_k, D] bf16 bits of the Key tokens to be quantized.
     Returns list of Fractions SQ_d * range_d (units of 2^-64)."""
-    q = np.abs(bf16_to_f64(q_bits)).reshape(-1, D)
-    sq = psi_sum(q, axis=0)
-    k = bf16_to_f64(k_bits)
-    rng = [Fraction(float(k[:, d].max())) - Fraction(float(k[:, d].min())) for d in range(D)]
-    return [Fraction(int(sq[d])) * rng[d] for d in range(D)]
+    return mixkvq_keys_from_sums(query_sums(q_bits), k_bits)
+
+
+def mixkvq_select_sums(sq, k_bits, n16: int, n4: int):
+    """Per-flush reselection (MixKVQ: I_d and S_d refreshed every R tokens;
+    the running accumulator of query magnitudes): the tiers of one page from
+    the accumulated query sums and the page's own Key tokens. Returns as
+    mixkvq_select."""
+    return _select_from_keys(mixkvq_keys_from_sums(sq, k_bits), n16, n4)
 
 
 def mixkvq_select(q_bits, k_bits, n16: int, n4: int):
     """Tier of every channel and the channel order (BF16, UINT4, UINT2 tiers,
     each ascending by channel index) for one KV head."""
-    keys = mixkvq_keys(q_bits, k_bits)
+    return _select_from_keys(mixkvq_keys(q_bits, k_bits), n16, n4)
+
+
+def _select_from_keys(keys, n16: int, n4: int):
     rank = _rank_desc(keys)
     tier = np.where(rank < n16, TIER_BF16, np.where(rank < n16 + n4, TIER_U4, TIER_U2))
     perm = np.concatenate([np.nonzero(tier == t)[0] for t in (TIER_BF16, TIER_U4, TIER_U2)])

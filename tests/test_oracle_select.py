@@ -11,6 +11,11 @@
 * PN-Mix Eq.6: ranking agrees with float64 means of pair norms when there is
   no near tie, is invariant to token order, and a zero-Key pair ranks last;
   the adjacent and half-split layouts pair the right channels.
+* Per-flush reselection (MixKVQ's running query-magnitude accumulator, tiers
+  refreshed at every flush): query sums accumulate exactly (chunked sums of
+  integers on the 2^-64 grid equal the one-shot sum; 1.0 counts 2^64); with
+  equal query sums the page's Key ranges alone order the channels, with
+  equal ranges the sums alone; a page's tiers follow its own Keys.
 """
 from fractions import Fraction
 
@@ -112,3 +117,58 @@ def test_pnmix_ranking_float_means_and_invariance():
     keys = select.pnmix_keys(qb, kb, "half")
     assert keys[5] == 0 and min(keys) == 0
     assert select.pair_channels("half")[1][5] == 69 and select.pair_channels("adjacent")[1][5] == 11
+
+
+def _bf16(x):
+    return synth.bf16_bits(__import__("torch").tensor(np.asarray(x, np.float32)).to(__import__("torch").bfloat16))
+
+
+def test_query_sums_accumulate_exactly():
+    rng = np.random.default_rng(5)
+    q = _bf16(rng.standard_normal((3, 40, 128)) * 4.0)
+    whole = select.query_sums(q)
+    parts = [select.query_sums(q[:, :13]), select.query_sums(q[:, 13:29]), select.query_sums(q[:, 29:])]
+    assert whole == [a + b + c for a, b, c in zip(*parts)]
+    ones = _bf16(np.ones((2, 3, 128)))
+    assert select.query_sums(ones) == [6 * 2 ** 64] * 128     # psi(1.0) = 2^64, six rows
+    half = _bf16(np.full((1, 1, 128), -0.5))
+    assert select.query_sums(half) == [2 ** 63] * 128          # magnitudes: |-0.5| = 2^-1
+
+
+def test_reselect_orders_by_range_with_equal_sums():
+    n16, n4 = 3, 10
+    sq = [2 ** 64] * 128
+    k = np.zeros((128, 128), np.float32)
+    k[1, :] = np.arange(128) + 1.0                               # range of channel d = d + 1
+    tier, perm, rank = select.mixkvq_select_sums(sq, _bf16(k), n16, n4)
+    assert list(rank) == [127 - d for d in range(128)]
+    assert list(perm[:n16]) == [125, 126, 127]                   # largest ranges, ascending order
+    assert list(perm[n16:n16 + n4]) == list(range(115, 125))
+    assert list(perm[n16 + n4:]) == list(range(115))
+    assert all(tier[d] == (2 if d >= 125 else 1 if d >= 115 else 0) for d in range(128))
+
+
+def test_reselect_orders_by_sums_with_equal_ranges():
+    n16, n4 = 2, 4
+    sq = [(d % 7 + 1) * 2 ** 60 for d in range(128)]               # ties within each residue class
+    k = np.zeros((128, 128), np.float32)
+    k[5, :] = 2.0                                                 # every range 2
+    tier, perm, rank = select.mixkvq_select_sums(sq, _bf16(k), n16, n4)
+    top = [d for d in range(128) if d % 7 == 6]                   # the largest sum, lower index first
+    assert list(perm[:n16]) == top[:n16]
+    assert sorted(perm[n16:n16 + n4]) == list(perm[n16:n16 + n4]) and set(perm[n16:n16 + n4]) == set(top[n16:n16 + n4])
+
+
+def test_reselect_follows_each_pages_keys():
+    w, qb, kb, oc = tiny_inputs()
+    sq = select.query_sums(qb)
+    # the prefill selection is the reselection over all the prefill Keys
+    t_all, p_all, _ = select.mixkvq_select(qb, kb, w.n_bf16, w.n_u4)
+    t_s, p_s, _ = select.mixkvq_select_sums(sq, kb, w.n_bf16, w.n_u4)
+    assert np.array_equal(p_all, p_s) and np.array_equal(t_all, t_s)
+    # a page whose outlier channels were flattened loses them from the BF16 tier
+    page = bf16_to_f64(kb[:128]).astype(np.float32)
+    page[:, oc[4:]] = 0.0
+    t_p, _, _ = select.mixkvq_select_sums(sq, _bf16(page), w.n_bf16, w.n_u4)
+    assert all(t_p[d] == 0 for d in oc[4:])
+    assert all(t_all[d] == 2 for d in oc[4:])
