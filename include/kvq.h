@@ -94,7 +94,10 @@ typedef struct kvq_config {
   int32_t pair_layout;        /* PN-Mix: kvq_pair_layout */
   int32_t n_hi_pairs;         /* PN-Mix: high-precision pairs, floor(r*D/2) (32 at r=0.5) */
   int32_t qjl_m;              /* QJL: sketch rows m, a multiple of 64, at most 512 */
-  int32_t reserved[4];        /* must be zero */
+  int32_t page_records;       /* MixKVQ: 0, one selection record per (batch, kv head) (selection at
+                                 prefill); 1, one record per page, written by kvq_flush_reselect
+                                 (tiers re-selected at every flush) and read per page by the decode */
+  int32_t reserved[3];        /* must be zero */
 } kvq_config;
 
 /* Persistent cache bytes of one layer for all (batch, kv head) pairs, by
@@ -182,11 +185,45 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
  * status_flags: device uint32 (not NULL) the kernels OR KVQ_FLAG_* bits into.
  * Returns KVQ_CAPACITY if first_page + n_pages exceeds max_pages (no table)
  * or table_stride (with a table). */
+/* (With cfg->page_records set, kvq_flush_quantize and kvq_decode_attention_flush
+ * return KVQ_UNSUPPORTED: the records then come from kvq_flush_reselect.) */
 kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src,
                               int64_t src_stride, int32_t n_pages, const void* mask,
                               const void* qjl_s, void* page_arena, const int32_t* page_table,
                               int32_t table_stride, int32_t first_page,
                               uint32_t* status_flags, void* stream);
+
+/* MixKVQ's running accumulator of query magnitudes (system section: at each
+ * decode step the current query's magnitude is added; I_d is refreshed from
+ * it every R tokens). Adds, for every (batch, kv head) and channel d, the
+ * exact sum of psi(|q|) (|q| rounded half-even to the grid 2^-64) over the
+ * l_q query rows of every query head of the group, as an unsigned 128-bit
+ * integer. Sums of several calls are the sum of one call over all the rows.
+ * Call it on the prefill queries (as kvq_select_channels reads them) and on
+ * every decode query (l_q = 1, q_stride = 1) to accumulate the whole history;
+ * zero the accumulator after each flush for the window-only reading.
+ * q: device bf16, element (b, h, t, d) at q[((b*Hq + h)*q_stride + t)*128 + d].
+ * q_accum: device, 16-byte aligned, [batch][n_kv_heads][128] uint128
+ *   (little-endian), read and written.
+ * MixKVQ only (else KVQ_UNSUPPORTED). */
+kvq_status kvq_accumulate_query(const kvq_config* cfg, const void* q, int64_t l_q, int64_t q_stride,
+                                void* q_accum, void* stream);
+
+/* kvq_flush_quantize with the MixKVQ tiers re-selected for every flushed page
+ * (MixKVQ: I_d and S_d are updated every R tokens, channel selection and group
+ * quantization run when the residual fills): channels are ranked by
+ * SQ_d * range_d, SQ_d from q_accum and range_d = max - min of the page's own
+ * 128 Keys, exactly as kvq_select_channels ranks (ties to the lower channel),
+ * and the page is packed with that order. The page's 160-byte record goes to
+ * page_records + ((b*Hkv + h)*rec_stride + p)*160 for logical page p, with
+ * rec_stride = table_stride with a page table, else max_pages.
+ * Requires cfg->page_records == 1 (MixKVQ only); other arguments as
+ * kvq_flush_quantize. Keys must be finite for the ranking. */
+kvq_status kvq_flush_reselect(const kvq_config* cfg, const void* k_src, const void* v_src,
+                              int64_t src_stride, int32_t n_pages, const void* q_accum,
+                              void* page_records, void* page_arena, const int32_t* page_table,
+                              int32_t table_stride, int32_t first_page, uint32_t* status_flags,
+                              void* stream);
 
 /* Single-token decode attention over [sinks | pages 0..n_pages-1 | residual]
  * with one global softmax (KIVI blog section 6; MixKVQ Algorithm 1
@@ -200,7 +237,8 @@ kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const vo
  *   table_stride with one). A table entry outside the pool is clamped into
  *   it (that page's contribution is then unspecified).
  * mask: the records of kvq_select_channels, 16-byte aligned (ignored for QJL
- *   and when n_pages is 0).
+ *   and when n_pages is 0); with cfg->page_records, the per-page records of
+ *   kvq_flush_reselect (same indexing as there), read page by page.
  * sink_k/sink_v: device bf16 [batch][n_kv_heads][n_sink][128] (n_sink <= 128; may be NULL if 0).
  * resid_k/resid_v: device bf16 [batch][n_kv_heads][resid_stride][128], first
  *   n_resid tokens visible (0 <= n_resid <= 128; may be NULL if 0).

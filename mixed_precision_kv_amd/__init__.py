@@ -25,6 +25,7 @@ EXPORTED = (
     "kvq_abi_version", "kvq_status_string", "kvq_page_bytes", "kvq_mask_bytes",
     "kvq_workspace_bytes", "kvq_storage_bytes", "kvq_select_channels",
     "kvq_flush_quantize", "kvq_decode_attention", "kvq_decode_attention_flush",
+    "kvq_accumulate_query", "kvq_flush_reselect",
 )
 
 
@@ -34,7 +35,7 @@ class KvqConfig(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("max_pages", ctypes.c_int32), ("n_bf16", ctypes.c_int32), ("n_u4", ctypes.c_int32),
         ("pair_layout", ctypes.c_int32), ("n_hi_pairs", ctypes.c_int32), ("qjl_m", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("page_records", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
                                        P, P, SZ, P]),
         "kvq_decode_attention_flush": (I32, [cfgp, P, P, P, I32, I32, P, P, P, P, I32, P, P, I32, I32,
                                              ctypes.c_float, P, P, SZ, P, P, I64, I32, I32, P, P]),
+        "kvq_accumulate_query": (I32, [cfgp, P, I64, I64, P, P]),
+        "kvq_flush_reselect": (I32, [cfgp, P, P, I64, I32, P, P, P, P, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -87,7 +90,7 @@ def load(path: str = LIB_PATH):
 
 def make_config(key_mode: int, batch: int, n_q_heads: int, n_kv_heads: int, max_pages: int, *,
                 n_bf16: int = 0, n_u4: int = 0, pair_layout: int = KVQ_PAIR_HALF_SPLIT,
-                n_hi_pairs: int = 32, qjl_m: int = 256, head_dim: int = 128) -> KvqConfig:
+                n_hi_pairs: int = 32, qjl_m: int = 256, head_dim: int = 128, page_records: int = 0) -> KvqConfig:
     c = KvqConfig()
     c.abi_version = KVQ_ABI_VERSION
     c.key_mode = key_mode
@@ -95,6 +98,7 @@ def make_config(key_mode: int, batch: int, n_q_heads: int, n_kv_heads: int, max_
     c.max_pages = max_pages
     c.n_bf16, c.n_u4 = n_bf16, n_u4
     c.pair_layout, c.n_hi_pairs, c.qjl_m = pair_layout, n_hi_pairs, qjl_m
+    c.page_records = page_records
     return c
 
 
@@ -169,6 +173,18 @@ def kvq_flush_quantize(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page
                        status_flags, *, page_table=None, table_stride=0, stream=None):
     _check("kvq_flush_quantize", load().kvq_flush_quantize(
         ctypes.byref(cfg), _ptr(k_src), _ptr(v_src), src_stride, n_pages, _ptr(mask), _ptr(qjl_s),
+        _ptr(page_arena), _ptr(page_table), table_stride, first_page, _ptr(status_flags), _stream(stream)))
+
+
+def kvq_accumulate_query(cfg, q, l_q, q_stride, q_accum, *, stream=None):
+    _check("kvq_accumulate_query", load().kvq_accumulate_query(
+        ctypes.byref(cfg), _ptr(q), l_q, q_stride, _ptr(q_accum), _stream(stream)))
+
+
+def kvq_flush_reselect(cfg, k_src, v_src, src_stride, n_pages, q_accum, page_records, page_arena, first_page,
+                       status_flags, *, page_table=None, table_stride=0, stream=None):
+    _check("kvq_flush_reselect", load().kvq_flush_reselect(
+        ctypes.byref(cfg), _ptr(k_src), _ptr(v_src), src_stride, n_pages, _ptr(q_accum), _ptr(page_records),
         _ptr(page_arena), _ptr(page_table), table_stride, first_page, _ptr(status_flags), _stream(stream)))
 
 

@@ -13,8 +13,10 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static kvq_status check_config(const kvq_config* c) {
   if (!c) return KVQ_INVALID_ARG;
   if (c->abi_version != KVQ_ABI_VERSION) return KVQ_INVALID_ARG;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
     if (c->reserved[i] != 0) return KVQ_INVALID_ARG;
+  if (c->page_records != 0 && c->page_records != 1) return KVQ_INVALID_ARG;
+  if (c->page_records && c->key_mode != KVQ_KEY_MIXKVQ) return KVQ_UNSUPPORTED;
   if (c->head_dim != D) return c->head_dim > 0 ? KVQ_UNSUPPORTED : KVQ_INVALID_ARG;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_pages < 1) return KVQ_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads * c->max_pages > INT32_MAX) return KVQ_INVALID_ARG;   // pool indices are int32
@@ -107,6 +109,9 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   a.pair_layout = cfg->pair_layout;
   a.qjl_m = cfg->qjl_m;
   a.flags = status_flags;
+  a.q_accum = nullptr;
+  a.rec_out = nullptr;
+  a.rec_stride = 0;
   return KVQ_OK;
 }
 
@@ -142,6 +147,7 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.max_pages = cfg->max_pages;
   a.n_pages = n_pages;
   a.n_seg_splits = seg_splits(n_sink + n_resid);
+  a.rec_stride = cfg->page_records ? (page_table ? table_stride : cfg->max_pages) : 0;
   a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
   a.n_page_splits = n_page_splits(cfg, n_pages);
   a.mask = (const uint8_t*)mask;
@@ -280,6 +286,23 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
   return launch_select(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 
+kvq_status kvq_accumulate_query(const kvq_config* cfg, const void* q, int64_t l_q, int64_t q_stride, void* q_accum,
+                                void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (cfg->key_mode != KVQ_KEY_MIXKVQ) return KVQ_UNSUPPORTED;
+  if (!q || !q_accum || !aligned16(q) || !aligned16(q_accum)) return KVQ_INVALID_ARG;
+  if (l_q < 1 || q_stride < l_q) return KVQ_INVALID_ARG;
+  SelectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = (const uint16_t*)q;
+  a.l_q = l_q;
+  a.q_stride = q_stride;
+  a.n_q_heads = cfg->n_q_heads;
+  a.n_kv_heads = cfg->n_kv_heads;
+  return launch_accumulate(a, q_accum, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
+}
+
 kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
                               int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
                               const int32_t* page_table, int32_t table_stride, int32_t first_page,
@@ -288,6 +311,25 @@ kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const vo
   const kvq_status st = flush_prepare(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, page_table,
                                       table_stride, first_page, status_flags, a);
   if (st != KVQ_OK || n_pages == 0) return st;
+  if (cfg->page_records) return KVQ_UNSUPPORTED;   // per-page records come from kvq_flush_reselect
+  return launch_flush(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_flush_reselect(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
+                              int32_t n_pages, const void* q_accum, void* page_records, void* page_arena,
+                              const int32_t* page_table, int32_t table_stride, int32_t first_page,
+                              uint32_t* status_flags, void* stream) {
+  if (cfg && cfg->key_mode == KVQ_KEY_MIXKVQ && !cfg->page_records) return KVQ_INVALID_ARG;
+  FlushArgs a;
+  const kvq_status st = flush_prepare(cfg, k_src, v_src, src_stride, n_pages, page_records, nullptr, page_arena,
+                                      page_table, table_stride, first_page, status_flags, a);
+  if (st != KVQ_OK) return st;
+  if (cfg->key_mode != KVQ_KEY_MIXKVQ) return KVQ_UNSUPPORTED;
+  if (!q_accum || !aligned16(q_accum) || !aligned16(page_records)) return KVQ_INVALID_ARG;
+  if (n_pages == 0) return KVQ_OK;
+  a.q_accum = q_accum;
+  a.rec_out = (uint8_t*)page_records;
+  a.rec_stride = page_table ? table_stride : cfg->max_pages;
   return launch_flush(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 
@@ -324,6 +366,7 @@ kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void
   st = flush_prepare(cfg, flush_k_src, flush_v_src, flush_src_stride, n_flush_pages, mask, qjl_s, page_arena,
                      page_table, table_stride, flush_first_page, status_flags, f);
   if (st != KVQ_OK) return st;
+  if (cfg->page_records) return KVQ_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
   if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false) != hipSuccess) return KVQ_HIP_ERROR;
   return launch_merge_flush(cfg->key_mode, d, f, cfg->batch, s) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;

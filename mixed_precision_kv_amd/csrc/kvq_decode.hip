@@ -78,32 +78,38 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   if constexpr (MODE == KVQ_KEY_MIXKVQ) {
     const MixGeo g = mix_geo(A.n16, A.n4);
     const int NKS = (g.F + 3) / 4;
-    const uint8_t* rec = A.mask + head * MIX_RECORD;
-    for (int s = lane; s < 32 * NKS; s += 64) {
-      int ch = -1;
-      if (s < 2 * g.n4) ch = rec[g.n16 + (s >> 1)];
-      else if (s >= g.s4 && s < g.s4 + g.n2) ch = rec[g.n16 + g.n4 + (s - g.s4)];
-      S.slot_ch[s] = ch;
-    }
-    __syncthreads();
-    for (int idx = lane; idx < NKS * 4 * G * 8; idx += 64) {
-      const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
-      const int ch = S.slot_ch[8 * (4 * ks + aa) + e];
-      S.u.qslot[ks][aa][hh][e] = ch >= 0 ? S.qf[hh][ch] : 0.f;
-    }
     const int NKB = (g.n16 + 31) / 32;
     bf16x8 Bq[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 32 * kb + 8 * a + e;
-        Bq[kb][e] = (__bf16)(c < g.n16 ? S.qf[h][rec[c]] * B_SCALE : 0.f);
+    // slot -> channel and the query tables of a record: once per split, or
+    // at every page when every page has its own record (per-flush reselection)
+    auto tables = [&](const uint8_t* rec) {
+      __syncthreads();
+      for (int s = lane; s < 32 * NKS; s += 64) {
+        int ch = -1;
+        if (s < 2 * g.n4) ch = rec[g.n16 + (s >> 1)];
+        else if (s >= g.s4 && s < g.s4 + g.n2) ch = rec[g.n16 + g.n4 + (s - g.s4)];
+        S.slot_ch[s] = ch;
       }
-    __syncthreads();
+      __syncthreads();
+      for (int idx = lane; idx < NKS * 4 * G * 8; idx += 64) {
+        const int e = idx & 7, hh = (idx >> 3) % G, aa = (idx >> 3) / G % 4, ks = (idx >> 3) / G / 4;
+        const int ch = S.slot_ch[8 * (4 * ks + aa) + e];
+        S.u.qslot[ks][aa][hh][e] = ch >= 0 ? S.qf[hh][ch] : 0.f;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * kb + 8 * a + e;
+          Bq[kb][e] = (__bf16)(c < g.n16 ? S.qf[h][rec[c]] * B_SCALE : 0.f);
+        }
+      __syncthreads();
+    };
+    if (A.rec_stride == 0) tables(A.mask + head * MIX_RECORD);
     const float xs = A.scale_log2 * B_UNSCALE;
 
     for (int pg = p0; pg < p1; ++pg) {
+      if (A.rec_stride) tables(A.mask + (head * A.rec_stride + pg) * MIX_RECORD);
       const uint8_t* page = page_ptr(A, head, pg);
       u32x4 vc[4];
 #pragma unroll

@@ -703,6 +703,7 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (g != 4 && g != 8) return false;
   if (a.table && a.pps > 64) return false;   // the split's page indices live in one register
+  if (a.rec_stride) return false;             // per-page records: the generic kernel rebuilds its tables per page
   if (key_mode == KVQ_KEY_MIXKVQ) {
     const MixGeo geo = mix_geo(a.n16, a.n4);
     const int nks = (geo.F + 3) / 4;

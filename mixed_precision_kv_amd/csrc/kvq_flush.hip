@@ -20,6 +20,7 @@
 // beyond the binary16 range are stored as infinity with KVQ_FLAG_RANGE.
 #include "kvq_internal.h"
 #include "kvq_merge.h"
+#include "kvq_rank.h"
 
 namespace kvq {
 
@@ -333,6 +334,8 @@ __device__ inline void stage_rows_padded(uint16_t* lds, const uint16_t* src, int
 
 struct KPartSmem {
   uint16_t tile[PAGE * KS];     // the page's Keys, row stride KS
+  double key_hi[D], key_lo[D];  // per-flush reselection: the channels' rank keys
+  uint8_t tier[D];
   GroupParam kp[D];             // Key group parameters (by slot or channel position)
   uint8_t ch[D];                // channel order (MixKVQ) / slot -> channel (PN-Mix)
   int kinfo[32];                // MixKVQ slot of the part: channel | shift << 8 | mask << 10 | param << 12 | u4 << 20
@@ -357,13 +360,54 @@ __device__ inline int mix_slot_pos(const MixGeo& g, int slot, int& levels, bool&
 
 // Key part fg: fragments 4 fg .. 4 fg + 3 (codes and scales / offsets); part
 // 0 also writes the BF16-tier rows.
-__device__ __attribute__((always_inline)) inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int fg,
-                                          KPartSmem& S) {
-  const MixGeo g = mix_geo(A.n16, A.n4);
-  const uint8_t chv = A.mask[head * MIX_RECORD + (threadIdx.x & (D - 1))];   // in flight with the staging
-  stage_rows_padded(S.tile, A.k_src, row0);
-  if (threadIdx.x < D) S.ch[threadIdx.x] = chv;
+// Per-flush reselection of one page (MixKVQ: I_d from the running
+// accumulator of query magnitudes, S_d from the page's own Keys; tiers
+// refreshed at each flush): rank keys SQ_d * range_d exactly as the prefill
+// selection, tiers by rank, the channel order into S.ch; `write` also stores
+// the page's record (order, then 2-bit tiers). Keys must be finite.
+__device__ inline void reselect_page(const FlushArgs& A, int64_t head, int lpage, bool write, KPartSmem& S) {
+  const int d = threadIdx.x >> 1, half = threadIdx.x & 1;   // two threads per channel, 64 tokens each
+  float mn = INFINITY, mx = -INFINITY;
+  for (int t = 64 * half; t < 64 * half + 64; ++t) {
+    const float v = bf16_to_f32(S.tile[t * KS + d]);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  mn = fminf(mn, __int_as_float(dpp_partner<1>(__float_as_int(mn))));
+  mx = fmaxf(mx, __int_as_float(dpp_partner<1>(__float_as_int(mx))));
+  if (half == 0) {
+    const u128 sq = reinterpret_cast<const u128*>(A.q_accum)[head * D + d];
+    dd_key(sq, (double)mx - (double)mn, S.key_hi[d], S.key_lo[d]);
+  }
   __syncthreads();
+  if (threadIdx.x < D) {
+    const int r = key_rank(S.key_hi, S.key_lo, threadIdx.x);
+    S.tier[threadIdx.x] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
+  }
+  __syncthreads();
+  uint8_t* rec = A.rec_out + (head * A.rec_stride + lpage) * MIX_RECORD;
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x, t = S.tier[c];
+    int pos = t == 2 ? 0 : (t == 1 ? A.n16 : A.n16 + A.n4);
+    for (int o = 0; o < c; ++o) pos += S.tier[o] == t;
+    S.ch[pos] = (uint8_t)c;
+    if (write) rec[pos] = (uint8_t)c;
+  } else if (write && threadIdx.x < D + 32) {
+    const int q = threadIdx.x - D;
+    rec[D + q] = (uint8_t)(S.tier[4 * q] | (S.tier[4 * q + 1] << 2) | (S.tier[4 * q + 2] << 4) | (S.tier[4 * q + 3] << 6));
+  }
+  __syncthreads();
+}
+
+__device__ __attribute__((always_inline)) inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int fg,
+                                          int lpage, KPartSmem& S) {
+  const MixGeo g = mix_geo(A.n16, A.n4);
+  const bool resel = A.q_accum != nullptr;
+  const uint8_t chv = resel ? (uint8_t)0 : A.mask[head * MIX_RECORD + (threadIdx.x & (D - 1))];   // in flight with the staging
+  stage_rows_padded(S.tile, A.k_src, row0);
+  if (!resel && threadIdx.x < D) S.ch[threadIdx.x] = chv;
+  __syncthreads();
+  if (resel) reselect_page(A, head, lpage, fg == 0, S);
   {  // parameters of the group's 32 slots, eight threads per slot (16 tokens each)
     const int ls = threadIdx.x >> 3, part = threadIdx.x & 7;
     int levels = 0;
@@ -657,12 +701,13 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
 // the page's whole Key tile, share that XCD's L2 rather than each fetching
 // the tile from memory.
 __device__ inline void part_coords(const FlushArgs& A, int parts, int lin, int& part, int64_t& head, int64_t& row0,
-                                   uint8_t*& page) {
+                                   uint8_t*& page, int& lpage) {
   (void)parts;
   part = lin / A.units;
   const int unit = lin - part * A.units;
   head = unit / A.n_pages;
   const int p = unit - (int)head * A.n_pages;
+  lpage = A.first_page + p;
   row0 = head * A.src_stride + (int64_t)p * PAGE;
   if (A.table == nullptr) {
     page = A.arena + (head * A.max_pages + A.first_page + p) * A.page_stride;
@@ -676,10 +721,10 @@ __device__ inline void part_coords(const FlushArgs& A, int parts, int lin, int& 
 // part of its page.
 template <int MODE>
 __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
-  int part;
+  int part, lpage;
   int64_t head, row0;
   uint8_t* page;
-  part_coords(A, parts, lin, part, head, row0, page);
+  part_coords(A, parts, lin, part, head, row0, page, lpage);
   if (page == nullptr) {   // uniform over the block: no barrier is reached
     if (threadIdx.x == 0 && part == 0) atomicOr(A.flags, KVQ_FLAG_TABLE);
     return;
@@ -691,7 +736,7 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
     } S;
     const MixGeo g = mix_geo(A.n16, A.n4);
     if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
-    else flush_mix_key_part(A, page, head, row0, part - V_PARTS, S.k);
+    else flush_mix_key_part(A, page, head, row0, part - V_PARTS, lpage, S.k);
   } else if constexpr (MODE == KVQ_KEY_PNMIX) {
     __shared__ union {
       VPartSmem v;

@@ -184,6 +184,9 @@ struct FlushArgs {
   int pair_layout;
   int qjl_m;
   unsigned* flags;
+  const void* q_accum;            // MixKVQ reselection: query sums (128-bit) per (head, channel); null: the mask records
+  uint8_t* rec_out;               // with q_accum: record of logical page p of head h at rec_out + (h rec_stride + p) * 160
+  int rec_stride;
 };
 struct SelectArgs {
   const uint16_t* q;
@@ -203,6 +206,7 @@ struct DecodeArgs {
   int pool_pages;
   int max_pages, n_pages, pps, n_page_splits;
   int n_seg_splits;               // BF16-segment workgroups per (batch, kv head), SEG_TOKENS tokens each
+  int rec_stride;                 // 0: one record per head; > 0: record of page p of head h at mask + (h rec_stride + p) * 160
   const uint8_t* mask;
   const float* sq;
   const uint16_t* sink_k;
@@ -223,6 +227,7 @@ struct DecodeArgs {
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);
 hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream);
+hipError_t launch_accumulate(const SelectArgs& a, void* acc, int batch, hipStream_t stream);
 // with_merge false: the split kernels only; the caller launches the merge
 // (launch_merge_flush) with the same DecodeArgs
 hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s,

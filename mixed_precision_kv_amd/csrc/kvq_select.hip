@@ -13,58 +13,9 @@
 // workgroup of 1024 threads handles one (batch, kv head): 64 column lanes x
 // 16 row lanes stream the rows with coalesced loads.
 #include "kvq_internal.h"
+#include "kvq_rank.h"
 
 namespace kvq {
-
-typedef unsigned __int128 u128;
-
-// round_half_even(|bf16| * 2^64) as an integer (|x| < 2^63 assumed)
-__device__ inline u128 psi_bf16(uint16_t bits) {
-  int e = (bits >> 7) & 0xFF;
-  uint32_t sig = (bits & 0x7F) | (e ? 0x80u : 0u);
-  int ex = (e ? e : 1) - 134;          // value = sig * 2^ex
-  int s = ex + 64;
-  if (sig == 0) return 0;
-  if (s >= 0) return (u128)sig << s;
-  int rs = -s;
-  if (rs > 9) return 0;
-  uint32_t q = sig >> rs;
-  uint32_t rem = sig & ((1u << rs) - 1);
-  uint32_t half = 1u << (rs - 1);
-  if (rem > half || (rem == half && (q & 1))) q += 1;
-  return (u128)q;
-}
-
-// round_half_even(y * 2^64) for a finite double y >= 0 (y < 2^63)
-__device__ inline u128 psi_f64(double y) {
-  if (y <= 0.0) return 0;
-  double z = y * 18446744073709551616.0;     // exact scaling by 2^64
-  if (z < 9007199254740992.0) return (u128)(uint64_t)rint(z);
-  union { double d; uint64_t u; } c;
-  c.d = z;
-  int e = (int)((c.u >> 52) & 0x7FF) - 1023;
-  uint64_t sig = (c.u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-  return (u128)sig << (e - 52);
-}
-
-// 128 x 128 -> 256-bit product as four 64-bit limbs (little end first)
-__device__ inline void mul128(u128 a, u128 b, uint64_t out[4]) {
-  uint64_t a0 = (uint64_t)a, a1 = (uint64_t)(a >> 64), b0 = (uint64_t)b, b1 = (uint64_t)(b >> 64);
-  u128 p00 = (u128)a0 * b0, p01 = (u128)a0 * b1, p10 = (u128)a1 * b0, p11 = (u128)a1 * b1;
-  u128 mid = (p00 >> 64) + (uint64_t)p01 + (uint64_t)p10;
-  out[0] = (uint64_t)p00;
-  out[1] = (uint64_t)mid;
-  u128 hi = (mid >> 64) + (p01 >> 64) + (p10 >> 64) + p11;
-  out[2] = (uint64_t)hi;
-  out[3] = (uint64_t)(hi >> 64);
-}
-__device__ inline int cmp256(const uint64_t x[4], const uint64_t y[4]) {
-  for (int i = 3; i >= 0; --i) {
-    if (x[i] != y[i]) return x[i] > y[i] ? 1 : -1;
-  }
-  return 0;
-}
-
 
 // ------------------------------------------------------------------ MixKVQ
 __global__ __launch_bounds__(1024) void select_mixkvq_kernel(SelectArgs A) {
@@ -111,25 +62,12 @@ __global__ __launch_bounds__(1024) void select_mixkvq_kernel(SelectArgs A) {
       mn = fminf(mn, kmin[r][d]);
       mx = fmaxf(mx, kmax[r][d]);
     }
-    double range = (A.l_k > 0) ? (double)mx - (double)mn : 0.0;
-    // double-double key: (hi + lo) * range with hi + lo == sq exactly
-    double hi = (double)sq;
-    double lo = (double)(__int128)(sq - (u128)hi);
-    double p = hi * range;
-    double e = fma(hi, range, -p) + lo * range;
-    double kh = p + e;                          // renormalise
-    double kl = e - (kh - p);
-    key_hi[d] = kh;
-    key_lo[d] = kl;
+    const double range = (A.l_k > 0) ? (double)mx - (double)mn : 0.0;
+    dd_key(sq, range, key_hi[d], key_lo[d]);
   }
   __syncthreads();
   if (threadIdx.x < D) {
-    int d = threadIdx.x, r = 0;
-    for (int o = 0; o < D; ++o) {
-      bool better = key_hi[o] > key_hi[d] || (key_hi[o] == key_hi[d] && key_lo[o] > key_lo[d]);
-      bool same = key_hi[o] == key_hi[d] && key_lo[o] == key_lo[d];
-      if (better || (same && o < d)) ++r;
-    }
+    const int d = threadIdx.x, r = key_rank(key_hi, key_lo, d);
     rank_s[d] = r;
     tier_s[d] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
   }
@@ -204,6 +142,42 @@ __global__ __launch_bounds__(1024) void select_pnmix_kernel(SelectArgs A) {
     for (int k = 0; k < 8; ++k) byte |= hi_s[8 * threadIdx.x + k] << k;
     A.out[((int64_t)b * A.n_kv_heads + kvh) * PN_RECORD + threadIdx.x] = byte;
   }
+}
+
+// ------------------------------------------------------------------ query accumulator
+// acc[(b Hkv + h) D + d] += sum of psi(|q|) over the l_q query rows of every
+// query head of the group: the running query-magnitude accumulator of the
+// MixKVQ system section, exact and independent of how the rows are split
+// between calls. One 1024-thread workgroup per (batch, kv head), the same
+// row / column lanes as the selection.
+__global__ __launch_bounds__(1024) void accumulate_query_kernel(SelectArgs A, u128* acc) {
+  __shared__ u128 part[16][D];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int g = A.n_q_heads / A.n_kv_heads;
+  const int j = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  u128 s0 = 0, s1 = 0;
+  const int64_t rows = (int64_t)g * A.l_q;
+  for (int64_t R = rl; R < rows; R += 16) {
+    const int hh = (int)(R / A.l_q);
+    const int64_t t = R - (int64_t)hh * A.l_q;
+    const uint16_t* row = A.q + (((int64_t)b * A.n_q_heads + (int64_t)kvh * g + hh) * A.q_stride + t) * D;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[j];
+    s0 += psi_bf16((uint16_t)(w & 0x7FFF));
+    s1 += psi_bf16((uint16_t)((w >> 16) & 0x7FFF));
+  }
+  part[rl][2 * j] = s0;
+  part[rl][2 * j + 1] = s1;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    u128 sq = 0;
+    for (int r = 0; r < 16; ++r) sq += part[r][threadIdx.x];
+    acc[((int64_t)b * A.n_kv_heads + kvh) * D + threadIdx.x] += sq;
+  }
+}
+
+hipError_t launch_accumulate(const SelectArgs& a, void* acc, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(accumulate_query_kernel, dim3(a.n_kv_heads, batch), dim3(1024), 0, stream, a, (u128*)acc);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream) {
