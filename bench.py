@@ -166,20 +166,29 @@ def parse():
 class Rig:
     """Resident inputs for a workload, with `copies` rotated cache copies."""
 
-    def __init__(self, w, copies, torch, kvq, synth):
+    def __init__(self, w, copies, torch, kvq, synth, reselect=False):
+        """reselect: MixKVQ with per-page records (the running query
+        accumulator filled from the prefill queries, every prefill page
+        flushed with its tiers re-selected)."""
         self.w, self.torch, self.kvq = w, torch, kvq
         dev = "cuda"
         self.g = w.group
         self.max_pages = w.n_pages + 1
+        self.reselect = reselect
         self.cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, self.max_pages,
-                                   n_bf16=w.n_bf16, n_u4=w.n_u4, n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m)
+                                   n_bf16=w.n_bf16, n_u4=w.n_u4, n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m,
+                                   page_records=1 if reselect else 0)
         pb = kvq.kvq_page_bytes(self.cfg)
         H = w.batch * w.n_kv_heads
         L = w.prefill_tokens
         q, k, v = synth.prefill(w, dev)
         self.S = synth.qjl_matrix(w, dev) if w.key_mode == 2 else None
         self.mask = torch.zeros(max(1, H * kvq.kvq_mask_bytes(self.cfg)), dtype=torch.uint8, device=dev)
-        if w.key_mode == 0:
+        if reselect:
+            self.acc = torch.zeros(H * 128 * 2, dtype=torch.int64, device=dev)
+            kvq.kvq_accumulate_query(self.cfg, q, L, L, self.acc)
+            self.mask = torch.zeros(H * self.max_pages * 160, dtype=torch.uint8, device=dev)
+        elif w.key_mode == 0:
             kvq.kvq_select_channels(self.cfg, q, L, k.data_ptr() + w.n_sink * 256, w.n_pages * 128, self.mask,
                                     k_stride=L)
         elif w.key_mode == 1:
@@ -187,8 +196,11 @@ class Rig:
         del q
         arena = torch.zeros(H * self.max_pages * pb, dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(4, dtype=torch.int32, device=dev)
-        kvq.kvq_flush_quantize(self.cfg, k.data_ptr() + w.n_sink * 256, v.data_ptr() + w.n_sink * 256, L,
-                               w.n_pages, self.mask, self.S, arena, 0, self.flags)
+        if reselect:
+            kvq.kvq_flush_reselect(self.cfg, k, v, L, w.n_pages, self.acc, self.mask, arena, 0, self.flags)
+        else:
+            kvq.kvq_flush_quantize(self.cfg, k.data_ptr() + w.n_sink * 256, v.data_ptr() + w.n_sink * 256, L,
+                                   w.n_pages, self.mask, self.S, arena, 0, self.flags)
         rk = torch.zeros(w.batch, w.n_kv_heads, 128, 128, dtype=torch.bfloat16, device=dev)
         rv = torch.zeros_like(rk)
         t0 = w.n_sink + w.n_pages * 128
@@ -219,6 +231,15 @@ class Rig:
         w = self.w
         c = i % len(self.arenas)
         self.kvq.kvq_flush_quantize(self.cfg, self.rks[c], self.rvs[c], 128, 1, self.mask, self.S,
+                                    self.arenas[c], w.n_pages, self.flags)
+
+    def accumulate(self, i):
+        self.kvq.kvq_accumulate_query(self.cfg, self.q, 1, 1, self.acc)
+
+    def flush_reselect(self, i):
+        w = self.w
+        c = i % len(self.arenas)
+        self.kvq.kvq_flush_reselect(self.cfg, self.rks[c], self.rvs[c], 128, 1, self.acc, self.mask,
                                     self.arenas[c], w.n_pages, self.flags)
 
     def make_paged(self, seed=7):
@@ -459,6 +480,26 @@ def main():
         del rig2
         torch.cuda.empty_cache()
 
+    # per-flush reselection (MixKVQ's running query accumulator; per-page
+    # records read by the decode): the decode, the accumulation of the step's
+    # query, the reselecting one-page flush, and the step of all three
+    resel = {}
+    if w.key_mode == 0:
+        rr = Rig(w, copies, torch, kvq, synth, reselect=True)
+        kr = max(10, K // 2)
+        r_dec, _ = graph_time(torch, [lambda i=i: rr.decode(i) for i in range(kr)], [lambda i=i: rr.decode(i) for i in range(3)])
+        r_acc, _ = graph_time(torch, [lambda i=i: rr.accumulate(i) for i in range(kr)], [])
+        r_fl, _ = graph_time(torch, [lambda i=i: rr.flush_reselect(i) for i in range(kr)], [])
+        steps_r = [c for i in range(kr) for c in (lambda i=i: rr.accumulate(i), lambda i=i: rr.decode(i),
+                                                  lambda i=i: rr.flush_reselect(i))]
+        r_step, _ = graph_time(torch, steps_r, [])
+        r_step *= 3   # graph_time divides by the number of calls
+        resel = {"decode_ms": r_dec, "accumulate_ms": r_acc, "flush_reselect_ms": r_fl, "step_ms": r_step,
+                 "decode_GBps": dbytes / (r_dec * 1e-3) / 1e9,
+                 "step_GBps": (dbytes + fbytes) / (r_step * 1e-3) / 1e9}
+        del rr
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -500,6 +541,7 @@ def main():
                      "kernel": "kvq_decode_attention (decode_mix_fast + combine_kernel)",
                      "bytes_per_launch": dbytes},
         "secondary": extra,
+        "reselect_per_flush": resel,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -368,6 +368,7 @@ __device__ inline int mix_slot_pos(const MixGeo& g, int slot, int& levels, bool&
 __device__ inline void reselect_page(const FlushArgs& A, int64_t head, int lpage, bool write, KPartSmem& S) {
   const int d = threadIdx.x >> 1, half = threadIdx.x & 1;   // two threads per channel, 64 tokens each
   float mn = INFINITY, mx = -INFINITY;
+#pragma unroll 16
   for (int t = 64 * half; t < 64 * half + 64; ++t) {
     const float v = bf16_to_f32(S.tile[t * KS + d]);
     mn = fminf(mn, v);
@@ -380,16 +381,31 @@ __device__ inline void reselect_page(const FlushArgs& A, int64_t head, int lpage
     dd_key(sq, (double)mx - (double)mn, S.key_hi[d], S.key_lo[d]);
   }
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int r = key_rank(S.key_hi, S.key_lo, threadIdx.x);
-    S.tier[threadIdx.x] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
+  {  // rank of channel d: both of its threads count half of the other channels
+    const double kh = S.key_hi[d], kl = S.key_lo[d];
+    int r = 0;
+#pragma unroll 16
+    for (int o = 64 * half; o < 64 * half + 64; ++o) {
+      const double oh = S.key_hi[o], ol = S.key_lo[o];
+      r += (oh > kh || (oh == kh && (ol > kl || (ol == kl && o < d)))) ? 1 : 0;
+    }
+    r += dpp_partner<1>(r);
+    if (half == 0) S.tier[d] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
   }
   __syncthreads();
   uint8_t* rec = A.rec_out + (head * A.rec_stride + lpage) * MIX_RECORD;
   if (threadIdx.x < D) {
+    // position in the channel order: the tier's base plus the lower channels
+    // of the same tier, counted four tier bytes at a time
     const int c = threadIdx.x, t = S.tier[c];
+    const uint32_t pat = 0x01010101u * (uint32_t)t;
+    const uint32_t* tw = reinterpret_cast<const uint32_t*>(S.tier);
     int pos = t == 2 ? 0 : (t == 1 ? A.n16 : A.n16 + A.n4);
-    for (int o = 0; o < c; ++o) pos += S.tier[o] == t;
+    for (int q = 0; q < (c >> 2); ++q) {
+      const uint32_t x = tw[q] ^ pat;   // tier bytes use bits 0-1: a zero byte is the same tier
+      pos += 4 - __builtin_popcount((x | (x >> 1)) & 0x01010101u);
+    }
+    for (int o = c & ~3; o < c; ++o) pos += S.tier[o] == t;
     S.ch[pos] = (uint8_t)c;
     if (write) rec[pos] = (uint8_t)c;
   } else if (write && threadIdx.x < D + 32) {
