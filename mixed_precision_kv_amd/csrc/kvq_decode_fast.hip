@@ -301,9 +301,64 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
   consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot.v_lo, slot.v_hi, a, col);
 }
 
+// The record's tables for the page loop: slot -> channel of this lane's slots
+// and the BF16-tier channels of its lane group (bytes of the record, one
+// dword per lane in recw), the query of each slot's channel per head into
+// S.u.pg (q * 2^-6 as the Key operand, binary16 q as the offset operand) and
+// the BF16-tier operand Bq. The staged bf16 query rows qb are read first,
+// then the tables written: interleaved, each read would wait for the writes
+// before it.
+template <int G, int NKS>
+__device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t* qb, MixSmem<G, NKS>& S,
+                                  bf16x8& Bq, int lane, int a, int h, int col) {
+  constexpr int NJ = (32 * NKS + 63) / 64;
+  int sch[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int s = lane + 64 * j;
+    int idx = -1;
+    if (s < 2 * g.n4) idx = g.n16 + (s >> 1);
+    else if (s >= g.s4 && s < g.s4 + g.n2) idx = g.n16 + g.n4 + (s - g.s4);
+    const int ch = rec_byte(recw, idx < 0 ? 0 : idx);
+    sch[j] = idx < 0 ? -1 : ch;
+  }
+  int bch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int ch = rec_byte(recw, 8 * a + e);
+    bch[e] = 8 * a + e < g.n16 ? ch : -1;
+  }
+  float qsl[NJ][G], qbf[8];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) qsl[j][hh] = qb_at(qb, hh, sch[j] >= 0 ? sch[j] : 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qbf[e] = qb_at(qb, h, bch[e] >= 0 ? bch[e] : 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int s = lane + 64 * j;
+    if (s < 32 * NKS) {
+      const int ks = s >> 5, aa = (s >> 3) & 3, e = s & 7;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float qf = sch[j] >= 0 ? qsl[j][hh] : 0.f;
+        S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
+        S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * B_SCALE : 0.f);
+}
+
 // Registers of 256 VGPRs (two waves per SIMD) fit every variant except the
 // eight-channel BF16 tier, which keeps one wave per SIMD rather than spill.
-template <int G, int NKS, int NB, bool PAGED>
+// PREC: every page has its own record (per-flush reselection). Page p's
+// record dword comes with the page's loads; its tables are rebuilt at the
+// top of the page, after the wait that covers them.
+template <int G, int NKS, int NB, bool PAGED, bool PREC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 : 2))) void decode_mix_fast(
     DecodeArgs A) {
   constexpr int C = 16 / G;
@@ -330,7 +385,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   // Then the first page, its metadata into registers: while an asynchronous
   // LDS copy is in flight every wait the compiler inserts drains all loads,
   // so the set-up issues none and its waits stay partial.
-  const uint32_t recw = ld4(A.mask + head * MIX_RECORD + 4 * min(lane, MIX_RECORD / 4 - 1));
+  auto rec_word = [&](int p) {   // this lane's dword of the record page p (split-relative) uses
+    const uint8_t* r0 = PREC ? A.mask + (head * A.rec_stride + p0 + p) * MIX_RECORD : A.mask + head * MIX_RECORD;
+    return ld4(r0 + 4 * min(lane, MIX_RECORD / 4 - 1));
+  };
+  const uint32_t recw = rec_word(0);
   u32x4 qv[G / 4];
   load_q<G>(A, b, kvh, lane, qv);
   const uint8_t* pages = pset.at(0);   // paged: waits for the table load only
@@ -341,54 +400,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   MixCodes<NKS, NB> c0, c1;
   mix_load(c0, pages, g, a, r);
   __builtin_amdgcn_sched_barrier(0);
-  // slot -> channel of this lane's slots and the BF16-tier channels of its
-  // lane group, from the record
-  constexpr int NJ = (32 * NKS + 63) / 64;
-  int sch[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int s = lane + 64 * j;
-    int idx = -1;
-    if (s < 2 * g.n4) idx = g.n16 + (s >> 1);
-    else if (s >= g.s4 && s < g.s4 + g.n2) idx = g.n16 + g.n4 + (s - g.s4);
-    const int ch = rec_byte(recw, idx < 0 ? 0 : idx);
-    sch[j] = idx < 0 ? -1 : ch;
-  }
-  int bch[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int ch = rec_byte(recw, 8 * a + e);
-    bch[e] = 8 * a + e < g.n16 ? ch : -1;
-  }
   stage_q<G>(qv, qb, lane);
   __syncthreads();
-  // q of each slot's channel, per head: q * 2^-6 (Key operand) and binary16
-  // (offset operand). Every read of the staged q comes first, then the table
-  // writes: interleaved, each read would wait for the writes before it.
-  float qsl[NJ][G], qbf[8];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) qsl[j][hh] = qb_at(qb, hh, sch[j] >= 0 ? sch[j] : 0);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qbf[e] = qb_at(qb, h, bch[e] >= 0 ? bch[e] : 0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int s = lane + 64 * j;
-    if (s < 32 * NKS) {
-      const int ks = s >> 5, aa = (s >> 3) & 3, e = s & 7;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float qf = sch[j] >= 0 ? qsl[j][hh] : 0.f;
-        S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
-        S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
-      }
-    }
-  }
   bf16x8 Bq;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * B_SCALE : 0.f);
+  mix_tables<G, NKS>(recw, g, qb, S, Bq, lane, a, h, col);
   *reinterpret_cast<u32x4*>(km0 + 16 * lane) = m0[0];
   *reinterpret_cast<u32x4*>(vl0 + 16 * lane) = m0[1];
   *reinterpret_cast<u32x4*>(vh0 + 16 * lane) = m0[2];
@@ -402,20 +417,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   // be computed, requested one page earlier), then request the next page and
   // compute this one. Draining before the copies are issued keeps the
   // compiler from draining after them, which would wait for the next page.
+  uint32_t recn = 0;   // PREC: the next page's record dword
   for (int it = 0; it < np; it += 2) {
     progress_prio(it, np);
     // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
     wait_vm<0>();
+    if constexpr (PREC) {
+      if (it > 0) mix_tables<G, NKS>(recn, g, qb, S, Bq, lane, a, h, col);
+    }
     if (it + 1 < np) {
       mix_issue_meta(pset.at(it + 1), slot1, g, lane);
       mix_load(c1, pset.at(it + 1), g, a, r);
+      if constexpr (PREC) recn = rec_word(it + 1);
     }
     mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col);
     if (it + 1 >= np) break;
     wait_vm<0>();
+    if constexpr (PREC) mix_tables<G, NKS>(recn, g, qb, S, Bq, lane, a, h, col);
     if (it + 2 < np) {
       mix_issue_meta(pset.at(it + 2), slot0, g, lane);
       mix_load(c0, pset.at(it + 2), g, a, r);
+      if constexpr (PREC) recn = rec_word(it + 2);
     }
     mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col);
   }
@@ -685,16 +707,21 @@ static void launch1(K kernel, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kernel, dim3(n_parts * a.n_kv_heads * a.batch), dim3(64), 0, s, a);
 }
 
-template <int G, int NKS, bool PAGED>
+template <int G, int NKS, bool PAGED, bool PREC>
 static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
-  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0, PAGED>, a, s);
-  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1, PAGED>, a, s);
-  else launch1(decode_mix_fast<G, NKS, 8, PAGED>, a, s);
+  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0, PAGED, PREC>, a, s);
+  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1, PAGED, PREC>, a, s);
+  else if constexpr (!PREC) launch1(decode_mix_fast<G, NKS, 8, PAGED, false>, a, s);
 }
 template <int G, int NKS>
 static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
-  if (a.table) launch_mix_nb<G, NKS, true>(a, nb, s);
-  else launch_mix_nb<G, NKS, false>(a, nb, s);
+  if (a.rec_stride) {
+    if (a.table) launch_mix_nb<G, NKS, true, true>(a, nb, s);
+    else launch_mix_nb<G, NKS, false, true>(a, nb, s);
+  } else {
+    if (a.table) launch_mix_nb<G, NKS, true, false>(a, nb, s);
+    else launch_mix_nb<G, NKS, false, false>(a, nb, s);
+  }
 }
 
 // Launches the pipelined kernel when one covers the configuration (with the
@@ -703,7 +730,7 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (g != 4 && g != 8) return false;
   if (a.table && a.pps > 64) return false;   // the split's page indices live in one register
-  if (a.rec_stride) return false;             // per-page records: the generic kernel rebuilds its tables per page
+  if (a.rec_stride && (key_mode != KVQ_KEY_MIXKVQ || a.n16 > 1)) return false;   // per-page records: no eight-row BF16 tier
   if (key_mode == KVQ_KEY_MIXKVQ) {
     const MixGeo geo = mix_geo(a.n16, a.n4);
     const int nks = (geo.F + 3) / 4;

@@ -8,6 +8,7 @@ per-page channel orders; after one decode query is accumulated, the
 residual's page is reselected with the updated sums.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -68,6 +69,16 @@ def test_reselect_flow(name):
                              128, scale, out, ws, ws_bytes)
     torch.cuda.synchronize()
     assert int(flags[0].item()) == 0
+    # the pipelined kernel (when it covers the shape) against the generic one
+    os.environ["KVQ_FORCE_GENERIC_DECODE"] = "1"
+    try:
+        out_g = torch.zeros_like(out)
+        kvq.kvq_decode_attention(cfg, qd, arena, w.n_pages, records, None, None, None, 0, resid_k, resid_v,
+                                 w.n_resid, 128, scale, out_g, ws, ws_bytes)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
+    assert np.all(rel_err(out.cpu().numpy().reshape(-1, D), out_g.cpu().numpy().reshape(-1, D)) <= 2 * TOL)
     rec_all = records.cpu().numpy().reshape(H, max_pages, 160)
     arena_np = arena.cpu().numpy().reshape(H, max_pages, pb)
     o = out.cpu().numpy()
