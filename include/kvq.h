@@ -7,7 +7,8 @@
  * allocates, frees or synchronizes, keeps no mutable global state and is
  * safe to call from several threads. Every call validates its arguments on
  * the host first; on an error it returns a status and launches nothing, and
- * no output is touched. Device pointers must be 16-byte aligned. Kernels are
+ * no output is touched. Device pointers must be 16-byte aligned (page tables:
+ * 4-byte). Kernels are
  * launched asynchronously on `stream` (a hipStream_t; NULL = default stream);
  * a launch failure is reported as KVQ_HIP_ERROR.
  *
@@ -16,7 +17,10 @@
  *    BF16 / UINT4 / UINT2 Key tiers ("方法细节"), GQA aggregation, lazy
  *    update with a 128-token full-precision residual ("MixKVQ的系统级实现
  *    细节", "通过延迟更新进行摊销调度"), Algorithm 1 (Prefill, Decoding,
- *    KeyQuant, GroupQuant).
+ *    KeyQuant, GroupQuant); the running accumulator of query magnitudes
+ *    ("高效的在线显著性估计") behind the per-flush reselection; the runtime
+ *    evaluation in vLLM's setting and the limitation on non-contiguous
+ *    blocks behind the page table.
  *  - PN-Mix reproduction notes: RoPE-pair score (Eq.6), min-max (Eq.2) and
  *    1-bit midpoint correction (Eq.7), H3/L1 bit planes (Appendix G), sinks
  *    and residual, the cache API (from_prefill / append / attention /
