@@ -117,3 +117,46 @@ def test_reselect_flow(name):
         tier, perm, _ = osel.mixkvq_select_sums(sq2, rkb, w.n_bf16, w.n_u4)
         assert np.array_equal(rec_all[head, w.n_pages], osel.mixkvq_record(tier, perm)), (b, h)
         assert np.array_equal(arena_np[head, w.n_pages], oflush.flush_mixkvq_page(rkb, rvb, perm, w.n_bf16, w.n_u4))
+
+
+def test_reselect_through_page_table():
+    """The same reselection flow with the pages scattered over the pool by a
+    page table: records (indexed by logical page), page bytes and the decode
+    output equal the contiguous run's, bit for bit."""
+    base = synth.WORKLOADS["llama8b_8k"]
+    w = base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=5, seed=base.seed + 1100)
+    print(f"\n[case] reselect paged {w}", flush=True)
+    H, L = w.batch * w.n_kv_heads, w.prefill_tokens
+    max_pages = w.n_pages + 1
+    cfg = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, w.batch, w.n_q_heads, w.n_kv_heads, max_pages, n_bf16=w.n_bf16,
+                          n_u4=w.n_u4, page_records=1)
+    pb = kvq.kvq_page_bytes(cfg)
+    q, k, v = synth.prefill(w, "cuda")
+    qd = synth.decode_query(w, "cuda")
+    acc = torch.zeros(H * D * 2, dtype=torch.int64, device="cuda")
+    kvq.kvq_accumulate_query(cfg, q, L, L, acc)
+    pool = H * max_pages
+    gen = torch.Generator(device="cpu").manual_seed(31)
+    table = torch.randperm(pool, generator=gen).to(torch.int32).reshape(H, max_pages).cuda()
+    runs = []
+    for tab in (None, table):
+        records = torch.zeros(H * max_pages * 160, dtype=torch.uint8, device="cuda")
+        arena = torch.zeros(pool * pb, dtype=torch.uint8, device="cuda")
+        flags = torch.zeros(4, dtype=torch.int32, device="cuda")
+        kw = {} if tab is None else {"page_table": tab, "table_stride": max_pages}
+        kvq.kvq_flush_reselect(cfg, k, v, L, w.n_pages, acc, records, arena, 0, flags, **kw)
+        out = torch.zeros(w.batch, w.n_q_heads, D, dtype=torch.float32, device="cuda")
+        ws_bytes = kvq.kvq_workspace_bytes(cfg, w.n_pages)
+        ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_attention(cfg, qd, arena, w.n_pages, records, None, None, None, 0, None, None, 0, 0,
+                                 1.0 / math.sqrt(D), out, ws, ws_bytes, **kw)
+        torch.cuda.synchronize()
+        runs.append((records, arena, out))
+    (rec_c, arena_c, out_c), (rec_t, arena_t, out_t) = runs
+    assert torch.equal(rec_c, rec_t)
+    assert torch.equal(out_c, out_t)
+    tab = table.cpu().numpy()
+    for h in range(H):
+        for pg in range(w.n_pages):
+            i = int(tab[h, pg])
+            assert torch.equal(arena_t[i * pb:(i + 1) * pb], arena_c[(h * max_pages + pg) * pb:(h * max_pages + pg + 1) * pb])
