@@ -143,7 +143,8 @@ kvq_status kvq_workspace_bytes(const kvq_config* cfg, int32_t n_pages, size_t* b
 
 /* Host-only and pure: persistent bytes of a cache holding n_quant_tokens
  * quantized tokens (a multiple of 128), n_resid residual and n_sink sink
- * tokens per (batch, kv head). KIVI blog section 7; PN-Mix storage(). */
+ * tokens per (batch, kv head). KIVI blog section 7; PN-Mix storage(). With
+ * cfg->page_records the MixKVQ selection counts one record per page. */
 kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant_tokens, int32_t n_resid,
                              int32_t n_sink, kvq_storage_breakdown* out);
 

@@ -240,7 +240,7 @@ kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant, int32_t n_r
     o.key_full = H * T * cfg->n_bf16 * 2;
     o.key_codes = H * T * (4 * (uint64_t)cfg->n_u4 + 2 * (uint64_t)n2) / 8;
     o.key_meta = H * pages * (uint64_t)(cfg->n_u4 + n2) * 2 * 2;
-    o.selection = H * (D + D / 4);
+    o.selection = H * (cfg->page_records ? pages : 1) * (D + D / 4);   // a record per page when re-selected
     key_bits_quant = (16.0 * cfg->n_bf16 + 4.0 * cfg->n_u4 + 2.0 * n2 + 32.0 * (cfg->n_u4 + n2) / PAGE) / D;
   } else if (cfg->key_mode == KVQ_KEY_PNMIX) {
     const uint64_t n_hi = 2 * (uint64_t)cfg->n_hi_pairs;

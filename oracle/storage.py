@@ -60,12 +60,15 @@ def pnmix_key_bits(*, d, n_quant, n_sink, r=Fraction(1, 2), G=128, b_hi=3, b_lo=
     return (n_quant * per_quant + n_sink * sink_bits) / Fraction(n_quant + n_sink)
 
 
-def mixkvq_breakdown(*, n_kv_heads, d, n16, n4, n_quant, n_resid, G=128, G_V=32, v_bits=2, e=2, f=2):
+def mixkvq_breakdown(*, n_kv_heads, d, n16, n4, n_quant, n_resid, G=128, G_V=32, v_bits=2, e=2, f=2,
+                     per_page_records=False):
     """Logical persistent bytes of the MixKVQ cache for one layer/request:
     per page and KV head, BF16 channels at f bytes/token, UINT4/UINT2 codes,
     one scale + offset (e bytes each) per quantized channel; Values at
     v_bits with one scale + offset per token per G_V channels; the BF16
-    residual for K and V; the selection record (channel order + tiers)."""
+    residual for K and V; the selection record (channel order + tiers), one
+    per KV head, or one per page when the tiers are re-selected at every
+    flush."""
     n2 = d - n16 - n4
     pages = n_quant // G
     H = n_kv_heads
@@ -76,7 +79,7 @@ def mixkvq_breakdown(*, n_kv_heads, d, n16, n4, n_quant, n_resid, G=128, G_V=32,
         "v_codes": H * n_quant * d * v_bits // 8,
         "v_meta": H * n_quant * (d // G_V) * 2 * e,
         "residual": H * 2 * n_resid * d * f,
-        "mask": H * (d + d // 4),
+        "mask": H * (pages if per_page_records else 1) * (d + d // 4),
     }
     out["total"] = sum(out.values())
     return out

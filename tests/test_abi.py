@@ -65,6 +65,12 @@ def test_storage_matches_oracle(lib):
     assert got["key_meta"] == ref["k_meta"] and got["value_codes"] == ref["v_codes"]
     assert got["value_meta"] == ref["v_meta"] and got["residual"] == ref["residual"]
     assert got["total"] == ref["total"]
+    # per-flush reselection: one selection record per page
+    cfg = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 8, 32, 8, 64, n_bf16=1, n_u4=12, page_records=1)
+    got = kvq.kvq_storage_bytes(cfg, 8192, 128, 0)
+    ref = storage.mixkvq_breakdown(n_kv_heads=64, d=128, n16=1, n4=12, n_quant=8192, n_resid=128,
+                                   per_page_records=True)
+    assert got["selection"] == ref["mask"] == 64 * 64 * 160 and got["total"] == ref["total"]
     # PN-Mix at the 32K configuration: about 2.26 K bits (residual excluded)
     cfg = kvq.make_config(kvq.KVQ_KEY_PNMIX, 1, 1, 1, 256, n_hi_pairs=32)
     got = kvq.kvq_storage_bytes(cfg, 32768, 0, 32)
