@@ -48,6 +48,8 @@ class Workload:
     n_hi_pairs: int = 32    # PN-Mix: floor(r * D / 2)
     qjl_m: int = 256
     n_append: int = 0       # extra tokens appended after the decode step (C1)
+    qjl_outliers: int = 0   # QJL outlier split: outlier channels per (batch, kv head)
+    qjl_m_out: int = 0      # ... and the outlier instance's sketch rows
 
     @property
     def group(self) -> int:
@@ -80,6 +82,10 @@ WORKLOADS = {
     "pnmix_16k": Workload("pnmix_16k", PNMIX, 32, 32, 8, 128, 128, 32, 1004),
     # QJL: 32/8 heads, batch 64, 32768 context, m = 256
     "qjl_32k": Workload("qjl_32k", QJL, 64, 32, 8, 256, 0, 0, 1005),
+    # QJL with the outlier split: the same shape, eight fixed outlier Key
+    # channels (20 z) found at the prompt, 64 more sketch rows for them
+    "qjl_outlier_32k": Workload("qjl_outlier_32k", QJL, 64, 32, 8, 256, 0, 0, 1006,
+                                outlier_scale=20.0, qjl_outliers=8, qjl_m_out=64),
 }
 
 
@@ -156,7 +162,7 @@ def appended_kv(w: Workload, n: int, device="cpu"):
 
 
 def qjl_matrix(w: Workload, device="cpu") -> torch.Tensor:
-    """The QJL sketch matrix S, bf16 [m, D].
+    """The QJL sketch matrix S, bf16 [m (+ m_out), D].
 
     i.i.d. N(0,1) rows; each block of D rows is orthogonalised by a QR
     factorisation and every row is then rescaled to the length of an
@@ -171,7 +177,12 @@ def qjl_matrix(w: Workload, device="cpu") -> torch.Tensor:
         qmat = qmat * np.sign(np.diag(rmat))[None, :]
         lengths = np.linalg.norm(gen.standard_normal((HEAD_DIM, HEAD_DIM)), axis=1)
         blocks.append(qmat.T * lengths[:, None])
-    s = np.ascontiguousarray(np.concatenate(blocks, axis=0)[:m], dtype=np.float32)
+    rows = np.concatenate(blocks, axis=0)[:m]
+    if w.qjl_m_out:
+        # the outlier instance: i.i.d. N(0,1) rows, used at each head's own
+        # outlier columns only (no orthogonalisation over a per-head subset)
+        rows = np.concatenate([rows, gen.standard_normal((w.qjl_m_out, HEAD_DIM))], axis=0)
+    s = np.ascontiguousarray(rows, dtype=np.float32)
     return torch.from_numpy(s).to(torch.bfloat16).contiguous().to(device)
 
 

@@ -25,6 +25,7 @@ import numpy as np
 from . import layout
 from .numerics import bf16_to_f64, f16_to_f64
 from .quant import dequantize
+from .qjl import estimate_scores_split
 from .select import hi_channels_from_record
 
 D = 128
@@ -55,9 +56,9 @@ def dequant_pnmix_page(page, hi_channels):
     return K, dequant_values(u["v"])
 
 
-def qjl_page_parts(page, m):
-    u = layout.unpack_qjl_page(page, m)
-    return u["bits"], u["norms"], dequant_values(u["v"])
+def qjl_page_parts(page, m, m_out=0):
+    u = layout.unpack_qjl_page(page, m, m_out)
+    return u["bits"][:m + m_out], u["norms"], u.get("norms_out"), dequant_values(u["v"])
 
 
 def softmax_attend(logits: np.ndarray, values: np.ndarray):
@@ -73,7 +74,9 @@ def decode_kv_head(q_heads, K_q, V_q, scale, sink=None, resid=None, qjl=None):
 
     q_heads [g, D] float64; K_q/V_q [Tq, D] the dequantized page tokens
     (ignored for QJL keys, where ``qjl`` = (S bits, sign bits [m,Tq],
-    norm bits [Tq]) supplies the estimator); sink/resid = (K, V) float64.
+    norm bits [Tq]) supplies the estimator, or with the outlier split
+    (S bits, m, outlier channels, sign bits, normal norms, outlier norms));
+    sink/resid = (K, V) float64.
     Returns (out [g, D], probs [g, T_total])."""
     segs_k, segs_v, kinds = [], [], []
     if sink is not None and sink[0].shape[0]:
@@ -90,6 +93,10 @@ def decode_kv_head(q_heads, K_q, V_q, scale, sink=None, resid=None, qjl=None):
             if kind == "exact":
                 parts.append(kk @ q * scale)
             else:
+                if len(qjl) == 6:
+                    s_bits, m, outl, bits, nu_i, nu_o = qjl
+                    parts.append(estimate_scores_split(q, s_bits, m, outl, bits, nu_i, nu_o) * scale)
+                    continue
                 s_bits, bits, norms = qjl
                 S = bf16_to_f64(s_bits)
                 m = S.shape[0]
@@ -111,15 +118,18 @@ def kl_divergence(p_ref: np.ndarray, p_q: np.ndarray) -> float:
 
 def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0, perm=None,
                       mask_rec=None, pair_layout="half", s_bits=None,
-                      sink_k=None, sink_v=None, resid_k=None, resid_v=None, page_perms=None):
+                      sink_k=None, sink_v=None, resid_k=None, resid_v=None, page_perms=None,
+                      qjl_m=None, outl=None):
     """Decode for one (batch, KV head) from packed pages.
 
     q_bits_heads [g, D] bf16 bits; arena_pages: list of page byte arrays;
     sink_*/resid_* [n, D] bf16 bits (or None); page_perms: MixKVQ channel
-    order of each page (per-flush reselection), else `perm` for every page.
+    order of each page (per-flush reselection), else `perm` for every page;
+    qjl_m / outl: the QJL outlier split (normal rows, outlier channels).
     Returns (out [g, D], probs)."""
     q = bf16_to_f64(q_bits_heads)
-    Ks, Vs, bits_l, norms_l = [], [], [], []
+    Ks, Vs, bits_l, norms_l, norms_o = [], [], [], [], []
+    split = key_mode == 2 and outl is not None
     hi = hi_channels_from_record(mask_rec, pair_layout) if key_mode == 1 else None
     for i, page in enumerate(arena_pages):
         if key_mode == 0:
@@ -127,10 +137,12 @@ def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0
         elif key_mode == 1:
             K, V = dequant_pnmix_page(page, hi)
         else:
-            b, nrm, V = qjl_page_parts(page, s_bits.shape[0])
+            m = qjl_m if split else s_bits.shape[0]
+            b, nrm, nrm_o, V = qjl_page_parts(page, m, s_bits.shape[0] - m)
             K = np.zeros((128, D))
             bits_l.append(b)
             norms_l.append(nrm)
+            norms_o.append(nrm_o)
         Ks.append(K)
         Vs.append(V)
     K_q = np.concatenate(Ks) if Ks else np.zeros((0, D))
@@ -138,6 +150,8 @@ def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0
     qjl = None
     if key_mode == 2 and bits_l:
         qjl = (s_bits, np.concatenate(bits_l, axis=1), np.concatenate(norms_l))
+        if split:
+            qjl = (s_bits, qjl_m, outl, qjl[1], qjl[2], np.concatenate(norms_o))
     sink = None if sink_k is None else (bf16_to_f64(sink_k), bf16_to_f64(sink_v))
     resid = None if resid_k is None else (bf16_to_f64(resid_k), bf16_to_f64(resid_v))
     return decode_kv_head(q, K_q, V_q, scale, sink=sink, resid=resid, qjl=qjl)

@@ -15,7 +15,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import layout
-from .qjl import key_norms, sketch_bits
+from .qjl import key_norms, sketch_bits, split_sketch
 from .quant import quantize_groups, quantize_groups_midpoint
 
 D = 128
@@ -61,9 +61,13 @@ def flush_pnmix_page(k_bits, v_bits, hi_channels) -> np.ndarray:
     return layout.pack_pnmix_page(hi, codes, scale, offset, v)
 
 
-def flush_qjl_page(k_bits, v_bits, s_bits) -> np.ndarray:
-    m = s_bits.shape[0]
-    bits = sketch_bits(s_bits, k_bits)
-    norms = key_norms(k_bits)
+def flush_qjl_page(k_bits, v_bits, s_bits, m=None, outl=None) -> np.ndarray:
+    """QJL page of 128 tokens. s_bits [m (+ m_o), D]; with the outlier split
+    (outl: [D] bool outlier channels of the head) rows m.. are the outlier
+    instance."""
     v = quantize_values(v_bits)
-    return layout.pack_qjl_page(m, bits, norms, v)
+    if outl is None:
+        m = s_bits.shape[0]
+        return layout.pack_qjl_page(m, sketch_bits(s_bits, k_bits), key_norms(k_bits), v)
+    bits, nu_i, nu_o = split_sketch(s_bits, m, k_bits, outl)
+    return layout.pack_qjl_page(m, bits, nu_i, v, norms_out=nu_o)

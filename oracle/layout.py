@@ -364,11 +364,15 @@ def unpack_pnmix_page(page, hi_channels):
 
 
 # --------------------------------------------------------------- QJL
-def qjl_geometry(m: int):
-    off_norm = 16 * m
-    off_v = off_norm + 256
+def qjl_geometry(m: int, m_out: int = 0):
+    """QJL page: sign bits of m (+ m_out outlier-instance) rows, 16 B per row
+    (fragment order of pack1_region), the binary16 norms, with the outlier
+    split a second norm array, then the value region."""
+    off_norm = 16 * (m + m_out)
+    off_norm_o = off_norm + 256
+    off_v = off_norm + (512 if m_out else 256)
     used = off_v + V_CODE_BYTES + V_META_BYTES
-    return dict(off_norm=off_norm, off_v=off_v, used=used, stride=_round_up(used, 256))
+    return dict(off_norm=off_norm, off_norm_o=off_norm_o, off_v=off_v, used=used, stride=_round_up(used, 256))
 
 
 def norm_position(t: int) -> int:
@@ -378,24 +382,38 @@ def norm_position(t: int) -> int:
     return 32 * a + 4 * i + e
 
 
-def pack_qjl_page(m, bits, norms, v):
-    """bits [m][128 t] sign bits (1 = non-negative); norms [128] f16 bits."""
-    g = qjl_geometry(m)
-    page = np.zeros(g["stride"], np.uint8)
-    page[0: 16 * m] = pack1_region(np.asarray(bits, np.uint8))
+def _put_norms(page, off, norms):
     nv = np.zeros(PAGE, np.uint16)
     for t in range(PAGE):
         nv[norm_position(t)] = norms[t]
-    page[g["off_norm"]: g["off_norm"] + 256] = _u16_bytes(nv)
+    page[off: off + 256] = _u16_bytes(nv)
+
+
+def _get_norms(page, off):
+    nv = _bytes_u16(page[off: off + 256])
+    return np.array([nv[norm_position(t)] for t in range(PAGE)], dtype=np.uint16)
+
+
+def pack_qjl_page(m, bits, norms, v, norms_out=None):
+    """bits [m (+ m_out)][128 t] sign bits (1 = non-negative); norms [128] f16
+    bits; norms_out: the outlier instance's norms (with m_out rows of bits)."""
+    bits = np.asarray(bits, np.uint8)
+    m_out = bits.shape[0] - m
+    g = qjl_geometry(m, m_out)
+    page = np.zeros(g["stride"], np.uint8)
+    page[0: 16 * (m + m_out)] = pack1_region(bits)
+    _put_norms(page, g["off_norm"], norms)
+    if m_out:
+        _put_norms(page, g["off_norm_o"], norms_out)
     page[g["off_v"]: g["off_v"] + V_CODE_BYTES + V_META_BYTES] = pack_v(*v)
     return page
 
 
-def unpack_qjl_page(page, m):
-    g = qjl_geometry(m)
+def unpack_qjl_page(page, m, m_out=0):
+    g = qjl_geometry(m, m_out)
     page = np.asarray(page, np.uint8)
-    bits = unpack1_region(page[0: 16 * m], m)
-    nv = _bytes_u16(page[g["off_norm"]: g["off_norm"] + 256])
-    norms = np.array([nv[norm_position(t)] for t in range(PAGE)], dtype=np.uint16)
-    v = unpack_v(page[g["off_v"]:])
-    return dict(bits=bits, norms=norms, v=v)
+    bits = unpack1_region(page[0: 16 * (m + m_out)], m + m_out)
+    out = dict(bits=bits, norms=_get_norms(page, g["off_norm"]), v=unpack_v(page[g["off_v"]:]))
+    if m_out:
+        out["norms_out"] = _get_norms(page, g["off_norm_o"])
+    return out

@@ -7,7 +7,15 @@
 * the moment identity of the proof, E|z_i| and E z_i^2 for
   z_i = sqrt(pi/2) |k| s_i.q sign(s_i.k);
 * exact sign bits (sign(0) = +1) and correctly rounded binary16 norms;
-* the score estimator equals the definition on the stored bits and norms.
+* the score estimator equals the definition on the stored bits and norms;
+* the outlier split ("处理异常值"): outlier channels are the largest exact
+  sums of |K| (constructed outliers found, ties to the lower channel, brute
+  force over Fractions); the split estimator is unbiased (a wrong instance
+  factor or norm makes it biased) and has a smaller error than one instance
+  when a few channels dominate the key norm (the distortion of Theorem 3.6
+  grows with the norm); with all outlier coordinates zero the normal
+  instance's bits and norm are plain QJL's and the outlier instance reads
+  +1 with norm 0; the packed page round-trips.
 """
 import math
 from fractions import Fraction
@@ -102,3 +110,110 @@ def test_estimator_on_stored_sketch():
         val = math.sqrt(math.pi / 2) / 256 * f16_to_f64(norms[t:t + 1])[0] * float((Sf @ q) @ signs)
         assert abs(val - est[t]) <= 1e-12 * max(1.0, abs(val))
     assert rn_f16_bits(Fraction(5)) == 0x4500
+
+
+# ------------------------------------------------------------------ outlier split
+def _bf16_bits(x):
+    import torch
+    return torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_outlier_channels_found_and_ties():
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((300, 128))
+    chans = [3, 17, 40, 41, 77, 90, 101, 127]
+    k[:, chans] *= 20.0
+    kb = _bf16_bits(k)
+    outl = qjl.outlier_mask(kb, 8)
+    assert sorted(np.nonzero(outl)[0].tolist()) == chans
+    # brute force: exact Fraction sums, sorted by (-sum, channel)
+    small = _bf16_bits(rng.standard_normal((7, 128)))
+    sums = [sum(abs(bf16_fraction(int(small[t, d]))) for t in range(7)) for d in range(128)]
+    want = sorted(range(128), key=lambda d: (-sums[d], d))[:5]
+    assert sorted(np.nonzero(qjl.outlier_mask(small, 5))[0].tolist()) == sorted(want)
+    # equal sums: the lower channel wins
+    tie = np.ones((4, 128), np.float32)
+    tie[:, 60] = tie[:, 9] = 2.0
+    tie[:, 100] = 2.0
+    got = np.nonzero(qjl.outlier_mask(_bf16_bits(tie), 2))[0].tolist()
+    assert got == [9, 60]
+    rec = qjl.outlier_record(qjl.outlier_mask(_bf16_bits(tie), 3))
+    assert rec[1] == 1 << 1 and rec[7] == 1 << 4 and rec[12] == 1 << 4 and rec.sum() == 2 + 16 + 16
+    assert np.array_equal(qjl.outlier_mask_from_record(rec), qjl.outlier_mask(_bf16_bits(tie), 3))
+
+
+def test_split_estimator_unbiased_and_tighter():
+    rng = np.random.default_rng(6)
+    d, m, m_o, trials = 16, 32, 16, 40000
+    outl = np.zeros(d, bool)
+    outl[[2, 11]] = True
+    q = rng.standard_normal(d)
+    q[outl] = [0.7, -0.9]                     # a query not aligned with the outliers
+    k = rng.standard_normal(d)
+    k[outl] *= 25.0
+    split, plain = np.empty(trials), np.empty(trials)
+    for t in range(trials):
+        S_i = rng.standard_normal((m, d))
+        S_o = rng.standard_normal((m_o, d))
+        split[t] = qjl.prod_qjl_split(q, k, S_i, S_o, outl)
+        plain[t] = qjl.prod_qjl(q, k, np.concatenate([S_i, S_o]))
+    mean, sd = split.mean(), split.std() / math.sqrt(trials)
+    assert abs(mean - q @ k) < 4 * sd
+    # closed-form variance (the moment identity E z^2 = pi/2 |q|^2 |k|^2 of
+    # each term, per instance): a wrong factor or norm moves it
+    def var(qq, kk, rows):
+        return (math.pi / 2 * (qq @ qq) * (kk @ kk) - (qq @ kk) ** 2) / rows
+    q_i, k_i = np.where(outl, 0.0, q), np.where(outl, 0.0, k)
+    want = var(q_i, k_i, m) + var(np.where(outl, q, 0.0), np.where(outl, k, 0.0), m_o)
+    assert abs(np.var(split) / want - 1) < 0.06
+    # one instance of the same total rows: the outlier norm inflates its error
+    assert np.mean((split - q @ k) ** 2) < 0.5 * np.mean((plain - q @ k) ** 2)
+    # a wrong outlier-instance factor (1/m instead of 1/m_o) is biased
+    q_o, k_o = np.where(outl, q, 0.0), np.where(outl, k, 0.0)
+    wrong = np.array([qjl.prod_qjl(np.where(outl, 0, q), np.where(outl, 0, k), rng.standard_normal((m, d)))
+                      + qjl.prod_qjl(q_o, k_o, rng.standard_normal((m_o, d))) * m_o / m for _ in range(4000)])
+    assert abs(wrong.mean() - q @ k) > 4 * wrong.std() / math.sqrt(4000)
+
+
+def test_split_sketch_reduces_and_page_roundtrip():
+    from oracle import flush, layout
+    rng = np.random.default_rng(7)
+    m, m_o = 128, 64
+    s = _bf16_bits(rng.standard_normal((m + m_o, 128)))
+    outl = np.zeros(128, bool)
+    outl[[5, 6, 70, 99]] = True
+    k = rng.standard_normal((128, 128))
+    k[:, outl] = 0.0
+    kb = _bf16_bits(k)
+    bits, nu_i, nu_o = qjl.split_sketch(s, m, kb, outl)
+    assert np.array_equal(bits[:m], qjl.sketch_bits(s[:m], kb))
+    assert np.array_equal(nu_i, qjl.key_norms(kb))
+    assert np.all(bits[m:] == 1) and np.all(nu_o == 0)
+    # nonzero outliers: each instance sees only its own coordinates
+    k2 = rng.standard_normal((128, 128))
+    k2[:, outl] *= 30.0
+    kb2 = _bf16_bits(k2)
+    bits2, nu_i2, nu_o2 = qjl.split_sketch(s, m, kb2, outl)
+    S = bf16_to_f64_(s)
+    K = bf16_to_f64_(kb2)
+    assert np.array_equal(bits2[m:], ((S[m:][:, outl] @ K[:, outl].T) >= 0).astype(np.uint8))
+    assert np.array_equal(bits2[:m], ((S[:m][:, ~outl] @ K[:, ~outl].T) >= 0).astype(np.uint8))
+    assert np.allclose(f16_to_f64(nu_o2), np.linalg.norm(K[:, outl], axis=1), rtol=1e-3)
+    v = _bf16_bits(rng.standard_normal((128, 128)))
+    page = flush.flush_qjl_page(kb2, v, s, m=m, outl=outl)
+    g = layout.qjl_geometry(m, m_o)
+    assert page.shape[0] == g["stride"] and g["off_v"] == 16 * (m + m_o) + 512
+    u = layout.unpack_qjl_page(page, m, m_o)
+    assert np.array_equal(u["bits"][:m + m_o], bits2)
+    assert np.array_equal(u["norms"], nu_i2) and np.array_equal(u["norms_out"], nu_o2)
+    # the estimator on the stored page equals the split definition
+    q = rng.standard_normal(128)
+    est = qjl.estimate_scores_split(q, s, m, outl, u["bits"][:m + m_o], u["norms"], u["norms_out"])
+    want = (math.sqrt(math.pi / 2) / m * f16_to_f64(nu_i2) * ((S[:m][:, ~outl] @ q[~outl]) @ (2.0 * bits2[:m] - 1))
+            + math.sqrt(math.pi / 2) / m_o * f16_to_f64(nu_o2) * ((S[m:][:, outl] @ q[outl]) @ (2.0 * bits2[m:] - 1)))
+    assert np.allclose(est, want, rtol=1e-12, atol=1e-12)
+
+
+def bf16_to_f64_(bits):
+    from oracle.numerics import bf16_to_f64
+    return bf16_to_f64(bits)
