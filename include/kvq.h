@@ -26,7 +26,10 @@
  *    and residual, the cache API (from_prefill / append / attention /
  *    storage).
  *  - QJL (AAAI 2025) summary: Definition 3.1, Algorithm 1 (sign sketch,
- *    norm, EstimateScores), orthogonalised S.
+ *    norm, EstimateScores), orthogonalised S, and its outlier handling
+ *    ("处理异常值（Outliers）" with Figure 2: outlier channels fixed at the
+ *    prompt, two independent QJL instances, more sketch rows per outlier
+ *    coordinate).
  *  - KIVI quantization-axes blog: per-channel Keys / per-token Values,
  *    round-half-to-even, low-bits-first packing, one global softmax,
  *    storage formula.
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_HEAD_DIM 128
 #define KVQ_PAGE_TOKENS 128
 #define KVQ_VALUE_GROUP 32
@@ -101,7 +104,11 @@ typedef struct kvq_config {
   int32_t page_records;       /* MixKVQ: 0, one selection record per (batch, kv head) (selection at
                                  prefill); 1, one record per page, written by kvq_flush_reselect
                                  (tiers re-selected at every flush) and read per page by the decode */
-  int32_t reserved[3];        /* must be zero */
+  int32_t qjl_outliers;       /* QJL: 0, one sketch instance; 1..64, outlier channels per (batch, kv head)
+                                 found by kvq_select_channels, sketched by a second instance */
+  int32_t qjl_m_out;          /* QJL with outliers: that instance's sketch rows, a multiple of 64,
+                                 qjl_m + qjl_m_out <= 384 (else 0) */
+  int32_t reserved;           /* must be zero */
 } kvq_config;
 
 /* Persistent cache bytes of one layer for all (batch, kv head) pairs, by
@@ -135,7 +142,8 @@ kvq_status kvq_page_bytes(const kvq_config* cfg, size_t* bytes);
  * MixKVQ: 160 bytes = channel order u8[128] (BF16 tier, then UINT4, then
  * UINT2, each ascending) + 2-bit tier codes (0 UINT2, 1 UINT4, 2 BF16, low
  * bits first). PN-Mix: 8 bytes, bit i = RoPE pair i kept at 3 bits.
- * QJL: 0 (S is an input). */
+ * QJL: 0 (S is an input); with qjl_outliers, 16 bytes: bit d % 8 of byte
+ * d / 8 set for outlier channel d. */
 kvq_status kvq_mask_bytes(const kvq_config* cfg, size_t* bytes);
 
 /* Device workspace kvq_decode_attention needs for n_pages pages. */
@@ -156,13 +164,17 @@ kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant_tokens, int3
  *    the n_bf16 best are BF16, the next n_u4 UINT4, the rest UINT2.
  *  PN-Mix (Eq.6): pairs ranked by sum_t ||q pair|| * sum_s ||k pair||
  *    (query sum over the whole GQA group), top n_hi_pairs kept at 3 bits.
- *  Both rank on exact integer sums of the per-element values rounded to a
+ *  QJL with qjl_outliers > 0 (outlier handling of the QJL page, Figure 2):
+ *    channels ranked by sum over the l_k Key tokens of |K| (ties: lower d
+ *    first), the qjl_outliers largest are the head's outlier channels;
+ *    q_pre is not read (may be NULL).
+ *  All rank on exact integer sums of the per-element values rounded to a
  *  2^-64 grid, so the result does not depend on summation order.
  * q_pre: device bf16, element (b, h, t, d) at q_pre[((b*Hq + h)*q_stride + t)*128 + d]
  * k_pre: device bf16, element (b, h, t, d) at k_pre[((b*Hkv + h)*k_stride + t)*128 + d]
  * mask_out: device, batch*n_kv_heads records of kvq_mask_bytes bytes.
  * Preconditions: finite inputs with |q|, |k| < 2^30.
- * QJL returns KVQ_UNSUPPORTED (S is generated by the caller). */
+ * QJL without outliers returns KVQ_UNSUPPORTED (S is generated by the caller). */
 kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t l_q, int64_t q_stride,
                                const void* k_pre, int64_t l_k, int64_t k_stride, void* mask_out,
                                void* stream);
@@ -176,8 +188,12 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
  * 32 channels, 2 bits.
  * k_src/v_src: device bf16, token t of page p of (b, h) at
  *   src[((b*Hkv + h)*src_stride + p*128 + t)*128 + d].
- * mask: the records of kvq_select_channels (ignored for QJL).
- * qjl_s: device bf16 [qjl_m][128] (QJL only, else may be NULL).
+ * mask: the records of kvq_select_channels (ignored for QJL without outliers).
+ * qjl_s: device bf16 [qjl_m + qjl_m_out][128] (QJL only, else may be NULL).
+ *   With outliers, rows < qjl_m sketch the key's normal channels (the row
+ *   restricted to them) and rows >= qjl_m its outlier channels; the page
+ *   keeps both instances' sign bits and the two binary16 norms ||k_normal||
+ *   and ||k_outlier||.
  * page_arena: device, batch * n_kv_heads * max_pages pages of kvq_page_bytes
  *   (the page pool).
  * page_table: NULL, or device int32 [batch][n_kv_heads][table_stride], 4-byte
@@ -235,14 +251,16 @@ kvq_status kvq_flush_reselect(const kvq_config* cfg, const void* k_src, const vo
  * Decoding; PN-Mix cache.attention; QJL EstimateScores + softmax):
  *   out[b, h, :] = sum_t softmax_t(logit_t) * v^_t,
  *   logit_t = softmax_scale * q . k^_t for BF16 and dequantized keys,
- *   logit_t = softmax_scale * sqrt(pi/2)/m * nu_t * <S q, sign(S k_t)> for QJL pages.
+ *   logit_t = softmax_scale * sqrt(pi/2)/m * nu_t * <S q, sign(S k_t)> for QJL pages;
+ *   with the outlier split the sum of that estimate over the normal channels
+ *   (m = qjl_m rows) and over the outlier channels (m = qjl_m_out rows).
  * q: device bf16 [batch][n_q_heads][128]; query head h uses kv head h / (Hq/Hkv).
  * page_arena, page_table, table_stride: as for kvq_flush_quantize; pages
  *   0 .. n_pages - 1 are read (n_pages <= max_pages without a table, <=
  *   table_stride with one). A table entry outside the pool is clamped into
  *   it (that page's contribution is then unspecified).
  * mask: the records of kvq_select_channels, 16-byte aligned (ignored for QJL
- *   and when n_pages is 0); with cfg->page_records, the per-page records of
+ *   without outliers and when n_pages is 0); with cfg->page_records, the per-page records of
  *   kvq_flush_reselect (same indexing as there), read page by page.
  * sink_k/sink_v: device bf16 [batch][n_kv_heads][n_sink][128] (n_sink <= 128; may be NULL if 0).
  * resid_k/resid_v: device bf16 [batch][n_kv_heads][resid_stride][128], first

@@ -15,7 +15,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_ABI_VERSION = 2
+KVQ_ABI_VERSION = 3
 KVQ_OK, KVQ_INVALID_ARG, KVQ_UNSUPPORTED, KVQ_WORKSPACE_TOO_SMALL, KVQ_CAPACITY, KVQ_HIP_ERROR = range(6)
 KVQ_KEY_MIXKVQ, KVQ_KEY_PNMIX, KVQ_KEY_QJL = 0, 1, 2
 KVQ_PAIR_HALF_SPLIT, KVQ_PAIR_ADJACENT = 0, 1
@@ -35,7 +35,8 @@ class KvqConfig(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("max_pages", ctypes.c_int32), ("n_bf16", ctypes.c_int32), ("n_u4", ctypes.c_int32),
         ("pair_layout", ctypes.c_int32), ("n_hi_pairs", ctypes.c_int32), ("qjl_m", ctypes.c_int32),
-        ("page_records", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+        ("page_records", ctypes.c_int32), ("qjl_outliers", ctypes.c_int32),
+        ("qjl_m_out", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -90,7 +91,8 @@ def load(path: str = LIB_PATH):
 
 def make_config(key_mode: int, batch: int, n_q_heads: int, n_kv_heads: int, max_pages: int, *,
                 n_bf16: int = 0, n_u4: int = 0, pair_layout: int = KVQ_PAIR_HALF_SPLIT,
-                n_hi_pairs: int = 32, qjl_m: int = 256, head_dim: int = 128, page_records: int = 0) -> KvqConfig:
+                n_hi_pairs: int = 32, qjl_m: int = 256, head_dim: int = 128, page_records: int = 0,
+                qjl_outliers: int = 0, qjl_m_out: int = 0) -> KvqConfig:
     c = KvqConfig()
     c.abi_version = KVQ_ABI_VERSION
     c.key_mode = key_mode
@@ -99,6 +101,7 @@ def make_config(key_mode: int, batch: int, n_q_heads: int, n_kv_heads: int, max_
     c.n_bf16, c.n_u4 = n_bf16, n_u4
     c.pair_layout, c.n_hi_pairs, c.qjl_m = pair_layout, n_hi_pairs, qjl_m
     c.page_records = page_records
+    c.qjl_outliers, c.qjl_m_out = qjl_outliers, qjl_m_out
     return c
 
 
@@ -161,7 +164,8 @@ def kvq_storage_bytes(cfg: KvqConfig, n_quant_tokens: int, n_resid: int, n_sink:
 
 
 def kvq_select_channels(cfg, q_pre, l_q, k_pre, l_k, mask_out, *, q_stride=None, k_stride=None, stream=None):
-    """q_pre [B,Hq,q_stride,128], k_pre [B,Hkv,k_stride,128] bf16 (device pointers or tensors)."""
+    """q_pre [B,Hq,q_stride,128], k_pre [B,Hkv,k_stride,128] bf16 (device pointers or tensors);
+    the QJL outlier selection reads no queries (q_pre None, l_q 0)."""
     q_stride = l_q if q_stride is None else q_stride
     k_stride = l_k if k_stride is None else k_stride
     _check("kvq_select_channels", load().kvq_select_channels(

@@ -13,8 +13,8 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static kvq_status check_config(const kvq_config* c) {
   if (!c) return KVQ_INVALID_ARG;
   if (c->abi_version != KVQ_ABI_VERSION) return KVQ_INVALID_ARG;
-  for (int i = 0; i < 3; ++i)
-    if (c->reserved[i] != 0) return KVQ_INVALID_ARG;
+  if (c->reserved != 0) return KVQ_INVALID_ARG;
+  if (c->key_mode != KVQ_KEY_QJL && (c->qjl_outliers != 0 || c->qjl_m_out != 0)) return KVQ_INVALID_ARG;
   if (c->page_records != 0 && c->page_records != 1) return KVQ_INVALID_ARG;
   if (c->page_records && c->key_mode != KVQ_KEY_MIXKVQ) return KVQ_UNSUPPORTED;
   if (c->head_dim != D) return c->head_dim > 0 ? KVQ_UNSUPPORTED : KVQ_INVALID_ARG;
@@ -34,6 +34,9 @@ static kvq_status check_config(const kvq_config* c) {
     case KVQ_KEY_QJL:
       if (c->qjl_m < 64 || c->qjl_m % 64) return KVQ_INVALID_ARG;
       if (c->qjl_m > 256) return KVQ_UNSUPPORTED;
+      if (c->qjl_outliers < 0 || c->qjl_outliers > 64 || c->qjl_m_out < 0 || c->qjl_m_out % 64) return KVQ_INVALID_ARG;
+      if ((c->qjl_outliers == 0) != (c->qjl_m_out == 0)) return KVQ_INVALID_ARG;
+      if (c->qjl_m + c->qjl_m_out > 384) return KVQ_UNSUPPORTED;
       break;
     default:
       return KVQ_INVALID_ARG;
@@ -47,13 +50,13 @@ static int pool_pages(const kvq_config* c) { return c->batch * c->n_kv_heads * c
 static size_t page_stride(const kvq_config* c) {
   if (c->key_mode == KVQ_KEY_MIXKVQ) return (size_t)mix_geo(c->n_bf16, c->n_u4).stride;
   if (c->key_mode == KVQ_KEY_PNMIX) return (size_t)pn_geo(2 * c->n_hi_pairs).stride;
-  return (size_t)qjl_geo(c->qjl_m).stride;
+  return (size_t)qjl_geo(c->qjl_m, c->qjl_m_out).stride;
 }
 
 static size_t record_bytes(const kvq_config* c) {
   if (c->key_mode == KVQ_KEY_MIXKVQ) return MIX_RECORD;
   if (c->key_mode == KVQ_KEY_PNMIX) return PN_RECORD;
-  return 0;
+  return c->qjl_outliers ? QJL_RECORD : 0;
 }
 
 static int n_page_splits(const kvq_config* c, int n_pages) {
@@ -67,7 +70,7 @@ static size_t workspace_for(const kvq_config* c, int n_pages) {
   size_t splits = (size_t)n_page_splits(c, n_pages) + MAX_SEG_SPLITS;
   size_t rows = (size_t)c->batch * c->n_q_heads;
   size_t bytes = splits * rows * 130 * sizeof(float);
-  if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)c->qjl_m * sizeof(float);
+  if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)(c->qjl_m + c->qjl_m_out) * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -84,7 +87,8 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   if (page_table && (table_stride < 1 || ((uintptr_t)page_table & 3u))) return KVQ_INVALID_ARG;
   if (n_pages < 0 || first_page < 0 || src_stride < (int64_t)n_pages * PAGE) return KVQ_INVALID_ARG;
   if ((int64_t)first_page + n_pages > (page_table ? table_stride : cfg->max_pages)) return KVQ_CAPACITY;
-  if (cfg->key_mode != KVQ_KEY_QJL && !mask) return KVQ_INVALID_ARG;
+  const bool needs_mask = cfg->key_mode != KVQ_KEY_QJL || cfg->qjl_outliers > 0;
+  if (needs_mask && !mask) return KVQ_INVALID_ARG;
   if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
   // one block per (page, part, kv head, batch) on a one-dimensional grid
   if ((int64_t)n_pages * 16 * cfg->n_kv_heads * cfg->batch > INT32_MAX / 2) return KVQ_INVALID_ARG;
@@ -108,6 +112,7 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   a.n_hi = 2 * cfg->n_hi_pairs;
   a.pair_layout = cfg->pair_layout;
   a.qjl_m = cfg->qjl_m;
+  a.qjl_mo = cfg->qjl_m_out;
   a.flags = status_flags;
   a.q_accum = nullptr;
   a.rec_out = nullptr;
@@ -130,7 +135,8 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   if (page_table && (table_stride < 1 || ((uintptr_t)page_table & 3u))) return KVQ_INVALID_ARG;
   if (n_pages < 0 || n_pages > (page_table ? table_stride : cfg->max_pages)) return KVQ_INVALID_ARG;
   if (n_pages > 0 && (!page_arena || !aligned16(page_arena))) return KVQ_INVALID_ARG;
-  if (n_pages > 0 && cfg->key_mode != KVQ_KEY_QJL && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
+  const bool needs_mask = cfg->key_mode != KVQ_KEY_QJL || cfg->qjl_outliers > 0;
+  if (n_pages > 0 && needs_mask && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
   if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
   if (n_sink < 0 || n_sink > PAGE || n_resid < 0 || n_resid > PAGE) return KVQ_INVALID_ARG;
   if (n_sink > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v))) return KVQ_INVALID_ARG;
@@ -173,6 +179,7 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.n_hi = 2 * cfg->n_hi_pairs;
   a.pair_layout = cfg->pair_layout;
   a.qjl_m = cfg->qjl_m;
+  a.qjl_mo = cfg->qjl_m_out;
   return KVQ_OK;
 }
 }  // namespace kvq
@@ -249,10 +256,11 @@ kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant, int32_t n_r
     o.selection = H * ((D / 2 + 7) / 8);
     key_bits_quant = (D + 2.0 * n_hi + 32.0 * D / PAGE) / D;
   } else {
-    o.key_codes = H * T * (uint64_t)cfg->qjl_m / 8;
-    o.key_meta = H * T * 2;
-    o.selection = 0;
-    key_bits_quant = ((double)cfg->qjl_m + 16.0) / D;
+    const int n_norms = cfg->qjl_m_out ? 2 : 1;   // the outlier split keeps a second norm
+    o.key_codes = H * T * (uint64_t)(cfg->qjl_m + cfg->qjl_m_out) / 8;
+    o.key_meta = H * T * 2 * n_norms;
+    o.selection = cfg->qjl_outliers ? H * QJL_RECORD : 0;
+    key_bits_quant = ((double)cfg->qjl_m + cfg->qjl_m_out + 16.0 * n_norms) / D;
   }
   o.total = o.key_full + o.key_codes + o.key_meta + o.value_codes + o.value_meta + o.residual + o.sink + o.selection;
   const double toks = (double)n_quant + n_sink;
@@ -265,11 +273,13 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
                                const void* k_pre, int64_t l_k, int64_t k_stride, void* mask_out, void* stream) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
-  if (cfg->key_mode == KVQ_KEY_QJL) return KVQ_UNSUPPORTED;
-  if (!q_pre || !k_pre || !mask_out) return KVQ_INVALID_ARG;
-  if (!aligned16(q_pre) || !aligned16(k_pre)) return KVQ_INVALID_ARG;
-  if (l_q < 1 || l_k < 1 || q_stride < l_q || k_stride < l_k) return KVQ_INVALID_ARG;
+  const bool qjl = cfg->key_mode == KVQ_KEY_QJL;
+  if (qjl && cfg->qjl_outliers == 0) return KVQ_UNSUPPORTED;
+  if ((!qjl && !q_pre) || !k_pre || !mask_out) return KVQ_INVALID_ARG;
+  if ((!qjl && !aligned16(q_pre)) || !aligned16(k_pre)) return KVQ_INVALID_ARG;
+  if ((!qjl && (l_q < 1 || q_stride < l_q)) || l_k < 1 || k_stride < l_k) return KVQ_INVALID_ARG;
   SelectArgs a;
+  memset(&a, 0, sizeof(a));
   a.q = (const uint16_t*)q_pre;
   a.k = (const uint16_t*)k_pre;
   a.l_q = l_q;
@@ -282,6 +292,7 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
   a.n4 = cfg->n_u4;
   a.n_hi_pairs = cfg->n_hi_pairs;
   a.pair_layout = cfg->pair_layout;
+  a.n_out = cfg->qjl_outliers;
   a.out = (uint8_t*)mask_out;
   return launch_select(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }

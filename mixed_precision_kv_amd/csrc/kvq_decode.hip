@@ -35,7 +35,7 @@
 
 namespace kvq {
 
-constexpr int QJL_MAX_KS = 8;   // m <= 256
+constexpr int QJL_MAX_KS = 12;  // m + mo <= 384
 
 struct DecodeSmem {
   float qf[8][D];                              // the group's query heads (float)
@@ -229,10 +229,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
                                 page + g.off_v + V_CODE_BYTES + 1024, a, col);
     }
   } else {   // QJL
-    const QjlGeo g = qjl_geo(A.qjl_m);
-    const int NKS = A.qjl_m / 32;
-    const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * A.qjl_m;
-    float ssum = 0.f;
+    // with the outlier split, k-steps NKI.. are the outlier instance: its
+    // estimate is accumulated apart and added with its own norm and factor
+    const QjlGeo g = qjl_geo(A.qjl_m, A.qjl_mo);
+    const int NKS = (A.qjl_m + A.qjl_mo) / 32, NKI = A.qjl_m / 32;
+    const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * (A.qjl_m + A.qjl_mo);
+    float ssum = 0.f, ssum_o = 0.f;
     for (int ks = 0; ks < NKS; ++ks) {
       float x[8];
 #pragma unroll
@@ -243,10 +245,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         S.u.bq[0][ks][a][h] = hi;
         S.u.bq[1][ks][a][h] = lo;
       }
+      float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ssum += (float)hi[e] + (float)lo[e];
+      for (int e = 0; e < 8; ++e) part += (float)hi[e] + (float)lo[e];
+      if (ks < NKI) ssum += part;
+      else ssum_o += part;
     }
     ssum = wave_sum_groups(ssum);          // sum_i (S q)_i * 2^-6 as seen by the MFMA
+    ssum_o = wave_sum_groups(ssum_o);
+    const float ratio = A.qjl_mo ? (float)A.qjl_m / (float)A.qjl_mo : 0.f;   // the instances' sqrt(pi/2)/m factors
     __syncthreads();
     const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
     for (int pg = p0; pg < p1; ++pg) {
@@ -254,39 +261,47 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
       u32x4 vc[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
-      f32x4 logit[8];
+      f32x4 logit[8], logit_o[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      for (int P2 = 0; P2 < NKS / 2; ++P2) {
-        const u32x4 v = ld16(page + 1024 * P2 + 256 * a + 16 * r);
+      for (int i = 0; i < 8; ++i) logit[i] = logit_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      auto sketch = [&](int P2b, int P2e, f32x4* acc) {
+        for (int P2 = P2b; P2 < P2e; ++P2) {
+          const u32x4 v = ld16(page + 1024 * P2 + 256 * a + 16 * r);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int ks = 2 * P2 + hf;
-          const half8 Bh = S.u.bq[0][ks][a][h], Bl = S.u.bq[1][ks][a][h];
-          const Row1 x = row1(rd(v, 2 * hf), rd(v, 2 * hf + 1));
+          for (int hf = 0; hf < 2; ++hf) {
+            const int ks = 2 * P2 + hf;
+            const half8 Bh = S.u.bq[0][ks][a][h], Bl = S.u.bq[1][ks][a][h];
+            const Row1 x = row1(rd(v, 2 * hf), rd(v, 2 * hf + 1));
 #pragma unroll
-          for (int T = 0; T < 8; ++T) {
-            const half8 At = tile1(x, T);
-            logit[T] = mfma(At, Bh, logit[T]);
-            logit[T] = mfma(At, Bl, logit[T]);
+            for (int T = 0; T < 8; ++T) {
+              const half8 At = tile1(x, T);
+              acc[T] = mfma(At, Bh, acc[T]);
+              acc[T] = mfma(At, Bl, acc[T]);
+            }
           }
         }
-      }
+      };
+      sketch(0, NKI / 2, logit);
+      sketch(NKI / 2, NKS / 2, logit_o);
       // estimator: nu_t * (2 <Sq, bits> - sum Sq); the norms of tokens 16 i + 4 a + e sit at 32 a + 4 i + e
       const uint8_t* nb = page + g.off_norm + 64 * a;
+      const uint8_t* nbo = page + g.off_norm_o + 64 * a;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const u32x4 nw = ld16(nb + 16 * qd);
+        const u32x4 nwo = A.qjl_mo ? ld16(nbo + 16 * qd) : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
           const int i = 2 * qd + ii;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t w = rd(nw, 2 * ii + (e >> 1));
-            const uint16_t hb = (uint16_t)(w >> (16 * (e & 1)));
-            _Float16 hv;
+            const uint32_t w = rd(nw, 2 * ii + (e >> 1)), wo = rd(nwo, 2 * ii + (e >> 1));
+            const uint16_t hb = (uint16_t)(w >> (16 * (e & 1))), hbo = (uint16_t)(wo >> (16 * (e & 1)));
+            _Float16 hv, hvo;
             __builtin_memcpy(&hv, &hb, 2);
-            logit[i][e] = (float)hv * fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum);
+            __builtin_memcpy(&hvo, &hbo, 2);
+            const float est_o = ratio * (float)hvo * fmaf(2.0f * tile_unscale(i), logit_o[i][e], -ssum_o);
+            logit[i][e] = fmaf((float)hv, fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum), est_o);
           }
         }
       }
@@ -298,19 +313,37 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, stage_buf(S));
 }
 
-// QJL projection: S q for every query head (float accumulation of bf16 products).
+// QJL projection: S q for every query head (float accumulation of bf16
+// products), m + mo values per head. With the outlier split the first m rows
+// see q's normal channels and the mo outlier-instance rows its outlier
+// channels (the head's record in mask; without pages there is no record and
+// the values are not read).
 __global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, const uint16_t* S, float* sq, int m,
-                                                          int n_rows) {
+                                                          int mo, const uint8_t* mask, int n_rows, int n_q_heads,
+                                                          int group) {
   const int row = blockIdx.x;          // (b, hq)
   if (row >= n_rows) return;
-  __shared__ float qs[D];
-  if (threadIdx.x < D) qs[threadIdx.x] = bf16_to_f32(q[(int64_t)row * D + threadIdx.x]);
+  __shared__ float qs[2][D];           // normal / outlier channels of q
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    const float x = bf16_to_f32(q[(int64_t)row * D + d]);
+    bool outlier = false;
+    if (mo > 0 && mask != nullptr) {
+      const int b = row / n_q_heads, kvh = (row - b * n_q_heads) / group;
+      const uint8_t* rec = mask + ((int64_t)b * (n_q_heads / group) + kvh) * QJL_RECORD;
+      outlier = (rec[d >> 3] >> (d & 7)) & 1;
+    }
+    qs[0][d] = outlier ? 0.f : x;
+    qs[1][d] = outlier ? x : 0.f;
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+  const int mt = m + mo;
+  for (int i = threadIdx.x; i < mt; i += blockDim.x) {
     const uint16_t* srow = S + (int64_t)i * D;
+    const float* qv = qs[i < m ? 0 : 1];
     float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(bf16_to_f32(srow[d]), qs[d], acc);
-    sq[(int64_t)row * m + i] = acc;
+    for (int d = 0; d < D; ++d) acc = fmaf(bf16_to_f32(srow[d]), qv[d], acc);
+    sq[(int64_t)row * mt + i] = acc;
   }
 }
 
@@ -364,7 +397,7 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
   if (n_parts > 0) {
     if (key_mode == KVQ_KEY_QJL) {
       hipLaunchKernelGGL(qjl_project_kernel, dim3(rows), dim3(256), 0, s, a.q, qjl_s, const_cast<float*>(a.sq),
-                         a.qjl_m, rows);
+                         a.qjl_m, a.qjl_mo, a.mask, rows, a.n_q_heads, g);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

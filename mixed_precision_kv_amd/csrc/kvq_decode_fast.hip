@@ -759,7 +759,7 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
     }
     return true;
   }
-  if (a.qjl_m != 256) return false;
+  if (a.qjl_m != 256 || a.qjl_mo != 0) return false;   // the outlier split runs on the generic kernel
   if (a.table) {
     if (g == 4) launch1(decode_qjl_fast<4, true>, a, s);
     else launch1(decode_qjl_fast<8, true>, a, s);

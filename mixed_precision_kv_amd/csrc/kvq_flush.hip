@@ -619,6 +619,7 @@ struct QPartSmem {
   float snorm[64];
   float knorm[PAGE];
   double ksq[PAGE];
+  double ksq_o[PAGE];           // outlier split: squared norm over the outlier channels
 };
 
 // Key part P: sketch rows 64 P .. 64 P + 63 (fragment pair P of the sign
@@ -626,14 +627,33 @@ struct QPartSmem {
 // MFMA (exact products, float accumulation) and is accepted when |dot| >
 // 2^-16 ||S_i|| ||k_t||, which exceeds the float summation error bound;
 // otherwise the dot product is recomputed in double.
-__device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int64_t row0, int P, QPartSmem& S) {
-  const QjlGeo g = qjl_geo(A.qjl_m);
-  stage_rows<64>(S.srow, A.qjl_s, 64 * P);    // S is [m][128] bf16
+// Outlier split (QJL outlier handling): parts of the normal instance (rows
+// below qjl_m) zero the head's outlier columns of their S rows and parts of
+// the outlier instance the other columns, so each dot product runs over its
+// instance's channels only; part 0 writes ||k_normal|| and ||k_outlier||.
+__device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const FlushArgs& A, uint8_t* page, int64_t head,
+                                                                         int64_t row0, int P, QPartSmem& S) {
+  const QjlGeo g = qjl_geo(A.qjl_m, A.qjl_mo);
+  const bool split = A.qjl_mo > 0;
+  uint32_t om[4] = {0u, 0u, 0u, 0u};          // outlier channel bits
+  if (split) {
+    const uint8_t* rec = A.mask + head * QJL_RECORD;
+    for (int k = 0; k < QJL_RECORD; ++k) om[k >> 2] |= (uint32_t)rec[k] << (8 * (k & 3));
+  }
+  stage_rows<64>(S.srow, A.qjl_s, 64 * P);    // S is [m + mo][128] bf16
   stage_rows<PAGE>(S.tile, A.k_src, row0);
   __syncthreads();
+  if (split) {
+    const uint32_t outlier_rows = 64 * P >= A.qjl_m ? 1u : 0u;
+    for (int i = threadIdx.x; i < 64 * D; i += blockDim.x) {
+      const int d = i & (D - 1);
+      if (((om[d >> 5] >> (d & 31)) & 1u) != outlier_rows) S.srow[i] = 0;
+    }
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < 64 + PAGE; i += blockDim.x) {
     const uint16_t* row = i < 64 ? S.srow + i * D : S.tile + (i - 64) * D;
-    double acc = 0.0;
+    double acc = 0.0, acc_o = 0.0;
     bool bad = false;
     for (int c = 0; c < D / 8; ++c) {
       const uint4 w8 = reinterpret_cast<const uint4*>(row)[c];
@@ -643,15 +663,18 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
         const uint16_t v = (uint16_t)(wv[k >> 1] >> (16 * (k & 1)));
         if (bf16_exp_field(v) == 0xFF) bad = true;
         const double x = bf16_to_f64(v);
-        acc = fma(x, x, acc);
+        const int d = 8 * c + k;
+        if ((om[d >> 5] >> (d & 31)) & 1u) acc_o = fma(x, x, acc_o);
+        else acc = fma(x, x, acc);
       }
     }
     if (bad) atomicOr(A.flags, KVQ_FLAG_NONFINITE);
     if (i < 64) {
-      S.snorm[i] = (float)sqrt(acc);
-    } else {
-      S.knorm[i - 64] = (float)sqrt(acc);
+      S.snorm[i] = (float)sqrt(acc + acc_o);
+    } else {   // acc: the normal channels (every channel without the split)
+      S.knorm[i - 64] = (float)sqrt(acc + acc_o);
       S.ksq[i - 64] = acc;
+      S.ksq_o[i - 64] = acc_o;
     }
   }
   __syncthreads();
@@ -672,7 +695,7 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
         bool pos;
         if (fabsf(dot) > 0x1.0p-16f * S.snorm[il] * S.knorm[t]) {
           pos = dot >= 0.f;
-        } else if (S.ksq[t] == 0.0) {    // k = 0: the dot product is exactly 0
+        } else if (S.ksq[t] + S.ksq_o[t] == 0.0) {    // k = 0: the dot product is exactly 0
           pos = true;
         } else {
           double x = 0.0;
@@ -699,13 +722,15 @@ __device__ __attribute__((always_inline)) inline void flush_qjl_key_part(const F
   }
   if (P == 0 && threadIdx.x < 64) {   // norms: position 32 a + 4 i + e holds token 16 i + 4 a + e
     const int qd = threadIdx.x >> 2, w = threadIdx.x & 3;
-    uint16_t v[2];
+    uint16_t v[2], vo[2];
     for (int k = 0; k < 2; ++k) {
       const int pos = 8 * qd + 2 * w + k;
       const int aa = pos >> 5, i = (pos >> 2) & 7, e = pos & 3;
       v[k] = sqrt_to_f16_rne(S.ksq[16 * i + 4 * aa + e]);
+      vo[k] = sqrt_to_f16_rne(S.ksq_o[16 * i + 4 * aa + e]);
     }
     store4(page + g.off_norm + 16 * qd + 4 * w, (uint32_t)v[0] | ((uint32_t)v[1] << 16));
+    if (split) store4(page + g.off_norm_o + 16 * qd + 4 * w, (uint32_t)vo[0] | ((uint32_t)vo[1] << 16));
   }
 }
 
@@ -766,9 +791,9 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
       VPartSmem v;
       QPartSmem q;
     } S;
-    const QjlGeo g = qjl_geo(A.qjl_m);
+    const QjlGeo g = qjl_geo(A.qjl_m, A.qjl_mo);
     if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
-    else flush_qjl_key_part(A, page, row0, part - V_PARTS, S.q);
+    else flush_qjl_key_part(A, page, head, row0, part - V_PARTS, S.q);
   }
 }
 
@@ -802,7 +827,7 @@ __global__ __launch_bounds__(256) void merge_flush_kernel(FlushArgs A, int parts
 static int flush_parts(int key_mode, const FlushArgs& a) {
   if (key_mode == KVQ_KEY_MIXKVQ) return V_PARTS + max(1, (mix_geo(a.n16, a.n4).F + 3) / 4);   // part 0 also writes the BF16 rows
   if (key_mode == KVQ_KEY_PNMIX) return V_PARTS + 2;
-  return V_PARTS + a.qjl_m / 64;
+  return V_PARTS + (a.qjl_m + a.qjl_mo) / 64;
 }
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream) {

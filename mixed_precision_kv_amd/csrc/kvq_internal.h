@@ -60,15 +60,18 @@ __host__ __device__ inline PnGeo pn_geo(int n_hi) {
   return g;
 }
 
-// QJL page: [sign bits (16*m) | norms (256) | V_CODES | V_META]
+// QJL page: [sign bits (16*(m + mo)) | norms (256) | outlier norms (256, mo > 0) | V_CODES | V_META];
+// with the outlier split (mo > 0) sign rows m .. m + mo - 1 are the outlier instance's
 struct QjlGeo {
-  int m, off_norm, off_v, used, stride;
+  int m, mo, off_norm, off_norm_o, off_v, used, stride;
 };
-__host__ __device__ inline QjlGeo qjl_geo(int m) {
+__host__ __device__ inline QjlGeo qjl_geo(int m, int mo = 0) {
   QjlGeo g;
   g.m = m;
-  g.off_norm = 16 * m;
-  g.off_v = g.off_norm + 256;
+  g.mo = mo;
+  g.off_norm = 16 * (m + mo);
+  g.off_norm_o = g.off_norm + 256;
+  g.off_v = g.off_norm + (mo ? 512 : 256);
   g.used = g.off_v + V_CODE_BYTES + V_META_BYTES;
   g.stride = round_up(g.used, 256);
   return g;
@@ -76,6 +79,7 @@ __host__ __device__ inline QjlGeo qjl_geo(int m) {
 
 constexpr int MIX_RECORD = 160;   // channel order u8[128] + 2-bit tiers [32]
 constexpr int PN_RECORD = 8;      // 64 pair bits
+constexpr int QJL_RECORD = 16;    // outlier-channel bits (QJL outlier split)
 
 // ---------------------------------------------------------------- number formats
 __host__ __device__ inline float bf16_to_f32(uint16_t b) {
@@ -183,6 +187,7 @@ struct FlushArgs {
   int n_hi;
   int pair_layout;
   int qjl_m;
+  int qjl_mo;                     // outlier-instance sketch rows (0: no outlier split)
   unsigned* flags;
   const void* q_accum;            // MixKVQ reselection: query sums (128-bit) per (head, channel); null: the mask records
   uint8_t* rec_out;               // with q_accum: record of logical page p of head h at rec_out + (h rec_stride + p) * 160
@@ -195,6 +200,7 @@ struct SelectArgs {
   int n_q_heads, n_kv_heads;
   int n16, n4;
   int n_hi_pairs, pair_layout;
+  int n_out;                      // QJL: outlier channels
   uint8_t* out;
 };
 struct DecodeArgs {
@@ -223,6 +229,7 @@ struct DecodeArgs {
   int n16, n4;
   int n_hi, pair_layout;
   int qjl_m;
+  int qjl_mo;                     // as FlushArgs::qjl_mo; the estimate's outlier term is scaled by qjl_m / qjl_mo
 };
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);

@@ -144,6 +144,48 @@ __global__ __launch_bounds__(1024) void select_pnmix_kernel(SelectArgs A) {
   }
 }
 
+// ------------------------------------------------------------------ QJL outlier channels
+// QJL outlier handling (Figure 2 orders channels by their mean magnitude
+// over tokens): channels ranked by the exact sum of psi(|K_{t,d}|) over the
+// prompt's Key tokens, ties to the lower channel; the n_out largest are the
+// head's outlier channels, written as a 128-bit record (bit d % 8 of byte d / 8).
+__global__ __launch_bounds__(1024) void select_qjl_outliers_kernel(SelectArgs A) {
+  __shared__ u128 part[16][D];
+  __shared__ u128 sum_s[D];
+  __shared__ uint8_t out_s[D];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int j = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  u128 s0 = 0, s1 = 0;
+  for (int64_t t = rl; t < A.l_k; t += 16) {
+    const uint16_t* row = A.k + (((int64_t)b * A.n_kv_heads + kvh) * A.k_stride + t) * D;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[j];
+    s0 += psi_bf16((uint16_t)(w & 0x7FFF));
+    s1 += psi_bf16((uint16_t)((w >> 16) & 0x7FFF));
+  }
+  part[rl][2 * j] = s0;
+  part[rl][2 * j + 1] = s1;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    u128 s = 0;
+    for (int r = 0; r < 16; ++r) s += part[r][threadIdx.x];
+    sum_s[threadIdx.x] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    const u128 me = sum_s[d];
+    int rank = 0;
+    for (int o = 0; o < D; ++o) rank += (sum_s[o] > me) || (sum_s[o] == me && o < d);
+    out_s[d] = rank < A.n_out;
+  }
+  __syncthreads();
+  if (threadIdx.x < QJL_RECORD) {
+    uint8_t byte = 0;
+    for (int k = 0; k < 8; ++k) byte |= out_s[8 * threadIdx.x + k] << k;
+    A.out[((int64_t)b * A.n_kv_heads + kvh) * QJL_RECORD + threadIdx.x] = byte;
+  }
+}
+
 // ------------------------------------------------------------------ query accumulator
 // acc[(b Hkv + h) D + d] += sum of psi(|q|) over the l_q query rows of every
 // query head of the group: the running query-magnitude accumulator of the
@@ -184,8 +226,10 @@ hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream
   dim3 grid(a.n_kv_heads, batch);
   if (key_mode == KVQ_KEY_MIXKVQ)
     hipLaunchKernelGGL(select_mixkvq_kernel, grid, dim3(1024), 0, stream, a);
-  else
+  else if (key_mode == KVQ_KEY_PNMIX)
     hipLaunchKernelGGL(select_pnmix_kernel, grid, dim3(1024), 0, stream, a);
+  else
+    hipLaunchKernelGGL(select_qjl_outliers_kernel, grid, dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

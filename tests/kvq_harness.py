@@ -13,6 +13,7 @@ import kvq_synth as synth
 import mixed_precision_kv_amd as kvq
 from oracle import attention as oatt
 from oracle import flush as oflush
+from oracle import qjl as oqjl
 from oracle import select as osel
 
 D = 128
@@ -31,7 +32,8 @@ class Pipeline:
         self.cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, self.max_pages,
                                    n_bf16=w.n_bf16, n_u4=w.n_u4,
                                    pair_layout=kvq.KVQ_PAIR_HALF_SPLIT if pair_layout == "half" else kvq.KVQ_PAIR_ADJACENT,
-                                   n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m)
+                                   n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m,
+                                   qjl_outliers=w.qjl_outliers, qjl_m_out=w.qjl_m_out)
         self.page_bytes = kvq.kvq_page_bytes(self.cfg)
         self.mask_bytes = kvq.kvq_mask_bytes(self.cfg)
         q, k, v = synth.prefill(w, device)
@@ -67,6 +69,8 @@ class Pipeline:
                                     w.n_pages * 128, self.mask, k_stride=self.L)
         elif w.key_mode == synth.PNMIX:
             kvq.kvq_select_channels(self.cfg, self.q_pre, self.q_pre.shape[2], self.k_pre, self.L, self.mask)
+        elif w.qjl_outliers:   # QJL outlier channels from the prompt's Keys
+            kvq.kvq_select_channels(self.cfg, None, 0, self.k_pre, self.L, self.mask)
 
     def flush_prefill(self):
         w = self.w
@@ -113,6 +117,10 @@ class Pipeline:
         base = (b * self.w.n_kv_heads + h) * mb
         return self.mask[base: base + mb].cpu().numpy()
 
+    def record(self, b, h):
+        """The GPU's selection record of (b, h), None where the mode has none."""
+        return self.gpu_record(b, h) if self.mask_bytes else None
+
     def bits(self, t):
         return synth.bf16_bits(t)
 
@@ -120,6 +128,8 @@ class Pipeline:
     def oracle_record(self, b, h):
         w = self.w
         g = self.g
+        if w.key_mode == synth.QJL:
+            return oqjl.outlier_record(oqjl.outlier_mask(self.bits(self.k_pre[b, h]), w.qjl_outliers))
         qb = self.bits(self.q_pre[b, h * g:(h + 1) * g])
         if w.key_mode == synth.MIXKVQ:
             kb = self.bits(self.k_pre[b, h, w.n_sink: w.n_sink + w.n_pages * 128])
@@ -133,10 +143,18 @@ class Pipeline:
         t0 = w.n_sink + 128 * p
         kb = self.bits(self.k_pre[b, h, t0:t0 + 128])
         vb = self.bits(self.v_pre[b, h, t0:t0 + 128])
+        return self.oracle_flush(kb, vb, record)
+
+    def oracle_flush(self, kb, vb, record):
+        """The oracle's page of 128 tokens (bf16 bits) under a selection record."""
+        w = self.w
         if w.key_mode == synth.MIXKVQ:
             return oflush.flush_mixkvq_page(kb, vb, record[:128], w.n_bf16, w.n_u4)
         if w.key_mode == synth.PNMIX:
             return oflush.flush_pnmix_page(kb, vb, osel.hi_channels_from_record(record, self.pair_layout))
+        if w.qjl_outliers:
+            return oflush.flush_qjl_page(kb, vb, self.bits(self.S), m=w.qjl_m,
+                                         outl=oqjl.outlier_mask_from_record(record))
         return oflush.flush_qjl_page(kb, vb, self.bits(self.S))
 
     def oracle_decode(self, b, h, pages, record, n_resid=None):
@@ -147,6 +165,8 @@ class Pipeline:
         kw = dict(n16=w.n_bf16, n4=w.n_u4, perm=None if record is None else record[:128],
                   mask_rec=record, pair_layout=self.pair_layout,
                   s_bits=None if self.S is None else self.bits(self.S))
+        if w.qjl_outliers:
+            kw.update(qjl_m=w.qjl_m, outl=oqjl.outlier_mask_from_record(record), mask_rec=None)
         if w.n_sink:
             kw["sink_k"] = self.bits(self.k_pre[b, h, :w.n_sink])
             kw["sink_v"] = self.bits(self.v_pre[b, h, :w.n_sink])

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(kvq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 2
+    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 3
     assert kvq.kvq_status_string(0) == "ok"
 
 
@@ -55,6 +55,31 @@ def test_pnmix_qjl_page_bytes(lib):
     cfg = kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 4, qjl_m=256)
     assert kvq.kvq_page_bytes(cfg) == layout.qjl_geometry(256)["stride"] == 10496
     assert kvq.kvq_mask_bytes(cfg) == 0
+
+
+def test_qjl_outlier_split_config(lib):
+    """QJL outlier split: page geometry and record size as the oracle packs
+    them, storage by region, and the configurations it rejects."""
+    cfg = kvq.make_config(kvq.KVQ_KEY_QJL, 2, 8, 2, 4, qjl_m=256, qjl_outliers=8, qjl_m_out=64)
+    g = layout.qjl_geometry(256, 64)
+    assert kvq.kvq_page_bytes(cfg) == g["stride"] and g["used"] == 16 * 320 + 512 + 6144
+    assert kvq.kvq_mask_bytes(cfg) == 16
+    st = kvq.kvq_storage_bytes(cfg, 1024, 0, 0)
+    H, T = 4, 1024
+    assert st["key_codes"] == H * T * 320 // 8 and st["key_meta"] == H * T * 4 and st["selection"] == H * 16
+    assert abs(st["key_bits_per_element"] - (320 + 32) / 128) < 1e-12
+    for kw, status in ((dict(qjl_outliers=8, qjl_m_out=0), kvq.KVQ_INVALID_ARG),
+                       (dict(qjl_outliers=0, qjl_m_out=64), kvq.KVQ_INVALID_ARG),
+                       (dict(qjl_outliers=65, qjl_m_out=64), kvq.KVQ_INVALID_ARG),
+                       (dict(qjl_outliers=8, qjl_m_out=96), kvq.KVQ_INVALID_ARG),
+                       (dict(qjl_outliers=8, qjl_m_out=192), kvq.KVQ_UNSUPPORTED)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_page_bytes(kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 4, qjl_m=256, **kw))
+        assert e.value.status == status, kw
+    # selection: plain QJL has none; the split needs K and a record buffer (rejected before launch)
+    plain = kvq.make_config(kvq.KVQ_KEY_QJL, 1, 4, 1, 4, qjl_m=256)
+    assert lib.kvq_select_channels(ctypes.byref(plain), None, 0, 0, None, 10, 10, None, None) == kvq.KVQ_UNSUPPORTED
+    assert lib.kvq_select_channels(ctypes.byref(cfg), None, 0, 0, None, 10, 10, None, None) == kvq.KVQ_INVALID_ARG
 
 
 def test_storage_matches_oracle(lib):
@@ -88,7 +113,8 @@ def test_validation_rejects_before_launch(lib):
         kvq.kvq_page_bytes(bad)
     assert e.value.status == kvq.KVQ_UNSUPPORTED
     for field, value, status in (("n_q_heads", 6, kvq.KVQ_UNSUPPORTED), ("n_kv_heads", 3, kvq.KVQ_INVALID_ARG),
-                                 ("abi_version", 3, kvq.KVQ_INVALID_ARG),
+                                 ("abi_version", 4, kvq.KVQ_INVALID_ARG), ("reserved", 1, kvq.KVQ_INVALID_ARG),
+                                 ("qjl_outliers", 8, kvq.KVQ_INVALID_ARG),
                                  ("n_bf16", 120, kvq.KVQ_INVALID_ARG), ("key_mode", 7, kvq.KVQ_INVALID_ARG)):
         c = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=16, n_u4=32)
         setattr(c, field, value)

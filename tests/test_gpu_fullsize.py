@@ -20,7 +20,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.timeout(600)]
 
 TOL = 2e-3
-NAMES = ["llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k"]
+NAMES = ["llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"]
 
 
 def slices(w):
@@ -34,7 +34,7 @@ def oracle_pages(p, b, h):
     GPU stored (the record itself is checked separately), cached per slice."""
     cache = p.__dict__.setdefault("_oracle_pages", {})
     if (b, h) not in cache:
-        rec = p.gpu_record(b, h) if p.w.key_mode != synth.QJL else None
+        rec = p.record(b, h)
         cache[(b, h)] = [p.oracle_page(b, h, pg, rec) for pg in range(p.w.n_pages)]
     return cache[(b, h)]
 
@@ -71,8 +71,8 @@ def test_fullsize_select_and_pages(full):
 def test_fullsize_records(full):
     name, p, _ = full
     w = p.w
-    if w.key_mode == synth.QJL:
-        pytest.skip("QJL has no selection")
+    if not p.mask_bytes:
+        pytest.skip("plain QJL has no selection")
     # the prefill queries were released after selection: regenerate them
     q_pre, _, _ = synth.prefill(w, "cuda")
     p.q_pre = q_pre
@@ -93,7 +93,7 @@ def test_fullsize_decode(full):
     g = p.g
     for b, h in slices(w):
         print(f"[decode] {name} b{b} h{h}", flush=True)
-        rec = p.gpu_record(b, h) if w.key_mode != synth.QJL else None
+        rec = p.record(b, h)
         ref, _ = p.oracle_decode(b, h, oracle_pages(p, b, h), rec)
         err = rel_err(o[b, h * g:(h + 1) * g], ref)
         print(f"[decode] {name} b{b} h{h}: worst relative error {err.max():.3e}")
@@ -103,16 +103,9 @@ def test_fullsize_decode(full):
 def test_fullsize_residual_flush(full):
     name, p, _ = full
     w = p.w
-    from oracle import flush as oflush
-    from oracle import select as osel
     for b, h in slices(w):
         kb, vb = p.bits(p.resid_k[b, h]), p.bits(p.resid_v[b, h])
-        if w.key_mode == synth.MIXKVQ:
-            ref = oflush.flush_mixkvq_page(kb, vb, p.gpu_record(b, h)[:128], w.n_bf16, w.n_u4)
-        elif w.key_mode == synth.PNMIX:
-            ref = oflush.flush_pnmix_page(kb, vb, osel.hi_channels_from_record(p.gpu_record(b, h)))
-        else:
-            ref = oflush.flush_qjl_page(kb, vb, p.bits(p.S))
+        ref = p.oracle_flush(kb, vb, p.record(b, h))
         assert np.array_equal(p.gpu_page(b, h, w.n_pages), ref), (name, b, h)
 
 
@@ -130,7 +123,7 @@ def test_fullsize_fidelity(full):
     name, p, out = full
     w = p.w
     b, h = slices(w)[0]
-    rec = p.gpu_record(b, h) if w.key_mode != synth.QJL else None
+    rec = p.record(b, h)
     _, probs_q = p.oracle_decode(b, h, oracle_pages(p, b, h), rec)
     out_r, probs_r = p.reference_probs(b, h, w.n_pages, w.n_resid)
     kl = float(np.mean([oatt.kl_divergence(pr, pq) for pr, pq in zip(probs_r, probs_q)]))
