@@ -64,8 +64,13 @@ def logical_page_bytes(w) -> int:
         n_hi = 2 * w.n_hi_pairs
         k = 128 * 128 // 8 + 128 * n_hi * 2 // 8 + 128 * 2 * 2
     else:
-        k = 128 * w.qjl_m // 8 + 128 * 2
+        # sign bits of both instances; one binary16 norm per instance
+        k = 128 * (w.qjl_m + w.qjl_m_out) // 8 + 128 * 2 * (2 if w.qjl_m_out else 1)
     return k + v
+
+
+def record_bytes(w) -> int:
+    return {0: 160, 1: 8, 2: 16 if w.qjl_outliers else 0}[w.key_mode]
 
 
 def decode_bytes(w) -> int:
@@ -73,17 +78,17 @@ def decode_bytes(w) -> int:
     residual, the selection record, the query and the float32 output."""
     heads = w.batch * w.n_kv_heads
     g = w.group
-    rec = {0: 160, 1: 8, 2: 0}[w.key_mode]
+    rec = record_bytes(w)
     per_head = (w.n_pages * logical_page_bytes(w) + (w.n_sink + w.n_resid) * 128 * 2 * 2 + rec
                 + g * 128 * 2 + g * 128 * 4)
-    extra = 256 * 128 * 2 if w.key_mode == 2 else 0
+    extra = (w.qjl_m + w.qjl_m_out) * 128 * 2 if w.key_mode == 2 else 0   # S
     return heads * per_head + extra
 
 
 def flush_bytes(w) -> int:
     """One 128-token flush: read K and V (bf16), read the record, write a page."""
     heads = w.batch * w.n_kv_heads
-    rec = {0: 160, 1: 8, 2: 0}[w.key_mode]
+    rec = record_bytes(w)
     return heads * (128 * 128 * 2 * 2 + rec + logical_page_bytes(w))
 
 
@@ -155,6 +160,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for >400 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="qwen32b_32k", help="extra decode-only workload ('' to skip)")
+    ap.add_argument("--no-qjl", action="store_true", help="skip the QJL decodes (plain and outlier split)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--decode-only", action="store_true", help="time the decode call only (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
@@ -177,7 +183,8 @@ class Rig:
         self.reselect = reselect
         self.cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, self.max_pages,
                                    n_bf16=w.n_bf16, n_u4=w.n_u4, n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m,
-                                   page_records=1 if reselect else 0)
+                                   page_records=1 if reselect else 0, qjl_outliers=w.qjl_outliers,
+                                   qjl_m_out=w.qjl_m_out)
         pb = kvq.kvq_page_bytes(self.cfg)
         H = w.batch * w.n_kv_heads
         L = w.prefill_tokens
@@ -193,6 +200,8 @@ class Rig:
                                     k_stride=L)
         elif w.key_mode == 1:
             kvq.kvq_select_channels(self.cfg, q, L, k, L, self.mask)
+        elif w.qjl_outliers:   # QJL outlier channels from the prompt's Keys
+            kvq.kvq_select_channels(self.cfg, None, 0, k, L, self.mask)
         del q
         arena = torch.zeros(H * self.max_pages * pb, dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -480,6 +489,21 @@ def main():
         del rig2
         torch.cuda.empty_cache()
 
+    # QJL at 32K context: the plain sketch and the outlier split (two sketch
+    # instances), decode calls over the resident cache
+    qjl = {}
+    if not args.no_qjl:
+        for name in ("qjl_32k", "qjl_outlier_32k"):
+            wq = synth.WORKLOADS[name]
+            print(f"[bench] {name}: {decode_bytes(wq) / 1e6:.1f} MB per decode", file=sys.stderr, flush=True)
+            rq = Rig(wq, 1, torch, kvq, synth)
+            kq = max(10, K // 2)
+            dq, _ = graph_time(torch, [lambda: rq.decode(0)] * kq, [lambda: rq.decode(0)] * 3)
+            qjl[name] = {"decode_ms": dq, "decode_GBps": decode_bytes(wq) / (dq * 1e-3) / 1e9,
+                         "bytes_per_decode": decode_bytes(wq), "page_bytes_logical": logical_page_bytes(wq)}
+            del rq
+            torch.cuda.empty_cache()
+
     # per-flush reselection (MixKVQ's running query accumulator; per-page
     # records read by the decode): the decode, the accumulation of the step's
     # query, the reselecting one-page flush, and the step of all three
@@ -542,6 +566,7 @@ def main():
                      "bytes_per_launch": dbytes},
         "secondary": extra,
         "reselect_per_flush": resel,
+        "qjl_decode": qjl,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -33,7 +33,7 @@ def check_decode(p, n_pages, n_resid, tag):
     g = p.g
     for b in range(p.w.batch):
         for h in range(p.w.n_kv_heads):
-            rec = p.gpu_record(b, h) if p.w.key_mode != synth.QJL else None
+            rec = p.record(b, h)
             pages = [p.oracle_page(b, h, pg, rec) for pg in range(n_pages)]
             ref, _ = p.oracle_decode(b, h, pages, rec, n_resid=n_resid)
             err = rel_err(out[b, h * g:(h + 1) * g], ref)
@@ -56,7 +56,7 @@ def generic_decode():
     os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
 
 
-@pytest.mark.parametrize("name", ["llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k"])
+@pytest.mark.parametrize("name", ["llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"])
 def test_generic_decode_matches_oracle_and_fast(name, generic_decode):
     base = synth.WORKLOADS[name]
     w = base.scaled(batch=1, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=3, n_resid=min(base.n_resid, 40),

@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a ROCm GPU")]
 
 
-@pytest.mark.parametrize("name", ["llama8b_8k", "pnmix_16k", "qjl_32k"])
+@pytest.mark.parametrize("name", ["llama8b_8k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"])
 def test_graph_replays_match_eager(name):
     base = synth.WORKLOADS[name]
     w = base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=5, n_resid=base.n_resid and 128,

@@ -51,7 +51,7 @@ def decode_into(p, arena, table, n_pages, n_resid, out):
                              table_stride=p.max_pages if table is not None else 0)
 
 
-@pytest.mark.parametrize("name", ["tiny_mixkvq", "llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k"])
+@pytest.mark.parametrize("name", ["tiny_mixkvq", "llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"])
 def test_paged_matches_contiguous(name):
     base = synth.WORKLOADS[name]
     w = base if name == "tiny_mixkvq" else base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=6,
@@ -84,7 +84,7 @@ def test_paged_matches_contiguous(name):
         os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
     o = out_g.cpu().numpy()
     b, hk = w.batch - 1, w.n_kv_heads - 1
-    rec = p.gpu_record(b, hk) if w.key_mode != synth.QJL else None
+    rec = p.record(b, hk)
     pages = [p.oracle_page(b, hk, pg, rec) for pg in range(w.n_pages)]
     ref, _ = p.oracle_decode(b, hk, pages, rec)
     assert np.all(rel_err(o[b, hk * p.g:(hk + 1) * p.g], ref) <= TOL)

@@ -63,7 +63,7 @@ def check_decode(p, n_pages, n_resid, tag):
             assert np.all(err <= TOL), (tag, b, h, err)
 
 
-@pytest.mark.parametrize("group,m,m_out", [(4, 256, 64), (8, 128, 128), (2, 192, 64)])
+@pytest.mark.parametrize("group,m,m_out", [(4, 256, 64), (8, 256, 64), (8, 128, 128), (2, 192, 64)])
 def test_split_select_flush_decode(group, m, m_out):
     w = small(group, m, m_out, seed=group)
     p = built(w)
