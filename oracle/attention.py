@@ -25,7 +25,7 @@ import numpy as np
 from . import layout
 from .numerics import bf16_to_f64, f16_to_f64
 from .quant import dequantize
-from .qjl import estimate_scores_split
+from .qjl import estimate_scores, estimate_scores_split
 from .select import hi_channels_from_record
 
 D = 128
@@ -69,7 +69,7 @@ def softmax_attend(logits: np.ndarray, values: np.ndarray):
     return p @ values, p
 
 
-def decode_kv_head(q_heads, K_q, V_q, scale, sink=None, resid=None, qjl=None):
+def decode_kv_head(q_heads, K_q, V_q, scale, sink=None, resid=None, qjl=None, with_logits=False):
     """Attention of the g query heads of one KV head.
 
     q_heads [g, D] float64; K_q/V_q [Tq, D] the dequantized page tokens
@@ -77,7 +77,8 @@ def decode_kv_head(q_heads, K_q, V_q, scale, sink=None, resid=None, qjl=None):
     norm bits [Tq]) supplies the estimator, or with the outlier split
     (S bits, m, outlier channels, sign bits, normal norms, outlier norms));
     sink/resid = (K, V) float64.
-    Returns (out [g, D], probs [g, T_total])."""
+    Returns (out [g, D], probs [g, T_total]), and the logits [g, T_total]
+    (scale included) with with_logits."""
     segs_k, segs_v, kinds = [], [], []
     if sink is not None and sink[0].shape[0]:
         segs_k.append(sink[0]); segs_v.append(sink[1]); kinds.append("exact")
@@ -86,27 +87,25 @@ def decode_kv_head(q_heads, K_q, V_q, scale, sink=None, resid=None, qjl=None):
     if resid is not None and resid[0].shape[0]:
         segs_k.append(resid[0]); segs_v.append(resid[1]); kinds.append("exact")
     values = np.concatenate(segs_v, axis=0) if segs_v else np.zeros((0, D))
-    outs, probs = [], []
+    outs, probs, logit_rows = [], [], []
     for q in q_heads:
         parts = []
         for kk, kind in zip(segs_k, kinds):
             if kind == "exact":
                 parts.append(kk @ q * scale)
-            else:
-                if len(qjl) == 6:
-                    s_bits, m, outl, bits, nu_i, nu_o = qjl
-                    parts.append(estimate_scores_split(q, s_bits, m, outl, bits, nu_i, nu_o) * scale)
-                    continue
+            elif len(qjl) == 6:          # QJL outlier split: two instances (outlier paragraph)
+                s_bits, m, outl, bits, nu_i, nu_o = qjl
+                parts.append(estimate_scores_split(q, s_bits, m, outl, bits, nu_i, nu_o) * scale)
+            else:                        # plain QJL, Definition 3.1 / Algorithm 1 EstimateScores
                 s_bits, bits, norms = qjl
-                S = bf16_to_f64(s_bits)
-                m = S.shape[0]
-                sq = S @ q
-                signs = 2.0 * bits.astype(np.float64) - 1.0
-                parts.append(math.sqrt(math.pi / 2) / m * f16_to_f64(norms) * (sq @ signs) * scale)
-        logits = np.concatenate(parts)
+                parts.append(estimate_scores(q, s_bits, bits, norms) * scale)
+        logits = np.concatenate(parts) if parts else np.zeros(0)
         o, p = softmax_attend(logits, values)
         outs.append(o)
         probs.append(p)
+        logit_rows.append(logits)
+    if with_logits:
+        return np.array(outs), np.array(probs), np.array(logit_rows)
     return np.array(outs), np.array(probs)
 
 
@@ -119,14 +118,14 @@ def kl_divergence(p_ref: np.ndarray, p_q: np.ndarray) -> float:
 def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0, perm=None,
                       mask_rec=None, pair_layout="half", s_bits=None,
                       sink_k=None, sink_v=None, resid_k=None, resid_v=None, page_perms=None,
-                      qjl_m=None, outl=None):
+                      qjl_m=None, outl=None, with_logits=False):
     """Decode for one (batch, KV head) from packed pages.
 
     q_bits_heads [g, D] bf16 bits; arena_pages: list of page byte arrays;
     sink_*/resid_* [n, D] bf16 bits (or None); page_perms: MixKVQ channel
     order of each page (per-flush reselection), else `perm` for every page;
     qjl_m / outl: the QJL outlier split (normal rows, outlier channels).
-    Returns (out [g, D], probs)."""
+    Returns (out [g, D], probs), and the logits with with_logits."""
     q = bf16_to_f64(q_bits_heads)
     Ks, Vs, bits_l, norms_l, norms_o = [], [], [], [], []
     split = key_mode == 2 and outl is not None
@@ -154,7 +153,7 @@ def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0
             qjl = (s_bits, qjl_m, outl, qjl[1], qjl[2], np.concatenate(norms_o))
     sink = None if sink_k is None else (bf16_to_f64(sink_k), bf16_to_f64(sink_v))
     resid = None if resid_k is None else (bf16_to_f64(resid_k), bf16_to_f64(resid_v))
-    return decode_kv_head(q, K_q, V_q, scale, sink=sink, resid=resid, qjl=qjl)
+    return decode_kv_head(q, K_q, V_q, scale, sink=sink, resid=resid, qjl=qjl, with_logits=with_logits)
 
 
 def reference_attention(q_bits_heads, k_bits, v_bits, scale):

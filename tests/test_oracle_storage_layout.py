@@ -13,6 +13,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 from oracle import cache, flush, layout, storage
 from oracle.quant import quantize_groups
@@ -54,15 +55,25 @@ def test_kivi_residual_trace():
     rows = cache.kivi_flash_trace(g["R"], g["G"], 9)
     for step, expect in g["table_rows"].items():
         assert list(rows[int(step) - 1][:4]) == expect
-    assert [r[1] for r in rows] == g["persisted_k_lengths_9_steps"]
-    assert [r[3] for r in rows] == g["persisted_v_lengths_9_steps"]
-    kc, vc = rows[8][4], rows[8][5]
+    assert [r.k_persist_full for r in rows] == g["persisted_k_lengths_9_steps"]
+    assert [r.v_persist_full for r in rows] == g["persisted_v_lengths_9_steps"]
+    kc, vc = rows[8].k_split, rows[8].v_split
     assert [len(kc[0]), len(kc[1])] == g["step9_key_split"]
     assert [len(vc[0]), len(vc[1])] == g["step9_value_split"]
     # mean persisted Key residual over full cycles is (R-1)/2
     R = 128
-    lens = [r[1] for r in cache.kivi_flash_trace(R, 32, 4 * R)]
+    trace = cache.kivi_flash_trace(R, 32, 4 * R)
+    lens = [r.k_persist_full for r in trace]
     assert Fraction(sum(lens), len(lens)) == Fraction(R - 1, 2)
+    # every step reads every token once, the Key history in whole segments of
+    # R and the Value window as the newest tokens
+    for t, r in enumerate(trace, start=1):
+        for q_ids, f_ids in (r.k_split, r.v_split):
+            assert list(q_ids) + list(f_ids) == list(range(1, t + 1))
+        assert len(r.k_split[0]) % R == 0 and 1 <= r.k_compute_full <= R
+        assert r.v_compute_full == min(t, R + 1)
+    with pytest.raises(ValueError):
+        cache.kivi_flash_trace(6, 4, 3)
 
 
 def rand_bits(rng, shape, scale=1.0):
