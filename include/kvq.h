@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 #define KVQ_HEAD_DIM 128
 #define KVQ_PAGE_TOKENS 128
 #define KVQ_VALUE_GROUP 32
@@ -74,6 +74,16 @@ typedef enum kvq_key_mode {
   KVQ_KEY_PNMIX = 1,          /* RoPE-pair mask, 3-bit / 1-bit midpoint planes */
   KVQ_KEY_QJL = 2             /* 1-bit sign sketch sign(S k) plus ||k||_2 */
 } kvq_key_mode;
+
+typedef enum kvq_select_mode {
+  KVQ_SELECT_COUNT = 0,       /* MixKVQ tiers by rank: the n_bf16 most salient channels BF16, the next n_u4 UINT4 */
+  KVQ_SELECT_THRESHOLD = 1    /* MixKVQ tiers by the salience thresholds tau_bf16 / tau_u4 */
+} kvq_select_mode;
+
+typedef enum kvq_decode_path {
+  KVQ_DECODE_AUTO = 0,        /* the software-pipelined kernel where one covers the shape, else the generic one */
+  KVQ_DECODE_GENERIC = 1      /* always the generic kernel (same results within the decode bound) */
+} kvq_decode_path;
 
 typedef enum kvq_pair_layout {
   KVQ_PAIR_HALF_SPLIT = 0,    /* RoPE pair i = (i, i + 64): Llama-style rotate-half */
@@ -108,7 +118,14 @@ typedef struct kvq_config {
                                  found by kvq_select_channels, sketched by a second instance */
   int32_t qjl_m_out;          /* QJL with outliers: that instance's sketch rows, a multiple of 64,
                                  qjl_m + qjl_m_out <= 384 (else 0) */
+  int32_t select_mode;        /* MixKVQ: kvq_select_mode. With KVQ_SELECT_THRESHOLD every (batch, kv head)
+                                 gets its own tier counts from its selection record, and n_bf16 / n_u4 are the
+                                 most BF16 / UINT4 channels a head may hold (they fix the page stride) */
+  int32_t decode_path;        /* kvq_decode_path */
   int32_t reserved;           /* must be zero */
+  double tau_bf16;            /* THRESHOLD: A_d > tau_bf16 -> BF16 */
+  double tau_u4;              /* THRESHOLD: tau_u4 < A_d <= tau_bf16 -> UINT4, else UINT2; finite, and 0 or
+                                 2^-900 <= |tau| <= 2^900 */
 } kvq_config;
 
 /* Persistent cache bytes of one layer for all (batch, kv head) pairs, by
@@ -134,7 +151,11 @@ int32_t kvq_abi_version(void);
 const char* kvq_status_string(kvq_status status);
 
 /* Byte stride of one page in the arena (a multiple of 256) for this
- * configuration. The arena is [batch][n_kv_heads][max_pages] pages. */
+ * configuration. The arena is [batch][n_kv_heads][max_pages] pages. With
+ * KVQ_SELECT_THRESHOLD it is the largest page any tier counts within the
+ * capacities n_bf16 / n_u4 need; a head's page then uses the first bytes of
+ * its slot, as its own counts lay them out, and the bytes after them are not
+ * written. */
 kvq_status kvq_page_bytes(const kvq_config* cfg, size_t* bytes);
 
 /* Bytes of the selection record of one (batch, kv head); the mask buffer of
@@ -152,7 +173,9 @@ kvq_status kvq_workspace_bytes(const kvq_config* cfg, int32_t n_pages, size_t* b
 /* Host-only and pure: persistent bytes of a cache holding n_quant_tokens
  * quantized tokens (a multiple of 128), n_resid residual and n_sink sink
  * tokens per (batch, kv head). KIVI blog section 7; PN-Mix storage(). With
- * cfg->page_records the MixKVQ selection counts one record per page. */
+ * cfg->page_records the MixKVQ selection counts one record per page. With
+ * KVQ_SELECT_THRESHOLD the counts are the data's, not the configuration's:
+ * the breakdown is that of heads filled to the capacities n_bf16 / n_u4. */
 kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant_tokens, int32_t n_resid,
                              int32_t n_sink, kvq_storage_breakdown* out);
 
@@ -161,7 +184,17 @@ kvq_status kvq_storage_bytes(const kvq_config* cfg, int64_t n_quant_tokens, int3
  *    SQ_d = sum of |Q| over the l_q prefill queries of all query heads that
  *    share the kv head, range_d = max - min of K over the l_k Key tokens to be
  *    quantized; channels ranked by SQ_d * range_d (ties: lower d first);
- *    the n_bf16 best are BF16, the next n_u4 UINT4, the rest UINT2.
+ *    KVQ_SELECT_COUNT: the n_bf16 best are BF16, the next n_u4 UINT4, the
+ *    rest UINT2.
+ *    KVQ_SELECT_THRESHOLD (the three-tier rule with Algorithm 1's tau_BF16,
+ *    tau_UINT4): the salience A_d = I_d * S_d with I_d = SQ_d / (g * l_q) (the
+ *    mean |Q| over the group's prefill queries) and S_d = range_d / (2^B - 1),
+ *    B = 2, is compared exactly with the thresholds: A_d > tau_bf16 is BF16,
+ *    tau_u4 < A_d <= tau_bf16 UINT4 (empty when tau_bf16 <= tau_u4), the
+ *    rest UINT2. A tier that receives more channels than its capacity
+ *    (n_bf16, n_u4) keeps the highest-ranked ones and passes the rest down
+ *    one tier. The tiers are contiguous in the ranking, so the record has the
+ *    same form, with the head's own counts in its tier codes.
  *  PN-Mix (Eq.6): pairs ranked by sum_t ||q pair|| * sum_s ||k pair||
  *    (query sum over the whole GQA group), top n_hi_pairs kept at 3 bits.
  *  QJL with qjl_outliers > 0 (outlier handling of the QJL page, Figure 2):
@@ -207,7 +240,9 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
  * Returns KVQ_CAPACITY if first_page + n_pages exceeds max_pages (no table)
  * or table_stride (with a table). */
 /* (With cfg->page_records set, kvq_flush_quantize and kvq_decode_attention_flush
- * return KVQ_UNSUPPORTED: the records then come from kvq_flush_reselect.) */
+ * return KVQ_UNSUPPORTED: the records then come from kvq_flush_reselect.
+ * With KVQ_SELECT_THRESHOLD every page of a head is laid out by the tier
+ * counts its record holds.) */
 kvq_status kvq_flush_quantize(const kvq_config* cfg, const void* k_src, const void* v_src,
                               int64_t src_stride, int32_t n_pages, const void* mask,
                               const void* qjl_s, void* page_arena, const int32_t* page_table,
@@ -238,8 +273,9 @@ kvq_status kvq_accumulate_query(const kvq_config* cfg, const void* q, int64_t l_
  * and the page is packed with that order. The page's 160-byte record goes to
  * page_records + ((b*Hkv + h)*rec_stride + p)*160 for logical page p, with
  * rec_stride = table_stride with a page table, else max_pages.
- * Requires cfg->page_records == 1 (MixKVQ only); other arguments as
- * kvq_flush_quantize. Keys must be finite for the ranking. */
+ * Requires cfg->page_records == 1 (MixKVQ only, KVQ_SELECT_COUNT: the
+ * accumulator keeps no row count for the mean |Q| a threshold needs); other
+ * arguments as kvq_flush_quantize. Keys must be finite for the ranking. */
 kvq_status kvq_flush_reselect(const kvq_config* cfg, const void* k_src, const void* v_src,
                               int64_t src_stride, int32_t n_pages, const void* q_accum,
                               void* page_records, void* page_arena, const int32_t* page_table,

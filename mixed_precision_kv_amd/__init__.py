@@ -15,10 +15,12 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_ABI_VERSION = 3
+KVQ_ABI_VERSION = 4
 KVQ_OK, KVQ_INVALID_ARG, KVQ_UNSUPPORTED, KVQ_WORKSPACE_TOO_SMALL, KVQ_CAPACITY, KVQ_HIP_ERROR = range(6)
 KVQ_KEY_MIXKVQ, KVQ_KEY_PNMIX, KVQ_KEY_QJL = 0, 1, 2
 KVQ_PAIR_HALF_SPLIT, KVQ_PAIR_ADJACENT = 0, 1
+KVQ_SELECT_COUNT, KVQ_SELECT_THRESHOLD = 0, 1
+KVQ_DECODE_AUTO, KVQ_DECODE_GENERIC = 0, 1
 KVQ_FLAG_NONFINITE, KVQ_FLAG_SPAN, KVQ_FLAG_MASK, KVQ_FLAG_RANGE, KVQ_FLAG_TABLE = 1, 2, 4, 8, 16
 
 EXPORTED = (
@@ -36,7 +38,8 @@ class KvqConfig(ctypes.Structure):
         ("max_pages", ctypes.c_int32), ("n_bf16", ctypes.c_int32), ("n_u4", ctypes.c_int32),
         ("pair_layout", ctypes.c_int32), ("n_hi_pairs", ctypes.c_int32), ("qjl_m", ctypes.c_int32),
         ("page_records", ctypes.c_int32), ("qjl_outliers", ctypes.c_int32),
-        ("qjl_m_out", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("qjl_m_out", ctypes.c_int32), ("select_mode", ctypes.c_int32), ("decode_path", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("tau_bf16", ctypes.c_double), ("tau_u4", ctypes.c_double),
     ]
 
 
@@ -92,7 +95,8 @@ def load(path: str = LIB_PATH):
 def make_config(key_mode: int, batch: int, n_q_heads: int, n_kv_heads: int, max_pages: int, *,
                 n_bf16: int = 0, n_u4: int = 0, pair_layout: int = KVQ_PAIR_HALF_SPLIT,
                 n_hi_pairs: int = 32, qjl_m: int = 256, head_dim: int = 128, page_records: int = 0,
-                qjl_outliers: int = 0, qjl_m_out: int = 0) -> KvqConfig:
+                qjl_outliers: int = 0, qjl_m_out: int = 0, select_mode: int = KVQ_SELECT_COUNT,
+                tau_bf16: float = 0.0, tau_u4: float = 0.0, decode_path: int = KVQ_DECODE_AUTO) -> KvqConfig:
     c = KvqConfig()
     c.abi_version = KVQ_ABI_VERSION
     c.key_mode = key_mode
@@ -102,6 +106,17 @@ def make_config(key_mode: int, batch: int, n_q_heads: int, n_kv_heads: int, max_
     c.pair_layout, c.n_hi_pairs, c.qjl_m = pair_layout, n_hi_pairs, qjl_m
     c.page_records = page_records
     c.qjl_outliers, c.qjl_m_out = qjl_outliers, qjl_m_out
+    c.select_mode, c.tau_bf16, c.tau_u4 = select_mode, tau_bf16, tau_u4
+    c.decode_path = decode_path
+    return c
+
+
+def with_fields(cfg: KvqConfig, **kw) -> KvqConfig:
+    """A copy of cfg with some fields replaced (e.g. decode_path)."""
+    c = KvqConfig()
+    ctypes.pointer(c)[0] = cfg
+    for k, v in kw.items():
+        setattr(c, k, v)
     return c
 
 

@@ -2,9 +2,13 @@
 // and kernel dispatch. Every entry point checks its arguments before it
 // launches anything; on error nothing is launched and no output is touched.
 #include <math.h>
+#include <stddef.h>
 #include <string.h>
 
 #include "kvq_internal.h"
+
+// the layout every binding mirrors (18 int32, then the two thresholds)
+static_assert(sizeof(kvq_config) == 88 && offsetof(kvq_config, tau_bf16) == 72, "kvq_config layout");
 
 namespace kvq {
 
@@ -17,6 +21,14 @@ static kvq_status check_config(const kvq_config* c) {
   if (c->key_mode != KVQ_KEY_QJL && (c->qjl_outliers != 0 || c->qjl_m_out != 0)) return KVQ_INVALID_ARG;
   if (c->page_records != 0 && c->page_records != 1) return KVQ_INVALID_ARG;
   if (c->page_records && c->key_mode != KVQ_KEY_MIXKVQ) return KVQ_UNSUPPORTED;
+  if (c->decode_path != KVQ_DECODE_AUTO && c->decode_path != KVQ_DECODE_GENERIC) return KVQ_INVALID_ARG;
+  if (c->select_mode != KVQ_SELECT_COUNT && c->select_mode != KVQ_SELECT_THRESHOLD) return KVQ_INVALID_ARG;
+  if (c->select_mode == KVQ_SELECT_THRESHOLD) {
+    if (c->key_mode != KVQ_KEY_MIXKVQ) return KVQ_INVALID_ARG;
+    for (double t : {c->tau_bf16, c->tau_u4})   // the exact comparison's domain
+      if (!isfinite(t) || (t != 0.0 && (fabs(t) < 0x1p-900 || fabs(t) > 0x1p900))) return KVQ_INVALID_ARG;
+    if (c->page_records) return KVQ_UNSUPPORTED;   // the query accumulator keeps no row count for the mean
+  }
   if (c->head_dim != D) return c->head_dim > 0 ? KVQ_UNSUPPORTED : KVQ_INVALID_ARG;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_pages < 1) return KVQ_INVALID_ARG;
   if ((int64_t)c->batch * c->n_kv_heads * c->max_pages > INT32_MAX) return KVQ_INVALID_ARG;   // pool indices are int32
@@ -47,8 +59,18 @@ static kvq_status check_config(const kvq_config* c) {
 // pages in the arena: the pool a page table indexes
 static int pool_pages(const kvq_config* c) { return c->batch * c->n_kv_heads * c->max_pages; }
 
+static bool head_tiers(const kvq_config* c) {
+  return c->key_mode == KVQ_KEY_MIXKVQ && c->select_mode == KVQ_SELECT_THRESHOLD;
+}
+
 static size_t page_stride(const kvq_config* c) {
-  if (c->key_mode == KVQ_KEY_MIXKVQ) return (size_t)mix_geo(c->n_bf16, c->n_u4).stride;
+  if (c->key_mode == KVQ_KEY_MIXKVQ) {
+    if (!head_tiers(c)) return (size_t)mix_geo(c->n_bf16, c->n_u4).stride;
+    int st = 0;   // threshold tiers: the largest page of any counts within the capacities
+    for (int a = 0; a <= c->n_bf16; ++a)
+      for (int b = 0; b <= c->n_u4 && a + b <= D; ++b) st = st > mix_geo(a, b).stride ? st : mix_geo(a, b).stride;
+    return (size_t)st;
+  }
   if (c->key_mode == KVQ_KEY_PNMIX) return (size_t)pn_geo(2 * c->n_hi_pairs).stride;
   return (size_t)qjl_geo(c->qjl_m, c->qjl_m_out).stride;
 }
@@ -89,6 +111,7 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   if ((int64_t)first_page + n_pages > (page_table ? table_stride : cfg->max_pages)) return KVQ_CAPACITY;
   const bool needs_mask = cfg->key_mode != KVQ_KEY_QJL || cfg->qjl_outliers > 0;
   if (needs_mask && !mask) return KVQ_INVALID_ARG;
+  if (head_tiers(cfg) && !aligned16(mask)) return KVQ_INVALID_ARG;   // the tier codes are read as dwords
   if (cfg->key_mode == KVQ_KEY_QJL && (!qjl_s || !aligned16(qjl_s))) return KVQ_INVALID_ARG;
   // one block per (page, part, kv head, batch) on a one-dimensional grid
   if ((int64_t)n_pages * 16 * cfg->n_kv_heads * cfg->batch > INT32_MAX / 2) return KVQ_INVALID_ARG;
@@ -117,6 +140,7 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   a.q_accum = nullptr;
   a.rec_out = nullptr;
   a.rec_stride = 0;
+  a.head_tiers = head_tiers(cfg) ? 1 : 0;
   return KVQ_OK;
 }
 
@@ -180,8 +204,11 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.pair_layout = cfg->pair_layout;
   a.qjl_m = cfg->qjl_m;
   a.qjl_mo = cfg->qjl_m_out;
+  a.head_tiers = head_tiers(cfg) ? 1 : 0;
   return KVQ_OK;
 }
+
+static bool generic_decode(const kvq_config* c) { return c->decode_path == KVQ_DECODE_GENERIC; }
 }  // namespace kvq
 
 using namespace kvq;
@@ -294,6 +321,10 @@ kvq_status kvq_select_channels(const kvq_config* cfg, const void* q_pre, int64_t
   a.pair_layout = cfg->pair_layout;
   a.n_out = cfg->qjl_outliers;
   a.out = (uint8_t*)mask_out;
+  a.threshold = head_tiers(cfg) ? 1 : 0;
+  a.tau_bf16 = cfg->tau_bf16;
+  a.tau_u4 = cfg->tau_u4;
+  if (a.threshold && 3.0 * (double)(cfg->n_q_heads / cfg->n_kv_heads) * (double)l_q >= 0x1p53) return KVQ_INVALID_ARG;
   return launch_select(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 
@@ -355,7 +386,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
                                        sink_v, n_sink, resid_k, resid_v, n_resid, resid_stride, softmax_scale, out,
                                        workspace, workspace_bytes, a);
   if (st != KVQ_OK) return st;
-  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream) == hipSuccess
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, generic_decode(cfg)) ==
+                 hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;
 }
@@ -379,7 +411,8 @@ kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void
   if (st != KVQ_OK) return st;
   if (cfg->page_records) return KVQ_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
-  if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false) != hipSuccess) return KVQ_HIP_ERROR;
+  if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false, generic_decode(cfg)) != hipSuccess)
+    return KVQ_HIP_ERROR;
   return launch_merge_flush(cfg->key_mode, d, f, cfg->batch, s) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }
 

@@ -28,8 +28,6 @@
 //    16 / g copies of each head's logits so every lane owns one (j, head).
 // Lane conventions (verified on gfx950): lane l, a = l / 16, r = l % 16;
 // A[row r][k 8a..8a+7], B[k 8a..8a+7][col r], D[row 4a..4a+3][col r].
-#include <stdlib.h>
-
 #include "kvq_decode_common.h"
 #include "kvq_merge.h"
 
@@ -76,7 +74,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   const int p1 = min(A.n_pages, p0 + A.pps);
 
   if constexpr (MODE == KVQ_KEY_MIXKVQ) {
-    const MixGeo g = mix_geo(A.n16, A.n4);
+    int hn16 = A.n16, hn4 = A.n4;
+    if (A.head_tiers) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);   // threshold tiers: the head's counts
+    const MixGeo g = mix_geo(hn16, hn4);
     const int NKS = (g.F + 3) / 4;
     const int NKB = (g.n16 + 31) / 32;
     bf16x8 Bq[4];
@@ -389,7 +389,7 @@ static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t
 int decode_parts(const DecodeArgs& a) { return a.n_page_splits + a.n_seg_splits; }
 
 hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s,
-                         bool with_merge) {
+                         bool with_merge, bool generic) {
   DecodeArgs a = args;
   const int g = a.n_q_heads / a.n_kv_heads;
   const int n_parts = decode_parts(a);
@@ -402,10 +402,10 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
       if (e != hipSuccess) return e;
     }
     hipError_t e = hipSuccess;
-    // The warp-specialised kernels cover the common shapes (and may choose
-    // their own split count); KVQ_FORCE_GENERIC_DECODE selects the generic
-    // kernel (same results) so tests can exercise both.
-    const bool fast = getenv("KVQ_FORCE_GENERIC_DECODE") == nullptr && launch_decode_fast(key_mode, a, s);
+    // The software-pipelined kernels cover the common shapes; the config's
+    // decode path can ask for the generic kernel (same results within the
+    // decode bound).
+    const bool fast = !generic && launch_decode_fast(key_mode, a, s);
     if (fast) {
       e = hipGetLastError();
     } else {

@@ -375,8 +375,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     return;
   }
   const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
-  const MixGeo g = mix_geo(A.n16, A.n4);
-  const uint8_t* rec = A.mask + head * MIX_RECORD;
+  int hn16 = A.n16, hn4 = A.n4;
+  if (A.head_tiers) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);   // threshold tiers: the head's counts
+  const MixGeo g = mix_geo(hn16, hn4);
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
   const PageSet<PAGED> pset = page_set<PAGED>(A, head, p0, np, lane);
 
@@ -732,8 +733,7 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   if (a.table && a.pps > 64) return false;   // the split's page indices live in one register
   if (a.rec_stride && (key_mode != KVQ_KEY_MIXKVQ || a.n16 > 1)) return false;   // per-page records: no eight-row BF16 tier
   if (key_mode == KVQ_KEY_MIXKVQ) {
-    const MixGeo geo = mix_geo(a.n16, a.n4);
-    const int nks = (geo.F + 3) / 4;
+    const int nks = (mix_max_fragments(a.n16, a.n4, a.head_tiers) + 3) / 4;
     if (a.n16 > 8) return false;   // the fast path keeps the BF16 tier in lane group 0 (<= 8 channels)
     const int nb = a.n16 == 0 ? 0 : (a.n16 == 1 ? 1 : 8);
     if (nks == 5) {

@@ -417,7 +417,9 @@ __device__ inline void reselect_page(const FlushArgs& A, int64_t head, int lpage
 
 __device__ __attribute__((always_inline)) inline void flush_mix_key_part(const FlushArgs& A, uint8_t* page, int64_t head, int64_t row0, int fg,
                                           int lpage, KPartSmem& S) {
-  const MixGeo g = mix_geo(A.n16, A.n4);
+  int hn16 = A.n16, hn4 = A.n4;
+  if (A.head_tiers) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);   // threshold tiers: the head's counts
+  const MixGeo g = mix_geo(hn16, hn4);
   const bool resel = A.q_accum != nullptr;
   const uint8_t chv = resel ? (uint8_t)0 : A.mask[head * MIX_RECORD + (threadIdx.x & (D - 1))];   // in flight with the staging
   stage_rows_padded(S.tile, A.k_src, row0);
@@ -775,7 +777,9 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
       VPartSmem v;
       KPartSmem k;
     } S;
-    const MixGeo g = mix_geo(A.n16, A.n4);
+    int hn16 = A.n16, hn4 = A.n4;
+    if (A.head_tiers && part < V_PARTS) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);
+    const MixGeo g = mix_geo(hn16, hn4);
     if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
     else flush_mix_key_part(A, page, head, row0, part - V_PARTS, lpage, S.k);
   } else if constexpr (MODE == KVQ_KEY_PNMIX) {
@@ -824,8 +828,20 @@ __global__ __launch_bounds__(256) void merge_flush_kernel(FlushArgs A, int parts
 }
 
 // ------------------------------------------------------------------ launchers
+// most code fragments a MixKVQ page can have: the configured counts, or with
+// threshold tiers any counts within the capacities (fewer BF16 channels leave
+// more UINT2 slots)
+int mix_max_fragments(int n16, int n4, bool head_tiers) {
+  if (!head_tiers) return mix_geo(n16, n4).F;
+  int f = 0;
+  for (int a = 0; a <= n16; ++a)
+    for (int c = 0; c <= n4 && a + c <= D; ++c) f = max(f, mix_geo(a, c).F);
+  return f;
+}
+
 static int flush_parts(int key_mode, const FlushArgs& a) {
-  if (key_mode == KVQ_KEY_MIXKVQ) return V_PARTS + max(1, (mix_geo(a.n16, a.n4).F + 3) / 4);   // part 0 also writes the BF16 rows
+  if (key_mode == KVQ_KEY_MIXKVQ)   // part 0 also writes the BF16 rows
+    return V_PARTS + max(1, (mix_max_fragments(a.n16, a.n4, a.head_tiers) + 3) / 4);
   if (key_mode == KVQ_KEY_PNMIX) return V_PARTS + 2;
   return V_PARTS + (a.qjl_m + a.qjl_mo) / 64;
 }

@@ -78,6 +78,22 @@ __host__ __device__ inline QjlGeo qjl_geo(int m, int mo = 0) {
 }
 
 constexpr int MIX_RECORD = 160;   // channel order u8[128] + 2-bit tiers [32]
+
+// Tier counts a MixKVQ record holds in its 2-bit codes (2 = BF16, 1 = UINT4):
+// with threshold tiers every head has its own counts, and its pages are laid
+// out by them. rec must be 4-byte aligned.
+__device__ inline void mix_record_counts(const uint8_t* rec, int& n16, int& n4) {
+  const uint32_t* tw = reinterpret_cast<const uint32_t*>(rec + 128);
+  int c2 = 0, c1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = tw[i], hi = (w >> 1) & 0x55555555u, lo = w & 0x55555555u;
+    c2 += __builtin_popcount(hi & ~lo);
+    c1 += __builtin_popcount(lo & ~hi);
+  }
+  n16 = c2;
+  n4 = c1;
+}
 constexpr int PN_RECORD = 8;      // 64 pair bits
 constexpr int QJL_RECORD = 16;    // outlier-channel bits (QJL outlier split)
 
@@ -192,6 +208,7 @@ struct FlushArgs {
   const void* q_accum;            // MixKVQ reselection: query sums (128-bit) per (head, channel); null: the mask records
   uint8_t* rec_out;               // with q_accum: record of logical page p of head h at rec_out + (h rec_stride + p) * 160
   int rec_stride;
+  int head_tiers;                 // MixKVQ threshold tiers: each head's counts come from its record (n16, n4: capacities)
 };
 struct SelectArgs {
   const uint16_t* q;
@@ -202,6 +219,8 @@ struct SelectArgs {
   int n_hi_pairs, pair_layout;
   int n_out;                      // QJL: outlier channels
   uint8_t* out;
+  int threshold;                  // MixKVQ: tiers by the salience thresholds (n16, n4: capacities)
+  double tau_bf16, tau_u4;
 };
 struct DecodeArgs {
   const uint16_t* q;
@@ -230,6 +249,7 @@ struct DecodeArgs {
   int n_hi, pair_layout;
   int qjl_m;
   int qjl_mo;                     // as FlushArgs::qjl_mo; the estimate's outlier term is scaled by qjl_m / qjl_mo
+  int head_tiers;                 // as FlushArgs::head_tiers
 };
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);
@@ -238,7 +258,7 @@ hipError_t launch_accumulate(const SelectArgs& a, void* acc, int batch, hipStrea
 // with_merge false: the split kernels only; the caller launches the merge
 // (launch_merge_flush) with the same DecodeArgs
 hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s,
-                         bool with_merge = true);
+                         bool with_merge, bool generic);
 int decode_parts(const DecodeArgs& a);
 hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s);
 constexpr int RECORD = 130;       // partial record per query head: m, l, out[128]
@@ -249,6 +269,7 @@ constexpr int SEG_TOKENS = 32;
 constexpr int MAX_SEG_SPLITS = 2 * PAGE / SEG_TOKENS;
 inline int seg_splits(int n_tokens) { return (n_tokens + SEG_TOKENS - 1) / SEG_TOKENS; }
 int decode_pages_per_split(int n_pages, int batch, int n_kv_heads);
+int mix_max_fragments(int n16, int n4, bool head_tiers);
 int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int slots);
 
 }  // namespace kvq

@@ -80,4 +80,71 @@ __device__ inline int key_rank(const double* key_hi, const double* key_lo, int d
   return r;
 }
 
+// ---------------------------------------------------------------- threshold tiers
+// Exact sign of a sum of doubles: the terms are added one by one into a
+// nonoverlapping expansion (Shewchuk, "Adaptive Precision Floating-Point
+// Arithmetic and Fast Robust Geometric Predicates", grow-expansion with the
+// error-free two-sum), whose largest nonzero component carries the sign.
+__device__ inline void two_sum_exact(double a, double b, double& s, double& e) {
+#pragma clang fp contract(off)
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+template <int N>
+__device__ inline int exact_sign(const double (&t)[N]) {
+  double h[N];
+  int m = 0;
+  for (int i = 0; i < N; ++i) {
+    double q = t[i];
+    for (int j = 0; j < m; ++j) {
+      double s, e;
+      two_sum_exact(q, h[j], s, e);
+      h[j] = e;
+      q = s;
+    }
+    h[m++] = q;
+  }
+  for (int j = m - 1; j >= 0; --j)
+    if (h[j] != 0.0) return h[j] > 0.0 ? 1 : -1;
+  return 0;
+}
+
+// Sign of A_d - tau for the MixKVQ salience A_d = I_d * S_d (MixKVQ
+// "方法细节"): I_d = SQ_d 2^-64 / (g l_q), S_d = (mx - mn) / 3 (B = 2), so
+// A_d - tau has the sign of SQ_d (mx - mn) - tau * 3 g l_q * 2^64, evaluated
+// exactly: SQ_d in three 43-bit pieces, mx - mn as an exact two-sum, every
+// product as an exact fused-multiply-add pair. n3 = 3 g l_q < 2^53; tau is 0
+// or 2^-900 <= |tau| <= 2^900, so no partial product underflows.
+__device__ inline int salience_vs_tau(u128 sq, float mx, float mn, double n3, double tau) {
+#pragma clang fp contract(off)
+  double rh, rl;
+  two_sum_exact((double)mx, -(double)mn, rh, rl);
+  const double c[3] = {(double)(uint64_t)(sq & ((((u128)1) << 43) - 1)),
+                       (double)(uint64_t)((sq >> 43) & ((((u128)1) << 43) - 1)) * 0x1p43,
+                       (double)(uint64_t)(sq >> 86) * 0x1p86};
+  double t[14];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    t[4 * i] = c[i] * rh;
+    t[4 * i + 1] = fma(c[i], rh, -t[4 * i]);
+    t[4 * i + 2] = c[i] * rl;
+    t[4 * i + 3] = fma(c[i], rl, -t[4 * i + 2]);
+  }
+  const double th = tau * n3;
+  const double tl = fma(tau, n3, -th);
+  t[12] = -th * 0x1p64;
+  t[13] = -tl * 0x1p64;
+  return exact_sign(t);
+}
+
+// Tier counts of a head under the thresholds: c16 channels have A_d >
+// tau_bf16, c4 have tau_u4 < A_d <= tau_bf16. The tiers are contiguous in the
+// ranking; capacities cap16 / cap4 keep the highest-ranked channels of a tier
+// that overflows and pass the rest down one tier.
+__device__ inline void threshold_counts(int c16, int c4, int cap16, int cap4, int& n16, int& n4) {
+  n16 = min(c16, cap16);
+  n4 = min(c16 - n16 + c4, cap4);
+}
+
 }  // namespace kvq

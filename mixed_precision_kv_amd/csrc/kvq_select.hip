@@ -24,6 +24,8 @@ __global__ __launch_bounds__(1024) void select_mixkvq_kernel(SelectArgs A) {
   __shared__ double key_hi[D], key_lo[D];
   __shared__ int rank_s[D];
   __shared__ uint8_t tier_s[D];
+  __shared__ uint8_t over_s[D];                // threshold tiers: 2 if A_d > tau_bf16, 1 if tau_u4 < A_d <= tau_bf16
+  __shared__ int count_s[2];
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int g = A.n_q_heads / A.n_kv_heads;
   const int j = threadIdx.x & 63, rl = threadIdx.x >> 6;   // channel pair, row lane
@@ -64,18 +66,52 @@ __global__ __launch_bounds__(1024) void select_mixkvq_kernel(SelectArgs A) {
     }
     const double range = (A.l_k > 0) ? (double)mx - (double)mn : 0.0;
     dd_key(sq, range, key_hi[d], key_lo[d]);
+    if (A.threshold) {
+      // the salience A_d against both thresholds, exactly (MixKVQ three-tier rule)
+      const double n3 = 3.0 * (double)g * (double)A.l_q;
+      const bool b16 = A.l_k > 0 && salience_vs_tau(sq, mx, mn, n3, A.tau_bf16) > 0;
+      const bool b4 = A.l_k > 0 && salience_vs_tau(sq, mx, mn, n3, A.tau_u4) > 0;
+      over_s[d] = b16 ? 2 : (b4 ? 1 : 0);
+    }
+    if (d < 2) count_s[d] = 0;
   }
   __syncthreads();
+  // better(o, d): channel o ranks above channel d (larger key, ties to the lower channel)
+  auto better = [&](int o, int d) {
+    return key_hi[o] > key_hi[d] || (key_hi[o] == key_hi[d] && (key_lo[o] > key_lo[d] || (key_lo[o] == key_lo[d] && o < d)));
+  };
   if (threadIdx.x < D) {
     const int d = threadIdx.x, r = key_rank(key_hi, key_lo, d);
     rank_s[d] = r;
-    tier_s[d] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
+    if (!A.threshold) {
+      tier_s[d] = r < A.n16 ? 2 : (r < A.n16 + A.n4 ? 1 : 0);
+    } else {
+      // BF16: above tau_bf16 and among the n16 best of those
+      int r16 = 0;
+      for (int o = 0; o < D; ++o) r16 += over_s[o] == 2 && better(o, d);
+      tier_s[d] = over_s[d] == 2 && r16 < A.n16 ? 2 : 0;
+    }
   }
+  __syncthreads();
+  if (A.threshold && threadIdx.x < D) {
+    // UINT4: the n4 best of the channels above tau_u4 only and those the
+    // BF16 tier had no room for
+    const int d = threadIdx.x;
+    auto cand = [&](int o) { return tier_s[o] != 2 && over_s[o] != 0; };
+    int r4 = 0;
+    for (int o = 0; o < D; ++o) r4 += cand(o) && better(o, d);
+    if (cand(d) && r4 < A.n4) over_s[d] = 3;   // marked; tier_s is still read by the other threads
+  }
+  __syncthreads();
+  if (A.threshold && threadIdx.x < D && over_s[threadIdx.x] == 3) tier_s[threadIdx.x] = 1;
+  __syncthreads();
+  if (threadIdx.x < D && tier_s[threadIdx.x] != 0) atomicAdd(&count_s[2 - tier_s[threadIdx.x]], 1);
   __syncthreads();
   uint8_t* rec = A.out + ((int64_t)b * A.n_kv_heads + kvh) * MIX_RECORD;
   if (threadIdx.x < D) {
     int d = threadIdx.x, t = tier_s[d];
-    int base = t == 2 ? 0 : (t == 1 ? A.n16 : A.n16 + A.n4);
+    const int n16 = count_s[0], n4 = count_s[1];   // the head's own counts (the configured ones by rank)
+    int base = t == 2 ? 0 : (t == 1 ? n16 : n16 + n4);
     int pos = base;
     for (int o = 0; o < d; ++o) pos += tier_s[o] == t;
     rec[pos] = (uint8_t)d;

@@ -9,6 +9,8 @@ tier sizes instead of the thresholds (12.5/25/62.5 % in the tiny workload,
 1/12/115 channels for "~2.3 bits"), so the tiers are taken by rank of A_d:
 the n16 highest channels are BF16, the next n4 are UINT4, the rest UINT2.
 Ties are broken towards the lower channel index (the pages are silent).
+The threshold form of the rule (mixkvq_threshold_select) compares A_d itself
+with tau_BF16 and tau_UINT4.
 
 Exactness. The mean and the 1/(2^B - 1) factor are positive constants common
 to every channel of a KV head and do not change the ranking, so the rank key
@@ -118,6 +120,57 @@ def _select_from_keys(keys, n16: int, n4: int):
     tier = np.where(rank < n16, TIER_BF16, np.where(rank < n16 + n4, TIER_U4, TIER_U2))
     perm = np.concatenate([np.nonzero(tier == t)[0] for t in (TIER_BF16, TIER_U4, TIER_U2)])
     return tier.astype(np.uint8), perm.astype(np.uint8), rank
+
+
+def mixkvq_salience(q_bits, k_bits):
+    """A_d = I_d * S_d of every channel, as exact Fractions (MixKVQ
+    "方法细节"): I_d = mean over the g * L_q prefill query rows of |Q_{t,d}|
+    (each |q| on the 2^-64 grid of query_sums), S_d = (max k_d - min k_d) /
+    (2^B - 1) with B = 2.
+
+    q_bits: [g, L_q, D] bf16 bits; k_bits: [L_k, D] bf16 bits."""
+    q_bits = np.asarray(q_bits)
+    rows = q_bits.shape[0] * q_bits.shape[1]
+    sq = query_sums(q_bits)
+    k = bf16_to_f64(k_bits)
+    out = []
+    for d in range(D):
+        i_d = Fraction(sq[d], 2 ** 64 * rows)
+        s_d = (Fraction(float(k[:, d].max())) - Fraction(float(k[:, d].min()))) / 3
+        out.append(i_d * s_d)
+    return out
+
+
+def mixkvq_threshold_select(q_bits, k_bits, cap16: int, cap4: int, tau_bf16: float, tau_u4: float):
+    """Tiers by the salience thresholds (MixKVQ three-tier rule, Algorithm 1's
+    tau_BF16 and tau_UINT4): A_d > tau_bf16 is BF16, tau_u4 < A_d <= tau_bf16
+    is UINT4, the rest UINT2 (so the UINT4 tier is empty when tau_bf16 <=
+    tau_u4). The comparisons are exact. Reading for storage with a fixed
+    page size: at most cap16 BF16 and cap4 UINT4 channels per head; a tier
+    given more channels keeps its highest-ranked ones (the COUNT ranking) and
+    the rest move down one tier. Returns (tier, perm, rank, n16, n4)."""
+    A = mixkvq_salience(q_bits, k_bits)
+    keys = mixkvq_keys(q_bits, k_bits)
+    rank = _rank_desc(keys)
+    t16, t4 = Fraction(tau_bf16), Fraction(tau_u4)
+    above16 = [A[d] > t16 for d in range(D)]
+    above4 = [A[d] > t4 and not above16[d] for d in range(D)]
+    by_rank = sorted(range(D), key=lambda d: rank[d])
+    bf16 = [d for d in by_rank if above16[d]][:cap16]
+    cand4 = [d for d in by_rank if (above16[d] and d not in bf16) or above4[d]]
+    u4 = cand4[:cap4]
+    tier = np.full(D, TIER_U2, dtype=np.uint8)
+    tier[bf16] = TIER_BF16
+    tier[u4] = TIER_U4
+    perm = np.concatenate([np.nonzero(tier == t)[0] for t in (TIER_BF16, TIER_U4, TIER_U2)])
+    return tier, perm.astype(np.uint8), rank, len(bf16), len(u4)
+
+
+def record_counts(rec) -> tuple:
+    """(BF16, UINT4) channel counts held in a record's 2-bit tier codes."""
+    rec = np.asarray(rec, np.uint8)
+    codes = [(int(rec[D + d // 4]) >> (2 * (d % 4))) & 3 for d in range(D)]
+    return codes.count(TIER_BF16), codes.count(TIER_U4)
 
 
 def mixkvq_record(tier: np.ndarray, perm: np.ndarray) -> np.ndarray:

@@ -22,8 +22,12 @@ D = 128
 class Pipeline:
     """select -> prefill flush -> decode for one workload on the GPU."""
 
-    def __init__(self, w: synth.Workload, device="cuda", max_pages=None, need_q_pre=True, pair_layout="half"):
+    def __init__(self, w: synth.Workload, device="cuda", max_pages=None, need_q_pre=True, pair_layout="half",
+                 tau=None):
+        """tau: (tau_bf16, tau_u4) selects the MixKVQ threshold tiers, with
+        the workload's n_bf16 / n_u4 as the capacities."""
         self.w = w
+        self.tau = tau
         self.dev = device
         self.g = w.group
         self.L = w.prefill_tokens
@@ -33,7 +37,9 @@ class Pipeline:
                                    n_bf16=w.n_bf16, n_u4=w.n_u4,
                                    pair_layout=kvq.KVQ_PAIR_HALF_SPLIT if pair_layout == "half" else kvq.KVQ_PAIR_ADJACENT,
                                    n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m,
-                                   qjl_outliers=w.qjl_outliers, qjl_m_out=w.qjl_m_out)
+                                   qjl_outliers=w.qjl_outliers, qjl_m_out=w.qjl_m_out,
+                                   select_mode=kvq.KVQ_SELECT_THRESHOLD if tau else kvq.KVQ_SELECT_COUNT,
+                                   tau_bf16=tau[0] if tau else 0.0, tau_u4=tau[1] if tau else 0.0)
         self.page_bytes = kvq.kvq_page_bytes(self.cfg)
         self.mask_bytes = kvq.kvq_mask_bytes(self.cfg)
         q, k, v = synth.prefill(w, device)
@@ -77,7 +83,8 @@ class Pipeline:
         kvq.kvq_flush_quantize(self.cfg, self.k_offset_ptr(self.k_pre, w.n_sink), self.k_offset_ptr(self.v_pre, w.n_sink),
                                self.L, w.n_pages, self.mask, self.S, self.arena, 0, self.flags)
 
-    def decode(self, n_pages=None, n_resid=None):
+    def decode(self, n_pages=None, n_resid=None, generic=False):
+        """generic: the config's decode path set to the generic kernel."""
         w = self.w
         n_pages = w.n_pages if n_pages is None else n_pages
         n_resid = w.n_resid if n_resid is None else n_resid
@@ -85,7 +92,8 @@ class Pipeline:
         if need > self.ws_bytes:
             self.ws_bytes = need
             self.ws = torch.zeros(need // 4 + 64, dtype=torch.float32, device=self.dev)
-        kvq.kvq_decode_attention(self.cfg, self.q_dec, self.arena, n_pages, self.mask, self.S,
+        cfg = kvq.with_fields(self.cfg, decode_path=kvq.KVQ_DECODE_GENERIC) if generic else self.cfg
+        kvq.kvq_decode_attention(cfg, self.q_dec, self.arena, n_pages, self.mask, self.S,
                                  self.sink_k, self.sink_v, w.n_sink, self.resid_k, self.resid_v, n_resid, 128,
                                  self.scale, self.out, self.ws, self.ws_bytes)
         return self.out
@@ -133,7 +141,10 @@ class Pipeline:
         qb = self.bits(self.q_pre[b, h * g:(h + 1) * g])
         if w.key_mode == synth.MIXKVQ:
             kb = self.bits(self.k_pre[b, h, w.n_sink: w.n_sink + w.n_pages * 128])
-            tier, perm, _ = osel.mixkvq_select(qb, kb, w.n_bf16, w.n_u4)
+            if self.tau:
+                tier, perm = osel.mixkvq_threshold_select(qb, kb, w.n_bf16, w.n_u4, *self.tau)[:2]
+            else:
+                tier, perm, _ = osel.mixkvq_select(qb, kb, w.n_bf16, w.n_u4)
             return osel.mixkvq_record(tier, perm)
         kb = self.bits(self.k_pre[b, h])
         return osel.pnmix_select(qb, kb, w.n_hi_pairs, self.pair_layout)[2]
@@ -149,7 +160,7 @@ class Pipeline:
         """The oracle's page of 128 tokens (bf16 bits) under a selection record."""
         w = self.w
         if w.key_mode == synth.MIXKVQ:
-            return oflush.flush_mixkvq_page(kb, vb, record[:128], w.n_bf16, w.n_u4)
+            return oflush.flush_mixkvq_page(kb, vb, record[:128], *self.tier_counts(record))
         if w.key_mode == synth.PNMIX:
             return oflush.flush_pnmix_page(kb, vb, osel.hi_channels_from_record(record, self.pair_layout))
         if w.qjl_outliers:
@@ -162,7 +173,8 @@ class Pipeline:
         g = self.g
         n_resid = w.n_resid if n_resid is None else n_resid
         qb = self.bits(self.q_dec[b, h * g:(h + 1) * g])
-        kw = dict(n16=w.n_bf16, n4=w.n_u4, perm=None if record is None else record[:128],
+        n16, n4 = self.tier_counts(record) if w.key_mode == synth.MIXKVQ else (0, 0)
+        kw = dict(n16=n16, n4=n4, perm=None if record is None else record[:128],
                   mask_rec=record, pair_layout=self.pair_layout,
                   s_bits=None if self.S is None else self.bits(self.S))
         if w.qjl_outliers:
@@ -174,6 +186,18 @@ class Pipeline:
             kw["resid_k"] = self.bits(self.resid_k[b, h, :n_resid])
             kw["resid_v"] = self.bits(self.resid_v[b, h, :n_resid])
         return oatt.decode_arena_head(w.key_mode, qb, pages, self.scale, **kw)
+
+    def tier_counts(self, record):
+        """(BF16, UINT4) counts a MixKVQ page is laid out by: the configured
+        ones, or with threshold tiers the head's own (from its record)."""
+        if self.tau:
+            return osel.record_counts(record)
+        return self.w.n_bf16, self.w.n_u4
+
+    def same_page(self, gpu_page, oracle_page):
+        """A GPU page slot holds the oracle's page (with threshold tiers the
+        slot is the largest page and its tail is not written)."""
+        return np.array_equal(np.asarray(gpu_page)[:oracle_page.size], oracle_page)
 
     def reference_probs(self, b, h, n_pages, n_resid):
         """Unquantized bf16 attention over the same visible tokens (fidelity)."""

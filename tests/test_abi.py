@@ -32,12 +32,12 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(kvq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 3
+    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 4
     assert kvq.kvq_status_string(0) == "ok"
 
 
 def test_config_struct_matches_header():
-    assert ctypes.sizeof(kvq.KvqConfig) == 16 * 4
+    assert ctypes.sizeof(kvq.KvqConfig) == 18 * 4 + 2 * 8 and kvq.KvqConfig.tau_bf16.offset == 72
     assert ctypes.sizeof(kvq.KvqStorage) == 9 * 8 + 8
 
 
@@ -113,7 +113,8 @@ def test_validation_rejects_before_launch(lib):
         kvq.kvq_page_bytes(bad)
     assert e.value.status == kvq.KVQ_UNSUPPORTED
     for field, value, status in (("n_q_heads", 6, kvq.KVQ_UNSUPPORTED), ("n_kv_heads", 3, kvq.KVQ_INVALID_ARG),
-                                 ("abi_version", 4, kvq.KVQ_INVALID_ARG), ("reserved", 1, kvq.KVQ_INVALID_ARG),
+                                 ("abi_version", 3, kvq.KVQ_INVALID_ARG), ("reserved", 1, kvq.KVQ_INVALID_ARG),
+                                 ("select_mode", 2, kvq.KVQ_INVALID_ARG), ("decode_path", 2, kvq.KVQ_INVALID_ARG),
                                  ("qjl_outliers", 8, kvq.KVQ_INVALID_ARG),
                                  ("n_bf16", 120, kvq.KVQ_INVALID_ARG), ("key_mode", 7, kvq.KVQ_INVALID_ARG)):
         c = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=16, n_u4=32)
@@ -164,3 +165,26 @@ def test_validation_rejects_before_launch(lib):
     st = S.kvq_select_channels(ctypes.byref(qcfg), 16, 10, 10, 16, 10, 10, 16, None)
     assert st == kvq.KVQ_UNSUPPORTED
     assert kvq.kvq_workspace_bytes(cfg, 8) > 0
+
+
+def test_threshold_config(lib):
+    """Threshold tiers: the thresholds' domain is checked; the page stride is
+    the largest page any counts within the capacities need (fewer BF16
+    channels can mean a larger code region)."""
+    def cfg(**kw):
+        return kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=1, n_u4=12,
+                               select_mode=kvq.KVQ_SELECT_THRESHOLD, **kw)
+    c = cfg(tau_bf16=1.44, tau_u4=0.79)
+    want = max(layout.mixkvq_geometry(a, b)["stride"] for a in range(2) for b in range(13))
+    assert kvq.kvq_page_bytes(c) == want >= layout.mixkvq_geometry(1, 12)["stride"]
+    for t16, t4 in ((float("nan"), 0.5), (1.0, float("inf")), (1e-300, 0.5), (1.0, 2.0 ** 950)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_page_bytes(cfg(tau_bf16=t16, tau_u4=t4))
+        assert e.value.status == kvq.KVQ_INVALID_ARG
+    kvq.kvq_page_bytes(cfg(tau_bf16=0.0, tau_u4=-1.5))   # zero and negative thresholds are valid
+    with pytest.raises(kvq.KvqError) as e:               # threshold tiers are MixKVQ's
+        kvq.kvq_page_bytes(kvq.make_config(kvq.KVQ_KEY_PNMIX, 1, 4, 1, 8, select_mode=kvq.KVQ_SELECT_THRESHOLD))
+    assert e.value.status == kvq.KVQ_INVALID_ARG
+    with pytest.raises(kvq.KvqError) as e:               # no mean |Q| from the running accumulator
+        kvq.kvq_page_bytes(cfg(tau_bf16=1.0, tau_u4=0.5, page_records=1))
+    assert e.value.status == kvq.KVQ_UNSUPPORTED

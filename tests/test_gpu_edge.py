@@ -1,6 +1,6 @@
 """GPU edge cases of libkvq against the oracle.
 
-* The generic decode kernel (KVQ_FORCE_GENERIC_DECODE) against the oracle
+* The generic decode kernel (decode_path KVQ_DECODE_GENERIC) against the oracle
   and against the pipelined kernels.
 * Degenerate visible sets: no pages, only residual; no pages and no
   residual; a prefix of the flushed pages.
@@ -12,7 +12,6 @@
 * PN-Mix with the adjacent pair layout.
 * Repeated decode calls give identical bits.
 """
-import os
 
 import numpy as np
 import pytest
@@ -49,24 +48,16 @@ def built(w, **kw):
     return p
 
 
-@pytest.fixture
-def generic_decode():
-    os.environ["KVQ_FORCE_GENERIC_DECODE"] = "1"
-    yield
-    os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
-
-
 @pytest.mark.parametrize("name", ["llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"])
-def test_generic_decode_matches_oracle_and_fast(name, generic_decode):
+def test_generic_decode_matches_oracle_and_fast(name):
     base = synth.WORKLOADS[name]
     w = base.scaled(batch=1, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=3, n_resid=min(base.n_resid, 40),
                     seed=base.seed + 100)
     p = built(w)
-    p.decode()
+    p.decode(generic=True)
     torch.cuda.synchronize()
     generic = p.out.clone()
     check_decode(p, w.n_pages, w.n_resid, name + "/generic")
-    os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
     p.decode()
     torch.cuda.synchronize()
     fast = p.out.clone()

@@ -7,7 +7,6 @@ bit, and the oracle's within the decode bound; the fused decode + flush call
 writes the residual's page through the table; a flush entry outside the pool
 writes nothing and raises KVQ_FLAG_TABLE.
 """
-import os
 
 import numpy as np
 import pytest
@@ -44,9 +43,10 @@ def pool_page(arena, p, idx):
     return arena[idx * p.page_bytes:(idx + 1) * p.page_bytes]
 
 
-def decode_into(p, arena, table, n_pages, n_resid, out):
+def decode_into(p, arena, table, n_pages, n_resid, out, generic=False):
     w = p.w
-    kvq.kvq_decode_attention(p.cfg, p.q_dec, arena, n_pages, p.mask, p.S, p.sink_k, p.sink_v, w.n_sink, p.resid_k,
+    cfg = kvq.with_fields(p.cfg, decode_path=kvq.KVQ_DECODE_GENERIC) if generic else p.cfg
+    kvq.kvq_decode_attention(cfg, p.q_dec, arena, n_pages, p.mask, p.S, p.sink_k, p.sink_v, w.n_sink, p.resid_k,
                              p.resid_v, n_resid, 128, p.scale, out, p.ws, p.ws_bytes, page_table=table,
                              table_stride=p.max_pages if table is not None else 0)
 
@@ -75,13 +75,9 @@ def test_paged_matches_contiguous(name):
     torch.cuda.synchronize()
     assert torch.equal(out_c, out_t)
     # the generic kernel through the table, against the oracle
-    os.environ["KVQ_FORCE_GENERIC_DECODE"] = "1"
-    try:
-        out_g = torch.empty_like(p.out)
-        decode_into(p, arena2, table, w.n_pages, w.n_resid, out_g)
-        torch.cuda.synchronize()
-    finally:
-        os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
+    out_g = torch.empty_like(p.out)
+    decode_into(p, arena2, table, w.n_pages, w.n_resid, out_g, generic=True)
+    torch.cuda.synchronize()
     o = out_g.cpu().numpy()
     b, hk = w.batch - 1, w.n_kv_heads - 1
     rec = p.record(b, hk)

@@ -8,7 +8,6 @@ per-page channel orders; after one decode query is accumulated, the
 residual's page is reselected with the updated sums.
 """
 import math
-import os
 
 import numpy as np
 import pytest
@@ -37,11 +36,15 @@ def acc_ints(acc, head):
     return [int(a[d, 0]) + (int(a[d, 1]) << 64) for d in range(D)]
 
 
-@pytest.mark.parametrize("name", ["tiny_mixkvq", "llama8b_8k"])
+@pytest.mark.parametrize("name", ["tiny_mixkvq", "llama8b_8k", "llama8b_8k_full"])
 def test_reselect_flow(name):
-    base = synth.WORKLOADS[name]
-    w = base if name == "tiny_mixkvq" else base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=4,
-                                                       seed=base.seed + 1000)
+    """llama8b_8k_full is the benchmark's reselection cache (two pages per
+    decode split, so the per-page tables are rebuilt inside a split)."""
+    base = synth.WORKLOADS[name.replace("_full", "")]
+    if name == "tiny_mixkvq" or name.endswith("_full"):
+        w = base
+    else:
+        w = base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=4, seed=base.seed + 1000)
     print(f"\n[case] reselect {w}", flush=True)
     g, H, L = w.group, w.batch * w.n_kv_heads, w.prefill_tokens
     max_pages = w.n_pages + 1
@@ -70,14 +73,10 @@ def test_reselect_flow(name):
     torch.cuda.synchronize()
     assert int(flags[0].item()) == 0
     # the pipelined kernel (when it covers the shape) against the generic one
-    os.environ["KVQ_FORCE_GENERIC_DECODE"] = "1"
-    try:
-        out_g = torch.zeros_like(out)
-        kvq.kvq_decode_attention(cfg, qd, arena, w.n_pages, records, None, None, None, 0, resid_k, resid_v,
-                                 w.n_resid, 128, scale, out_g, ws, ws_bytes)
-        torch.cuda.synchronize()
-    finally:
-        os.environ.pop("KVQ_FORCE_GENERIC_DECODE", None)
+    out_g = torch.zeros_like(out)
+    kvq.kvq_decode_attention(kvq.with_fields(cfg, decode_path=kvq.KVQ_DECODE_GENERIC), qd, arena, w.n_pages, records,
+                             None, None, None, 0, resid_k, resid_v, w.n_resid, 128, scale, out_g, ws, ws_bytes)
+    torch.cuda.synchronize()
     assert np.all(rel_err(out.cpu().numpy().reshape(-1, D), out_g.cpu().numpy().reshape(-1, D)) <= 2 * TOL)
     rec_all = records.cpu().numpy().reshape(H, max_pages, 160)
     arena_np = arena.cpu().numpy().reshape(H, max_pages, pb)
@@ -119,12 +118,15 @@ def test_reselect_flow(name):
         assert np.array_equal(arena_np[head, w.n_pages], oflush.flush_mixkvq_page(rkb, rvb, perm, w.n_bf16, w.n_u4))
 
 
-def test_reselect_through_page_table():
+@pytest.mark.parametrize("full", [False, True])
+def test_reselect_through_page_table(full):
     """The same reselection flow with the pages scattered over the pool by a
     page table: records (indexed by logical page), page bytes and the decode
-    output equal the contiguous run's, bit for bit."""
+    output equal the contiguous run's, bit for bit (full: the llama8b_8k
+    shape, two pages per decode split)."""
     base = synth.WORKLOADS["llama8b_8k"]
-    w = base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=5, seed=base.seed + 1100)
+    w = base if full else base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=5,
+                                      seed=base.seed + 1100)
     print(f"\n[case] reselect paged {w}", flush=True)
     H, L = w.batch * w.n_kv_heads, w.prefill_tokens
     max_pages = w.n_pages + 1

@@ -172,3 +172,69 @@ def test_reselect_follows_each_pages_keys():
     t_p, _, _ = select.mixkvq_select_sums(sq, _bf16(page), w.n_bf16, w.n_u4)
     assert all(t_p[d] == 0 for d in oc[4:])
     assert all(t_all[d] == 2 for d in oc[4:])
+
+
+# ------------------------------------------------------------------ threshold tiers
+# MixKVQ three-tier rule with the salience thresholds: A_d > tau_BF16 is
+# BF16, tau_UINT4 < A_d <= tau_BF16 is UINT4, A_d <= tau_UINT4 is UINT2.
+
+def _ramp_inputs():
+    """Closed form: every |q| = 1 (I_d = 1), Keys 0 and (d + 1)/16 (range
+    (d + 1)/16), so A_d = (d + 1)/48 exactly, over g = 2 heads, L_q = 4."""
+    qb = np.full((2, 4, 128), 0x3F80, np.uint16)                      # bf16 1.0
+    k = np.zeros((3, 128), np.float32)
+    k[1] = (np.arange(128) + 1) / 16.0
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)                 # exact in bf16
+    return qb, kb
+
+
+def test_threshold_salience_closed_form():
+    qb, kb = _ramp_inputs()
+    A = select.mixkvq_salience(qb, kb)
+    assert A == [Fraction(d + 1, 48) for d in range(128)]
+    # tau_bf16 = 2.5 = A_119 exactly, tau_u4 = 2 = A_95 exactly: both
+    # comparisons are strict on the upper side
+    tier, perm, _, n16, n4 = select.mixkvq_threshold_select(qb, kb, 128, 128, 2.5, 2.0)
+    expect = np.where(np.arange(128) >= 120, select.TIER_BF16, np.where(np.arange(128) >= 96, select.TIER_U4, select.TIER_U2))
+    assert np.array_equal(tier, expect) and (n16, n4) == (8, 24)
+    assert list(perm[:8]) == list(range(120, 128)) and list(perm[8:32]) == list(range(96, 120))
+    assert select.record_counts(select.mixkvq_record(tier, perm)) == (8, 24)
+    # capacities: the BF16 tier keeps its 4 best (127..124), the other 4 move
+    # down to compete for the 10 UINT4 places with the 24 channels above 2
+    tier, _, _, n16, n4 = select.mixkvq_threshold_select(qb, kb, 4, 10, 2.5, 2.0)
+    assert (n16, n4) == (4, 10)
+    assert set(np.nonzero(tier == select.TIER_BF16)[0]) == set(range(124, 128))
+    assert set(np.nonzero(tier == select.TIER_U4)[0]) == set(range(114, 124))
+
+
+def test_threshold_empty_uint4_tier_with_published_thresholds():
+    # the MixKVQ page's R1-Qwen-14B thresholds (tau_BF16, tau_UINT4) = (1.52, 1.60):
+    # tau_BF16 <= tau_UINT4 leaves no A_d with tau_UINT4 < A_d <= tau_BF16
+    w, qb, kb, _ = tiny_inputs()
+    A = select.mixkvq_salience(qb, kb)
+    tier, _, _, n16, n4 = select.mixkvq_threshold_select(qb, kb, 128, 128, 1.52, 1.60)
+    assert n4 == 0 and not np.any(tier == select.TIER_U4)
+    assert n16 == sum(a > Fraction(1.52) for a in A)
+    # the Llama-8B pair (1.44, 0.79) gives all three tiers on the outlier workload
+    tier, _, _, n16, n4 = select.mixkvq_threshold_select(qb, kb, 128, 128, 1.44, 0.79)
+    assert n16 == sum(a > Fraction(1.44) for a in A)
+    assert n4 == sum(Fraction(0.79) < a <= Fraction(1.44) for a in A)
+
+
+def test_threshold_between_ranks_reproduces_count_mode():
+    w, qb, kb, _ = tiny_inputs()
+    A = select.mixkvq_salience(qb, kb)
+    tier_c, perm_c, rank = select.mixkvq_select(qb, kb, w.n_bf16, w.n_u4)
+    by_rank = sorted(range(128), key=lambda d: rank[d])
+    # A_d and the COUNT ranking key differ by a positive constant factor
+    assert all(A[by_rank[i]] >= A[by_rank[i + 1]] for i in range(127))
+
+    def between(i):   # a double strictly between the i-th and (i+1)-th salience
+        hi, lo = A[by_rank[i]], A[by_rank[i + 1]]
+        t = float((hi + lo) / 2)
+        assert lo < Fraction(t) < hi
+        return t
+    t16, t4 = between(w.n_bf16 - 1), between(w.n_bf16 + w.n_u4 - 1)
+    tier, perm, _, n16, n4 = select.mixkvq_threshold_select(qb, kb, 128, 128, t16, t4)
+    assert (n16, n4) == (w.n_bf16, w.n_u4)
+    assert np.array_equal(tier, tier_c) and np.array_equal(perm, perm_c)
