@@ -44,11 +44,28 @@ def sketch_bits(s_bits: np.ndarray, k_bits: np.ndarray) -> np.ndarray:
 
 
 def key_norms(k_bits: np.ndarray) -> np.ndarray:
-    """[T] binary16 bit patterns of ||k_t||_2, correctly rounded."""
-    out = np.zeros(k_bits.shape[0], dtype=np.uint16)
-    for t in range(k_bits.shape[0]):
-        s = sum((bf16_fraction(int(b)) ** 2 for b in k_bits[t]), Fraction(0))
-        out[t] = rn_f16_sqrt_bits(s)
+    """[T] binary16 bit patterns of ||k_t||_2, correctly rounded from the
+    exact sum of squares. A bf16 value is an integer significand s (< 256)
+    times 2^e, so its square is s^2 * 2^(2e): squares sharing an exponent add
+    exactly as integers, and the per-exponent sums are joined exactly with
+    Python integers on the smallest exponent of the row."""
+    b = np.asarray(k_bits, dtype=np.int64)
+    if np.any(((b >> 7) & 0xFF) == 0xFF):
+        raise ValueError("non-finite bf16")
+    e = (b >> 7) & 0xFF
+    sig = np.where(e > 0, (b & 0x7F) | 0x80, b & 0x7F)
+    ex2 = 2 * (np.maximum(e, 1) - 134)                 # value^2 = sig^2 * 2^ex2
+    sq = sig * sig
+    out = np.zeros(b.shape[0], dtype=np.uint16)
+    for t in range(b.shape[0]):
+        nz = sq[t] != 0
+        if not nz.any():
+            continue
+        lo = int(ex2[t][nz].min())
+        total = 0
+        for u in np.unique(ex2[t][nz]):
+            total += int(sq[t][nz & (ex2[t] == u)].sum()) << (int(u) - lo)
+        out[t] = rn_f16_sqrt_bits(Fraction(total) * Fraction(2) ** lo)
     return out
 
 
