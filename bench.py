@@ -161,6 +161,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="qwen32b_32k", help="extra decode-only workload ('' to skip)")
     ap.add_argument("--no-qjl", action="store_true", help="skip the QJL decodes (plain and outlier split)")
+    ap.add_argument("--no-pnmix", action="store_true", help="skip the PN-Mix decode and flush")
+    ap.add_argument("--no-fidelity", action="store_true", help="skip the per-workload fidelity (oracle, CPU)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--decode-only", action="store_true", help="time the decode call only (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
@@ -216,6 +218,11 @@ class Rig:
         if w.n_resid:
             rk[:, :, :w.n_resid] = k[:, :, t0:t0 + w.n_resid]
             rv[:, :, :w.n_resid] = v[:, :, t0:t0 + w.n_resid]
+        if w.n_resid < 128:   # the flush's source rows past the visible residual: the next tokens' K and V
+            nk, nv = synth.appended_kv(w, 128, dev)
+            rk[:, :, w.n_resid:] = nk[:, :, :128 - w.n_resid]
+            rv[:, :, w.n_resid:] = nv[:, :, :128 - w.n_resid]
+            del nk, nv
         self.sink_k = k[:, :, :w.n_sink].contiguous() if w.n_sink else None
         self.sink_v = v[:, :, :w.n_sink].contiguous() if w.n_sink else None
         del k, v
@@ -346,38 +353,88 @@ def graph_time(torch, calls, warmup_calls):
     return gpu_ms / len(calls), wall
 
 
-def cpu_baseline(w, synth, budget_s):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole (batch, kv head) slices of batch 0. A step is one page flush plus
-    one decode over all pages and the residual, as on the GPU. Every one of a
-    slice's page flushes (the prefill pages are built by the same flush) and
-    its decode are timed; the selection is setup and is not. While the time
-    budget lasts, the built slices are decoded again with the queries of
-    later decode steps. The step time is the mean flush time plus the mean
-    decode time. Runs single-threaded."""
-    from threadpoolctl import threadpool_limits
-    from oracle import attention as oatt, flush as oflush, select as osel
+def fidelity(w, synth):
+    """Fidelity context of the method on this data (not a parity gate), by the
+    oracle alone on the slice (batch 0, kv head 0): KL(p_bf16 || p_quantized)
+    of every query head of the group against exact attention over the
+    unquantized bf16 cache of the same visible tokens, the quantized output's
+    cosine and relative error, mean and worst over the heads."""
+    import numpy as np
+    from oracle import attention as oatt, flush as oflush, qjl as oqjl, select as osel
     w1 = w.scaled(batch=1)
     q, k, v = synth.prefill(w1, "cpu")
     bits = synth.bf16_bits
+    g, h = w.group, 0
+    qd = bits(synth.decode_query(w1, "cpu")[0, :g])
+    kb, vb = bits(k[0, h]), bits(v[0, h])
+    qb = bits(q[0, :g]) if w.key_mode != 2 else None
+    del q
+    ns, nq = w.n_sink, w.n_pages * 128
+    kw = dict(scale=1 / math.sqrt(128))
+    if w.key_mode == 0:
+        tier, perm, _ = osel.mixkvq_select(qb, kb[ns:ns + nq], w.n_bf16, w.n_u4)
+        pages = [oflush.flush_mixkvq_page(kb[ns + 128 * p:ns + 128 * p + 128], vb[ns + 128 * p:ns + 128 * p + 128],
+                                          perm, w.n_bf16, w.n_u4) for p in range(w.n_pages)]
+        extra = dict(n16=w.n_bf16, n4=w.n_u4, perm=perm)
+    elif w.key_mode == 1:
+        _, hi, rec = osel.pnmix_select(qb, kb, w.n_hi_pairs)
+        pages = [oflush.flush_pnmix_page(kb[ns + 128 * p:ns + 128 * p + 128], vb[ns + 128 * p:ns + 128 * p + 128], hi)
+                 for p in range(w.n_pages)]
+        extra = dict(mask_rec=rec)
+    else:
+        S = bits(synth.qjl_matrix(w1, "cpu"))
+        extra = dict(s_bits=S)
+        if w.qjl_outliers:
+            outl = oqjl.outlier_mask(kb, w.qjl_outliers)
+            pages = [oflush.flush_qjl_page(kb[128 * p:128 * p + 128], vb[128 * p:128 * p + 128], S, m=w.qjl_m,
+                                           outl=outl) for p in range(w.n_pages)]
+            extra.update(qjl_m=w.qjl_m, outl=outl)
+        else:
+            pages = [oflush.flush_qjl_page(kb[128 * p:128 * p + 128], vb[128 * p:128 * p + 128], S)
+                     for p in range(w.n_pages)]
+    if ns:
+        extra.update(sink_k=kb[:ns], sink_v=vb[:ns])
+    if w.n_resid:
+        extra.update(resid_k=kb[ns + nq:ns + nq + w.n_resid], resid_v=vb[ns + nq:ns + nq + w.n_resid])
+    out_q, p_q = oatt.decode_arena_head(w.key_mode, qd, pages, kw["scale"], **extra)
+    end = ns + nq + w.n_resid
+    out_r, p_r = oatt.reference_attention(qd, kb[:end], vb[:end], kw["scale"])
+    kl = [oatt.kl_divergence(a, b) for a, b in zip(p_r, p_q)]
+    cos = np.sum(out_q * out_r, -1) / (np.linalg.norm(out_q, axis=-1) * np.linalg.norm(out_r, axis=-1))
+    rel = np.max(np.abs(out_q - out_r), -1) / np.max(np.abs(out_r), -1)
+    return {"slice": "batch 0, kv head 0", "visible_tokens": end, "kl_mean": float(np.mean(kl)),
+            "kl_max": float(np.max(kl)), "cosine_mean": float(np.mean(cos)), "cosine_min": float(np.min(cos)),
+            "out_rel_err_max": float(np.max(rel))}
+
+
+def _cpu_worker(args):
+    """One host process of the CPU baseline: the oracle on whole (batch, kv
+    head) slices `heads` of the workload, single-threaded, until `budget_s`
+    of its own time is spent (see cpu_baseline)."""
+    name, heads, budget_s = args
+    import kvq_synth as synth
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oatt, flush as oflush, select as osel
+    w = synth.WORKLOADS[name]
+    bmax = max(b for b, _ in heads)
+    w1 = w.scaled(batch=bmax + 1)
+    q, k, v = synth.prefill(w1, "cpu")
+    bits = synth.bf16_bits
     g = w.group
-    per_slice_bytes = (decode_bytes(w) + flush_bytes(w)) / (w.batch * w.n_kv_heads)
     t_flush, n_flush, t_dec, n_dec = 0.0, 0, 0.0, 0
     built = []
 
-    def decode(h, pages, rec, kb, vb, step):
+    def decode(b, h, pages, perm, kb, vb, step):
         qd = synth.decode_query(w1, "cpu", step=step)
         t0 = time.perf_counter()
-        oatt.decode_arena_head(0, bits(qd[0, h * g:(h + 1) * g]), pages, 1 / math.sqrt(128), n16=w.n_bf16,
-                               n4=w.n_u4, perm=rec[:128], resid_k=kb[w.n_pages * 128:],
-                               resid_v=vb[w.n_pages * 128:])
+        oatt.decode_arena_head(0, bits(qd[b, h * g:(h + 1) * g]), pages, 1 / math.sqrt(128), n16=w.n_bf16,
+                               n4=w.n_u4, perm=perm, resid_k=kb[w.n_pages * 128:], resid_v=vb[w.n_pages * 128:])
         return time.perf_counter() - t0
 
     with threadpool_limits(limits=1):
-        for h in range(w.n_kv_heads):
-            qb, kb, vb = bits(q[0, h * g:(h + 1) * g]), bits(k[0, h]), bits(v[0, h])
+        for b, h in heads:
+            qb, kb, vb = bits(q[b, h * g:(h + 1) * g]), bits(k[b, h]), bits(v[b, h])
             tier, perm, _ = osel.mixkvq_select(qb, kb[:w.n_pages * 128], w.n_bf16, w.n_u4)
-            rec = osel.mixkvq_record(tier, perm)
             pages = []
             t0 = time.perf_counter()
             for p in range(w.n_pages):
@@ -385,21 +442,95 @@ def cpu_baseline(w, synth, budget_s):
                                                       perm, w.n_bf16, w.n_u4))
             t_flush += time.perf_counter() - t0
             n_flush += w.n_pages
-            t_dec += decode(h, pages, rec, kb, vb, 0)
+            t_dec += decode(b, h, pages, perm, kb, vb, 0)
             n_dec += 1
-            built.append((h, pages, rec, kb, vb))
+            built.append((b, h, pages, perm, kb, vb))
             if t_flush + t_dec > budget_s:
                 break
         step = 1
         while t_flush + t_dec <= budget_s:
-            for h, pages, rec, kb, vb in built:
-                t_dec += decode(h, pages, rec, kb, vb, step)
+            for b, h, pages, perm, kb, vb in built:
+                t_dec += decode(b, h, pages, perm, kb, vb, step)
                 n_dec += 1
                 if t_flush + t_dec > budget_s:
                     break
             step += 1
-    step_s = t_flush / n_flush + t_dec / n_dec
-    return per_slice_bytes / step_s / 1e9, len(built), t_flush + t_dec, n_flush, n_dec
+    return t_flush, n_flush, t_dec, n_dec, len(built)
+
+
+def host_cpu():
+    """(usable cores, capped at the 16 a one-GPU machine's host share allows; CPU model)."""
+    n = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return min(n, 16), n, model
+
+
+def cpu_baseline_parallel(w, budget_s):
+    """The oracle, as it stands, on the host's cores: one single-threaded
+    process per core, each on its own whole (batch, kv head) slices of the
+    workload (every page flush of the slice and its decode, then further
+    decodes with the queries of later steps while its budget lasts). A step
+    of a slice is one page flush plus one decode over all its pages and the
+    residual, as on the GPU; the rate is the bytes of all the processes'
+    flushes and decodes over the wall time."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    cores, avail, model = host_cpu()
+    slices = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)][:cores]
+    per = (decode_bytes(w) + flush_bytes(w)) / (w.batch * w.n_kv_heads)   # bytes of one slice step
+    flush_b = flush_bytes(w) / (w.batch * w.n_kv_heads)
+    dec_b = decode_bytes(w) / (w.batch * w.n_kv_heads)
+    t0 = time.perf_counter()
+    # fresh interpreters (spawn): forked copies of a process whose thread
+    # pools are running can deadlock
+    with ProcessPoolExecutor(max_workers=cores, mp_context=multiprocessing.get_context("spawn")) as ex:
+        res = list(ex.map(_cpu_worker, [(w.name, [bh], budget_s) for bh in slices]))
+    wall = time.perf_counter() - t0
+    n_flush = sum(r[1] for r in res)
+    n_dec = sum(r[3] for r in res)
+    busy = sum(r[0] + r[2] for r in res)
+    total = n_flush * flush_b + n_dec * dec_b
+    return {"value": total / busy * cores / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "host_cores_available": avail,
+            "sample": f"{len(slices)} (batch, kv head) slices of {w.name}, one single-threaded oracle process per "
+                      f"core: {n_flush} page flushes and {n_dec} decodes over {w.n_pages} pages + {w.n_resid} "
+                      f"residual tokens, {budget_s:.0f} s of timed work per process ({wall:.1f} s wall with "
+                      f"set-up); rate = algorithmic bytes of all of them / timed seconds per process",
+            "step_s_per_slice": per / (total / busy) if total else None}
+
+
+def cpu_tiny_one_thread(synth):
+    """The oracle on the tiny MixKVQ workload, one thread: one decode over 8
+    pages + 64 residual tokens, and one page flush, as s per step."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oatt, flush as oflush, select as osel
+    w = synth.WORKLOADS["tiny_mixkvq"]
+    q, k, v = synth.prefill(w, "cpu")
+    bits = synth.bf16_bits
+    qb, kb, vb = bits(q[0]), bits(k[0, 0]), bits(v[0, 0])
+    qd = bits(synth.decode_query(w, "cpu")[0])
+    with threadpool_limits(limits=1):
+        tier, perm, _ = osel.mixkvq_select(qb, kb[:w.n_pages * 128], w.n_bf16, w.n_u4)
+        t0 = time.perf_counter()
+        pages = [oflush.flush_mixkvq_page(kb[128 * p:128 * p + 128], vb[128 * p:128 * p + 128], perm, w.n_bf16,
+                                          w.n_u4) for p in range(w.n_pages)]
+        t_fl = (time.perf_counter() - t0) / w.n_pages
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oatt.decode_arena_head(0, qd, pages, 1 / math.sqrt(128), n16=w.n_bf16, n4=w.n_u4, perm=perm,
+                                   resid_k=kb[w.n_pages * 128:], resid_v=vb[w.n_pages * 128:])
+        t_dec = (time.perf_counter() - t0) / reps
+    return {"workload": w.name, "threads": 1, "flush_s_per_page": t_fl, "decode_s": t_dec,
+            "step_GBps": (decode_bytes(w) + flush_bytes(w)) / (t_fl + t_dec) / 1e9}
 
 
 def main():
@@ -412,6 +543,14 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU sharding is "
               "described in DESIGN.md but not run", file=sys.stderr)
         sys.exit(2)
+    # the CPU baseline runs first, in processes of its own, before this
+    # process touches the GPU
+    cpu = None
+    if not (args.no_cpu_baseline or args.summarize_pmc or args.copy_calibration or args.decode_only):
+        import kvq_synth as synth
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_parallel(synth.WORKLOADS[args.workload], args.cpu_seconds)
+        cpu["tiny_one_thread"] = cpu_tiny_one_thread(synth)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -489,8 +628,29 @@ def main():
         del rig2
         torch.cuda.empty_cache()
 
+    # PN-Mix H3/L1 (32 sinks + 16K quantized + 128 residual, batch 32): the
+    # decode over rotated cache copies and the flush of the residual
+    pnmix = {}
+    if not args.no_pnmix:
+        wp = synth.WORKLOADS["pnmix_16k"]
+        mbp = decode_bytes(wp) / 1e6
+        print(f"[bench] pnmix_16k: {mbp:.1f} MB per decode", file=sys.stderr, flush=True)
+        rp = Rig(wp, max(1, math.ceil(400.0 / mbp)), torch, kvq, synth)
+        kp = max(10, K // 2)
+        dp, _ = graph_time(torch, [lambda i=i: rp.decode(i) for i in range(kp)],
+                           [lambda i=i: rp.decode(i) for i in range(3)])
+        fp, _ = graph_time(torch, [lambda i=i: rp.flush(i) for i in range(kp)], [])
+        gb = decode_bytes(wp) / (dp * 1e-3) / 1e9
+        pnmix = {"workload": wp.name, "decode_ms": dp, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
+                 "bytes_per_decode": decode_bytes(wp), "cache_copies_rotated": len(rp.arenas),
+                 "flush_ms": fp, "flush_tokens_per_s": wp.batch * 128 / (fp * 1e-3),
+                 "flush_GBps": flush_bytes(wp) / (fp * 1e-3) / 1e9}
+        del rp
+        torch.cuda.empty_cache()
+
     # QJL at 32K context: the plain sketch and the outlier split (two sketch
-    # instances), decode calls over the resident cache
+    # instances), decode calls over the resident cache and the sketch flush
+    # of 128 new tokens
     qjl = {}
     if not args.no_qjl:
         for name in ("qjl_32k", "qjl_outlier_32k"):
@@ -499,8 +659,12 @@ def main():
             rq = Rig(wq, 1, torch, kvq, synth)
             kq = max(10, K // 2)
             dq, _ = graph_time(torch, [lambda: rq.decode(0)] * kq, [lambda: rq.decode(0)] * 3)
-            qjl[name] = {"decode_ms": dq, "decode_GBps": decode_bytes(wq) / (dq * 1e-3) / 1e9,
-                         "bytes_per_decode": decode_bytes(wq), "page_bytes_logical": logical_page_bytes(wq)}
+            fq, _ = graph_time(torch, [lambda: rq.flush(0)] * kq, [])
+            gb = decode_bytes(wq) / (dq * 1e-3) / 1e9
+            qjl[name] = {"decode_ms": dq, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
+                         "bytes_per_decode": decode_bytes(wq), "page_bytes_logical": logical_page_bytes(wq),
+                         "flush_ms": fq, "flush_tokens_per_s": wq.batch * 128 / (fq * 1e-3),
+                         "flush_GBps": flush_bytes(wq) / (fq * 1e-3) / 1e9}
             del rq
             torch.cuda.empty_cache()
 
@@ -524,14 +688,12 @@ def main():
         del rr
         torch.cuda.empty_cache()
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        gbps, slices, secs, n_flush, n_dec = cpu_baseline(w, synth, args.cpu_seconds)
-        cpu = {"value": gbps, "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{slices} (batch, kv head) slices of {w.name}: {n_flush} page flushes and {n_dec} decodes "
-                         f"over {w.n_pages} pages + {w.n_resid} residual tokens (queries of successive decode "
-                         f"steps), step = mean flush + mean decode; {secs:.1f} s timed, single-threaded"}
+
+    fid = {}
+    if not args.no_fidelity:
+        for name in ("llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"):
+            print(f"[bench] fidelity {name} (oracle)", file=sys.stderr, flush=True)
+            fid[name] = fidelity(synth.WORKLOADS[name], synth)
 
     line = {
         "metric": METRIC,
@@ -565,8 +727,10 @@ def main():
                      "kernel": "kvq_decode_attention (decode_mix_fast + combine_kernel)",
                      "bytes_per_launch": dbytes},
         "secondary": extra,
+        "pnmix": pnmix,
         "reselect_per_flush": resel,
         "qjl_decode": qjl,
+        "fidelity": fid,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -39,16 +39,17 @@ def salience_quantiles(w, qs):
 
 
 CASES = [
-    # (workload, its reshaping, quantiles of tau_bf16 / tau_u4, capacities)
-    ("llama8b_8k", dict(batch=2, n_kv_heads=4, n_q_heads=16, n_pages=3, n_resid=40), (0.93, 0.7), (32, 64)),
-    ("llama8b_8k", dict(batch=2, n_kv_heads=4, n_q_heads=16, n_pages=3, n_resid=40), (0.9, 0.5), (4, 8)),
-    ("qwen32b_32k", dict(batch=2, n_kv_heads=2, n_q_heads=16, n_pages=2, n_resid=0), (0.97, 0.8), (8, 40)),
-    ("tiny_mixkvq", dict(), (0.5, 0.6), (128, 0)),   # tau_bf16 < tau_u4: no UINT4 tier
+    # (workload, its reshaping, quantiles of tau_bf16 / tau_u4, capacities, what the counts show)
+    ("llama8b_8k", dict(batch=2, n_kv_heads=4, n_q_heads=16, n_pages=3, n_resid=40), (0.93, 0.7), (32, 64), "varied"),
+    # about 13 BF16 and 51 UINT4 candidates per head: both capacities overflow
+    ("llama8b_8k", dict(batch=2, n_kv_heads=4, n_q_heads=16, n_pages=3, n_resid=40), (0.9, 0.5), (4, 8), "full"),
+    ("qwen32b_32k", dict(batch=2, n_kv_heads=2, n_q_heads=16, n_pages=2, n_resid=0), (0.97, 0.8), (8, 40), "varied"),
+    ("tiny_mixkvq", dict(), (0.5, 0.6), (128, 0), "no_u4"),   # tau_bf16 < tau_u4: no UINT4 tier
 ]
 
 
-@pytest.mark.parametrize("name,shape,quant,caps", CASES)
-def test_threshold_records_pages_decode(name, shape, quant, caps):
+@pytest.mark.parametrize("name,shape,quant,caps,expect", CASES)
+def test_threshold_records_pages_decode(name, shape, quant, caps, expect):
     base = synth.WORKLOADS[name]
     w = base.scaled(n_bf16=caps[0], n_u4=caps[1], seed=base.seed + 300, **shape)
     tau = tuple(salience_quantiles(w, quant))
@@ -78,8 +79,10 @@ def test_threshold_records_pages_decode(name, shape, quant, caps):
                 err = rel_err(out.cpu().numpy()[b, h * g:(h + 1) * g], ref_out)
                 assert np.all(err <= TOL), (tag, b, h, err)
     print(f"[threshold] {name}: tier counts (BF16, UINT4) per head: {sorted(counts)}")
-    if caps[1] == 0 or quant[0] < quant[1]:
+    if expect == "no_u4":
         assert all(n4 == 0 for _, n4 in counts)
+    elif expect == "full":
+        assert counts == {caps}
     else:
         assert len(counts) > 1   # the heads' counts differ: per-head page layouts are exercised
 
