@@ -4,8 +4,9 @@
  *
  * Plain C ABI: every argument is a host pointer, a device pointer or a size.
  * The caller owns every buffer and the HIP stream; the library never
- * allocates, frees or synchronizes, keeps no mutable global state and is
- * safe to call from several threads. Every call validates its arguments on
+ * allocates, frees or synchronizes, keeps no mutable global state (apart from
+ * the per-GPU scratch array of kvq_decode_attention_noalloc) and is safe to
+ * call from several threads. Every call validates its arguments on
  * the host first; on an error it returns a status and launches nothing, and
  * no output is touched. Device pointers must be 16-byte aligned (page tables:
  * 4-byte). Kernels are
@@ -312,6 +313,24 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
                                 const void* resid_k, const void* resid_v, int32_t n_resid,
                                 int32_t resid_stride, float softmax_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* kvq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The split partials (and QJL's S q) go to
+ * a scratch array of KVQ_NOALLOC_SCRATCH_BYTES that the library keeps on
+ * every GPU it runs on until the process ends; this call allocates nothing
+ * and calls no allocating routine. Arguments and results as
+ * kvq_decode_attention. Returns KVQ_WORKSPACE_TOO_SMALL when the call would
+ * need more scratch than that (kvq_workspace_bytes(cfg, n_pages) >
+ * KVQ_NOALLOC_SCRATCH_BYTES), KVQ_HIP_ERROR if the array's device address
+ * cannot be found. All calls on one GPU share its array: calls that overlap
+ * on one GPU (on different streams, or from several threads) race. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const void* q, const void* page_arena,
+                                        const int32_t* page_table, int32_t table_stride, int32_t n_pages,
+                                        const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
+                                        int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
+                                        int32_t resid_stride, float softmax_scale, float* out, void* stream);
 
 /* kvq_decode_attention, then kvq_flush_quantize, in one call: the decode step
  * at which the residual has filled and is packed into the next page (KIVI

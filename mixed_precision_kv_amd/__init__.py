@@ -27,8 +27,9 @@ EXPORTED = (
     "kvq_abi_version", "kvq_status_string", "kvq_page_bytes", "kvq_mask_bytes",
     "kvq_workspace_bytes", "kvq_storage_bytes", "kvq_select_channels",
     "kvq_flush_quantize", "kvq_decode_attention", "kvq_decode_attention_flush",
-    "kvq_accumulate_query", "kvq_flush_reselect",
+    "kvq_accumulate_query", "kvq_flush_reselect", "kvq_decode_attention_noalloc",
 )
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class KvqConfig(ctypes.Structure):
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
                                        P, P, SZ, P]),
         "kvq_decode_attention_flush": (I32, [cfgp, P, P, P, I32, I32, P, P, P, P, I32, P, P, I32, I32,
                                              ctypes.c_float, P, P, SZ, P, P, I64, I32, I32, P, P]),
+        "kvq_decode_attention_noalloc": (I32, [cfgp, P, P, P, I32, I32, P, P, P, P, I32, P, P, I32, I32,
+                                               ctypes.c_float, P, P]),
         "kvq_accumulate_query": (I32, [cfgp, P, I64, I64, P, P]),
         "kvq_flush_reselect": (I32, [cfgp, P, P, I64, I32, P, P, P, P, I32, I32, P, P]),
     }
@@ -231,3 +234,13 @@ def kvq_decode_attention(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_
         _ptr(qjl_s), _ptr(sink_k),
         _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride, softmax_scale, _ptr(out),
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kvq_decode_attention_noalloc(cfg, q, page_arena, n_pages, mask, qjl_s, sink_k, sink_v, n_sink, resid_k, resid_v,
+                                 n_resid, resid_stride, softmax_scale, out, *, page_table=None, table_stride=0,
+                                 stream=None):
+    """kvq_decode_attention with the library's per-GPU scratch instead of a workspace."""
+    _check("kvq_decode_attention_noalloc", load().kvq_decode_attention_noalloc(
+        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), _ptr(page_table), table_stride, n_pages, _ptr(mask),
+        _ptr(qjl_s), _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride,
+        softmax_scale, _ptr(out), _stream(stream)))

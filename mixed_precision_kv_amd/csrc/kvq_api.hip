@@ -5,6 +5,9 @@
 #include <stddef.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kvq_internal.h"
 
 // the layout every binding mirrors (18 int32, then the two thresholds)
@@ -209,6 +212,37 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
 }
 
 static bool generic_decode(const kvq_config* c) { return c->decode_path == KVQ_DECODE_GENERIC; }
+
+// ------------------------------------------------------------------ allocation-free decode
+// The decode's scratch (split partials, QJL S q) for callers that cannot
+// allocate: one array per GPU, kept until the process ends. In host code the
+// array's name is only a stand-in; its device address, different on every
+// GPU, is looked up once per device (with that device current) and used
+// wherever the host needs the array.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)KVQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+static std::atomic<void*> scratch_ptr[MAX_DEVICES];
+static std::mutex scratch_mu;
+
+static hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 }  // namespace kvq
 
 using namespace kvq;
@@ -385,6 +419,27 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
   const kvq_status st = decode_prepare(cfg, q, page_arena, page_table, table_stride, n_pages, mask, qjl_s, sink_k,
                                        sink_v, n_sink, resid_k, resid_v, n_resid, resid_stride, softmax_scale, out,
                                        workspace, workspace_bytes, a);
+  if (st != KVQ_OK) return st;
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, generic_decode(cfg)) ==
+                 hipSuccess
+             ? KVQ_OK
+             : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const void* q, const void* page_arena,
+                                        const int32_t* page_table, int32_t table_stride, int32_t n_pages,
+                                        const void* mask, const void* qjl_s, const void* sink_k, const void* sink_v,
+                                        int32_t n_sink, const void* resid_k, const void* resid_v, int32_t n_resid,
+                                        int32_t resid_stride, float softmax_scale, float* out, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (n_pages < 0 || n_pages > (page_table ? table_stride : cfg->max_pages)) return KVQ_INVALID_ARG;
+  if (workspace_for(cfg, n_pages) > NOALLOC_SCRATCH_BYTES) return KVQ_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return KVQ_HIP_ERROR;
+  DecodeArgs a;
+  st = decode_prepare(cfg, q, page_arena, page_table, table_stride, n_pages, mask, qjl_s, sink_k, sink_v, n_sink,
+                      resid_k, resid_v, n_resid, resid_stride, softmax_scale, out, ws, NOALLOC_SCRATCH_BYTES, a);
   if (st != KVQ_OK) return st;
   return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, generic_decode(cfg)) ==
                  hipSuccess
