@@ -314,6 +314,55 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
                                 int32_t resid_stride, float softmax_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* KIVI's Value FIFO (KIVI blog sections 4-5), the residual policy in which
+ * Keys are sealed a whole 128-token segment at a time but Values leave the
+ * full-precision residual one token at a time, once R = 128 newer tokens
+ * follow. A Value's codes (per token, 32-channel groups) do not depend on when
+ * it is quantized, so pages keep their layout: kvq_flush_keys seals the Keys
+ * of full segments and clears the pages' Value parts, kvq_value_push
+ * quantizes the Value rows that leave the window into their pages, and
+ * kvq_decode_attention_fifo attends with the Key boundary and the Value
+ * boundary apart (one global softmax). Not with cfg->page_records. */
+
+/* kvq_flush_quantize for the Value FIFO: the Keys of pages first_page ..
+ * first_page + n_pages - 1 quantized and packed as kvq_flush_quantize does,
+ * their Value parts cleared (codes, scales and offsets zero); v_src is not
+ * read (may equal k_src). Same arguments, errors and flags. */
+kvq_status kvq_flush_keys(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
+                          int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
+                          const int32_t* page_table, int32_t table_stride, int32_t first_page,
+                          uint32_t* status_flags, void* stream);
+
+/* The Value rows of tokens first_token .. first_token + n_rows - 1 of every
+ * (batch, kv head), leaving the full-precision window: each quantized per token
+ * (four groups of 32 channels, 2 bits, the flush's quantizer, flags as there)
+ * and ORed into its page (logical page token / 128, row token % 128). The
+ * pages must hold sealed Keys (kvq_flush_keys) and these rows must not have
+ * been pushed before: the push adds bits to the cleared Value part.
+ * v_src: device bf16 [batch][n_kv_heads][src_stride][128], row j = token
+ * first_token + j. mask, page_arena, page_table, table_stride, status_flags:
+ * as kvq_flush_quantize. KVQ_CAPACITY if a row's page is past max_pages (or
+ * table_stride). */
+kvq_status kvq_value_push(const kvq_config* cfg, const void* v_src, int64_t src_stride, int32_t n_rows,
+                          int32_t first_token, const void* mask, void* page_arena, const int32_t* page_table,
+                          int32_t table_stride, uint32_t* status_flags, void* stream);
+
+/* Decode attention with the Value FIFO: the visible tokens are n_pages * 128
+ * sealed Keys (pages) followed by n_kres Key-residual rows (resid_k,
+ * [batch][n_kv_heads][kres_stride][128] bf16); the Values of tokens 0 ..
+ * n_vq - 1 are the pages' quantized rows and those of tokens n_vq .. T - 1
+ * the window rows (vwin, [batch][n_kv_heads][vwin_stride][128] bf16, row j =
+ * token n_vq + j), T = n_pages * 128 + n_kres = n_vq + n_vwin. Constraints:
+ * n_vq <= n_pages * 128, 0 <= n_kres <= 128, n_vwin <= 256. Logits and the
+ * global softmax as kvq_decode_attention; the generic decode kernel runs.
+ * Other arguments and the workspace as kvq_decode_attention. */
+kvq_status kvq_decode_attention_fifo(const kvq_config* cfg, const void* q, const void* page_arena,
+                                     const int32_t* page_table, int32_t table_stride, int32_t n_pages,
+                                     int32_t n_vq, const void* mask, const void* qjl_s, const void* resid_k,
+                                     int32_t n_kres, int32_t kres_stride, const void* vwin, int32_t n_vwin,
+                                     int32_t vwin_stride, float softmax_scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* kvq_decode_attention without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). The split partials (and QJL's S q) go to

@@ -28,6 +28,7 @@ EXPORTED = (
     "kvq_workspace_bytes", "kvq_storage_bytes", "kvq_select_channels",
     "kvq_flush_quantize", "kvq_decode_attention", "kvq_decode_attention_flush",
     "kvq_accumulate_query", "kvq_flush_reselect", "kvq_decode_attention_noalloc",
+    "kvq_flush_keys", "kvq_value_push", "kvq_decode_attention_fifo",
 )
 KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH):
                                              ctypes.c_float, P, P, SZ, P, P, I64, I32, I32, P, P]),
         "kvq_decode_attention_noalloc": (I32, [cfgp, P, P, P, I32, I32, P, P, P, P, I32, P, P, I32, I32,
                                                ctypes.c_float, P, P]),
+        "kvq_flush_keys": (I32, [cfgp, P, P, I64, I32, P, P, P, P, I32, I32, P, P]),
+        "kvq_value_push": (I32, [cfgp, P, I64, I32, I32, P, P, P, I32, P, P]),
+        "kvq_decode_attention_fifo": (I32, [cfgp, P, P, P, I32, I32, I32, P, P, P, I32, I32, P, I32, I32,
+                                            ctypes.c_float, P, P, SZ, P]),
         "kvq_accumulate_query": (I32, [cfgp, P, I64, I64, P, P]),
         "kvq_flush_reselect": (I32, [cfgp, P, P, I64, I32, P, P, P, P, I32, I32, P, P]),
     }
@@ -244,3 +249,29 @@ def kvq_decode_attention_noalloc(cfg, q, page_arena, n_pages, mask, qjl_s, sink_
         ctypes.byref(cfg), _ptr(q), _ptr(page_arena), _ptr(page_table), table_stride, n_pages, _ptr(mask),
         _ptr(qjl_s), _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride,
         softmax_scale, _ptr(out), _stream(stream)))
+
+
+def kvq_flush_keys(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, first_page, status_flags, *,
+                   page_table=None, table_stride=0, stream=None):
+    """The Value-FIFO seal: Keys packed, the pages' Value parts cleared."""
+    _check("kvq_flush_keys", load().kvq_flush_keys(
+        ctypes.byref(cfg), _ptr(k_src), _ptr(v_src), src_stride, n_pages, _ptr(mask), _ptr(qjl_s),
+        _ptr(page_arena), _ptr(page_table), table_stride, first_page, _ptr(status_flags), _stream(stream)))
+
+
+def kvq_value_push(cfg, v_src, src_stride, n_rows, first_token, mask, page_arena, status_flags, *,
+                   page_table=None, table_stride=0, stream=None):
+    _check("kvq_value_push", load().kvq_value_push(
+        ctypes.byref(cfg), _ptr(v_src), src_stride, n_rows, first_token, _ptr(mask), _ptr(page_arena),
+        _ptr(page_table), table_stride, _ptr(status_flags), _stream(stream)))
+
+
+def kvq_decode_attention_fifo(cfg, q, page_arena, n_pages, n_vq, mask, qjl_s, resid_k, n_kres, kres_stride, vwin,
+                              n_vwin, vwin_stride, softmax_scale, out, workspace, workspace_bytes=None, *,
+                              page_table=None, table_stride=0, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("kvq_decode_attention_fifo", load().kvq_decode_attention_fifo(
+        ctypes.byref(cfg), _ptr(q), _ptr(page_arena), _ptr(page_table), table_stride, n_pages, n_vq, _ptr(mask),
+        _ptr(qjl_s), _ptr(resid_k), n_kres, kres_stride, _ptr(vwin), n_vwin, vwin_stride, softmax_scale, _ptr(out),
+        _ptr(workspace), workspace_bytes, _stream(stream)))

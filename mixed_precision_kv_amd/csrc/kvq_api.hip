@@ -90,12 +90,18 @@ static int n_page_splits(const kvq_config* c, int n_pages) {
   return (n_pages + pps - 1) / pps;
 }
 
-static size_t workspace_for(const kvq_config* c, int n_pages) {
-  // the page splits plus the most segment workgroups any call can have
+// Workspace of a decode call: [split partials | QJL S q]. The partials hold
+// the page splits plus the most segment workgroups any call can have.
+static size_t partial_bytes(const kvq_config* c, int n_pages) {
   size_t splits = (size_t)n_page_splits(c, n_pages) + MAX_SEG_SPLITS;
-  size_t rows = (size_t)c->batch * c->n_q_heads;
-  size_t bytes = splits * rows * 130 * sizeof(float);
-  if (c->key_mode == KVQ_KEY_QJL) bytes += rows * (size_t)(c->qjl_m + c->qjl_m_out) * sizeof(float);
+  return splits * (size_t)c->batch * c->n_q_heads * RECORD * sizeof(float);
+}
+static size_t sq_bytes(const kvq_config* c) {
+  if (c->key_mode != KVQ_KEY_QJL) return 0;
+  return (size_t)c->batch * c->n_q_heads * (size_t)(c->qjl_m + c->qjl_m_out) * sizeof(float);
+}
+static size_t workspace_for(const kvq_config* c, int n_pages) {
+  size_t bytes = partial_bytes(c, n_pages) + sq_bytes(c);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -144,6 +150,9 @@ static kvq_status flush_prepare(const kvq_config* cfg, const void* k_src, const 
   a.rec_out = nullptr;
   a.rec_stride = 0;
   a.head_tiers = head_tiers(cfg) ? 1 : 0;
+  a.keys_only = 0;
+  a.push_first = 0;
+  a.push_rows = 0;
   return KVQ_OK;
 }
 
@@ -184,10 +193,11 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.pps = n_pages > 0 ? decode_pages_per_split(n_pages, cfg->batch, cfg->n_kv_heads) : 1;
   a.n_page_splits = n_page_splits(cfg, n_pages);
   a.mask = (const uint8_t*)mask;
-  const size_t rows = (size_t)cfg->batch * cfg->n_q_heads;
-  const size_t part_bytes = ((size_t)a.n_page_splits + MAX_SEG_SPLITS) * rows * 130 * sizeof(float);
   a.partial = (float*)workspace;
-  a.sq = (const float*)((uint8_t*)workspace + part_bytes);
+  a.sq = (const float*)((uint8_t*)workspace + partial_bytes(cfg, n_pages));
+  a.vq_end = INT32_MAX;   // no KIVI Value FIFO: every page token's Value is quantized
+  a.vwin = nullptr;
+  a.vwin_stride = 0;
   a.out = out;
   a.sink_k = (const uint16_t*)sink_k;
   a.sink_v = (const uint16_t*)sink_v;
@@ -196,6 +206,7 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.resid_v = (const uint16_t*)resid_v;
   a.n_resid = n_resid;
   a.resid_stride = resid_stride;
+  a.resid_v_stride = resid_stride;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.qjl_coef = cfg->key_mode == KVQ_KEY_QJL ? (float)(sqrt(M_PI / 2.0) / cfg->qjl_m) : 0.f;
   a.batch = cfg->batch;
@@ -211,7 +222,6 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   return KVQ_OK;
 }
 
-static bool generic_decode(const kvq_config* c) { return c->decode_path == KVQ_DECODE_GENERIC; }
 
 // ------------------------------------------------------------------ allocation-free decode
 // The decode's scratch (split partials, QJL S q) for callers that cannot
@@ -420,7 +430,92 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const void* q, const void
                                        sink_v, n_sink, resid_k, resid_v, n_resid, resid_stride, softmax_scale, out,
                                        workspace, workspace_bytes, a);
   if (st != KVQ_OK) return st;
-  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, generic_decode(cfg)) ==
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, cfg->decode_path) ==
+                 hipSuccess
+             ? KVQ_OK
+             : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_flush_keys(const kvq_config* cfg, const void* k_src, const void* v_src, int64_t src_stride,
+                          int32_t n_pages, const void* mask, const void* qjl_s, void* page_arena,
+                          const int32_t* page_table, int32_t table_stride, int32_t first_page,
+                          uint32_t* status_flags, void* stream) {
+  FlushArgs a;
+  const kvq_status st = flush_prepare(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, page_table,
+                                      table_stride, first_page, status_flags, a);
+  if (st != KVQ_OK || n_pages == 0) return st;
+  if (cfg->page_records) return KVQ_UNSUPPORTED;
+  a.keys_only = 1;
+  return launch_flush(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_value_push(const kvq_config* cfg, const void* v_src, int64_t src_stride, int32_t n_rows,
+                          int32_t first_token, const void* mask, void* page_arena, const int32_t* page_table,
+                          int32_t table_stride, uint32_t* status_flags, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (cfg->page_records) return KVQ_UNSUPPORTED;
+  if (!v_src || !page_arena || !status_flags || !aligned16(v_src) || !aligned16(page_arena)) return KVQ_INVALID_ARG;
+  if (page_table && (table_stride < 1 || ((uintptr_t)page_table & 3u))) return KVQ_INVALID_ARG;
+  if (n_rows < 0 || first_token < 0 || src_stride < n_rows) return KVQ_INVALID_ARG;
+  if (n_rows == 0) return KVQ_OK;
+  const int64_t last_page = ((int64_t)first_token + n_rows - 1) / PAGE;
+  if (last_page >= (page_table ? table_stride : cfg->max_pages)) return KVQ_CAPACITY;
+  if (head_tiers(cfg) && (!mask || !aligned16(mask))) return KVQ_INVALID_ARG;
+  if ((int64_t)cfg->batch * cfg->n_kv_heads * n_rows > INT32_MAX) return KVQ_INVALID_ARG;
+  FlushArgs a;
+  memset(&a, 0, sizeof(a));
+  a.v_src = (const uint16_t*)v_src;
+  a.src_stride = src_stride;
+  a.mask = (const uint8_t*)mask;
+  a.arena = (uint8_t*)page_arena;
+  a.page_stride = (int64_t)page_stride(cfg);
+  a.table = page_table;
+  a.table_stride = page_table ? table_stride : 0;
+  a.pool_pages = pool_pages(cfg);
+  a.max_pages = cfg->max_pages;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.n16 = cfg->n_bf16;
+  a.n4 = cfg->n_u4;
+  a.n_hi = 2 * cfg->n_hi_pairs;
+  a.qjl_m = cfg->qjl_m;
+  a.qjl_mo = cfg->qjl_m_out;
+  a.flags = status_flags;
+  a.head_tiers = head_tiers(cfg) ? 1 : 0;
+  a.push_first = first_token;
+  a.push_rows = n_rows;
+  return launch_value_push(cfg->key_mode, a, cfg->batch, (hipStream_t)stream) == hipSuccess ? KVQ_OK
+                                                                                            : KVQ_HIP_ERROR;
+}
+
+kvq_status kvq_decode_attention_fifo(const kvq_config* cfg, const void* q, const void* page_arena,
+                                     const int32_t* page_table, int32_t table_stride, int32_t n_pages,
+                                     int32_t n_vq, const void* mask, const void* qjl_s, const void* resid_k,
+                                     int32_t n_kres, int32_t kres_stride, const void* vwin, int32_t n_vwin,
+                                     int32_t vwin_stride, float softmax_scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (cfg->page_records) return KVQ_UNSUPPORTED;
+  if (n_pages < 0 || n_vq < 0 || n_kres < 0 || n_kres > PAGE || n_vwin < 0 || n_vwin > 2 * PAGE)
+    return KVQ_INVALID_ARG;
+  if (n_vq > (int64_t)n_pages * PAGE || (int64_t)n_pages * PAGE + n_kres != (int64_t)n_vq + n_vwin)
+    return KVQ_INVALID_ARG;
+  if (n_vwin > 0 && (!vwin || !aligned16(vwin) || vwin_stride < n_vwin)) return KVQ_INVALID_ARG;
+  if (n_kres > 0 && kres_stride < n_kres) return KVQ_INVALID_ARG;
+  // the Key residual's Values are the window's last n_kres rows (256-byte steps: alignment kept)
+  const int kres_row = n_pages * PAGE - n_vq;
+  const void* resid_v = n_kres > 0 ? (const void*)((const uint16_t*)vwin + (size_t)kres_row * D) : nullptr;
+  DecodeArgs a;
+  st = decode_prepare(cfg, q, page_arena, page_table, table_stride, n_pages, mask, qjl_s, nullptr, nullptr, 0,
+                      resid_k, resid_v, n_kres, n_kres > 0 ? kres_stride : 0, softmax_scale, out, workspace,
+                      workspace_bytes, a);
+  if (st != KVQ_OK) return st;
+  a.resid_v_stride = vwin_stride;
+  a.vq_end = n_vq;
+  a.vwin = (const uint16_t*)vwin;
+  a.vwin_stride = vwin_stride;
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, KVQ_DECODE_GENERIC) ==
                  hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;
@@ -441,7 +536,7 @@ kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const void* q, co
   st = decode_prepare(cfg, q, page_arena, page_table, table_stride, n_pages, mask, qjl_s, sink_k, sink_v, n_sink,
                       resid_k, resid_v, n_resid, resid_stride, softmax_scale, out, ws, NOALLOC_SCRATCH_BYTES, a);
   if (st != KVQ_OK) return st;
-  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, generic_decode(cfg)) ==
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, cfg->decode_path) ==
                  hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;
@@ -466,7 +561,8 @@ kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void
   if (st != KVQ_OK) return st;
   if (cfg->page_records) return KVQ_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
-  if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false, generic_decode(cfg)) != hipSuccess)
+  // the split kernels, then one launch holding the flush and the split merge
+  if (launch_decode(cfg->key_mode, d, (const uint16_t*)qjl_s, s, false, cfg->decode_path) != hipSuccess)
     return KVQ_HIP_ERROR;
   return launch_merge_flush(cfg->key_mode, d, f, cfg->batch, s) == hipSuccess ? KVQ_OK : KVQ_HIP_ERROR;
 }

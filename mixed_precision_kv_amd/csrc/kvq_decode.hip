@@ -46,12 +46,56 @@ struct DecodeSmem {
   float mh[16];
 };
 
+// KIVI Value FIFO (KIVI blog sections 4-5): tokens of page pg from vlim on
+// have sealed Keys but their Values still in the full-precision window (row
+// pg * 128 + t - vq_end). Their probabilities, staged in hp by the HYB
+// consume_values, weight those rows here; lane l owns channels 2l, 2l+1 of
+// every head.
+template <int G>
+__device__ inline void fifo_values(const DecodeArgs& A, int64_t head, int pg, int vlim, float (*hp)[8],
+                                   float (&ow)[8][2], int lane) {
+  __syncthreads();   // hp written
+  for (int t = max(vlim, 0); t < PAGE; ++t) {
+    const int64_t row = (int64_t)pg * PAGE + t - A.vq_end;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(A.vwin + (head * A.vwin_stride + row) * D)[lane];
+    const float v0 = lo_bf(w), v1 = hi_bf(w);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      ow[hh][0] = fmaf(hp[t][hh], v0, ow[hh][0]);
+      ow[hh][1] = fmaf(hp[t][hh], v1, ow[hh][1]);
+    }
+  }
+  __syncthreads();   // hp free for the next page
+}
+
+// The page's first token whose Value is not quantized yet (PAGE: all are).
+__device__ inline int fifo_vlim(const DecodeArgs& A, int pg) {
+  return (int)min((int64_t)PAGE, max((int64_t)0, (int64_t)A.vq_end - (int64_t)pg * PAGE));
+}
+
+// After a page's consume_values: ow follows the running maximum like the
+// value accumulators, then takes the page's full-precision Values.
+template <int G, int NPASS>
+__device__ inline void fifo_after(const DecodeArgs& A, const SoftState<NPASS>& st, float m0, int64_t head, int pg,
+                                  int vlim, float (*hp)[8], float (&ow)[8][2], int lane) {
+  if (st.m != m0) {
+    const float alpha = m0 == -INFINITY ? 0.f : fast_exp2(m0 - st.m);
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) ow[hh][0] *= alpha, ow[hh][1] *= alpha;
+  }
+  if (vlim < PAGE) fifo_values<G>(A, head, pg, vlim, hp, ow, lane);
+}
+
 // ------------------------------------------------------------------ decode kernel
-template <int MODE, int G>
+// FIFO: KIVI Value-FIFO decodes (tokens from A.vq_end on take full-precision
+// Values); their probability staging hp[PAGE][8] is the launch's dynamic LDS.
+template <int MODE, int G, bool FIFO>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
   __shared__ DecodeSmem S;
+  extern __shared__ float fifo_lds[];
+  float (*hp)[8] = reinterpret_cast<float (*)[8]>(fifo_lds);
   const DecodeBlock blk = decode_block(A);
   const int split = blk.split, kvh = blk.kvh, b = blk.b;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r;
@@ -70,6 +114,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
     S.qf[i / D][i % D] = bf16_to_f32(A.q[((int64_t)b * A.n_q_heads + kvh * G + i / D) * D + i % D]);
   SoftState<NPASS> st;
   init_state(st);
+  float ow[8][2];   // KIVI Value FIFO: full-precision Values of the split's pages, lane's channels
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) ow[hh][0] = ow[hh][1] = 0.f;
   const int p0 = split * A.pps;
   const int p1 = min(A.n_pages, p0 + A.pps);
 
@@ -158,8 +205,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         }
       }
       bias = wave_sum_groups(bias);
-      consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES,
-                                page + g.off_v + V_CODE_BYTES + 1024, a, col);
+      const uint8_t *vlo = page + g.off_v + V_CODE_BYTES, *vhi = vlo + 1024;
+      if constexpr (FIFO) {
+        const int vlim = fifo_vlim(A, pg);
+        const float m0 = st.m;
+        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
+        else consume_values<G, NPASS, true>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col, vlim, hp);
+        fifo_after<G, NPASS>(A, st, m0, head, pg, vlim, hp, ow, lane);
+      } else {
+        consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
+      }
     }
   } else if constexpr (MODE == KVQ_KEY_PNMIX) {
     const PnGeo g = pn_geo(A.n_hi);
@@ -225,8 +280,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
       bias = wave_sum_groups(bias);
-      consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, page + g.off_v + V_CODE_BYTES,
-                                page + g.off_v + V_CODE_BYTES + 1024, a, col);
+      const uint8_t *vlo = page + g.off_v + V_CODE_BYTES, *vhi = vlo + 1024;
+      if constexpr (FIFO) {
+        const int vlim = fifo_vlim(A, pg);
+        const float m0 = st.m;
+        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
+        else consume_values<G, NPASS, true>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col, vlim, hp);
+        fifo_after<G, NPASS>(A, st, m0, head, pg, vlim, hp, ow, lane);
+      } else {
+        consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
+      }
     }
   } else {   // QJL
     // with the outlier split, k-steps NKI.. are the outlier instance: its
@@ -305,45 +368,76 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
           }
         }
       }
-      consume_values<G, NPASS>(st, logit, xs, 0.f, vc, page + g.off_v + V_CODE_BYTES,
-                                page + g.off_v + V_CODE_BYTES + 1024, a, col);
+      const uint8_t *vlo = page + g.off_v + V_CODE_BYTES, *vhi = vlo + 1024;
+      if constexpr (FIFO) {
+        const int vlim = fifo_vlim(A, pg);
+        const float m0 = st.m;
+        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, 0.f, vc, vlo, vhi, a, col);
+        else consume_values<G, NPASS, true>(st, logit, xs, 0.f, vc, vlo, vhi, a, col, vlim, hp);
+        fifo_after<G, NPASS>(A, st, m0, head, pg, vlim, hp, ow, lane);
+      } else {
+        consume_values<G, NPASS>(st, logit, xs, 0.f, vc, vlo, vhi, a, col);
+      }
     }
   }
   __syncthreads();
-  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, stage_buf(S));
+  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, stage_buf(S), FIFO ? ow : nullptr);
 }
 
-// QJL projection: S q for every query head (float accumulation of bf16
-// products), m + mo values per head. With the outlier split the first m rows
-// see q's normal channels and the mo outlier-instance rows its outlier
-// channels (the head's record in mask; without pages there is no record and
-// the values are not read).
-__global__ __launch_bounds__(256) void qjl_project_kernel(const uint16_t* q, const uint16_t* S, float* sq, int m,
-                                                          int mo, const uint8_t* mask, int n_rows, int n_q_heads,
-                                                          int group) {
-  const int row = blockIdx.x;          // (b, hq)
-  if (row >= n_rows) return;
-  __shared__ float qs[2][D];           // normal / outlier channels of q
-  if (threadIdx.x < D) {
-    const int d = threadIdx.x;
-    const float x = bf16_to_f32(q[(int64_t)row * D + d]);
-    bool outlier = false;
-    if (mo > 0 && mask != nullptr) {
-      const int b = row / n_q_heads, kvh = (row - b * n_q_heads) / group;
-      const uint8_t* rec = mask + ((int64_t)b * (n_q_heads / group) + kvh) * QJL_RECORD;
-      outlier = (rec[d >> 3] >> (d & 7)) & 1;
-    }
-    qs[0][d] = outlier ? 0.f : x;
-    qs[1][d] = outlier ? x : 0.f;
-  }
-  __syncthreads();
+// S q on the bf16 MFMA (QJL Algorithm 1 step 4, the projection of the query):
+// sq[row][i] = sum_d S[i][d] q[row][d] for the query rows (batch, head) and
+// the m + mo sketch rows, as a [rows x 128] x [128 x (m + mo)] product. A wave
+// takes 16 query rows (the A operand: rows = query heads, k = channels) and
+// QJL_PROJ_TILES tiles of 16 sketch rows (the B operand: k = channels,
+// columns = sketch rows, read straight from S's rows). With the outlier split
+// the rows below m see q's normal channels and the rest its outlier channels;
+// m and mo are multiples of 64, so a tile belongs to one instance. Products
+// of bf16 are exact and the sums are float, as in the scalar form.
+constexpr int QJL_PROJ_TILES = 4;
+__global__ __launch_bounds__(64) void qjl_project_mfma(const uint16_t* q, const uint16_t* S, float* sq, int m, int mo,
+                                                       const uint8_t* mask, int n_rows, int n_q_heads, int group) {
+  const int lane = threadIdx.x, a = lane >> 4, r = lane & 15;
+  const int row0 = blockIdx.x * 16;
   const int mt = m + mo;
-  for (int i = threadIdx.x; i < mt; i += blockDim.x) {
-    const uint16_t* srow = S + (int64_t)i * D;
-    const float* qv = qs[i < m ? 0 : 1];
-    float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(bf16_to_f32(srow[d]), qv[d], acc);
-    sq[(int64_t)row * mt + i] = acc;
+  const int qrow = min(row0 + r, n_rows - 1);                 // A row r: query row row0 + r
+  bf16x8 an[4], ao[4];
+  uint32_t obits = 0;                                          // outlier bits of channels 32 ks + 8 a + e
+  if (mo > 0 && mask != nullptr) {
+    const int b = qrow / n_q_heads, kvh = (qrow - b * n_q_heads) / group;
+    const uint8_t* rec = mask + ((int64_t)b * (n_q_heads / group) + kvh) * QJL_RECORD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) obits |= (uint32_t)rec[4 * ks + a] << (8 * ks);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 raw = ld16(reinterpret_cast<const uint8_t*>(q + (int64_t)qrow * D + 32 * ks + 8 * a));
+    uint16_t hv[8], nv[8], ov[8];
+    __builtin_memcpy(hv, &raw, 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool out = (obits >> (8 * ks + e)) & 1;
+      nv[e] = out ? (uint16_t)0 : hv[e];
+      ov[e] = out ? hv[e] : (uint16_t)0;
+    }
+    __builtin_memcpy(&an[ks], nv, 16);
+    __builtin_memcpy(&ao[ks], ov, 16);
+  }
+  for (int t = 0; t < QJL_PROJ_TILES; ++t) {
+    const int tile = blockIdx.y * QJL_PROJ_TILES + t;
+    if (16 * tile >= mt) break;                                // uniform
+    const int srow = 16 * tile + r;                            // B column r: sketch row
+    const bool outlier = 16 * tile >= m;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 bs = as_bf16x8(ld16(reinterpret_cast<const uint8_t*>(S + (int64_t)srow * D + 32 * ks + 8 * a)));
+      acc = mfma_bf(outlier ? ao[ks] : an[ks], bs, acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {                              // D row 4 a + e: query row row0 + 4 a + e
+      const int row = row0 + 4 * a + e;
+      if (row < n_rows) sq[(int64_t)row * mt + srow] = acc[e];
+    }
   }
 }
 
@@ -374,37 +468,48 @@ int decode_pages_per_split(int n_pages, int batch, int n_kv_heads) {
   return decode_pages_per_split_slots(n_pages, batch, n_kv_heads, DECODE_SLOTS);
 }
 
-template <int MODE>
-static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t s) {
+template <int MODE, bool FIFO>
+static hipError_t launch_mode_f(const DecodeArgs& a, int g, dim3 grid, hipStream_t s) {
+  const size_t dyn = FIFO ? (size_t)PAGE * 8 * sizeof(float) : 0;
   switch (g) {
-    case 1: hipLaunchKernelGGL((decode_kernel<MODE, 1>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<MODE, 2>), grid, dim3(64), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<MODE, 4>), grid, dim3(64), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<MODE, 8>), grid, dim3(64), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<MODE, 1, FIFO>), grid, dim3(64), dyn, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<MODE, 2, FIFO>), grid, dim3(64), dyn, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<MODE, 4, FIFO>), grid, dim3(64), dyn, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<MODE, 8, FIFO>), grid, dim3(64), dyn, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <int MODE>
+static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t s) {
+  return a.vq_end != INT32_MAX ? launch_mode_f<MODE, true>(a, g, grid, s) : launch_mode_f<MODE, false>(a, g, grid, s);
 }
 
 int decode_parts(const DecodeArgs& a) { return a.n_page_splits + a.n_seg_splits; }
 
 hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s,
-                         bool with_merge, bool generic) {
+                         bool with_merge, int path) {
   DecodeArgs a = args;
+  const bool generic = path == KVQ_DECODE_GENERIC;
   const int g = a.n_q_heads / a.n_kv_heads;
   const int n_parts = decode_parts(a);
   const int rows = a.batch * a.n_q_heads;
   if (n_parts > 0) {
     if (key_mode == KVQ_KEY_QJL) {
-      hipLaunchKernelGGL(qjl_project_kernel, dim3(rows), dim3(256), 0, s, a.q, qjl_s, const_cast<float*>(a.sq),
-                         a.qjl_m, a.qjl_mo, a.mask, rows, a.n_q_heads, g);
+      const int tiles = (a.qjl_m + a.qjl_mo) / 16;
+      const dim3 pgrid((rows + 15) / 16, (tiles + QJL_PROJ_TILES - 1) / QJL_PROJ_TILES);
+      hipLaunchKernelGGL(qjl_project_mfma, pgrid, dim3(64), 0, s, a.q, qjl_s, const_cast<float*>(a.sq), a.qjl_m,
+                         a.qjl_mo, a.n_pages > 0 ? a.mask : nullptr, rows, a.n_q_heads, g);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     hipError_t e = hipSuccess;
     // The software-pipelined kernels cover the common shapes; the config's
     // decode path can ask for the generic kernel (same results within the
-    // decode bound).
+    // decode bound). (Merging the splits inside the split kernel, by
+    // workgroups that wait for a slice's parts, measured slower than this
+    // separate pass: the waits' device-scope polls slow the page stream, and
+    // a store-acknowledge, count, poll, load chain costs about a launch.)
     const bool fast = !generic && launch_decode_fast(key_mode, a, s);
     if (fast) {
       e = hipGetLastError();

@@ -137,10 +137,15 @@ __device__ inline void init_state(SoftState<NPASS>& st) {
 
 // Consume one page: logit[i][e] is the raw Key accumulator of tile i row e
 // (token 16 i + 4 a + e); the log2-domain logit is logit * xs + xb.
-template <int G, int NPASS>
+// HYB (KIVI Value FIFO): page tokens from vlim on have no quantized Value
+// yet: their scales and offsets are masked out of the value MFMAs (their
+// probabilities still count in the normaliser) and their binary16
+// probabilities go to hp[token][head] for the caller to weight the
+// full-precision Values with.
+template <int G, int NPASS, bool HYB = false>
 __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)[8], float xs, float xb,
                                       const u32x4 (&vc)[4], const uint8_t* vm_lo, const uint8_t* vm_hi, int a,
-                                      int col) {
+                                      int col, int vlim = PAGE, float (*hp)[8] = nullptr) {
   constexpr int C = 16 / G;
   float pm = -INFINITY;
 #pragma unroll
@@ -176,9 +181,24 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
     half8 ph;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ph[e] = (_Float16)p[e];
+    u32x4 keep = {~0u, ~0u, ~0u, ~0u};   // HYB: binary16 lanes of tokens with a quantized Value
+    if constexpr (HYB) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 32 * ks + 16 * (e >> 2) + 4 * a + (e & 3);   // pi(ks, a, e)
+        if (tok >= vlim) {
+          if (col < G) hp[tok][col] = (float)ph[e];
+          const uint32_t m = ~(0xFFFFu << (16 * (e & 1)));
+          if ((e >> 1) == 0) keep.x &= m;
+          else if ((e >> 1) == 1) keep.y &= m;
+          else if ((e >> 1) == 2) keep.z &= m;
+          else keep.w &= m;
+        }
+      }
+    }
     {
       // sum p * offset per value group and sum p, on the MFMA (p as binary16)
-      const u32x4 zw = ld16(kb + 32 * zr + 16);
+      const u32x4 zw = ld16(kb + 32 * zr + 16) & keep;
       u32x4 za;
       za.x = col < 4 ? zw.x : zconst;
       za.y = col < 4 ? zw.y : zconst;
@@ -189,7 +209,7 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
       const int j = (jl + P * C) & 3;            // this lane's value group in pass P
-      const half8 s8 = as_half8(ld16(kb + 32 * j));
+      const half8 s8 = as_half8(ld16(kb + 32 * j) & keep);
       const half8 B = ph * s8;
       const u32x4 v8 = vc[ks] >> 8u;
 #pragma unroll
@@ -214,9 +234,11 @@ __device__ inline float* stage_buf(Smem& S) {
 // only tiles of value group jl + P*C are meaningful. The tiles go through
 // LDS with static indices (stage: 64 lanes x 32 floats), then every lane
 // writes 2 channels of each head's record, coalesced.
+// extra (optional): per head, two channels 2 lane, 2 lane + 1 added to the
+// output (the full-precision Values of a KIVI FIFO page).
 template <int G, int NPASS>
 __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, int split, int b, int kvh, int a,
-                                     int col, float* stage) {
+                                     int col, float* stage, const float (*extra)[2] = nullptr) {
   constexpr int C = 16 / G;
   const int lane = threadIdx.x & 63;   // lane within the calling wave
   // sum p (row 4: lane group 1) and sum p * offset of value group j (row j:
@@ -254,7 +276,8 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
       const int ch = 2 * lane + k;                 // channel = 16 u + 4 a' + e
       const int u = ch >> 4, aa = (ch >> 2) & 3, e = ch & 3;
       const int j = u >> 1, c = (j % C) * G + hh;  // column holding (group j, head hh)
-      __builtin_nontemporal_store(stage[(c * 8 + u) * 16 + aa * 4 + e], &base[hh * RECORD + 2 + ch]);
+      const float v = stage[(c * 8 + u) * 16 + aa * 4 + e] + (extra ? extra[hh][k] : 0.f);
+      __builtin_nontemporal_store(v, &base[hh * RECORD + 2 + ch]);
     }
   }
 }
@@ -394,7 +417,7 @@ __device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int k
     for (int j = 0; j < 32; ++j) {
       const int t = min(t0 + j, T - 1);
       const uint16_t* vrow = t < A.n_sink ? A.sink_v + (head * A.n_sink + t) * D
-                                          : A.resid_v + (head * A.resid_stride + (t - A.n_sink)) * D;
+                                          : A.resid_v + (head * A.resid_v_stride + (t - A.n_sink)) * D;
       vr[j] = reinterpret_cast<const uint32_t*>(vrow)[lane];
     }
     float x[2][4];

@@ -418,6 +418,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   // be computed, requested one page earlier), then request the next page and
   // compute this one. Draining before the copies are issued keeps the
   // compiler from draining after them, which would wait for the next page.
+  // (Two pages in flight, the next one requested before this one arrives,
+  // measured slower: the memory then serves each split's pages back to back,
+  // so the splits served last start computing last; with one page ahead,
+  // every split's first page comes before any split's second.)
   uint32_t recn = 0;   // PREC: the next page's record dword
   for (int it = 0; it < np; it += 2) {
     progress_prio(it, np);

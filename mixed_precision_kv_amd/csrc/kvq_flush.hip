@@ -119,7 +119,7 @@ __device__ inline bool f16_is_inf(uint16_t h) { return (h & 0x7FFF) == 0x7C00; }
 __device__ inline void raise_flags(const Scan& s, const GroupParam& p, unsigned* flags) {
   const unsigned f = (s.nonfinite ? KVQ_FLAG_NONFINITE : 0u) | (scan_span(s) ? KVQ_FLAG_SPAN : 0u) |
                      (f16_is_inf(p.scale) || f16_is_inf(p.offset) ? KVQ_FLAG_RANGE : 0u);
-  if (f) atomicOr(flags, f);
+  if (f && flags) atomicOr(flags, f);
 }
 
 // min-max quantizer parameters for `levels` = 2^b - 1
@@ -308,6 +308,15 @@ __device__ __attribute__((always_inline)) inline void flush_value_part(uint8_t* 
     const uint16_t lo = half ? p0.offset : p0.scale, hi = half ? p1.offset : p1.scale;
     store4(page_v + V_CODE_BYTES + 512 * s + 128 * a + 32 * j + 16 * half + 4 * w, (uint32_t)lo | ((uint32_t)hi << 16));
   }
+}
+
+// KIVI Value FIFO seal (KIVI blog section 4): the Keys of a full residual are
+// quantized into the page and its value k-step s is cleared (codes, scales,
+// offsets all zero); each token's Value row is ORed in later by the value
+// push, when it leaves the full-precision window.
+__device__ inline void zero_value_part(uint8_t* page_v, int s) {
+  store4(page_v + 1024 * s + 4 * threadIdx.x, 0u);
+  if (threadIdx.x < 128) store4(page_v + V_CODE_BYTES + 512 * s + 4 * threadIdx.x, 0u);
 }
 
 // Key tiles are read down columns (one channel over many tokens); rows of
@@ -780,7 +789,8 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
     int hn16 = A.n16, hn4 = A.n4;
     if (A.head_tiers && part < V_PARTS) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);
     const MixGeo g = mix_geo(hn16, hn4);
-    if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+    if (part < V_PARTS && A.keys_only) zero_value_part(page + g.off_v, part);
+    else if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
     else flush_mix_key_part(A, page, head, row0, part - V_PARTS, lpage, S.k);
   } else if constexpr (MODE == KVQ_KEY_PNMIX) {
     __shared__ union {
@@ -788,7 +798,8 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
       KPartSmem k;
     } S;
     const PnGeo g = pn_geo(A.n_hi);
-    if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+    if (part < V_PARTS && A.keys_only) zero_value_part(page + g.off_v, part);
+    else if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
     else flush_pn_key_part(A, page, head, row0, part - V_PARTS, S.k);
   } else {
     __shared__ union {
@@ -796,7 +807,8 @@ __device__ inline void flush_block(const FlushArgs& A, int parts, int lin) {
       QPartSmem q;
     } S;
     const QjlGeo g = qjl_geo(A.qjl_m, A.qjl_mo);
-    if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
+    if (part < V_PARTS && A.keys_only) zero_value_part(page + g.off_v, part);
+    else if (part < V_PARTS) flush_value_part(page + g.off_v, A.v_src, row0, part, A.flags, S.v);
     else flush_qjl_key_part(A, page, head, row0, part - V_PARTS, S.q);
   }
 }
@@ -828,6 +840,83 @@ __global__ __launch_bounds__(256) void merge_flush_kernel(FlushArgs A, int parts
 }
 
 // ------------------------------------------------------------------ launchers
+// ------------------------------------------------------------------ value push
+// KIVI Value FIFO (KIVI blog section 4): the Value rows of tokens that leave
+// the full-precision window are quantized per token (four groups of 32
+// channels, 2 bits, the flush's exact quantizer) and ORed into their pages,
+// whose value part the Key seal has cleared. One wave per (head, row): lane
+// l holds channels 2l, 2l+1; a group is 16 lanes. In the page's value layout
+// the token's 128 codes fill bits 2u + 16hh of 16 dwords (one per channel
+// residue r = c % 16, u = c / 16) and its 4 scales and offsets the 16-bit
+// half hh of 8 metadata dwords.
+__global__ __launch_bounds__(64) void value_push_kernel(FlushArgs A, int key_mode) {
+  const int lane = threadIdx.x;
+  const int64_t head = blockIdx.x / A.push_rows;
+  const int j = blockIdx.x - (int)head * A.push_rows;
+  const int tok = A.push_first + j, lpage = tok / PAGE, rr = tok % PAGE;
+  uint8_t* page;
+  if (A.table == nullptr) {
+    page = A.arena + (head * A.max_pages + lpage) * A.page_stride;
+  } else {
+    const int v = A.table[head * A.table_stride + lpage];
+    if (v < 0 || v >= A.pool_pages) {   // uniform: nothing written
+      if (lane == 0) atomicOr(A.flags, KVQ_FLAG_TABLE);
+      return;
+    }
+    page = A.arena + (int64_t)v * A.page_stride;
+  }
+  int off_v;
+  if (key_mode == KVQ_KEY_MIXKVQ) {
+    int hn16 = A.n16, hn4 = A.n4;
+    if (A.head_tiers) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);
+    off_v = mix_geo(hn16, hn4).off_v;
+  } else if (key_mode == KVQ_KEY_PNMIX) {
+    off_v = pn_geo(A.n_hi).off_v;
+  } else {
+    off_v = qjl_geo(A.qjl_m, A.qjl_mo).off_v;
+  }
+  const uint32_t w = reinterpret_cast<const uint32_t*>(A.v_src + (head * A.src_stride + j) * D)[lane];
+  const uint32_t cw[1] = {w};
+  Scan sc = scan_words(cw);
+  scan_merge<1>(sc);
+  scan_merge<2>(sc);
+  scan_merge<4>(sc);
+  {   // lanes 8 apart within the group of 16
+    sc.mn = fminf(sc.mn, __shfl_xor(sc.mn, 8));
+    sc.mx = fmaxf(sc.mx, __shfl_xor(sc.mx, 8));
+    sc.am1 = min(sc.am1, (uint32_t)__shfl_xor((int)sc.am1, 8));
+    sc.nonfinite = sc.nonfinite || __shfl_xor((int)sc.nonfinite, 8);
+  }
+  const int grp = lane >> 4;
+  const GroupParam p = make_param(sc, 3, (lane & 15) == 0 ? A.flags : nullptr);   // one status write per group
+  const int c0 = quant_code(p, 3, bf16_to_f32((uint16_t)w)), c1 = quant_code(p, 3, bf16_to_f32((uint16_t)(w >> 16)));
+  // token -> (k-step s, lane group a, element k = 2 w + hh) of the value layout
+  const int s = rr >> 5, rem = rr & 31, a = (rem & 15) >> 2, k = 4 * (rem >> 4) + (rem & 3);
+  const int wd = k >> 1, hh = k & 1;
+  uint8_t* pv = page + off_v;
+  // the dword of channel residue r = lane % 16: codes of channels 16 u + r,
+  // held by lane 8 u + r / 2 (gathered with every lane active, stored by 16)
+  uint32_t word = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int src = 8 * u + ((lane & 15) >> 1);
+    const int x0 = __shfl(c0, src), x1 = __shfl(c1, src);
+    word |= (uint32_t)((lane & 1) ? x1 : x0) << (2 * u + 16 * hh);
+  }
+  if (lane < 16) atomicOr(reinterpret_cast<unsigned*>(pv + 1024 * s + 256 * a + 16 * lane + 4 * wd), word);
+  if ((lane & 15) == 0) {   // group grp's scale (half 0) and offset (half 1)
+    uint8_t* m = pv + V_CODE_BYTES + 512 * s + 128 * a + 32 * grp + 4 * wd;
+    atomicOr(reinterpret_cast<unsigned*>(m), (uint32_t)p.scale << (16 * hh));
+    atomicOr(reinterpret_cast<unsigned*>(m + 16), (uint32_t)p.offset << (16 * hh));
+  }
+}
+
+hipError_t launch_value_push(int key_mode, const FlushArgs& a, int batch, hipStream_t stream) {
+  const int64_t heads = (int64_t)batch * a.n_kv_heads;
+  hipLaunchKernelGGL(value_push_kernel, dim3((unsigned)(heads * a.push_rows)), dim3(64), 0, stream, a, key_mode);
+  return hipGetLastError();
+}
+
 // most code fragments a MixKVQ page can have: the configured counts, or with
 // threshold tiers any counts within the capacities (fewer BF16 channels leave
 // more UINT2 slots)

@@ -209,6 +209,8 @@ struct FlushArgs {
   uint8_t* rec_out;               // with q_accum: record of logical page p of head h at rec_out + (h rec_stride + p) * 160
   int rec_stride;
   int head_tiers;                 // MixKVQ threshold tiers: each head's counts come from its record (n16, n4: capacities)
+  int keys_only;                  // KIVI Value FIFO: seal the Keys, zero the Value part (rows arrive by value push)
+  int push_first, push_rows;      // value push: tokens push_first .. push_first + push_rows - 1 of every head
 };
 struct SelectArgs {
   const uint16_t* q;
@@ -240,6 +242,10 @@ struct DecodeArgs {
   const uint16_t* resid_k;
   const uint16_t* resid_v;
   int n_resid, resid_stride;
+  int resid_v_stride;             // row stride of resid_v (resid_stride, or the Value window's in FIFO decodes)
+  int vq_end;                     // KIVI Value FIFO: tokens from vq_end on take their Value from vwin (else INT32_MAX)
+  const uint16_t* vwin;           // [batch][n_kv_heads][vwin_stride][128] bf16: Value of token vq_end + j at row j
+  int vwin_stride;
   float scale_log2;
   float qjl_coef;
   float* partial;                 // [n_splits][B][Hq][130]: m, l, out[128]
@@ -253,12 +259,14 @@ struct DecodeArgs {
 };
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);
+hipError_t launch_value_push(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);
 hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream_t stream);
 hipError_t launch_accumulate(const SelectArgs& a, void* acc, int batch, hipStream_t stream);
 // with_merge false: the split kernels only; the caller launches the merge
 // (launch_merge_flush) with the same DecodeArgs
+// path: kvq_decode_path
 hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s,
-                         bool with_merge, bool generic);
+                         bool with_merge, int path);
 int decode_parts(const DecodeArgs& a);
 hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s);
 constexpr int RECORD = 130;       // partial record per query head: m, l, out[128]

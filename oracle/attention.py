@@ -118,13 +118,19 @@ def kl_divergence(p_ref: np.ndarray, p_q: np.ndarray) -> float:
 def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0, perm=None,
                       mask_rec=None, pair_layout="half", s_bits=None,
                       sink_k=None, sink_v=None, resid_k=None, resid_v=None, page_perms=None,
-                      qjl_m=None, outl=None, with_logits=False):
+                      qjl_m=None, outl=None, with_logits=False, n_vq=None, vwin=None):
     """Decode for one (batch, KV head) from packed pages.
 
     q_bits_heads [g, D] bf16 bits; arena_pages: list of page byte arrays;
     sink_*/resid_* [n, D] bf16 bits (or None); page_perms: MixKVQ channel
     order of each page (per-flush reselection), else `perm` for every page;
     qjl_m / outl: the QJL outlier split (normal rows, outlier channels).
+    n_vq / vwin: KIVI's Value FIFO (KIVI blog sections 4-6): only the Values
+    of tokens 0 .. n_vq - 1 are quantized (in the pages); every later token,
+    sealed Key page or Key residual alike, takes its Value from the
+    full-precision window vwin [T - n_vq, D] (bf16 bits), and resid_v is not
+    used. The Key boundary (pages | resid_k) and the Value boundary (n_vq)
+    differ; one softmax covers all tokens.
     Returns (out [g, D], probs), and the logits with with_logits."""
     q = bf16_to_f64(q_bits_heads)
     Ks, Vs, bits_l, norms_l, norms_o = [], [], [], [], []
@@ -152,8 +158,31 @@ def decode_arena_head(key_mode, q_bits_heads, arena_pages, scale, *, n16=0, n4=0
         if split:
             qjl = (s_bits, qjl_m, outl, qjl[1], qjl[2], np.concatenate(norms_o))
     sink = None if sink_k is None else (bf16_to_f64(sink_k), bf16_to_f64(sink_v))
-    resid = None if resid_k is None else (bf16_to_f64(resid_k), bf16_to_f64(resid_v))
+    if vwin is not None:
+        W = bf16_to_f64(vwin)
+        Tk = V_q.shape[0]
+        n_kres = 0 if resid_k is None else resid_k.shape[0]
+        assert n_vq <= Tk and W.shape[0] == Tk + n_kres - n_vq
+        V_q = V_q.copy()
+        V_q[n_vq:] = W[:Tk - n_vq]
+        resid = None if resid_k is None else (bf16_to_f64(resid_k), W[Tk - n_vq:])
+    else:
+        resid = None if resid_k is None else (bf16_to_f64(resid_k), bf16_to_f64(resid_v))
     return decode_kv_head(q, K_q, V_q, scale, sink=sink, resid=resid, qjl=qjl, with_logits=with_logits)
+
+
+def fifo_page(page, off_v: int, n_rows: int) -> np.ndarray:
+    """A page as KIVI's Value FIFO leaves it (KIVI blog section 4): its Keys
+    sealed, Values quantized only for its first n_rows tokens (those that
+    have left the full-precision window); the other rows hold code 0 and a
+    zero scale and offset."""
+    page = np.array(page, dtype=np.uint8, copy=True)
+    codes, sc, of = layout.unpack_v(page[off_v:])
+    codes[n_rows:] = 0
+    sc[n_rows:] = 0
+    of[n_rows:] = 0
+    page[off_v: off_v + layout.V_CODE_BYTES + layout.V_META_BYTES] = layout.pack_v(codes, sc, of)
+    return page
 
 
 def reference_attention(q_bits_heads, k_bits, v_bits, scale):
