@@ -487,8 +487,8 @@ static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t
 
 int decode_parts(const DecodeArgs& a) { return a.n_page_splits + a.n_seg_splits; }
 
-hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s,
-                         bool with_merge, int path) {
+hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s, bool with_merge,
+                         int path) {
   DecodeArgs a = args;
   const bool generic = path == KVQ_DECODE_GENERIC;
   const int g = a.n_q_heads / a.n_kv_heads;
@@ -513,6 +513,8 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
     const bool fast = !generic && launch_decode_fast(key_mode, a, s);
     if (fast) {
       e = hipGetLastError();
+      args.pps = a.pps;   // the kernel's own split geometry, for the caller's merge
+      args.n_page_splits = a.n_page_splits;
     } else {
       dim3 grid(n_parts * a.n_kv_heads * a.batch);
       if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
@@ -522,12 +524,14 @@ hipError_t launch_decode(int key_mode, const DecodeArgs& args, const uint16_t* q
     if (e != hipSuccess) return e;
   }
   if (!with_merge) return hipSuccess;
-  // with nothing to attend to (no part) every output row is zero
+  // with nothing to attend to (no part) every output row is zero; a kernel
+  // may have chosen its own split count (in a)
+  const int parts = decode_parts(a);
   const dim3 cgrid(rows);
-  switch (merge_batch(n_parts)) {
-    case 16: hipLaunchKernelGGL(combine_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, n_parts, rows); break;
-    case 32: hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, n_parts, rows); break;
-    default: hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.partial, a.out, n_parts, rows); break;
+  switch (merge_batch(parts)) {
+    case 16: hipLaunchKernelGGL(combine_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
+    case 32: hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
+    default: hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
   }
   return hipGetLastError();
 }

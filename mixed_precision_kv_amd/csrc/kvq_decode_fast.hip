@@ -47,30 +47,41 @@ __device__ inline void async16_in(__amdgpu_buffer_rsrc_t r, int off, uint8_t* ld
 }
 
 // Where a split's pages are. PAGED false: contiguous from the split's first
-// page. PAGED true: through the page table, lane i holding the pool index of
-// page p0 + i (np <= 64; one range-limited load, lanes past np read zero),
-// clamped into the pool; page `it` (uniform) is then one lane read away.
-template <bool PAGED>
+// page. PAGED true: through the page table, lane i of register j holding the
+// pool index of page p0 + 64 j + i (np <= 64 NT; range-limited loads, lanes
+// past np read zero), clamped into the pool; page `it` (uniform) is then one
+// lane read away.
+template <bool PAGED, int NT = 1>
 struct PageSet {
   const uint8_t* base;
   int64_t stride;
-  int tab;
+  int tab[NT];
   __device__ const uint8_t* at(int it) const {
-    if constexpr (PAGED) return base + (int64_t)__builtin_amdgcn_readlane(tab, it) * stride;
-    else return base + (int64_t)it * stride;
+    if constexpr (PAGED) {
+      const int t = NT == 1 || it < 64 ? __builtin_amdgcn_readlane(tab[0], it)
+                                       : __builtin_amdgcn_readlane(tab[NT - 1], it - 64);
+      return base + (int64_t)t * stride;
+    } else {
+      return base + (int64_t)it * stride;
+    }
   }
 };
-template <bool PAGED>
-__device__ inline PageSet<PAGED> page_set(const DecodeArgs& A, int64_t head, int p0, int np, int lane) {
-  PageSet<PAGED> s;
+template <bool PAGED, int NT = 1>
+__device__ inline PageSet<PAGED, NT> page_set(const DecodeArgs& A, int64_t head, int p0, int np, int lane) {
+  static_assert(NT == 1 || NT == 2, "up to 128 pages per split");
+  PageSet<PAGED, NT> s;
   s.stride = A.page_stride;
   if constexpr (PAGED) {
     const auto r = range_rsrc(reinterpret_cast<const uint8_t*>(A.table + head * A.table_stride + p0), 4 * np);
-    const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(r, 4 * lane, 0, 0);
-    s.tab = min(max(v, 0), A.pool_pages - 1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (lane + 64 * j), 0, 0);
+      s.tab[j] = min(max(v, 0), A.pool_pages - 1);
+    }
     s.base = A.arena;
   } else {
-    s.tab = 0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) s.tab[j] = 0;
     s.base = A.arena + (head * A.max_pages + p0) * A.page_stride;
   }
   return s;
@@ -140,11 +151,11 @@ struct MixSmem {
   float mh[16];
 };
 
-template <int G>
+template <int G, int NK = 8>
 struct QjSmem {
   union {
     struct {
-      half8 bq[2][8][4][G];        // S q hi/lo [k-step][lane group][head]
+      half8 bq[2][NK][4][G];       // S q hi/lo [k-step][lane group][head]
       uint8_t meta[2][META_SLOT];
     } qj;
     float p_lds[256][8];
@@ -586,23 +597,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 }
 
 // ------------------------------------------------------------------ QJL (m = 256)
+// OUT: the outlier split (m = 256 inlier and 64 outlier sketch rows): a fifth
+// 1 KB block of sign bits, the outlier norms beside the inlier ones, and the
+// outlier instance's estimate added with its own norm and factor m / mo.
+template <bool OUT>
 struct QjKey {
   u32x4 m[3];
-  u32x4 bits[4];
+  u32x4 bits[OUT ? 5 : 4];
 };
 
-__device__ inline void qj_load_key(QjKey& c, const uint8_t* page, const QjlGeo& g, int lane, int a, int r) {
-  c.m[0] = ld16(page + g.off_norm + 16 * (lane & 15));     // 256 B of norms (lanes 16+ repeat them)
+template <bool OUT>
+__device__ inline void qj_load_key(QjKey<OUT>& c, const uint8_t* page, const QjlGeo& g, int lane, int a, int r) {
+  // 256 B of norms (OUT: 512 B, the outlier norms after them); the lanes past
+  // them repeat them
+  c.m[0] = ld16(page + g.off_norm + 16 * (lane & (OUT ? 31 : 15)));
   load_vmeta(c.m, page + g.off_v + V_CODE_BYTES, lane);
 #pragma unroll
-  for (int P2 = 0; P2 < 4; ++P2) c.bits[P2] = ld16(page + 1024 * P2 + 256 * a + 16 * r);
+  for (int P2 = 0; P2 < (OUT ? 5 : 4); ++P2) c.bits[P2] = ld16(page + 1024 * P2 + 256 * a + 16 * r);
 }
 
 // Estimator logits nu_t * (2 <Sq, bits_t> - sum Sq) of one page (before the
-// sqrt(pi/2)/m and softmax factors, which ride on xs).
-template <int G>
-__device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey& c, const uint8_t* slot, const QjSmem<G>& S,
-                               float ssum, int a, int h, int col) {
+// sqrt(pi/2)/m and softmax factors, which ride on xs); OUT adds
+// (m / mo) nu'_t * (2 <S'q, bits'_t> - sum S'q) of the outlier instance, whose
+// MFMAs run one tile at a time once the inlier tiles are done (four more
+// accumulator registers, not 32).
+template <int G, bool OUT>
+__device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey<OUT>& c, const uint8_t* slot,
+                               const QjSmem<G, OUT ? 10 : 8>& S, float ssum, float ssum_o, float ratio, int a, int h,
+                               int col) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -622,26 +644,47 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey& c, const uint8_t*
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
     const u32x4 nw = lds16(nb + 16 * qd);
+    u32x4 nwo = {0u, 0u, 0u, 0u};
+    if constexpr (OUT) nwo = lds16(nb + 256 + 16 * qd);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * qd + ii;
+      f32x4 lo = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (OUT) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const half8 B = S.u.qj.bq[col >> 3][8 + hf][a][h];
+          const u32x4& ob = c.bits[OUT ? 4 : 0];   // the outlier block
+          lo = mfma(tile1(row1(rd(ob, 2 * hf), rd(ob, 2 * hf + 1)), i), B, lo);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo[e] += from_partner8(lo[e]);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t w = rd(nw, 2 * ii + (e >> 1));
         const uint16_t hb = (uint16_t)(w >> (16 * (e & 1)));
         _Float16 hv;
         __builtin_memcpy(&hv, &hb, 2);
-        logit[i][e] = (float)hv * fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum);
+        float est_o = 0.f;
+        if constexpr (OUT) {
+          const uint16_t hbo = (uint16_t)(rd(nwo, 2 * ii + (e >> 1)) >> (16 * (e & 1)));
+          _Float16 hvo;
+          __builtin_memcpy(&hvo, &hbo, 2);
+          est_o = ratio * (float)hvo * fmaf(2.0f * tile_unscale(i), lo[e], -ssum_o);
+        }
+        logit[i][e] = fmaf((float)hv, fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum), est_o);
       }
     }
   }
 }
 
-template <int G, bool PAGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_qjl_fast(DecodeArgs A) {
+template <int G, bool PAGED, bool OUT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2))) void decode_qjl_fast(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
-  __shared__ QjSmem<G> S;
+  constexpr int NK = OUT ? 10 : 8;   // k-steps of 32 sketch rows
+  __shared__ QjSmem<G, NK> S;
   const DecodeBlock blk = decode_block(A);
   const int split = blk.split, kvh = blk.kvh, b = blk.b;
   const int lane = threadIdx.x, a = lane >> 4, r = lane & 15, col = r, h = col % G;
@@ -650,29 +693,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     return;
   }
   const int64_t head = (int64_t)b * A.n_kv_heads + kvh;
-  const QjlGeo g = qjl_geo(A.qjl_m);
+  const QjlGeo g = qjl_geo(A.qjl_m, OUT ? A.qjl_mo : 0);
   const int p0 = split * A.pps, np = min(A.n_pages, p0 + A.pps) - p0;
-  const PageSet<PAGED> pset = page_set<PAGED>(A, head, p0, np, lane);
+  const PageSet<PAGED, OUT ? 2 : 1> pset = page_set<PAGED, OUT ? 2 : 1>(A, head, p0, np, lane);
 
-  // S q of this lane's head first (all of it, so the set-up waits once),
-  // then the first page, before any load is waited for
+  // S q of this lane's head first (the inlier rows, so the set-up waits
+  // once; OUT: the outlier rows after the first page's loads), then the
+  // first page, before any load is waited for
   const int hq = kvh * G + h;
-  const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * A.qjl_m;
-  float4 sqv[8][2];
+  const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * (A.qjl_m + (OUT ? A.qjl_mo : 0));
+  float4 sqv[NK][2];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) sqv[ks][hf] = *reinterpret_cast<const float4*>(sqrow + 32 * ks + 8 * a + 4 * hf);
   const uint8_t* pages = pset.at(0);   // paged: waits for the table load only
-  QjKey kp[2];
+  QjKey<OUT> kp[2];
   ValCodes vp[2];
   qj_load_key(kp[0], pages, g, lane, a, r);
   load_vcodes(vp[0], pages, g.off_v, a, r);
   __builtin_amdgcn_sched_barrier(0);
 
-  float ssum = 0.f;
+  float ssum = 0.f, ssum_o = 0.f;   // sum_i (S q)_i * 2^-6 as the MFMA sees it, per instance
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < NK; ++ks) {
+    if (ks >= 8) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) sqv[ks][hf] = *reinterpret_cast<const float4*>(sqrow + 32 * ks + 8 * a + 4 * hf);
+    }
     const float x[8] = {sqv[ks][0].x * B_SCALE, sqv[ks][0].y * B_SCALE, sqv[ks][0].z * B_SCALE, sqv[ks][0].w * B_SCALE,
                         sqv[ks][1].x * B_SCALE, sqv[ks][1].y * B_SCALE, sqv[ks][1].z * B_SCALE, sqv[ks][1].w * B_SCALE};
     half8 hi, lo;
@@ -681,23 +729,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       S.u.qj.bq[0][ks][a][h] = hi;
       S.u.qj.bq[1][ks][a][h] = lo;
     }
+    float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ssum += (float)hi[e] + (float)lo[e];
+    for (int e = 0; e < 8; ++e) part += (float)hi[e] + (float)lo[e];
+    if (ks < 8) ssum += part;
+    else ssum_o += part;
   }
   ssum = wave_sum_groups(ssum);
+  if constexpr (OUT) ssum_o = wave_sum_groups(ssum_o);
+  const float ratio = OUT ? (float)A.qjl_m / (float)A.qjl_mo : 0.f;   // the instances' sqrt(pi/2)/m factors
   __syncthreads();
 
   SoftState<NPASS> st;
   init_state(st);
   const float xs = A.scale_log2 * A.qjl_coef * B_UNSCALE;
   page_loop(
-      np, kp, vp, [&](QjKey& k, int p) { qj_load_key(k, pset.at(p), g, lane, a, r); },
+      np, kp, vp, [&](QjKey<OUT>& k, int p) { qj_load_key(k, pset.at(p), g, lane, a, r); },
       [&](ValCodes& v, int p) { load_vcodes(v, pset.at(p), g.off_v, a, r); },
-      [&](const QjKey& k, const ValCodes& v, int s, auto mid) {
+      [&](const QjKey<OUT>& k, const ValCodes& v, int s, auto mid) {
         uint8_t* slot = S.u.qj.meta[s];
         commit_meta(k.m, slot, lane);
         f32x4 logit[8];
-        qj_keys<G>(logit, k, slot, S, ssum, a, h, col);
+        qj_keys<G, OUT>(logit, k, slot, S, ssum, ssum_o, ratio, a, h, col);
         mid();
         consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, slot + 1024, slot + 2048, a, col);
       });
@@ -763,13 +816,29 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
     }
     return true;
   }
-  if (a.qjl_m != 256 || a.qjl_mo != 0) return false;   // the outlier split runs on the generic kernel
+  if (a.qjl_m != 256 || (a.qjl_mo != 0 && a.qjl_mo != 64)) return false;   // other sketch sizes: the generic kernel
+  if (a.qjl_mo) {
+    // one wave per SIMD (the outlier split's registers): half the splits, so
+    // that one round of resident waves covers every page
+    const int pps = a.n_pages > 0 ? decode_pages_per_split_slots(a.n_pages, a.batch, a.n_kv_heads, DECODE_SLOTS / 2) : 1;
+    if (a.table && pps > 128) return false;   // the split's page indices live in two registers
+    a.pps = pps;
+    a.n_page_splits = a.n_pages > 0 ? (a.n_pages + pps - 1) / pps : 0;
+    if (a.table) {
+      if (g == 4) launch1(decode_qjl_fast<4, true, true>, a, s);
+      else launch1(decode_qjl_fast<8, true, true>, a, s);
+    } else {
+      if (g == 4) launch1(decode_qjl_fast<4, false, true>, a, s);
+      else launch1(decode_qjl_fast<8, false, true>, a, s);
+    }
+    return true;
+  }
   if (a.table) {
-    if (g == 4) launch1(decode_qjl_fast<4, true>, a, s);
-    else launch1(decode_qjl_fast<8, true>, a, s);
+    if (g == 4) launch1(decode_qjl_fast<4, true, false>, a, s);
+    else launch1(decode_qjl_fast<8, true, false>, a, s);
   } else {
-    if (g == 4) launch1(decode_qjl_fast<4, false>, a, s);
-    else launch1(decode_qjl_fast<8, false>, a, s);
+    if (g == 4) launch1(decode_qjl_fast<4, false, false>, a, s);
+    else launch1(decode_qjl_fast<8, false, false>, a, s);
   }
   return true;
 }

@@ -264,9 +264,11 @@ hipError_t launch_select(int key_mode, const SelectArgs& a, int batch, hipStream
 hipError_t launch_accumulate(const SelectArgs& a, void* acc, int batch, hipStream_t stream);
 // with_merge false: the split kernels only; the caller launches the merge
 // (launch_merge_flush) with the same DecodeArgs
-// path: kvq_decode_path
-hipError_t launch_decode(int key_mode, const DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s,
-                         bool with_merge, int path);
+// path: kvq_decode_path. A pipelined kernel may choose its own split count:
+// a.pps and a.n_page_splits are updated to what was launched (the merge that
+// follows, in the call or from the caller, uses them).
+hipError_t launch_decode(int key_mode, DecodeArgs& a, const uint16_t* qjl_s, hipStream_t s, bool with_merge,
+                         int path);
 int decode_parts(const DecodeArgs& a);
 hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s);
 constexpr int RECORD = 130;       // partial record per query head: m, l, out[128]
