@@ -21,6 +21,9 @@ Prints one JSON line. `value` is the step's algorithmic packed-KV bytes
 (decode reads + flush reads and writes) divided by the step time; the
 decode-only GB/s, its fraction of the 8 TB/s HBM peak and the flush rate in
 tokens/s are reported beside it, as is the CPU oracle on a bounded sample.
+Every decode leg also reports `read_stream_GBps`: a plain read (torch's max
+reduction) of the same rotated cache copies, timed the same way, i.e. the
+read rate this GPU reaches at that size, and the decode's fraction of it.
 The roofline object is the decode call (decode kernel + split combine); its `traffic`
 comes from profiles/decode_llama8b_8k_traffic.txt (rocprofv3 FETCH_SIZE / WRITE_SIZE
 of the decode kernel, calibrated on a plain copy) and is null when the
@@ -353,6 +356,17 @@ def graph_time(torch, calls, warmup_calls):
     return gpu_ms / len(calls), wall
 
 
+def read_stream(torch, arenas, reps):
+    """GB/s of a plain read of the same rotated cache copies: torch's max
+    reduction over their int32 words (no arithmetic to speak of), timed like
+    the decode. The achievable read-stream rate at this size, which the
+    decode's fraction of the 8 TB/s peak is to be read against."""
+    views = [a.view(torch.int32) for a in arenas]
+    ms, _ = graph_time(torch, [lambda i=i: views[i % len(views)].max() for i in range(reps)],
+                       [lambda: views[0].max()] * 2)
+    return arenas[0].numel() / (ms * 1e-3) / 1e9
+
+
 def fidelity(w, synth):
     """Fidelity context of the method on this data (not a parity gate), by the
     oracle alone on the slice (batch 0, kv head 0): KL(p_bf16 || p_quantized)
@@ -603,6 +617,7 @@ def main():
     # warm-cache decode (no rotation) as a secondary number
     dec_w_ms, _ = graph_time(torch, [lambda: rig.decode(0)] * K, [lambda: rig.decode(0)] * 3)
     dec_warm_gbps = dbytes / (dec_w_ms * 1e-3) / 1e9
+    rs_gbps = read_stream(torch, rig.arenas, K)
     # the same decode with its pages scattered over the pool (page table)
     rig.make_paged()
     dec_p_ms, _ = graph_time(torch, [lambda i=i: rig.decode_paged(i) for i in range(K)],
@@ -619,11 +634,14 @@ def main():
         k2 = max(10, K // 2)
         d2, _ = graph_time(torch, [lambda i=i: rig2.decode(i) for i in range(k2)],
                            [lambda i=i: rig2.decode(i) for i in range(3)])
+        rs2 = read_stream(torch, rig2.arenas, k2)
         rig2.make_paged()
         d2p, _ = graph_time(torch, [lambda i=i: rig2.decode_paged(i) for i in range(k2)],
                             [lambda i=i: rig2.decode_paged(i) for i in range(3)])
-        extra = {"workload": w2.name, "decode_ms": d2, "decode_GBps": decode_bytes(w2) / (d2 * 1e-3) / 1e9,
-                 "decode_frac_hbm_peak": decode_bytes(w2) / (d2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        gb2 = decode_bytes(w2) / (d2 * 1e-3) / 1e9
+        extra = {"workload": w2.name, "decode_ms": d2, "decode_GBps": gb2,
+                 "decode_frac_hbm_peak": gb2 / HBM_PEAK_GBPS, "read_stream_GBps": rs2,
+                 "decode_frac_read_stream": gb2 / rs2,
                  "decode_paged_ms": d2p, "decode_paged_GBps": decode_bytes(w2) / (d2p * 1e-3) / 1e9}
         del rig2
         torch.cuda.empty_cache()
@@ -640,8 +658,10 @@ def main():
         dp, _ = graph_time(torch, [lambda i=i: rp.decode(i) for i in range(kp)],
                            [lambda i=i: rp.decode(i) for i in range(3)])
         fp, _ = graph_time(torch, [lambda i=i: rp.flush(i) for i in range(kp)], [])
+        rsp = read_stream(torch, rp.arenas, kp)
         gb = decode_bytes(wp) / (dp * 1e-3) / 1e9
         pnmix = {"workload": wp.name, "decode_ms": dp, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
+                 "read_stream_GBps": rsp, "decode_frac_read_stream": gb / rsp,
                  "bytes_per_decode": decode_bytes(wp), "cache_copies_rotated": len(rp.arenas),
                  "flush_ms": fp, "flush_tokens_per_s": wp.batch * 128 / (fp * 1e-3),
                  "flush_GBps": flush_bytes(wp) / (fp * 1e-3) / 1e9}
@@ -660,8 +680,10 @@ def main():
             kq = max(10, K // 2)
             dq, _ = graph_time(torch, [lambda: rq.decode(0)] * kq, [lambda: rq.decode(0)] * 3)
             fq, _ = graph_time(torch, [lambda: rq.flush(0)] * kq, [])
+            rsq = read_stream(torch, rq.arenas, kq)
             gb = decode_bytes(wq) / (dq * 1e-3) / 1e9
             qjl[name] = {"decode_ms": dq, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
+                         "read_stream_GBps": rsq, "decode_frac_read_stream": gb / rsq,
                          "bytes_per_decode": decode_bytes(wq), "page_bytes_logical": logical_page_bytes(wq),
                          "flush_ms": fq, "flush_tokens_per_s": wq.batch * 128 / (fq * 1e-3),
                          "flush_GBps": flush_bytes(wq) / (fq * 1e-3) / 1e9}
@@ -718,6 +740,8 @@ def main():
         "decode_frac_hbm_peak": dec_gbps / HBM_PEAK_GBPS,
         "decode_ms": dec_ms,
         "decode_warm_GBps": dec_warm_gbps,
+        "read_stream_GBps": rs_gbps,
+        "decode_frac_read_stream": dec_gbps / rs_gbps,
         "decode_paged_ms": dec_p_ms,
         "decode_paged_GBps": dbytes / (dec_p_ms * 1e-3) / 1e9,
         "flush_tokens_per_s": flush_tok_s,
