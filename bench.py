@@ -21,9 +21,11 @@ Prints one JSON line. `value` is the step's algorithmic packed-KV bytes
 (decode reads + flush reads and writes) divided by the step time; the
 decode-only GB/s, its fraction of the 8 TB/s HBM peak and the flush rate in
 tokens/s are reported beside it, as is the CPU oracle on a bounded sample.
-Every decode leg also reports `read_stream_GBps`: a plain read (torch's max
-reduction) of the same rotated cache copies, timed the same way, i.e. the
-read rate this GPU reaches at that size, and the decode's fraction of it.
+Every decode leg also reports `read_stream_GBps`: a plain read of the same
+rotated cache copies by the library's read-stream reference (kvq_read_stream,
+the decode kernels' load shape with nothing computed), timed the same way,
+i.e. the read rate this GPU reaches at that size, and the decode's fraction
+of it.
 The roofline object is the decode call (decode kernel + split combine); its `traffic`
 comes from profiles/decode_llama8b_8k_traffic.txt (rocprofv3 FETCH_SIZE / WRITE_SIZE
 of the decode kernel, calibrated on a plain copy) and is null when the
@@ -356,15 +358,17 @@ def graph_time(torch, calls, warmup_calls):
     return gpu_ms / len(calls), wall
 
 
-def read_stream(torch, arenas, reps):
-    """GB/s of a plain read of the same rotated cache copies: torch's max
-    reduction over their int32 words (no arithmetic to speak of), timed like
-    the decode. The achievable read-stream rate at this size, which the
-    decode's fraction of the 8 TB/s peak is to be read against."""
-    views = [a.view(torch.int32) for a in arenas]
-    ms, _ = graph_time(torch, [lambda i=i: views[i % len(views)].max() for i in range(reps)],
-                       [lambda: views[0].max()] * 2)
-    return arenas[0].numel() / (ms * 1e-3) / 1e9
+def read_stream(torch, kvq, arenas, reps):
+    """GB/s of a plain read of the same rotated cache copies by the library's
+    read-stream reference (kvq_read_stream: the decode's load shape, one XOR
+    word kept per 16 KB), timed like the decode. The read rate this GPU
+    reaches at this size, which the decode's fraction of the 8 TB/s peak is
+    to be read against."""
+    nbytes = arenas[0].numel()
+    sink = torch.zeros((nbytes + 16383) // 16384, dtype=torch.int32, device=arenas[0].device)
+    call = lambda i: kvq.kvq_read_stream(arenas[i % len(arenas)], nbytes, sink, sink.numel() * 4)
+    ms, _ = graph_time(torch, [lambda i=i: call(i) for i in range(reps)], [lambda i=i: call(i) for i in range(3)])
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def fidelity(w, synth):
@@ -617,7 +621,7 @@ def main():
     # warm-cache decode (no rotation) as a secondary number
     dec_w_ms, _ = graph_time(torch, [lambda: rig.decode(0)] * K, [lambda: rig.decode(0)] * 3)
     dec_warm_gbps = dbytes / (dec_w_ms * 1e-3) / 1e9
-    rs_gbps = read_stream(torch, rig.arenas, K)
+    rs_gbps = read_stream(torch, kvq, rig.arenas, K)
     # the same decode with its pages scattered over the pool (page table)
     rig.make_paged()
     dec_p_ms, _ = graph_time(torch, [lambda i=i: rig.decode_paged(i) for i in range(K)],
@@ -634,7 +638,7 @@ def main():
         k2 = max(10, K // 2)
         d2, _ = graph_time(torch, [lambda i=i: rig2.decode(i) for i in range(k2)],
                            [lambda i=i: rig2.decode(i) for i in range(3)])
-        rs2 = read_stream(torch, rig2.arenas, k2)
+        rs2 = read_stream(torch, kvq, rig2.arenas, k2)
         rig2.make_paged()
         d2p, _ = graph_time(torch, [lambda i=i: rig2.decode_paged(i) for i in range(k2)],
                             [lambda i=i: rig2.decode_paged(i) for i in range(3)])
@@ -658,7 +662,7 @@ def main():
         dp, _ = graph_time(torch, [lambda i=i: rp.decode(i) for i in range(kp)],
                            [lambda i=i: rp.decode(i) for i in range(3)])
         fp, _ = graph_time(torch, [lambda i=i: rp.flush(i) for i in range(kp)], [])
-        rsp = read_stream(torch, rp.arenas, kp)
+        rsp = read_stream(torch, kvq, rp.arenas, kp)
         gb = decode_bytes(wp) / (dp * 1e-3) / 1e9
         pnmix = {"workload": wp.name, "decode_ms": dp, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
                  "read_stream_GBps": rsp, "decode_frac_read_stream": gb / rsp,
@@ -680,7 +684,7 @@ def main():
             kq = max(10, K // 2)
             dq, _ = graph_time(torch, [lambda: rq.decode(0)] * kq, [lambda: rq.decode(0)] * 3)
             fq, _ = graph_time(torch, [lambda: rq.flush(0)] * kq, [])
-            rsq = read_stream(torch, rq.arenas, kq)
+            rsq = read_stream(torch, kvq, rq.arenas, kq)
             gb = decode_bytes(wq) / (dq * 1e-3) / 1e9
             qjl[name] = {"decode_ms": dq, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
                          "read_stream_GBps": rsq, "decode_frac_read_stream": gb / rsq,

@@ -410,6 +410,17 @@ kvq_status kvq_decode_attention_flush(const kvq_config* cfg, const void* q, void
                                       int32_t flush_first_page, uint32_t* status_flags,
                                       void* stream);
 
+/* Measurement helper, not part of the method: the read-stream reference a
+ * decode's fraction of the HBM peak is read against. Reads the `bytes` bytes
+ * at src (device, 16-byte aligned, bytes a multiple of 16) with the load
+ * shape of the decode kernels (16-byte lane loads, 1 KB per wave
+ * instruction, 16 KB per workgroup, all of a workgroup's loads in flight
+ * together) and writes, for chunk c of 16384 bytes (the last one possibly
+ * short), the XOR of its 32-bit little-endian words to sink[c] (device,
+ * sink_bytes >= 4 * ceil(bytes / 16384), else KVQ_WORKSPACE_TOO_SMALL).
+ * bytes == 0 launches nothing. Asynchronous on `stream`. */
+kvq_status kvq_read_stream(const void* src, size_t bytes, uint32_t* sink, size_t sink_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ EXPORTED = (
     "kvq_workspace_bytes", "kvq_storage_bytes", "kvq_select_channels",
     "kvq_flush_quantize", "kvq_decode_attention", "kvq_decode_attention_flush",
     "kvq_accumulate_query", "kvq_flush_reselect", "kvq_decode_attention_noalloc",
-    "kvq_flush_keys", "kvq_value_push", "kvq_decode_attention_fifo",
+    "kvq_flush_keys", "kvq_value_push", "kvq_decode_attention_fifo", "kvq_read_stream",
 )
 KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -91,6 +91,7 @@ def load(path: str = LIB_PATH):
                                             ctypes.c_float, P, P, SZ, P]),
         "kvq_accumulate_query": (I32, [cfgp, P, I64, I64, P, P]),
         "kvq_flush_reselect": (I32, [cfgp, P, P, I64, I32, P, P, P, P, I32, I32, P, P]),
+        "kvq_read_stream": (I32, [P, SZ, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -249,6 +250,11 @@ def kvq_decode_attention_noalloc(cfg, q, page_arena, n_pages, mask, qjl_s, sink_
         ctypes.byref(cfg), _ptr(q), _ptr(page_arena), _ptr(page_table), table_stride, n_pages, _ptr(mask),
         _ptr(qjl_s), _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(resid_k), _ptr(resid_v), n_resid, resid_stride,
         softmax_scale, _ptr(out), _stream(stream)))
+
+
+def kvq_read_stream(src, nbytes, sink, sink_bytes, *, stream=None):
+    """The measurement read-stream reference: one XOR word per 16 KB of src."""
+    _check("kvq_read_stream", load().kvq_read_stream(_ptr(src), nbytes, _ptr(sink), sink_bytes, _stream(stream)))
 
 
 def kvq_flush_keys(cfg, k_src, v_src, src_stride, n_pages, mask, qjl_s, page_arena, first_page, status_flags, *,

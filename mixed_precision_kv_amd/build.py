@@ -10,7 +10,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["kvq_api.hip", "kvq_select.hip", "kvq_flush.hip", "kvq_decode.hip", "kvq_decode_fast.hip"]
+SOURCES = ["kvq_api.hip", "kvq_select.hip", "kvq_flush.hip", "kvq_decode.hip", "kvq_decode_fast.hip",
+           "kvq_stream.hip"]
 LIB = os.path.join(HERE, "libkvq.so")
 
 HIPCC_FLAGS = [

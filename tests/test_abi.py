@@ -165,6 +165,11 @@ def test_validation_rejects_before_launch(lib):
     st = S.kvq_select_channels(ctypes.byref(qcfg), 16, 10, 10, 16, 10, 10, 16, None)
     assert st == kvq.KVQ_UNSUPPORTED
     assert kvq.kvq_workspace_bytes(cfg, 8) > 0
+    # the read-stream reference checks its buffers before it launches
+    assert S.kvq_read_stream(16, 0, 16, 0, None) == kvq.KVQ_OK                      # nothing to read
+    assert S.kvq_read_stream(8, 64, 16, 4, None) == kvq.KVQ_INVALID_ARG             # misaligned source
+    assert S.kvq_read_stream(16, 40, 16, 4, None) == kvq.KVQ_INVALID_ARG            # not whole 16-byte loads
+    assert S.kvq_read_stream(16, 16384 + 16, 16, 4, None) == kvq.KVQ_WORKSPACE_TOO_SMALL   # 2 chunks, 1 word
 
 
 def test_threshold_config(lib):
