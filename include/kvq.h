@@ -95,7 +95,9 @@ typedef enum kvq_pair_layout {
 #define KVQ_FLAG_NONFINITE 1u   /* a non-finite input was seen; that group's codes are unspecified */
 #define KVQ_FLAG_SPAN 2u        /* a group spans more than 38 binades; its codes may be off by one */
 #define KVQ_FLAG_MASK 4u        /* a PN-Mix record selects a pair count other than n_hi_pairs */
-#define KVQ_FLAG_RANGE 8u       /* a group's scale or offset exceeds the binary16 range (stored as inf) */
+#define KVQ_FLAG_RANGE 8u       /* a group's scale or offset exceeds the binary16 range (stored as inf); a
+                                   decode over that page gives non-finite outputs (NaN or inf) for every
+                                   query head of its (batch, kv head), and only for those */
 #define KVQ_FLAG_TABLE 16u      /* a page-table entry of a flushed page lies outside the pool; that page is not written */
 
 /* Plain-old-data configuration, passed by pointer to every call. */

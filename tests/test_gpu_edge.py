@@ -9,6 +9,8 @@
   (bit-exact), decode again over 9 pages.
 * Flush status flags: non-finite inputs, values beyond the binary16 range,
   groups spanning more than 38 binades; constant groups bit-exact.
+* A page flagged KVQ_FLAG_RANGE (infinite binary16 metadata) decodes to
+  non-finite outputs for its own (batch, kv head)'s query heads only.
 * PN-Mix with the adjacent pair layout.
 * Repeated decode calls give identical bits.
 """
@@ -211,3 +213,33 @@ def test_flush_ties_bit_exact(name):
         else:
             ref = oflush.flush_qjl_page(kb, vb, p.bits(p.S))
         assert np.array_equal(p.gpu_page(0, h, 0), ref), (name, h)
+
+
+@pytest.mark.parametrize("part", ["key", "value"])
+def test_range_flagged_page_decodes_non_finite(part):
+    """The decode over a page whose flush stored an infinite binary16 scale or
+    offset (KVQ_FLAG_RANGE) gives non-finite outputs for every query head of
+    that (batch, kv head), on both decode kernels; the other kv head's heads,
+    in the same call, stay within the bound of the oracle."""
+    w = synth.WORKLOADS["tiny_mixkvq"].scaled(batch=1, n_kv_heads=2, n_q_heads=8, n_pages=1, n_resid=0,
+                                              n_append=0, seed=1331)
+    p = built(w)
+    rec = p.gpu_record(0, 0)
+    k = p.k_pre[:, :, :128].clone()
+    v = p.v_pre[:, :, :128].clone()
+    if part == "key":
+        k[0, 0, 10, int(rec[100])] = 4.0e5     # a UINT2 channel: infinite scale
+    else:
+        v[0, 0, 9, 40] = -3.0e5                # a value group: infinite offset
+    f = _flush_one(p, k, v)
+    assert f & kvq.KVQ_FLAG_RANGE, f
+    g = w.group
+    for generic in (False, True):
+        p.decode(n_pages=1, n_resid=0, generic=generic)
+        torch.cuda.synchronize()
+        out = p.out.cpu().numpy()
+        for hq in range(g):
+            assert not np.all(np.isfinite(out[0, hq])), (part, generic, hq)
+        rec1 = p.gpu_record(0, 1)
+        ref, _ = p.oracle_decode(0, 1, [p.oracle_page(0, 1, 0, rec1)], rec1, n_resid=0)
+        assert np.all(np.isfinite(out[0, g:])) and np.all(rel_err(out[0, g:], ref) <= TOL), (part, generic)
