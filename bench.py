@@ -168,6 +168,7 @@ def parse():
     ap.add_argument("--no-qjl", action="store_true", help="skip the QJL decodes (plain and outlier split)")
     ap.add_argument("--no-pnmix", action="store_true", help="skip the PN-Mix decode and flush")
     ap.add_argument("--no-fidelity", action="store_true", help="skip the per-workload fidelity (oracle, CPU)")
+    ap.add_argument("--no-fifo", action="store_true", help="skip the Value-FIFO leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--decode-only", action="store_true", help="time the decode call only (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
@@ -369,6 +370,72 @@ def read_stream(torch, kvq, arenas, reps):
     call = lambda i: kvq.kvq_read_stream(arenas[i % len(arenas)], nbytes, sink, sink.numel() * 4)
     ms, _ = graph_time(torch, [lambda i=i: call(i) for i in range(reps)], [lambda i=i: call(i) for i in range(3)])
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def fifo_leg(w, copies, torch, kvq, synth, K, W):
+    """KIVI's Value FIFO (blog sections 4-5) on the workload's shape in its
+    steady state: n_pages sealed Key pages, 64 Key-residual rows, a 128-token
+    full-precision Value window, every older Value quantized into its page.
+    Times the FIFO decode (kvq_decode_attention_fifo) over rotated cache
+    copies, the push of one Value row of every (batch, kv head)
+    (kvq_value_push, distinct rows) and the seal of one Key page of every
+    (batch, kv head) (kvq_flush_keys). The decode is timed on the default
+    path (the pipelined kernel over the pages whose Values are all quantized
+    and the Key residual, the generic kernel over the window's page, one
+    combine) and on the generic path alone."""
+    dev = "cuda"
+    n_pages, n_kres, R = w.n_pages, 64, 128
+    T = n_pages * 128 + n_kres
+    n_vq = T - R
+    H = w.batch * w.n_kv_heads
+    L = w.prefill_tokens
+    assert T <= L
+    cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, n_pages + 1, n_bf16=w.n_bf16,
+                          n_u4=w.n_u4, n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m)
+    q, k, v = synth.prefill(w, dev)
+    mask = torch.zeros(max(1, H * kvq.kvq_mask_bytes(cfg)), dtype=torch.uint8, device=dev)
+    kvq.kvq_select_channels(cfg, q, L, k, n_pages * 128, mask, k_stride=L)
+    del q
+    arena = torch.zeros(H * (n_pages + 1) * kvq.kvq_page_bytes(cfg), dtype=torch.uint8, device=dev)
+    flags = torch.zeros(4, dtype=torch.int32, device=dev)
+    kvq.kvq_flush_keys(cfg, k, k, L, n_pages, mask, None, arena, 0, flags)
+    kvq.kvq_value_push(cfg, v, L, n_vq, 0, mask, arena, flags)
+    arenas = [arena] + [arena.clone() for _ in range(copies - 1)]
+    row = 128 * 2
+    kres, vwin = k.data_ptr() + n_pages * 128 * row, v.data_ptr() + n_vq * row
+    qd = synth.decode_query(w, dev)
+    out = torch.zeros(w.batch, w.n_q_heads, 128, dtype=torch.float32, device=dev)
+    ws_bytes = kvq.kvq_workspace_bytes(cfg, n_pages)
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(128)
+
+    cfg_generic = kvq.with_fields(cfg, decode_path=kvq.KVQ_DECODE_GENERIC)
+
+    def dec(i, c=cfg):
+        kvq.kvq_decode_attention_fifo(c, qd, arenas[i % copies], n_pages, n_vq, mask, None, kres, n_kres, L, vwin,
+                                      R, L, scale, out, ws, ws_bytes)
+    d_ms, _ = graph_time(torch, [lambda i=i: dec(i) for i in range(K)], [lambda i=i: dec(i) for i in range(W)])
+    g_ms, _ = graph_time(torch, [lambda i=i: dec(i, cfg_generic) for i in range(K)],
+                         [lambda i=i: dec(i, cfg_generic) for i in range(W)])
+    # one Value row per call, rows n_vq, n_vq + 1, ... (not pushed before), into a scratch copy
+    scratch = arenas[-1]
+    n_push = min(K, R - n_kres)
+    p_ms, _ = graph_time(torch, [lambda i=i: kvq.kvq_value_push(cfg, v.data_ptr() + (n_vq + i) * row, L, 1, n_vq + i,
+                                                                 mask, scratch, flags) for i in range(n_push)], [])
+    s_ms, _ = graph_time(torch, [lambda: kvq.kvq_flush_keys(cfg, kres, kres, L, 1, mask, None, scratch, n_pages,
+                                                             flags)] * K, [])
+    assert int(flags[0].item()) == 0
+    per_head = n_pages * logical_page_bytes(w) + (n_kres + R) * row + record_bytes(w) + w.group * 128 * (2 + 4)
+    dbytes = H * per_head
+    gb = dbytes / (d_ms * 1e-3) / 1e9
+    return {"workload": w.name, "sealed_pages": n_pages, "key_residual_tokens": n_kres, "quantized_values": n_vq,
+            "value_window": R, "decode_ms": d_ms, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
+            "bytes_per_decode": dbytes,
+            "decode_kernels": f"decode_mix_fast (pages 0-{n_vq // 128 - 1}, Key residual) + decode_kernel<MixKVQ, "
+                              f"FIFO> (pages {n_vq // 128}-{n_pages - 1}) + combine",
+            "generic_path_ms": g_ms, "generic_path_GBps": dbytes / (g_ms * 1e-3) / 1e9,
+            "value_push_ms": p_ms, "value_push_tokens_per_s": H / (p_ms * 1e-3),
+            "key_seal_ms": s_ms, "key_seal_tokens_per_s": H * 128 / (s_ms * 1e-3)}
 
 
 def fidelity(w, synth):
@@ -715,6 +782,13 @@ def main():
         torch.cuda.empty_cache()
 
 
+    # KIVI's Value FIFO in its steady state on the same shape
+    fifo = {}
+    if w.key_mode == 0 and not args.no_fifo:
+        print(f"[bench] value FIFO on {w.name}", file=sys.stderr, flush=True)
+        fifo = fifo_leg(w, copies, torch, kvq, synth, max(10, K // 2), 3)
+        torch.cuda.empty_cache()
+
     fid = {}
     if not args.no_fidelity:
         for name in ("llama8b_8k", "qwen32b_32k", "pnmix_16k", "qjl_32k", "qjl_outlier_32k"):
@@ -757,6 +831,7 @@ def main():
         "secondary": extra,
         "pnmix": pnmix,
         "reselect_per_flush": resel,
+        "value_fifo": fifo,
         "qjl_decode": qjl,
         "fidelity": fid,
         "cpu_baseline": cpu,

@@ -515,7 +515,7 @@ kvq_status kvq_decode_attention_fifo(const kvq_config* cfg, const void* q, const
   a.vq_end = n_vq;
   a.vwin = (const uint16_t*)vwin;
   a.vwin_stride = vwin_stride;
-  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, KVQ_DECODE_GENERIC) ==
+  return launch_decode(cfg->key_mode, a, (const uint16_t*)qjl_s, (hipStream_t)stream, true, cfg->decode_path) ==
                  hipSuccess
              ? KVQ_OK
              : KVQ_HIP_ERROR;

@@ -50,19 +50,31 @@ struct DecodeSmem {
 // have sealed Keys but their Values still in the full-precision window (row
 // pg * 128 + t - vq_end). Their probabilities, staged in hp by the HYB
 // consume_values, weight those rows here; lane l owns channels 2l, 2l+1 of
-// every head.
+// every head. Sixteen rows' loads are issued together (one wait per chunk,
+// not one memory latency per token); past the page's end a lane reloads row
+// PAGE - 1, which is in the window since vlim < PAGE, and adds nothing.
 template <int G>
 __device__ inline void fifo_values(const DecodeArgs& A, int64_t head, int pg, int vlim, float (*hp)[8],
                                    float (&ow)[8][2], int lane) {
   __syncthreads();   // hp written
-  for (int t = max(vlim, 0); t < PAGE; ++t) {
-    const int64_t row = (int64_t)pg * PAGE + t - A.vq_end;
-    const uint32_t w = reinterpret_cast<const uint32_t*>(A.vwin + (head * A.vwin_stride + row) * D)[lane];
-    const float v0 = lo_bf(w), v1 = hi_bf(w);
+  const uint32_t* win = reinterpret_cast<const uint32_t*>(A.vwin + head * A.vwin_stride * D) + lane;
+  for (int t0 = max(vlim, 0); t0 < PAGE; t0 += 16) {
+    uint32_t w[16];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      ow[hh][0] = fmaf(hp[t][hh], v0, ow[hh][0]);
-      ow[hh][1] = fmaf(hp[t][hh], v1, ow[hh][1]);
+    for (int j = 0; j < 16; ++j) {
+      const int64_t row = (int64_t)pg * PAGE + min(t0 + j, PAGE - 1) - A.vq_end;
+      w[j] = win[row * (D / 2)];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (t0 + j < PAGE) {
+        const float v0 = lo_bf(w[j]), v1 = hi_bf(w[j]);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          ow[hh][0] = fmaf(hp[t0 + j][hh], v0, ow[hh][0]);
+          ow[hh][1] = fmaf(hp[t0 + j][hh], v1, ow[hh][1]);
+        }
+      }
     }
   }
   __syncthreads();   // hp free for the next page
@@ -487,6 +499,55 @@ static hipError_t launch_mode(const DecodeArgs& a, int g, dim3 grid, hipStream_t
 
 int decode_parts(const DecodeArgs& a) { return a.n_page_splits + a.n_seg_splits; }
 
+static hipError_t launch_generic(int key_mode, const DecodeArgs& a, int g, hipStream_t s) {
+  const dim3 grid(decode_parts(a) * a.n_kv_heads * a.batch);
+  if (key_mode == KVQ_KEY_MIXKVQ) return launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
+  if (key_mode == KVQ_KEY_PNMIX) return launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
+  return launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
+}
+
+// KIVI Value FIFO (KIVI blog sections 4-5): only the pages the full-precision
+// Value window reaches into (logical pages from vq_end / 128 on, at most
+// three) need the window's Values. The pages before them and the Key
+// residual are an ordinary decode, which goes to the pipelined kernel; the
+// window's pages go to the generic kernel, whose partials follow the
+// pipelined kernel's in the workspace, and one combine merges both. The
+// generic launch sees the window's pages as pages 0.. of a shifted arena (or
+// page table) with vq_end shifted alike, so every row it addresses is the
+// same. Returns false, having launched nothing, when the pipelined kernel
+// does not cover the configuration or the partials would not fit the
+// workspace (page splits of the whole decode + MAX_SEG_SPLITS); else `parts`
+// is the merged split count and `err` the launches' status.
+static bool launch_fifo_split(int key_mode, const DecodeArgs& a, int g, hipStream_t s, int& parts, hipError_t& err) {
+  const int n_clean = (int)min((int64_t)a.n_pages, (int64_t)a.vq_end / PAGE);
+  const int n_tail = a.n_pages - n_clean;
+  if (n_clean == 0 || a.n_seg_splits + n_tail > MAX_SEG_SPLITS) return false;
+  DecodeArgs f = a;
+  f.n_pages = n_clean;
+  f.n_page_splits = (n_clean + a.pps - 1) / a.pps;   // <= the whole decode's page splits
+  f.vq_end = INT32_MAX;
+  f.vwin = nullptr;
+  f.vwin_stride = 0;
+  if (!launch_decode_fast(key_mode, f, s)) return false;
+  err = hipGetLastError();
+  const int fparts = decode_parts(f);
+  parts = fparts + n_tail;
+  if (err != hipSuccess || n_tail == 0) return true;
+  DecodeArgs t = a;
+  if (a.table) t.table = a.table + n_clean;
+  else t.arena = a.arena + (int64_t)n_clean * a.page_stride;
+  t.n_pages = n_tail;
+  t.pps = 1;
+  t.n_page_splits = n_tail;
+  t.n_seg_splits = 0;
+  t.n_sink = 0;
+  t.n_resid = 0;
+  t.vq_end = a.vq_end - n_clean * PAGE;
+  t.partial = a.partial + (size_t)fparts * a.batch * a.n_q_heads * RECORD;
+  err = launch_generic(key_mode, t, g, s);
+  return true;
+}
+
 hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, hipStream_t s, bool with_merge,
                          int path) {
   DecodeArgs a = args;
@@ -510,16 +571,20 @@ hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, 
     // workgroups that wait for a slice's parts, measured slower than this
     // separate pass: the waits' device-scope polls slow the page stream, and
     // a store-acknowledge, count, poll, load chain costs about a launch.)
-    const bool fast = !generic && launch_decode_fast(key_mode, a, s);
-    if (fast) {
+    bool done = false;
+    if (!generic && a.vq_end != INT32_MAX) {
+      int parts = 0;
+      done = launch_fifo_split(key_mode, a, g, s, parts, e);
+      if (done) a.n_page_splits = parts - a.n_seg_splits;   // the merged geometry, for the merge below
+    } else if (!generic && launch_decode_fast(key_mode, a, s)) {
+      done = true;
       e = hipGetLastError();
-      args.pps = a.pps;   // the kernel's own split geometry, for the caller's merge
+    }
+    if (done) {
+      args.pps = a.pps;   // the kernels' own split geometry, for the caller's merge
       args.n_page_splits = a.n_page_splits;
     } else {
-      dim3 grid(n_parts * a.n_kv_heads * a.batch);
-      if (key_mode == KVQ_KEY_MIXKVQ) e = launch_mode<KVQ_KEY_MIXKVQ>(a, g, grid, s);
-      else if (key_mode == KVQ_KEY_PNMIX) e = launch_mode<KVQ_KEY_PNMIX>(a, g, grid, s);
-      else e = launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
+      e = launch_generic(key_mode, a, g, s);
     }
     if (e != hipSuccess) return e;
   }

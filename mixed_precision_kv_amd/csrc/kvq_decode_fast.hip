@@ -819,8 +819,11 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   if (a.qjl_m != 256 || (a.qjl_mo != 0 && a.qjl_mo != 64)) return false;   // other sketch sizes: the generic kernel
   if (a.qjl_mo) {
     // one wave per SIMD (the outlier split's registers): half the splits, so
-    // that one round of resident waves covers every page
-    const int pps = a.n_pages > 0 ? decode_pages_per_split_slots(a.n_pages, a.batch, a.n_kv_heads, DECODE_SLOTS / 2) : 1;
+    // that one round of resident waves covers every page; never more splits
+    // than the caller's geometry (a.pps), which the workspace is sized for
+    const int pps = max(a.pps, a.n_pages > 0 ? decode_pages_per_split_slots(a.n_pages, a.batch, a.n_kv_heads,
+                                                                               DECODE_SLOTS / 2)
+                                             : 1);
     if (a.table && pps > 128) return false;   // the split's page indices live in two registers
     a.pps = pps;
     a.n_page_splits = a.n_pages > 0 ? (a.n_pages + pps - 1) / pps : 0;
