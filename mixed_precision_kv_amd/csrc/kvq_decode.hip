@@ -44,6 +44,7 @@ struct DecodeSmem {
   } u;
   int slot_ch[256];
   float mh[16];
+  alignas(16) uint8_t rec[MIX_RECORD];         // MixKVQ: the head's record (one record per head)
 };
 
 // KIVI Value FIFO (KIVI blog sections 4-5): tokens of page pg from vlim on
@@ -122,8 +123,33 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   }
 
   // ---------------------------------------------------------------- page splits
-  for (int i = lane; i < G * D; i += 64)
-    S.qf[i / D][i % D] = bf16_to_f32(A.q[((int64_t)b * A.n_q_heads + kvh * G + i / D) * D + i % D]);
+  // The set-up's loads are issued together: the group's query rows (G x 128
+  // bf16, contiguous: one 16-byte piece per lane and step) and, for MixKVQ
+  // with one record per head, that record (staged in LDS).
+  {
+    constexpr int QP = G * D / 8;
+    constexpr int QS = (QP + 63) / 64;
+    const uint8_t* qg = reinterpret_cast<const uint8_t*>(A.q + ((int64_t)b * A.n_q_heads + kvh * G) * D);
+    u32x4 qv[QS];
+#pragma unroll
+    for (int j = 0; j < QS; ++j) qv[j] = lane + 64 * j < QP ? ld16(qg + 16 * (lane + 64 * j)) : (u32x4){0u, 0u, 0u, 0u};
+    const bool rec_lds = MODE == KVQ_KEY_MIXKVQ && A.rec_stride == 0 && lane < MIX_RECORD / 16;
+    const u32x4 rv = rec_lds ? ld16(A.mask + head * MIX_RECORD + 16 * lane) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < QS; ++j) {
+      const int i = lane + 64 * j;
+      if (i < QP) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w = rd(qv[j], k);
+          S.qf[(8 * i) / D][(8 * i) % D + 2 * k] = lo_bf(w);
+          S.qf[(8 * i) / D][(8 * i) % D + 2 * k + 1] = hi_bf(w);
+        }
+      }
+    }
+    if (rec_lds) *reinterpret_cast<u32x4*>(S.rec + 16 * lane) = rv;
+    __syncthreads();
+  }
   SoftState<NPASS> st;
   init_state(st);
   float ow[8][2];   // KIVI Value FIFO: full-precision Values of the split's pages, lane's channels
@@ -133,8 +159,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
   const int p1 = min(A.n_pages, p0 + A.pps);
 
   if constexpr (MODE == KVQ_KEY_MIXKVQ) {
+    const uint8_t* hrec = A.rec_stride == 0 ? S.rec : A.mask + head * MIX_RECORD;   // the head's record
     int hn16 = A.n16, hn4 = A.n4;
-    if (A.head_tiers) mix_record_counts(A.mask + head * MIX_RECORD, hn16, hn4);   // threshold tiers: the head's counts
+    if (A.head_tiers) mix_record_counts(hrec, hn16, hn4);   // threshold tiers: the head's counts
     const MixGeo g = mix_geo(hn16, hn4);
     const int NKS = (g.F + 3) / 4;
     const int NKB = (g.n16 + 31) / 32;
@@ -164,37 +191,55 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         }
       __syncthreads();
     };
-    if (A.rec_stride == 0) tables(A.mask + head * MIX_RECORD);
+    if (A.rec_stride == 0) tables(hrec);
     const float xs = A.scale_log2 * B_UNSCALE;
 
     for (int pg = p0; pg < p1; ++pg) {
       if (A.rec_stride) tables(A.mask + (head * A.rec_stride + pg) * MIX_RECORD);
       const uint8_t* page = page_ptr(A, head, pg);
+      // the page's loads are issued together: Value codes and metadata, the
+      // first BF16 block and four Key k-steps at a time
       u32x4 vc[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) vc[ks] = ld16(page + g.off_v + 1024 * ks + 256 * a + 16 * r);
+      const uint8_t *vlo = page + g.off_v + V_CODE_BYTES, *vhi = vlo + 1024;
+      VMeta<G, NPASS> vm;
+      load_vmeta<G, NPASS>(vm, vlo, vhi, a, col);
+      u32x4 raw0[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * a + e;
+        raw0[e] = c < g.n16 ? ld16(page + 256 * c + 16 * r) : (u32x4){0u, 0u, 0u, 0u};
+      }
       f32x4 logit[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
       float bias = 0.f;
+      for (int k0 = 0; k0 < NKS; k0 += 4) {
+        u32x4 kc[4], sw[4], zw[4];
 #pragma unroll
-      for (int ks = 0; ks < MAX_KS; ++ks) {
-        if (ks >= NKS) break;
-        const int f = 4 * ks + a;
-        u32x4 kc = {0u, 0u, 0u, 0u}, sw = {0u, 0u, 0u, 0u}, zw = {0u, 0u, 0u, 0u};
-        if (f < g.F) {
-          kc = ld16(page + g.off_codes + 256 * f + 16 * r);
-          sw = ld16(page + g.off_meta + 32 * f);
-          zw = ld16(page + g.off_meta + 32 * f + 16);
+        for (int j = 0; j < 4; ++j) {
+          const int f = 4 * (k0 + j) + a;
+          kc[j] = sw[j] = zw[j] = (u32x4){0u, 0u, 0u, 0u};
+          if (k0 + j < NKS && f < g.F) {
+            kc[j] = ld16(page + g.off_codes + 256 * f + 16 * r);
+            sw[j] = ld16(page + g.off_meta + 32 * f);
+            zw[j] = ld16(page + g.off_meta + 32 * f + 16);
+          }
         }
-        half8 Bhi, Blo;
-        key_operand(S.u.qslot[ks][a][h], sw, zw, Bhi, Blo, bias);
-        const u32x4 kc8 = kc >> 8u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const half8 At = tile2(kc, kc8, i);
-          logit[i] = mfma(At, Bhi, logit[i]);
-          logit[i] = mfma(At, Blo, logit[i]);
+        for (int j = 0; j < 4; ++j) {
+          const int ks = k0 + j;
+          if (ks >= NKS) break;
+          half8 Bhi, Blo;
+          key_operand(S.u.qslot[ks][a][h], sw[j], zw[j], Bhi, Blo, bias);
+          const u32x4 kc8 = kc[j] >> 8u;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const half8 At = tile2(kc[j], kc8, i);
+            logit[i] = mfma(At, Bhi, logit[i]);
+            logit[i] = mfma(At, Blo, logit[i]);
+          }
         }
       }
 #pragma unroll
@@ -204,7 +249,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int c = 32 * kb + 8 * a + e;
-          raw[e] = c < g.n16 ? ld16(page + 256 * c + 16 * r) : (u32x4){0u, 0u, 0u, 0u};
+          raw[e] = kb == 0 ? raw0[e] : c < g.n16 ? ld16(page + 256 * c + 16 * r) : (u32x4){0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -217,30 +262,30 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
         }
       }
       bias = wave_sum_groups(bias);
-      const uint8_t *vlo = page + g.off_v + V_CODE_BYTES, *vhi = vlo + 1024;
       if constexpr (FIFO) {
         const int vlim = fifo_vlim(A, pg);
         const float m0 = st.m;
-        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
-        else consume_values<G, NPASS, true>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col, vlim, hp);
+        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vm, a, col);
+        else consume_values<G, NPASS, true>(st, logit, xs, bias * A.scale_log2, vc, vm, a, col, vlim, hp);
         fifo_after<G, NPASS>(A, st, m0, head, pg, vlim, hp, ow, lane);
       } else {
-        consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
+        consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vm, a, col);
       }
     }
   } else if constexpr (MODE == KVQ_KEY_PNMIX) {
     const PnGeo g = pn_geo(A.n_hi);
-    const uint8_t* rec = A.mask + head * PN_RECORD;
+    // the 64 pair bits, bit i of byte i / 8 (one 8-byte load; records are 8-byte aligned)
+    const uint64_t pbits = *reinterpret_cast<const uint64_t*>(A.mask + head * PN_RECORD);
     if (lane == 0) {                      // slot order: high channels ascending, then low ones
       int nh = 0;
       for (int d = 0; d < D; ++d) {
         const int pair = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? (d & 63) : (d >> 1);
-        if ((rec[pair >> 3] >> (pair & 7)) & 1) S.slot_ch[nh++] = d;
+        if ((pbits >> pair) & 1) S.slot_ch[nh++] = d;
       }
       int nl = nh;
       for (int d = 0; d < D; ++d) {
         const int pair = A.pair_layout == KVQ_PAIR_HALF_SPLIT ? (d & 63) : (d >> 1);
-        if (!((rec[pair >> 3] >> (pair & 7)) & 1)) S.slot_ch[nl++] = d;
+        if (!((pbits >> pair) & 1)) S.slot_ch[nl++] = d;
       }
     }
     __syncthreads();
@@ -296,11 +341,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
       if constexpr (FIFO) {
         const int vlim = fifo_vlim(A, pg);
         const float m0 = st.m;
-        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
-        else consume_values<G, NPASS, true>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col, vlim, hp);
+        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, VMetaAt{vlo, vhi}, a, col);
+        else consume_values<G, NPASS, true>(st, logit, xs, bias * A.scale_log2, vc, VMetaAt{vlo, vhi}, a, col, vlim, hp);
         fifo_after<G, NPASS>(A, st, m0, head, pg, vlim, hp, ow, lane);
       } else {
-        consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, vlo, vhi, a, col);
+        consume_values<G, NPASS>(st, logit, xs, bias * A.scale_log2, vc, VMetaAt{vlo, vhi}, a, col);
       }
     }
   } else {   // QJL
@@ -310,21 +355,31 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
     const int NKS = (A.qjl_m + A.qjl_mo) / 32, NKI = A.qjl_m / 32;
     const float* sqrow = A.sq + ((int64_t)b * A.n_q_heads + hq) * (A.qjl_m + A.qjl_mo);
     float ssum = 0.f, ssum_o = 0.f;
-    for (int ks = 0; ks < NKS; ++ks) {
-      float x[8];
+    for (int k0 = 0; k0 < NKS; k0 += 4) {  // four k-steps' S q loads issued together
+      float sqv[4][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = sqrow[32 * ks + 8 * a + e] * B_SCALE;
-      half8 hi, lo;
-      split8(x, hi, lo);
-      if (col < G) {
-        S.u.bq[0][ks][a][h] = hi;
-        S.u.bq[1][ks][a][h] = lo;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sqv[j][e] = k0 + j < NKS ? sqrow[32 * (k0 + j) + 8 * a + e] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ks = k0 + j;
+        if (ks >= NKS) break;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sqv[j][e] * B_SCALE;
+        half8 hi, lo;
+        split8(x, hi, lo);
+        if (col < G) {
+          S.u.bq[0][ks][a][h] = hi;
+          S.u.bq[1][ks][a][h] = lo;
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)hi[e] + (float)lo[e];
+        if (ks < NKI) ssum += part;
+        else ssum_o += part;
       }
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += (float)hi[e] + (float)lo[e];
-      if (ks < NKI) ssum += part;
-      else ssum_o += part;
     }
     ssum = wave_sum_groups(ssum);          // sum_i (S q)_i * 2^-6 as seen by the MFMA
     ssum_o = wave_sum_groups(ssum_o);
@@ -384,11 +439,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
       if constexpr (FIFO) {
         const int vlim = fifo_vlim(A, pg);
         const float m0 = st.m;
-        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, 0.f, vc, vlo, vhi, a, col);
-        else consume_values<G, NPASS, true>(st, logit, xs, 0.f, vc, vlo, vhi, a, col, vlim, hp);
+        if (vlim >= PAGE) consume_values<G, NPASS>(st, logit, xs, 0.f, vc, VMetaAt{vlo, vhi}, a, col);
+        else consume_values<G, NPASS, true>(st, logit, xs, 0.f, vc, VMetaAt{vlo, vhi}, a, col, vlim, hp);
         fifo_after<G, NPASS>(A, st, m0, head, pg, vlim, hp, ow, lane);
       } else {
-        consume_values<G, NPASS>(st, logit, xs, 0.f, vc, vlo, vhi, a, col);
+        consume_values<G, NPASS>(st, logit, xs, 0.f, vc, VMetaAt{vlo, vhi}, a, col);
       }
     }
   }
@@ -404,7 +459,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
 // columns = sketch rows, read straight from S's rows). With the outlier split
 // the rows below m see q's normal channels and the rest its outlier channels;
 // m and mo are multiples of 64, so a tile belongs to one instance. Products
-// of bf16 are exact and the sums are float, as in the scalar form.
+// of bf16 are exact and the sums are float, as in the scalar form. Every
+// load (the query rows and all of the wave's sketch tiles) is issued before
+// the first product, so a wave waits for memory once; a tile past m + mo
+// reloads the last sketch row and stores nothing.
 constexpr int QJL_PROJ_TILES = 4;
 __global__ __launch_bounds__(64) void qjl_project_mfma(const uint16_t* q, const uint16_t* S, float* sq, int m, int mo,
                                                        const uint8_t* mask, int n_rows, int n_q_heads, int group) {
@@ -412,6 +470,15 @@ __global__ __launch_bounds__(64) void qjl_project_mfma(const uint16_t* q, const 
   const int row0 = blockIdx.x * 16;
   const int mt = m + mo;
   const int qrow = min(row0 + r, n_rows - 1);                 // A row r: query row row0 + r
+  const int tile0 = blockIdx.y * QJL_PROJ_TILES;
+  bf16x8 bs[QJL_PROJ_TILES][4];                                // B column r of each tile: sketch row
+#pragma unroll
+  for (int t = 0; t < QJL_PROJ_TILES; ++t) {
+    const int srow = min(16 * (tile0 + t) + r, mt - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      bs[t][ks] = as_bf16x8(ld16(reinterpret_cast<const uint8_t*>(S + (int64_t)srow * D + 32 * ks + 8 * a)));
+  }
   bf16x8 an[4], ao[4];
   uint32_t obits = 0;                                          // outlier bits of channels 32 ks + 8 a + e
   if (mo > 0 && mask != nullptr) {
@@ -434,17 +501,15 @@ __global__ __launch_bounds__(64) void qjl_project_mfma(const uint16_t* q, const 
     __builtin_memcpy(&an[ks], nv, 16);
     __builtin_memcpy(&ao[ks], ov, 16);
   }
+#pragma unroll
   for (int t = 0; t < QJL_PROJ_TILES; ++t) {
-    const int tile = blockIdx.y * QJL_PROJ_TILES + t;
+    const int tile = tile0 + t;
     if (16 * tile >= mt) break;                                // uniform
-    const int srow = 16 * tile + r;                            // B column r: sketch row
+    const int srow = 16 * tile + r;
     const bool outlier = 16 * tile >= m;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 bs = as_bf16x8(ld16(reinterpret_cast<const uint8_t*>(S + (int64_t)srow * D + 32 * ks + 8 * a)));
-      acc = mfma_bf(outlier ? ao[ks] : an[ks], bs, acc);
-    }
+    for (int ks = 0; ks < 4; ++ks) acc = mfma_bf(outlier ? ao[ks] : an[ks], bs[t][ks], acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {                              // D row 4 a + e: query row row0 + 4 a + e
       const int row = row0 + 4 * a + e;

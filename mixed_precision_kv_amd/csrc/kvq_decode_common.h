@@ -135,17 +135,51 @@ __device__ inline void init_state(SoftState<NPASS>& st) {
   for (int u = 0; u < 8; ++u) st.acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
 }
 
+// Where consume_values takes a page's Value scale and offset words from, per
+// k-step ks: the offset row zr of the lane's value group, and the scale row
+// of value group j. VMetaAt reads them from the page's metadata halves
+// vm_lo / vm_hi where they are used; VMeta holds them loaded beforehand
+// (load_vmeta), with the page's other loads, so that a page waits for
+// memory once.
+struct VMetaAt {
+  const uint8_t* lo;
+  const uint8_t* hi;
+  __device__ inline const uint8_t* row(int ks, int a) const { return (ks < 2 ? lo : hi) + 512 * (ks & 1) + 128 * a; }
+  __device__ inline u32x4 z(int ks, int a, int zr) const { return ld16(row(ks, a) + 32 * zr + 16); }
+  __device__ inline u32x4 s(int ks, int, int a, int j) const { return ld16(row(ks, a) + 32 * j); }
+};
+template <int G, int NPASS>
+struct VMeta {
+  u32x4 zw[4];
+  u32x4 sw[4][NPASS];
+  __device__ inline u32x4 z(int ks, int, int) const { return zw[ks]; }
+  __device__ inline u32x4 s(int ks, int P, int, int) const { return sw[ks][P]; }
+};
+template <int G, int NPASS>
+__device__ inline void load_vmeta(VMeta<G, NPASS>& m, const uint8_t* vm_lo, const uint8_t* vm_hi, int a, int col) {
+  constexpr int C = 16 / G;
+  const VMetaAt at{vm_lo, vm_hi};
+  const int jl = col / G, zr = col < 4 ? col : 3;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    m.zw[ks] = at.z(ks, a, zr);
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) m.sw[ks][P] = at.s(ks, P, a, (jl + P * C) & 3);
+  }
+}
+
 // Consume one page: logit[i][e] is the raw Key accumulator of tile i row e
-// (token 16 i + 4 a + e); the log2-domain logit is logit * xs + xb.
+// (token 16 i + 4 a + e); the log2-domain logit is logit * xs + xb; vm gives
+// the page's Value metadata words (VMetaAt or VMeta).
 // HYB (KIVI Value FIFO): page tokens from vlim on have no quantized Value
 // yet: their scales and offsets are masked out of the value MFMAs (their
 // probabilities still count in the normaliser) and their binary16
 // probabilities go to hp[token][head] for the caller to weight the
 // full-precision Values with.
-template <int G, int NPASS, bool HYB = false>
+template <int G, int NPASS, bool HYB = false, class Meta>
 __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)[8], float xs, float xb,
-                                      const u32x4 (&vc)[4], const uint8_t* vm_lo, const uint8_t* vm_hi, int a,
-                                      int col, int vlim = PAGE, float (*hp)[8] = nullptr) {
+                                      const u32x4 (&vc)[4], const Meta& vm, int a, int col, int vlim = PAGE,
+                                      float (*hp)[8] = nullptr) {
   constexpr int C = 16 / G;
   float pm = -INFINITY;
 #pragma unroll
@@ -175,7 +209,6 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       p[e] = fast_exp2(fmaf(logit[2 * ks + (e >> 2)][e & 3], xs, shift));   // token pi(ks, a, e)
-    const uint8_t* kb = (ks < 2 ? vm_lo : vm_hi) + 512 * (ks & 1) + 128 * a;
     // p as binary16: the B operand of the offset MFMA, and p s of the value
     // MFMAs as one packed multiply per two tokens (two roundings of p s)
     half8 ph;
@@ -198,7 +231,7 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
     }
     {
       // sum p * offset per value group and sum p, on the MFMA (p as binary16)
-      const u32x4 zw = ld16(kb + 32 * zr + 16) & keep;
+      const u32x4 zw = vm.z(ks, a, zr) & keep;
       u32x4 za;
       za.x = col < 4 ? zw.x : zconst;
       za.y = col < 4 ? zw.y : zconst;
@@ -209,7 +242,7 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
       const int j = (jl + P * C) & 3;            // this lane's value group in pass P
-      const half8 s8 = as_half8(ld16(kb + 32 * j) & keep);
+      const half8 s8 = as_half8(vm.s(ks, P, a, j) & keep);
       const half8 B = ph * s8;
       const u32x4 v8 = vc[ks] >> 8u;
 #pragma unroll

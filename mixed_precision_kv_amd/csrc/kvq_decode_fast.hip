@@ -309,7 +309,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
     }
   }
   join_halves(logit);
-  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, slot.v_lo, slot.v_hi, a, col);
+  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, VMetaAt{slot.v_lo, slot.v_hi}, a, col);
 }
 
 // The record's tables for the page loop: slot -> channel of this lane's slots
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         f32x4 logit[8], zacc;
         pn_keys<G>(logit, zacc, k, slot, S, a, h, col);
         mid();
-        consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, slot + 1024, slot + 2048, a, col);
+        consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
@@ -752,7 +752,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2)
         f32x4 logit[8];
         qj_keys<G, OUT>(logit, k, slot, S, ssum, ssum_o, ratio, a, h, col);
         mid();
-        consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, slot + 1024, slot + 2048, a, col);
+        consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
