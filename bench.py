@@ -380,9 +380,9 @@ def fifo_leg(w, copies, torch, kvq, synth, K, W):
     copies, the push of one Value row of every (batch, kv head)
     (kvq_value_push, distinct rows) and the seal of one Key page of every
     (batch, kv head) (kvq_flush_keys). The decode is timed on the default
-    path (the pipelined kernel over the pages whose Values are all quantized
-    and the Key residual, the generic kernel over the window's page, one
-    combine) and on the generic path alone."""
+    path (the pipelined kernel over every page and the Key residual, the
+    merge adding the window Values of the tokens inside the pages) and on the
+    generic path alone."""
     dev = "cuda"
     n_pages, n_kres, R = w.n_pages, 64, 128
     T = n_pages * 128 + n_kres
@@ -431,8 +431,8 @@ def fifo_leg(w, copies, torch, kvq, synth, K, W):
     return {"workload": w.name, "sealed_pages": n_pages, "key_residual_tokens": n_kres, "quantized_values": n_vq,
             "value_window": R, "decode_ms": d_ms, "decode_GBps": gb, "decode_frac_hbm_peak": gb / HBM_PEAK_GBPS,
             "bytes_per_decode": dbytes,
-            "decode_kernels": f"decode_mix_fast (pages 0-{n_vq // 128 - 1}, Key residual) + decode_kernel<MixKVQ, "
-                              f"FIFO> (pages {n_vq // 128}-{n_pages - 1}) + combine",
+            "decode_kernels": "decode_mix_fast<FIFO> (every page, Key residual; window-page logits) + "
+                              "combine_fifo_kernel (merge + window Values)",
             "generic_path_ms": g_ms, "generic_path_GBps": dbytes / (g_ms * 1e-3) / 1e9,
             "value_push_ms": p_ms, "value_push_tokens_per_s": H / (p_ms * 1e-3),
             "key_seal_ms": s_ms, "key_seal_tokens_per_s": H * 128 / (s_ms * 1e-3)}

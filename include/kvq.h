@@ -355,13 +355,17 @@ kvq_status kvq_value_push(const kvq_config* cfg, const void* v_src, int64_t src_
  * n_vq - 1 are the pages' quantized rows and those of tokens n_vq .. T - 1
  * the window rows (vwin, [batch][n_kv_heads][vwin_stride][128] bf16, row j =
  * token n_vq + j), T = n_pages * 128 + n_kres = n_vq + n_vwin. Constraints:
- * n_vq <= n_pages * 128, 0 <= n_kres <= 128, n_vwin <= 256. Logits and the
- * global softmax as kvq_decode_attention. The pages whose Values are all
- * quantized (below n_vq / 128) and the Key residual take the pipelined
- * kernel where it covers the configuration, the pages the window reaches
- * into the generic kernel, and one merge combines them; cfg->decode_path =
- * KVQ_DECODE_GENERIC sends every page to the generic kernel (results within
- * the same bound). Other arguments and the workspace as kvq_decode_attention. */
+ * n_vq <= n_pages * 128, 0 <= n_kres <= 128, n_vwin <= 256. The pages'
+ * Value rows of tokens n_vq and later must be as kvq_flush_keys left them
+ * (cleared; the FIFO pushes a row only when it leaves the window). Logits
+ * and the global softmax as kvq_decode_attention. Where a pipelined kernel
+ * covers the configuration it runs over every page and the Key residual;
+ * the window tokens inside the pages add nothing there (cleared rows), and
+ * the split merge adds their window Values, weighted by their logits, which
+ * that kernel leaves in spare workspace records. cfg->decode_path =
+ * KVQ_DECODE_GENERIC runs the generic kernel, which takes those Values
+ * inside the page pass (results within the same bound). Other arguments and
+ * the workspace as kvq_decode_attention. */
 kvq_status kvq_decode_attention_fifo(const kvq_config* cfg, const void* q, const void* page_arena,
                                      const int32_t* page_table, int32_t table_stride, int32_t n_pages,
                                      int32_t n_vq, const void* mask, const void* qjl_s, const void* resid_k,

@@ -198,6 +198,8 @@ static kvq_status decode_prepare(const kvq_config* cfg, const void* q, const voi
   a.vq_end = INT32_MAX;   // no KIVI Value FIFO: every page token's Value is quantized
   a.vwin = nullptr;
   a.vwin_stride = 0;
+  a.fifo_clean = INT32_MAX;
+  a.fifo_wsplit = 0;
   a.out = out;
   a.sink_k = (const uint16_t*)sink_k;
   a.sink_v = (const uint16_t*)sink_v;

@@ -524,7 +524,32 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* partial, float
   merge_row<NB>(partial, out, n_parts, rows, blockIdx.x);
 }
 
-bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s);
+// The window of a Value-FIFO decode on the pipelined kernels, for its merge.
+struct FifoMerge {
+  int wsplit;                 // record of the first window page's logits
+  int t_lo, n_tok;            // first window token in that page, window tokens inside the pages
+  const uint16_t* vwin;
+  int vwin_stride;
+  int n_q_heads, n_kv_heads;
+};
+
+// Split merge plus the window tokens inside the pages (FifoWindow).
+template <int NB>
+__global__ __launch_bounds__(64) void combine_fifo_kernel(const float* partial, float* out, int n_parts, int rows,
+                                                          FifoMerge f) {
+  const int row = blockIdx.x;
+  const int b = row / f.n_q_heads, hq = row - b * f.n_q_heads;
+  const int64_t head = (int64_t)b * f.n_kv_heads + hq / (f.n_q_heads / f.n_kv_heads);
+  FifoWindow w;
+  w.logits = partial + ((int64_t)f.wsplit * rows + row) * RECORD;
+  w.rec_stride = (int64_t)rows * RECORD;
+  w.vrow0 = reinterpret_cast<const uint32_t*>(f.vwin + head * f.vwin_stride * D);
+  w.t_lo = f.t_lo;
+  w.n_tok = f.n_tok;
+  merge_row<NB>(partial, out, n_parts, rows, row, w);
+}
+
+bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s, bool fifo);
 
 // Pages per split: the page splits of every (batch, kv head) are sized to
 // fill `slots` resident workgroups in one round, with the pages spread
@@ -571,45 +596,34 @@ static hipError_t launch_generic(int key_mode, const DecodeArgs& a, int g, hipSt
   return launch_mode<KVQ_KEY_QJL>(a, g, grid, s);
 }
 
-// KIVI Value FIFO (KIVI blog sections 4-5): only the pages the full-precision
-// Value window reaches into (logical pages from vq_end / 128 on, at most
-// three) need the window's Values. The pages before them and the Key
-// residual are an ordinary decode, which goes to the pipelined kernel; the
-// window's pages go to the generic kernel, whose partials follow the
-// pipelined kernel's in the workspace, and one combine merges both. The
-// generic launch sees the window's pages as pages 0.. of a shifted arena (or
-// page table) with vq_end shifted alike, so every row it addresses is the
-// same. Returns false, having launched nothing, when the pipelined kernel
-// does not cover the configuration or the partials would not fit the
-// workspace (page splits of the whole decode + MAX_SEG_SPLITS); else `parts`
-// is the merged split count and `err` the launches' status.
-static bool launch_fifo_split(int key_mode, const DecodeArgs& a, int g, hipStream_t s, int& parts, hipError_t& err) {
+// KIVI Value FIFO on the pipelined kernels (KIVI blog sections 4-5): every
+// page and the Key residual go to the FIFO variant of the pipelined kernel
+// as an ordinary decode. The pages the full-precision Value window reaches
+// into (from vq_end / 128 on; at most two, as the window holds at most 256
+// tokens) keep their window tokens' Value rows as the Key seal left them
+// (zero), so the split kernel adds nothing for those tokens but counts their
+// probabilities; it leaves their logits in spare partial records (the last
+// n_win records the workspace holds per query head), and the merge adds
+// their window Values (combine_fifo_kernel). Returns false, having launched
+// nothing, when no pipelined kernel covers the configuration; otherwise
+// `win` is set when the merge has window tokens to add.
+static bool launch_fifo_fast(int key_mode, DecodeArgs& a, hipStream_t s, FifoMerge& fm, bool& win, hipError_t& err) {
   const int n_clean = (int)min((int64_t)a.n_pages, (int64_t)a.vq_end / PAGE);
-  const int n_tail = a.n_pages - n_clean;
-  if (n_clean == 0 || a.n_seg_splits + n_tail > MAX_SEG_SPLITS) return false;
-  DecodeArgs f = a;
-  f.n_pages = n_clean;
-  f.n_page_splits = (n_clean + a.pps - 1) / a.pps;   // <= the whole decode's page splits
-  f.vq_end = INT32_MAX;
-  f.vwin = nullptr;
-  f.vwin_stride = 0;
-  if (!launch_decode_fast(key_mode, f, s)) return false;
+  const int n_win = a.n_pages - n_clean;
+  const int cap = a.n_page_splits + MAX_SEG_SPLITS;   // records per query head in the workspace
+  if (a.n_seg_splits + n_win > MAX_SEG_SPLITS) return false;   // spare records for the window pages
+  a.fifo_clean = n_clean;
+  a.fifo_wsplit = cap - n_win;
+  if (!launch_decode_fast(key_mode, a, s, n_win > 0)) return false;
   err = hipGetLastError();
-  const int fparts = decode_parts(f);
-  parts = fparts + n_tail;
-  if (err != hipSuccess || n_tail == 0) return true;
-  DecodeArgs t = a;
-  if (a.table) t.table = a.table + n_clean;
-  else t.arena = a.arena + (int64_t)n_clean * a.page_stride;
-  t.n_pages = n_tail;
-  t.pps = 1;
-  t.n_page_splits = n_tail;
-  t.n_seg_splits = 0;
-  t.n_sink = 0;
-  t.n_resid = 0;
-  t.vq_end = a.vq_end - n_clean * PAGE;
-  t.partial = a.partial + (size_t)fparts * a.batch * a.n_q_heads * RECORD;
-  err = launch_generic(key_mode, t, g, s);
+  win = n_win > 0;
+  fm.wsplit = a.fifo_wsplit;
+  fm.t_lo = a.vq_end - n_clean * PAGE;
+  fm.n_tok = a.n_pages * PAGE - a.vq_end;
+  fm.vwin = a.vwin;
+  fm.vwin_stride = a.vwin_stride;
+  fm.n_q_heads = a.n_q_heads;
+  fm.n_kv_heads = a.n_kv_heads;
   return true;
 }
 
@@ -620,6 +634,8 @@ hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, 
   const int g = a.n_q_heads / a.n_kv_heads;
   const int n_parts = decode_parts(a);
   const int rows = a.batch * a.n_q_heads;
+  FifoMerge fm{};
+  bool win = false;   // the merge adds a Value-FIFO window (launch_fifo_fast)
   if (n_parts > 0) {
     if (key_mode == KVQ_KEY_QJL) {
       const int tiles = (a.qjl_m + a.qjl_mo) / 16;
@@ -637,11 +653,9 @@ hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, 
     // separate pass: the waits' device-scope polls slow the page stream, and
     // a store-acknowledge, count, poll, load chain costs about a launch.)
     bool done = false;
-    if (!generic && a.vq_end != INT32_MAX) {
-      int parts = 0;
-      done = launch_fifo_split(key_mode, a, g, s, parts, e);
-      if (done) a.n_page_splits = parts - a.n_seg_splits;   // the merged geometry, for the merge below
-    } else if (!generic && launch_decode_fast(key_mode, a, s)) {
+    if (!generic && a.vq_end != INT32_MAX) {   // the window is added by the merge below
+      if (with_merge) done = launch_fifo_fast(key_mode, a, s, fm, win, e);
+    } else if (!generic && launch_decode_fast(key_mode, a, s, false)) {
       done = true;
       e = hipGetLastError();
     }
@@ -658,6 +672,14 @@ hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, 
   // may have chosen its own split count (in a)
   const int parts = decode_parts(a);
   const dim3 cgrid(rows);
+  if (win) {
+    switch (merge_batch(parts)) {
+      case 16: hipLaunchKernelGGL(combine_fifo_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
+      case 32: hipLaunchKernelGGL(combine_fifo_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
+      default: hipLaunchKernelGGL(combine_fifo_kernel<64>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
+    }
+    return hipGetLastError();
+  }
   switch (merge_batch(parts)) {
     case 16: hipLaunchKernelGGL(combine_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
     case 32: hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;

@@ -359,6 +359,30 @@ __device__ inline void join_halves(f32x4 (&logit)[8]) {
     for (int e = 0; e < 4; ++e) logit[i][e] += from_partner8(logit[i][e]);
 }
 
+// KIVI Value FIFO on the pipelined kernels (KIVI blog sections 4-5): pages
+// from A.fifo_clean on hold tokens whose Values are still in the
+// full-precision window. Their page rows are as the Key seal left them
+// (codes, scales and offsets zero), so the page's Value pass adds nothing
+// for them while their probabilities count in the split's l. Their
+// log2-domain logits (logit * xs + xb, as the softmax forms them) go to a
+// spare partial record of the query head, record A.fifo_wsplit + pg -
+// A.fifo_clean, float = token in the page, for the merge to weight the
+// window's Values with. After join_halves lanes col < G hold head col's
+// logits; records are 8-byte aligned.
+template <int G>
+__device__ inline void fifo_store_logits(const DecodeArgs& A, int b, int kvh, int pg, const f32x4 (&logit)[8],
+                                         float xs, float xb, int a, int col) {
+  if (pg < A.fifo_clean || col >= G) return;
+  float* rec = A.partial + ((int64_t)(A.fifo_wsplit + pg - A.fifo_clean) * A.batch * A.n_q_heads +
+                            (int64_t)b * A.n_q_heads + kvh * G + col) * RECORD;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float2* d = reinterpret_cast<float2*>(rec + 16 * i + 4 * a);
+    d[0] = make_float2(fmaf(logit[i][0], xs, xb), fmaf(logit[i][1], xs, xb));
+    d[1] = make_float2(fmaf(logit[i][2], xs, xb), fmaf(logit[i][3], xs, xb));
+  }
+}
+
 // This lane's half of B = q * s, with qh = binary16(q * 2^-6): the hi part
 // binary16(qh s) (columns 0-7) or its rounding error binary16(qh s - hi)
 // (columns 8-15, one fused rounding). Packed half-precision arithmetic, two

@@ -207,18 +207,19 @@ __device__ inline void commit_meta(const u32x4 (&m)[3], uint8_t* slot, int lane)
 // that page p-1's Value phase has just released. Each part is in flight for
 // about one page of compute, and only one Value set is live in the Key phase.
 // Every load is unconditional (same count per page), which keeps the
-// compiler's wait counts exact.
+// compiler's wait counts exact. page(k, v, slot, p, mid): p is the page's
+// index in the split.
 template <class KP, class VP, class LK, class LV, class PG>
 __device__ inline void page_loop(int np, KP (&k)[2], VP (&v)[2], LK load_k, LV load_v, PG page) {
   for (int it = 0; it < np; it += 2) {
     progress_prio(it, np);
     if (it + 1 < np) load_k(k[1], it + 1);
-    page(k[0], v[0], 0, [&] {
+    page(k[0], v[0], 0, it, [&] {
       if (it + 1 < np) load_v(v[1], it + 1);
     });
     if (it + 1 >= np) break;
     if (it + 2 < np) load_k(k[0], it + 2);
-    page(k[1], v[1], 1, [&] {
+    page(k[1], v[1], 1, it + 1, [&] {
       if (it + 2 < np) load_v(v[0], it + 2);
     });
   }
@@ -273,10 +274,16 @@ __device__ inline void mix_issue_meta(const uint8_t* page, const MixSlot& slot, 
   async16(page + g.off_v + V_CODE_BYTES + 1024 + 16 * lane, slot.v_hi);
 }
 
-template <int G, int NKS, int NB, int NPASS>
+// win(logit, xb): sees the page's joined logits (log2 domain: logit * xs + xb)
+// before the softmax takes them (the FIFO's window logits); NoLogits ignores
+// them.
+struct NoLogits {
+  __device__ inline void operator()(const f32x4 (&)[8], float) const {}
+};
+template <int G, int NKS, int NB, int NPASS, class Win>
 __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c, const MixSlot& slot,
                                 const MixSmem<G, NKS>& S, const bf16x8& Bq, float xs, float scale_log2, int a,
-                                int h, int col) {
+                                int h, int col, Win win) {
   f32x4 logit[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -309,6 +316,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
     }
   }
   join_halves(logit);
+  win(logit, zacc[0] * scale_log2);
   consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, VMetaAt{slot.v_lo, slot.v_hi}, a, col);
 }
 
@@ -368,8 +376,9 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
 // eight-channel BF16 tier, which keeps one wave per SIMD rather than spill.
 // PREC: every page has its own record (per-flush reselection). Page p's
 // record dword comes with the page's loads; its tables are rebuilt at the
-// top of the page, after the wait that covers them.
-template <int G, int NKS, int NB, bool PAGED, bool PREC>
+// top of the page, after the wait that covers them. FIFO: the KIVI Value
+// FIFO's window pages store their logits (fifo_store_logits).
+template <int G, int NKS, int NB, bool PAGED, bool PREC, bool FIFO>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 : 2))) void decode_mix_fast(
     DecodeArgs A) {
   constexpr int C = 16 / G;
@@ -446,7 +455,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
       mix_load(c1, pset.at(it + 1), g, a, r);
       if constexpr (PREC) recn = rec_word(it + 1);
     }
-    mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col);
+    if constexpr (FIFO)
+      mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col,
+                                  [&](const f32x4 (&lg)[8], float xb) {
+                                    fifo_store_logits<G>(A, b, kvh, p0 + it, lg, xs, xb, a, col);
+                                  });
+    else
+      mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
     if (it + 1 >= np) break;
     wait_vm<0>();
     if constexpr (PREC) mix_tables<G, NKS>(recn, g, qb, S, Bq, lane, a, h, col);
@@ -455,7 +470,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
       mix_load(c0, pset.at(it + 2), g, a, r);
       if constexpr (PREC) recn = rec_word(it + 2);
     }
-    mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col);
+    if constexpr (FIFO)
+      mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col,
+                                  [&](const f32x4 (&lg)[8], float xb) {
+                                    fifo_store_logits<G>(A, b, kvh, p0 + it + 1, lg, xs, xb, a, col);
+                                  });
+    else
+      mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
   }
   __syncthreads();
   write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
@@ -506,7 +527,7 @@ __device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, c
   join_halves(logit);
 }
 
-template <int G, bool PAGED>
+template <int G, bool PAGED, bool FIFO>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_pn_fast(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
@@ -584,11 +605,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   page_loop(
       np, kp, vp, [&](PnKey& k, int p) { pn_load_key(k, pset.at(p), g, lane, a, r); },
       [&](ValCodes& v, int p) { load_vcodes(v, pset.at(p), g.off_v, a, r); },
-      [&](const PnKey& k, const ValCodes& v, int s, auto mid) {
+      [&](const PnKey& k, const ValCodes& v, int s, int p, auto mid) {
         uint8_t* slot = S.u.pg.meta[s];
         commit_meta(k.m, slot, lane);
         f32x4 logit[8], zacc;
         pn_keys<G>(logit, zacc, k, slot, S, a, h, col);
+        if constexpr (FIFO) fifo_store_logits<G>(A, b, kvh, p0 + p, logit, xs, zacc[0] * A.scale_log2, a, col);
         mid();
         consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
@@ -679,7 +701,7 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey<OUT>& c, const uin
   }
 }
 
-template <int G, bool PAGED, bool OUT>
+template <int G, bool PAGED, bool OUT, bool FIFO>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2))) void decode_qjl_fast(DecodeArgs A) {
   constexpr int C = 16 / G;
   constexpr int NPASS = (4 + C - 1) / C;
@@ -746,11 +768,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2)
   page_loop(
       np, kp, vp, [&](QjKey<OUT>& k, int p) { qj_load_key(k, pset.at(p), g, lane, a, r); },
       [&](ValCodes& v, int p) { load_vcodes(v, pset.at(p), g.off_v, a, r); },
-      [&](const QjKey<OUT>& k, const ValCodes& v, int s, auto mid) {
+      [&](const QjKey<OUT>& k, const ValCodes& v, int s, int p, auto mid) {
         uint8_t* slot = S.u.qj.meta[s];
         commit_meta(k.m, slot, lane);
         f32x4 logit[8];
         qj_keys<G, OUT>(logit, k, slot, S, ssum, ssum_o, ratio, a, h, col);
+        if constexpr (FIFO) fifo_store_logits<G>(A, b, kvh, p0 + p, logit, xs, 0.f, a, col);
         mid();
         consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
@@ -765,42 +788,44 @@ static void launch1(K kernel, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kernel, dim3(n_parts * a.n_kv_heads * a.batch), dim3(64), 0, s, a);
 }
 
-template <int G, int NKS, bool PAGED, bool PREC>
+template <int G, int NKS, bool PAGED, bool PREC, bool FIFO>
 static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
-  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0, PAGED, PREC>, a, s);
-  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1, PAGED, PREC>, a, s);
-  else if constexpr (!PREC) launch1(decode_mix_fast<G, NKS, 8, PAGED, false>, a, s);
+  if (nb == 0) launch1(decode_mix_fast<G, NKS, 0, PAGED, PREC, FIFO>, a, s);
+  else if (nb == 1) launch1(decode_mix_fast<G, NKS, 1, PAGED, PREC, FIFO>, a, s);
+  else if constexpr (!PREC) launch1(decode_mix_fast<G, NKS, 8, PAGED, false, FIFO>, a, s);
 }
-template <int G, int NKS>
+template <int G, int NKS, bool FIFO>
 static void launch_mix_nb(const DecodeArgs& a, int nb, hipStream_t s) {
-  if (a.rec_stride) {
-    if (a.table) launch_mix_nb<G, NKS, true, true>(a, nb, s);
-    else launch_mix_nb<G, NKS, false, true>(a, nb, s);
+  if constexpr (FIFO) {   // no per-page records with the Value FIFO
+    if (a.table) launch_mix_nb<G, NKS, true, false, true>(a, nb, s);
+    else launch_mix_nb<G, NKS, false, false, true>(a, nb, s);
+  } else if (a.rec_stride) {
+    if (a.table) launch_mix_nb<G, NKS, true, true, false>(a, nb, s);
+    else launch_mix_nb<G, NKS, false, true, false>(a, nb, s);
   } else {
-    if (a.table) launch_mix_nb<G, NKS, true, false>(a, nb, s);
-    else launch_mix_nb<G, NKS, false, false>(a, nb, s);
+    if (a.table) launch_mix_nb<G, NKS, true, false, false>(a, nb, s);
+    else launch_mix_nb<G, NKS, false, false, false>(a, nb, s);
   }
 }
 
-// Launches the pipelined kernel when one covers the configuration (with the
-// split geometry in `a`); returns false (nothing launched) otherwise.
-bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
+template <bool FIFO>
+static bool launch_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (g != 4 && g != 8) return false;
   if (a.table && a.pps > 64) return false;   // the split's page indices live in one register
-  if (a.rec_stride && (key_mode != KVQ_KEY_MIXKVQ || a.n16 > 1)) return false;   // per-page records: no eight-row BF16 tier
+  if (a.rec_stride && (FIFO || key_mode != KVQ_KEY_MIXKVQ || a.n16 > 1)) return false;   // per-page records: no eight-row BF16 tier
   if (key_mode == KVQ_KEY_MIXKVQ) {
     const int nks = (mix_max_fragments(a.n16, a.n4, a.head_tiers) + 3) / 4;
     if (a.n16 > 8) return false;   // the fast path keeps the BF16 tier in lane group 0 (<= 8 channels)
     const int nb = a.n16 == 0 ? 0 : (a.n16 == 1 ? 1 : 8);
     if (nks == 5) {
-      if (g == 4) launch_mix_nb<4, 5>(a, nb, s);
-      else launch_mix_nb<8, 5>(a, nb, s);
+      if (g == 4) launch_mix_nb<4, 5, FIFO>(a, nb, s);
+      else launch_mix_nb<8, 5, FIFO>(a, nb, s);
       return true;
     }
     if (nks == 4) {
-      if (g == 4) launch_mix_nb<4, 4>(a, nb, s);
-      else launch_mix_nb<8, 4>(a, nb, s);
+      if (g == 4) launch_mix_nb<4, 4, FIFO>(a, nb, s);
+      else launch_mix_nb<8, 4, FIFO>(a, nb, s);
       return true;
     }
     return false;
@@ -808,11 +833,11 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
   if (key_mode == KVQ_KEY_PNMIX) {
     if (a.n_hi != 64) return false;
     if (a.table) {
-      if (g == 4) launch1(decode_pn_fast<4, true>, a, s);
-      else launch1(decode_pn_fast<8, true>, a, s);
+      if (g == 4) launch1(decode_pn_fast<4, true, FIFO>, a, s);
+      else launch1(decode_pn_fast<8, true, FIFO>, a, s);
     } else {
-      if (g == 4) launch1(decode_pn_fast<4, false>, a, s);
-      else launch1(decode_pn_fast<8, false>, a, s);
+      if (g == 4) launch1(decode_pn_fast<4, false, FIFO>, a, s);
+      else launch1(decode_pn_fast<8, false, FIFO>, a, s);
     }
     return true;
   }
@@ -828,22 +853,30 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
     a.pps = pps;
     a.n_page_splits = a.n_pages > 0 ? (a.n_pages + pps - 1) / pps : 0;
     if (a.table) {
-      if (g == 4) launch1(decode_qjl_fast<4, true, true>, a, s);
-      else launch1(decode_qjl_fast<8, true, true>, a, s);
+      if (g == 4) launch1(decode_qjl_fast<4, true, true, FIFO>, a, s);
+      else launch1(decode_qjl_fast<8, true, true, FIFO>, a, s);
     } else {
-      if (g == 4) launch1(decode_qjl_fast<4, false, true>, a, s);
-      else launch1(decode_qjl_fast<8, false, true>, a, s);
+      if (g == 4) launch1(decode_qjl_fast<4, false, true, FIFO>, a, s);
+      else launch1(decode_qjl_fast<8, false, true, FIFO>, a, s);
     }
     return true;
   }
   if (a.table) {
-    if (g == 4) launch1(decode_qjl_fast<4, true, false>, a, s);
-    else launch1(decode_qjl_fast<8, true, false>, a, s);
+    if (g == 4) launch1(decode_qjl_fast<4, true, false, FIFO>, a, s);
+    else launch1(decode_qjl_fast<8, true, false, FIFO>, a, s);
   } else {
-    if (g == 4) launch1(decode_qjl_fast<4, false, false>, a, s);
-    else launch1(decode_qjl_fast<8, false, false>, a, s);
+    if (g == 4) launch1(decode_qjl_fast<4, false, false, FIFO>, a, s);
+    else launch1(decode_qjl_fast<8, false, false, FIFO>, a, s);
   }
   return true;
+}
+
+// Launches the pipelined kernel when one covers the configuration (with the
+// split geometry in `a`); returns false (nothing launched) otherwise. fifo:
+// the KIVI Value FIFO variant, whose window pages store their logits
+// (fifo_store_logits; a.fifo_clean and a.fifo_wsplit set by the caller).
+bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s, bool fifo) {
+  return fifo ? launch_fast<true>(key_mode, a, s) : launch_fast<false>(key_mode, a, s);
 }
 
 }  // namespace kvq

@@ -256,6 +256,8 @@ struct DecodeArgs {
   int qjl_m;
   int qjl_mo;                     // as FlushArgs::qjl_mo; the estimate's outlier term is scaled by qjl_m / qjl_mo
   int head_tiers;                 // as FlushArgs::head_tiers
+  int fifo_clean;                 // FIFO on the pipelined kernels: pages from here on hold window tokens
+  int fifo_wsplit;                // ... whose logits go to partial record fifo_wsplit + page - fifo_clean
 };
 
 hipError_t launch_flush(int key_mode, const FlushArgs& a, int batch, hipStream_t stream);

@@ -17,6 +17,52 @@ __device__ inline float wave_sum64(float v) {
   return v;
 }
 
+// What a merge adds beyond the split partials: NoWindow nothing.
+struct NoWindow {
+  __device__ inline void issue(int) {}
+  __device__ inline void apply(float, float&, float&, int) {}
+};
+
+// KIVI Value FIFO on the pipelined kernels (KIVI blog sections 4-5): the
+// window tokens inside the pages, n_tok of them from token t_lo of the first
+// window page on, whose logits the split kernel left in spare records (one
+// per window page, float = token in the page) and whose Values are the
+// window's first n_tok rows. They add 2^(x_t - M) v_t to the output sum;
+// their probabilities are already in the splits' l. Lane t of a batch of 64
+// tokens loads token t's logit, every lane its two channels of the batch's
+// rows; the first batch is issued with the merge's first loads.
+struct FifoWindow {
+  const float* logits;     // this query head's record of the first window page
+  int64_t rec_stride;      // floats from one window page's record to the next
+  const uint32_t* vrow0;   // the head's window row 0 as bf16 pairs (lane l: channels 2l, 2l + 1)
+  int t_lo, n_tok;         // n_tok >= 1
+  float x;
+  uint32_t v[64];
+  __device__ inline void load(int t0, int lane) {
+    const int p = t_lo + min(t0 + lane, n_tok - 1);
+    x = t0 + lane < n_tok ? logits[(int64_t)(p >> 7) * rec_stride + (p & 127)] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) v[j] = vrow0[(int64_t)min(t0 + j, n_tok - 1) * (D / 2) + lane];
+  }
+  __device__ inline void issue(int lane) { load(0, lane); }
+  __device__ inline void apply(float M, float& o0, float& o1, int lane) {
+    for (int t0 = 0;;) {
+      const float w = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x - M);
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        if (t0 + j < n_tok) {                                 // uniform
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+          o0 = fmaf(wj, __uint_as_float(v[j] << 16), o0);
+          o1 = fmaf(wj, __uint_as_float(v[j] & 0xFFFF0000u), o1);
+        }
+      }
+      t0 += 64;
+      if (t0 >= n_tok) break;
+      load(t0, lane);
+    }
+  }
+};
+
 // Merge of one query head's split partials (m, l, out[128] per split, out
 // scaled by 2^-m) by one wave, lane l owning channels 2l and 2l+1:
 //   M = max_j m_j, w_j = 2^(m_j - M), out = (sum_j w_j out_j) / (sum_j w_j l_j).
@@ -26,9 +72,11 @@ __device__ inline float wave_sum64(float v) {
 // the lanes as lane reads (no LDS, no barrier). The result does not depend
 // on NB, bit for bit. The first batch's loads are issued with the (m, l)
 // loads, before any reduction, so up to min(NB, 64) parts cost one memory
-// round trip. Zero parts give zero output.
-template <int NB>
-__device__ inline void merge_row(const float* partial, float* out, int n_parts, int rows, int row) {
+// round trip. Zero parts give zero output. win adds its terms to the output
+// sum before the division (its loads issued with the first batch's).
+template <int NB, class Win = NoWindow>
+__device__ inline void merge_row(const float* partial, float* out, int n_parts, int rows, int row,
+                                 Win win = Win()) {
   static_assert(NB == 16 || NB == 32 || NB == 64, "batch of parts");
   const int lane = threadIdx.x & 63;
   float* dst = out + (int64_t)row * D + 2 * lane;
@@ -44,6 +92,7 @@ __device__ inline void merge_row(const float* partial, float* out, int n_parts, 
   float2 v[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) v[j] = *reinterpret_cast<const float2*>(base + min(j, last) * stride + 2 + 2 * lane);
+  win.issue(lane);
   auto weight = [](float m, float Mx) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mx); };
   float mloc = lane <= last ? ml.x : -INFINITY;
   for (int p = lane + 64; p <= last; p += 64) mloc = fmaxf(mloc, base[p * stride]);
@@ -72,6 +121,7 @@ __device__ inline void merge_row(const float* partial, float* out, int n_parts, 
       v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, last) * stride + 2 + 2 * lane);
     w = weight(base[min(s0 + (lane & (NB - 1)), last) * stride], M);
   }
+  win.apply(M, o0, o1, lane);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   dst[0] = o0 * inv;
   dst[1] = o1 * inv;
