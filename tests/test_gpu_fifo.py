@@ -9,7 +9,9 @@ bit against the oracle's pages with their pushed Value rows. Each decode
 runs twice: on the default path (the pipelined kernel over the pages whose
 Values are all quantized and the Key residual, the generic kernel over the
 window's pages) and on the generic path alone. Cases: each Key mode; a
-longer stream (several all-quantized pages before the window); pages reached
+longer stream (several all-quantized pages before the window); a 200-token
+Value window (wider than a page: the window tokens inside the pages then
+span two pages, up to 200 of them); pages reached
 through a page table (a random permutation of the pool), run beside the
 contiguous arena and equal to it bit for bit at every step; MixKVQ threshold
 tiers (each head's page laid out by its own tier counts); the QJL outlier
@@ -52,6 +54,9 @@ CASES = [
     ("llama8b_8k", "paged"),
     ("llama8b_8k", "threshold"),
     ("qjl_outlier_32k", "count"),
+    ("llama8b_8k", "wide"),
+    ("pnmix_16k", "wide"),
+    ("qjl_outlier_32k", "wide"),
 ]
 
 
@@ -74,7 +79,8 @@ def test_fifo_decode_flow(name, variant):
                     n_resid=0, n_sink=0, seed=base.seed + 1200 + (7 if variant != "count" else 0))
     if variant == "threshold":
         w = w.scaled(n_bf16=32, n_u4=64)
-    P, S = (700 if variant == "long" else 200), 100   # prefill tokens, decode steps
+    P, S = {"long": 700, "wide": 300}.get(variant, 200), 100   # prefill tokens, decode steps
+    RV = 200 if variant == "wide" else R  # Value window (Key segments stay R = 128 tokens)
     L = w.n_pages * 128                   # the token stream (rows per head)
     g, H = w.group, w.batch * w.n_kv_heads
     print(f"\n[case] fifo {variant} {w}", flush=True)
@@ -124,7 +130,7 @@ def test_fifo_decode_flow(name, variant):
 
     # the prefill's persisted state (KIVI blog section 5, state after P tokens)
     tk = R * (P // R)                      # sealed Key tokens
-    n_vq = P - min(P, R)                   # quantized Values
+    n_vq = P - min(P, RV)                  # quantized Values
     for pg in range(tk // R):
         seal(pg * R, pg)
     if n_vq:
@@ -184,8 +190,9 @@ def test_fifo_decode_flow(name, variant):
     worst = 0.0
     for s in range(S):
         n = P + s                          # the new token's index; n + 1 tokens visible
-        st = ocache.flash_step(R, n + 1)   # section 5 state at this step
-        assert st.k_compute_full == n + 1 - tk and st.v_compute_full == n + 1 - n_vq
+        if RV == R:                        # section 5 state at this step
+            st = ocache.flash_step(R, n + 1)
+            assert st.k_compute_full == n + 1 - tk and st.v_compute_full == n + 1 - n_vq
         qd = synth.decode_query(w, dev, step=s)
         for c, r, o in [(cfg, r, r["out"]) for r in runs] + [(cfg_generic, runs[0], out_generic)]:
             kvq.kvq_decode_attention_fifo(c, qd, r["arena"], tk // R, n_vq, mask, Sm, kp + tk * row, n + 1 - tk,
@@ -207,7 +214,7 @@ def test_fifo_decode_flow(name, variant):
         if n + 1 - tk == R:
             seal(tk, tk // R)
             tk += R
-        if n + 1 - n_vq > R:
+        if n + 1 - n_vq > RV:
             push(n_vq, 1)
             n_vq += 1
     torch.cuda.synchronize()
