@@ -543,7 +543,7 @@ __global__ __launch_bounds__(64) void combine_fifo_kernel(const float* partial, 
   FifoWindow w;
   w.logits = partial + ((int64_t)f.wsplit * rows + row) * RECORD;
   w.rec_stride = (int64_t)rows * RECORD;
-  w.vrow0 = reinterpret_cast<const uint32_t*>(f.vwin + head * f.vwin_stride * D);
+  w.vrow0 = reinterpret_cast<const uint8_t*>(f.vwin + head * f.vwin_stride * D);
   w.t_lo = f.t_lo;
   w.n_tok = f.n_tok;
   merge_row<NB>(partial, out, n_parts, rows, row, w);
@@ -676,6 +676,8 @@ hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, 
     switch (merge_batch(parts)) {
       case 16: hipLaunchKernelGGL(combine_fifo_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
       case 32: hipLaunchKernelGGL(combine_fifo_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
+      case 40: hipLaunchKernelGGL(combine_fifo_kernel<40>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
+      case 48: hipLaunchKernelGGL(combine_fifo_kernel<48>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
       default: hipLaunchKernelGGL(combine_fifo_kernel<64>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows, fm); break;
     }
     return hipGetLastError();
@@ -683,6 +685,8 @@ hipError_t launch_decode(int key_mode, DecodeArgs& args, const uint16_t* qjl_s, 
   switch (merge_batch(parts)) {
     case 16: hipLaunchKernelGGL(combine_kernel<16>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
     case 32: hipLaunchKernelGGL(combine_kernel<32>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
+    case 40: hipLaunchKernelGGL(combine_kernel<40>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
+    case 48: hipLaunchKernelGGL(combine_kernel<48>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
     default: hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(64), 0, s, a.partial, a.out, parts, rows); break;
   }
   return hipGetLastError();

@@ -28,38 +28,66 @@ struct NoWindow {
 // window page on, whose logits the split kernel left in spare records (one
 // per window page, float = token in the page) and whose Values are the
 // window's first n_tok rows. They add 2^(x_t - M) v_t to the output sum;
-// their probabilities are already in the splits' l. Lane t of a batch of 64
-// tokens loads token t's logit, every lane its two channels of the batch's
-// rows; the first batch is issued with the merge's first loads.
+// their probabilities are already in the splits' l. A batch of 64 tokens:
+// lane t loads token t's logit, and sixteen 16-byte loads per lane bring the
+// rows, four per load (lane group g = lane / 16 row 4k + g, eight channels
+// 8 (lane % 16) ..); the sums over the four row groups and the move to the
+// merge's layout (lane l: channels 2l, 2l + 1) go through lane shuffles.
+// The first batch is issued with the merge's first loads (17 loads, so that
+// with a batch of up to 40 parts they stay within the 63 a wave keeps in
+// flight).
 struct FifoWindow {
   const float* logits;     // this query head's record of the first window page
   int64_t rec_stride;      // floats from one window page's record to the next
-  const uint32_t* vrow0;   // the head's window row 0 as bf16 pairs (lane l: channels 2l, 2l + 1)
+  const uint8_t* vrow0;    // the head's window row 0 (bf16 rows of 256 bytes)
   int t_lo, n_tok;         // n_tok >= 1
   float x;
-  uint32_t v[64];
+  uint4 v[16];
   __device__ inline void load(int t0, int lane) {
     const int p = t_lo + min(t0 + lane, n_tok - 1);
     x = t0 + lane < n_tok ? logits[(int64_t)(p >> 7) * rec_stride + (p & 127)] : -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) v[j] = vrow0[(int64_t)min(t0 + j, n_tok - 1) * (D / 2) + lane];
+    for (int k = 0; k < 16; ++k) {
+      const int t = min(t0 + 4 * k + (lane >> 4), n_tok - 1);
+      v[k] = *reinterpret_cast<const uint4*>(vrow0 + (int64_t)t * (2 * D) + 16 * (lane & 15));
+    }
   }
   __device__ inline void issue(int lane) { load(0, lane); }
   __device__ inline void apply(float M, float& o0, float& o1, int lane) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int t0 = 0;;) {
-      const float w = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x - M);
+      const float w = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x - M);   // tokens past n_tok weigh 0
 #pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        if (t0 + j < n_tok) {                                 // uniform
-          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-          o0 = fmaf(wj, __uint_as_float(v[j] << 16), o0);
-          o1 = fmaf(wj, __uint_as_float(v[j] & 0xFFFF0000u), o1);
+      for (int k = 0; k < 16; ++k) {
+        const float wk = __shfl(w, 4 * k + (lane >> 4));
+        const uint32_t d[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(wk, __uint_as_float(d[q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wk, __uint_as_float(d[q] & 0xFFFF0000u), acc[2 * q + 1]);
         }
       }
       t0 += 64;
       if (t0 >= n_tok) break;
       load(t0, lane);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[e] += __shfl_xor(acc[e], 16);
+      acc[e] += __shfl_xor(acc[e], 32);
+    }
+    // channels 2 lane, 2 lane + 1 are elements 2 (lane % 4), + 1 of lane (lane / 4)'s block
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a0 = __shfl(acc[2 * q], lane >> 2), a1 = __shfl(acc[2 * q + 1], lane >> 2);
+      if ((lane & 3) == q) {
+        s0 = a0;
+        s1 = a1;
+      }
+    }
+    o0 += s0;
+    o1 += s1;
   }
 };
 
@@ -77,7 +105,7 @@ struct FifoWindow {
 template <int NB, class Win = NoWindow>
 __device__ inline void merge_row(const float* partial, float* out, int n_parts, int rows, int row,
                                  Win win = Win()) {
-  static_assert(NB == 16 || NB == 32 || NB == 64, "batch of parts");
+  static_assert(NB == 16 || NB == 32 || NB == 40 || NB == 48 || NB == 64, "batch of parts");
   const int lane = threadIdx.x & 63;
   float* dst = out + (int64_t)row * D + 2 * lane;
   if (n_parts <= 0) {
@@ -119,7 +147,7 @@ __device__ inline void merge_row(const float* partial, float* out, int n_parts, 
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, last) * stride + 2 + 2 * lane);
-    w = weight(base[min(s0 + (lane & (NB - 1)), last) * stride], M);
+    w = weight(base[min(s0 + lane % NB, last) * stride], M);
   }
   win.apply(M, o0, o1, lane);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -127,7 +155,11 @@ __device__ inline void merge_row(const float* partial, float* out, int n_parts, 
   dst[1] = o1 * inv;
 }
 
-// NB for a call with n_parts parts: one batch whenever n_parts <= 64.
-inline int merge_batch(int n_parts) { return n_parts <= 16 ? 16 : (n_parts <= 32 ? 32 : 64); }
+// NB for a call with n_parts parts: one batch whenever n_parts <= 64, and
+// the smallest that covers the call (a wave keeps at most 63 loads in
+// flight: NB + 1 loads of a batch past that wait for a second round trip).
+inline int merge_batch(int n_parts) {
+  return n_parts <= 16 ? 16 : n_parts <= 32 ? 32 : n_parts <= 40 ? 40 : n_parts <= 48 ? 48 : 64;
+}
 
 }  // namespace kvq
