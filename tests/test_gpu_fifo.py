@@ -15,7 +15,8 @@ span two pages, up to 200 of them); pages reached
 through a page table (a random permutation of the pool), run beside the
 contiguous arena and equal to it bit for bit at every step; MixKVQ threshold
 tiers (each head's page laid out by its own tier counts); the QJL outlier
-split.
+split; and single decodes in the states the flows do not reach (no sealed
+page at all, a window over every sealed page, a window of 252 tokens).
 """
 import math
 
@@ -39,6 +40,7 @@ pytestmark = [pytest.mark.gpu,
 TOL = 2e-3
 D = 128
 R = 128
+ROW = 128 * 2                             # bytes per bf16 token row
 
 
 def bits(t):
@@ -72,6 +74,145 @@ def threshold_taus(q_pre, k, w, qs):
     return tuple(float(np.quantile(vals, x)) for x in qs)
 
 
+class FifoRig:
+    """A Value-FIFO cache of workload w on the GPU (its records selected over
+    the prefill's first Key segment) and the oracle's view of two of its
+    (batch, kv head) slices. paged: a second arena reached through a random
+    permutation of the pool, kept beside the contiguous one."""
+
+    def __init__(self, w, tau=None, paged=False):
+        self.w, self.tau = w, tau
+        self.L = L = w.n_pages * 128      # the token stream (rows per head)
+        self.g, H = w.group, w.batch * w.n_kv_heads
+        dev = "cuda"
+        self.q_pre, self.k, self.v = q_pre, k, v = synth.prefill(w, dev)
+        self.cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, w.n_pages, n_bf16=w.n_bf16,
+                                   n_u4=w.n_u4, n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m, qjl_outliers=w.qjl_outliers,
+                                   qjl_m_out=w.qjl_m_out,
+                                   select_mode=kvq.KVQ_SELECT_THRESHOLD if tau else kvq.KVQ_SELECT_COUNT,
+                                   tau_bf16=tau[0] if tau else 0.0, tau_u4=tau[1] if tau else 0.0)
+        self.cfg_generic = kvq.with_fields(self.cfg, decode_path=kvq.KVQ_DECODE_GENERIC)
+        self.Sm = Sm = synth.qjl_matrix(w, dev) if w.key_mode == synth.QJL else None
+        self.mb = mb = kvq.kvq_mask_bytes(self.cfg)
+        self.mask = torch.zeros(max(1, H * mb), dtype=torch.uint8, device=dev)
+        if w.key_mode != synth.QJL:       # selection over the prefill's first Key segment
+            kvq.kvq_select_channels(self.cfg, q_pre, 128, k, 128, self.mask, q_stride=L, k_stride=L)
+        elif w.qjl_outliers:              # outlier channels from the same segment's Keys
+            kvq.kvq_select_channels(self.cfg, None, 0, k, 128, self.mask, k_stride=L)
+        self.pb = pb = kvq.kvq_page_bytes(self.cfg)
+        self.flags = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.ws_bytes = kvq.kvq_workspace_bytes(self.cfg, w.n_pages)
+        self.ws = torch.zeros(self.ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+        self.kp, self.vp = k.data_ptr(), v.data_ptr()
+        self.runs = [dict(arena=torch.zeros(H * w.n_pages * pb, dtype=torch.uint8, device=dev), table=None,
+                          out=torch.zeros(w.batch, w.n_q_heads, D, dtype=torch.float32, device=dev))]
+        if paged:
+            gen = torch.Generator(device="cpu").manual_seed(w.seed)
+            table = torch.randperm(H * w.n_pages, generator=gen).to(torch.int32).reshape(H, w.n_pages)
+            self.runs.append(dict(arena=torch.zeros_like(self.runs[0]["arena"]), table=table.to(dev),
+                                  out=torch.zeros_like(self.runs[0]["out"])))
+        self.out_generic = torch.zeros_like(self.runs[0]["out"])
+        self._oracle_side()
+
+    def tab(self, r):
+        return dict(page_table=r["table"], table_stride=self.w.n_pages if r["table"] is not None else 0)
+
+    def seal(self, tok, page):
+        for r in self.runs:
+            kvq.kvq_flush_keys(self.cfg, self.kp + tok * ROW, self.kp + tok * ROW, self.L, 1, self.mask, self.Sm,
+                               r["arena"], page, self.flags, **self.tab(r))
+
+    def push(self, first, n_rows):
+        for r in self.runs:
+            kvq.kvq_value_push(self.cfg, self.vp + first * ROW, self.L, n_rows, first, self.mask, r["arena"],
+                               self.flags, **self.tab(r))
+
+    def _oracle_side(self):
+        """The records, the full pages and the decode arguments of two slices."""
+        w, g = self.w, self.g
+        self.kb = {(b, h): bits(self.k[b, h]) for b in range(w.batch) for h in range(w.n_kv_heads)}
+        self.vb = {(b, h): bits(self.v[b, h]) for b in range(w.batch) for h in range(w.n_kv_heads)}
+        self.heads = [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]
+        s_bits = bits(self.Sm) if self.Sm is not None else None
+        self.off_v, self.dkw, full = {}, {}, {}
+        for b, h in self.heads:
+            kb, vb = self.kb[(b, h)], self.vb[(b, h)]
+            qb = bits(self.q_pre[b, h * g:(h + 1) * g, :128])
+            if w.key_mode == synth.MIXKVQ:
+                if self.tau:
+                    tier, perm = osel.mixkvq_threshold_select(qb, kb[:128], w.n_bf16, w.n_u4, *self.tau)[:2]
+                else:
+                    tier, perm, _ = osel.mixkvq_select(qb, kb[:128], w.n_bf16, w.n_u4)
+                rec = osel.mixkvq_record(tier, perm)
+                n16, n4 = osel.record_counts(rec) if self.tau else (w.n_bf16, w.n_u4)
+                self.off_v[(b, h)] = olayout.mixkvq_geometry(n16, n4)["off_v"]
+                self.dkw[(b, h)] = dict(n16=n16, n4=n4, perm=rec[:128])
+                page = lambda kk, vv, rec=rec, n16=n16, n4=n4: oflush.flush_mixkvq_page(kk, vv, rec[:128], n16, n4)
+            elif w.key_mode == synth.PNMIX:
+                rec = osel.pnmix_select(qb, kb[:128], w.n_hi_pairs)[2]
+                self.off_v[(b, h)] = olayout.pnmix_geometry(2 * w.n_hi_pairs)["off_v"]
+                self.dkw[(b, h)] = dict(mask_rec=rec)
+                page = lambda kk, vv, rec=rec: oflush.flush_pnmix_page(kk, vv, osel.hi_channels_from_record(rec))
+            elif w.qjl_outliers:
+                rec = oqjl.outlier_record(oqjl.outlier_mask(kb[:128], w.qjl_outliers))
+                outl = oqjl.outlier_mask_from_record(rec)
+                self.off_v[(b, h)] = olayout.qjl_geometry(w.qjl_m, w.qjl_m_out)["off_v"]
+                self.dkw[(b, h)] = dict(s_bits=s_bits, qjl_m=w.qjl_m, outl=outl)
+                page = lambda kk, vv, outl=outl: oflush.flush_qjl_page(kk, vv, s_bits, m=w.qjl_m, outl=outl)
+            else:
+                rec = None
+                self.off_v[(b, h)] = olayout.qjl_geometry(w.qjl_m)["off_v"]
+                self.dkw[(b, h)] = dict(s_bits=s_bits)
+                page = lambda kk, vv: oflush.flush_qjl_page(kk, vv, s_bits)
+            if self.mb:                   # the GPU's record is the oracle's
+                i = b * w.n_kv_heads + h
+                assert np.array_equal(self.mask[i * self.mb:(i + 1) * self.mb].cpu().numpy(), rec), (b, h)
+            full[(b, h)] = [page(kb[128 * pg:128 * pg + 128], vb[128 * pg:128 * pg + 128]) for pg in range(w.n_pages)]
+        self.full = full
+
+    def oracle_pages(self, b, h, tk, n_vq):
+        return [oatt.fifo_page(self.full[(b, h)][pg], self.off_v[(b, h)], min(R, max(0, n_vq - R * pg)))
+                for pg in range(tk // R)]
+
+    def decode_check(self, tk, n_vq, T, qd, tag):
+        """Decode the T visible tokens (tk sealed Key tokens, Values below
+        n_vq quantized) on the default and the generic path; every arena's
+        default output equal, both within the bound of the oracle. Returns
+        the worst error."""
+        w, g = self.w, self.g
+        for c, r, o in [(self.cfg, r, r["out"]) for r in self.runs] + [(self.cfg_generic, self.runs[0],
+                                                                         self.out_generic)]:
+            kvq.kvq_decode_attention_fifo(c, qd, r["arena"], tk // R, n_vq, self.mask, self.Sm,
+                                          self.kp + tk * ROW, T - tk, self.L, self.vp + n_vq * ROW, T - n_vq, self.L,
+                                          1 / math.sqrt(D), o, self.ws, self.ws_bytes, **self.tab(r))
+        torch.cuda.synchronize()
+        for r in self.runs[1:]:
+            assert torch.equal(r["out"], self.runs[0]["out"]), tag
+        outs = {"default": self.runs[0]["out"].cpu().numpy(), "generic": self.out_generic.cpu().numpy()}
+        worst = 0.0
+        for b, h in self.heads:
+            kb, vb = self.kb[(b, h)], self.vb[(b, h)]
+            ref, _ = oatt.decode_arena_head(w.key_mode, bits(qd[b, h * g:(h + 1) * g]),
+                                            self.oracle_pages(b, h, tk, n_vq), 1 / math.sqrt(D),
+                                            resid_k=kb[tk:T], n_vq=n_vq, vwin=vb[n_vq:T], **self.dkw[(b, h)])
+            for path, o in outs.items():
+                err = rel_err(o[b, h * g:(h + 1) * g], ref)
+                worst = max(worst, float(err.max()))
+                assert np.all(err <= TOL), (tag, path, b, h, err)
+        return worst
+
+    def pages_check(self, tk, n_vq, tag):
+        H, pb = self.w.batch * self.w.n_kv_heads, self.pb
+        for r in self.runs:
+            a = r["arena"].cpu().numpy().reshape(H * self.w.n_pages, pb)
+            t = r["table"].cpu().numpy() if r["table"] is not None else None
+            for b, h in self.heads:
+                hi = b * self.w.n_kv_heads + h
+                for pg, ref in enumerate(self.oracle_pages(b, h, tk, n_vq)):
+                    slot = int(t[hi, pg]) if t is not None else hi * self.w.n_pages + pg
+                    assert np.array_equal(a[slot][:ref.size], ref), (tag, b, h, pg)
+
+
 @pytest.mark.parametrize("name,variant", CASES)
 def test_fifo_decode_flow(name, variant):
     base = synth.WORKLOADS[name]
@@ -81,111 +222,20 @@ def test_fifo_decode_flow(name, variant):
         w = w.scaled(n_bf16=32, n_u4=64)
     P, S = {"long": 700, "wide": 300}.get(variant, 200), 100   # prefill tokens, decode steps
     RV = 200 if variant == "wide" else R  # Value window (Key segments stay R = 128 tokens)
-    L = w.n_pages * 128                   # the token stream (rows per head)
-    g, H = w.group, w.batch * w.n_kv_heads
     print(f"\n[case] fifo {variant} {w}", flush=True)
-    dev = "cuda"
-    q_pre, k, v = synth.prefill(w, dev)
-    tau = threshold_taus(q_pre.cpu(), k.cpu(), w, (0.93, 0.7)) if variant == "threshold" else None
-    cfg = kvq.make_config(w.key_mode, w.batch, w.n_q_heads, w.n_kv_heads, w.n_pages, n_bf16=w.n_bf16, n_u4=w.n_u4,
-                          n_hi_pairs=w.n_hi_pairs, qjl_m=w.qjl_m, qjl_outliers=w.qjl_outliers,
-                          qjl_m_out=w.qjl_m_out,
-                          select_mode=kvq.KVQ_SELECT_THRESHOLD if tau else kvq.KVQ_SELECT_COUNT,
-                          tau_bf16=tau[0] if tau else 0.0, tau_u4=tau[1] if tau else 0.0)
-    Sm = synth.qjl_matrix(w, dev) if w.key_mode == synth.QJL else None
-    mb = kvq.kvq_mask_bytes(cfg)
-    mask = torch.zeros(max(1, H * mb), dtype=torch.uint8, device=dev)
-    if w.key_mode != synth.QJL:           # selection over the prefill's first Key segment
-        kvq.kvq_select_channels(cfg, q_pre, 128, k, 128, mask, q_stride=L, k_stride=L)
-    elif w.qjl_outliers:                  # outlier channels from the same segment's Keys
-        kvq.kvq_select_channels(cfg, None, 0, k, 128, mask, k_stride=L)
-    pb = kvq.kvq_page_bytes(cfg)
-    flags = torch.zeros(4, dtype=torch.int32, device=dev)
-    ws_bytes = kvq.kvq_workspace_bytes(cfg, w.n_pages)
-    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
-    kp, vp = k.data_ptr(), v.data_ptr()
-    row = 128 * 2                          # bytes per token row
-    # the arenas the flow runs on: contiguous, and with "paged" also one through a table
-    runs = [dict(arena=torch.zeros(H * w.n_pages * pb, dtype=torch.uint8, device=dev), table=None,
-                 out=torch.zeros(w.batch, w.n_q_heads, D, dtype=torch.float32, device=dev))]
-    if variant == "paged":
-        gen = torch.Generator(device="cpu").manual_seed(w.seed)
-        table = torch.randperm(H * w.n_pages, generator=gen).to(torch.int32).reshape(H, w.n_pages)
-        runs.append(dict(arena=torch.zeros_like(runs[0]["arena"]), table=table.to(dev),
-                         out=torch.zeros_like(runs[0]["out"])))
-
-    cfg_generic = kvq.with_fields(cfg, decode_path=kvq.KVQ_DECODE_GENERIC)
-    out_generic = torch.zeros_like(runs[0]["out"])
-
-    def tab(r):
-        return dict(page_table=r["table"], table_stride=w.n_pages if r["table"] is not None else 0)
-
-    def seal(tok, page):
-        for r in runs:
-            kvq.kvq_flush_keys(cfg, kp + tok * row, kp + tok * row, L, 1, mask, Sm, r["arena"], page, flags, **tab(r))
-
-    def push(first, n_rows):
-        for r in runs:
-            kvq.kvq_value_push(cfg, vp + first * row, L, n_rows, first, mask, r["arena"], flags, **tab(r))
+    tau = None
+    if variant == "threshold":             # quantiles of the same (device-generated) prefill
+        q_pre, k, _ = synth.prefill(w, "cuda")
+        tau = threshold_taus(q_pre.cpu(), k.cpu(), w, (0.93, 0.7))
+    rig = FifoRig(w, tau=tau, paged=variant == "paged")
 
     # the prefill's persisted state (KIVI blog section 5, state after P tokens)
     tk = R * (P // R)                      # sealed Key tokens
     n_vq = P - min(P, RV)                  # quantized Values
     for pg in range(tk // R):
-        seal(pg * R, pg)
+        rig.seal(pg * R, pg)
     if n_vq:
-        push(0, n_vq)
-
-    # oracle side: the records, the sealed pages (Values added as they leave)
-    kb = {(b, h): bits(k[b, h]) for b in range(w.batch) for h in range(w.n_kv_heads)}
-    vb = {(b, h): bits(v[b, h]) for b in range(w.batch) for h in range(w.n_kv_heads)}
-    heads = [(0, 0), (w.batch - 1, w.n_kv_heads - 1)]
-    s_bits = bits(Sm) if Sm is not None else None
-    recs, off_v, dkw = {}, {}, {}
-    for b, h in heads:
-        qb = bits(q_pre[b, h * g:(h + 1) * g, :128])
-        if w.key_mode == synth.MIXKVQ:
-            if tau:
-                tier, perm = osel.mixkvq_threshold_select(qb, kb[(b, h)][:128], w.n_bf16, w.n_u4, *tau)[:2]
-            else:
-                tier, perm, _ = osel.mixkvq_select(qb, kb[(b, h)][:128], w.n_bf16, w.n_u4)
-            rec = osel.mixkvq_record(tier, perm)
-            n16, n4 = osel.record_counts(rec) if tau else (w.n_bf16, w.n_u4)
-            off_v[(b, h)] = olayout.mixkvq_geometry(n16, n4)["off_v"]
-            dkw[(b, h)] = dict(n16=n16, n4=n4, perm=rec[:128])
-        elif w.key_mode == synth.PNMIX:
-            rec = osel.pnmix_select(qb, kb[(b, h)][:128], w.n_hi_pairs)[2]
-            off_v[(b, h)] = olayout.pnmix_geometry(2 * w.n_hi_pairs)["off_v"]
-            dkw[(b, h)] = dict(mask_rec=rec)
-        elif w.qjl_outliers:
-            rec = oqjl.outlier_record(oqjl.outlier_mask(kb[(b, h)][:128], w.qjl_outliers))
-            off_v[(b, h)] = olayout.qjl_geometry(w.qjl_m, w.qjl_m_out)["off_v"]
-            dkw[(b, h)] = dict(s_bits=s_bits, qjl_m=w.qjl_m, outl=oqjl.outlier_mask_from_record(rec))
-        else:
-            rec = None
-            off_v[(b, h)] = olayout.qjl_geometry(w.qjl_m)["off_v"]
-            dkw[(b, h)] = dict(s_bits=s_bits)
-        recs[(b, h)] = rec
-        if mb:                             # the GPU's record is the oracle's
-            gpu_rec = mask[(b * w.n_kv_heads + h) * mb:(b * w.n_kv_heads + h + 1) * mb].cpu().numpy()
-            assert np.array_equal(gpu_rec, rec), (name, variant, b, h)
-
-    def oracle_full_page(b, h, pg):
-        kk, vv = kb[(b, h)][128 * pg:128 * pg + 128], vb[(b, h)][128 * pg:128 * pg + 128]
-        rec = recs[(b, h)]
-        if w.key_mode == synth.MIXKVQ:
-            return oflush.flush_mixkvq_page(kk, vv, rec[:128], dkw[(b, h)]["n16"], dkw[(b, h)]["n4"])
-        if w.key_mode == synth.PNMIX:
-            return oflush.flush_pnmix_page(kk, vv, osel.hi_channels_from_record(rec))
-        if w.qjl_outliers:
-            return oflush.flush_qjl_page(kk, vv, s_bits, m=w.qjl_m, outl=dkw[(b, h)]["outl"])
-        return oflush.flush_qjl_page(kk, vv, s_bits)
-
-    full_pages = {(b, h): [oracle_full_page(b, h, pg) for pg in range(w.n_pages)] for b, h in heads}
-
-    def oracle_pages(b, h, tk, n_vq):
-        return [oatt.fifo_page(full_pages[(b, h)][pg], off_v[(b, h)], min(R, max(0, n_vq - R * pg)))
-                for pg in range(tk // R)]
+        rig.push(0, n_vq)
 
     worst = 0.0
     for s in range(S):
@@ -193,39 +243,47 @@ def test_fifo_decode_flow(name, variant):
         if RV == R:                        # section 5 state at this step
             st = ocache.flash_step(R, n + 1)
             assert st.k_compute_full == n + 1 - tk and st.v_compute_full == n + 1 - n_vq
-        qd = synth.decode_query(w, dev, step=s)
-        for c, r, o in [(cfg, r, r["out"]) for r in runs] + [(cfg_generic, runs[0], out_generic)]:
-            kvq.kvq_decode_attention_fifo(c, qd, r["arena"], tk // R, n_vq, mask, Sm, kp + tk * row, n + 1 - tk,
-                                          L, vp + n_vq * row, n + 1 - n_vq, L, 1 / math.sqrt(D), o, ws,
-                                          ws_bytes, **tab(r))
-        torch.cuda.synchronize()
-        for r in runs[1:]:
-            assert torch.equal(r["out"], runs[0]["out"]), (name, variant, s)
-        outs = {"default": runs[0]["out"].cpu().numpy(), "generic": out_generic.cpu().numpy()}
-        for b, h in heads:
-            ref, _ = oatt.decode_arena_head(w.key_mode, bits(qd[b, h * g:(h + 1) * g]), oracle_pages(b, h, tk, n_vq),
-                                            1 / math.sqrt(D), resid_k=kb[(b, h)][tk:n + 1], n_vq=n_vq,
-                                            vwin=vb[(b, h)][n_vq:n + 1], **dkw[(b, h)])
-            for tag, o in outs.items():
-                err = rel_err(o[b, h * g:(h + 1) * g], ref)
-                worst = max(worst, float(err.max()))
-                assert np.all(err <= TOL), (name, variant, tag, s, b, h, err)
+        worst = max(worst, rig.decode_check(tk, n_vq, n + 1, synth.decode_query(w, "cuda", step=s),
+                                            (name, variant, s)))
         # after the step: seal a full Key segment, move the oldest Value out
         if n + 1 - tk == R:
-            seal(tk, tk // R)
+            rig.seal(tk, tk // R)
             tk += R
         if n + 1 - n_vq > RV:
-            push(n_vq, 1)
+            rig.push(n_vq, 1)
             n_vq += 1
     torch.cuda.synchronize()
-    assert int(flags[0].item()) == 0
-    for r in runs:
-        a = r["arena"].cpu().numpy().reshape(H * w.n_pages, pb)
-        t = r["table"].cpu().numpy() if r["table"] is not None else None
-        for b, h in heads:
-            hi = b * w.n_kv_heads + h
-            for pg, ref in enumerate(oracle_pages(b, h, tk, n_vq)):
-                slot = int(t[hi, pg]) if t is not None else hi * w.n_pages + pg
-                assert np.array_equal(a[slot][:ref.size], ref), (name, variant, b, h, pg)
+    assert int(rig.flags[0].item()) == 0
+    rig.pages_check(tk, n_vq, (name, variant))
     print(f"[fifo] {name} {variant}: {S} steps, sealed {tk} Key tokens, {n_vq} quantized Values, "
           f"worst error {worst:.2e}")
+
+
+EDGE = [
+    # (sealed Key tokens, quantized Values, visible tokens)
+    (0, 0, 50),       # no sealed page: every token in the Key residual and the window
+    (128, 0, 228),    # the window over the whole sealed page and the Key residual (228 rows)
+    (256, 256, 300),  # no window token inside the pages
+    (256, 48, 300),   # a window of 252 tokens: two window pages, 208 of its tokens inside them
+    (384, 384, 384),  # no residual, no window
+]
+
+
+@pytest.mark.parametrize("name", ["llama8b_8k", "pnmix_16k", "qjl_outlier_32k"])
+def test_fifo_edge_states(name):
+    """Single FIFO decodes in states the flows do not reach, on both paths
+    against the oracle; the pages of the last state bit for bit."""
+    base = synth.WORKLOADS[name]
+    w = base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=4, n_resid=0, n_sink=0,
+                    seed=base.seed + 1250)
+    print(f"\n[case] fifo edges {w}", flush=True)
+    for tk, n_vq, T in EDGE:
+        rig = FifoRig(w)
+        for pg in range(tk // R):
+            rig.seal(pg * R, pg)
+        if n_vq:
+            rig.push(0, n_vq)
+        err = rig.decode_check(tk, n_vq, T, synth.decode_query(w, "cuda"), (name, tk, n_vq, T))
+        assert int(rig.flags[0].item()) == 0
+        rig.pages_check(tk, n_vq, (name, tk, n_vq, T))
+        print(f"[fifo edge] {name} sealed {tk} quantized {n_vq} visible {T}: worst error {err:.2e}")
