@@ -172,6 +172,44 @@ def test_validation_rejects_before_launch(lib):
     assert S.kvq_read_stream(16, 16384 + 16, 16, 4, None) == kvq.KVQ_WORKSPACE_TOO_SMALL   # 2 chunks, 1 word
 
 
+def test_fifo_validation_rejects_before_launch(lib):
+    """The KIVI Value FIFO's entry points check their arguments before any
+    launch (every call here fails a check, so no pointer is touched)."""
+    S = lib
+    cfg = kvq.make_config(kvq.KVQ_KEY_MIXKVQ, 1, 4, 1, 8, n_bf16=16, n_u4=32)
+    rec = kvq.with_fields(cfg, page_records=1)
+    big = 1 << 30
+    # Key seal: the flush's checks, and no per-page records
+    assert S.kvq_flush_keys(ctypes.byref(cfg), 16, 16, 128, 1, 16, None, 16, None, 0, 8, 16, None) == kvq.KVQ_CAPACITY
+    assert S.kvq_flush_keys(ctypes.byref(cfg), 8, 8, 128, 1, 16, None, 16, None, 0, 0, 16, None) == kvq.KVQ_INVALID_ARG
+    assert S.kvq_flush_keys(ctypes.byref(rec), 16, 16, 128, 1, 16, None, 16, None, 0, 0, 16, None) == kvq.KVQ_UNSUPPORTED
+    # Value push
+    push = S.kvq_value_push
+    assert push(ctypes.byref(cfg), 16, 128, 0, 0, 16, 16, None, 0, 16, None) == kvq.KVQ_OK            # nothing to push
+    assert push(ctypes.byref(cfg), 16, 128, -1, 0, 16, 16, None, 0, 16, None) == kvq.KVQ_INVALID_ARG
+    assert push(ctypes.byref(cfg), 16, 4, 8, 0, 16, 16, None, 0, 16, None) == kvq.KVQ_INVALID_ARG     # stride < rows
+    assert push(ctypes.byref(cfg), 8, 128, 1, 0, 16, 16, None, 0, 16, None) == kvq.KVQ_INVALID_ARG    # misaligned rows
+    assert push(ctypes.byref(cfg), 16, 128, 1, 0, 16, 16, None, 0, None, None) == kvq.KVQ_INVALID_ARG  # no status word
+    assert push(ctypes.byref(cfg), 16, 2048, 1, 8 * 128, 16, 16, None, 0, 16, None) == kvq.KVQ_CAPACITY   # page 8
+    assert push(ctypes.byref(cfg), 16, 2048, 1, 4 * 128, 16, 16, 16, 4, 16, None) == kvq.KVQ_CAPACITY   # past the table
+    assert push(ctypes.byref(rec), 16, 128, 1, 0, 16, 16, None, 0, 16, None) == kvq.KVQ_UNSUPPORTED
+
+    # FIFO decode: cfg, q, arena, table, table_stride, n_pages, n_vq, mask, qjl_s, resid_k, n_kres, kres_stride,
+    # vwin, n_vwin, vwin_stride, scale, out, workspace, workspace_bytes, stream
+    def fifo(c, n_pages, n_vq, n_kres, n_vwin, vwin=16, ws_bytes=big):
+        return S.kvq_decode_attention_fifo(ctypes.byref(c), 16, 16, None, 0, n_pages, n_vq, 16, None, 16, n_kres,
+                                           max(n_kres, 1), vwin, n_vwin, max(n_vwin, 1), 0.088, 16, 16, ws_bytes, None)
+    assert fifo(cfg, 2, 100, 129, 285) == kvq.KVQ_INVALID_ARG          # Key residual longer than 128
+    assert fifo(cfg, 2, 0, 1, 257) == kvq.KVQ_INVALID_ARG              # window longer than 256
+    assert fifo(cfg, 1, 129, 1, 0) == kvq.KVQ_INVALID_ARG              # quantized Values past the pages
+    assert fifo(cfg, 1, 100, 0, -1) == kvq.KVQ_INVALID_ARG             # negative window
+    assert fifo(cfg, 2, 100, 10, 100) == kvq.KVQ_INVALID_ARG           # n_pages 128 + n_kres != n_vq + n_vwin
+    assert fifo(cfg, 2, 100, 10, 166, vwin=8) == kvq.KVQ_INVALID_ARG   # misaligned window
+    assert fifo(cfg, 2, 100, 10, 166, vwin=None) == kvq.KVQ_INVALID_ARG
+    assert fifo(cfg, 2, 100, 10, 166, ws_bytes=16) == kvq.KVQ_WORKSPACE_TOO_SMALL
+    assert fifo(rec, 2, 100, 10, 166) == kvq.KVQ_UNSUPPORTED
+
+
 def test_threshold_config(lib):
     """Threshold tiers: the thresholds' domain is checked; the page stride is
     the largest page any counts within the capacities need (fewer BF16
