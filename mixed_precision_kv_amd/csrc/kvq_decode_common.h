@@ -11,6 +11,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float B_SCALE = 0.015625f;   // 2^-6 applied to every Key B operand (f16 range headroom)
@@ -315,6 +316,35 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
   }
 }
 
+
+// write_partial without the LDS staging: each lane stores its meaningful
+// tiles straight from the accumulators. Lane (a, col), col = (copy jl, head
+// h), holds channels 16 u + 4 a .. + 3 of head h for the value tiles u whose
+// group u / 2 it covers ((u / 2) % C == jl); those tiles are stored as two
+// 8-byte pairs each (records are 8-byte aligned), so every (head, channel)
+// is written once, with no barrier and no LDS traffic.
+template <int G, int NPASS>
+__device__ inline void write_partial_direct(const DecodeArgs& A, const SoftState<NPASS>& st, int split, int b,
+                                            int kvh, int a, int col) {
+  constexpr int C = 16 / G;
+  const int h = col % G, jl = col / G;
+  const float l = __shfl(st.zl[0], 16 + col);   // row 4 (lane group 1): sum p
+  float zg[4];                                   // rows 0-3 (lane group 0): sum p * offset of group j
+#pragma unroll
+  for (int j = 0; j < 4; ++j) zg[j] = __shfl(st.zl[j], col);
+  float* rec = A.partial + (((int64_t)split * A.batch + b) * A.n_q_heads + kvh * G + h) * RECORD;
+  if (a == 0 && jl == 0) __builtin_nontemporal_store((f32x2){st.m, l}, reinterpret_cast<f32x2*>(rec));
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int j = u >> 1;
+    if (j % C != jl) continue;                   // this lane's column carries another group's scale
+    const float z = j == 0 ? zg[0] : (j == 1 ? zg[1] : (j == 2 ? zg[2] : zg[3]));
+    const float sc = tile_unscale(u);            // value tiles carry the operand factor 4^(u & 3) * 2^-24
+    f32x2* d = reinterpret_cast<f32x2*>(rec + 2 + 16 * u + 4 * a);
+    __builtin_nontemporal_store((f32x2){fmaf(st.acc[u][0], sc, z), fmaf(st.acc[u][1], sc, z)}, d);
+    __builtin_nontemporal_store((f32x2){fmaf(st.acc[u][2], sc, z), fmaf(st.acc[u][3], sc, z)}, d + 1);
+  }
+}
 
 // Key slot operand for k-step ks: B = q * s * 2^-6 (hi/lo), bias += q . z
 // (s, z binary16; q * s has at most 8 + 11 significant bits, so hi + lo

@@ -478,8 +478,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     else
       mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
   }
-  __syncthreads();
-  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
+  write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
 
 // ------------------------------------------------------------------ PN-Mix
@@ -614,8 +613,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         mid();
         consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
-  __syncthreads();
-  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
+  write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
 
 // ------------------------------------------------------------------ QJL (m = 256)
@@ -777,8 +775,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2)
         mid();
         consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
-  __syncthreads();
-  write_partial<G, NPASS>(A, st, split, b, kvh, a, col, &S.u.p_lds[0][0]);
+  write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
 
 // ------------------------------------------------------------------ dispatch
