@@ -256,6 +256,115 @@ __device__ inline void consume_values(SoftState<NPASS>& st, const f32x4 (&logit)
   }
 }
 
+// DPP within each 16-lane row (ctrl 0x128 = rotate by 8: lane c reads lane
+// c ^ 8, its partner across the hi/lo Key operand halves); lanes outside the
+// bank mask keep `old`.
+template <int CTRL, int BANKS>
+__device__ inline uint32_t dpp_u(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANKS, false);
+}
+template <int CTRL, int BANKS>
+__device__ inline float dpp_f(float old, float src) {
+  return __uint_as_float(dpp_u<CTRL, BANKS>(__float_as_uint(old), __float_as_uint(src)));
+}
+
+// lane col ^ 8's value (row rotate by 8)
+__device__ inline float from_partner8(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+// Hi/lo column split (pipelined kernels): columns col < 8 carry the f16 hi
+// part of the Key operand, columns col >= 8 the lo part, so one MFMA per
+// tile covers both, leaving the two partial logits in lanes col and col ^ 8.
+// Rather than both lanes of a pair adding all 32 values, each forms half of
+// them: lanes col < 8 the joined logits of tiles 0-3, lanes col >= 8 those
+// of tiles 4-7, in J[0..3].
+__device__ inline void half_join(const f32x4 (&L)[8], f32x4 (&J)[4], bool hi) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float own = hi ? L[t][e] : L[t + 4][e];    // the tile this lane joins
+      const float give = hi ? L[t + 4][e] : L[t][e];   // the tile its partner joins
+      J[t][e] = own + from_partner8(give);
+    }
+}
+
+// consume_values for logits joined by half_join: the softmax maximum, the
+// exponentials and their binary16 conversion run on the lane's 16 tokens
+// (tiles 0-3 or 4-7); the two k-steps' binary16 probabilities the partner
+// lane formed arrive by DPP, so every lane then holds all four k-steps'
+// operands as before. Same results as consume_values on the fully joined
+// logits, bit for bit.
+template <int G, int NPASS, class Meta>
+__device__ inline void consume_own(SoftState<NPASS>& st, const f32x4 (&J)[4], float xs, float xb,
+                                   const u32x4 (&vc)[4], const Meta& vm, int a, int col) {
+  constexpr int C = 16 / G;
+  float pm = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pm = fmaxf(pm, J[t][e]);
+  pm = fmaxf(pm, dpp_f<0x128, 0xF>(pm, pm));
+  pm = fmaf(wave_max_groups(pm), xs, xb);
+  const float mn = fmaxf(st.m, pm);
+  if (__any(mn > st.m)) {
+    const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - mn);
+    st.zl *= alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st.acc[u] *= alpha;
+    st.m = mn;
+  }
+  const float shift = xb - st.m;
+  // own k-steps: lanes < 8 hold k-steps 0, 1 (tiles 0-3), lanes >= 8 k-steps 2, 3
+  u32x4 own[2], oth[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    half8 ph;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      ph[e] = (_Float16)fast_exp2(fmaf(J[2 * k2 + (e >> 2)][e & 3], xs, shift));   // token pi(ks, a, e)
+    __builtin_memcpy(&own[k2], &ph, 16);
+    oth[k2].x = dpp_u<0x128, 0xF>(0u, own[k2].x);   // the partner's two k-steps
+    oth[k2].y = dpp_u<0x128, 0xF>(0u, own[k2].y);
+    oth[k2].z = dpp_u<0x128, 0xF>(0u, own[k2].z);
+    oth[k2].w = dpp_u<0x128, 0xF>(0u, own[k2].w);
+  }
+  const bool hi = col < 8;
+  const int jl = col / G;
+  const int zr = col < 4 ? col : 3;
+  const uint32_t zconst = col == 4 ? 0x3C003C00u : 0u;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    // k-steps 0, 1 are the own ones of lanes < 8, k-steps 2, 3 of lanes >= 8
+    const bool mine = (ks < 2) == hi;
+    const half8 ph = as_half8(mine ? own[ks & 1] : oth[ks & 1]);
+    {
+      const u32x4 zw = vm.z(ks, a, zr);
+      u32x4 za;
+      za.x = col < 4 ? zw.x : zconst;
+      za.y = col < 4 ? zw.y : zconst;
+      za.z = col < 4 ? zw.z : zconst;
+      za.w = col < 4 ? zw.w : zconst;
+      st.zl = mfma(as_half8(za), ph, st.zl);
+    }
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) {
+      const int j = (jl + P * C) & 3;
+      const half8 s8 = as_half8(vm.s(ks, P, a, j));
+      const half8 B = ph * s8;
+      const u32x4 v8 = vc[ks] >> 8u;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        if (w2 / C != P) continue;
+        st.acc[2 * w2] = mfma(tile2(vc[ks], v8, 2 * w2), B, st.acc[2 * w2]);
+        st.acc[2 * w2 + 1] = mfma(tile2(vc[ks], v8, 2 * w2 + 1), B, st.acc[2 * w2 + 1]);
+      }
+    }
+  }
+}
+
 // LDS staging area (8 KB) for write_partial: the BF16-segment buffer, free
 // once a split's page loop has ended.
 template <class Smem>
@@ -373,43 +482,29 @@ __device__ inline void key_operand_scaled(const float* qv, const u32x4& sw, half
   }
 }
 
-// Hi/lo column split (pipelined kernels): columns col < 8 carry the f16 hi
-// part of the Key operand, columns col >= 8 the lo part, so one MFMA per
-// tile covers both; the two partial logits are then added across the lanes
-// col and col ^ 8 of each 16-lane row (DPP row_ror:8).
-__device__ inline float from_partner8(float v) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-}
-
-__device__ inline void join_halves(f32x4 (&logit)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) logit[i][e] += from_partner8(logit[i][e]);
-}
-
 // KIVI Value FIFO on the pipelined kernels (KIVI blog sections 4-5): pages
 // from A.fifo_clean on hold tokens whose Values are still in the
 // full-precision window. Their page rows are as the Key seal left them
 // (codes, scales and offsets zero), so the page's Value pass adds nothing
 // for them while their probabilities count in the split's l. Their
-// log2-domain logits (logit * xs + xb, as the softmax forms them) go to a
-// spare partial record of the query head, record A.fifo_wsplit + pg -
+// log2-domain logits (J * xs + xb, as the softmax forms them) go to a spare
+// partial record of the query head, record A.fifo_wsplit + pg -
 // A.fifo_clean, float = token in the page, for the merge to weight the
-// window's Values with. After join_halves lanes col < G hold head col's
-// logits; records are 8-byte aligned.
+// window's Values with. After half_join, lanes (col & 7) < G hold head
+// col & 7's logits of tiles 0-3 (col < 8) or 4-7 (col >= 8); records are
+// 8-byte aligned.
 template <int G>
-__device__ inline void fifo_store_logits(const DecodeArgs& A, int b, int kvh, int pg, const f32x4 (&logit)[8],
-                                         float xs, float xb, int a, int col) {
-  if (pg < A.fifo_clean || col >= G) return;
+__device__ inline void fifo_store_own(const DecodeArgs& A, int b, int kvh, int pg, const f32x4 (&J)[4], float xs,
+                                      float xb, int a, int col) {
+  if (pg < A.fifo_clean || (col & 7) >= G) return;
+  const int h = col & 7, t0 = col >= 8 ? 4 : 0;
   float* rec = A.partial + ((int64_t)(A.fifo_wsplit + pg - A.fifo_clean) * A.batch * A.n_q_heads +
-                            (int64_t)b * A.n_q_heads + kvh * G + col) * RECORD;
+                            (int64_t)b * A.n_q_heads + kvh * G + h) * RECORD;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float2* d = reinterpret_cast<float2*>(rec + 16 * i + 4 * a);
-    d[0] = make_float2(fmaf(logit[i][0], xs, xb), fmaf(logit[i][1], xs, xb));
-    d[1] = make_float2(fmaf(logit[i][2], xs, xb), fmaf(logit[i][3], xs, xb));
+  for (int t = 0; t < 4; ++t) {
+    float2* d = reinterpret_cast<float2*>(rec + 16 * (t0 + t) + 4 * a);
+    d[0] = make_float2(fmaf(J[t][0], xs, xb), fmaf(J[t][1], xs, xb));
+    d[1] = make_float2(fmaf(J[t][2], xs, xb), fmaf(J[t][3], xs, xb));
   }
 }
 

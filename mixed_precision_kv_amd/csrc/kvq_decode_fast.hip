@@ -274,15 +274,20 @@ __device__ inline void mix_issue_meta(const uint8_t* page, const MixSlot& slot, 
   async16(page + g.off_v + V_CODE_BYTES + 1024 + 16 * lane, slot.v_hi);
 }
 
-// win(logit, xb): sees the page's joined logits (log2 domain: logit * xs + xb)
-// before the softmax takes them (the FIFO's window logits); NoLogits ignores
-// them.
+// win(J, xb): sees the page's logits as half_join leaves them (log2 domain:
+// J * xs + xb) before the softmax takes them (the FIFO's window logits);
+// NoLogits ignores them.
 struct NoLogits {
-  __device__ inline void operator()(const f32x4 (&)[8], float) const {}
+  __device__ inline void operator()(const f32x4 (&)[4], float) const {}
 };
-template <int G, int NKS, int NB, int NPASS, class Win>
+// NQ = 4: Bq[k] is the BF16-tier operand of the tiles i with i & 3 = k,
+// scaled like their code operands, and the tile factor is undone after the
+// join on the lane's 16 logits. NQ = 1 (fewer registers, for the per-page
+// record variant): Bq[0] in true units, the factor undone on all 32 raw
+// logits before the BF16 tier is added.
+template <int G, int NKS, int NB, int NPASS, int NQ, class Win>
 __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c, const MixSlot& slot,
-                                const MixSmem<G, NKS>& S, const bf16x8& Bq, float xs, float scale_log2, int a,
+                                const MixSmem<G, NKS>& S, const bf16x8 (&Bq)[NQ], float xs, float scale_log2, int a,
                                 int h, int col, Win win) {
   f32x4 logit[8];
 #pragma unroll
@@ -301,8 +306,11 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
       logit[2 * w + 1] = mfma(tile2(c.kc[ks], k8, 2 * w + 1), B, logit[2 * w + 1]);
     }
   }
+  // the code operands carry 4^(i & 3) * 2^-24
+  if constexpr (NQ == 1) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);   // code operands carry 4^(i & 3) * 2^-24
+    for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
+  }
   if constexpr (NB > 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -312,24 +320,29 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
         tmp[e] = e < NB ? (uint16_t)(rd(c.bf[e < NB ? e : 0], i >> 1) >> (16 * (i & 1))) : (uint16_t)0;
       bf16x8 Ak;
       __builtin_memcpy(&Ak, tmp, 16);
-      logit[i] = mfma_bf(Ak, Bq, logit[i]);   // Bq is zero in the lo columns
+      logit[i] = mfma_bf(Ak, Bq[NQ == 4 ? (i & 3) : 0], logit[i]);   // Bq is zero in the lo columns
     }
   }
-  join_halves(logit);
-  win(logit, zacc[0] * scale_log2);
-  consume_values<G, NPASS>(st, logit, xs, zacc[0] * scale_log2, c.vc, VMetaAt{slot.v_lo, slot.v_hi}, a, col);
+  f32x4 J[4];
+  half_join(logit, J, col < 8);
+  if constexpr (NQ == 4) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) J[t] *= tile_unscale(t);   // tiles t and t + 4 carry the same factor
+  }
+  win(J, zacc[0] * scale_log2);
+  consume_own<G, NPASS>(st, J, xs, zacc[0] * scale_log2, c.vc, VMetaAt{slot.v_lo, slot.v_hi}, a, col);
 }
 
 // The record's tables for the page loop: slot -> channel of this lane's slots
 // and the BF16-tier channels of its lane group (bytes of the record, one
 // dword per lane in recw), the query of each slot's channel per head into
 // S.u.pg (q * 2^-6 as the Key operand, binary16 q as the offset operand) and
-// the BF16-tier operand Bq. The staged bf16 query rows qb are read first,
+// the BF16-tier operands Bq4. The staged bf16 query rows qb are read first,
 // then the tables written: interleaved, each read would wait for the writes
 // before it.
-template <int G, int NKS>
+template <int G, int NKS, int NQ>
 __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t* qb, MixSmem<G, NKS>& S,
-                                  bf16x8& Bq, int lane, int a, int h, int col) {
+                                  bf16x8 (&Bq)[NQ], int lane, int a, int h, int col) {
   constexpr int NJ = (32 * NKS + 63) / 64;
   int sch[NJ];
 #pragma unroll
@@ -368,8 +381,13 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
       }
     }
   }
+  // the BF16-tier operand: q * 2^-6, for NQ = 4 also times 4^k * 2^-24 for the
+  // tiles with i & 3 = k (exact power-of-two scalings of the bf16 query)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) Bq[e] = (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * B_SCALE : 0.f);
+  for (int k = 0; k < NQ; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      Bq[k][e] = (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * (NQ == 4 ? B_SCALE / tile_unscale(k) : B_SCALE) : 0.f);
 }
 
 // Registers of 256 VGPRs (two waves per SIMD) fit every variant except the
@@ -377,7 +395,7 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
 // PREC: every page has its own record (per-flush reselection). Page p's
 // record dword comes with the page's loads; its tables are rebuilt at the
 // top of the page, after the wait that covers them. FIFO: the KIVI Value
-// FIFO's window pages store their logits (fifo_store_logits).
+// FIFO's window pages store their logits (fifo_store_own).
 template <int G, int NKS, int NB, bool PAGED, bool PREC, bool FIFO>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 : 2))) void decode_mix_fast(
     DecodeArgs A) {
@@ -423,8 +441,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   __builtin_amdgcn_sched_barrier(0);
   stage_q<G>(qv, qb, lane);
   __syncthreads();
-  bf16x8 Bq;
-  mix_tables<G, NKS>(recw, g, qb, S, Bq, lane, a, h, col);
+  constexpr int NQ = PREC ? 1 : 4;
+  bf16x8 Bq[NQ];
+  mix_tables<G, NKS, NQ>(recw, g, qb, S, Bq, lane, a, h, col);
   *reinterpret_cast<u32x4*>(km0 + 16 * lane) = m0[0];
   *reinterpret_cast<u32x4*>(vl0 + 16 * lane) = m0[1];
   *reinterpret_cast<u32x4*>(vh0 + 16 * lane) = m0[2];
@@ -448,7 +467,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
     wait_vm<0>();
     if constexpr (PREC) {
-      if (it > 0) mix_tables<G, NKS>(recn, g, qb, S, Bq, lane, a, h, col);
+      if (it > 0) mix_tables<G, NKS, NQ>(recn, g, qb, S, Bq, lane, a, h, col);
     }
     if (it + 1 < np) {
       mix_issue_meta(pset.at(it + 1), slot1, g, lane);
@@ -456,27 +475,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
       if constexpr (PREC) recn = rec_word(it + 1);
     }
     if constexpr (FIFO)
-      mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col,
-                                  [&](const f32x4 (&lg)[8], float xb) {
-                                    fifo_store_logits<G>(A, b, kvh, p0 + it, lg, xs, xb, a, col);
+      mix_page<G, NKS, NB, NPASS, NQ>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col,
+                                  [&](const f32x4 (&lg)[4], float xb) {
+                                    fifo_store_own<G>(A, b, kvh, p0 + it, lg, xs, xb, a, col);
                                   });
     else
-      mix_page<G, NKS, NB, NPASS>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
+      mix_page<G, NKS, NB, NPASS, NQ>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
     if (it + 1 >= np) break;
     wait_vm<0>();
-    if constexpr (PREC) mix_tables<G, NKS>(recn, g, qb, S, Bq, lane, a, h, col);
+    if constexpr (PREC) mix_tables<G, NKS, NQ>(recn, g, qb, S, Bq, lane, a, h, col);
     if (it + 2 < np) {
       mix_issue_meta(pset.at(it + 2), slot0, g, lane);
       mix_load(c0, pset.at(it + 2), g, a, r);
       if constexpr (PREC) recn = rec_word(it + 2);
     }
     if constexpr (FIFO)
-      mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col,
-                                  [&](const f32x4 (&lg)[8], float xb) {
-                                    fifo_store_logits<G>(A, b, kvh, p0 + it + 1, lg, xs, xb, a, col);
+      mix_page<G, NKS, NB, NPASS, NQ>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col,
+                                  [&](const f32x4 (&lg)[4], float xb) {
+                                    fifo_store_own<G>(A, b, kvh, p0 + it + 1, lg, xs, xb, a, col);
                                   });
     else
-      mix_page<G, NKS, NB, NPASS>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
+      mix_page<G, NKS, NB, NPASS, NQ>(st, c1, slot1, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
   }
   write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
@@ -498,8 +517,9 @@ __device__ inline void pn_load_key(PnKey& c, const uint8_t* page, const PnGeo& g
 }
 
 template <int G>
-__device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, const uint8_t* slot,
+__device__ inline void pn_keys(f32x4 (&J)[4], f32x4& zacc, const PnKey& c, const uint8_t* slot,
                                const PgSmem<G, 4>& S, int a, int h, int col) {
+  f32x4 logit[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   zacc = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -521,9 +541,9 @@ __device__ inline void pn_keys(f32x4 (&logit)[8], f32x4& zacc, const PnKey& c, c
       for (int i = 0; i < 8; ++i) logit[i] = mfma(tile2(c.up[ks], u8, i), U, logit[i]);
     }
   }
+  half_join(logit, J, col < 8);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) logit[i] *= tile_unscale(i);
-  join_halves(logit);
+  for (int t = 0; t < 4; ++t) J[t] *= tile_unscale(t);   // code operands carry 4^(t & 3) * 2^-24
 }
 
 template <int G, bool PAGED, bool FIFO>
@@ -607,11 +627,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       [&](const PnKey& k, const ValCodes& v, int s, int p, auto mid) {
         uint8_t* slot = S.u.pg.meta[s];
         commit_meta(k.m, slot, lane);
-        f32x4 logit[8], zacc;
-        pn_keys<G>(logit, zacc, k, slot, S, a, h, col);
-        if constexpr (FIFO) fifo_store_logits<G>(A, b, kvh, p0 + p, logit, xs, zacc[0] * A.scale_log2, a, col);
+        f32x4 J[4], zacc;
+        pn_keys<G>(J, zacc, k, slot, S, a, h, col);
+        if constexpr (FIFO) fifo_store_own<G>(A, b, kvh, p0 + p, J, xs, zacc[0] * A.scale_log2, a, col);
         mid();
-        consume_values<G, NPASS>(st, logit, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
+        consume_own<G, NPASS>(st, J, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
   write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
@@ -642,9 +662,10 @@ __device__ inline void qj_load_key(QjKey<OUT>& c, const uint8_t* page, const Qjl
 // MFMAs run one tile at a time once the inlier tiles are done (four more
 // accumulator registers, not 32).
 template <int G, bool OUT>
-__device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey<OUT>& c, const uint8_t* slot,
+__device__ inline void qj_keys(f32x4 (&J)[4], const QjKey<OUT>& c, const uint8_t* slot,
                                const QjSmem<G, OUT ? 10 : 8>& S, float ssum, float ssum_o, float ratio, int a, int h,
                                int col) {
+  f32x4 logit[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) logit[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -658,27 +679,33 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey<OUT>& c, const uin
       for (int T = 0; T < 8; ++T) logit[T] = mfma(tile1(x, T), B, logit[T]);
     }
   }
-  join_halves(logit);
-  // tokens 16 i + 4 a + e have their norms at 32 a + 4 i + e
-  const uint8_t* nb = slot + 64 * a;
+  const bool hi = col < 8;
+  half_join(logit, J, hi);   // this lane's tiles: t (lanes < 8) or t + 4
+  // tokens 16 i + 4 a + e have their norms at 32 a + 4 i + e; the lane's
+  // tiles 2 q2, 2 q2 + 1 (own numbering) are one 16-byte read
+  const uint8_t* nb = slot + 64 * a + (hi ? 0 : 32);
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    const u32x4 nw = lds16(nb + 16 * qd);
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const u32x4 nw = lds16(nb + 16 * q2);
     u32x4 nwo = {0u, 0u, 0u, 0u};
-    if constexpr (OUT) nwo = lds16(nb + 256 + 16 * qd);
+    if constexpr (OUT) nwo = lds16(nb + 256 + 16 * q2);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * qd + ii;
-      f32x4 lo = {0.f, 0.f, 0.f, 0.f};
+      const int t = 2 * q2 + ii;   // tiles t and t + 4 carry the same factor
+      f32x4 jo = {0.f, 0.f, 0.f, 0.f};
       if constexpr (OUT) {
+        // the outlier instance's tiles t and t + 4, joined like the inlier ones
+        f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const half8 B = S.u.qj.bq[col >> 3][8 + hf][a][h];
           const u32x4& ob = c.bits[OUT ? 4 : 0];   // the outlier block
-          lo = mfma(tile1(row1(rd(ob, 2 * hf), rd(ob, 2 * hf + 1)), i), B, lo);
+          const Row1 x = row1(rd(ob, 2 * hf), rd(ob, 2 * hf + 1));
+          oa = mfma(tile1(x, t), B, oa);
+          ob4 = mfma(tile1(x, t + 4), B, ob4);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo[e] += from_partner8(lo[e]);
+        for (int e = 0; e < 4; ++e) jo[e] = (hi ? oa[e] : ob4[e]) + from_partner8(hi ? ob4[e] : oa[e]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -691,9 +718,9 @@ __device__ inline void qj_keys(f32x4 (&logit)[8], const QjKey<OUT>& c, const uin
           const uint16_t hbo = (uint16_t)(rd(nwo, 2 * ii + (e >> 1)) >> (16 * (e & 1)));
           _Float16 hvo;
           __builtin_memcpy(&hvo, &hbo, 2);
-          est_o = ratio * (float)hvo * fmaf(2.0f * tile_unscale(i), lo[e], -ssum_o);
+          est_o = ratio * (float)hvo * fmaf(2.0f * tile_unscale(t), jo[e], -ssum_o);
         }
-        logit[i][e] = fmaf((float)hv, fmaf(2.0f * tile_unscale(i), logit[i][e], -ssum), est_o);
+        J[t][e] = fmaf((float)hv, fmaf(2.0f * tile_unscale(t), J[t][e], -ssum), est_o);
       }
     }
   }
@@ -769,11 +796,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2)
       [&](const QjKey<OUT>& k, const ValCodes& v, int s, int p, auto mid) {
         uint8_t* slot = S.u.qj.meta[s];
         commit_meta(k.m, slot, lane);
-        f32x4 logit[8];
-        qj_keys<G, OUT>(logit, k, slot, S, ssum, ssum_o, ratio, a, h, col);
-        if constexpr (FIFO) fifo_store_logits<G>(A, b, kvh, p0 + p, logit, xs, 0.f, a, col);
+        f32x4 J[4];
+        qj_keys<G, OUT>(J, k, slot, S, ssum, ssum_o, ratio, a, h, col);
+        if constexpr (FIFO) fifo_store_own<G>(A, b, kvh, p0 + p, J, xs, 0.f, a, col);
         mid();
-        consume_values<G, NPASS>(st, logit, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
+        consume_own<G, NPASS>(st, J, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
       });
   write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
@@ -871,7 +898,7 @@ static bool launch_fast(int key_mode, DecodeArgs& a, hipStream_t s) {
 // Launches the pipelined kernel when one covers the configuration (with the
 // split geometry in `a`); returns false (nothing launched) otherwise. fifo:
 // the KIVI Value FIFO variant, whose window pages store their logits
-// (fifo_store_logits; a.fifo_clean and a.fifo_wsplit set by the caller).
+// (fifo_store_own; a.fifo_clean and a.fifo_wsplit set by the caller).
 bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s, bool fifo) {
   return fifo ? launch_fast<true>(key_mode, a, s) : launch_fast<false>(key_mode, a, s);
 }
