@@ -420,7 +420,7 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
       const int u = ch >> 4, aa = (ch >> 2) & 3, e = ch & 3;
       const int j = u >> 1, c = (j % C) * G + hh;  // column holding (group j, head hh)
       const float v = stage[(c * 8 + u) * 16 + aa * 4 + e] + (extra ? extra[hh][k] : 0.f);
-      __builtin_nontemporal_store(v, &base[hh * RECORD + 2 + ch]);
+      __builtin_nontemporal_store(v, &base[hh * RECORD + REC_OUT + ch]);
     }
   }
 }
@@ -429,9 +429,9 @@ __device__ inline void write_partial(const DecodeArgs& A, SoftState<NPASS>& st, 
 // write_partial without the LDS staging: each lane stores its meaningful
 // tiles straight from the accumulators. Lane (a, col), col = (copy jl, head
 // h), holds channels 16 u + 4 a .. + 3 of head h for the value tiles u whose
-// group u / 2 it covers ((u / 2) % C == jl); those tiles are stored as two
-// 8-byte pairs each (records are 8-byte aligned), so every (head, channel)
-// is written once, with no barrier and no LDS traffic.
+// group u / 2 it covers ((u / 2) % C == jl); each such tile is one 16-byte
+// store (the four lane groups fill 64 contiguous bytes of the record), so
+// every (head, channel) is written once, with no barrier and no LDS traffic.
 template <int G, int NPASS>
 __device__ inline void write_partial_direct(const DecodeArgs& A, const SoftState<NPASS>& st, int split, int b,
                                             int kvh, int a, int col) {
@@ -449,9 +449,9 @@ __device__ inline void write_partial_direct(const DecodeArgs& A, const SoftState
     if (j % C != jl) continue;                   // this lane's column carries another group's scale
     const float z = j == 0 ? zg[0] : (j == 1 ? zg[1] : (j == 2 ? zg[2] : zg[3]));
     const float sc = tile_unscale(u);            // value tiles carry the operand factor 4^(u & 3) * 2^-24
-    f32x2* d = reinterpret_cast<f32x2*>(rec + 2 + 16 * u + 4 * a);
-    __builtin_nontemporal_store((f32x2){fmaf(st.acc[u][0], sc, z), fmaf(st.acc[u][1], sc, z)}, d);
-    __builtin_nontemporal_store((f32x2){fmaf(st.acc[u][2], sc, z), fmaf(st.acc[u][3], sc, z)}, d + 1);
+    __builtin_nontemporal_store((f32x4){fmaf(st.acc[u][0], sc, z), fmaf(st.acc[u][1], sc, z),
+                                        fmaf(st.acc[u][2], sc, z), fmaf(st.acc[u][3], sc, z)},
+                                reinterpret_cast<f32x4*>(rec + REC_OUT + 16 * u + 4 * a));
   }
 }
 
@@ -660,8 +660,8 @@ __device__ inline void bf16_segment(const DecodeArgs& A, int split, int b, int k
       rec[0] = mh[8 + hh];
       rec[1] = lsum[hh];
     }
-    rec[2 + 2 * lane] = o[hh][0];
-    rec[2 + 2 * lane + 1] = o[hh][1];
+    rec[REC_OUT + 2 * lane] = o[hh][0];
+    rec[REC_OUT + 2 * lane + 1] = o[hh][1];
   }
 }
 

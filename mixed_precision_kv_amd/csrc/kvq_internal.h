@@ -248,7 +248,7 @@ struct DecodeArgs {
   int vwin_stride;
   float scale_log2;
   float qjl_coef;
-  float* partial;                 // [n_splits][B][Hq][130]: m, l, out[128]
+  float* partial;                 // [n_splits][B][Hq][RECORD]: m, l, unused, out[128] (from REC_OUT)
   float* out;                     // [B][Hq][128]
   int batch, n_kv_heads, n_q_heads;
   int n16, n4;
@@ -273,7 +273,8 @@ hipError_t launch_decode(int key_mode, DecodeArgs& a, const uint16_t* qjl_s, hip
                          int path);
 int decode_parts(const DecodeArgs& a);
 hipError_t launch_merge_flush(int key_mode, const DecodeArgs& d, const FlushArgs& f, int batch, hipStream_t s);
-constexpr int RECORD = 130;       // partial record per query head: m, l, out[128]
+constexpr int RECORD = 144;       // partial record per query head: m, l, 14 unused, out[128]
+constexpr int REC_OUT = 16;       // out[] offset: records and out[] are 64-byte aligned (whole-line stores)
 constexpr int DECODE_SLOTS = 2048;
 // Sink + residual tokens per BF16-segment workgroup; at most 256 segment
 // tokens (128 sinks + 128 residual) make MAX_SEG_SPLITS workgroups.

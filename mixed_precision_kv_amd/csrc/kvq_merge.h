@@ -119,7 +119,7 @@ __device__ inline void merge_row(const float* partial, float* out, int n_parts, 
   const float2 ml = *reinterpret_cast<const float2*>(base + min(lane, last) * stride);
   float2 v[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) v[j] = *reinterpret_cast<const float2*>(base + min(j, last) * stride + 2 + 2 * lane);
+  for (int j = 0; j < NB; ++j) v[j] = *reinterpret_cast<const float2*>(base + min(j, last) * stride + REC_OUT + 2 * lane);
   win.issue(lane);
   auto weight = [](float m, float Mx) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mx); };
   float mloc = lane <= last ? ml.x : -INFINITY;
@@ -146,7 +146,7 @@ __device__ inline void merge_row(const float* partial, float* out, int n_parts, 
     if (s0 > last) break;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, last) * stride + 2 + 2 * lane);
+      v[j] = *reinterpret_cast<const float2*>(base + min(s0 + j, last) * stride + REC_OUT + 2 * lane);
     w = weight(base[min(s0 + lane % NB, last) * stride], M);
   }
   win.apply(M, o0, o1, lane);
