@@ -340,7 +340,9 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
 // the BF16-tier operands Bq4. The staged bf16 query rows qb are read first,
 // then the tables written: interleaved, each read would wait for the writes
 // before it.
-template <int G, int NKS, int NQ>
+// NE: BF16-tier elements a lane group can hold (0, 1 or 8: the kernel's NB),
+// the rest of Bq left zero.
+template <int G, int NKS, int NQ, int NE>
 __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t* qb, MixSmem<G, NKS>& S,
                                   bf16x8 (&Bq)[NQ], int lane, int a, int h, int col) {
   constexpr int NJ = (32 * NKS + 63) / 64;
@@ -357,8 +359,8 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
   int bch[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int ch = rec_byte(recw, 8 * a + e);
-    bch[e] = 8 * a + e < g.n16 ? ch : -1;
+    const int ch = e < NE ? rec_byte(recw, 8 * a + e) : 0;
+    bch[e] = e < NE && 8 * a + e < g.n16 ? ch : -1;
   }
   float qsl[NJ][G], qbf[8];
 #pragma unroll
@@ -366,7 +368,7 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) qsl[j][hh] = qb_at(qb, hh, sch[j] >= 0 ? sch[j] : 0);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qbf[e] = qb_at(qb, h, bch[e] >= 0 ? bch[e] : 0);
+  for (int e = 0; e < 8; ++e) qbf[e] = e < NE ? qb_at(qb, h, bch[e] >= 0 ? bch[e] : 0) : 0.f;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -387,7 +389,8 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
   for (int k = 0; k < NQ; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      Bq[k][e] = (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * (NQ == 4 ? B_SCALE / tile_unscale(k) : B_SCALE) : 0.f);
+      Bq[k][e] = e < NE ? (__bf16)(bch[e] >= 0 && col < 8 ? qbf[e] * (NQ == 4 ? B_SCALE / tile_unscale(k) : B_SCALE) : 0.f)
+                        : (__bf16)0.f;
 }
 
 // Registers of 256 VGPRs (two waves per SIMD) fit every variant except the
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   __syncthreads();
   constexpr int NQ = PREC ? 1 : 4;
   bf16x8 Bq[NQ];
-  mix_tables<G, NKS, NQ>(recw, g, qb, S, Bq, lane, a, h, col);
+  mix_tables<G, NKS, NQ, NB>(recw, g, qb, S, Bq, lane, a, h, col);
   *reinterpret_cast<u32x4*>(km0 + 16 * lane) = m0[0];
   *reinterpret_cast<u32x4*>(vl0 + 16 * lane) = m0[1];
   *reinterpret_cast<u32x4*>(vh0 + 16 * lane) = m0[2];
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
     // page it: codes c0, meta slot 0; prefetch page it + 1 into c1 / slot 1
     wait_vm<0>();
     if constexpr (PREC) {
-      if (it > 0) mix_tables<G, NKS, NQ>(recn, g, qb, S, Bq, lane, a, h, col);
+      if (it > 0) mix_tables<G, NKS, NQ, NB>(recn, g, qb, S, Bq, lane, a, h, col);
     }
     if (it + 1 < np) {
       mix_issue_meta(pset.at(it + 1), slot1, g, lane);
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
       mix_page<G, NKS, NB, NPASS, NQ>(st, c0, slot0, S, Bq, xs, A.scale_log2, a, h, col, NoLogits{});
     if (it + 1 >= np) break;
     wait_vm<0>();
-    if constexpr (PREC) mix_tables<G, NKS, NQ>(recn, g, qb, S, Bq, lane, a, h, col);
+    if constexpr (PREC) mix_tables<G, NKS, NQ, NB>(recn, g, qb, S, Bq, lane, a, h, col);
     if (it + 2 < np) {
       mix_issue_meta(pset.at(it + 2), slot0, g, lane);
       mix_load(c0, pset.at(it + 2), g, a, r);
