@@ -87,14 +87,20 @@ __device__ inline int fifo_vlim(const DecodeArgs& A, int pg) {
 }
 
 // After a page's consume_values: ow follows the running maximum like the
-// value accumulators, then takes the page's full-precision Values.
+// value accumulators, then takes the page's full-precision Values. A lane's
+// st.m is its own column's head's maximum, while ow holds every head's
+// channels, so head hh's factor comes from lane hh (column hh, head hh).
 template <int G, int NPASS>
 __device__ inline void fifo_after(const DecodeArgs& A, const SoftState<NPASS>& st, float m0, int64_t head, int pg,
                                   int vlim, float (*hp)[8], float (&ow)[8][2], int lane) {
-  if (st.m != m0) {
-    const float alpha = m0 == -INFINITY ? 0.f : fast_exp2(m0 - st.m);
+  if (__any(st.m != m0)) {
+    const float alpha = m0 == -INFINITY ? 0.f : fast_exp2(m0 - st.m);   // 1 where the maximum held
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) ow[hh][0] *= alpha, ow[hh][1] *= alpha;
+    for (int hh = 0; hh < G; ++hh) {
+      const float ah = __shfl(alpha, hh);
+      ow[hh][0] *= ah;
+      ow[hh][1] *= ah;
+    }
   }
   if (vlim < PAGE) fifo_values<G>(A, head, pg, vlim, hp, ow, lane);
 }
@@ -553,16 +559,25 @@ bool launch_decode_fast(int key_mode, DecodeArgs& a, hipStream_t s, bool fifo);
 
 // Pages per split: the page splits of every (batch, kv head) are sized to
 // fill `slots` resident workgroups in one round, with the pages spread
-// evenly; the BF16-segment workgroups are dispatched after them (see
-// decode_block). DECODE_SLOTS (256 CUs x 8 resident single-wave workgroups on
-// MI355X) bounds every kernel's split count, and the workspace is sized for it.
+// evenly, but never fewer than MIN_PAGES_PER_SPLIT pages; the BF16-segment
+// workgroups are dispatched after them (see decode_block). DECODE_SLOTS (256
+// CUs x 8 resident single-wave workgroups on MI355X) bounds every kernel's
+// split count, and the workspace is sized for it. The floor matters for short
+// contexts: llama8b_8k's 64 pages per (batch, kv head) as 16 splits of 4
+// pages (1024 split waves, the 256 segment workgroups resident beside them)
+// measured 19.5 us per decode call against 20.3 us as 32 splits of 2 pages
+// (every slot taken, the segment workgroups waiting for the splits); 3, 6 or
+// 8 pages measured 21.4, 22.1 and 25.2 us. Longer contexts keep the
+// two-waves-per-SIMD split count (qwen32b_32k: 16 splits of 16 pages, 82.5
+// against 89.1 us as 8 of 32).
+constexpr int MIN_PAGES_PER_SPLIT = 4;
 int decode_pages_per_split_slots(int n_pages, int batch, int n_kv_heads, int slots) {
   const int64_t pairs = (int64_t)batch * n_kv_heads;
   const int64_t budget = slots;
   int64_t splits = budget / pairs;
   if (splits < 1) splits = 1;
   int64_t pps = (n_pages + splits - 1) / splits;
-  if (pps < 1) pps = 1;
+  if (pps < MIN_PAGES_PER_SPLIT) pps = MIN_PAGES_PER_SPLIT;
   return (int)pps;
 }
 

@@ -6,7 +6,7 @@ The whole cache is built on the GPU; the oracle recomputes sampled
 page of the slice bit-exact, the decode output of the slice's query heads
 within the 2e-3 relative bound, and the benchmark's one-page flush of the
 residual into page n_pages bit-exact. At these sizes every split of the
-decode covers several pages (2 for llama8b_8k, 16 for the others), so the
+decode covers several pages (4 for llama8b_8k, 16 or more for the others), so the
 multi-page paths the benchmark times are the ones checked:
 
 * the pipelined kernel over the contiguous cache (the benchmark's call);

@@ -38,7 +38,7 @@ def acc_ints(acc, head):
 
 @pytest.mark.parametrize("name", ["tiny_mixkvq", "llama8b_8k", "llama8b_8k_full"])
 def test_reselect_flow(name):
-    """llama8b_8k_full is the benchmark's reselection cache (two pages per
+    """llama8b_8k_full is the benchmark's reselection cache (four pages per
     decode split, so the per-page tables are rebuilt inside a split)."""
     base = synth.WORKLOADS[name.replace("_full", "")]
     if name == "tiny_mixkvq" or name.endswith("_full"):
@@ -123,7 +123,7 @@ def test_reselect_through_page_table(full):
     """The same reselection flow with the pages scattered over the pool by a
     page table: records (indexed by logical page), page bytes and the decode
     output equal the contiguous run's, bit for bit (full: the llama8b_8k
-    shape, two pages per decode split)."""
+    shape, four pages per decode split)."""
     base = synth.WORKLOADS["llama8b_8k"]
     w = base if full else base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * base.group, n_pages=5,
                                       seed=base.seed + 1100)
