@@ -110,7 +110,11 @@ __device__ inline void scan_merge(Scan& s) {
   s.mn = fminf(s.mn, __int_as_float(dpp_partner<W>(__float_as_int(s.mn))));
   s.mx = fmaxf(s.mx, __int_as_float(dpp_partner<W>(__float_as_int(s.mx))));
   s.am1 = min(s.am1, (uint32_t)dpp_partner<W>((int)s.am1));
-  s.nonfinite = s.nonfinite || dpp_partner<W>((int)s.nonfinite);
+  // not `||`: a short circuit would run the lane move only in the lanes
+  // without a non-finite value, and a DPP move reads nothing from lanes that
+  // are switched off, so the partner's flag would be lost
+  const int partner_nonfinite = dpp_partner<W>((int)s.nonfinite);
+  s.nonfinite = s.nonfinite | (partner_nonfinite != 0);
 }
 
 __device__ inline bool f16_is_inf(uint16_t h) { return (h & 0x7FFF) == 0x7C00; }
@@ -286,7 +290,9 @@ __device__ __attribute__((always_inline)) inline void flush_value_part(uint8_t* 
     for (int p = 0; p < 16; ++p) {
       const int u = p & 7, hh = p >> 3;
       bool amb;
-      word |= (uint32_t)fast_code(m[hh][u >> 1], inv[hh][u >> 1], x[p], amb) << (2 * p);
+      // cut to the code's field: an infinite input (t infinite, redone below)
+      // converts to a full-width integer that would reach the other codes
+      word |= ((uint32_t)fast_code(m[hh][u >> 1], inv[hh][u >> 1], x[p], amb) & 3u) << (2 * p);
       redo |= (uint32_t)amb << p;
     }
     while (redo) {   // the few codes within 2^-14 of a rounding midpoint, one by one
@@ -885,7 +891,8 @@ __global__ __launch_bounds__(64) void value_push_kernel(FlushArgs A, int key_mod
     sc.mn = fminf(sc.mn, __shfl_xor(sc.mn, 8));
     sc.mx = fmaxf(sc.mx, __shfl_xor(sc.mx, 8));
     sc.am1 = min(sc.am1, (uint32_t)__shfl_xor((int)sc.am1, 8));
-    sc.nonfinite = sc.nonfinite || __shfl_xor((int)sc.nonfinite, 8);
+    const int partner_nonfinite = __shfl_xor((int)sc.nonfinite, 8);   // every lane (see scan_merge)
+    sc.nonfinite = sc.nonfinite | (partner_nonfinite != 0);
   }
   const int grp = lane >> 4;
   const GroupParam p = make_param(sc, 3, (lane & 15) == 0 ? A.flags : nullptr);   // one status write per group

@@ -8,7 +8,10 @@
   residual tokens, append 64 tokens, flush the full residual into page 8
   (bit-exact), decode again over 9 pages.
 * Flush status flags: non-finite inputs, values beyond the binary16 range,
-  groups spanning more than 38 binades; constant groups bit-exact.
+  groups spanning more than 38 binades; constant groups bit-exact. The
+  non-finite flag for an element in any part of a group's scan (MixKVQ and
+  PN-Mix); an infinite Value element leaves every other group of its page
+  as the oracle's.
 * A page flagged KVQ_FLAG_RANGE (infinite binary16 metadata) decodes to
   non-finite outputs for its own (batch, kv head)'s query heads only.
 * PN-Mix with the adjacent pair layout.
@@ -160,6 +163,66 @@ def test_flush_constant_groups_and_flags():
     k5 = k.clone()
     k5[0, 0, 4, int(rec[0])] = float("inf")          # a BF16-tier channel
     assert _flush_one(p, k5, v) & kvq.KVQ_FLAG_NONFINITE
+
+
+def test_flush_infinite_value_stays_in_its_group():
+    """An infinite Value element: KVQ_FLAG_NONFINITE, its group's codes are
+    unspecified, and every other code, scale and offset of the page is the
+    oracle's. The group's bits are those that change when the element is
+    replaced by finite values far above, far below and inside the group's
+    range (widened to whole 16-bit halves, so that the group's scale and
+    offset are free too). The element sits in an even token, whose codes
+    share their 32-bit words with the next token's: a code that is not cut to
+    its 2-bit field reaches them."""
+    from oracle import flush as oflush
+    w = synth.WORKLOADS["tiny_mixkvq"].scaled(n_pages=1, n_resid=0, n_append=0, seed=1305)
+    p = built(w)
+    rec = p.gpu_record(0, 0)
+    k = p.k_pre[:, :, :128].clone()
+    v = p.v_pre[:, :, :128].clone()
+    for tok, ch in ((4, 37), (66, 0), (34, 20), (120, 127)):
+        v_inf = v.clone()
+        v_inf[0, 0, tok, ch] = float("inf")
+        f = _flush_one(p, k, v_inf)
+        assert f & kvq.KVQ_FLAG_NONFINITE, (tok, ch, f)
+        gpu = p.gpu_page(0, 0, 0)
+        refs = []
+        for sub in (1.0e4, -1.0e4, 0.0):
+            v_sub = v.clone()
+            v_sub[0, 0, tok, ch] = sub
+            refs.append(oflush.flush_mixkvq_page(p.bits(k[0, 0]), p.bits(v_sub[0, 0]), rec[:128], w.n_bf16, w.n_u4))
+        free = np.zeros_like(refs[0])
+        for r in refs[1:]:
+            free |= refs[0] ^ r
+        pairs = free.reshape(-1, 2).any(axis=1)
+        free = np.repeat(np.where(pairs, 0xFF, 0), 2).astype(np.uint8)
+        assert 0 < np.count_nonzero(free) < 64, (tok, ch)
+        got = np.asarray(gpu)[:refs[0].size]
+        assert np.array_equal(got & ~free, refs[0] & ~free), (tok, ch)
+
+
+@pytest.mark.parametrize("name", ["tiny_mixkvq", "pnmix_16k"])
+def test_flush_nonfinite_flag_at_every_position(name):
+    """KVQ_FLAG_NONFINITE for one infinite or NaN Key or Value element, wherever
+    it sits: a group's minimum, maximum and status are reduced over the
+    threads that scan parts of it (two per value group and PN-Mix Key slot,
+    eight per MixKVQ Key slot), and the flag of every part reaches the
+    thread that reports it."""
+    base = synth.WORKLOADS[name]
+    w = base.scaled(batch=1, n_kv_heads=1, n_q_heads=base.group, n_pages=1, n_resid=0, n_append=0,
+                    seed=base.seed + 1307)
+    p = built(w)
+    k = p.k_pre[:, :, :128].clone()
+    v = p.v_pre[:, :, :128].clone()
+    assert _flush_one(p, k, v) == 0
+    for val in (float("inf"), float("-inf"), float("nan")):
+        for tok in (0, 17, 63, 64, 100, 127):
+            for ch in (0, 16, 31, 45, 112, 127):
+                for which in ("k", "v"):
+                    kk, vv = k.clone(), v.clone()
+                    (kk if which == "k" else vv)[0, 0, tok, ch] = val
+                    f = _flush_one(p, kk, vv)
+                    assert f & kvq.KVQ_FLAG_NONFINITE, (name, which, val, tok, ch, f)
 
 
 def test_pnmix_adjacent_pairs():
