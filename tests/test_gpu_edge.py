@@ -14,7 +14,8 @@
   as the oracle's.
 * A page flagged KVQ_FLAG_RANGE (infinite binary16 metadata) decodes to
   non-finite outputs for its own (batch, kv head)'s query heads only.
-* PN-Mix with the adjacent pair layout.
+* PN-Mix with the adjacent pair layout; a PN-Mix record with another pair
+  count raises KVQ_FLAG_MASK.
 * Repeated decode calls give identical bits.
 """
 
@@ -223,6 +224,29 @@ def test_flush_nonfinite_flag_at_every_position(name):
                     (kk if which == "k" else vv)[0, 0, tok, ch] = val
                     f = _flush_one(p, kk, vv)
                     assert f & kvq.KVQ_FLAG_NONFINITE, (name, which, val, tok, ch, f)
+
+
+def test_pnmix_record_pair_count_flag():
+    """A PN-Mix record that selects another pair count than n_hi_pairs (one
+    pair more, one fewer) raises KVQ_FLAG_MASK; the selection's own record
+    raises nothing."""
+    base = synth.WORKLOADS["pnmix_16k"]
+    w = base.scaled(batch=1, n_kv_heads=1, n_q_heads=base.group, n_pages=1, n_resid=0, n_append=0,
+                    seed=base.seed + 1309)
+    p = built(w)
+    k = p.k_pre[:, :, :128].clone()
+    v = p.v_pre[:, :, :128].clone()
+    assert _flush_one(p, k, v) == 0
+    own = p.mask[:8].clone()
+    pm = int.from_bytes(bytes(own.cpu().numpy().tolist()), "little")
+    assert bin(pm).count("1") == w.n_hi_pairs
+    unset = next(i for i in range(64) if not (pm >> i) & 1)
+    first = next(i for i in range(64) if (pm >> i) & 1)
+    for other in (pm | (1 << unset), pm & ~(1 << first)):
+        p.mask[:8] = torch.tensor(list(other.to_bytes(8, "little")), dtype=torch.uint8, device="cuda")
+        assert _flush_one(p, k, v) & kvq.KVQ_FLAG_MASK, hex(other)
+    p.mask[:8] = own
+    assert _flush_one(p, k, v) == 0
 
 
 def test_pnmix_adjacent_pairs():

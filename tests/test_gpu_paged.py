@@ -5,7 +5,8 @@ bytes, bit for bit, where its table entry says; the decode through the table
 (pipelined and generic kernels) gives the contiguous decode's output bit for
 bit, and the oracle's within the decode bound; the fused decode + flush call
 writes the residual's page through the table; a flush entry outside the pool
-writes nothing and raises KVQ_FLAG_TABLE.
+writes nothing and raises KVQ_FLAG_TABLE; a decode entry outside the pool is
+clamped into it.
 """
 
 import numpy as np
@@ -126,3 +127,20 @@ def test_paged_fused_step_and_bad_entry(name):
         if h != 1:
             assert torch.equal(pool_page(arena2, p, int(tab[h, w.n_pages])), pool_page(before, p, int(tab[h, w.n_pages])))
     assert torch.equal(arena2, before)
+    # decode entries outside the pool are clamped into it (0 and the last
+    # pool page): the same bits as the explicitly clamped table, both kernels
+    pool = w.batch * w.n_kv_heads * p.max_pages
+    wild, clamped = table.clone(), table.clone()
+    wild[0, 0], clamped[0, 0] = -3, 0
+    wild[1, 2], clamped[1, 2] = pool + 5, pool - 1
+    for cfg in (p.cfg, kvq.with_fields(p.cfg, decode_path=kvq.KVQ_DECODE_GENERIC)):
+        outs = []
+        for tab_ in (wild, clamped):
+            o = torch.zeros_like(p.out)
+            kvq.kvq_decode_attention(cfg, p.q_dec, arena2, w.n_pages, p.mask, p.S, p.sink_k, p.sink_v, w.n_sink,
+                                     p.resid_k, p.resid_v, w.n_resid, 128, p.scale, o, p.ws, p.ws_bytes,
+                                     page_table=tab_, table_stride=p.max_pages)
+            outs.append(o)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        assert bool(torch.isfinite(outs[0]).all())
