@@ -317,29 +317,35 @@ __device__ inline void consume_own(SoftState<NPASS>& st, const f32x4 (&J)[4], fl
     st.m = mn;
   }
   const float shift = xb - st.m;
-  // own k-steps: lanes < 8 hold k-steps 0, 1 (tiles 0-3), lanes >= 8 k-steps 2, 3
-  u32x4 own[2], oth[2];
+  // own k-steps: lanes < 8 hold k-steps 0, 1 (tiles 0-3), lanes >= 8 k-steps
+  // 2, 3. Every lane needs all four: k-step k2 (k2 < 2) is lane col - 8's own
+  // in lanes 8-15 of each row (DPP banks 2-3) and k-step 2 + k2 lane col + 8's
+  // in lanes 0-7 (banks 0-1); a row rotate by 8 written to those banks only
+  // leaves the own value in the others.
+  u32x4 pk[4];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
     half8 ph;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       ph[e] = (_Float16)fast_exp2(fmaf(J[2 * k2 + (e >> 2)][e & 3], xs, shift));   // token pi(ks, a, e)
-    __builtin_memcpy(&own[k2], &ph, 16);
-    oth[k2].x = dpp_u<0x128, 0xF>(0u, own[k2].x);   // the partner's two k-steps
-    oth[k2].y = dpp_u<0x128, 0xF>(0u, own[k2].y);
-    oth[k2].z = dpp_u<0x128, 0xF>(0u, own[k2].z);
-    oth[k2].w = dpp_u<0x128, 0xF>(0u, own[k2].w);
+    u32x4 own;
+    __builtin_memcpy(&own, &ph, 16);
+    pk[k2].x = dpp_u<0x128, 0xC>(own.x, own.x);
+    pk[k2].y = dpp_u<0x128, 0xC>(own.y, own.y);
+    pk[k2].z = dpp_u<0x128, 0xC>(own.z, own.z);
+    pk[k2].w = dpp_u<0x128, 0xC>(own.w, own.w);
+    pk[2 + k2].x = dpp_u<0x128, 0x3>(own.x, own.x);
+    pk[2 + k2].y = dpp_u<0x128, 0x3>(own.y, own.y);
+    pk[2 + k2].z = dpp_u<0x128, 0x3>(own.z, own.z);
+    pk[2 + k2].w = dpp_u<0x128, 0x3>(own.w, own.w);
   }
-  const bool hi = col < 8;
   const int jl = col / G;
   const int zr = col < 4 ? col : 3;
   const uint32_t zconst = col == 4 ? 0x3C003C00u : 0u;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    // k-steps 0, 1 are the own ones of lanes < 8, k-steps 2, 3 of lanes >= 8
-    const bool mine = (ks < 2) == hi;
-    const half8 ph = as_half8(mine ? own[ks & 1] : oth[ks & 1]);
+    const half8 ph = as_half8(pk[ks]);
     {
       const u32x4 zw = vm.z(ks, a, zr);
       u32x4 za;
