@@ -516,13 +516,14 @@ __device__ inline void fifo_store_own(const DecodeArgs& A, int b, int kvh, int p
 
 // This lane's half of B = q * s, with qh = binary16(q * 2^-6): the hi part
 // binary16(qh s) (columns 0-7) or its rounding error binary16(qh s - hi)
-// (columns 8-15, one fused rounding). Packed half-precision arithmetic, two
-// slots per instruction.
-__device__ inline half8 key_operand_half(const half8& qh, const u32x4& sw, bool lo_col) {
+// (columns 8-15, one fused rounding), both as fma(qh, s, binary16(qn s)):
+// qn = 0 in columns 0-7 (the exact product rounded once) and qn = -qh in
+// columns 8-15 (binary16(-qh s) = -hi, rounding being symmetric), read from
+// a table whose head G is zero, so no per-lane select is needed. Packed
+// half-precision arithmetic, two slots per instruction.
+__device__ inline half8 key_operand_half(const half8& qh, const half8& qn, const u32x4& sw) {
   const half8 s8 = as_half8(sw);
-  const half8 hi = qh * s8;
-  const half8 lo = __builtin_elementwise_fma(qh, s8, -hi);
-  return lo_col ? lo : hi;
+  return __builtin_elementwise_fma(qh, s8, qn * s8);
 }
 
 __device__ inline bf16x8 as_bf16x8(const u32x4& v) {

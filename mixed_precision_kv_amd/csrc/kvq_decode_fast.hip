@@ -127,6 +127,7 @@ struct PgSmem {
     struct {
       half8 qh[NKS][4][G];         // [k-step][lane group][head]: binary16 q * 2^-6 of the slot's channel
       half8 qz[NKS][4][G];         // q of the slot's channel as binary16 (offset MFMA operand)
+      half8 qn[NKS][4][G + 1];     // -qh, and zero at head G (the Key operand's correction term)
       uint8_t meta[2][META_SLOT];  // double-buffered page metadata
     } pg;
     float p_lds[256][8];
@@ -145,6 +146,7 @@ struct MixSmem {
     struct {
       half8 qh[NKS][4][G];         // [k-step][lane group][head]: binary16 q * 2^-6 of the slot's channel
       half8 qz[NKS][4][G];         // q of the slot's channel as binary16 (offset MFMA operand)
+      half8 qn[NKS][4][G + 1];     // -qh, and zero at head G (the Key operand's correction term)
     } pg;
     float p_lds[256][8];
   } u;
@@ -297,7 +299,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
   for (int ks = 0; ks < NKS; ++ks) {
     const uint8_t* km = slot.k + 32 * (4 * ks + a);   // past F: zero meta
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
-    const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], sw, col >= 8);
+    const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], S.u.pg.qn[ks][a][col >= 8 ? h : G], sw);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
     const u32x4 k8 = c.kc[ks] >> 8u;
 #pragma unroll
@@ -378,11 +380,14 @@ __device__ inline void mix_tables(uint32_t recw, const MixGeo& g, const uint8_t*
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         const float qf = sch[j] >= 0 ? qsl[j][hh] : 0.f;
-        S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
+        const _Float16 qhv = (_Float16)(qf * B_SCALE);   // exact unless |q| < 2^-11
+        S.u.pg.qh[ks][aa][hh][e] = qhv;
+        S.u.pg.qn[ks][aa][hh][e] = -qhv;
         S.u.pg.qz[ks][aa][hh][e] = (_Float16)qf;   // exact for bf16 q inside the binary16 range
       }
     }
   }
+  if (lane < 4 * NKS) S.u.pg.qn[lane >> 2][lane & 3][G] = half8{};
   // the BF16-tier operand: q * 2^-6, for NQ = 4 also times 4^k * 2^-24 for the
   // tiles with i & 3 = k (exact power-of-two scalings of the bf16 query)
 #pragma unroll
@@ -530,7 +535,7 @@ __device__ inline void pn_keys(f32x4 (&J)[4], f32x4& zacc, const PnKey& c, const
   for (int ks = 0; ks < 4; ++ks) {
     const uint8_t* km = slot + 32 * (4 * ks + a);
     const u32x4 sw = lds16(km), zw = lds16(km + 16);
-    const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], sw, col >= 8);
+    const half8 B = key_operand_half(S.u.pg.qh[ks][a][h], S.u.pg.qn[ks][a][col >= 8 ? h : G], sw);
     zacc = mfma(as_half8(zw), S.u.pg.qz[ks][a][h], zacc);
     {                                       // LSB plane: 1-bit codes, weight s
       const Row1 x = row1(rd(c.lsb[ks >> 1], 2 * (ks & 1)), rd(c.lsb[ks >> 1], 2 * (ks & 1) + 1));
@@ -615,10 +620,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int s = lane + 64 * j, ks = s >> 5, aa = (s >> 3) & 3, e = s & 7;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      S.u.pg.qh[ks][aa][hh][e] = (_Float16)(qsl[j][hh] * B_SCALE);   // exact unless |q| < 2^-11
+      const _Float16 qhv = (_Float16)(qsl[j][hh] * B_SCALE);   // exact unless |q| < 2^-11
+      S.u.pg.qh[ks][aa][hh][e] = qhv;
+      S.u.pg.qn[ks][aa][hh][e] = -qhv;
       S.u.pg.qz[ks][aa][hh][e] = (_Float16)qsl[j][hh];
     }
   }
+  if (lane < 4 * 4) S.u.pg.qn[lane >> 2][lane & 3][G] = half8{};
   __syncthreads();
 
   SoftState<NPASS> st;
