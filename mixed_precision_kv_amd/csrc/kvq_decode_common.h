@@ -142,11 +142,29 @@ __device__ inline void init_state(SoftState<NPASS>& st) {
 // vm_lo / vm_hi where they are used; VMeta holds them loaded beforehand
 // (load_vmeta), with the page's other loads, so that a page waits for
 // memory once.
+// The constant rows of the offset MFMA's A operand, in LDS: ones, then
+// zeros. Written once per workgroup before the page loop's first barrier.
+struct ZConst {
+  u32x4 v[2];
+  __device__ inline void init(int lane) {
+    if (lane < 2) v[lane] = lane == 0 ? (u32x4){0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                                      : (u32x4){0u, 0u, 0u, 0u};
+  }
+  __device__ inline const uint8_t* ptr() const { return reinterpret_cast<const uint8_t*>(v); }
+};
+
 struct VMetaAt {
   const uint8_t* lo;
   const uint8_t* hi;
+  const uint8_t* zc;   // 32 bytes: eight binary16 ones, then zeros (ZConst)
   __device__ inline const uint8_t* row(int ks, int a) const { return (ks < 2 ? lo : hi) + 512 * (ks & 1) + 128 * a; }
   __device__ inline u32x4 z(int ks, int a, int zr) const { return ld16(row(ks, a) + 32 * zr + 16); }
+  // the offset MFMA's A operand of column col: the offsets of head col
+  // (col < 4), ones (col 4: the probability sum) or zeros, each lane
+  // reading its own 16 bytes
+  __device__ inline u32x4 za(int ks, int a, int col) const {
+    return ld16(col < 4 ? row(ks, a) + 32 * col + 16 : zc + (col == 4 ? 0 : 16));
+  }
   __device__ inline u32x4 s(int ks, int, int a, int j) const { return ld16(row(ks, a) + 32 * j); }
 };
 template <int G, int NPASS>
@@ -341,20 +359,10 @@ __device__ inline void consume_own(SoftState<NPASS>& st, const f32x4 (&J)[4], fl
     pk[2 + k2].w = dpp_u<0x128, 0x3>(own.w, own.w);
   }
   const int jl = col / G;
-  const int zr = col < 4 ? col : 3;
-  const uint32_t zconst = col == 4 ? 0x3C003C00u : 0u;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const half8 ph = as_half8(pk[ks]);
-    {
-      const u32x4 zw = vm.z(ks, a, zr);
-      u32x4 za;
-      za.x = col < 4 ? zw.x : zconst;
-      za.y = col < 4 ? zw.y : zconst;
-      za.z = col < 4 ? zw.z : zconst;
-      za.w = col < 4 ? zw.w : zconst;
-      st.zl = mfma(as_half8(za), ph, st.zl);
-    }
+    st.zl = mfma(as_half8(vm.za(ks, a, col)), ph, st.zl);
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
       const int j = (jl + P * C) & 3;

@@ -134,6 +134,7 @@ struct PgSmem {
   } u;
   int slot_ch[32 * NKS];
   float mh[16];
+  ZConst zc;                     // constant rows of the offset MFMA operand
 };
 
 // Shared memory of the MixKVQ kernel. The page metadata lives in six
@@ -151,6 +152,7 @@ struct MixSmem {
     float p_lds[256][8];
   } u;
   float mh[16];
+  ZConst zc;                     // constant rows of the offset MFMA operand
 };
 
 template <int G, int NK = 8>
@@ -163,6 +165,7 @@ struct QjSmem {
     float p_lds[256][8];
   } u;
   float mh[16];
+  ZConst zc;                     // constant rows of the offset MFMA operand
 };
 
 // value meta (2048 B) of a page -> LDS slot + 1024: two async loads
@@ -332,7 +335,7 @@ __device__ inline void mix_page(SoftState<NPASS>& st, const MixCodes<NKS, NB>& c
     for (int t = 0; t < 4; ++t) J[t] *= tile_unscale(t);   // tiles t and t + 4 carry the same factor
   }
   win(J, zacc[0] * scale_log2);
-  consume_own<G, NPASS>(st, J, xs, zacc[0] * scale_log2, c.vc, VMetaAt{slot.v_lo, slot.v_hi}, a, col);
+  consume_own<G, NPASS>(st, J, xs, zacc[0] * scale_log2, c.vc, VMetaAt{slot.v_lo, slot.v_hi, S.zc.ptr()}, a, col);
 }
 
 // The record's tables for the page loop: slot -> channel of this lane's slots
@@ -455,6 +458,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB == 8 ? 1 
   *reinterpret_cast<u32x4*>(km0 + 16 * lane) = m0[0];
   *reinterpret_cast<u32x4*>(vl0 + 16 * lane) = m0[1];
   *reinterpret_cast<u32x4*>(vh0 + 16 * lane) = m0[2];
+  S.zc.init(lane);
   __syncthreads();
 
   SoftState<NPASS> st;
@@ -627,6 +631,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
   }
   if (lane < 4 * 4) S.u.pg.qn[lane >> 2][lane & 3][G] = half8{};
+  S.zc.init(lane);
   __syncthreads();
 
   SoftState<NPASS> st;
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         pn_keys<G>(J, zacc, k, slot, S, a, h, col);
         if constexpr (FIFO) fifo_store_own<G>(A, b, kvh, p0 + p, J, xs, zacc[0] * A.scale_log2, a, col);
         mid();
-        consume_own<G, NPASS>(st, J, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
+        consume_own<G, NPASS>(st, J, xs, zacc[0] * A.scale_log2, v.vc, VMetaAt{slot + 1024, slot + 2048, S.zc.ptr()}, a, col);
       });
   write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
@@ -796,6 +801,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2)
   ssum = wave_sum_groups(ssum);
   if constexpr (OUT) ssum_o = wave_sum_groups(ssum_o);
   const float ratio = OUT ? (float)A.qjl_m / (float)A.qjl_mo : 0.f;   // the instances' sqrt(pi/2)/m factors
+  S.zc.init(lane);
   __syncthreads();
 
   SoftState<NPASS> st;
@@ -811,7 +817,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OUT ? 1 : 2)
         qj_keys<G, OUT>(J, k, slot, S, ssum, ssum_o, ratio, a, h, col);
         if constexpr (FIFO) fifo_store_own<G>(A, b, kvh, p0 + p, J, xs, 0.f, a, col);
         mid();
-        consume_own<G, NPASS>(st, J, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048}, a, col);
+        consume_own<G, NPASS>(st, J, xs, 0.f, v.vc, VMetaAt{slot + 1024, slot + 2048, S.zc.ptr()}, a, col);
       });
   write_partial_direct<G, NPASS>(A, st, split, b, kvh, a, col);
 }
